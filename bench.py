@@ -1,0 +1,305 @@
+#!/usr/bin/env python3
+"""Benchmark of the NVFP4 W4A4 MoE hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  rollout side   nvfp4_quantize(X) -> resq_select_and_requant(X, expert units)
+                 -> gate/up grouped GEMM (+comp, SwiGLU, amax) -> nvfp4_quantize(h)
+                 -> resq_select_and_requant(h) -> down grouped GEMM (+comp, scatter-add)
+  trainer side   qdq_weights(all expert matrices) -> guided_round(X_train vs rollout codes)
+Inputs are resident in HBM before the timed region; weights are pre-quantized
+to NVFP4 (the rollout holds NVFP4 weights) outside it.
+
+Prints ONE JSON line.  value = algorithmic FLOPs of the compensated expert
+GEMMs per step / step time.  Per-part times come from HIP events recorded on
+the stream the kernels run on; the roofline object is for the kernel that
+takes most of the step, and "parts" gives every part's own rate.
+"""
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP4_PEAK_TFLOPS = 10100.0
+
+
+def gemm_flops(rows, n, k, kc):
+    return 2.0 * rows * n * (k + kc)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="moe_T8192_H4096_E256_I1536_k64_trainer")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    return ap.parse_args()
+
+
+class Timeline:
+    """HIP events recorded on the current stream between the parts of a step."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.marks = []
+
+    def mark(self, name):
+        ev = self.torch.cuda.Event(enable_timing=True)
+        ev.record(self.torch.cuda.current_stream())
+        self.marks.append((name, ev))
+
+    def durations(self):
+        out = {}
+        for (n0, e0), (n1, e1) in zip(self.marks[:-1], self.marks[1:]):
+            out[n1] = out.get(n1, 0.0) + e0.elapsed_time(e1)
+        return out
+
+
+def build_inputs(torch, P, synth, wl, dev):
+    t_gen = time.time()
+    x = synth.activations(wl.tokens, wl.hidden, seed=wl.seed, device=dev.type,
+                          heavy_frac=wl.heavy_frac)
+    rt = synth.route(wl.tokens, wl.experts, seed=wl.seed, top_k=wl.top_k, zipf_s=wl.zipf_s)
+    wgu = synth.weights(wl.experts, 2 * wl.inter, wl.hidden, seed=wl.seed, tensor_id=synth.WGU_ID,
+                        device=dev.type)
+    wd = synth.weights(wl.experts, wl.hidden, wl.inter, seed=wl.seed, tensor_id=synth.WD_ID,
+                       device=dev.type)
+    x_train = synth.guided_noise(x, seed=wl.seed, rel=wl.guided_rel) if wl.trainer else None
+    # rollout-side NVFP4 weights (pre-quantized outside the timed region)
+    _, gc, gs, gg = P.qdq_weights(wgu)
+    _, dc, ds, dg = P.qdq_weights(wd)
+    torch.cuda.synchronize()
+    inp = dict(
+        x=x, x_train=x_train, wgu=wgu, wd=wd, gc=gc, gs=gs, gg=gg, dc=dc, ds=ds, dg=dg,
+        offs=torch.from_numpy(rt["offsets"]).to(dev),
+        slot_token=torch.from_numpy(rt["slot_token"]).to(dev),
+        slot_weight=torch.from_numpy(rt["slot_weight"]).to(dev),
+        rows=int(rt["offsets"][-1]), routing=rt,
+        y=torch.zeros(wl.tokens, wl.hidden, dtype=torch.float32, device=dev),
+        amax=torch.empty(1, dtype=torch.float32, device=dev),
+    )
+    return inp, time.time() - t_gen
+
+
+def run_step(P, inp, wl, tl, trainer=True):
+    tl.mark("start")
+    xq_c, xq_s, xq_g, _ = P.nvfp4_quantize(inp["x"])
+    tl.mark("quantize_x")
+    sel1, rc1, rs1, rg1 = P.resq_select_and_requant(
+        inp["x"], xq_c, xq_s, xq_g, wl.k, unit_offsets=inp["offs"], rows_total=inp["rows"],
+        row_index=inp["slot_token"])
+    tl.mark("resq_x")
+    h = P.moe_w4a4_grouped_gemm(xq_c, xq_s, xq_g, inp["offs"], inp["rows"], inp["gc"], inp["gs"],
+                                inp["gg"], epilogue=P.EPI_SWIGLU_BF16, a_row_index=inp["slot_token"],
+                                sel_idx=sel1, r_codes=rc1, r_scales=rs1, r_global=rg1,
+                                out_amax=inp["amax"])
+    tl.mark("gemm_gate_up")
+    hq_c, hq_s, hq_g, _ = P.nvfp4_quantize(h, amax_in=inp["amax"])
+    tl.mark("quantize_h")
+    sel2, rc2, rs2, rg2 = P.resq_select_and_requant(h, hq_c, hq_s, hq_g, wl.k,
+                                                    unit_offsets=inp["offs"], rows_total=inp["rows"])
+    tl.mark("resq_h")
+    inp["y"].zero_()
+    tl.mark("zero_y")
+    P.moe_w4a4_grouped_gemm(hq_c, hq_s, hq_g, inp["offs"], inp["rows"], inp["dc"], inp["ds"],
+                            inp["dg"], epilogue=P.EPI_SCATTER_ADD_F32, sel_idx=sel2, r_codes=rc2,
+                            r_scales=rs2, r_global=rg2, row_weight=inp["slot_weight"],
+                            scatter_index=inp["slot_token"], out=inp["y"])
+    tl.mark("gemm_down")
+    out = dict(xq=(xq_c, xq_s, xq_g), sel1=(sel1, rc1, rs1, rg1), h=h, hq=(hq_c, hq_s, hq_g),
+               sel2=(sel2, rc2, rs2, rg2))
+    if trainer and inp["x_train"] is not None:
+        P.qdq_weights(inp["wgu"], want_codes=False)
+        P.qdq_weights(inp["wd"], want_codes=False)
+        tl.mark("qdq")
+        out["guided"] = P.guided_round(inp["x_train"], xq_c, xq_s, xq_g, want_fq=True)
+        tl.mark("guided")
+    return out
+
+
+def part_work(wl, rows):
+    """Algorithmic bytes / flops of each part of one step."""
+    T, H, I, E, k = wl.tokens, wl.hidden, wl.inter, wl.experts, wl.k
+    nv = lambda n: n * (0.5 + 1 / 16)                       # NVFP4 bytes of n elements
+    w = {}
+    w["quantize_x"] = dict(bytes=T * H * 2 + nv(T * H), unit="GB/s")
+    w["resq_x"] = dict(bytes=rows * H * 2 + nv(rows * H) + nv(rows * k) + E * k * 4, unit="GB/s")
+    w["gemm_gate_up"] = dict(flops=gemm_flops(rows, 2 * I, H, k),
+                             bytes=E * nv(2 * I * H) + nv(rows * H) + nv(rows * k) + rows * I * 2,
+                             unit="TFLOP/s")
+    w["quantize_h"] = dict(bytes=rows * I * 2 + nv(rows * I), unit="GB/s")
+    w["resq_h"] = dict(bytes=rows * I * 2 + nv(rows * I) + nv(rows * k) + E * k * 4, unit="GB/s")
+    w["gemm_down"] = dict(flops=gemm_flops(rows, H, I, k),
+                          bytes=E * nv(H * I) + nv(rows * I) + nv(rows * k) + T * H * 4,
+                          unit="TFLOP/s")
+    if wl.trainer:
+        n_w = E * (2 * I * H + H * I)
+        w["qdq"] = dict(bytes=n_w * 2 * 2, unit="GB/s")
+        w["guided"] = dict(bytes=T * H * 2 + nv(T * H) + T * H / 2 + T * H * 2, unit="GB/s")
+    return w
+
+
+def cpu_baseline(wl, inp, budget_s):
+    """The oracle (as it stands) on a bounded sample of the same workload:
+    compensated gate/up and down GEMMs of whole experts, taken in expert order
+    until the time budget is spent.  Returns GEMM TFLOP/s on the host."""
+    import torch
+    from oracle import gemm as OG
+    from oracle import nvfp4 as OQ
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count()
+    offs = inp["routing"]["offsets"]
+    tok = inp["routing"]["slot_token"]
+    xs = inp["x"].float().cpu().numpy()
+    flops = 0.0
+    done = 0
+    t0 = time.time()
+    for e in range(wl.experts):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if b == a:
+            continue
+        rows_x = xs[tok[a:b]]
+        xc, xsc, xg = OQ.quantize(xs)
+        sel, rc, rs, rg = OQ.resq_select_and_requant(xs, xc, xsc, xg, [0, b - a], wl.k, row_index=tok[a:b])
+        wgu = inp["wgu"][e:e + 1].float().cpu().numpy()
+        _, gc, gs, gg = OQ.qdq_weights(wgu)
+        OG.gemm_comp(xc[tok[a:b]], xsc[tok[a:b]], xg, gc[0], gs[0], gg[0], sel[0], rc, rs, rg[0])
+        flops += gemm_flops(b - a, 2 * wl.inter, wl.hidden, wl.k)
+        done += 1
+        del rows_x
+        if time.time() - t0 > budget_s:
+            break
+    dt = time.time() - t0
+    return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
+                sample=f"{done} expert(s) of the gate/up projection ({wl.hidden}->{2 * wl.inter}, "
+                       f"k={wl.k}), each with NVFP4 quantization of X, residual selection, weight "
+                       f"quantization and the fp64 compensated GEMM; {dt:.1f} s",
+                seconds=round(dt, 2))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); nothing in this "
+              "library uses a second GPU.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import precision_gemm_nvfp4_amd as P
+    import synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    P.load()
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[args.workload]
+    assert wl.kind == "moe", "bench.py runs MoE workloads"
+    print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
+    inp, gen_s = build_inputs(torch, P, synth, wl, dev)
+    print(f"[bench] inputs ready in {gen_s:.1f}s; rows={inp['rows']}; warmup {args.warmup}",
+          file=sys.stderr, flush=True)
+
+    for _ in range(args.warmup):
+        run_step(P, inp, wl, Timeline(torch))
+    torch.cuda.synchronize()
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    timelines = []
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(args.steps):
+        tl = Timeline(torch)
+        run_step(P, inp, wl, tl)
+        timelines.append(tl)
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(end)
+    ms_per_step = total_ms / args.steps
+
+    parts_ms = {}
+    for tl in timelines:
+        for k, v in tl.durations().items():
+            parts_ms[k] = parts_ms.get(k, 0.0) + v / args.steps
+    work = part_work(wl, inp["rows"])
+    parts = {}
+    for name, ms in parts_ms.items():
+        if name not in work:
+            continue
+        w = work[name]
+        d = dict(ms=round(ms, 4))
+        if "flops" in w:
+            d["tflops"] = round(w["flops"] / (ms * 1e-3) / 1e12, 2)
+            d["frac_bf16_peak"] = round(d["tflops"] / BF16_PEAK_TFLOPS, 4)
+            d["frac_fp4_peak"] = round(d["tflops"] / FP4_PEAK_TFLOPS, 4)
+        d["gbs"] = round(w["bytes"] / (ms * 1e-3) / 1e9, 1)
+        d["frac_hbm"] = round(d["gbs"] / HBM_PEAK_GBS, 4)
+        parts[name] = d
+
+    gemm_flops_step = work["gemm_gate_up"]["flops"] + work["gemm_down"]["flops"]
+    value = gemm_flops_step / (ms_per_step * 1e-3) / 1e12
+    gemm_ms = parts_ms["gemm_gate_up"] + parts_ms["gemm_down"]
+    dominant = max(parts_ms, key=lambda k: parts_ms[k])
+    if dominant.startswith("gemm"):
+        ach = gemm_flops_step / (gemm_ms * 1e-3) / 1e12
+        roofline = dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                        frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None,
+                        kernel="grouped_gemm_kernel", mfma_dtype="bf16",
+                        frac_fp4_peak=round(ach / FP4_PEAK_TFLOPS, 4))
+    else:
+        w = work[dominant]
+        ach = w["bytes"] / (parts_ms[dominant] * 1e-3) / 1e9
+        roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                        frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, kernel=dominant)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(wl, inp, args.cpu_budget_s)
+
+    line = {
+        "metric": "compensated W4A4 MoE GEMM TFLOPS (% FP4 peak); quantizer GB/s (% HBM)",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "nvfp4 (e2m1 + e4m3 scales) operands, bf16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded; Gaussian activations with 1% Student-t(3) x8 channels, "
+                "N(0,0.02) weights, top-8 softmax routing)",
+        "config": {"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden,
+                   "experts": wl.experts, "inter": wl.inter, "top_k": wl.top_k, "k_comp": wl.k,
+                   "routed_rows": inp["rows"], "parallelism": "single GPU"},
+        "gemm_tflops": round(gemm_flops_step / (gemm_ms * 1e-3) / 1e12, 2),
+        "parts": parts,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "wall_s_timed": round(wall, 3),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+/*
+ * nvfp4_resq.h -- C ABI of the MI355X (gfx950) NVFP4 W4A4 MoE expert GEMM with
+ * residual activation compensation, plus the trainer-side weight QDQ and
+ * rollout-guided rounding.
+ *
+ * Sources of the operations (web pages; cited by title and section):
+ *   [QUADS]  "QUADS: Stabilizing NVFP4 Reinforcement Learning for MoE via
+ *            QUantization-error Alignment across Dual Sides", technical
+ *            summary (gist.science), sections 1, 2.1, 2.2A, 2.2B; digest
+ *            (yfxerp.com).
+ *   [TRACE]  "TRACE: Rollout-Guided Quantization-Aware Training for FP4
+ *            Reinforcement Learning of MoE Language Models", summary
+ *            (paper.rainbus.top): "Prerequisites: NVFP4 and the E2M1
+ *            codebook", "Research motivation", "Core method", "Method steps".
+ *
+ * Number format (NVFP4), one definition for every entry point:
+ *   - element: 4-bit E2M1 code = sign<<3 | index, magnitudes by index
+ *     0, 0.5, 1, 1.5, 2, 3, 4, 6 ([QUADS] sec. 1 counts eight levels a sign;
+ *     [TRACE] prerequisites: E2M1 codebook, round-to-nearest);
+ *   - block: 16 consecutive elements of a row share one E4M3 (OCP E4M3FN,
+ *     max 448) scale byte s_b;
+ *   - tensor: one fp32 global scale g = RNE32(amax / 2688) (1 if that is 0);
+ *   - s_b = E4M3 nearest to amax_b / (6 g), ties to even, saturating at 448;
+ *   - S_b = RNE32(s_b * g); element index = E2M1 index nearest to |x| / S_b
+ *     (exact real quotient; ties to the even index; above 6 gives 6; S_b = 0
+ *     gives 0); the sign bit copies x's sign bit;
+ *   - dequantized value DQ = RNE32(value * S_b).
+ *   Storage: codes [rows, K/2] bytes, element 2j in the low nibble of byte j;
+ *   scales [rows, K/16] bytes, row-major.  4.5 bit per element.
+ *
+ * Conventions of every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; scalars
+ *     such as g, amax and r_global stay on the device.  Sizes and counts are
+ *     host integers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Calls are asynchronous on it; nothing synchronizes the host.
+ *   - Arguments are validated on the host before any launch; on error
+ *     nothing is written and a negative status is returned; the message is
+ *     available from nvfp4_last_error() (thread-local).
+ *   - Index inputs that only the device can read (row indexes, offsets,
+ *     selected channels) are clamped or skipped when out of range; they
+ *     never cause out-of-bounds accesses, but out-of-range values give
+ *     unspecified results.
+ *   - Workspace: `ws` points to at least <name>_workspace_size(...) bytes of
+ *     device memory, 256-byte aligned; its contents need no initialization
+ *     and are garbage afterwards.  The library allocates nothing.
+ *   - Base pointers must be 16-byte aligned; K % 16 == 0 and the compensated
+ *     channel count k % 16 == 0, 16 <= k <= K.
+ *   - Non-finite inputs are outside the contract.
+ *   - Calls that share a workspace or outputs on one stream are ordered by
+ *     the stream; concurrent use of one workspace from two streams races.
+ */
+#ifndef NVFP4_RESQ_H
+#define NVFP4_RESQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* status codes */
+#define NVFP4_OK            0
+#define NVFP4_EINVAL       -1   /* invalid argument */
+#define NVFP4_EUNSUPPORTED -2   /* unsupported dtype, shape or device */
+#define NVFP4_EWORKSPACE   -3   /* workspace missing or too small */
+#define NVFP4_EHIP         -4   /* a HIP call failed (message has the HIP error) */
+
+/* activation dtypes */
+#define NVFP4_DTYPE_BF16 0
+#define NVFP4_DTYPE_F32  1
+
+/* grouped-GEMM epilogues */
+#define NVFP4_EPI_F32              0  /* out fp32 [rows, N] = Y */
+#define NVFP4_EPI_SWIGLU_BF16      1  /* out bf16 [rows, N/2] = silu(Y[:, :N/2]) * Y[:, N/2:] */
+#define NVFP4_EPI_SCATTER_ADD_F32  2  /* out fp32 [out_rows, N]: out[scatter_index[r]] += row_weight[r] * Y[r] */
+
+/* Library version (major*10000 + minor*100 + patch). */
+int nvfp4_version(void);
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* nvfp4_last_error(void);
+
+/* ------------------------------------------------------------------------ *
+ * nvfp4_quantize -- online NVFP4 quantization of an activation tensor.
+ *
+ * Computes, for x [M, K] (row stride ldx elements): the global scale g (from
+ * the tensor's amax, or from *amax_in when given), the E4M3 block scales and
+ * the packed E2M1 codes, with the format rules above ([TRACE] prerequisites
+ * and the research-motivation worked example; online per-forward activation
+ * quantization: [QUADS] sec. 2.1).
+ *
+ * Optionally (tile_partials != NULL) also the residual channel-score
+ * partials used by resq_select_and_requant: for every 128-row tile t of x,
+ * tile_partials[t, c] = sum of |x - DQ| over the tile's rows of channel c,
+ * summed in fp32 in increasing row order from 0 ([QUADS] sec. 2.2B ranks
+ * channels by residual magnitude).
+ *
+ *   x              bf16 or fp32 [M, ldx]
+ *   dtype          NVFP4_DTYPE_BF16 | NVFP4_DTYPE_F32
+ *   amax_in        NULL, or device fp32: use this amax instead of computing it
+ *   codes          out [M, K/2];  scales out [M, K/16];  g_out out fp32 [1] (may be NULL)
+ *   tile_partials  NULL or out fp32 [ceil(M/128), K]
+ * Errors: EINVAL for null required pointers, K % 16 != 0, ldx < K, M < 0;
+ *         EWORKSPACE if ws_bytes < nvfp4_quantize_workspace_size(M, K).
+ * M == 0 is valid: g_out = 1, nothing else written.
+ * ------------------------------------------------------------------------ */
+size_t nvfp4_quantize_workspace_size(int64_t M, int64_t K);
+int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* g_out,
+                   float* tile_partials, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * resq_select_and_requant -- residual activation compensation: pick the
+ * high-residual channels of each selection unit and quantize their residual
+ * a second time ([QUADS] sec. 2.2B: binary channel mask over channels of
+ * largest residual magnitude, second FP4 quantization; the yfxerp digest:
+ * the result is added back by the GEMM).
+ *
+ * Unit u owns "unit rows" unit_offsets[u] .. unit_offsets[u+1]-1; unit row r
+ * is row row_index[r] of x (row r when row_index is NULL).  For each unit:
+ *   R = x - DQ(codes, scales, *g) on its rows;
+ *   score[c] = sum |R[:, c]|: unit rows cut into consecutive 128-row tiles,
+ *              each summed in fp32 in increasing row order from 0, then the
+ *              tile sums added in tile order from 0;
+ *   sel_idx[u] = the k channels of largest score (ties to the lower index),
+ *              written in ascending channel order;
+ *   R_S = R[:, sel_idx[u]] (compact fp32 [rows_u, k]) quantized to NVFP4
+ *         with its own global scale r_global[u] (blocks of 16 along the
+ *         compact axis) -> r_codes / r_scales rows of the unit.
+ * A unit with no rows gets sel_idx = 0..k-1 and r_global = 1.
+ *
+ *   x, dtype, K, ldx   the activation (bf16/fp32 [x_rows, ldx])
+ *   row_index          NULL or int32 [rows_total]
+ *   codes, scales, g   its NVFP4 quantization (from nvfp4_quantize)
+ *   unit_offsets       int64 [U+1], non-decreasing, unit_offsets[U] == rows_total;
+ *                      may be NULL when tile_partials is given
+ *   tile_partials      NULL, or the partials nvfp4_quantize wrote for x; then
+ *                      the units must be x's 128-row tiles: row_index NULL,
+ *                      rows_total == x_rows, U == ceil(x_rows/128)
+ *   sel_idx out int32 [U, k]; r_codes out [rows_total, k/2];
+ *   r_scales out [rows_total, k/16]; r_global out fp32 [U]
+ * Errors: EINVAL (shapes, k, null pointers, tile-unit mismatch), EWORKSPACE.
+ * ------------------------------------------------------------------------ */
+size_t resq_select_and_requant_workspace_size(int64_t K, int64_t rows_total, int64_t U, int32_t k);
+int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+                            const int32_t* row_index, const uint8_t* codes, const uint8_t* scales,
+                            const float* g, const int64_t* unit_offsets, int64_t U,
+                            int64_t rows_total, int32_t k, const float* tile_partials,
+                            int32_t* sel_idx, uint8_t* r_codes, uint8_t* r_scales,
+                            float* r_global, void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * moe_w4a4_grouped_gemm -- routed grouped expert GEMM over NVFP4 weights and
+ * NVFP4 activations, with the compensation term fused in ([QUADS] sec. 1:
+ * native W4A4 GEMM; sec. 2.2B: the residual correction of the selected
+ * channels is added back into the result).
+ *
+ * Group (expert) e owns unit rows group_offsets[e] .. group_offsets[e+1]-1;
+ * unit row r reads activation row a_row_index[r] (r when NULL).  For every
+ * unit row r of group e and output n < N:
+ *   Y[r, n] = sum_k DQA[r, k] * DQW[e, n, k]
+ *           + sum_j DQR[r, j] * DQW[e, n, sel_idx[e, j]]      (if sel_idx)
+ * where DQW keeps each weight element's own block scale and w_global[e]
+ * (the stored NVFP4 weight restricted to the selected channels).  Products
+ * of dequantized operands are exact; accumulation is fp32.
+ *
+ *   a_codes/a_scales   [a_rows, K/2] / [a_rows, K/16];  a_global fp32 [1]
+ *   group_offsets      int64 [E+1] (device), group_offsets[E] == rows_total
+ *   w_codes/w_scales   [E, N, K/2] / [E, N, K/16];  w_global fp32 [E]
+ *   sel_idx            NULL (no compensation) or int32 [E, kc] ascending
+ *   r_codes/r_scales   [rows_total, kc/2] / [rows_total, kc/16]; r_global fp32 [E]
+ *   epilogue           NVFP4_EPI_*: F32 writes fp32 [rows_total, ldo];
+ *                      SWIGLU_BF16 needs N even, gate = outputs 0..N/2-1,
+ *                      up = N/2..N-1, writes bf16 h [rows_total, ldo] =
+ *                      bf16(silu(gate) * up) and, when out_amax != NULL,
+ *                      stores max |h| (fp32) into *out_amax;
+ *                      SCATTER_ADD_F32 atomically adds row_weight[r] * Y[r]
+ *                      into out row scatter_index[r] (< out_rows) of fp32
+ *                      [out_rows, ldo]; the caller initializes out.
+ * Errors: EINVAL (shapes, pointers, epilogue arguments, kc), EWORKSPACE.
+ * rows_total == 0 is valid (out_amax set to 0, nothing else written).
+ * ------------------------------------------------------------------------ */
+size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K);
+int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                          const int32_t* a_row_index, int64_t a_rows,
+                          const int64_t* group_offsets, int32_t E, int64_t rows_total, int64_t K,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                          int64_t N, const int32_t* sel_idx, const uint8_t* r_codes,
+                          const uint8_t* r_scales, const float* r_global, int32_t kc,
+                          int epilogue, const float* row_weight, const int32_t* scatter_index,
+                          int64_t out_rows, void* out, int64_t ldo, float* out_amax,
+                          void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * qdq_weights -- trainer-side weight quantize-dequantize of the asymmetric
+ * W4A16 QAT ([QUADS] sec. 2.2A: weights are fake-quantized to NVFP4 on the
+ * trainer so that its forward sees the rollout's weights; activations stay
+ * BF16).  Every matrix i of w [nmat, N, K] gets its own global scale;
+ * blocks run along K.  w_qdq = bf16(DQ) with DQ = RNE32(value * S_b).
+ *   w        bf16 [nmat, N, K];  w_qdq out bf16 [nmat, N, K]
+ *   codes    NULL or out [nmat, N, K/2];  scales NULL or out [nmat, N, K/16]
+ *   g        NULL or out fp32 [nmat]
+ * Errors: EINVAL (K % 16, null w / w_qdq, in-place w == w_qdq), EWORKSPACE.
+ * ------------------------------------------------------------------------ */
+size_t qdq_weights_workspace_size(int64_t nmat, int64_t N, int64_t K);
+int qdq_weights(const void* w, int64_t nmat, int64_t N, int64_t K, void* w_qdq,
+                uint8_t* codes, uint8_t* scales, float* g, void* ws, size_t ws_bytes,
+                void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * guided_round -- rollout-guided neighbour-codeword rounding ([TRACE] core
+ * method and method step four).  For each element, with the rollout
+ * block's scale S = RNE32(s_roll * g_roll) and v = x_train / S (exact), the
+ * candidates are the neighbouring signed E2M1 levels q- <= v <= q+ (clamped
+ * to +-6); the output is the one closer to the recorded rollout level,
+ * instead of round-to-nearest.  This never moves farther from the rollout
+ * level than round-to-nearest ([TRACE] Eq. (3)).  A zero result takes
+ * x_train's sign bit; S == 0 gives magnitude 0.
+ *   x_train       bf16/fp32 [M, ldx]
+ *   roll_codes    [M, K/2];  roll_scales [M, K/16];  roll_global fp32 [1]
+ *   guided_codes  out [M, K/2]
+ *   x_fq          NULL or out bf16 [M, K] = bf16(RNE32(value * S))
+ *   dist_hist     NULL or out int64 [3]: numbers of elements whose signed
+ *                 level index under round-to-nearest differs from the
+ *                 rollout's by 0, by 1, and by 2 or more (overwritten)
+ * Errors: EINVAL (shapes, null pointers).
+ * ------------------------------------------------------------------------ */
+int guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                 const uint8_t* roll_codes, const uint8_t* roll_scales,
+                 const float* roll_global, uint8_t* guided_codes, void* x_fq,
+                 int64_t* dist_hist, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_RESQ_H */

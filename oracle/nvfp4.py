@@ -297,8 +297,8 @@ def guided_round(x_train, roll_codes, roll_scales, roll_g):
     never equidistant unless equal.  A zero result takes x_train's sign bit
     (reading).  S == 0 gives magnitude 0.
 
-    Returns (guided codes [M, K/2], x_fq bf16 bits [M, K] of RNE32(value*S)
-    rounded to bf16, dist_hist int64[3] = counts of |signed index of RTN(v)
+    Returns (guided codes [M, K/2], x_fq bf16 bits [M, K]: the guided code's
+    value times S, RNE32 then bf16 (the value of code 0x8 is -0, as in DQ), dist_hist int64[3] = counts of |signed index of RTN(v)
     - signed index of q_roll| equal to 0, 1 and >= 2).
     """
     x = np.asarray(x_train, dtype=np.float32)
@@ -327,7 +327,7 @@ def guided_round(x_train, roll_codes, roll_scales, roll_g):
         mag_idx = np.searchsorted(E2M1_LEVELS, np.abs(q))
         neg = (q < 0) | ((q == 0) & np.signbit(xs))
         nib[r0:r1] = (neg.astype(np.int64) << 3) | mag_idx
-        x_fq[r0:r1] = f32_to_bf16_bits((q * S).astype(np.float32))
+        x_fq[r0:r1] = f32_to_bf16_bits((e2m1_decode(nib[r0:r1]) * S).astype(np.float32))
         # distance between round-to-nearest under the rollout scale and q_roll
         rtn_idx = e2m1_index_nearest(np.abs(xd), S)
         rtn_signed = np.where(np.signbit(xs), -rtn_idx, rtn_idx)

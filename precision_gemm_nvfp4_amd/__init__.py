@@ -1,0 +1,224 @@
+"""Python binding of libnvfp4_resq.so: the MI355X NVFP4 W4A4 MoE expert GEMM
+with residual activation compensation, weight QDQ and rollout-guided
+rounding.
+
+Argument marshalling only: every step runs in the HIP library.  torch
+provides device memory (outputs and workspaces are torch tensors) and the
+stream (torch.cuda.current_stream()).  The functions carry the C ABI's names;
+see include/nvfp4_resq.h for the contract of each.  There is no CPU fallback:
+without the built library every call raises.
+"""
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnvfp4_resq.so")
+
+NVFP4_DTYPE_BF16 = 0
+NVFP4_DTYPE_F32 = 1
+EPI_F32 = 0
+EPI_SWIGLU_BF16 = 1
+EPI_SCATTER_ADD_F32 = 2
+
+_lib = None
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_INT = ctypes.c_int
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "nvfp4_version": (_INT, []),
+    "nvfp4_last_error": (ctypes.c_char_p, []),
+    "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
+    "nvfp4_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "resq_select_and_requant_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
+    "resq_select_and_requant": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64,
+                                       _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_w4a4_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64]),
+    "moe_w4a4_grouped_gemm": (_INT, [_P, _P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _P,
+                                     _I64, _P, _P, _P, _P, _I32, _INT, _P, _P, _I64, _P, _I64,
+                                     _P, _P, _SZ, _P]),
+    "qdq_weights_workspace_size": (_SZ, [_I64, _I64, _I64]),
+    "qdq_weights": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "guided_round": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+}
+
+
+def load():
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run python -m precision_gemm_nvfp4_amd.build")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def exported_symbols():
+    return list(_SIGNATURES)
+
+
+def _check(status, name):
+    if status != 0:
+        msg = load().nvfp4_last_error().decode()
+        raise RuntimeError(f"{name} failed with status {status}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return NVFP4_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return NVFP4_DTYPE_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _workspace(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _require_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+
+
+# ---------------------------------------------------------------------------
+def nvfp4_quantize(x, amax_in=None, tile_partials=False):
+    """NVFP4 quantization of x [M, K] (bf16/fp32, GPU).
+
+    Returns (codes uint8 [M, K/2], scales uint8 [M, K/16], g fp32 [1],
+    tile_partials fp32 [ceil(M/128), K] or None)."""
+    lib = load()
+    _require_cuda(x, amax_in)
+    m, k = x.shape
+    dev = x.device
+    codes = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(m, k // 16, dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    tp = torch.empty((m + 127) // 128, k, dtype=torch.float32, device=dev) if tile_partials else None
+    ws_n = lib.nvfp4_quantize_workspace_size(m, k)
+    ws = _workspace(ws_n, dev)
+    _check(lib.nvfp4_quantize(_ptr(x), _dtype_code(x), m, k, x.stride(0), _ptr(amax_in),
+                              _ptr(codes), _ptr(scales), _ptr(g), _ptr(tp), _ptr(ws), ws.numel(),
+                              _stream()), "nvfp4_quantize")
+    return codes, scales, g, tp
+
+
+def resq_select_and_requant(x, codes, scales, g, k, unit_offsets=None, rows_total=None,
+                            row_index=None, tile_partials=None):
+    """Select the top-k residual channels of each unit and requantize R_S.
+
+    unit_offsets: int64 GPU tensor [U+1] (with rows_total = its last value as
+    a host int), or None with tile_partials from nvfp4_quantize (units = the
+    128-row tiles of x).  Returns (sel_idx int32 [U, k], r_codes [rows, k/2],
+    r_scales [rows, k/16], r_global fp32 [U])."""
+    lib = load()
+    _require_cuda(x, codes, scales, g, unit_offsets, row_index, tile_partials)
+    x_rows, kk = x.shape
+    dev = x.device
+    if tile_partials is not None:
+        n_units = (x_rows + 127) // 128
+        rows_total = x_rows
+    else:
+        n_units = unit_offsets.numel() - 1
+        if rows_total is None:
+            raise ValueError("rows_total (host int) is required with unit_offsets")
+    sel = torch.empty(n_units, k, dtype=torch.int32, device=dev)
+    rc = torch.empty(rows_total, k // 2, dtype=torch.uint8, device=dev)
+    rs = torch.empty(rows_total, k // 16, dtype=torch.uint8, device=dev)
+    rg = torch.empty(n_units, dtype=torch.float32, device=dev)
+    ws = _workspace(lib.resq_select_and_requant_workspace_size(kk, rows_total, n_units, k), dev)
+    _check(lib.resq_select_and_requant(
+        _ptr(x), _dtype_code(x), x_rows, kk, x.stride(0), _ptr(row_index), _ptr(codes),
+        _ptr(scales), _ptr(g), _ptr(unit_offsets), n_units, rows_total, k, _ptr(tile_partials),
+        _ptr(sel), _ptr(rc), _ptr(rs), _ptr(rg), _ptr(ws), ws.numel(), _stream()),
+        "resq_select_and_requant")
+    return sel, rc, rs, rg
+
+
+def moe_w4a4_grouped_gemm(a_codes, a_scales, a_global, group_offsets, rows_total,
+                          w_codes, w_scales, w_global, epilogue=EPI_F32, a_row_index=None,
+                          sel_idx=None, r_codes=None, r_scales=None, r_global=None,
+                          row_weight=None, scatter_index=None, out=None, out_rows=None,
+                          out_amax=None):
+    """Grouped W4A4 GEMM with the fused compensation term.
+
+    w_codes [E, N, K/2].  Returns out: fp32 [rows_total, N] (EPI_F32), bf16
+    [rows_total, N/2] (EPI_SWIGLU_BF16), or the given fp32 out
+    [out_rows, N] after the scatter-add (EPI_SCATTER_ADD_F32)."""
+    lib = load()
+    _require_cuda(a_codes, a_scales, a_global, group_offsets, w_codes, w_scales, w_global,
+                  a_row_index, sel_idx, r_codes, r_scales, r_global, row_weight, scatter_index,
+                  out, out_amax)
+    n_exp, n, k_half = w_codes.shape
+    kk = k_half * 2
+    dev = w_codes.device
+    if out is None:
+        if epilogue == EPI_F32:
+            out = torch.empty(rows_total, n, dtype=torch.float32, device=dev)
+        elif epilogue == EPI_SWIGLU_BF16:
+            out = torch.empty(rows_total, n // 2, dtype=torch.bfloat16, device=dev)
+        else:
+            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor")
+    if out_rows is None:
+        out_rows = out.shape[0]
+    kc = 0 if sel_idx is None else sel_idx.shape[1]
+    ws = _workspace(lib.moe_w4a4_grouped_gemm_workspace_size(n_exp, rows_total, n, kk), dev)
+    a_rows = a_codes.shape[0] if a_codes is not None else 0
+    _check(lib.moe_w4a4_grouped_gemm(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_global), _ptr(a_row_index), a_rows,
+        _ptr(group_offsets), n_exp, rows_total, kk, _ptr(w_codes), _ptr(w_scales),
+        _ptr(w_global), n, _ptr(sel_idx), _ptr(r_codes), _ptr(r_scales), _ptr(r_global), kc,
+        epilogue, _ptr(row_weight), _ptr(scatter_index), out_rows, _ptr(out), out.stride(0),
+        _ptr(out_amax), _ptr(ws), ws.numel(), _stream()), "moe_w4a4_grouped_gemm")
+    return out
+
+
+def qdq_weights(w, want_codes=True):
+    """Weight QDQ of w bf16 [nmat, N, K].  Returns (w_qdq bf16, codes, scales, g)."""
+    lib = load()
+    _require_cuda(w)
+    nmat, n, kk = w.shape
+    dev = w.device
+    w_qdq = torch.empty_like(w)
+    codes = torch.empty(nmat, n, kk // 2, dtype=torch.uint8, device=dev) if want_codes else None
+    scales = torch.empty(nmat, n, kk // 16, dtype=torch.uint8, device=dev) if want_codes else None
+    g = torch.empty(nmat, dtype=torch.float32, device=dev)
+    ws = _workspace(lib.qdq_weights_workspace_size(nmat, n, kk), dev)
+    _check(lib.qdq_weights(_ptr(w), nmat, n, kk, _ptr(w_qdq), _ptr(codes), _ptr(scales), _ptr(g),
+                           _ptr(ws), ws.numel(), _stream()), "qdq_weights")
+    return w_qdq, codes, scales, g
+
+
+def guided_round(x_train, roll_codes, roll_scales, roll_global, want_fq=True, want_hist=True):
+    """Rollout-guided rounding.  Returns (codes [M, K/2], x_fq bf16 or None,
+    dist_hist int64 [3] or None)."""
+    lib = load()
+    _require_cuda(x_train, roll_codes, roll_scales, roll_global)
+    m, kk = x_train.shape
+    dev = x_train.device
+    codes = torch.empty(m, kk // 2, dtype=torch.uint8, device=dev)
+    fq = torch.empty(m, kk, dtype=torch.bfloat16, device=dev) if want_fq else None
+    hist = torch.empty(3, dtype=torch.int64, device=dev) if want_hist else None
+    _check(lib.guided_round(_ptr(x_train), _dtype_code(x_train), m, kk, x_train.stride(0),
+                            _ptr(roll_codes), _ptr(roll_scales), _ptr(roll_global), _ptr(codes),
+                            _ptr(fq), _ptr(hist), _stream()), "guided_round")
+    return codes, fq, hist

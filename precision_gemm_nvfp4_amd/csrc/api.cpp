@@ -1,0 +1,248 @@
+// C ABI of the library: argument validation, workspace carving, launches.
+// Every check runs on the host before anything is enqueued, so a failing call
+// writes nothing.  See include/nvfp4_resq.h for the contract of each entry.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "../../include/nvfp4_resq.h"
+#include "kernels.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_err[0] = '\0';
+  return NVFP4_OK;
+}
+
+int hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(NVFP4_EHIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+int elem_size(int dtype) { return dtype == NVFP4_DTYPE_BF16 ? 2 : 4; }
+
+// Common checks of an activation operand x [M, ldx] with K used columns.
+int check_act(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, const char* fn) {
+  if (dtype != NVFP4_DTYPE_BF16 && dtype != NVFP4_DTYPE_F32)
+    return fail(NVFP4_EUNSUPPORTED, "%s: dtype %d is not BF16 (0) or F32 (1)", fn, dtype);
+  if (M < 0 || K <= 0) return fail(NVFP4_EINVAL, "%s: M=%lld K=%lld", fn, (long long)M, (long long)K);
+  if (K % 16 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+  if (ldx < K) return fail(NVFP4_EINVAL, "%s: ldx=%lld < K=%lld", fn, (long long)ldx, (long long)K);
+  if ((ldx * elem_size(dtype)) % 16 != 0)
+    return fail(NVFP4_EINVAL, "%s: row stride ldx=%lld elements is not a multiple of 16 bytes", fn,
+                (long long)ldx);
+  if (M > 0 && !x) return fail(NVFP4_EINVAL, "%s: x is NULL", fn);
+  if (x && !aligned16(x)) return fail(NVFP4_EINVAL, "%s: x is not 16-byte aligned", fn);
+  return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_version(void) { return 100; }
+
+const char* nvfp4_last_error(void) { return g_err; }
+
+// ---------------------------------------------------------------------------
+size_t nvfp4_quantize_workspace_size(int64_t M, int64_t K) {
+  return align256((size_t)nvfp4::amax_partials_count(M, K) * sizeof(float));
+}
+
+int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* g_out,
+                   float* tile_partials, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "nvfp4_quantize";
+  if (int s = check_act(x, dtype, M, K, ldx, fn)) return s;
+  if (M > 0 && (!codes || !scales)) return fail(NVFP4_EINVAL, "%s: codes/scales are NULL", fn);
+  if (codes && !aligned16(codes)) return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
+  if (tile_partials && !aligned16(tile_partials))
+    return fail(NVFP4_EINVAL, "%s: tile_partials not 16-byte aligned", fn);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    if (g_out) return hip_status(nvfp4::launch_fill_f32(g_out, 1, 1.0f, st), fn);
+    return ok();
+  }
+  if (!amax_in) {
+    if (!ws) return fail(NVFP4_EWORKSPACE, "%s: workspace is NULL", fn);
+    if (ws_bytes < nvfp4_quantize_workspace_size(M, K))
+      return fail(NVFP4_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes,
+                  nvfp4_quantize_workspace_size(M, K));
+  }
+  return hip_status(nvfp4::launch_quantize(x, dtype, M, K, ldx, amax_in, codes, scales, g_out,
+                                           tile_partials, static_cast<float*>(ws), st),
+                    fn);
+}
+
+// ---------------------------------------------------------------------------
+size_t resq_select_and_requant_workspace_size(int64_t K, int64_t rows_total, int64_t U, int32_t k) {
+  const int64_t slots = nvfp4::resq_max_slots(rows_total, U);
+  return align256((size_t)(U + 1) * 4) + align256((size_t)slots * K * 4) +
+         align256((size_t)rows_total * k * 4) + align256((size_t)slots * 4);
+}
+
+int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+                            const int32_t* row_index, const uint8_t* codes, const uint8_t* scales,
+                            const float* g, const int64_t* unit_offsets, int64_t U,
+                            int64_t rows_total, int32_t k, const float* tile_partials,
+                            int32_t* sel_idx, uint8_t* r_codes, uint8_t* r_scales,
+                            float* r_global, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "resq_select_and_requant";
+  if (int s = check_act(x, dtype, x_rows, K, ldx, fn)) return s;
+  if (K > 16384) return fail(NVFP4_EUNSUPPORTED, "%s: K=%lld > 16384", fn, (long long)K);
+  if (k < 16 || k % 16 != 0 || k > K)
+    return fail(NVFP4_EINVAL, "%s: k=%d must be a multiple of 16 in [16, K]", fn, k);
+  if (U < 0 || rows_total < 0) return fail(NVFP4_EINVAL, "%s: U or rows_total negative", fn);
+  if (U > 2147483647LL || rows_total > 2147483647LL)
+    return fail(NVFP4_EUNSUPPORTED, "%s: U or rows_total above 2^31-1", fn);
+  if (!codes || !scales || !g) return fail(NVFP4_EINVAL, "%s: codes/scales/g NULL", fn);
+  if (U > 0 && (!sel_idx || !r_global)) return fail(NVFP4_EINVAL, "%s: sel_idx/r_global NULL", fn);
+  if (rows_total > 0 && (!r_codes || !r_scales))
+    return fail(NVFP4_EINVAL, "%s: r_codes/r_scales NULL", fn);
+  if (r_codes && !aligned16(r_codes)) return fail(NVFP4_EINVAL, "%s: r_codes not aligned", fn);
+  if (tile_partials) {
+    if (row_index) return fail(NVFP4_EINVAL, "%s: tile_partials needs row_index == NULL", fn);
+    if (rows_total != x_rows || U != (x_rows + 127) / 128)
+      return fail(NVFP4_EINVAL, "%s: tile_partials needs rows_total == x_rows and U == ceil(x_rows/128)", fn);
+  } else if (U > 0 && !unit_offsets) {
+    return fail(NVFP4_EINVAL, "%s: unit_offsets NULL", fn);
+  }
+  if (!ws) return fail(NVFP4_EWORKSPACE, "%s: workspace is NULL", fn);
+  const size_t need = resq_select_and_requant_workspace_size(K, rows_total, U, k);
+  if (ws_bytes < need) return fail(NVFP4_EWORKSPACE, "%s: workspace %zu < %zu bytes", fn, ws_bytes, need);
+  if (U == 0) return ok();
+  char* w = static_cast<char*>(ws);
+  const int64_t slots = nvfp4::resq_max_slots(rows_total, U);
+  nvfp4::ResqWorkspace rw;
+  rw.tile_start = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)(U + 1) * 4);
+  rw.partials = reinterpret_cast<float*>(w);
+  w += align256((size_t)slots * K * 4);
+  rw.r_s = reinterpret_cast<float*>(w);
+  w += align256((size_t)rows_total * k * 4);
+  rw.amax_part = reinterpret_cast<float*>(w);
+  return hip_status(nvfp4::launch_resq(x, dtype, x_rows, K, ldx, row_index, codes, scales, g,
+                                       unit_offsets, U, rows_total, k, tile_partials, sel_idx,
+                                       r_codes, r_scales, r_global, rw,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+// ---------------------------------------------------------------------------
+size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K) {
+  (void)E; (void)rows_total; (void)N; (void)K;
+  return 0;
+}
+
+int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
+                          const int32_t* a_row_index, int64_t a_rows,
+                          const int64_t* group_offsets, int32_t E, int64_t rows_total, int64_t K,
+                          const uint8_t* w_codes, const uint8_t* w_scales, const float* w_global,
+                          int64_t N, const int32_t* sel_idx, const uint8_t* r_codes,
+                          const uint8_t* r_scales, const float* r_global, int32_t kc,
+                          int epilogue, const float* row_weight, const int32_t* scatter_index,
+                          int64_t out_rows, void* out, int64_t ldo, float* out_amax,
+                          void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_w4a4_grouped_gemm";
+  (void)ws; (void)ws_bytes;
+  if (E <= 0 || K <= 0 || N <= 0 || rows_total < 0 || a_rows < 0)
+    return fail(NVFP4_EINVAL, "%s: E=%d K=%lld N=%lld rows_total=%lld", fn, E, (long long)K,
+                (long long)N, (long long)rows_total);
+  if (K % 64 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 64", fn, (long long)K);
+  if (rows_total > 2147483647LL) return fail(NVFP4_EUNSUPPORTED, "%s: rows_total above 2^31-1", fn);
+  if (!group_offsets || !w_codes || !w_scales || !w_global || !a_global || !out)
+    return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if (rows_total > 0 && (!a_codes || !a_scales)) return fail(NVFP4_EINVAL, "%s: a_codes/a_scales NULL", fn);
+  if (!aligned16(w_codes) || (a_codes && !aligned16(a_codes)))
+    return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
+  if (sel_idx) {
+    if (kc < 16 || kc % 16 != 0 || kc > K || kc > 256)
+      return fail(NVFP4_EINVAL, "%s: kc=%d must be a multiple of 16 in [16, min(K, 256)]", fn, kc);
+    if (rows_total > 0 && (!r_codes || !r_scales)) return fail(NVFP4_EINVAL, "%s: r_codes/r_scales NULL", fn);
+    if (!r_global) return fail(NVFP4_EINVAL, "%s: r_global NULL", fn);
+  }
+  if (epilogue == NVFP4_EPI_F32) {
+    if (ldo < N) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N", fn, (long long)ldo);
+  } else if (epilogue == NVFP4_EPI_SWIGLU_BF16) {
+    if (N % 2 != 0) return fail(NVFP4_EINVAL, "%s: SwiGLU needs N even", fn);
+    if (ldo < N / 2) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N/2", fn, (long long)ldo);
+  } else if (epilogue == NVFP4_EPI_SCATTER_ADD_F32) {
+    if (ldo < N) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N", fn, (long long)ldo);
+    if (!row_weight || !scatter_index) return fail(NVFP4_EINVAL, "%s: scatter needs row_weight and scatter_index", fn);
+    if (out_rows < 0) return fail(NVFP4_EINVAL, "%s: out_rows negative", fn);
+  } else {
+    return fail(NVFP4_EINVAL, "%s: unknown epilogue %d", fn, epilogue);
+  }
+  nvfp4::GemmArgs a;
+  a.a_codes = a_codes; a.a_scales = a_scales; a.a_global = a_global;
+  a.a_row_index = a_row_index; a.a_rows = a_rows;
+  a.group_offsets = group_offsets; a.E = E; a.rows_total = rows_total; a.K = K;
+  a.w_codes = w_codes; a.w_scales = w_scales; a.w_global = w_global; a.N = N;
+  a.sel_idx = sel_idx; a.r_codes = r_codes; a.r_scales = r_scales; a.r_global = r_global;
+  a.kc = sel_idx ? kc : 0;
+  a.epilogue = epilogue; a.row_weight = row_weight; a.scatter_index = scatter_index;
+  a.out_rows = out_rows; a.out = out; a.ldo = ldo;
+  a.out_amax = epilogue == NVFP4_EPI_SWIGLU_BF16 ? out_amax : nullptr;
+  return hip_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
+size_t qdq_weights_workspace_size(int64_t nmat, int64_t N, int64_t K) {
+  (void)N; (void)K;
+  return align256((size_t)(nmat > 0 ? nmat : 0) * 4);
+}
+
+int qdq_weights(const void* w, int64_t nmat, int64_t N, int64_t K, void* w_qdq, uint8_t* codes,
+                uint8_t* scales, float* g, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "qdq_weights";
+  if (nmat < 0 || N < 0 || K <= 0) return fail(NVFP4_EINVAL, "%s: bad shape", fn);
+  if (K % 16 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld not a multiple of 16", fn, (long long)K);
+  if (nmat > 65535) return fail(NVFP4_EUNSUPPORTED, "%s: nmat > 65535", fn);
+  if (nmat == 0 || N == 0) return ok();
+  if (!w || !w_qdq) return fail(NVFP4_EINVAL, "%s: w / w_qdq NULL", fn);
+  if (w == w_qdq) return fail(NVFP4_EINVAL, "%s: in-place operation is not supported", fn);
+  if (!aligned16(w) || !aligned16(w_qdq) || (codes && !aligned16(codes)))
+    return fail(NVFP4_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  if (!ws || ws_bytes < qdq_weights_workspace_size(nmat, N, K))
+    return fail(NVFP4_EWORKSPACE, "%s: workspace too small", fn);
+  return hip_status(nvfp4::launch_qdq(static_cast<const __bf16*>(w), nmat, N, K,
+                                      static_cast<__bf16*>(w_qdq), codes, scales, g,
+                                      static_cast<float*>(ws), static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+// ---------------------------------------------------------------------------
+int guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                 const uint8_t* roll_codes, const uint8_t* roll_scales, const float* roll_global,
+                 uint8_t* guided_codes, void* x_fq, int64_t* dist_hist, void* stream) {
+  const char* fn = "guided_round";
+  if (int s = check_act(x_train, dtype, M, K, ldx, fn)) return s;
+  if (M > 0 && (!roll_codes || !roll_scales || !roll_global || !guided_codes))
+    return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if ((roll_codes && !aligned16(roll_codes)) || (guided_codes && !aligned16(guided_codes)) ||
+      (x_fq && !aligned16(x_fq)))
+    return fail(NVFP4_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_guided(x_train, dtype, M, K, ldx, roll_codes, roll_scales,
+                                         roll_global, guided_codes, static_cast<__bf16*>(x_fq),
+                                         dist_hist, static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,212 @@
+// Device-side NVFP4 helpers for gfx950: E4M3 scale encode/decode, exact
+// E2M1 rounding, the fast convert-and-verify element quantizer, and wave
+// reductions.
+//
+// Format and rounding rules (one definition for the whole library):
+//   g   = RNE32(amax / 2688), 1 when that is 0;
+//   s_b = E4M3FN value nearest to amax_b / (6 g) (ties to the even byte,
+//         saturating at 448); S_b = RNE32(s_b * g);
+//   element index = E2M1 index nearest to |x| / S_b, ties to the even index,
+//         saturating at 6, 0 when S_b == 0; sign bit = sign bit of x;
+//   DQ  = RNE32(value * S_b).
+// The pages fix the codebook, the round-to-nearest rule under a global and
+// a per-block scale, and the worked example (TRACE summary, "Prerequisites:
+// NVFP4 and the E2M1 codebook" and "Research motivation"); the formulas for
+// the scales and the tie rule are readings of what the pages leave open.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+constexpr int kBlock = 16;                  // elements per block scale
+constexpr float kBlockMax = 2688.0f;        // 6 (E2M1 max) * 448 (E4M3 max)
+constexpr int kScoreTileRows = 128;         // rows per tile of the residual-score sum order
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// ---------------------------------------------------------------------------
+// bf16
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (finite inputs).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// ---------------------------------------------------------------------------
+// global scale
+// ---------------------------------------------------------------------------
+// g = RNE32(amax / 2688): '/' on floats is the correctly rounded division
+// (hipcc's default); a zero quotient gives 1.
+__device__ __forceinline__ float global_scale_from_amax(float amax) {
+  float g = amax / kBlockMax;
+  return g == 0.0f ? 1.0f : g;
+}
+
+// ---------------------------------------------------------------------------
+// E4M3FN block scale
+// ---------------------------------------------------------------------------
+// Value of an E4M3FN byte 0x00..0x7E: subnormal m * 2^-9, normal
+// (1 + m/8) * 2^(e-7) whose fp32 exponent field is e + 120.
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  uint32_t e = (b >> 3) & 15u, m = b & 7u;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120u) << 23) | (m << 20));
+}
+
+// E4M3FN byte nearest to q >= 0 (ties to even, saturating at 448).
+// q is the correctly rounded float64 quotient amax_b / (6 g).  That is as good
+// as the exact quotient: every E4M3 rounding boundary has at most 5
+// significant bits, so "quotient == boundary" means amax_b == boundary * 6g
+// with both sides exact in float64 (<= 31 bits), and a quotient that is not
+// on a boundary lies at least 2^-31 (relative) away from it -- far beyond the
+// 2^-53 of the float64 rounding, which therefore never crosses a boundary.
+__device__ __forceinline__ uint32_t e4m3_nearest(double q) {
+  if (q >= 448.0) return 0x7Eu;
+  // below the smallest normal (2^-6) the spacing is 2^-9; n == 8 is byte 0x08 = 2^-6
+  if (q < 0x1p-6) return (uint32_t)rint(q * 512.0);
+  int e;
+  (void)frexp(q, &e);                        // q = f * 2^e, f in [0.5, 1)
+  int lead = e - 1;                          // q in [2^lead, 2^(lead+1)), lead >= -6
+  uint32_t n = (uint32_t)rint(ldexp(q, 3 - lead));   // exact scaling, RNE: 8..16
+  if (n == 16) { n = 8; ++lead; }
+  uint32_t byte = ((uint32_t)(lead + 7) << 3) | (n - 8);
+  return byte > 0x7Eu ? 0x7Eu : byte;
+}
+
+// Block scale byte and effective fp32 scale S_b for a block amax.
+__device__ __forceinline__ uint32_t block_scale(float amax_b, double six_g, float g, float& S) {
+  uint32_t sb = e4m3_nearest((double)amax_b / six_g);
+  S = e4m3_value(sb) * g;                    // RNE32(s_b * g): one rounding
+  return sb;
+}
+
+// ---------------------------------------------------------------------------
+// E2M1
+// ---------------------------------------------------------------------------
+// Magnitude of E2M1 index i (0..7): 0, 0.5, then (1 + (i&1)/2) * 2^((i>>1)-1),
+// whose fp32 bits are (i + 252) << 22.
+__device__ __forceinline__ float e2m1_mag(uint32_t i) {
+  return i < 2 ? (i ? 0.5f : 0.0f) : __uint_as_float((i + 252u) << 22);
+}
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  return __uint_as_float(__float_as_uint(e2m1_mag(code & 7u)) | ((code & 8u) << 28));
+}
+
+// Exact E2M1 code of x under S: the index counts midpoints m below |x|/S,
+// deciding each by the sign of fma(m, S, -|x|) -- the exact m*S - |x|
+// rounded once, which keeps its sign and is zero only on an exact tie.
+// Midpoint j lies between index j and j+1; on a tie the even index wins,
+// i.e. index j+1 exactly when j is odd.
+__device__ __forceinline__ uint32_t e2m1_code_exact(float x, float S) {
+  uint32_t sign = __float_as_uint(x) >> 31;
+  if (S == 0.0f) return sign << 3;
+  float ax = fabsf(x);
+  const float mid[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+  uint32_t idx = 0;
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    float d = __builtin_fmaf(mid[j], S, -ax);
+    idx += (j & 1) ? (d <= 0.0f) : (d < 0.0f);
+  }
+  return (sign << 3) | idx;
+}
+
+// Fast path for 8 elements sharing a scale.  v = x * (1/S) is within 2^-22
+// (relative) of the exact quotient; the hardware FP4 convert (round to
+// nearest, saturating, sign kept) of v * (1 +- 2^-20) brackets that error
+// band.  When both brackets give the same codes, no rounding boundary lies in
+// the band and those codes are the exact ones; otherwise (a tie, or a value
+// within 2^-20 of a boundary) the caller takes the exact path.
+// Returns the packed codes (element 2j in the low nibble of byte j) in *out.
+__device__ __forceinline__ bool e2m1_pack8_fast(const float* x, float inv, uint32_t* out) {
+  const float up = 1.0f + 0x1p-20f, dn = 1.0f - 0x1p-20f;
+  uint32_t wu = 0, wd = 0;
+  float a[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) a[i] = x[i] * inv;
+#define NVFP4_CVT_PAIR(P)                                                                   \
+  wu = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wu, a[2 * P] * up, a[2 * P + 1] * up, 1.0f, P); \
+  wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, a[2 * P] * dn, a[2 * P + 1] * dn, 1.0f, P);
+  NVFP4_CVT_PAIR(0)
+  NVFP4_CVT_PAIR(1)
+  NVFP4_CVT_PAIR(2)
+  NVFP4_CVT_PAIR(3)
+#undef NVFP4_CVT_PAIR
+  *out = wu;
+  return wu == wd;
+}
+
+__device__ __forceinline__ uint32_t e2m1_pack8_exact(const float* x, float S) {
+  uint32_t w = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) w |= e2m1_code_exact(x[j], S) << (4 * j);
+  return w;
+}
+
+// Quantize one 16-element block held in registers.  Writes the scale byte and
+// two packed code words; returns S_b.
+__device__ __forceinline__ float quantize_block16(const float* v, float g, double six_g,
+                                                  uint32_t* sbyte, uint32_t* w0, uint32_t* w1) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  float S;
+  *sbyte = block_scale(amax, six_g, g, S);
+  // Fast path needs 1/S finite and accurate: S >= 2^-100 (a normal number).
+  bool ok = S >= 0x1p-100f;
+  if (ok) {
+    float inv = __builtin_amdgcn_rcpf(S);    // within 1 ulp
+    ok = e2m1_pack8_fast(v, inv, w0);
+    ok = e2m1_pack8_fast(v + 8, inv, w1) && ok;
+  }
+  if (!ok) {
+    *w0 = e2m1_pack8_exact(v, S);
+    *w1 = e2m1_pack8_exact(v + 8, S);
+  }
+  return S;
+}
+
+// Values of the 8 codes packed in w (element 2j in the low nibble of byte j),
+// by the hardware FP4 -> fp32 convert (exact).
+__device__ __forceinline__ void e2m1_unpack8(uint32_t w, float* f) {
+  f32x2 t;
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); f[0] = t[0]; f[1] = t[1];
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); f[2] = t[0]; f[3] = t[1];
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); f[4] = t[0]; f[5] = t[1];
+  t = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); f[6] = t[0]; f[7] = t[1];
+}
+
+// Dequantized value of 4-bit code c under S: RNE32(value * S).
+__device__ __forceinline__ float dq(uint32_t c, float S) { return e2m1_value(c) * S; }
+
+// ---------------------------------------------------------------------------
+// wave reductions (64 lanes)
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+// Atomic max of a non-negative float stored as fp32 bits (non-negative
+// floats order like their bit patterns).
+__device__ __forceinline__ void atomic_max_nonneg(float* p, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(p), __float_as_uint(v));
+}
+
+}  // namespace nvfp4

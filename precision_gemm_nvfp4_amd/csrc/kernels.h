@@ -1,0 +1,71 @@
+// Internal launchers of the HIP kernels (host side).  The C ABI in api.cpp
+// validates arguments and carves the caller's workspace, then calls these.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// quantize.hip
+int amax_partials_count(int64_t M, int64_t K);
+hipError_t launch_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                           const float* amax_in, uint8_t* codes, uint8_t* scales, float* g_out,
+                           float* tile_partials, float* ws_partials, hipStream_t stream);
+hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
+
+// resq.hip
+struct ResqWorkspace {
+  int32_t* tile_start;   // [U+1]
+  float* partials;       // [max_slots, K] (unused when the caller gives tile partials)
+  float* r_s;            // [rows_total, k]
+  float* amax_part;      // [max_slots]
+};
+int64_t resq_max_slots(int64_t rows_total, int64_t U);
+hipError_t launch_resq(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+                       const int32_t* row_index, const uint8_t* codes, const uint8_t* scales,
+                       const float* g, const int64_t* unit_offsets, int64_t U, int64_t rows_total,
+                       int32_t k, const float* tile_partials, int32_t* sel_idx, uint8_t* r_codes,
+                       uint8_t* r_scales, float* r_global, const ResqWorkspace& ws,
+                       hipStream_t stream);
+
+// gemm.hip
+struct GemmArgs {
+  const uint8_t* a_codes;
+  const uint8_t* a_scales;
+  const float* a_global;
+  const int32_t* a_row_index;
+  int64_t a_rows;
+  const int64_t* group_offsets;
+  int32_t E;
+  int64_t rows_total;
+  int64_t K;
+  const uint8_t* w_codes;
+  const uint8_t* w_scales;
+  const float* w_global;
+  int64_t N;
+  const int32_t* sel_idx;
+  const uint8_t* r_codes;
+  const uint8_t* r_scales;
+  const float* r_global;
+  int32_t kc;
+  int epilogue;
+  const float* row_weight;
+  const int32_t* scatter_index;
+  int64_t out_rows;
+  void* out;
+  int64_t ldo;
+  float* out_amax;
+};
+hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+
+// trainer.hip
+hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
+                      uint8_t* codes, uint8_t* scales, float* g, float* ws_amax,
+                      hipStream_t stream);
+hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                         const uint8_t* roll_codes, const uint8_t* roll_scales,
+                         const float* roll_global, uint8_t* guided, __bf16* x_fq,
+                         int64_t* hist, hipStream_t stream);
+
+}  // namespace nvfp4

@@ -1,0 +1,231 @@
+// Trainer-side elementwise kernels.
+//
+// qdq_weights: the asymmetric W4A16 QAT of the QUADS technical summary
+// (section 2.2A) fake-quantizes weights to NVFP4 on the trainer so its
+// forward pass sees the same discretized weights as the rollout; activations
+// stay BF16.  Per matrix: amax pass (atomic max per workgroup), then one pass
+// that quantizes every 16-block and writes bf16(DQ) (plus, optionally, the
+// codes, scales and global scale).
+//
+// guided_round: the rollout-guided rounding of the TRACE summary ("Core
+// method", method step four).  Under the rollout block's scale S, the trainer
+// value v = x/S has two neighbouring E2M1 levels q- <= v <= q+; instead of
+// round-to-nearest the kernel keeps whichever is closer to the recorded
+// rollout level.  Round-to-nearest is one of the two neighbours, so the
+// kernel computes it (exactly), finds on which side of v it lies with one
+// exact fma, takes the neighbour on the other side, and compares distances
+// to the rollout level.
+#include "device_common.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------------------
+// weight QDQ
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void qdq_amax_kernel(const __bf16* __restrict__ w, int64_t per_mat,
+                                                       float* __restrict__ amax) {
+  const int64_t mat = blockIdx.y;
+  const u32x4* p = reinterpret_cast<const u32x4*>(w + mat * per_mat);
+  const int64_t chunks = per_mat / 8;
+  float m = 0.0f;
+  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
+       c += (int64_t)gridDim.x * blockDim.x) {
+    u32x4 v = p[c];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+  }
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float b = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    atomic_max_nonneg(amax + mat, b);
+  }
+}
+
+__global__ __launch_bounds__(256) void qdq_kernel(const __bf16* __restrict__ w, int64_t N, int64_t K,
+                                                  const float* __restrict__ amax,
+                                                  __bf16* __restrict__ w_qdq, uint8_t* __restrict__ codes,
+                                                  uint8_t* __restrict__ scales, float* __restrict__ g_out) {
+  const int64_t mat = blockIdx.y;
+  const float g = global_scale_from_amax(amax[mat]);
+  const double six_g = 6.0 * (double)g;
+  if (g_out && blockIdx.x == 0 && threadIdx.x == 0) g_out[mat] = g;
+  const int64_t nb = N * (K / kBlock);                  // blocks in this matrix
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (b >= nb) return;
+  const int64_t base = mat * N * K + b * kBlock;        // blocks are contiguous in row-major order
+  const u32x4* src = reinterpret_cast<const u32x4*>(w + base);
+  u32x4 a = src[0], c = src[1];
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(a[i]);
+    v[2 * i + 1] = bf16_hi(a[i]);
+    v[8 + 2 * i] = bf16_lo(c[i]);
+    v[8 + 2 * i + 1] = bf16_hi(c[i]);
+  }
+  uint32_t sb, w0, w1;
+  const float S = quantize_block16(v, g, six_g, &sb, &w0, &w1);
+  u32x4 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t c0 = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 15u;
+    const uint32_t c1 = ((i < 4 ? w0 : w1) >> (8 * (i & 3) + 4)) & 15u;
+    const uint32_t lo = f32_to_bf16_rne(dq(c0, S)), hi = f32_to_bf16_rne(dq(c1, S));
+    const uint32_t word = lo | (hi << 16);
+    if (i < 4) o0[i] = word; else o1[i - 4] = word;
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(w_qdq + base);
+  dst[0] = o0;
+  dst[1] = o1;
+  if (codes) *reinterpret_cast<u32x2*>(codes + base / 2) = u32x2{w0, w1};
+  if (scales) scales[base / kBlock] = (uint8_t)sb;
+}
+
+hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
+                      uint8_t* codes, uint8_t* scales, float* g, float* ws_amax,
+                      hipStream_t stream) {
+  hipError_t err = launch_fill_f32(ws_amax, nmat, 0.0f, stream);
+  if (err != hipSuccess) return err;
+  const int64_t per_mat = N * K;
+  int64_t gx = (per_mat / 8 + 255) / 256;
+  gx = gx > 256 ? 256 : (gx < 1 ? 1 : gx);
+  qdq_amax_kernel<<<dim3((unsigned)gx, (unsigned)nmat), 256, 0, stream>>>(w, per_mat, ws_amax);
+  const int64_t nb = N * (K / kBlock);
+  qdq_kernel<<<dim3((unsigned)((nb + 255) / 256), (unsigned)nmat), 256, 0, stream>>>(
+      w, N, K, ws_amax, w_qdq, codes, scales, g);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// guided rounding
+// ---------------------------------------------------------------------------
+// signed level index -7..7 of a 4-bit code (+0 and -0 are both 0)
+__device__ __forceinline__ int signed_index(uint32_t c) {
+  const int i = (int)(c & 7u);
+  return (c & 8u) ? -i : i;
+}
+__device__ __forceinline__ float level_of(int si) {      // value of signed index
+  const float m = e2m1_mag((uint32_t)(si < 0 ? -si : si));
+  return si < 0 ? -m : m;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void guided_kernel(
+    const T* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const uint8_t* __restrict__ roll_codes,
+    const uint8_t* __restrict__ roll_scales, const float* __restrict__ roll_global,
+    uint8_t* __restrict__ guided, __bf16* __restrict__ x_fq, unsigned long long* __restrict__ hist) {
+  const int64_t nb = K / kBlock;
+  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint32_t h0 = 0, h1 = 0, h2 = 0;
+  if (b < M * nb) {
+    const int64_t r = b / nb, bc = b % nb;
+    float v[16];
+    const T* src = x + r * ldx + bc * kBlock;
+    if constexpr (sizeof(T) == 2) {
+      const u32x4* q = reinterpret_cast<const u32x4*>(src);
+      u32x4 a = q[0], c = q[1];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_lo(a[i]);
+        v[2 * i + 1] = bf16_hi(a[i]);
+        v[8 + 2 * i] = bf16_lo(c[i]);
+        v[8 + 2 * i + 1] = bf16_hi(c[i]);
+      }
+    } else {
+      const f32x4* q = reinterpret_cast<const f32x4*>(src);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        f32x4 a = q[i];
+        v[4 * i] = a[0]; v[4 * i + 1] = a[1]; v[4 * i + 2] = a[2]; v[4 * i + 3] = a[3];
+      }
+    }
+    const float S = e4m3_value(roll_scales[r * nb + bc]) * *roll_global;
+    // round-to-nearest codes under S (fast path, exact fallback)
+    uint32_t w0, w1;
+    bool ok = S >= 0x1p-100f;
+    if (ok) {
+      const float inv = __builtin_amdgcn_rcpf(S);
+      ok = e2m1_pack8_fast(v, inv, &w0);
+      ok = e2m1_pack8_fast(v + 8, inv, &w1) && ok;
+    }
+    if (!ok) {
+      w0 = e2m1_pack8_exact(v, S);
+      w1 = e2m1_pack8_exact(v + 8, S);
+    }
+    const u32x2 rw = *reinterpret_cast<const u32x2*>(roll_codes + r * (K / 2) + bc * 8);
+    uint32_t g0 = 0, g1 = 0;
+    uint32_t fq[8];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t c = ((j < 8 ? w0 : w1) >> (4 * (j & 7))) & 15u;
+      const uint32_t cr = (rw[j >> 3] >> (4 * (j & 7))) & 15u;
+      const int s_rtn = signed_index(c), s_roll = signed_index(cr);
+      const int dist = s_rtn > s_roll ? s_rtn - s_roll : s_roll - s_rtn;
+      h0 += dist == 0;
+      h1 += dist == 1;
+      h2 += dist >= 2;
+      int s_pick = s_rtn;
+      if (S != 0.0f) {
+        const float L = level_of(s_rtn);
+        const float d = __builtin_fmaf(L, S, -v[j]);    // sign of L*S - x, exact
+        int s_other = d < 0.0f ? s_rtn + 1 : (d > 0.0f ? s_rtn - 1 : s_rtn);
+        s_other = s_other > 7 ? 7 : (s_other < -7 ? -7 : s_other);
+        const float q_roll = level_of(s_roll);
+        if (fabsf(level_of(s_other) - q_roll) < fabsf(L - q_roll)) s_pick = s_other;
+      }
+      uint32_t code = (uint32_t)(s_pick < 0 ? -s_pick : s_pick);
+      if (s_pick < 0 || (s_pick == 0 && (__float_as_uint(v[j]) >> 31))) code |= 8u;
+      if (j < 8) g0 |= code << (4 * j); else g1 |= code << (4 * (j - 8));
+      if (x_fq) {
+        const uint32_t hb = f32_to_bf16_rne(dq(code, S));
+        if (j & 1) fq[j >> 1] |= hb << 16; else fq[j >> 1] = hb;
+      }
+    }
+    *reinterpret_cast<u32x2*>(guided + r * (K / 2) + bc * 8) = u32x2{g0, g1};
+    if (x_fq) {
+      u32x4* dst = reinterpret_cast<u32x4*>(x_fq + r * K + bc * kBlock);
+      dst[0] = u32x4{fq[0], fq[1], fq[2], fq[3]};
+      dst[1] = u32x4{fq[4], fq[5], fq[6], fq[7]};
+    }
+  }
+  if (hist) {
+    h0 = wave_sum_u32(h0);
+    h1 = wave_sum_u32(h1);
+    h2 = wave_sum_u32(h2);
+    if ((threadIdx.x & 63) == 0) {
+      if (h0) atomicAdd(hist + 0, (unsigned long long)h0);
+      if (h1) atomicAdd(hist + 1, (unsigned long long)h1);
+      if (h2) atomicAdd(hist + 2, (unsigned long long)h2);
+    }
+  }
+}
+
+__global__ void zero_i64_kernel(unsigned long long* p, int n) {
+  if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
+}
+
+hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                         const uint8_t* roll_codes, const uint8_t* roll_scales,
+                         const float* roll_global, uint8_t* guided, __bf16* x_fq,
+                         int64_t* hist, hipStream_t stream) {
+  unsigned long long* h = reinterpret_cast<unsigned long long*>(hist);
+  if (h) zero_i64_kernel<<<1, 64, 0, stream>>>(h, 3);
+  const int64_t nb = M * (K / kBlock);
+  if (nb == 0) return hipGetLastError();
+  const unsigned grid = (unsigned)((nb + 255) / 256);
+  if (dtype == 0)
+    guided_kernel<__bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16*>(x), M, K, ldx,
+                                                    roll_codes, roll_scales, roll_global, guided,
+                                                    x_fq, h);
+  else
+    guided_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), M, K, ldx,
+                                                   roll_codes, roll_scales, roll_global, guided,
+                                                   x_fq, h);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4

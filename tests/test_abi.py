@@ -1,0 +1,116 @@
+"""The C-ABI library: it loads, exports every symbol the header declares, and
+rejects invalid arguments on the host before touching a GPU (these calls
+never reach a launch, so they run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import precision_gemm_nvfp4_amd as P
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4_resq.h")
+
+FAKE = ctypes.c_void_p(0x1000)          # aligned, never dereferenced: validation fails first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_0-9]+)\s*\(", text)) - {"defined"})
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(P.LIB_PATH):
+        pytest.skip("library not built")
+    return P.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert len(declared) == 11      # 5 operations, 4 workspace queries, version, last error
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(P.exported_symbols()) == declared
+    assert lib.nvfp4_version() >= 100
+
+
+def test_workspace_sizes(lib):
+    assert lib.nvfp4_quantize_workspace_size(16384, 4096) >= 1024 * 4
+    n = lib.resq_select_and_requant_workspace_size(2048, 131072, 128, 64)
+    assert n >= (131072 // 128 + 128) * 2048 * 4 + 131072 * 64 * 4
+    assert lib.qdq_weights_workspace_size(512, 3072, 4096) >= 512 * 4
+
+
+def err(lib):
+    return lib.nvfp4_last_error().decode()
+
+
+def test_quantize_validation(lib):
+    assert lib.nvfp4_quantize(None, 0, 4, 32, 32, None, FAKE, FAKE, None, None, FAKE, 4096, None) == -1
+    assert "x is NULL" in err(lib)
+    assert lib.nvfp4_quantize(FAKE, 0, 4, 30, 32, None, FAKE, FAKE, None, None, FAKE, 4096, None) == -1
+    assert "multiple of 16" in err(lib)
+    assert lib.nvfp4_quantize(FAKE, 0, 4, 32, 20, None, FAKE, FAKE, None, None, FAKE, 4096, None) == -1
+    assert lib.nvfp4_quantize(FAKE, 7, 4, 32, 32, None, FAKE, FAKE, None, None, FAKE, 4096, None) == -2
+    assert lib.nvfp4_quantize(FAKE, 0, 4, 32, 36, None, FAKE, FAKE, None, None, FAKE, 4096, None) == -1
+    assert "16 bytes" in err(lib)
+    assert lib.nvfp4_quantize(FAKE, 0, 4, 32, 32, None, FAKE, FAKE, None, None, None, 0, None) == -3
+    assert lib.nvfp4_quantize(ctypes.c_void_p(0x1004), 0, 4, 32, 32, None, FAKE, FAKE, None, None,
+                              FAKE, 4096, None) == -1
+    assert "aligned" in err(lib)
+
+
+def test_resq_validation(lib):
+    f = lib.resq_select_and_requant
+    base = dict(x=FAKE, dtype=0, x_rows=256, K=512, ldx=512, row_index=None, codes=FAKE, scales=FAKE,
+                g=FAKE, unit_offsets=FAKE, U=2, rows_total=256, k=64, tile_partials=None,
+                sel=FAKE, rc=FAKE, rs=FAKE, rg=FAKE, ws=FAKE, ws_bytes=1 << 30, stream=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+
+    assert call(k=24) == -1 and "k=24" in err(lib)
+    assert call(k=1024) == -1
+    assert call(K=32768, ldx=32768) == -2
+    assert call(unit_offsets=None) == -1
+    assert call(tile_partials=FAKE, row_index=FAKE) == -1
+    assert call(tile_partials=FAKE, U=3) == -1
+    assert call(ws_bytes=16) == -3
+    assert call(ws=None) == -3
+
+
+def test_gemm_validation(lib):
+    f = lib.moe_w4a4_grouped_gemm
+    base = dict(ac=FAKE, as_=FAKE, ag=FAKE, ari=None, a_rows=128, go=FAKE, E=4, rows=128, K=512,
+                wc=FAKE, ws_=FAKE, wg=FAKE, N=256, sel=None, rc=None, rs=None, rg=None, kc=0,
+                epi=0, rw=None, si=None, out_rows=0, out=FAKE, ldo=256, amax=None, ws=None,
+                ws_bytes=0, stream=None)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return f(*a.values())
+
+    assert call(K=520) == -1 and "multiple of 64" in err(lib)
+    assert call(sel=FAKE, kc=24, rc=FAKE, rs=FAKE, rg=FAKE) == -1
+    assert call(sel=FAKE, kc=64, rg=None, rc=FAKE, rs=FAKE) == -1
+    assert call(epi=1, N=255) == -1
+    assert call(epi=2) == -1 and "scatter" in err(lib)
+    assert call(epi=9) == -1
+    assert call(ldo=100) == -1
+    assert call(out=None) == -1
+    assert call(E=0) == -1
+
+
+def test_qdq_and_guided_validation(lib):
+    assert lib.qdq_weights(FAKE, 2, 16, 40, FAKE, None, None, None, FAKE, 4096, None) == -1
+    assert lib.qdq_weights(FAKE, 2, 16, 32, FAKE, None, None, None, FAKE, 4096, None) == -1
+    assert "in-place" in err(lib)
+    assert lib.qdq_weights(FAKE, 2, 16, 32, ctypes.c_void_p(0x2000), None, None, None, None, 0,
+                           None) == -3
+    assert lib.guided_round(FAKE, 0, 4, 32, 32, None, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert lib.guided_round(FAKE, 0, 4, 24, 24, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1

@@ -1,0 +1,295 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on
+identical seeded inputs.
+
+Bar: codes, scales, global scales, selected channels, requantized residuals,
+QDQ output and guided codes bit-exact; GEMM outputs within
+max|Y_gpu - Y_ref| / max|Y_ref| <= 1e-3 per output tensor (per expert for
+grouped GEMMs) against the float64 reference on the same quantized operands.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import gemm as OG
+from oracle import nvfp4 as OQ
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 1e-3
+
+
+def np32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def npu8(t):
+    return t.detach().cpu().numpy()
+
+
+def rel_err(y, ref):
+    den = np.abs(ref).max()
+    return float(np.abs(y - ref).max() / (den if den > 0 else 1.0))
+
+
+# ---------------------------------------------------------------------------
+# quantize
+# ---------------------------------------------------------------------------
+
+def test_quantize_exhaustive_bf16_many_scales(gpu_lib):
+    """Every finite bf16 value, under global scales forced through amax_in."""
+    P = gpu_lib
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = F.bf16_bits_to_f32(bits)
+    vals = vals[np.isfinite(vals)]
+    vals = np.concatenate([vals, np.zeros((-vals.size) % 128, np.float32)])
+    rng = np.random.default_rng(0)
+    x_np = vals[rng.permutation(vals.size)].reshape(-1, 16 * 8)   # blocks mix magnitudes
+    x = torch.from_numpy(x_np).to(torch.bfloat16).cuda()
+    for amax in [np.float32(2688.0), np.float32(1.0), np.float32(3.0e38), np.float32(7.5e-3),
+                 np.float32(1e-30), np.float32(123.456)]:
+        amax_t = torch.tensor([amax], device="cuda")
+        codes, scales, g, _ = P.nvfp4_quantize(x, amax_in=amax_t)
+        g_ref = OQ.global_scale(amax)
+        c_ref, s_ref, _ = OQ.quantize(x_np, g=g_ref)
+        assert np32(g)[0] == g_ref
+        assert np.array_equal(npu8(scales), s_ref), f"scales differ at amax={amax}"
+        assert np.array_equal(npu8(codes), c_ref), f"codes differ at amax={amax}"
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("m,k", [(128, 512), (300, 4096), (1, 16), (7, 48)])
+def test_quantize_random_with_tile_partials(gpu_lib, dtype, m, k):
+    P = gpu_lib
+    x = synth.activations(m, k, seed=5, heavy_frac=0.01).to(dtype)
+    if dtype == torch.float32:
+        x = x + torch.randn(x.shape, generator=torch.Generator().manual_seed(1)) * 1e-3
+    x_np = x.float().numpy()
+    codes, scales, g, tp = P.nvfp4_quantize(x.cuda(), tile_partials=True)
+    c_ref, s_ref, g_ref = OQ.quantize(x_np)
+    assert np32(g)[0] == g_ref
+    assert np.array_equal(npu8(scales), s_ref)
+    assert np.array_equal(npu8(codes), c_ref)
+    r = np.abs(OQ.residual(x_np, c_ref, s_ref, g_ref))
+    tp_ref = np.stack([OQ.channel_scores(r[t:t + 128]) for t in range(0, m, 128)])
+    assert np.array_equal(np32(tp), tp_ref)
+
+
+def test_quantize_zero_and_ragged_stride(gpu_lib):
+    P = gpu_lib
+    z = torch.zeros(5, 32, dtype=torch.bfloat16, device="cuda")
+    z[1] = -0.0
+    codes, scales, g, _ = P.nvfp4_quantize(z)
+    assert np32(g)[0] == 1.0 and int(scales.sum()) == 0
+    nib = OQ.unpack_nibbles(npu8(codes))
+    assert np.all(nib[0] == 0) and np.all(nib[1] == 8)
+    # a strided view (row stride 96 elements, K = 64)
+    base = synth.activations(40, 96, seed=6).cuda()
+    view = base[:, :64]
+    codes, scales, g, _ = P.nvfp4_quantize(view)
+    c_ref, s_ref, g_ref = OQ.quantize(view.float().cpu().numpy())
+    assert np.array_equal(npu8(codes), c_ref) and np.array_equal(npu8(scales), s_ref)
+
+
+def test_quantize_worked_example(gpu_lib):
+    """TRACE research motivation: 60.25 (train) and 59.75 (rollout) in bf16
+    under scale 24 round to 3 and 2."""
+    P = gpu_lib
+    x = torch.zeros(2, 32, dtype=torch.bfloat16)
+    x[:, 16] = 2688.0
+    x[:, 0] = 144.0
+    x[0, 1] = 60.25
+    x[1, 1] = 59.75
+    codes, scales, g, _ = P.nvfp4_quantize(x.cuda())
+    nib = OQ.unpack_nibbles(npu8(codes))
+    assert np32(g)[0] == 1.0 and npu8(scales)[0, 0] == 0x5C
+    assert nib[0, 1] == 5 and nib[1, 1] == 4
+
+
+# ---------------------------------------------------------------------------
+# residual selection and requantization
+# ---------------------------------------------------------------------------
+
+def test_resq_tile_units(gpu_lib):
+    P = gpu_lib
+    m, k_dim, k = 300, 1024, 128
+    x = synth.activations(m, k_dim, seed=7, heavy_frac=0.01)
+    xc = x.cuda()
+    codes, scales, g, tp = P.nvfp4_quantize(xc, tile_partials=True)
+    sel, rc, rs, rg = P.resq_select_and_requant(xc, codes, scales, g, k, tile_partials=tp)
+    x_np = x.float().numpy()
+    c_ref, s_ref, g_ref = OQ.quantize(x_np)
+    offs = list(range(0, m, 128)) + [m]
+    sel_r, rc_r, rs_r, rg_r = OQ.resq_select_and_requant(x_np, c_ref, s_ref, g_ref, offs, k)
+    assert np.array_equal(npu8(sel), sel_r)
+    assert np.array_equal(np32(rg), rg_r)
+    assert np.array_equal(npu8(rs), rs_r)
+    assert np.array_equal(npu8(rc), rc_r)
+
+
+@pytest.mark.parametrize("k", [16, 64])
+def test_resq_gathered_expert_units(gpu_lib, k):
+    """Units = experts' routed tokens (gather through the slot->token map),
+    with skewed loads, an empty expert and units longer than one 128-row tile."""
+    P = gpu_lib
+    tokens, hidden, n_exp = 400, 256, 6
+    x = synth.activations(tokens, hidden, seed=8, heavy_frac=0.02)
+    rt = synth.route(tokens, n_exp, seed=8, top_k=2, zipf_s=1.5)
+    offs = rt["offsets"].copy()
+    # make expert 3 empty by moving its slots to expert 4 (offsets stay sorted)
+    offs[4] = offs[3]
+    xc = x.cuda()
+    codes, scales, g, _ = P.nvfp4_quantize(xc)
+    sel, rc, rs, rg = P.resq_select_and_requant(
+        xc, codes, scales, g, k, unit_offsets=torch.from_numpy(offs).cuda(),
+        rows_total=int(offs[-1]), row_index=torch.from_numpy(rt["slot_token"]).cuda())
+    x_np = x.float().numpy()
+    c_ref, s_ref, g_ref = OQ.quantize(x_np)
+    sel_r, rc_r, rs_r, rg_r = OQ.resq_select_and_requant(x_np, c_ref, s_ref, g_ref, offs, k,
+                                                         row_index=rt["slot_token"])
+    assert np.diff(offs).max() > 128
+    assert np.array_equal(npu8(sel), sel_r)
+    assert np.array_equal(np32(rg), rg_r)
+    assert np.array_equal(npu8(rs), rs_r)
+    assert np.array_equal(npu8(rc), rc_r)
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def _quant_weights(P, w):
+    _, c, s, g = P.qdq_weights(w.cuda())
+    return c, s, g
+
+
+def test_dense_linear_compensated(gpu_lib):
+    """Single dense linear 128 x 512 -> 1024 with top-32 compensation over
+    all 128 tokens (E = 1)."""
+    P = gpu_lib
+    wl = synth.WORKLOADS["dense_T128_K512_N1024_k32"]
+    x = synth.activations(wl.tokens, wl.hidden, seed=wl.seed, outlier_channels=wl.outliers)
+    w = synth.weights(1, wl.n_out, wl.hidden, seed=wl.seed, tensor_id=synth.WDENSE_ID)
+    xc = x.cuda()
+    codes, scales, g, _ = P.nvfp4_quantize(xc)
+    offs = torch.tensor([0, wl.tokens], dtype=torch.int64, device="cuda")
+    sel, rc, rs, rg = P.resq_select_and_requant(xc, codes, scales, g, wl.k, unit_offsets=offs,
+                                                rows_total=wl.tokens)
+    wc, ws_, wg = _quant_weights(P, w)
+    y = P.moe_w4a4_grouped_gemm(codes, scales, g, offs, wl.tokens, wc, ws_, wg,
+                                sel_idx=sel, r_codes=rc, r_scales=rs, r_global=rg)
+    y0 = P.moe_w4a4_grouped_gemm(codes, scales, g, offs, wl.tokens, wc, ws_, wg)
+    ref = OG.gemm_comp(npu8(codes), npu8(scales), np32(g)[0], npu8(wc)[0], npu8(ws_)[0],
+                       np32(wg)[0], npu8(sel)[0], npu8(rc), npu8(rs), np32(rg)[0])
+    ref0 = OG.gemm_comp(npu8(codes), npu8(scales), np32(g)[0], npu8(wc)[0], npu8(ws_)[0],
+                        np32(wg)[0])
+    assert rel_err(np32(y), ref) <= GEMM_TOL
+    assert rel_err(np32(y0), ref0) <= GEMM_TOL
+    # compensation moves the result toward the unquantized product
+    exact = x.float().numpy().astype(np.float64) @ OQ.dequantize(
+        npu8(wc)[0], npu8(ws_)[0], np32(wg)[0]).astype(np.float64).T
+    assert np.linalg.norm(np32(y) - exact) < np.linalg.norm(np32(y0) - exact)
+
+
+def _moe_setup(P, tokens, hidden, n_exp, inter, k, seed, zipf=0.0, top_k=8, empty_expert=None):
+    x = synth.activations(tokens, hidden, seed=seed, heavy_frac=0.01)
+    rt = synth.route(tokens, n_exp, seed=seed, top_k=top_k, zipf_s=zipf)
+    offs = rt["offsets"].copy()
+    if empty_expert is not None:
+        offs[empty_expert + 1] = offs[empty_expert]
+    wgu = synth.weights(n_exp, 2 * inter, hidden, seed=seed, tensor_id=synth.WGU_ID)
+    wd = synth.weights(n_exp, hidden, inter, seed=seed, tensor_id=synth.WD_ID)
+    return x, rt, offs, wgu, wd
+
+
+@pytest.mark.parametrize("comp", [True, False])
+def test_grouped_gemm_swiglu_and_scatter(gpu_lib, comp):
+    P = gpu_lib
+    tokens, hidden, n_exp, inter, k = 200, 256, 8, 192, 32
+    x, rt, offs, wgu, wd = _moe_setup(P, tokens, hidden, n_exp, inter, k, seed=9, zipf=1.2,
+                                      top_k=4, empty_expert=5)
+    xc = x.cuda()
+    rows = int(offs[-1])
+    offs_t = torch.from_numpy(offs).cuda()
+    slot_tok = torch.from_numpy(rt["slot_token"]).cuda()
+    codes, scales, g, _ = P.nvfp4_quantize(xc)
+    comp1 = {}
+    if comp:
+        sel, rc, rs, rg = P.resq_select_and_requant(xc, codes, scales, g, k, unit_offsets=offs_t,
+                                                    rows_total=rows, row_index=slot_tok)
+        comp1 = dict(sel_idx=sel, r_codes=rc, r_scales=rs, r_global=rg)
+    gc, gs, gg = _quant_weights(P, wgu)
+    # F32 epilogue of gate/up (reference GEMM check per expert)
+    gu = P.moe_w4a4_grouped_gemm(codes, scales, g, offs_t, rows, gc, gs, gg, a_row_index=slot_tok,
+                                 **comp1)
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    h = P.moe_w4a4_grouped_gemm(codes, scales, g, offs_t, rows, gc, gs, gg, a_row_index=slot_tok,
+                                epilogue=P.EPI_SWIGLU_BF16, out_amax=amax, **comp1)
+    comp_ref = {}
+    if comp:
+        comp_ref = dict(sel_idx=npu8(sel), r_codes=npu8(rc), r_scales=npu8(rs), r_g=np32(rg))
+    gu_ref, h_ref = OG.moe_gate_up(npu8(codes), npu8(scales), np32(g)[0], rt["slot_token"], offs,
+                                   npu8(gc), npu8(gs), np32(gg), inter, **comp_ref)
+    gu_np = np32(gu)
+    for e in range(n_exp):
+        a, b = offs[e], offs[e + 1]
+        if a < b:
+            assert rel_err(gu_np[a:b], gu_ref[a:b]) <= GEMM_TOL, f"expert {e}"
+    # h: bf16 of silu(G)*U -- within one bf16 ulp plus the GEMM tolerance
+    h_np = np32(h)
+    h_r = F.bf16_bits_to_f32(h_ref)
+    tol = np.abs(h_r) * 2.0 ** -7 + GEMM_TOL * np.abs(h_r).max()
+    assert np.all(np.abs(h_np - h_r) <= tol)
+    assert np32(amax)[0] == np.abs(h_np).max()
+    # down projection with scatter-add, on the GPU's own h
+    hq_c, hq_s, hq_g, _ = P.nvfp4_quantize(h, amax_in=amax)
+    hc_r, hs_r, hg_r = OQ.quantize(h_np)
+    assert np.array_equal(npu8(hq_c), hc_r) and np.array_equal(npu8(hq_s), hs_r)
+    comp2, comp2_ref = {}, {}
+    if comp:
+        sel2, rc2, rs2, rg2 = P.resq_select_and_requant(h, hq_c, hq_s, hq_g, k, unit_offsets=offs_t,
+                                                        rows_total=rows)
+        s2r = OQ.resq_select_and_requant(h_np, hc_r, hs_r, hg_r, offs, k)
+        assert np.array_equal(npu8(sel2), s2r[0]) and np.array_equal(npu8(rc2), s2r[1])
+        assert np.array_equal(npu8(rs2), s2r[2]) and np.array_equal(np32(rg2), s2r[3])
+        comp2 = dict(sel_idx=sel2, r_codes=rc2, r_scales=rs2, r_global=rg2)
+        comp2_ref = dict(sel_idx=s2r[0], r_codes=s2r[1], r_scales=s2r[2], r_g=s2r[3])
+    dc, ds, dg = _quant_weights(P, wd)
+    y = torch.zeros(tokens, hidden, dtype=torch.float32, device="cuda")
+    P.moe_w4a4_grouped_gemm(hq_c, hq_s, hq_g, offs_t, rows, dc, ds, dg,
+                            epilogue=P.EPI_SCATTER_ADD_F32,
+                            row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
+                            scatter_index=slot_tok, out=y, **comp2)
+    y_ref = OG.moe_down(hc_r, hs_r, hg_r, offs, npu8(dc), npu8(ds), np32(dg), rt["slot_token"],
+                        rt["slot_weight"], tokens, **comp2_ref)
+    assert rel_err(np32(y), y_ref) <= GEMM_TOL
+
+
+# ---------------------------------------------------------------------------
+# trainer side
+# ---------------------------------------------------------------------------
+
+def test_qdq_weights(gpu_lib):
+    P = gpu_lib
+    w = synth.weights(3, 96, 256, seed=10, tensor_id=synth.WGU_ID)
+    w[1, 5, 7] = 3.0                      # one outlier per matrix changes g
+    wq, c, s, g = P.qdq_weights(w.cuda())
+    wq_r, c_r, s_r, g_r = OQ.qdq_weights(w.float().numpy())
+    assert np.array_equal(np32(g), g_r)
+    assert np.array_equal(npu8(c), c_r) and np.array_equal(npu8(s), s_r)
+    assert np.array_equal(wq.cpu().view(torch.int16).numpy().view(np.uint16), wq_r)
+
+
+@pytest.mark.parametrize("rel", [1e-3, 8e-3, 0.2])
+def test_guided_round(gpu_lib, rel):
+    P = gpu_lib
+    x_roll = synth.activations(257, 512, seed=11, heavy_frac=0.01)
+    x_train = synth.guided_noise(x_roll, seed=11, rel=rel)
+    rc, rs, rg, _ = P.nvfp4_quantize(x_roll.cuda())
+    gc, fq, hist = P.guided_round(x_train.cuda(), rc, rs, rg)
+    gc_r, fq_r, hist_r = OQ.guided_round(x_train.float().numpy(), npu8(rc), npu8(rs), np32(rg)[0])
+    assert np.array_equal(npu8(gc), gc_r)
+    assert np.array_equal(fq.cpu().view(torch.int16).numpy().view(np.uint16), fq_r)
+    assert np.array_equal(hist.cpu().numpy(), hist_r)
