@@ -169,12 +169,12 @@ def cpu_baseline(wl, inp, budget_s):
     flops = 0.0
     done = 0
     t0 = time.time()
+    xc, xsc, xg = OQ.quantize(xs)
     for e in range(wl.experts):
         a, b = int(offs[e]), int(offs[e + 1])
         if b == a:
             continue
         rows_x = xs[tok[a:b]]
-        xc, xsc, xg = OQ.quantize(xs)
         sel, rc, rs, rg = OQ.resq_select_and_requant(xs, xc, xsc, xg, [0, b - a], wl.k, row_index=tok[a:b])
         wgu = inp["wgu"][e:e + 1].float().cpu().numpy()
         _, gc, gs, gg = OQ.qdq_weights(wgu)
@@ -186,10 +186,77 @@ def cpu_baseline(wl, inp, budget_s):
             break
     dt = time.time() - t0
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"{done} expert(s) of the gate/up projection ({wl.hidden}->{2 * wl.inter}, "
-                       f"k={wl.k}), each with NVFP4 quantization of X, residual selection, weight "
-                       f"quantization and the fp64 compensated GEMM; {dt:.1f} s",
+                sample=f"NVFP4 quantization of X, then {done} expert(s) of the gate/up projection "
+                       f"({wl.hidden}->{2 * wl.inter}, k={wl.k}) in expert order, each with residual "
+                       f"selection, weight quantization and the fp64 compensated GEMM; {dt:.1f} s",
                 seconds=round(dt, 2))
+
+
+def quant_select_bench(args, torch, P, synth, wl, dev):
+    """Quantizer + residual select only (bandwidth-bound): per step,
+    nvfp4_quantize with fused 128-row tile scores, then resq_select_and_requant
+    over the 128-token tiles.  value = algorithmic GB/s."""
+    x = synth.activations(wl.tokens, wl.hidden, seed=wl.seed, device=dev.type,
+                          heavy_frac=wl.heavy_frac)
+    torch.cuda.synchronize()
+
+    def step(tl):
+        tl.mark("start")
+        c, s, g, tp = P.nvfp4_quantize(x, tile_partials=True)
+        tl.mark("quantize")
+        out = P.resq_select_and_requant(x, c, s, g, wl.k, tile_partials=tp)
+        tl.mark("resq")
+        return out
+
+    for _ in range(args.warmup):
+        step(Timeline(torch))
+    torch.cuda.synchronize()
+    tls = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        tl = Timeline(torch)
+        step(tl)
+        tls.append(tl)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    T, K, k = wl.tokens, wl.hidden, wl.k
+    tiles = (T + 127) // 128
+    nv = lambda n: n * (0.5 + 1 / 16)
+    b_quant = T * K * 2 + nv(T * K)
+    b_resq = tiles * k * 4 + nv(T * k) + tiles * 4
+    parts_ms = {}
+    for tl in tls:
+        for name, v in tl.durations().items():
+            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
+    parts = {n: dict(ms=round(v, 4)) for n, v in parts_ms.items()}
+    parts["quantize"]["gbs"] = round(b_quant / (parts_ms["quantize"] * 1e-3) / 1e9, 1)
+    total_bytes = b_quant + b_resq
+    value = total_bytes / (ms * 1e-3) / 1e9
+    ach = b_quant / (parts_ms["quantize"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import nvfp4 as OQ
+        rows = 1024
+        xs = x[:rows].float().cpu().numpy()
+        t0 = time.time()
+        c, sc, g = OQ.quantize(xs)
+        OQ.resq_select_and_requant(xs, c, sc, g, list(range(0, rows, 128)) + [rows], k)
+        dt = time.time() - t0
+        cpu = dict(value=round(rows * K * (2 + 0.5625) / dt / 1e9, 4), unit="GB/s", cores=1,
+                   kind="oracle", sample=f"first {rows} of {T} rows (8 tiles): quantize + select + "
+                                         f"requant, {dt:.1f} s")
+    return dict(
+        metric="compensated W4A4 MoE GEMM TFLOPS (% FP4 peak); quantizer GB/s (% HBM)",
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 4),
+        config={"workload": wl.name, "tokens": T, "hidden": K, "k_comp": k,
+                "units": "128-token tiles", "parallelism": "single GPU"},
+        algorithmic_bytes=int(total_bytes), parts=parts,
+        roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                      kernel="amax_partials_kernel + quantize_kernel<SCORES>"),
+        frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
 
 
 def main():
@@ -208,7 +275,17 @@ def main():
     P.load()
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
-    assert wl.kind == "moe", "bench.py runs MoE workloads"
+    if wl.kind == "quant_select":
+        res = quant_select_bench(args, torch, P, synth, wl, dev)
+        line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
+                "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
+                "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, nvfp4 out",
+                "data": "synthetic (seeded; N(0,1) with 1% Student-t(3) x8 channels)"}
+        line.update(res)
+        print(json.dumps(line))
+        return
+    assert wl.kind == "moe", "bench.py runs MoE and quantizer workloads"
     print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
     inp, gen_s = build_inputs(torch, P, synth, wl, dev)
     print(f"[bench] inputs ready in {gen_s:.1f}s; rows={inp['rows']}; warmup {args.warmup}",

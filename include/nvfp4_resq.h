@@ -166,23 +166,30 @@ int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K,
  * (the stored NVFP4 weight restricted to the selected channels).  Products
  * of dequantized operands are exact; accumulation is fp32.
  *
- *   a_codes/a_scales   [a_rows, K/2] / [a_rows, K/16];  a_global fp32 [1]
+ *   a_codes/a_scales   [a_rows, K/2] / [a_rows, K/16];  a_global fp32 [1];
+ *                      a_rows >= 1 whenever rows_total > 0 (row 0 must exist);
+ *                      a row index outside [0, a_rows) reads as zeros
  *   group_offsets      int64 [E+1] (device), group_offsets[E] == rows_total
  *   w_codes/w_scales   [E, N, K/2] / [E, N, K/16];  w_global fp32 [E]
- *   sel_idx            NULL (no compensation) or int32 [E, kc] ascending
+ *   sel_idx            NULL (no compensation) or int32 [E, kc] ascending, kc <= 128
  *   r_codes/r_scales   [rows_total, kc/2] / [rows_total, kc/16]; r_global fp32 [E]
  *   epilogue           NVFP4_EPI_*: F32 writes fp32 [rows_total, ldo];
  *                      SWIGLU_BF16 needs N even, gate = outputs 0..N/2-1,
  *                      up = N/2..N-1, writes bf16 h [rows_total, ldo] =
  *                      bf16(silu(gate) * up) and, when out_amax != NULL,
  *                      stores max |h| (fp32) into *out_amax;
- *                      SCATTER_ADD_F32 atomically adds row_weight[r] * Y[r]
- *                      into out row scatter_index[r] (< out_rows) of fp32
- *                      [out_rows, ldo]; the caller initializes out.
+ *                      SCATTER_ADD_F32 adds row_weight[r] * Y[r] into out row
+ *                      scatter_index[r] (< out_rows) of fp32 [out_rows, ldo],
+ *                      the rows of each output row in increasing r (a fixed
+ *                      order: the result is reproducible); the caller
+ *                      initializes out.  Needs the workspace
+ *                      (rows_total * N * 4 bytes plus index lists); the
+ *                      other epilogues need none.
  * Errors: EINVAL (shapes, pointers, epilogue arguments, kc), EWORKSPACE.
  * rows_total == 0 is valid (out_amax set to 0, nothing else written).
  * ------------------------------------------------------------------------ */
-size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K);
+size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K,
+                                            int epilogue, int64_t out_rows);
 int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
                           const int32_t* a_row_index, int64_t a_rows,
                           const int64_t* group_offsets, int32_t E, int64_t rows_total, int64_t K,

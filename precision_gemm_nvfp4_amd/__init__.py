@@ -39,7 +39,7 @@ _SIGNATURES = {
     "resq_select_and_requant_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "resq_select_and_requant": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64,
                                        _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "moe_w4a4_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64]),
+    "moe_w4a4_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _INT, _I64]),
     "moe_w4a4_grouped_gemm": (_INT, [_P, _P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _P,
                                      _I64, _P, _P, _P, _P, _I32, _INT, _P, _P, _I64, _P, _I64,
                                      _P, _P, _SZ, _P]),
@@ -181,7 +181,8 @@ def moe_w4a4_grouped_gemm(a_codes, a_scales, a_global, group_offsets, rows_total
     if out_rows is None:
         out_rows = out.shape[0]
     kc = 0 if sel_idx is None else sel_idx.shape[1]
-    ws = _workspace(lib.moe_w4a4_grouped_gemm_workspace_size(n_exp, rows_total, n, kk), dev)
+    ws = _workspace(lib.moe_w4a4_grouped_gemm_workspace_size(n_exp, rows_total, n, kk, epilogue,
+                                                             out_rows), dev)
     a_rows = a_codes.shape[0] if a_codes is not None else 0
     _check(lib.moe_w4a4_grouped_gemm(
         _ptr(a_codes), _ptr(a_scales), _ptr(a_global), _ptr(a_row_index), a_rows,

@@ -63,7 +63,7 @@ const char* nvfp4_last_error(void) { return g_err; }
 
 // ---------------------------------------------------------------------------
 size_t nvfp4_quantize_workspace_size(int64_t M, int64_t K) {
-  return align256((size_t)nvfp4::amax_partials_count(M, K) * sizeof(float));
+  return align256((size_t)(nvfp4::amax_partials_count(M, K) + 1) * sizeof(float));
 }
 
 int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
@@ -94,8 +94,9 @@ int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
 // ---------------------------------------------------------------------------
 size_t resq_select_and_requant_workspace_size(int64_t K, int64_t rows_total, int64_t U, int32_t k) {
   const int64_t slots = nvfp4::resq_max_slots(rows_total, U);
-  return align256((size_t)(U + 1) * 4) + align256((size_t)slots * K * 4) +
-         align256((size_t)rows_total * k * 4) + align256((size_t)slots * 4);
+  const int64_t gslots = nvfp4::resq_max_gather_slots(rows_total, U);
+  return 2 * align256((size_t)(U + 1) * 4) + align256((size_t)slots * K * 4) +
+         align256((size_t)rows_total * k * 4) + align256((size_t)gslots * 4);
 }
 
 int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
@@ -133,6 +134,8 @@ int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K,
   nvfp4::ResqWorkspace rw;
   rw.tile_start = reinterpret_cast<int32_t*>(w);
   w += align256((size_t)(U + 1) * 4);
+  rw.slot_start = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)(U + 1) * 4);
   rw.partials = reinterpret_cast<float*>(w);
   w += align256((size_t)slots * K * 4);
   rw.r_s = reinterpret_cast<float*>(w);
@@ -146,9 +149,11 @@ int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K,
 }
 
 // ---------------------------------------------------------------------------
-size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K) {
-  (void)E; (void)rows_total; (void)N; (void)K;
-  return 0;
+size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K,
+                                            int epilogue, int64_t out_rows) {
+  (void)E; (void)K;
+  if (epilogue != NVFP4_EPI_SCATTER_ADD_F32 || rows_total < 0 || N < 0 || out_rows < 0) return 0;
+  return nvfp4::combine_workspace_bytes(rows_total, N, out_rows);
 }
 
 int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const float* a_global,
@@ -161,20 +166,22 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int64_t out_rows, void* out, int64_t ldo, float* out_amax,
                           void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "moe_w4a4_grouped_gemm";
-  (void)ws; (void)ws_bytes;
   if (E <= 0 || K <= 0 || N <= 0 || rows_total < 0 || a_rows < 0)
     return fail(NVFP4_EINVAL, "%s: E=%d K=%lld N=%lld rows_total=%lld", fn, E, (long long)K,
                 (long long)N, (long long)rows_total);
   if (K % 64 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 64", fn, (long long)K);
+  if (K > 65536) return fail(NVFP4_EUNSUPPORTED, "%s: K=%lld > 65536", fn, (long long)K);
   if (rows_total > 2147483647LL) return fail(NVFP4_EUNSUPPORTED, "%s: rows_total above 2^31-1", fn);
   if (!group_offsets || !w_codes || !w_scales || !w_global || !a_global || !out)
     return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
   if (rows_total > 0 && (!a_codes || !a_scales)) return fail(NVFP4_EINVAL, "%s: a_codes/a_scales NULL", fn);
+  if (rows_total > 0 && a_rows < 1)      // the kernel reads row 0 in place of rows outside a tile
+    return fail(NVFP4_EINVAL, "%s: a_rows must be at least 1 when rows_total > 0", fn);
   if (!aligned16(w_codes) || (a_codes && !aligned16(a_codes)))
     return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
   if (sel_idx) {
-    if (kc < 16 || kc % 16 != 0 || kc > K || kc > 256)
-      return fail(NVFP4_EINVAL, "%s: kc=%d must be a multiple of 16 in [16, min(K, 256)]", fn, kc);
+    if (kc < 16 || kc % 16 != 0 || kc > K || kc > 128)
+      return fail(NVFP4_EINVAL, "%s: kc=%d must be a multiple of 16 in [16, min(K, 128)]", fn, kc);
     if (rows_total > 0 && (!r_codes || !r_scales)) return fail(NVFP4_EINVAL, "%s: r_codes/r_scales NULL", fn);
     if (!r_global) return fail(NVFP4_EINVAL, "%s: r_global NULL", fn);
   }
@@ -186,7 +193,11 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
   } else if (epilogue == NVFP4_EPI_SCATTER_ADD_F32) {
     if (ldo < N) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N", fn, (long long)ldo);
     if (!row_weight || !scatter_index) return fail(NVFP4_EINVAL, "%s: scatter needs row_weight and scatter_index", fn);
-    if (out_rows < 0) return fail(NVFP4_EINVAL, "%s: out_rows negative", fn);
+    if (out_rows < 0 || out_rows > 2147483647LL)
+      return fail(NVFP4_EINVAL, "%s: out_rows must be in [0, 2^31-1]", fn);
+    const size_t need = moe_w4a4_grouped_gemm_workspace_size(E, rows_total, N, K, epilogue, out_rows);
+    if (!ws || ws_bytes < need)
+      return fail(NVFP4_EWORKSPACE, "%s: scatter epilogue needs a %zu-byte workspace", fn, need);
   } else {
     return fail(NVFP4_EINVAL, "%s: unknown epilogue %d", fn, epilogue);
   }
@@ -200,6 +211,8 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
   a.epilogue = epilogue; a.row_weight = row_weight; a.scatter_index = scatter_index;
   a.out_rows = out_rows; a.out = out; a.ldo = ldo;
   a.out_amax = epilogue == NVFP4_EPI_SWIGLU_BF16 ? out_amax : nullptr;
+  a.block_m = 0;
+  a.y_rows = epilogue == NVFP4_EPI_SCATTER_ADD_F32 ? static_cast<float*>(ws) : nullptr;
   return hip_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -234,6 +247,8 @@ int guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t l
                  uint8_t* guided_codes, void* x_fq, int64_t* dist_hist, void* stream) {
   const char* fn = "guided_round";
   if (int s = check_act(x_train, dtype, M, K, ldx, fn)) return s;
+  if (M * (K / 16) > 2147483647LL)
+    return fail(NVFP4_EUNSUPPORTED, "%s: more than 2^31-1 blocks", fn);
   if (M > 0 && (!roll_codes || !roll_scales || !roll_global || !guided_codes))
     return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
   if ((roll_codes && !aligned16(roll_codes)) || (guided_codes && !aligned16(guided_codes)) ||

@@ -123,12 +123,15 @@ __device__ __forceinline__ uint32_t e2m1_code_exact(float x, float S) {
 
 // Fast path for 8 elements sharing a scale.  v = x * (1/S) is within 2^-22
 // (relative) of the exact quotient; the hardware FP4 convert (round to
-// nearest, saturating, sign kept) of v * (1 +- 2^-20) brackets that error
-// band.  When both brackets give the same codes, no rounding boundary lies in
-// the band and those codes are the exact ones; otherwise (a tie, or a value
-// within 2^-20 of a boundary) the caller takes the exact path.
-// Returns the packed codes (element 2j in the low nibble of byte j) in *out.
-__device__ __forceinline__ bool e2m1_pack8_fast(const float* x, float inv, uint32_t* out) {
+// nearest even, saturating, sign kept) of v * (1 + 2^-20) and v * (1 - 2^-20)
+// brackets that error band.  Where the two agree, no rounding boundary lies in
+// the band and the code is exact.  Where they differ, exactly one midpoint m
+// lies in the band, between the two (adjacent) magnitudes the brackets gave;
+// the sign of fma(m, S, -|x|) -- the exact m*S - |x| rounded once -- decides
+// the side, and a zero (an exact tie, common when S has few significant bits)
+// goes to the even index.  Returns the packed codes (element 2j in the low
+// nibble of byte j).
+__device__ __forceinline__ uint32_t e2m1_pack8_fast(const float* x, float inv, float S) {
   const float up = 1.0f + 0x1p-20f, dn = 1.0f - 0x1p-20f;
   uint32_t wu = 0, wd = 0;
   float a[8];
@@ -142,8 +145,21 @@ __device__ __forceinline__ bool e2m1_pack8_fast(const float* x, float inv, uint3
   NVFP4_CVT_PAIR(2)
   NVFP4_CVT_PAIR(3)
 #undef NVFP4_CVT_PAIR
-  *out = wu;
-  return wu == wd;
+  uint32_t diff = wu ^ wd;
+  while (diff) {                               // rare: elements near a rounding boundary
+    const int sh = (__builtin_ctz(diff) >> 2) << 2;
+    const uint32_t iu = (wu >> sh) & 7u, id = (wd >> sh) & 7u;
+    const uint32_t lo = iu < id ? iu : id, hi = iu < id ? id : iu;   // hi == lo + 1
+    const float m = 0.5f * (e2m1_mag(lo) + e2m1_mag(hi));            // exact
+    float xi = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) xi = (sh >> 2) == i ? x[i] : xi;
+    const float d = __builtin_fmaf(m, S, -fabsf(xi));
+    const uint32_t idx = d < 0.0f ? hi : (d > 0.0f ? lo : ((lo & 1u) ? hi : lo));
+    wu = (wu & ~(7u << sh)) | (idx << sh);    // the sign bit (bit 3) already copies x's
+    diff &= ~(15u << sh);
+  }
+  return wu;
 }
 
 __device__ __forceinline__ uint32_t e2m1_pack8_exact(const float* x, float S) {
@@ -162,14 +178,12 @@ __device__ __forceinline__ float quantize_block16(const float* v, float g, doubl
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   float S;
   *sbyte = block_scale(amax, six_g, g, S);
-  // Fast path needs 1/S finite and accurate: S >= 2^-100 (a normal number).
-  bool ok = S >= 0x1p-100f;
-  if (ok) {
-    float inv = __builtin_amdgcn_rcpf(S);    // within 1 ulp
-    ok = e2m1_pack8_fast(v, inv, w0);
-    ok = e2m1_pack8_fast(v + 8, inv, w1) && ok;
-  }
-  if (!ok) {
+  // The fast path needs 1/S finite and accurate: S >= 2^-100 (a normal number).
+  if (S >= 0x1p-100f) {
+    const float inv = __builtin_amdgcn_rcpf(S);    // within 1 ulp
+    *w0 = e2m1_pack8_fast(v, inv, S);
+    *w1 = e2m1_pack8_fast(v + 8, inv, S);
+  } else {
     *w0 = e2m1_pack8_exact(v, S);
     *w1 = e2m1_pack8_exact(v + 8, S);
   }
@@ -188,6 +202,15 @@ __device__ __forceinline__ void e2m1_unpack8(uint32_t w, float* f) {
 
 // Dequantized value of 4-bit code c under S: RNE32(value * S).
 __device__ __forceinline__ float dq(uint32_t c, float S) { return e2m1_value(c) * S; }
+
+// Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
+// operations, then meets the other waves.  Unlike __syncthreads() it does not
+// wait for outstanding global loads, so loads issued ahead for later K-steps
+// stay in flight across the barrier.  The memory clobber keeps the compiler
+// from moving LDS accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
 
 // ---------------------------------------------------------------------------
 // wave reductions (64 lanes)

@@ -16,12 +16,14 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 
 // resq.hip
 struct ResqWorkspace {
-  int32_t* tile_start;   // [U+1]
+  int32_t* tile_start;   // [U+1] first 128-row score tile of each unit
+  int32_t* slot_start;   // [U+1] first 32-row gather slot of each unit
   float* partials;       // [max_slots, K] (unused when the caller gives tile partials)
   float* r_s;            // [rows_total, k]
-  float* amax_part;      // [max_slots]
+  float* amax_part;      // [max_gather_slots]
 };
 int64_t resq_max_slots(int64_t rows_total, int64_t U);
+int64_t resq_max_gather_slots(int64_t rows_total, int64_t U);
 hipError_t launch_resq(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
                        const int32_t* row_index, const uint8_t* codes, const uint8_t* scales,
                        const float* g, const int64_t* unit_offsets, int64_t U, int64_t rows_total,
@@ -56,8 +58,17 @@ struct GemmArgs {
   void* out;
   int64_t ldo;
   float* out_amax;
+  float* y_rows;         // scatter epilogue: row_weight * Y rows [rows_total, N] (workspace)
+  int block_m;           // rows per tile: 256, 128, 64, 32, or 0 to pick from the average group size
 };
+int grouped_gemm_block_m(int64_t rows_total, int32_t E);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+
+// combine.hip
+size_t combine_workspace_bytes(int64_t rows, int64_t N, int64_t out_rows);
+hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
+                          const int32_t* scatter_index, int64_t out_rows, float* out, int64_t ldo,
+                          void* ws, hipStream_t stream);
 
 // trainer.hip
 hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,

@@ -6,13 +6,13 @@
 // Two passes over x, both coalesced HBM streams:
 //   amax_partials_kernel  per-workgroup max |x|  -> workspace (no atomics, no
 //                         initialisation, order-independent hence deterministic)
-//   quantize_kernel       every workgroup folds the partial maxima into the
-//                         tensor amax and g, then quantizes its tile: one lane
-//                         owns one 16-element block column and walks the tile's
-//                         rows; optionally it accumulates |x - DQ| of its 16
-//                         channels over the 128-row tile in fp32, in row order
-//                         (the residual channel-score partials of the residual
-//                         activation compensation, QUADS section 2.2B).
+//   amax_fold_kernel      one workgroup folds the partial maxima into one float
+//   quantize_tile_kernel  every workgroup derives g from that amax, then
+//                         quantizes a 128 x 64 tile;
+//                         optionally it also sums |x - DQ| of each channel over
+//                         the tile's 128 rows in fp32, in row order (the residual
+//                         channel-score partials of the residual activation
+//                         compensation, QUADS section 2.2B).
 #include "device_common.h"
 #include "kernels.h"
 
@@ -85,59 +85,92 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const T* __restrict_
   }
 }
 
-// Max over n partial maxima, read by one wave (lanes stride the array).
-__device__ __forceinline__ float fold_partials(const float* partials, int n) {
+// Folds the n partial maxima into partials[n] (one workgroup), so that every
+// quantize workgroup reads a single float.
+__global__ __launch_bounds__(256) void amax_fold_kernel(float* __restrict__ partials, int n) {
   float m = 0.0f;
-  for (int i = threadIdx.x & 63; i < n; i += 64) m = fmaxf(m, partials[i]);
-  return wave_max(m);
+  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, partials[i]);
+  m = wave_max(m);
+  __shared__ float red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) partials[n] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // ---------------------------------------------------------------------------
 // pass 2: block quantization (+ optional residual-score partials)
 // ---------------------------------------------------------------------------
-// grid: x = ceil(K/16 / 64) block columns of 64 lanes, y = row tiles of ROWS.
-template <typename T, bool SCORES, int ROWS>
-__global__ __launch_bounds__(64) void quantize_kernel(
+// One workgroup (256 threads) owns a tile of 128 rows x 64 columns.  Thread t
+// quantizes the 16-element block column t % 4 of rows t / 4 and t / 4 + 64:
+// both rows are loaded before any arithmetic, so every thread has two loads in
+// flight.  With SCORES, each thread also writes |x - DQ| of its blocks into LDS
+// (34 KB: four workgroups fit a CU), and after a barrier threads 0..63 each add
+// one column's 128 values in increasing row order (rows past the tensor
+// contribute +0, which leaves an fp32 sum unchanged).
+constexpr int kTileCols = 64;
+constexpr int kTileBlocks = kTileCols / kBlock;     // 4
+constexpr int kRowsPerThread = kScoreTileRows / (256 / kTileBlocks);   // 2
+constexpr int kAbsStride = kTileCols + 4;          // floats per LDS row
+
+template <typename T, bool SCORES>
+__global__ __launch_bounds__(256) void quantize_tile_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    const float* __restrict__ amax_partials, int n_partials, const float* __restrict__ amax_in,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ g_out,
-    float* __restrict__ tile_partials) {
-  const float amax = amax_in ? *amax_in : fold_partials(amax_partials, n_partials);
-  const float g = global_scale_from_amax(amax);
+    const float* __restrict__ amax, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+    float* __restrict__ g_out, float* __restrict__ tile_partials) {
+  __shared__ float absr[SCORES ? kScoreTileRows * kAbsStride : 1];
+  const int tid = threadIdx.x;
+  const float g = global_scale_from_amax(*amax);
   const double six_g = 6.0 * (double)g;
-  if (g_out && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *g_out = g;
+  if (g_out && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *g_out = g;
 
   const int64_t nb = K / kBlock;
-  const int64_t bc = (int64_t)blockIdx.x * 64 + threadIdx.x;
-  if (bc >= nb) return;
-  const int64_t r0 = (int64_t)blockIdx.y * ROWS;
-  const int64_t r1 = r0 + ROWS < M ? r0 + ROWS : M;
-
-  float acc[16];
+  const int bl = tid % kTileBlocks, rsub = tid / kTileBlocks;
+  const int64_t bc = (int64_t)blockIdx.x * kTileBlocks + bl;
+  const int64_t r0 = (int64_t)blockIdx.y * kScoreTileRows;
+  float v[kRowsPerThread][16];
+  bool live[kRowsPerThread];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-
-#pragma unroll 4
-  for (int64_t r = r0; r < r1; ++r) {
-    float v[16];
-    Row16<T>::load(x + r * ldx + bc * kBlock, v);
-    uint32_t sb, w0, w1;
-    const float S = quantize_block16(v, g, six_g, &sb, &w0, &w1);
-    *reinterpret_cast<u32x2*>(codes + r * (K / 2) + bc * 8) = u32x2{w0, w1};
-    scales[r * nb + bc] = (uint8_t)sb;
-    if constexpr (SCORES) {
+  for (int j = 0; j < kRowsPerThread; ++j) {         // all loads first
+    const int64_t r = r0 + rsub + (256 / kTileBlocks) * j;
+    live[j] = r < M && bc < nb;
+    if (live[j]) Row16<T>::load(x + r * ldx + bc * kBlock, v[j]);
+  }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const uint32_t c = ((j < 8 ? w0 : w1) >> (4 * (j & 7))) & 15u;
-        const float res = v[j] - dq(c, S);         // exact (Sterbenz); no contraction
-        acc[j] = acc[j] + fabsf(res);
+  for (int j = 0; j < kRowsPerThread; ++j) {
+    const int rl = rsub + (256 / kTileBlocks) * j;
+    const int64_t r = r0 + rl;
+    float res[16];
+    if (live[j]) {
+      uint32_t sb, w0, w1;
+      const float S = quantize_block16(v[j], g, six_g, &sb, &w0, &w1);
+      *reinterpret_cast<u32x2*>(codes + r * (K / 2) + bc * 8) = u32x2{w0, w1};
+      scales[r * nb + bc] = (uint8_t)sb;
+      if constexpr (SCORES) {
+        float f[16];
+        e2m1_unpack8(w0, f);
+        e2m1_unpack8(w1, f + 8);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) res[i] = fabsf(v[j][i] - f[i] * S);   // exact; no contraction
       }
+    } else if constexpr (SCORES) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) res[i] = 0.0f;
+    }
+    if constexpr (SCORES) {
+      f32x4* dst = reinterpret_cast<f32x4*>(absr + rl * kAbsStride + bl * kBlock);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dst[i] = f32x4{res[4 * i], res[4 * i + 1], res[4 * i + 2], res[4 * i + 3]};
     }
   }
   if constexpr (SCORES) {
-    f32x4* out = reinterpret_cast<f32x4*>(tile_partials + (int64_t)blockIdx.y * K + bc * kBlock);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+    __syncthreads();
+    const int64_t c = (int64_t)blockIdx.x * kTileCols + tid;
+    if (tid < kTileCols && c < K) {
+      float sum = 0.0f;
+#pragma unroll 16
+      for (int rl = 0; rl < kScoreTileRows; ++rl) sum = sum + absr[rl * kAbsStride + tid];
+      tile_partials[(int64_t)blockIdx.y * K + c] = sum;
+    }
   }
 }
 
@@ -156,21 +189,20 @@ static hipError_t launch_quantize_t(const T* x, int64_t M, int64_t K, int64_t ld
                                     float* g_out, float* tile_partials, float* ws_partials,
                                     hipStream_t stream) {
   const int np = amax_partials_count(M, K);
+  const float* amax = amax_in;
   if (!amax_in) {
     amax_partials_kernel<T><<<np, 256, 0, stream>>>(x, M, K, ldx, ws_partials);
+    amax_fold_kernel<<<1, 256, 0, stream>>>(ws_partials, np);
+    amax = ws_partials + np;
   }
-  const int64_t nb = K / kBlock;
-  const unsigned gx = (unsigned)((nb + 63) / 64);
-  if (tile_partials) {
-    dim3 grid(gx, (unsigned)((M + kScoreTileRows - 1) / kScoreTileRows));
-    quantize_kernel<T, true, kScoreTileRows><<<grid, 64, 0, stream>>>(
-        x, M, K, ldx, ws_partials, np, amax_in, codes, scales, g_out, tile_partials);
-  } else {
-    constexpr int R = 8;
-    dim3 grid(gx, (unsigned)((M + R - 1) / R));
-    quantize_kernel<T, false, R><<<grid, 64, 0, stream>>>(
-        x, M, K, ldx, ws_partials, np, amax_in, codes, scales, g_out, nullptr);
-  }
+  dim3 grid((unsigned)((K + kTileCols - 1) / kTileCols),
+            (unsigned)((M + kScoreTileRows - 1) / kScoreTileRows));
+  if (tile_partials)
+    quantize_tile_kernel<T, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, amax, codes, scales,
+                                                            g_out, tile_partials);
+  else
+    quantize_tile_kernel<T, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, amax, codes, scales,
+                                                             g_out, nullptr);
   return hipGetLastError();
 }
 

@@ -6,23 +6,28 @@
 //
 // Kernels (one stream, in order):
 //   plan      tile_start[u]: first 128-row tile of unit u (exclusive scan)
-//   scores    per (tile, 1024-channel slice): fp32 sum of |R| over the tile's
+//   scores    per (128-row tile, 64 channels): fp32 sum of |R| over the tile's
 //             rows in increasing row order          (skipped when nvfp4_quantize
 //                                                    already produced them)
-//   select    per unit: tile sums added in tile order -> LDS; radix select of
-//             the k-th largest score; ties to the lower channel; compaction in
-//             ascending channel order (block scans)
-//   gather    per tile: R_S = x[:, sel] - DQ(codes, scales)[:, sel] -> workspace,
-//             with the tile's max |R_S|
-//   requant   per tile: unit amax -> g_R, NVFP4 of R_S rows (16-blocks along
-//             the compact axis) -> r_codes, r_scales, r_global
+//   select    per unit: tile sums added in tile order -> LDS; the k-th largest
+//             score found bit by bit (31 block-wide counts); ties to the lower
+//             channel; compaction in ascending channel order (block scans)
+//   gather    per 32-row slot: R_S = x[:, sel] - DQ(codes, scales)[:, sel] ->
+//             workspace, with the slot's max |R_S|
+//   requant   per 32-row slot: unit amax -> g_R, NVFP4 of R_S rows (16-blocks
+//             along the compact axis) -> r_codes, r_scales, r_global
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nvfp4 {
 
+constexpr int kGatherRows = 32;               // rows per gather / requant slot
+
 int64_t resq_max_slots(int64_t rows_total, int64_t U) {
   return (rows_total + kScoreTileRows - 1) / kScoreTileRows + U;
+}
+int64_t resq_max_gather_slots(int64_t rows_total, int64_t U) {
+  return (rows_total + kGatherRows - 1) / kGatherRows + U;
 }
 
 struct Units {
@@ -81,23 +86,33 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // ---------------------------------------------------------------------------
 // plan
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* tile_start) {
+__global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* tile_start,
+                                                         int32_t* slot_start) {
   __shared__ uint32_t sh[16];
-  uint32_t carry = 0;
+  uint32_t carry_t = 0, carry_s = 0;
   for (int64_t base = 0; base < units.U; base += blockDim.x) {
     int64_t u = base + threadIdx.x;
-    uint32_t n = 0;
+    uint32_t nt = 0, ns = 0;
     if (u < units.U) {
       int64_t b, e;
       units.range(u, b, e);
-      n = (uint32_t)((e - b + kScoreTileRows - 1) / kScoreTileRows);
+      nt = (uint32_t)((e - b + kScoreTileRows - 1) / kScoreTileRows);
+      ns = (uint32_t)((e - b + kGatherRows - 1) / kGatherRows);
     }
-    uint32_t tot;
-    uint32_t ex = block_exclusive_scan(n, sh, &tot);
-    if (u < units.U) tile_start[u] = (int32_t)(carry + ex);
-    carry += tot;
+    uint32_t tot_t, tot_s;
+    const uint32_t ex_t = block_exclusive_scan(nt, sh, &tot_t);
+    const uint32_t ex_s = block_exclusive_scan(ns, sh, &tot_s);
+    if (u < units.U) {
+      tile_start[u] = (int32_t)(carry_t + ex_t);
+      slot_start[u] = (int32_t)(carry_s + ex_s);
+    }
+    carry_t += tot_t;
+    carry_s += tot_s;
   }
-  if (threadIdx.x == 0) tile_start[units.U] = (int32_t)carry;
+  if (threadIdx.x == 0) {
+    tile_start[units.U] = (int32_t)carry_t;
+    slot_start[units.U] = (int32_t)carry_s;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -136,55 +151,97 @@ __device__ __forceinline__ float load1(const T* p) {
   }
 }
 
+// One workgroup per (128-row tile of a unit, 64 channels).  Thread t computes
+// |R| of block column t % 4 for rows t / 4 and t / 4 + 64 (loads first, then
+// arithmetic) into LDS; then threads 0..63 add one channel each over the
+// tile's rows in increasing row order (missing rows add +0, which changes no
+// fp32 sum).
+constexpr int kScoreCols = 64;
+constexpr int kScoreBlocks = kScoreCols / kBlock;
+constexpr int kAbsStride = kScoreCols + 4;
+
 template <typename T>
-__global__ __launch_bounds__(64) void resq_scores_kernel(
+__global__ __launch_bounds__(256) void resq_scores_kernel(
     const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
     const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ gp, Units units,
     const int32_t* __restrict__ tile_start, float* __restrict__ partials) {
-  const int64_t slot = blockIdx.x;
+  __shared__ float absr[kScoreTileRows * kAbsStride];
+  const int64_t slot = blockIdx.y;
   const int64_t u = unit_of_slot(tile_start, units.U, slot);
   if (u < 0) return;
+  const int tid = threadIdx.x;
   const int64_t nb = K / kBlock;
-  const int64_t bc = (int64_t)blockIdx.y * 64 + threadIdx.x;
-  if (bc >= nb) return;
+  const int bl = tid % kScoreBlocks, rsub = tid / kScoreBlocks;
+  const int64_t bc = (int64_t)blockIdx.x * kScoreBlocks + bl;
   int64_t b, e;
   units.range(u, b, e);
   const int64_t r0 = b + (slot - tile_start[u]) * kScoreTileRows;
-  const int64_t r1 = r0 + kScoreTileRows < e ? r0 + kScoreTileRows : e;
   const float g = *gp;
-  float acc[16];
+  float v[2][16];
+  u32x2 w[2];
+  uint32_t sb[2];
+  bool live[2];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
-  for (int64_t r = r0; r < r1; ++r) {
-    const int64_t xr = row_index ? (int64_t)row_index[r] : r;
-    if (xr < 0 || xr >= x_rows) continue;
-    float v[16];
-    load16<T>(x + xr * ldx + bc * kBlock, v);
-    const u32x2 w = *reinterpret_cast<const u32x2*>(codes + xr * (K / 2) + bc * 8);
-    const float S = e4m3_value(scales[xr * nb + bc]) * g;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t c = (w[j >> 3] >> (4 * (j & 7))) & 15u;
-      acc[j] = acc[j] + fabsf(v[j] - dq(c, S));
+  for (int j = 0; j < 2; ++j) {                  // all loads first
+    const int64_t r = r0 + rsub + 64 * j;
+    const int64_t xr = r < e ? (row_index ? (int64_t)row_index[r] : r) : -1;
+    live[j] = xr >= 0 && xr < x_rows && bc < nb;
+    if (live[j]) {
+      load16<T>(x + xr * ldx + bc * kBlock, v[j]);
+      w[j] = *reinterpret_cast<const u32x2*>(codes + xr * (K / 2) + bc * 8);
+      sb[j] = scales[xr * nb + bc];
     }
   }
-  f32x4* out = reinterpret_cast<f32x4*>(partials + slot * K + bc * kBlock);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) out[i] = f32x4{acc[4 * i], acc[4 * i + 1], acc[4 * i + 2], acc[4 * i + 3]};
+  for (int j = 0; j < 2; ++j) {
+    const int rl = rsub + 64 * j;
+    float res[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) res[i] = 0.0f;
+    if (live[j]) {
+      const float S = e4m3_value(sb[j]) * g;
+      float f[16];
+      e2m1_unpack8(w[j][0], f);
+      e2m1_unpack8(w[j][1], f + 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) res[i] = fabsf(v[j][i] - f[i] * S);   // exact; no contraction
+    }
+    f32x4* dst = reinterpret_cast<f32x4*>(absr + rl * kAbsStride + bl * kBlock);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = f32x4{res[4 * i], res[4 * i + 1], res[4 * i + 2], res[4 * i + 3]};
+  }
+  __syncthreads();
+  const int64_t c = (int64_t)blockIdx.x * kScoreCols + tid;
+  if (tid < kScoreCols && c < K) {
+    float sum = 0.0f;
+#pragma unroll 16
+    for (int rl = 0; rl < kScoreTileRows; ++rl) sum = sum + absr[rl * kAbsStride + tid];
+    partials[slot * K + c] = sum;
+  }
 }
 
 // ---------------------------------------------------------------------------
 // select: scores -> top-k (ties to the lower index) -> ascending channel list
 // ---------------------------------------------------------------------------
+// Block-wide sum of one uint32 per thread (256 threads); all threads get it.
+__device__ __forceinline__ uint32_t block_sum256(uint32_t v, uint32_t* sh4) {
+  v = wave_sum_u32(v);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) sh4[threadIdx.x >> 6] = v;
+  __syncthreads();
+  return sh4[0] + sh4[1] + sh4[2] + sh4[3];
+}
+
+// Keys live in LDS chunk by chunk: thread t owns channels [t*chunk, (t+1)*chunk)
+// stored at t*(chunk+1) + j, one pad word per chunk so that the 64 lanes of a
+// wave reading "their" j-th key hit different banks.
 __global__ __launch_bounds__(256) void resq_select_kernel(
     const float* __restrict__ partials, int64_t K, Units units,
     const int32_t* __restrict__ tile_start, int32_t k, int32_t* __restrict__ sel_idx,
     float* __restrict__ r_global) {
-  extern __shared__ uint32_t keys[];          // [K] score bits (scores are >= +0)
-  __shared__ uint32_t hist[256];
+  extern __shared__ uint32_t keys[];          // [256 * (chunk + 1)] score bits (scores >= +0)
   __shared__ uint32_t sh_waves[4];
-  __shared__ uint32_t sh_digit, sh_rem;
   const int64_t u = blockIdx.x;
   const int tid = threadIdx.x;
   int64_t b, e;
@@ -195,56 +252,43 @@ __global__ __launch_bounds__(256) void resq_select_kernel(
     if (tid == 0) r_global[u] = 1.0f;
     return;
   }
+  const int chunk = (int)((K + blockDim.x - 1) / blockDim.x);
   const int64_t t0 = tile_start[u], t1 = tile_start[u + 1];
   for (int64_t c = tid; c < K; c += blockDim.x) {
     float s = 0.0f;
     for (int64_t t = t0; t < t1; ++t) s = s + partials[t * K + c];   // tile order
-    keys[c] = __float_as_uint(s);
+    keys[(c / chunk) * (chunk + 1) + c % chunk] = __float_as_uint(s);
   }
   __syncthreads();
+  const uint32_t* my = keys + tid * (chunk + 1);
+  const int64_t c0 = (int64_t)tid * chunk;
+  const int n_my = (int)(c0 >= K ? 0 : (c0 + chunk <= K ? chunk : K - c0));
 
-  // radix select (8-bit digits, most significant first) of the k-th largest key
-  uint32_t prefix = 0, mask = 0;
-  uint32_t remaining = (uint32_t)k;
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    hist[tid] = 0;
-    __syncthreads();
-    for (int64_t c = tid; c < K; c += blockDim.x) {
-      uint32_t key = keys[c];
-      if ((key & mask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      uint32_t above = 0;
-      int d = 255;
-      for (; d > 0; --d) {
-        if (above + hist[d] >= remaining) break;
-        above += hist[d];
-      }
-      sh_digit = (uint32_t)d;
-      sh_rem = remaining - above;
-    }
-    __syncthreads();
-    prefix |= sh_digit << shift;
-    mask |= 255u << shift;
-    remaining = sh_rem;
-    __syncthreads();
+  // The k-th largest key T, one bit at a time from the top: T is the largest
+  // value with at least k keys >= T.  Non-negative float bits order like the
+  // floats, and bit 31 (sign) is 0.
+  uint32_t T = 0;
+  for (int bit = 30; bit >= 0; --bit) {
+    const uint32_t cand = T | (1u << bit);
+    uint32_t n = 0;
+    for (int j = 0; j < n_my; ++j) n += my[j] >= cand;
+    if (block_sum256(n, sh_waves) >= (uint32_t)k) T = cand;
   }
-  const uint32_t T = prefix;     // k-th largest key; `remaining` keys equal to T are taken
+  uint32_t n_gt = 0, n_eq = 0;
+  for (int j = 0; j < n_my; ++j) {
+    n_gt += my[j] > T;
+    n_eq += my[j] == T;
+  }
+  const uint32_t remaining = (uint32_t)k - block_sum256(n_gt, sh_waves);   // keys == T to take
 
-  // selection in index order: thread owns a contiguous chunk of channels
-  const int64_t chunk = (K + blockDim.x - 1) / blockDim.x;
-  const int64_t c0 = tid * chunk;
-  const int64_t c1 = c0 + chunk < K ? c0 + chunk : K;
-  uint32_t n_eq = 0;
-  for (int64_t c = c0; c < c1; ++c) n_eq += keys[c] == T;
+  // selection in index order: thread owns the contiguous chunk [c0, c0 + n_my)
   uint32_t tot;
-  uint32_t eq_before = block_exclusive_scan(n_eq, sh_waves, &tot);
+  const uint32_t eq_before = block_exclusive_scan(n_eq, sh_waves, &tot);
   uint32_t n_sel = 0;
   {
     uint32_t eq_seen = eq_before;
-    for (int64_t c = c0; c < c1; ++c) {
-      uint32_t key = keys[c];
+    for (int j = 0; j < n_my; ++j) {
+      const uint32_t key = my[j];
       if (key > T) ++n_sel;
       else if (key == T && eq_seen++ < remaining) ++n_sel;
     }
@@ -252,33 +296,33 @@ __global__ __launch_bounds__(256) void resq_select_kernel(
   uint32_t pos = block_exclusive_scan(n_sel, sh_waves, &tot);
   {
     uint32_t eq_seen = eq_before;
-    for (int64_t c = c0; c < c1; ++c) {
-      uint32_t key = keys[c];
-      bool take = key > T || (key == T && eq_seen++ < remaining);
-      if (take && pos < (uint32_t)k) out[pos++] = (int32_t)c;
+    for (int j = 0; j < n_my; ++j) {
+      const uint32_t key = my[j];
+      const bool take = key > T || (key == T && eq_seen++ < remaining);
+      if (take && pos < (uint32_t)k) out[pos++] = (int32_t)(c0 + j);
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// gather R_S and per-tile max |R_S|
+// gather R_S and per-slot max |R_S|
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void resq_gather_kernel(
     const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
     const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ gp, Units units,
-    const int32_t* __restrict__ tile_start, const int32_t* __restrict__ sel_idx, int32_t k,
+    const int32_t* __restrict__ slot_start, const int32_t* __restrict__ sel_idx, int32_t k,
     float* __restrict__ r_s, float* __restrict__ amax_part) {
   extern __shared__ int32_t sel[];           // [k]
   __shared__ float red[4];
   const int64_t slot = blockIdx.x;
-  const int64_t u = unit_of_slot(tile_start, units.U, slot);
+  const int64_t u = unit_of_slot(slot_start, units.U, slot);
   if (u < 0) return;
   int64_t b, e;
   units.range(u, b, e);
-  const int64_t r0 = b + (slot - tile_start[u]) * kScoreTileRows;
-  const int64_t r1 = r0 + kScoreTileRows < e ? r0 + kScoreTileRows : e;
+  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
+  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
   for (int j = threadIdx.x; j < k; j += blockDim.x) {
     int32_t c = sel_idx[u * k + j];
     sel[j] = c < 0 ? 0 : (c >= K ? (int32_t)(K - 1) : c);
@@ -317,18 +361,18 @@ __global__ __launch_bounds__(256) void resq_gather_kernel(
 // requantize R_S with the unit's own global scale
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void resq_requant_kernel(
-    const float* __restrict__ r_s, Units units, const int32_t* __restrict__ tile_start,
+    const float* __restrict__ r_s, Units units, const int32_t* __restrict__ slot_start,
     const float* __restrict__ amax_part, int32_t k, uint8_t* __restrict__ r_codes,
     uint8_t* __restrict__ r_scales, float* __restrict__ r_global) {
   __shared__ float sh_g;
   const int64_t slot = blockIdx.x;
-  const int64_t u = unit_of_slot(tile_start, units.U, slot);
+  const int64_t u = unit_of_slot(slot_start, units.U, slot);
   if (u < 0) return;
   int64_t b, e;
   units.range(u, b, e);
   if (threadIdx.x < 64) {
     float m = 0.0f;
-    for (int64_t t = tile_start[u] + threadIdx.x; t < tile_start[u + 1]; t += 64)
+    for (int64_t t = slot_start[u] + threadIdx.x; t < slot_start[u + 1]; t += 64)
       m = fmaxf(m, amax_part[t]);
     m = wave_max(m);
     if (threadIdx.x == 0) sh_g = global_scale_from_amax(m);
@@ -336,9 +380,9 @@ __global__ __launch_bounds__(256) void resq_requant_kernel(
   __syncthreads();
   const float g = sh_g;
   const double six_g = 6.0 * (double)g;
-  if (slot == tile_start[u] && threadIdx.x == 0) r_global[u] = g;
-  const int64_t r0 = b + (slot - tile_start[u]) * kScoreTileRows;
-  const int64_t r1 = r0 + kScoreTileRows < e ? r0 + kScoreTileRows : e;
+  if (slot == slot_start[u] && threadIdx.x == 0) r_global[u] = g;
+  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
+  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
   const int kb = k / kBlock;
   const int64_t n = (r1 - r0) * kb;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
@@ -366,23 +410,30 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
                                 const ResqWorkspace& ws, hipStream_t stream) {
   Units units{tile_partials ? nullptr : unit_offsets, U, rows_total};
   const int64_t slots = tile_partials ? U : resq_max_slots(rows_total, U);
-  resq_plan_kernel<<<1, 1024, 0, stream>>>(units, ws.tile_start);
+  const int64_t gslots = resq_max_gather_slots(rows_total, U);
+  resq_plan_kernel<<<1, 1024, 0, stream>>>(units, ws.tile_start, ws.slot_start);
   const float* partials = tile_partials;
   if (!tile_partials) {
-    dim3 grid((unsigned)slots, (unsigned)((K / kBlock + 63) / 64));
-    resq_scores_kernel<T><<<grid, 64, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
-                                                   units, ws.tile_start, ws.partials);
+    dim3 grid((unsigned)((K + kScoreCols - 1) / kScoreCols), (unsigned)slots);
+    resq_scores_kernel<T><<<grid, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
+                                                    units, ws.tile_start, ws.partials);
     partials = ws.partials;
   }
-  resq_select_kernel<<<(unsigned)U, 256, (size_t)K * 4, stream>>>(partials, K, units, ws.tile_start,
-                                                                   k, sel_idx, r_global);
-  if (slots > 0) {
-    resq_gather_kernel<T><<<(unsigned)slots, 256, (size_t)k * 4, stream>>>(
-        x, x_rows, K, ldx, row_index, codes, scales, g, units, ws.tile_start, sel_idx, k, ws.r_s,
+  const size_t sel_lds = (size_t)256 * ((K + 255) / 256 + 1) * 4;
+  if (sel_lds > 65536) {
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&resq_select_kernel),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
+    if (err != hipSuccess) return err;
+  }
+  resq_select_kernel<<<(unsigned)U, 256, sel_lds, stream>>>(partials, K, units, ws.tile_start, k,
+                                                            sel_idx, r_global);
+  if (gslots > 0) {
+    resq_gather_kernel<T><<<(unsigned)gslots, 256, (size_t)k * 4, stream>>>(
+        x, x_rows, K, ldx, row_index, codes, scales, g, units, ws.slot_start, sel_idx, k, ws.r_s,
         ws.amax_part);
-    resq_requant_kernel<<<(unsigned)slots, 256, 0, stream>>>(ws.r_s, units, ws.tile_start,
-                                                             ws.amax_part, k, r_codes, r_scales,
-                                                             r_global);
+    resq_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start,
+                                                              ws.amax_part, k, r_codes, r_scales,
+                                                              r_global);
   }
   return hipGetLastError();
 }

@@ -45,6 +45,7 @@ __global__ __launch_bounds__(256) void qdq_amax_kernel(const __bf16* __restrict_
   }
 }
 
+// grid: x over the matrix's 16-blocks (grid-stride), y = matrix in the group
 __global__ __launch_bounds__(256) void qdq_kernel(const __bf16* __restrict__ w, int64_t N, int64_t K,
                                                   const float* __restrict__ amax,
                                                   __bf16* __restrict__ w_qdq, uint8_t* __restrict__ codes,
@@ -54,36 +55,42 @@ __global__ __launch_bounds__(256) void qdq_kernel(const __bf16* __restrict__ w, 
   const double six_g = 6.0 * (double)g;
   if (g_out && blockIdx.x == 0 && threadIdx.x == 0) g_out[mat] = g;
   const int64_t nb = N * (K / kBlock);                  // blocks in this matrix
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (b >= nb) return;
-  const int64_t base = mat * N * K + b * kBlock;        // blocks are contiguous in row-major order
-  const u32x4* src = reinterpret_cast<const u32x4*>(w + base);
-  u32x4 a = src[0], c = src[1];
-  float v[16];
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t base = mat * N * K + b * kBlock;      // blocks are contiguous in row-major order
+    const u32x4* src = reinterpret_cast<const u32x4*>(w + base);
+    u32x4 a = src[0], c = src[1];
+    float v[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    v[2 * i] = bf16_lo(a[i]);
-    v[2 * i + 1] = bf16_hi(a[i]);
-    v[8 + 2 * i] = bf16_lo(c[i]);
-    v[8 + 2 * i + 1] = bf16_hi(c[i]);
-  }
-  uint32_t sb, w0, w1;
-  const float S = quantize_block16(v, g, six_g, &sb, &w0, &w1);
-  u32x4 o0, o1;
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_lo(a[i]);
+      v[2 * i + 1] = bf16_hi(a[i]);
+      v[8 + 2 * i] = bf16_lo(c[i]);
+      v[8 + 2 * i + 1] = bf16_hi(c[i]);
+    }
+    uint32_t sb, w0, w1;
+    const float S = quantize_block16(v, g, six_g, &sb, &w0, &w1);
+    u32x4 o0, o1;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t c0 = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 15u;
-    const uint32_t c1 = ((i < 4 ? w0 : w1) >> (8 * (i & 3) + 4)) & 15u;
-    const uint32_t lo = f32_to_bf16_rne(dq(c0, S)), hi = f32_to_bf16_rne(dq(c1, S));
-    const uint32_t word = lo | (hi << 16);
-    if (i < 4) o0[i] = word; else o1[i - 4] = word;
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t c0 = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 15u;
+      const uint32_t c1 = ((i < 4 ? w0 : w1) >> (8 * (i & 3) + 4)) & 15u;
+      const uint32_t lo = f32_to_bf16_rne(dq(c0, S)), hi = f32_to_bf16_rne(dq(c1, S));
+      const uint32_t word = lo | (hi << 16);
+      if (i < 4) o0[i] = word; else o1[i - 4] = word;
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(w_qdq + base);
+    dst[0] = o0;
+    dst[1] = o1;
+    if (codes) *reinterpret_cast<u32x2*>(codes + base / 2) = u32x2{w0, w1};
+    if (scales) scales[base / kBlock] = (uint8_t)sb;
   }
-  u32x4* dst = reinterpret_cast<u32x4*>(w_qdq + base);
-  dst[0] = o0;
-  dst[1] = o1;
-  if (codes) *reinterpret_cast<u32x2*>(codes + base / 2) = u32x2{w0, w1};
-  if (scales) scales[base / kBlock] = (uint8_t)sb;
 }
+
+// All matrices in one amax launch, then one quantize launch (smaller groups,
+// which would let the second read hit the MALL, measured slower: the launch
+// count grows faster than the re-read shrinks).
+constexpr int64_t kQdqGroupBytes = 1ll << 62;
 
 hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
                       uint8_t* codes, uint8_t* scales, float* g, float* ws_amax,
@@ -91,12 +98,22 @@ hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf1
   hipError_t err = launch_fill_f32(ws_amax, nmat, 0.0f, stream);
   if (err != hipSuccess) return err;
   const int64_t per_mat = N * K;
-  int64_t gx = (per_mat / 8 + 255) / 256;
-  gx = gx > 256 ? 256 : (gx < 1 ? 1 : gx);
-  qdq_amax_kernel<<<dim3((unsigned)gx, (unsigned)nmat), 256, 0, stream>>>(w, per_mat, ws_amax);
+  int64_t group = kQdqGroupBytes / (per_mat * 2);
+  group = group < 1 ? 1 : (group > 65535 ? 65535 : group);
   const int64_t nb = N * (K / kBlock);
-  qdq_kernel<<<dim3((unsigned)((nb + 255) / 256), (unsigned)nmat), 256, 0, stream>>>(
-      w, N, K, ws_amax, w_qdq, codes, scales, g);
+  for (int64_t m0 = 0; m0 < nmat; m0 += group) {
+    const int64_t gm = nmat - m0 < group ? nmat - m0 : group;
+    int64_t ga = (per_mat / 8 + 255) / 256;              // about 4096 workgroups in all
+    ga = ga > 4096 / gm + 1 ? 4096 / gm + 1 : (ga < 1 ? 1 : ga);
+    qdq_amax_kernel<<<dim3((unsigned)ga, (unsigned)gm), 256, 0, stream>>>(w + m0 * per_mat, per_mat,
+                                                                           ws_amax + m0);
+    int64_t gq = (nb + 255) / 256;                       // about 16384 workgroups in all
+    gq = gq > 16384 / gm + 1 ? 16384 / gm + 1 : gq;
+    qdq_kernel<<<dim3((unsigned)gq, (unsigned)gm), 256, 0, stream>>>(
+        w + m0 * per_mat, N, K, ws_amax + m0, w_qdq + m0 * per_mat,
+        codes ? codes + m0 * per_mat / 2 : nullptr, scales ? scales + m0 * per_mat / kBlock : nullptr,
+        g ? g + m0 : nullptr);
+  }
   return hipGetLastError();
 }
 
@@ -115,16 +132,17 @@ __device__ __forceinline__ float level_of(int si) {      // value of signed inde
 
 template <typename T>
 __global__ __launch_bounds__(256) void guided_kernel(
-    const T* __restrict__ x, int64_t M, int64_t K, int64_t ldx, const uint8_t* __restrict__ roll_codes,
+    const T* __restrict__ x, uint32_t M, uint32_t K, int64_t ldx, const uint8_t* __restrict__ roll_codes,
     const uint8_t* __restrict__ roll_scales, const float* __restrict__ roll_global,
     uint8_t* __restrict__ guided, __bf16* __restrict__ x_fq, unsigned long long* __restrict__ hist) {
-  const int64_t nb = K / kBlock;
-  const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t nb = K / kBlock;
+  const uint32_t total = M * nb;
+  const float g_roll = *roll_global;
   uint32_t h0 = 0, h1 = 0, h2 = 0;
-  if (b < M * nb) {
-    const int64_t r = b / nb, bc = b % nb;
+  for (uint32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < total; b += gridDim.x * blockDim.x) {
+    const uint32_t r = b / nb, bc = b - r * nb;
     float v[16];
-    const T* src = x + r * ldx + bc * kBlock;
+    const T* src = x + (int64_t)r * ldx + bc * kBlock;
     if constexpr (sizeof(T) == 2) {
       const u32x4* q = reinterpret_cast<const u32x4*>(src);
       u32x4 a = q[0], c = q[1];
@@ -143,20 +161,18 @@ __global__ __launch_bounds__(256) void guided_kernel(
         v[4 * i] = a[0]; v[4 * i + 1] = a[1]; v[4 * i + 2] = a[2]; v[4 * i + 3] = a[3];
       }
     }
-    const float S = e4m3_value(roll_scales[r * nb + bc]) * *roll_global;
+    const float S = e4m3_value(roll_scales[b]) * g_roll;
     // round-to-nearest codes under S (fast path, exact fallback)
     uint32_t w0, w1;
-    bool ok = S >= 0x1p-100f;
-    if (ok) {
+    if (S >= 0x1p-100f) {
       const float inv = __builtin_amdgcn_rcpf(S);
-      ok = e2m1_pack8_fast(v, inv, &w0);
-      ok = e2m1_pack8_fast(v + 8, inv, &w1) && ok;
-    }
-    if (!ok) {
+      w0 = e2m1_pack8_fast(v, inv, S);
+      w1 = e2m1_pack8_fast(v + 8, inv, S);
+    } else {
       w0 = e2m1_pack8_exact(v, S);
       w1 = e2m1_pack8_exact(v + 8, S);
     }
-    const u32x2 rw = *reinterpret_cast<const u32x2*>(roll_codes + r * (K / 2) + bc * 8);
+    const u32x2 rw = *reinterpret_cast<const u32x2*>(roll_codes + (int64_t)b * 8);
     uint32_t g0 = 0, g1 = 0;
     uint32_t fq[8];
 #pragma unroll
@@ -185,21 +201,28 @@ __global__ __launch_bounds__(256) void guided_kernel(
         if (j & 1) fq[j >> 1] |= hb << 16; else fq[j >> 1] = hb;
       }
     }
-    *reinterpret_cast<u32x2*>(guided + r * (K / 2) + bc * 8) = u32x2{g0, g1};
+    *reinterpret_cast<u32x2*>(guided + (int64_t)b * 8) = u32x2{g0, g1};
     if (x_fq) {
-      u32x4* dst = reinterpret_cast<u32x4*>(x_fq + r * K + bc * kBlock);
+      u32x4* dst = reinterpret_cast<u32x4*>(x_fq + (int64_t)b * kBlock);
       dst[0] = u32x4{fq[0], fq[1], fq[2], fq[3]};
       dst[1] = u32x4{fq[4], fq[5], fq[6], fq[7]};
     }
   }
-  if (hist) {
+  if (hist) {                                // one atomic per bin per workgroup
+    __shared__ uint32_t sh[3][4];
     h0 = wave_sum_u32(h0);
     h1 = wave_sum_u32(h1);
     h2 = wave_sum_u32(h2);
     if ((threadIdx.x & 63) == 0) {
-      if (h0) atomicAdd(hist + 0, (unsigned long long)h0);
-      if (h1) atomicAdd(hist + 1, (unsigned long long)h1);
-      if (h2) atomicAdd(hist + 2, (unsigned long long)h2);
+      sh[0][threadIdx.x >> 6] = h0;
+      sh[1][threadIdx.x >> 6] = h1;
+      sh[2][threadIdx.x >> 6] = h2;
+    }
+    __syncthreads();
+    if (threadIdx.x < 3) {
+      unsigned long long t = 0;
+      for (int w = 0; w < (int)(blockDim.x >> 6); ++w) t += sh[threadIdx.x][w];
+      if (t) atomicAdd(hist + threadIdx.x, t);
     }
   }
 }
@@ -216,15 +239,16 @@ hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t
   if (h) zero_i64_kernel<<<1, 64, 0, stream>>>(h, 3);
   const int64_t nb = M * (K / kBlock);
   if (nb == 0) return hipGetLastError();
-  const unsigned grid = (unsigned)((nb + 255) / 256);
+  int64_t grid = (nb + 255) / 256;
+  if (grid > 2048) grid = 2048;
   if (dtype == 0)
-    guided_kernel<__bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16*>(x), M, K, ldx,
-                                                    roll_codes, roll_scales, roll_global, guided,
-                                                    x_fq, h);
+    guided_kernel<__bf16><<<(unsigned)grid, 256, 0, stream>>>(
+        static_cast<const __bf16*>(x), (uint32_t)M, (uint32_t)K, ldx, roll_codes, roll_scales,
+        roll_global, guided, x_fq, h);
   else
-    guided_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), M, K, ldx,
-                                                   roll_codes, roll_scales, roll_global, guided,
-                                                   x_fq, h);
+    guided_kernel<float><<<(unsigned)grid, 256, 0, stream>>>(
+        static_cast<const float*>(x), (uint32_t)M, (uint32_t)K, ldx, roll_codes, roll_scales,
+        roll_global, guided, x_fq, h);
   return hipGetLastError();
 }
 

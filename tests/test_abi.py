@@ -100,6 +100,7 @@ def test_gemm_validation(lib):
     assert call(sel=FAKE, kc=64, rg=None, rc=FAKE, rs=FAKE) == -1
     assert call(epi=1, N=255) == -1
     assert call(epi=2) == -1 and "scatter" in err(lib)
+    assert call(epi=2, rw=FAKE, si=FAKE, out_rows=64) == -3 and "workspace" in err(lib)
     assert call(epi=9) == -1
     assert call(ldo=100) == -1
     assert call(out=None) == -1

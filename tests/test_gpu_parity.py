@@ -293,3 +293,74 @@ def test_guided_round(gpu_lib, rel):
     assert np.array_equal(npu8(gc), gc_r)
     assert np.array_equal(fq.cpu().view(torch.int16).numpy().view(np.uint16), fq_r)
     assert np.array_equal(hist.cpu().numpy(), hist_r)
+
+
+@pytest.mark.parametrize("tokens,n_exp,top_k,zipf", [
+    (600, 2, 2, 0.0),     # 600 rows per expert: 256-row tiles
+    (300, 4, 2, 0.5),     # 150 rows per expert: 128-row tiles
+    (200, 8, 3, 1.0),     # 75 rows per expert: 64-row tiles
+    (64, 16, 4, 0.0),     # 16 rows per expert: 32-row tiles
+])
+def test_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
+    """Every tile shape of the grouped GEMM (chosen from the average rows per
+    expert) against the reference, with compensation, F32 and SwiGLU epilogues,
+    K = 320 (a K-step count that is not a power of two) and N = 2 x 160 (a
+    partial N tile)."""
+    P = gpu_lib
+    hidden, inter, k = 320, 160, 32
+    x, rt, offs, wgu, _ = _moe_setup(P, tokens, hidden, n_exp, inter, k, seed=21, zipf=zipf,
+                                     top_k=top_k)
+    xc = x.cuda()
+    rows = int(offs[-1])
+    offs_t = torch.from_numpy(offs).cuda()
+    slot_tok = torch.from_numpy(rt["slot_token"]).cuda()
+    codes, scales, g, _ = P.nvfp4_quantize(xc)
+    sel, rc, rs, rg = P.resq_select_and_requant(xc, codes, scales, g, k, unit_offsets=offs_t,
+                                                rows_total=rows, row_index=slot_tok)
+    gc, gs, gg = _quant_weights(P, wgu)
+    comp = dict(sel_idx=sel, r_codes=rc, r_scales=rs, r_global=rg)
+    gu = P.moe_w4a4_grouped_gemm(codes, scales, g, offs_t, rows, gc, gs, gg, a_row_index=slot_tok,
+                                 **comp)
+    h = P.moe_w4a4_grouped_gemm(codes, scales, g, offs_t, rows, gc, gs, gg, a_row_index=slot_tok,
+                                epilogue=P.EPI_SWIGLU_BF16, **comp)
+    gu_ref, h_ref = OG.moe_gate_up(npu8(codes), npu8(scales), np32(g)[0], rt["slot_token"], offs,
+                                   npu8(gc), npu8(gs), np32(gg), inter, sel_idx=npu8(sel),
+                                   r_codes=npu8(rc), r_scales=npu8(rs), r_g=np32(rg))
+    gu_np = np32(gu)
+    for e in range(n_exp):
+        a, b = offs[e], offs[e + 1]
+        if a < b:
+            assert rel_err(gu_np[a:b], gu_ref[a:b]) <= GEMM_TOL, f"expert {e}"
+    h_r = F.bf16_bits_to_f32(h_ref)
+    tol = np.abs(h_r) * 2.0 ** -7 + GEMM_TOL * np.abs(h_r).max()
+    assert np.all(np.abs(np32(h) - h_r) <= tol)
+
+
+def test_scatter_add_fixed_order_and_ragged_n(gpu_lib):
+    """Scatter-add epilogue: each output row receives its rows in increasing
+    row order on top of the caller's initial values, for an N that is not a
+    multiple of 4; two runs are bit-identical."""
+    P = gpu_lib
+    tokens, hidden, n_exp, inter = 96, 100, 5, 64
+    rng = np.random.default_rng(3)
+    h = torch.from_numpy(rng.standard_normal((tokens * 3, inter)).astype(np.float32)).to(torch.bfloat16)
+    rt = synth.route(tokens, n_exp, seed=13, top_k=3)
+    offs = rt["offsets"]
+    rows = int(offs[-1])
+    wd = synth.weights(n_exp, hidden, inter, seed=13, tensor_id=synth.WD_ID)
+    hc, hs, hg, _ = P.nvfp4_quantize(h.cuda())
+    dc, ds, dg = _quant_weights(P, wd)
+    y0 = torch.from_numpy(rng.standard_normal((tokens, hidden)).astype(np.float32))
+    outs = []
+    for _ in range(2):
+        y = y0.clone().cuda()
+        P.moe_w4a4_grouped_gemm(hc, hs, hg, torch.from_numpy(offs).cuda(), rows, dc, ds, dg,
+                                epilogue=P.EPI_SCATTER_ADD_F32,
+                                row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
+                                scatter_index=torch.from_numpy(rt["slot_token"]).cuda(), out=y)
+        outs.append(np32(y))
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    y_ref = y0.numpy().astype(np.float64) + OG.moe_down(
+        npu8(hc), npu8(hs), np32(hg)[0], offs, npu8(dc), npu8(ds), np32(dg), rt["slot_token"],
+        rt["slot_weight"], tokens)
+    assert rel_err(outs[0], y_ref) <= GEMM_TOL
