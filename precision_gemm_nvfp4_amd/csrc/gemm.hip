@@ -8,14 +8,16 @@
 //           + gR gW sum_j (q s_q)[r, j] (w s_w)[n, sel[j]]
 //
 // How the NVFP4 scales are applied (gfx950).  An element's value is
-// e2m1 * e4m3 * g.  e2m1 * e4m3 has at most 6 significant bits: exact in bf16,
-// not in FP8 (4 bits), and the block-scaled FP4 MFMA takes one power-of-two
-// scale per 32 elements, not an E4M3 per 16.  So the operands stay NVFP4 in
-// memory and in LDS, and each wave dequantizes its own MFMA fragments in
-// registers right before use: the hardware FP4 -> fp32 convert, one multiply
-// by the block's E4M3 scale (exact), one byte permute to bf16.  The MFMA is
-// v_mfma_f32_32x32x16_bf16 with fp32 accumulation; the global scales gA gW
-// (gR gW) are applied in the epilogue.
+// e2m1 * e4m3 * g.  e2m1 * e4m3 has at most 6 significant bits and lies in
+// [2^-10, 2688]: exact in fp16 (and bf16), not in FP8 (4 bits), and the
+// block-scaled FP4 MFMA takes one power-of-two scale per 32 elements, not an
+// E4M3 per 16.  So the operands stay NVFP4 in memory and in LDS, and each wave
+// dequantizes its own MFMA fragments in registers right before use: the
+// hardware FP4 -> fp16 convert (two elements per instruction) and one packed
+// fp16 multiply by the block's E4M3 scale (itself converted to fp16 by the
+// hardware FP8 -> fp16 convert), both exact.  The MFMA is
+// v_mfma_f32_32x32x16_f16 with fp32 accumulation (the same rate as bf16);
+// the global scales gA gW (gR gW) are applied in the epilogue.
 //
 // K order inside a 32-wide K-step: in both MFMA substeps, lane half h (lanes
 // 32h .. 32h+31) supplies the 16 consecutive k of NVFP4 block h of the step
@@ -23,18 +25,27 @@
 // scale byte give a lane a whole block.  A and B use the same order, so the
 // sum over the step's 32 k is unchanged.
 //
-// Pipeline: LDS holds three stages of raw codes + scales (9 KB per stage for a
-// 256 x 256 tile); global loads run two steps ahead in a double register set;
-// one barrier per step.
+// Pipeline: LDS holds two stages of raw codes + scales (9 KB per stage for a
+// 256 x 256 tile); global loads run two K-steps ahead in a double register
+// set.  In step s each wave issues its MFMAs of step s one at a time, and
+// between them (fenced groups, so the order survives scheduling) the LDS
+// reads of its step s+1 fragments, the stage write of step s+2, the global
+// loads of step s+4 and the dequantization of the step s+1 fragments, half a
+// fragment per MFMA.  One barrier per step.  On gfx950 a SIMD does not run
+// VALU instructions while an MFMA executes, so the dequantization adds to the
+// MFMA time (about 4.5 VALU instructions per MFMA for a 128 x 128 wave tile);
+// the schedule keeps the MFMA pipe from also waiting on LDS or memory.
 //
 // The compensation term is an extra chunk of kc: while the main loop streams
 // the expert's weight tile through LDS, the elements of the selected columns
-// are dequantized into a bf16 [BN, kc] buffer, so W is read from memory once.
+// are dequantized into an fp16 [BN, kc] buffer, so W is read from memory once.
 // After the main loop the accumulators are rescaled by gA/gR, Q(R_S) x W_S is
 // accumulated, and the epilogue multiplies by gR gW.
 //
-// Scatter epilogue: row_weight * Y rows are stored (plain, coalesced) into the
-// workspace and combine.hip adds them into the output rows in a fixed order.
+// Epilogues (gemm_common.h) stage each wave's 32-row blocks through LDS and
+// write whole row segments with 16-byte stores.  Scatter epilogue:
+// row_weight * Y rows go into the workspace and combine.hip adds them into
+// the output rows in a fixed order.
 //
 // Work decomposition: the logical tiles are the (expert, n-tile, m-tile)
 // triples of the ragged groups, expert-major, then n-tile, m-tile innermost
@@ -45,13 +56,12 @@
 // on it (the weight tile is read once), and the expert's activation rows stay
 // in its L2 across the n-tiles.  Four waves per workgroup; each wave owns
 // MI x NJ MFMA blocks of 32 x 32.
-#include "device_common.h"
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace nvfp4 {
 
 constexpr int BN = 256, BK = 32;
-constexpr int NSTAGE = 3;                   // LDS stages of raw NVFP4 tiles
+constexpr int NSTAGE = 2;                   // LDS stages of raw NVFP4 tiles
 constexpr int MAX_KC = 128;                 // largest compensated channel count handled
 
 struct RowLoad {                            // one row's K-step: 32 codes + 2 scale bytes
@@ -59,102 +69,68 @@ struct RowLoad {                            // one row's K-step: 32 codes + 2 sc
   uint32_t scales;
 };
 
-// Two bf16x8 fragments (substeps 0 and 1) from 16 codes (8 bytes) and a scale.
-__device__ __forceinline__ void dequant16(u32x2 c, float s, bf16x8& f0, bf16x8& f1) {
-  float f[16];
-  e2m1_unpack8(c[0], f);
-  e2m1_unpack8(c[1], f + 8);
-  u32x4 o0, o1;
-#pragma unroll
-  for (int b = 0; b < 4; ++b) {
-    o0[b] = __builtin_amdgcn_perm(__float_as_uint(f[2 * b + 1] * s), __float_as_uint(f[2 * b] * s),
-                                  0x07060302u);
-    o1[b] = __builtin_amdgcn_perm(__float_as_uint(f[8 + 2 * b + 1] * s),
-                                  __float_as_uint(f[8 + 2 * b] * s), 0x07060302u);
-  }
-  f0 = __builtin_bit_cast(bf16x8, o0);
-  f1 = __builtin_bit_cast(bf16x8, o1);
+// The E4M3 scale byte b (bits 0..7 of the argument) as fp16 in both halves.
+__device__ __forceinline__ f16x2 e4m3_f16x2(uint32_t b) {
+  const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
+  return f16x2{v[0], v[0]};
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
-
-__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
-  return v < lo ? lo : (v > hi ? hi : v);
+// Two fp16x8 fragments (substeps 0 and 1) from 16 codes (8 bytes) and the
+// block scale s: element i is the code of nibble i (low nibble first).
+__device__ __forceinline__ void dequant16(u32x2 c, f16x2 s, f16x8& f0, f16x8& f1) {
+#define NVFP4_CVT(w, sel) (__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w), 1.0f, (sel)) * s)
+  const f16x2 v0 = NVFP4_CVT(c[0], 0), v1 = NVFP4_CVT(c[0], 1), v2 = NVFP4_CVT(c[0], 2),
+              v3 = NVFP4_CVT(c[0], 3), v4 = NVFP4_CVT(c[1], 0), v5 = NVFP4_CVT(c[1], 1),
+              v6 = NVFP4_CVT(c[1], 2), v7 = NVFP4_CVT(c[1], 3);
+#undef NVFP4_CVT
+  f0 = f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+  f1 = f16x8{v4[0], v4[1], v5[0], v5[1], v6[0], v6[1], v7[0], v7[1]};
 }
+
+// One fp16x8 fragment half from 8 codes (4 bytes) and the block scale.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s) {
+#define NVFP4_CVT(sel) (__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, (sel)) * s)
+  const f16x2 v0 = NVFP4_CVT(0), v1 = NVFP4_CVT(1), v2 = NVFP4_CVT(2), v3 = NVFP4_CVT(3);
+#undef NVFP4_CVT
+  return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+// LDS layout of one pipeline stage for a BM-row A tile and the BN-row W tile.
+template <int BM>
+struct StageLayout {
+  static constexpr int AR = BM < 256 ? BM + 1 : BM;
+  static constexpr int A_CODES = 0;
+  static constexpr int A_SC = AR * 16;
+  static constexpr int B_CODES = (A_SC + AR * 2 + 15) / 16 * 16;
+  static constexpr int B_SC = B_CODES + BN * 16;
+  static constexpr int BYTES = (B_SC + BN * 2 + 15) / 16 * 16;
+};
 
 template <int MI, int NJ, int WM, int WN>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles, int total) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
   static_assert(WM * WN == 4, "four waves");
-  // LDS: NSTAGE x {A codes [BM][16 B], A scales [BM][2 B], B codes [BN][16 B],
-  // B scales [BN][2 B]}, then the bf16 W_S buffer, the selected channels and
-  // their K-step ranges.
-  constexpr int A_CODES = 0, A_SC = BM * 16, B_CODES = A_SC + BM * 2, B_SC = B_CODES + BN * 16;
-  constexpr int STAGE = B_SC + BN * 2;
+  // LDS: NSTAGE x {A codes [AR][16 B], A scales [AR][2 B], B codes [BN][16 B],
+  // B scales [BN][2 B]}, then the fp16 W_S buffer, the selected channels and
+  // their K-step ranges.  AR = BM + 1 when BM < 256: threads past BM write
+  // their A data into the spare row, so staging has no branch.
+  using L = StageLayout<BM>;
+  constexpr int A_CODES = L::A_CODES, A_SC = L::A_SC, B_CODES = L::B_CODES, B_SC = L::B_SC;
+  constexpr int STAGE = L::BYTES;
+  static_assert(4 * BM * 18 <= NSTAGE * STAGE, "compensation chunks fit in the stages");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __bf16* WS = reinterpret_cast<__bf16*>(smem + NSTAGE * STAGE);    // [BN][ws_stride]
-  __shared__ int32_t sh_e, sh_mt, sh_nt;
-  __shared__ uint32_t sh_waves[4];
+  _Float16* WS = reinterpret_cast<_Float16*>(smem + NSTAGE * STAGE);   // [BN][ws_stride]
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
-  // ---- logical tile of this workgroup (XCD-contiguous ranges) --------------
-  // Logical tiles are ordered expert by expert; inside an expert's block of
-  // cnt_e * ntiles tiles, n-tile major and m-tile minor, so the m-tiles that
-  // share a weight tile run together on one XCD.  Expert e's block starts at
-  // tile_start_e * ntiles, where tile_start_e counts the m-tiles of experts < e.
-  const int per_xcd = (total + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (logical >= total) return;
-  const int m_key = logical / ntiles;        // lies inside expert e's m-tile range
-
-  if (tid == 0) sh_e = -1;
-  __syncthreads();
-  {
-    uint32_t carry = 0;
-    for (int base = 0; base < p.E; base += 256) {
-      const int e = base + tid;
-      int64_t rb = 0, re = 0;
-      if (e < p.E) {
-        rb = clamp64(p.group_offsets[e], 0, p.rows_total);
-        re = clamp64(p.group_offsets[e + 1], rb, p.rows_total);
-      }
-      const uint32_t n = (uint32_t)((re - rb + BM - 1) / BM);
-      uint32_t inc = n;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        uint32_t t = __shfl_up(inc, o, 64);
-        if (lane >= o) inc += t;
-      }
-      if (lane == 63) sh_waves[wave] = inc;
-      __syncthreads();
-      uint32_t before = carry, tot = 0;
-      for (int w = 0; w < 4; ++w) {
-        if (w < wave) before += sh_waves[w];
-        tot += sh_waves[w];
-      }
-      before += inc - n;
-      if (e < p.E && (uint32_t)m_key >= before && (uint32_t)m_key < before + n) {
-        const int off = logical - (int)before * ntiles;   // position inside the expert's block
-        sh_e = e;
-        sh_nt = off / (int)n;
-        sh_mt = off % (int)n;
-      }
-      carry += tot;
-      __syncthreads();
-    }
-  }
-  const int e = sh_e;
-  if (e < 0) return;
-  const int n_tile = sh_nt;
-  const int64_t g0 = clamp64(p.group_offsets[e], 0, p.rows_total);
-  const int64_t g1 = clamp64(p.group_offsets[e + 1], g0, p.rows_total);
-  const int64_t row0 = g0 + (int64_t)sh_mt * BM;            // first unit row of the tile
-  const int rows_valid = (int)((g1 - row0) < BM ? (g1 - row0) : BM);
+  const TileCoord tc = find_tile<BM>(p, ntiles, total);
+  if (tc.e < 0) return;
+  const int e = tc.e, n_tile = tc.n_tile, rows_valid = tc.rows_valid;
+  const int64_t row0 = tc.row0;
 
   const int64_t K = p.K;
   const int nsteps = (int)(K / BK);
@@ -165,8 +141,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   int32_t* sel = reinterpret_cast<int32_t*>(WS + (comp ? BN * ws_stride : 0));   // [MAX_KC]
   int32_t* jr = sel + MAX_KC;                                                   // [nsteps + 1]
 
-  const bool swiglu = p.epilogue == 1;
-  const int64_t inter = p.N / 2;
 
   // ---- this thread's rows: A row tid (if < BM), W row tid ------------------
   // Loads are branch-free: a row outside the tile reads row 0 of its operand
@@ -182,22 +156,17 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   }
   const uint8_t* a_cp = p.a_codes + ar * (K / 2);
   const uint8_t* a_sp = p.a_scales + ar * (K / 16);
-  int64_t b_row;
-  if (swiglu) {                               // LDS row r: 32-row groups alternate gate / up
-    const int q = tid >> 5;
-    const int64_t i = (int64_t)n_tile * (BN / 2) + (q >> 1) * 32 + (tid & 31);
-    b_row = i < inter ? ((q & 1) ? inter + i : i) : -1;
-  } else {
-    const int64_t n = (int64_t)n_tile * BN + tid;
-    b_row = n < p.N ? n : -1;
-  }
+  const int64_t b_row = weight_row<BN>(p, n_tile, tid);
   const bool b_ok = b_row >= 0;
   const uint8_t* b_cp = p.w_codes + ((int64_t)e * p.N + (b_ok ? b_row : 0)) * (K / 2);
   const uint8_t* b_sp = p.w_scales + ((int64_t)e * p.N + (b_ok ? b_row : 0)) * (K / 16);
-  const uint32_t a_mask = a_ok ? 0xFFFFFFFFu : 0u, b_mask = b_ok ? 0xFFFFFFFFu : 0u;
+  // A row outside the tile or with an index outside [0, a_rows) gets zero
+  // scales (so it reads as zeros); a W row past N keeps row 0's data: those
+  // output columns are never stored.
+  const uint32_t a_mask = a_ok ? 0xFFFFu : 0u;
 
   auto load_step = [&](int s, RowLoad& ta, RowLoad& tb) {
-    ta.codes = *reinterpret_cast<const u32x4*>(a_cp + s * (BK / 2));   // masked when staged
+    ta.codes = *reinterpret_cast<const u32x4*>(a_cp + s * (BK / 2));
     ta.scales = *reinterpret_cast<const uint16_t*>(a_sp + s * (BK / 16));
     tb.codes = *reinterpret_cast<const u32x4*>(b_cp + s * (BK / 2));
     tb.scales = *reinterpret_cast<const uint16_t*>(b_sp + s * (BK / 16));
@@ -205,11 +174,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 
   auto stage_write = [&](int st, const RowLoad& ta, const RowLoad& tb) {
     unsigned char* base = smem + st * STAGE;
-    if (tid < BM) {
-      *reinterpret_cast<u32x4*>(base + A_CODES + tid * 16) = ta.codes & a_mask;
-      *reinterpret_cast<uint16_t*>(base + A_SC + tid * 2) = (uint16_t)ta.scales;
-    }
-    *reinterpret_cast<u32x4*>(base + B_CODES + tid * 16) = tb.codes & b_mask;
+    const int a_slot = tid < BM ? tid : BM;                   // BM: the spare row
+    *reinterpret_cast<u32x4*>(base + A_CODES + a_slot * 16) = ta.codes;
+    *reinterpret_cast<uint16_t*>(base + A_SC + a_slot * 2) = (uint16_t)(ta.scales & a_mask);
+    *reinterpret_cast<u32x4*>(base + B_CODES + tid * 16) = tb.codes;
     *reinterpret_cast<uint16_t*>(base + B_SC + tid * 2) = (uint16_t)tb.scales;
   };
 
@@ -240,53 +208,68 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // One K-step from LDS stage st: each lane dequantizes its 16-element block of
-  // every fragment, then both substeps of MFMAs run.
-  auto compute_step = [&](int st) {
+  // A wave's dequantized fragments of one K-step: a0/b0 feed MFMA substep 0,
+  // a1/b1 substep 1.
+  struct Frags {
+    f16x8 a0[MI], a1[MI], b0[NJ], b1[NJ];
+  };
+  auto read_frags = [&](int st, Frags& f) {
     const unsigned char* base = smem + st * STAGE;
-    bf16x8 a0[MI], a1[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int r = wm * MI * 32 + i * 32 + l32;
       const u32x2 c = *reinterpret_cast<const u32x2*>(base + A_CODES + r * 16 + half * 8);
-      const float s = e4m3_value(base[A_SC + r * 2 + half]);
-      dequant16(c, s, a0[i], a1[i]);
+      dequant16(c, e4m3_f16x2(base[A_SC + r * 2 + half]), f.a0[i], f.a1[i]);
     }
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {            // one B fragment pair live at a time
+    for (int j = 0; j < NJ; ++j) {
       const int r = wn * NJ * 32 + j * 32 + l32;
       const u32x2 c = *reinterpret_cast<const u32x2*>(base + B_CODES + r * 16 + half * 8);
-      const float s = e4m3_value(base[B_SC + r * 2 + half]);
-      bf16x8 b0, b1;
-      dequant16(c, s, b0, b1);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0, acc[i][j], 0, 0, 0);
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1, acc[i][j], 0, 0, 0);
+      dequant16(c, e4m3_f16x2(base[B_SC + r * 2 + half]), f.b0[j], f.b1[j]);
     }
   };
+  auto mfma_step = [&](const Frags& f) {
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a0[i], f.b0[j], acc[i][j], 0, 0, 0);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a1[i], f.b1[j], acc[i][j], 0, 0, 0);
+  };
 
-  // W columns of sel inside K-step s, from LDS stage st, dequantized into W_S.
+  // W elements of the selected channels inside K-step s (LDS stage st) into
+  // W_S: thread t handles weight row t of the tile, so the loop count is the
+  // same for every thread.
   auto gather_ws = [&](int s, int st) {
     const unsigned char* base = smem + st * STAGE;
-    const int j0 = jr[s], nj = jr[s + 1] - j0;
-    for (int i = tid; i < nj * BN; i += 256) {
-      const int n = i & (BN - 1), jj = j0 + (i >> 8);
+    const int j1 = jr[s + 1];
+    for (int jj = jr[s]; jj < j1; ++jj) {
       const int kk = sel[jj] - s * BK;                       // 0..31 inside the step
-      const uint32_t code = (base[B_CODES + n * 16 + (kk >> 1)] >> (4 * (kk & 1))) & 15u;
-      const float v = e2m1_value(code) * e4m3_value(base[B_SC + n * 2 + (kk >> 4)]);
-      reinterpret_cast<uint16_t*>(WS)[n * ws_stride + jj] = (uint16_t)(__float_as_uint(v) >> 16);
+      const uint32_t byte = base[B_CODES + tid * 16 + (kk >> 1)] >> (4 * (kk & 1));
+      const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(byte, 1.0f, 0);
+      const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(base[B_SC + tid * 2 + (kk >> 4)], 1.0f, false);
+      WS[tid * ws_stride + jj] = v[0] * sc[0];               // exact: see the header
     }
   };
 
-  // ---- main K loop: stage s%3 is read, stage (s+2)%3 written, loads 2 ahead --
-  // Every load is issued unconditionally (a step past the end re-reads the last
-  // step, and its stage is never read): with no path that skips a load, the
-  // compiler waits only for the older step's loads (vmcnt = 4), not for all.
-  // K is a multiple of 64, so nsteps is even and at least 2.
+  // ---- main K loop ----------------------------------------------------------
+  // Step s: MFMAs on the fragments of step s (registers), while the fragments
+  // of step s+1 are read from LDS stage (s+1)%2 and dequantized (and the
+  // selected W columns of step s+1 copied into W_S), the raw data of step s+2
+  // goes from registers into stage s%2 and the loads of step s+4 are issued.
+  // One barrier per step: it orders this step's writes of stage s%2 before
+  // the next step's reads of it, and this step's reads of stage (s+1)%2
+  // before the next step's writes.  Every load is issued unconditionally (a step past
+  // the end re-reads the last step; its stage is never read), so the compiler
+  // waits only for the older step's loads.  K is a multiple of 64, so nsteps
+  // is even and at least 2, and the loop, unrolled by two, sees each stage at
+  // a fixed LDS offset.
   RowLoad ra[2], rb[2];
+  Frags fr[2];
   const int last = nsteps - 1;
   load_step(0, ra[0], rb[0]);
   load_step(1, ra[1], rb[1]);
@@ -296,20 +279,79 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   __builtin_amdgcn_sched_barrier(0);          // keep the loop's load order in the prologue
   load_step(3 < last ? 3 : last, ra[1], rb[1]);
   lds_barrier();
-  auto step = [&](int s, RowLoad& ta, RowLoad& tb) {
-    const int st = s % NSTAGE;
-    compute_step(st);
-    stage_write((s + 2) % NSTAGE, ta, tb);                    // data of step s+2
-    load_step(s + 4 < last ? s + 4 : last, ta, tb);
-    if (comp) gather_ws(s, st);
-    lds_barrier();
+  read_frags(0, fr[0]);
+  if (comp) gather_ws(0, 0);
+
+  // One K-step in issue order: the MFMAs of this step one at a time, and
+  // between them (each group fenced off from the scheduler) the rest of the
+  // step's work: the LDS reads of the next step's fragments right after MFMA
+  // 0, the stage writes after MFMA 1, the global loads after MFMA 2, and the
+  // dequantization of the next step's fragments, half a fragment (8 VALU
+  // instructions, about one MFMA's duration) per MFMA from MFMA kDeq0 on.
+  constexpr int kFr = MI + NJ;                // fragments per wave and step
+  constexpr int kMf = 2 * MI * NJ;            // MFMAs per wave and step
+  constexpr int kDeq0 = kMf > 8 ? 4 : 3;
+  auto step = [&](int s, int st, const Frags& cur, Frags& nxt, RowLoad& ta, RowLoad& tb) {
+    const unsigned char* nb = smem + (st ^ 1) * STAGE;       // stage of step s+1
+    u32x2 rc[kFr];
+    uint32_t rs[kFr];
+    f16x2 sc[kFr];
+#pragma unroll
+    for (int m = 0; m < kMf; ++m) {
+      __builtin_amdgcn_sched_barrier(0);
+      {
+        const int sub = m / (MI * NJ), j = (m % (MI * NJ)) / MI, i = m % MI;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sub ? cur.a1[i] : cur.a0[i],
+                                                           sub ? cur.b1[j] : cur.b0[j],
+                                                           acc[i][j], 0, 0, 0);
+      }
+      if (m == 0) {
+#pragma unroll
+        for (int f = 0; f < kFr; ++f) {
+          const int r = f < MI ? wm * MI * 32 + f * 32 + l32 : wn * NJ * 32 + (f - MI) * 32 + l32;
+          const int co = f < MI ? A_CODES : B_CODES, so = f < MI ? A_SC : B_SC;
+          rc[f] = *reinterpret_cast<const u32x2*>(nb + co + r * 16 + half * 8);
+          rs[f] = nb[so + r * 2 + half];
+        }
+      }
+      if (m == 1) stage_write(st, ta, tb);                    // data of step s+2
+      if (m == 2) load_step(s + 4 < last ? s + 4 : last, ta, tb);
+      if (m >= kDeq0 || kMf <= kDeq0) {
+#pragma unroll
+        for (int hf = 0; hf < 2 * kFr; ++hf) {
+          const int at = kMf <= kDeq0 ? kMf - 1 : kDeq0 + hf * (kMf - kDeq0) / (2 * kFr);
+          if (at != m) continue;
+          const int f = hf >> 1, h = hf & 1;
+          // The empty asm statements fix this work to this slot: inputs pass
+          // through one before it (nothing is hoisted to its loads), outputs
+          // after it (nothing is sunk to its use).
+          uint32_t w = rc[f][h];
+          asm volatile("" : "+v"(w));
+          if (h == 0) {
+            uint32_t b = rs[f];
+            asm volatile("" : "+v"(b));
+            sc[f] = e4m3_f16x2(b);
+            asm volatile("" : "+v"(sc[f]));
+          }
+          f16x8 v = dequant8(w, sc[f]);
+          asm volatile("" : "+v"(v));
+          if (f < MI) {
+            if (h == 0) nxt.a0[f] = v; else nxt.a1[f] = v;
+          } else {
+            if (h == 0) nxt.b0[f - MI] = v; else nxt.b1[f - MI] = v;
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    if (comp && s + 1 < nsteps) gather_ws(s + 1, st ^ 1);
   };
-  int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    step(s, ra[0], rb[0]);
-    step(s + 1, ra[1], rb[1]);
+  for (int s = 0; s < nsteps; s += 2) {
+    step(s, 0, fr[0], fr[1], ra[0], rb[0]);
+    lds_barrier();
+    step(s + 1, 1, fr[1], fr[0], ra[1], rb[1]);
+    lds_barrier();
   }
-  if (s < nsteps) step(s, ra[0], rb[0]);
 
   // ---- compensation chunk ---------------------------------------------------
   float scale = *p.a_global * p.w_global[e];
@@ -323,95 +365,54 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = acc[i][j][q] * ratio;
     scale = gr * p.w_global[e];
-    for (int c = 0; c < kcp / BK; ++c) {
-      unsigned char* base = smem + (c & 1) * STAGE;
-      if (tid < BM) {                            // Q(R_S) row tid, compact columns c*32 ..
+    // Q(R_S) rows of the tile into LDS (chunk c of 32 compact channels at
+    // c * BM * 18 bytes: codes [BM][16 B], then scales [BM][2 B]; four chunks
+    // fit in the space of the three stages), all chunks before one barrier.
+    const int nchunk = kcp / BK;
+    if (tid < BM) {
+      const int64_t ur = row0 + tid;
+      const bool ok = tid < rows_valid;
+      for (int c = 0; c < nchunk; ++c) {
         u32x4 codes = u32x4{0, 0, 0, 0};
         uint32_t sc = 0;
-        if (tid < rows_valid) {
-          const int64_t ur = row0 + tid;
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            const int j = c * BK + q * 16;
-            if (j < kc) {
-              const u32x2 w = *reinterpret_cast<const u32x2*>(p.r_codes + ur * (kc / 2) + j / 2);
-              codes[2 * q] = w[0];
-              codes[2 * q + 1] = w[1];
-              sc |= (uint32_t)p.r_scales[ur * (kc / 16) + j / 16] << (8 * q);
-            }
+        for (int q = 0; q < 2; ++q) {
+          const int j = c * BK + q * 16;
+          if (ok && j < kc) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(p.r_codes + ur * (kc / 2) + j / 2);
+            codes[2 * q] = w[0];
+            codes[2 * q + 1] = w[1];
+            sc |= (uint32_t)p.r_scales[ur * (kc / 16) + j / 16] << (8 * q);
           }
         }
-        *reinterpret_cast<u32x4*>(base + A_CODES + tid * 16) = codes;
-        *reinterpret_cast<uint16_t*>(base + A_SC + tid * 2) = (uint16_t)sc;
+        unsigned char* base = smem + c * (BM * 18);
+        *reinterpret_cast<u32x4*>(base + tid * 16) = codes;
+        *reinterpret_cast<uint16_t*>(base + BM * 16 + tid * 2) = (uint16_t)sc;
       }
-      lds_barrier();
-      bf16x8 a0[MI], a1[MI], b0[NJ], b1[NJ];
+    }
+    lds_barrier();
+    for (int c = 0; c < nchunk; ++c) {
+      const unsigned char* base = smem + c * (BM * 18);
+      Frags f;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int r = wm * MI * 32 + i * 32 + l32;
-        const u32x2 cc = *reinterpret_cast<const u32x2*>(base + A_CODES + r * 16 + half * 8);
-        dequant16(cc, e4m3_value(base[A_SC + r * 2 + half]), a0[i], a1[i]);
+        const u32x2 cc = *reinterpret_cast<const u32x2*>(base + r * 16 + half * 8);
+        dequant16(cc, e4m3_f16x2(base[BM * 16 + r * 2 + half]), f.a0[i], f.a1[i]);
       }
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {            // W_S in the same K order: block half of the chunk
         const int r = wn * NJ * 32 + j * 32 + l32;
-        b0[j] = *reinterpret_cast<const bf16x8*>(WS + r * ws_stride + c * BK + half * 16);
-        b1[j] = *reinterpret_cast<const bf16x8*>(WS + r * ws_stride + c * BK + half * 16 + 8);
+        f.b0[j] = *reinterpret_cast<const f16x8*>(WS + r * ws_stride + c * BK + half * 16);
+        f.b1[j] = *reinterpret_cast<const f16x8*>(WS + r * ws_stride + c * BK + half * 16 + 8);
       }
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a0[i], b0[j], acc[i][j], 0, 0, 0);
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a1[i], b1[j], acc[i][j], 0, 0, 0);
-        }
+      mfma_step(f);
     }
   }
 
-  // ---- epilogue -------------------------------------------------------------
-  if (p.epilogue == 0 || p.epilogue == 2) {
-    float* out = static_cast<float*>(p.out);
-#pragma unroll
-    for (int i = 0; i < MI; ++i)
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int64_t n = (int64_t)n_tile * BN + wn * NJ * 32 + j * 32 + l32;
-        if (n >= p.N) continue;
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = wm * MI * 32 + i * 32 + (q >> 2) * 8 + half * 4 + (q & 3);
-          if (r >= rows_valid) continue;
-          const int64_t s2 = row0 + r;
-          const float y = acc[i][j][q] * scale;
-          if (p.epilogue == 0) out[s2 * p.ldo + n] = y;
-          else p.y_rows[s2 * p.N + n] = p.row_weight[s2] * y;   // added into out by the combine
-        }
-      }
-  } else {
-    // SwiGLU: block j (even) is gate, j+1 is up, for the same 32 channels
-    uint16_t* out = static_cast<uint16_t*>(p.out);
-    float m = 0.0f;
-#pragma unroll
-    for (int j = 0; j < NJ; j += 2) {
-      const int64_t ch = (int64_t)n_tile * (BN / 2) + wn * (NJ / 2) * 32 + (j / 2) * 32 + l32;
-      if (ch >= inter) continue;
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int r = wm * MI * 32 + i * 32 + (q >> 2) * 8 + half * 4 + (q & 3);
-          if (r >= rows_valid) continue;
-          const float gte = acc[i][j][q] * scale, up = acc[i][j + 1][q] * scale;
-          const uint32_t hb = f32_to_bf16_rne(silu_f32(gte) * up);
-          m = fmaxf(m, fabsf(__uint_as_float(hb << 16)));
-          out[(row0 + r) * p.ldo + ch] = (uint16_t)hb;
-        }
-    }
-    if (p.out_amax) {
-      m = wave_max(m);
-      if (lane == 0) atomic_max_nonneg(p.out_amax, m);
-    }
-  }
+  __syncthreads();                             // LDS free for the epilogue staging
+  gemm_epilogue<MI, NJ, BN>(p, acc, tc, wm * MI * 32, wn * NJ * 32, scale,
+                            reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>());
 }
 
 template <int MI, int NJ, int WM, int WN>
@@ -421,9 +422,11 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.epilogue == 1 ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const int64_t total = mtiles * ntiles;
   const int kcp = a.sel_idx ? (a.kc + BK - 1) / BK * BK : 0;
-  const size_t stage = (size_t)BM * 18 + (size_t)BN * 18;
-  const size_t lds = NSTAGE * stage + (a.sel_idx ? (size_t)BN * (kcp + 8) * 2 : 0) +
-                     (size_t)(MAX_KC + a.K / BK + 1) * 4;
+  const size_t stage = StageLayout<BM>::BYTES;
+  const size_t loop_lds = NSTAGE * stage + (a.sel_idx ? (size_t)BN * (kcp + 8) * 2 : 0) +
+                          (size_t)(MAX_KC + a.K / BK + 1) * 4;
+  const size_t epi_lds = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
+  const size_t lds = loop_lds > epi_lds ? loop_lds : epi_lds;
   auto kern = grouped_gemm_kernel<MI, NJ, WM, WN>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -448,7 +451,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   }
   if (a.rows_total == 0) return hipSuccess;
   hipError_t err;
-  switch (a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E)) {
+  const int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
+  switch (bm) {
     case 256: err = launch_cfg<4, 4, 2, 2>(a, stream); break;
     case 128: err = launch_cfg<2, 4, 2, 2>(a, stream); break;
     case 64: err = launch_cfg<1, 4, 2, 2>(a, stream); break;

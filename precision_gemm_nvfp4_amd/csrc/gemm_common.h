@@ -1,0 +1,206 @@
+// Pieces of the grouped GEMM kept apart from its main loop: the mapping of
+// workgroups to (expert, m-tile, n-tile), the weight-row order of a SwiGLU
+// tile, and the epilogues.
+#pragma once
+#include "device_common.h"
+#include "kernels.h"
+
+namespace nvfp4 {
+
+__device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
+  return v < lo ? lo : (v > hi ? hi : v);
+}
+
+__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+
+struct TileCoord {
+  int e;            // expert, -1: surplus workgroup
+  int n_tile;
+  int64_t row0;     // first unit row of the tile
+  int rows_valid;   // rows of the tile inside the expert's group
+};
+
+// Logical tile of this workgroup.  The logical tiles are the (expert, n-tile,
+// m-tile) triples of the ragged groups, expert by expert; inside an expert's
+// block of cnt_e * ntiles tiles n-tile major and m-tile minor, so the m-tiles
+// that share a weight tile run side by side.  Workgroup ids are dealt
+// round-robin to the 8 XCDs, so hardware id h runs logical tile
+// (h % 8) * ceil(total / 8) + h / 8: each XCD owns a contiguous range.
+// Called by all threads of a 256-thread workgroup.
+template <int BM>
+__device__ TileCoord find_tile(const GemmArgs& p, int ntiles, int total) {
+  __shared__ int32_t sh_e, sh_mt, sh_nt;
+  __shared__ uint32_t sh_waves[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  TileCoord t{-1, 0, 0, 0};
+  const int per_xcd = (total + 7) / 8;
+  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
+  if (logical >= total) return t;             // uniform over the workgroup
+  const int m_key = logical / ntiles;         // lies inside expert e's m-tile range
+  if (tid == 0) sh_e = -1;
+  __syncthreads();
+  uint32_t carry = 0;
+  for (int base = 0; base < p.E; base += 256) {
+    const int e = base + tid;
+    int64_t rb = 0, re = 0;
+    if (e < p.E) {
+      rb = clamp64(p.group_offsets[e], 0, p.rows_total);
+      re = clamp64(p.group_offsets[e + 1], rb, p.rows_total);
+    }
+    const uint32_t n = (uint32_t)((re - rb + BM - 1) / BM);
+    uint32_t inc = n;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      uint32_t u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) sh_waves[wave] = inc;
+    __syncthreads();
+    uint32_t before = carry, tot = 0;
+    for (int w = 0; w < 4; ++w) {
+      if (w < wave) before += sh_waves[w];
+      tot += sh_waves[w];
+    }
+    before += inc - n;
+    if (e < p.E && (uint32_t)m_key >= before && (uint32_t)m_key < before + n) {
+      const int off = logical - (int)before * ntiles;   // position inside the expert's block
+      sh_e = e;
+      sh_nt = off / (int)n;
+      sh_mt = off % (int)n;
+    }
+    carry += tot;
+    __syncthreads();
+  }
+  t.e = sh_e;
+  if (t.e < 0) return t;
+  t.n_tile = sh_nt;
+  const int64_t g0 = clamp64(p.group_offsets[t.e], 0, p.rows_total);
+  const int64_t g1 = clamp64(p.group_offsets[t.e + 1], g0, p.rows_total);
+  t.row0 = g0 + (int64_t)sh_mt * BM;
+  t.rows_valid = (int)((g1 - t.row0) < BM ? (g1 - t.row0) : BM);
+  return t;
+}
+
+// Weight row held at row r (0 .. BN-1) of an n-tile, or -1 past the end.
+// With SwiGLU the 32-row groups alternate gate / up for the same 32
+// channels, so a wave's column blocks j (gate) and j+1 (up) pair up.
+template <int BN>
+__device__ __forceinline__ int64_t weight_row(const GemmArgs& p, int n_tile, int r) {
+  if (p.epilogue == 1) {
+    const int64_t inter = p.N / 2;
+    const int q = r >> 5;
+    const int64_t i = (int64_t)n_tile * (BN / 2) + (q >> 1) * 32 + (r & 31);
+    return i < inter ? ((q & 1) ? inter + i : i) : -1;
+  }
+  const int64_t n = (int64_t)n_tile * BN + r;
+  return n < p.N ? n : -1;
+}
+
+// LDS floats a wave needs for the epilogue: one 32-row block of its
+// 32 NJ columns, rows padded by 8 floats.
+template <int NJ>
+constexpr int epilogue_wave_floats() { return 32 * (NJ * 32 + 8); }
+
+// Epilogue of a wave's MI x NJ blocks of 32 x 32 (tile rows wr0 + 32 i ..,
+// tile columns wc0 + 32 j ..).  MFMA 32x32 output element q of lane l sits at
+// row (q / 4) * 8 + (l / 32) * 4 + q % 4 and column l % 32 of its block.
+// Each 32-row block goes through the wave's own LDS region (lds, wave-private,
+// epilogue_wave_floats<NJ>() floats) so that it leaves as whole row segments
+// with 16-byte stores (a store per element would write 4 bytes per lane
+// into rows far apart).  The caller has synchronized the workgroup, so the
+// region is free.
+template <int MI, int NJ, int BN>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&acc)[MI][NJ],
+                                              const TileCoord& t, int wr0, int wc0, float scale,
+                                              float* lds) {
+  constexpr int CS = NJ * 32 + 8;               // LDS row stride (floats)
+  const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
+  if (p.epilogue == 0 || p.epilogue == 2) {
+    const bool scatter = p.epilogue == 2;
+    float* out = scatter ? p.y_rows : static_cast<float*>(p.out);
+    const int64_t ld = scatter ? p.N : p.ldo;
+    const bool vec = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    const int64_t n0 = (int64_t)t.n_tile * BN + wc0;     // first column of the wave
+    constexpr int LPR = NJ * 8;                         // lanes per row (4 floats each)
+    constexpr int RPI = 64 / LPR;                       // rows per store instruction
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q)
+          lds[((q >> 2) * 8 + half * 4 + (q & 3)) * CS + j * 32 + l32] = acc[i][j][q] * scale;
+      __builtin_amdgcn_s_waitcnt(0xc07f);               // lgkmcnt(0): the wave's writes landed
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += RPI) {
+        const int rl = rr + lane / LPR, c4 = (lane % LPR) * 4;
+        const int r = wr0 + i * 32 + rl;
+        const f32x4 v = *reinterpret_cast<const f32x4*>(lds + rl * CS + c4);
+        if (r < t.rows_valid) {
+          const int64_t s2 = t.row0 + r;
+          const float w = scatter ? p.row_weight[s2] : 1.0f;
+          float* dst = out + s2 * ld + n0 + c4;
+          if (vec && n0 + c4 + 4 <= p.N) {
+            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0] * w, v[1] * w, v[2] * w, v[3] * w};
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+              if (n0 + c4 + u < p.N) dst[u] = v[u] * w;
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);               // reads done before the next block's writes
+    }
+  } else {
+    // SwiGLU: block j (even) is gate, j+1 is up, for the same 32 channels;
+    // h = bf16(silu(gate) * up) staged as 16-bit values.
+    const int64_t inter = p.N / 2;
+    uint16_t* out = static_cast<uint16_t*>(p.out);
+    uint16_t* lh = reinterpret_cast<uint16_t*>(lds);
+    constexpr int CH = NJ * 16;                         // channels of the wave
+    constexpr int HS = CH + 8;                          // LDS row stride (halves)
+    constexpr int LPR = CH / 8;                         // lanes per row (8 channels each)
+    constexpr int RPI = 64 / LPR;
+    const bool vec = (p.ldo & 7) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+    const int64_t c0 = (int64_t)t.n_tile * (BN / 2) + wc0 / 2;   // first channel of the wave
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+#pragma unroll
+      for (int j = 0; j < NJ; j += 2)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int rl = (q >> 2) * 8 + half * 4 + (q & 3);
+          const float gte = acc[i][j][q] * scale, up = acc[i][j + 1][q] * scale;
+          const uint32_t hb = f32_to_bf16_rne(silu_f32(gte) * up);
+          const bool valid = wr0 + i * 32 + rl < t.rows_valid && c0 + (j / 2) * 32 + l32 < inter;
+          if (valid) m = fmaxf(m, fabsf(__uint_as_float(hb << 16)));
+          lh[rl * HS + (j / 2) * 32 + l32] = (uint16_t)hb;
+        }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+#pragma unroll
+      for (int rr = 0; rr < 32; rr += RPI) {
+        const int rl = rr + lane / LPR, c8 = (lane % LPR) * 8;
+        const int r = wr0 + i * 32 + rl;
+        const u32x4 v = *reinterpret_cast<const u32x4*>(lh + rl * HS + c8);
+        if (r < t.rows_valid) {
+          uint16_t* dst = out + (t.row0 + r) * p.ldo + c0 + c8;
+          if (vec && c0 + c8 + 8 <= inter) {
+            *reinterpret_cast<u32x4*>(dst) = v;
+          } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+              if (c0 + c8 + u < inter) dst[u] = (uint16_t)(v[u >> 1] >> (16 * (u & 1)));
+          }
+        }
+      }
+      __builtin_amdgcn_s_waitcnt(0xc07f);
+    }
+    if (p.out_amax) {
+      m = wave_max(m);
+      if (lane == 0) atomic_max_nonneg(p.out_amax, m);
+    }
+  }
+}
+
+}  // namespace nvfp4
