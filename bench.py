@@ -29,8 +29,41 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-BF16_PEAK_TFLOPS = 2500.0
+FP16_PEAK_TFLOPS = 2500.0        # dense fp16 / bf16 MFMA, MI355X
 FP4_PEAK_TFLOPS = 10100.0
+
+
+def profiled_traffic(workload, kernel):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    rocprofv3 summary (profiles/), or None when there is none or the kernel's
+    sources have changed since the counters were taken (hash of its files)."""
+    import hashlib
+    import re
+    path = os.path.join(ROOT, "profiles", f"grouped_gemm_{workload.replace('_trainer', '')}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    fields = dict(re.findall(r"^(traffic_kernel|traffic_bytes_per_launch|source_sha256_16|source_files): (.*)$",
+                             text, re.M))
+    if len(fields) != 4 or kernel not in fields["traffic_kernel"]:
+        return None
+    h = hashlib.sha256()
+    for f in fields["source_files"].split():
+        with open(os.path.join(ROOT, "precision_gemm_nvfp4_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    if h.hexdigest()[:16] != fields["source_sha256_16"].strip():
+        return None
+    return float(fields["traffic_bytes_per_launch"])
+
+
+def gemm_kernel_name(rows, experts, epilogue):
+    """Name of the grouped-GEMM kernel instance the library picks: rows per
+    tile from the average rows per expert (>= 512: 256, >= 128: 128,
+    >= 48: 64, else 32), epilogue 1 = SwiGLU, 2 = scatter."""
+    avg = rows // max(experts, 1)
+    cfg = "4, 4, 2, 2" if avg >= 512 else "2, 4, 2, 2" if avg >= 128 else \
+          "1, 4, 2, 2" if avg >= 48 else "1, 2, 1, 4"
+    return f"nvfp4::grouped_gemm_kernel<{cfg}, {epilogue}>"
 
 
 def gemm_flops(rows, n, k, kc):
@@ -45,7 +78,31 @@ def parse():
     ap.add_argument("--workload", default="moe_T8192_H4096_E256_I1536_k64_trainer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="calibration: time a plain device copy of this many bytes instead "
+                         "(its FETCH_SIZE / WRITE_SIZE per dispatch scale the traffic counters)")
     return ap.parse_args()
+
+
+def copy_calibration(args, torch):
+    """A plain device-to-device copy of known size (torch's copy kernel), for
+    scaling the HBM traffic counters: FETCH_SIZE and WRITE_SIZE of one
+    dispatch should read copy_bytes each."""
+    n = args.copy_bytes // 4
+    src = torch.randn(n, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / args.steps
+    print(json.dumps({"calibration": "device copy", "bytes_read": n * 4, "bytes_written": n * 4,
+                      "ms": round(ms, 4), "gbs": round(2 * n * 4 / (ms * 1e-3) / 1e9, 1)}))
 
 
 class Timeline:
@@ -272,6 +329,9 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
+    if args.copy_bytes:
+        copy_calibration(args, torch)
+        return
     P.load()
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
@@ -325,7 +385,7 @@ def main():
         d = dict(ms=round(ms, 4))
         if "flops" in w:
             d["tflops"] = round(w["flops"] / (ms * 1e-3) / 1e12, 2)
-            d["frac_bf16_peak"] = round(d["tflops"] / BF16_PEAK_TFLOPS, 4)
+            d["frac_fp16_peak"] = round(d["tflops"] / FP16_PEAK_TFLOPS, 4)
             d["frac_fp4_peak"] = round(d["tflops"] / FP4_PEAK_TFLOPS, 4)
         d["gbs"] = round(w["bytes"] / (ms * 1e-3) / 1e9, 1)
         d["frac_hbm"] = round(d["gbs"] / HBM_PEAK_GBS, 4)
@@ -334,18 +394,19 @@ def main():
     gemm_flops_step = work["gemm_gate_up"]["flops"] + work["gemm_down"]["flops"]
     value = gemm_flops_step / (ms_per_step * 1e-3) / 1e12
     gemm_ms = parts_ms["gemm_gate_up"] + parts_ms["gemm_down"]
-    dominant = max(parts_ms, key=lambda k: parts_ms[k])
-    if dominant.startswith("gemm"):
-        ach = gemm_flops_step / (gemm_ms * 1e-3) / 1e12
-        roofline = dict(bound="mfma", achieved=round(ach, 2), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                        frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None,
-                        kernel="grouped_gemm_kernel", mfma_dtype="bf16",
-                        frac_fp4_peak=round(ach / FP4_PEAK_TFLOPS, 4))
-    else:
-        w = work[dominant]
-        ach = w["bytes"] / (parts_ms[dominant] * 1e-3) / 1e9
-        roofline = dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                        frac=round(ach / HBM_PEAK_GBS, 4), traffic=None, kernel=dominant)
+    # Dominant kernel: the gate/up grouped GEMM (one launch per step, the
+    # largest single kernel of the step).  Its part also holds the 1-thread
+    # fill that zeroes out_amax (about 2 us).
+    ach = work["gemm_gate_up"]["flops"] / (parts_ms["gemm_gate_up"] * 1e-3) / 1e12
+    kname = gemm_kernel_name(inp["rows"], wl.experts, 1)
+    traffic = profiled_traffic(wl.name, kname)
+    roofline = dict(bound="mfma", achieved=round(ach, 2), peak=FP16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=round(ach / FP16_PEAK_TFLOPS, 4),
+                    traffic=None if traffic is None else int(traffic),
+                    kernel=kname, mfma_dtype="fp16",
+                    launch_ms=round(parts_ms["gemm_gate_up"], 4),
+                    flops_per_launch=work["gemm_gate_up"]["flops"],
+                    frac_fp4_peak=round(ach / FP4_PEAK_TFLOPS, 4))
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -363,7 +424,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 (e2m1 + e4m3 scales) operands, bf16 MFMA, fp32 accumulate",
+        "dtype": "nvfp4 (e2m1 + e4m3 scales) operands, fp16 MFMA (exact products), fp32 accumulate",
         "data": "synthetic (seeded; Gaussian activations with 1% Student-t(3) x8 channels, "
                 "N(0,0.02) weights, top-8 softmax routing)",
         "config": {"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden,

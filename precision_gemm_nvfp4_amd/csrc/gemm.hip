@@ -106,7 +106,8 @@ struct StageLayout {
   static constexpr int BYTES = (B_SC + BN * 2 + 15) / 16 * 16;
 };
 
-template <int MI, int NJ, int WM, int WN>
+// EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows), fixed per kernel.
+template <int MI, int NJ, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles, int total) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
@@ -411,11 +412,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   }
 
   __syncthreads();                             // LDS free for the epilogue staging
-  gemm_epilogue<MI, NJ, BN>(p, acc, tc, wm * MI * 32, wn * NJ * 32, scale,
+  gemm_epilogue<MI, NJ, BN, EPI>(p, acc, tc, wm * MI * 32, wn * NJ * 32, scale,
                             reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>());
 }
 
-template <int MI, int NJ, int WM, int WN>
+template <int MI, int NJ, int WM, int WN, int EPI>
 static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int BM = WM * MI * 32;
   const int64_t mtiles = (a.rows_total + BM - 1) / BM + a.E;
@@ -427,13 +428,22 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
                           (size_t)(MAX_KC + a.K / BK + 1) * 4;
   const size_t epi_lds = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
   const size_t lds = loop_lds > epi_lds ? loop_lds : epi_lds;
-  auto kern = grouped_gemm_kernel<MI, NJ, WM, WN>;
+  auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, EPI>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
   const int64_t grid = (total + 7) / 8 * 8;
   kern<<<(unsigned)grid, 256, lds, stream>>>(a, (int)ntiles, (int)total);
   return hipGetLastError();
+}
+
+template <int MI, int NJ, int WM, int WN>
+static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
+  switch (a.epilogue) {
+    case 0: return launch_cfg<MI, NJ, WM, WN, 0>(a, stream);
+    case 1: return launch_cfg<MI, NJ, WM, WN, 1>(a, stream);
+    default: return launch_cfg<MI, NJ, WM, WN, 2>(a, stream);
+  }
 }
 
 int grouped_gemm_block_m(int64_t rows_total, int32_t E) {
@@ -453,10 +463,10 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   hipError_t err;
   const int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
   switch (bm) {
-    case 256: err = launch_cfg<4, 4, 2, 2>(a, stream); break;
-    case 128: err = launch_cfg<2, 4, 2, 2>(a, stream); break;
-    case 64: err = launch_cfg<1, 4, 2, 2>(a, stream); break;
-    default: err = launch_cfg<1, 2, 1, 4>(a, stream); break;
+    case 256: err = launch_epi<4, 4, 2, 2>(a, stream); break;
+    case 128: err = launch_epi<2, 4, 2, 2>(a, stream); break;
+    case 64: err = launch_epi<1, 4, 2, 2>(a, stream); break;
+    default: err = launch_epi<1, 2, 1, 4>(a, stream); break;
   }
   if (err != hipSuccess || a.epilogue != 2) return err;
   return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,

@@ -109,14 +109,14 @@ constexpr int epilogue_wave_floats() { return 32 * (NJ * 32 + 8); }
 // with 16-byte stores (a store per element would write 4 bytes per lane
 // into rows far apart).  The caller has synchronized the workgroup, so the
 // region is free.
-template <int MI, int NJ, int BN>
+template <int MI, int NJ, int BN, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&acc)[MI][NJ],
                                               const TileCoord& t, int wr0, int wc0, float scale,
                                               float* lds) {
   constexpr int CS = NJ * 32 + 8;               // LDS row stride (floats)
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
-  if (p.epilogue == 0 || p.epilogue == 2) {
-    const bool scatter = p.epilogue == 2;
+  if constexpr (EPI == 0 || EPI == 2) {
+    constexpr bool scatter = EPI == 2;
     float* out = scatter ? p.y_rows : static_cast<float*>(p.out);
     const int64_t ld = scatter ? p.N : p.ldo;
     const bool vec = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
