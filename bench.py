@@ -58,11 +58,11 @@ def profiled_traffic(workload, kernel):
 
 def gemm_kernel_name(rows, experts, epilogue):
     """Name of the grouped-GEMM kernel instance the library picks: rows per
-    tile from the average rows per expert (>= 512: 256, >= 128: 128,
-    >= 48: 64, else 32), epilogue 1 = SwiGLU, 2 = scatter."""
+    tile from the average rows per expert (>= 160: 256, >= 64: 128,
+    >= 24: 64, else 32), epilogue 1 = SwiGLU, 2 = scatter."""
     avg = rows // max(experts, 1)
-    cfg = "4, 4, 2, 2" if avg >= 512 else "2, 4, 2, 2" if avg >= 128 else \
-          "1, 4, 2, 2" if avg >= 48 else "1, 2, 1, 4"
+    cfg = "4, 4, 2, 2" if avg >= 160 else "2, 4, 2, 2" if avg >= 64 else \
+          "1, 4, 2, 2" if avg >= 24 else "1, 2, 1, 4"
     return f"nvfp4::grouped_gemm_kernel<{cfg}, {epilogue}>"
 
 

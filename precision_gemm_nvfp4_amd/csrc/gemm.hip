@@ -61,6 +61,11 @@
 namespace nvfp4 {
 
 constexpr int BN = 256, BK = 32;
+
+template <int V>
+struct IntC {
+  static constexpr int value = V;
+};
 constexpr int NSTAGE = 2;                   // LDS stages of raw NVFP4 tiles
 constexpr int MAX_KC = 128;                 // largest compensated channel count handled
 
@@ -270,7 +275,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   // is even and at least 2, and the loop, unrolled by two, sees each stage at
   // a fixed LDS offset.
   RowLoad ra[2], rb[2];
-  Frags fr[2];
   const int last = nsteps - 1;
   load_step(0, ra[0], rb[0]);
   load_step(1, ra[1], rb[1]);
@@ -280,8 +284,34 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   __builtin_amdgcn_sched_barrier(0);          // keep the loop's load order in the prologue
   load_step(3 < last ? 3 : last, ra[1], rb[1]);
   lds_barrier();
-  read_frags(0, fr[0]);
   if (comp) gather_ws(0, 0);
+
+  auto main_loop = [&](auto ma_c) {
+  constexpr int MA = decltype(ma_c)::value;
+  // fragment f of the step is read and dequantized only if some MFMA uses it
+  auto frag_live = [&](int f) { return f < MI ? f < MA : MA > 0; };
+  Frags fr[2];
+  {
+    const unsigned char* base = smem;                          // stage 0: fragments of step 0
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      if (i >= MA) continue;
+      const int r = wm * MI * 32 + i * 32 + l32;
+      const u32x2 c = *reinterpret_cast<const u32x2*>(base + A_CODES + r * 16 + half * 8);
+      dequant16(c, e4m3_f16x2(base[A_SC + r * 2 + half]), fr[0].a0[i], fr[0].a1[i]);
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      if (MA == 0) continue;
+      const int r = wn * NJ * 32 + j * 32 + l32;
+      const u32x2 c = *reinterpret_cast<const u32x2*>(base + B_CODES + r * 16 + half * 8);
+      dequant16(c, e4m3_f16x2(base[B_SC + r * 2 + half]), fr[0].b0[j], fr[0].b1[j]);
+    }
+  }
+  // Step 0 overwrites stage 0 (with the data of step 2) once every wave has
+  // read its step-0 fragments from it; waves with fewer live fragments get
+  // there sooner.
+  lds_barrier();
 
   // One K-step in issue order: the MFMAs of this step one at a time, and
   // between them (each group fenced off from the scheduler) the rest of the
@@ -302,13 +332,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
       __builtin_amdgcn_sched_barrier(0);
       {
         const int sub = m / (MI * NJ), j = (m % (MI * NJ)) / MI, i = m % MI;
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sub ? cur.a1[i] : cur.a0[i],
-                                                           sub ? cur.b1[j] : cur.b0[j],
-                                                           acc[i][j], 0, 0, 0);
+        if (i < MA)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sub ? cur.a1[i] : cur.a0[i],
+                                                             sub ? cur.b1[j] : cur.b0[j],
+                                                             acc[i][j], 0, 0, 0);
       }
       if (m == 0) {
 #pragma unroll
         for (int f = 0; f < kFr; ++f) {
+          if (!frag_live(f)) continue;
           const int r = f < MI ? wm * MI * 32 + f * 32 + l32 : wn * NJ * 32 + (f - MI) * 32 + l32;
           const int co = f < MI ? A_CODES : B_CODES, so = f < MI ? A_SC : B_SC;
           rc[f] = *reinterpret_cast<const u32x2*>(nb + co + r * 16 + half * 8);
@@ -323,6 +355,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
           const int at = kMf <= kDeq0 ? kMf - 1 : kDeq0 + hf * (kMf - kDeq0) / (2 * kFr);
           if (at != m) continue;
           const int f = hf >> 1, h = hf & 1;
+          if (!frag_live(f)) continue;
           // The empty asm statements fix this work to this slot: inputs pass
           // through one before it (nothing is hoisted to its loads), outputs
           // after it (nothing is sunk to its use).
@@ -352,6 +385,24 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     lds_barrier();
     step(s + 1, 1, fr[1], fr[0], ra[1], rb[1]);
     lds_barrier();
+  }
+  };
+  // The number of this wave's 32-row A fragments that hold rows of the tile
+  // (0 .. MI): a ragged last m-tile of an expert skips the MFMAs and the
+  // dequantization of its empty fragments (a wave with none skips its W
+  // fragments too), with the loop specialized for each count.
+  // The count is the same for every lane of the wave; readfirstlane makes
+  // that visible to the compiler, so the switch is a scalar branch (a
+  // lane-divergent branch around loops holding barriers would be undefined).
+  const int ma_rows = rows_valid - wm * MI * 32;
+  const int ma = __builtin_amdgcn_readfirstlane(
+      ma_rows <= 0 ? 0 : (ma_rows >= MI * 32 ? MI : (ma_rows + 31) / 32));
+  switch (ma) {
+    case 0: main_loop(IntC<0>{}); break;
+    case 1: main_loop(IntC<1>{}); break;
+    case 2: if constexpr (MI >= 2) main_loop(IntC<2>{}); break;
+    case 3: if constexpr (MI >= 3) main_loop(IntC<3>{}); break;
+    default: main_loop(IntC<MI>{}); break;
   }
 
   // ---- compensation chunk ---------------------------------------------------
@@ -446,11 +497,15 @@ static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
   }
 }
 
+// Rows per m-tile from the average rows per expert.  The last m-tile of an
+// expert is ragged; its empty 32-row fragments cost no MFMAs and no A
+// dequantization, so large tiles (which dequantize fewer W elements per MFMA)
+// pay off from about 160 rows per expert.
 int grouped_gemm_block_m(int64_t rows_total, int32_t E) {
   const int64_t avg = E > 0 ? rows_total / E : rows_total;
-  if (avg >= 512) return 256;
-  if (avg >= 128) return 128;
-  if (avg >= 48) return 64;
+  if (avg >= 160) return 256;
+  if (avg >= 64) return 128;
+  if (avg >= 24) return 64;
   return 32;
 }
 

@@ -296,9 +296,10 @@ def test_guided_round(gpu_lib, rel):
 
 
 @pytest.mark.parametrize("tokens,n_exp,top_k,zipf", [
-    (600, 2, 2, 0.0),     # 600 rows per expert: 256-row tiles
+    (600, 2, 2, 0.0),     # 600 rows per expert: 256-row tiles, last one 88 rows
+    (340, 4, 2, 0.3),     # ~170 rows per expert: one 256-row tile, waves with 2-4 live fragments
     (300, 4, 2, 0.5),     # 150 rows per expert: 128-row tiles
-    (200, 8, 3, 1.0),     # 75 rows per expert: 64-row tiles
+    (200, 8, 2, 1.0),     # 50 rows per expert: 64-row tiles
     (64, 16, 4, 0.0),     # 16 rows per expert: 32-row tiles
 ])
 def test_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
