@@ -48,14 +48,16 @@
 // the output rows in a fixed order.
 //
 // Work decomposition: the logical tiles are the (expert, n-tile, m-tile)
-// triples of the ragged groups, expert-major, then n-tile, m-tile innermost
-// (upper bound (ceil(rows/BM) + E) x n-tiles; surplus workgroups exit).
-// Workgroup ids are dealt round-robin to the 8 XCDs, so hardware id h runs
-// logical tile (h % 8) * ceil(total / 8) + h / 8: each XCD owns a contiguous
-// range of experts; the m-tiles that share one weight tile run side by side
-// on it (the weight tile is read once), and the expert's activation rows stay
-// in its L2 across the n-tiles.  Four waves per workgroup; each wave owns
-// MI x NJ MFMA blocks of 32 x 32.
+// triples of the ragged groups, expert-major, then n-tile, m-tile innermost;
+// their number T comes from the group offsets on the device, and the grid is
+// an upper bound ((ceil(rows / BM) + E) x n-tiles, rounded up to a multiple of
+// 8).  Workgroup ids are dealt round-robin to the 8 XCDs, so hardware id h
+// runs logical tile (h % 8) * ceil(T / 8) + h / 8 and the rest exit: each XCD
+// owns a contiguous eighth of the real tiles (dividing the upper bound instead
+// would leave whole XCDs with surplus workgroups only).  The m-tiles that
+// share one weight tile run side by side (the weight tile is read once), and
+// the expert's activation rows stay in the XCD's L2 across the n-tiles.  Four
+// waves per workgroup; each wave owns MI x NJ MFMA blocks of 32 x 32.
 #include "gemm_common.h"
 
 namespace nvfp4 {
@@ -113,7 +115,7 @@ struct StageLayout {
 
 // EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows), fixed per kernel.
 template <int MI, int NJ, int WM, int WN, int EPI>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles, int total) {
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
   static_assert(WM * WN == 4, "four waves");
@@ -133,8 +135,15 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
-  const TileCoord tc = find_tile<BM>(p, ntiles, total);
-  if (tc.e < 0) return;
+  // XCD x = blockIdx % 8 takes the logical tiles [x * per_xcd, (x + 1) * per_xcd)
+  // of the T real ones (per_xcd = ceil(T / 8)); the grid, a multiple of 8 and
+  // at least T, leaves surplus workgroups that exit here.
+  const int real = (int)count_mtiles<BM>(p) * ntiles;
+  const int per_xcd = (real + 7) / 8;
+  const int jt = (int)blockIdx.x / 8;
+  const int logical = ((int)blockIdx.x % 8) * per_xcd + jt;
+  if (jt >= per_xcd || logical >= real) return;     // uniform over the workgroup
+  const TileCoord tc = locate_tile<BM>(p, ntiles, logical);
   const int e = tc.e, n_tile = tc.n_tile, rows_valid = tc.rows_valid;
   const int64_t row0 = tc.row0;
 
@@ -483,8 +492,8 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  const int64_t grid = (total + 7) / 8 * 8;
-  kern<<<(unsigned)grid, 256, lds, stream>>>(a, (int)ntiles, (int)total);
+  const int64_t grid = (total + 7) / 8 * 8;       // upper bound on the tiles, one share per XCD
+  kern<<<(unsigned)grid, 256, lds, stream>>>(a, (int)ntiles);
   return hipGetLastError();
 }
 

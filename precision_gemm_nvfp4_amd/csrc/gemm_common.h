@@ -14,65 +14,84 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
 struct TileCoord {
-  int e;            // expert, -1: surplus workgroup
+  int e;            // expert
   int n_tile;
   int64_t row0;     // first unit row of the tile
   int rows_valid;   // rows of the tile inside the expert's group
 };
 
-// Logical tile of this workgroup.  The logical tiles are the (expert, n-tile,
-// m-tile) triples of the ragged groups, expert by expert; inside an expert's
-// block of cnt_e * ntiles tiles n-tile major and m-tile minor, so the m-tiles
-// that share a weight tile run side by side.  Workgroup ids are dealt
-// round-robin to the 8 XCDs, so hardware id h runs logical tile
-// (h % 8) * ceil(total / 8) + h / 8: each XCD owns a contiguous range.
-// Called by all threads of a 256-thread workgroup.
+// m-tiles of BM rows of expert e's group, for the threads of a 256-thread
+// workgroup in chunks of 256 experts.
 template <int BM>
-__device__ TileCoord find_tile(const GemmArgs& p, int ntiles, int total) {
+__device__ __forceinline__ uint32_t expert_mtiles(const GemmArgs& p, int e) {
+  if (e >= p.E) return 0;
+  const int64_t rb = clamp64(p.group_offsets[e], 0, p.rows_total);
+  const int64_t re = clamp64(p.group_offsets[e + 1], rb, p.rows_total);
+  return (uint32_t)((re - rb + BM - 1) / BM);
+}
+
+// Inclusive prefix sum over the 256 threads of a workgroup; every thread also
+// gets the workgroup total.  sh_waves: 4 words of LDS, free on entry.
+__device__ __forceinline__ uint32_t block_scan_256(uint32_t v, uint32_t* sh_waves, uint32_t& total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    uint32_t u = __shfl_up(v, o, 64);
+    if (lane >= o) v += u;
+  }
+  if (lane == 63) sh_waves[wave] = v;
+  __syncthreads();
+  uint32_t before = 0;
+  total = 0;
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) before += sh_waves[w];
+    total += sh_waves[w];
+  }
+  __syncthreads();
+  return before + v;
+}
+
+// Number of m-tiles over all experts (the same in every thread).
+template <int BM>
+__device__ uint32_t count_mtiles(const GemmArgs& p) {
+  __shared__ uint32_t sh_waves[4];
+  uint32_t carry = 0;
+  for (int base = 0; base < p.E; base += 256) {
+    uint32_t tot;
+    block_scan_256(expert_mtiles<BM>(p, base + (int)threadIdx.x), sh_waves, tot);
+    carry += tot;
+  }
+  return carry;
+}
+
+// Coordinates of logical tile `logical` (0 <= logical < m-tiles x ntiles).
+// The logical tiles are the (expert, n-tile, m-tile) triples, expert by
+// expert; inside an expert's block of cnt_e * ntiles tiles n-tile major and
+// m-tile minor, so consecutive tiles share a weight tile.  Called by all
+// threads of a 256-thread workgroup.
+template <int BM>
+__device__ TileCoord locate_tile(const GemmArgs& p, int ntiles, int logical) {
   __shared__ int32_t sh_e, sh_mt, sh_nt;
   __shared__ uint32_t sh_waves[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  TileCoord t{-1, 0, 0, 0};
-  const int per_xcd = (total + 7) / 8;
-  const int logical = (int)(blockIdx.x % 8) * per_xcd + (int)(blockIdx.x / 8);
-  if (logical >= total) return t;             // uniform over the workgroup
-  const int m_key = logical / ntiles;         // lies inside expert e's m-tile range
-  if (tid == 0) sh_e = -1;
-  __syncthreads();
+  const int tid = threadIdx.x;
+  const uint32_t m_key = (uint32_t)(logical / ntiles);   // lies inside expert e's m-tile range
   uint32_t carry = 0;
   for (int base = 0; base < p.E; base += 256) {
     const int e = base + tid;
-    int64_t rb = 0, re = 0;
-    if (e < p.E) {
-      rb = clamp64(p.group_offsets[e], 0, p.rows_total);
-      re = clamp64(p.group_offsets[e + 1], rb, p.rows_total);
-    }
-    const uint32_t n = (uint32_t)((re - rb + BM - 1) / BM);
-    uint32_t inc = n;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      uint32_t u = __shfl_up(inc, o, 64);
-      if (lane >= o) inc += u;
-    }
-    if (lane == 63) sh_waves[wave] = inc;
-    __syncthreads();
-    uint32_t before = carry, tot = 0;
-    for (int w = 0; w < 4; ++w) {
-      if (w < wave) before += sh_waves[w];
-      tot += sh_waves[w];
-    }
-    before += inc - n;
-    if (e < p.E && (uint32_t)m_key >= before && (uint32_t)m_key < before + n) {
-      const int off = logical - (int)before * ntiles;   // position inside the expert's block
+    const uint32_t n = expert_mtiles<BM>(p, e);
+    uint32_t tot;
+    const uint32_t before = carry + block_scan_256(n, sh_waves, tot) - n;
+    if (e < p.E && m_key >= before && m_key < before + n) {   // exactly one thread
+      const int off = logical - (int)before * ntiles;          // position inside the expert's block
       sh_e = e;
       sh_nt = off / (int)n;
       sh_mt = off % (int)n;
     }
     carry += tot;
-    __syncthreads();
   }
+  __syncthreads();
+  TileCoord t;
   t.e = sh_e;
-  if (t.e < 0) return t;
   t.n_tile = sh_nt;
   const int64_t g0 = clamp64(p.group_offsets[t.e], 0, p.rows_total);
   const int64_t g1 = clamp64(p.group_offsets[t.e + 1], g0, p.rows_total);
