@@ -47,17 +47,22 @@
 // row_weight * Y rows go into the workspace and combine.hip adds them into
 // the output rows in a fixed order.
 //
-// Work decomposition: the logical tiles are the (expert, n-tile, m-tile)
-// triples of the ragged groups, expert-major, then n-tile, m-tile innermost;
+// Work decomposition: the logical tiles are the (expert, m-tile, n-tile)
+// triples of the ragged groups, expert-major, then m-tile, n-tile innermost;
 // their number T comes from the group offsets on the device, and the grid is
 // an upper bound ((ceil(rows / BM) + E) x n-tiles, rounded up to a multiple of
 // 8).  Workgroup ids are dealt round-robin to the 8 XCDs, so hardware id h
 // runs logical tile (h % 8) * ceil(T / 8) + h / 8 and the rest exit: each XCD
 // owns a contiguous eighth of the real tiles (dividing the upper bound instead
-// would leave whole XCDs with surplus workgroups only).  The m-tiles that
-// share one weight tile run side by side (the weight tile is read once), and
-// the expert's activation rows stay in the XCD's L2 across the n-tiles.  Four
-// waves per workgroup; each wave owns MI x NJ MFMA blocks of 32 x 32.
+// would leave whole XCDs with surplus workgroups only).  Inside an XCD the
+// workgroups go to its shader engines in a fixed rotation and in order, so
+// neighbouring tiles should cost the same: with n-tiles innermost a ragged
+// last m-tile is a run of equally cheap tiles (with m-tiles innermost, full
+// and nearly empty tiles alternate and half the engines get all the full
+// ones).  The m-tiles that share one weight tile still run within one
+// window of the XCD's CUs (the weight tile comes from L2 the second time),
+// and an A tile is reused by consecutive n-tiles.  Four waves per workgroup;
+// each wave owns MI x NJ MFMA blocks of 32 x 32.
 #include "gemm_common.h"
 
 namespace nvfp4 {

@@ -65,10 +65,11 @@ __device__ uint32_t count_mtiles(const GemmArgs& p) {
 }
 
 // Coordinates of logical tile `logical` (0 <= logical < m-tiles x ntiles).
-// The logical tiles are the (expert, n-tile, m-tile) triples, expert by
-// expert; inside an expert's block of cnt_e * ntiles tiles n-tile major and
-// m-tile minor, so consecutive tiles share a weight tile.  Called by all
-// threads of a 256-thread workgroup.
+// The logical tiles are the (expert, m-tile, n-tile) triples, expert by
+// expert; inside an expert's block of cnt_e * ntiles tiles m-tile major and
+// n-tile minor, so consecutive tiles cost the same (a ragged last m-tile
+// comes as a run of ntiles cheap tiles).  Called by all threads of a
+// 256-thread workgroup.
 template <int BM>
 __device__ TileCoord locate_tile(const GemmArgs& p, int ntiles, int logical) {
   __shared__ int32_t sh_e, sh_mt, sh_nt;
@@ -84,8 +85,8 @@ __device__ TileCoord locate_tile(const GemmArgs& p, int ntiles, int logical) {
     if (e < p.E && m_key >= before && m_key < before + n) {   // exactly one thread
       const int off = logical - (int)before * ntiles;          // position inside the expert's block
       sh_e = e;
-      sh_nt = off / (int)n;
-      sh_mt = off % (int)n;
+      sh_mt = off / ntiles;
+      sh_nt = off % ntiles;
     }
     carry += tot;
   }
