@@ -219,7 +219,7 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
 // ---------------------------------------------------------------------------
 size_t qdq_weights_workspace_size(int64_t nmat, int64_t N, int64_t K) {
   (void)N; (void)K;
-  return align256((size_t)(nmat > 0 ? nmat : 0) * 4);
+  return nvfp4::qdq_workspace_bytes(nmat);
 }
 
 int qdq_weights(const void* w, int64_t nmat, int64_t N, int64_t K, void* w_qdq, uint8_t* codes,
@@ -236,8 +236,8 @@ int qdq_weights(const void* w, int64_t nmat, int64_t N, int64_t K, void* w_qdq, 
   if (!ws || ws_bytes < qdq_weights_workspace_size(nmat, N, K))
     return fail(NVFP4_EWORKSPACE, "%s: workspace too small", fn);
   return hip_status(nvfp4::launch_qdq(static_cast<const __bf16*>(w), nmat, N, K,
-                                      static_cast<__bf16*>(w_qdq), codes, scales, g,
-                                      static_cast<float*>(ws), static_cast<hipStream_t>(stream)),
+                                      static_cast<__bf16*>(w_qdq), codes, scales, g, ws,
+                                      static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -45,6 +45,14 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Two fp32 values to packed bf16 bits (a in the low half), round to nearest
+// even: one hardware convert (v_cvt_pk_bf16_f32; the kernels keep fp32
+// denormals, so subnormal inputs round like normal ones).
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2_t));
+}
+
 // ---------------------------------------------------------------------------
 // global scale
 // ---------------------------------------------------------------------------

@@ -71,9 +71,9 @@ hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
                           void* ws, hipStream_t stream);
 
 // trainer.hip
+size_t qdq_workspace_bytes(int64_t nmat);
 hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
-                      uint8_t* codes, uint8_t* scales, float* g, float* ws_amax,
-                      hipStream_t stream);
+                      uint8_t* codes, uint8_t* scales, float* g, void* ws, hipStream_t stream);
 hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                          const uint8_t* roll_codes, const uint8_t* roll_scales,
                          const float* roll_global, uint8_t* guided, __bf16* x_fq,

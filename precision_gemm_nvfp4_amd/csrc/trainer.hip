@@ -23,18 +23,27 @@ namespace nvfp4 {
 // ---------------------------------------------------------------------------
 // weight QDQ
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ float absmax8(const u32x4& a, float m) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(a[i])), fabsf(bf16_hi(a[i]))));
+  return m;
+}
+
+// grid: x over the matrix's 16-byte chunks (grid-stride, four loads in flight
+// per thread), y = matrix
 __global__ __launch_bounds__(256) void qdq_amax_kernel(const __bf16* __restrict__ w, int64_t per_mat,
                                                        float* __restrict__ amax) {
   const int64_t mat = blockIdx.y;
   const u32x4* p = reinterpret_cast<const u32x4*>(w + mat * per_mat);
   const int64_t chunks = per_mat / 8;
+  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   float m = 0.0f;
-  for (int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; c < chunks;
-       c += (int64_t)gridDim.x * blockDim.x) {
-    u32x4 v = p[c];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(v[i])), fabsf(bf16_hi(v[i]))));
+  for (; c + 3 * stride < chunks; c += 4 * stride) {
+    const u32x4 v0 = p[c], v1 = p[c + stride], v2 = p[c + 2 * stride], v3 = p[c + 3 * stride];
+    m = absmax8(v3, absmax8(v2, absmax8(v1, absmax8(v0, m))));
   }
+  for (; c < chunks; c += stride) m = absmax8(p[c], m);
   m = wave_max(m);
   __shared__ float red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -43,6 +52,40 @@ __global__ __launch_bounds__(256) void qdq_amax_kernel(const __bf16* __restrict_
     float b = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     atomic_max_nonneg(amax + mat, b);
   }
+}
+
+// One 16-block (elements a, c as bf16 pairs) quantized under g: writes
+// bf16(DQ) at w_qdq + base and, when asked, the codes and the block scale.
+__device__ __forceinline__ void qdq_block(const u32x4& a, const u32x4& c, float g, double six_g,
+                                          int64_t base, __bf16* __restrict__ w_qdq,
+                                          uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    v[2 * i] = bf16_lo(a[i]);
+    v[2 * i + 1] = bf16_hi(a[i]);
+    v[8 + 2 * i] = bf16_lo(c[i]);
+    v[8 + 2 * i + 1] = bf16_hi(c[i]);
+  }
+  uint32_t sb, w0, w1;
+  const float S = quantize_block16(v, g, six_g, &sb, &w0, &w1);
+  // bf16(DQ) two elements at a time: the hardware FP4 convert gives the codes'
+  // exact values, one fp32 multiply each rounds value * S, one packed convert
+  // rounds both to bf16.
+  float d[16];
+  e2m1_unpack8(w0, d);
+  e2m1_unpack8(w1, d + 8);
+  u32x4 o0, o1;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t word = pack_bf16x2_rne(d[2 * i] * S, d[2 * i + 1] * S);
+    if (i < 4) o0[i] = word; else o1[i - 4] = word;
+  }
+  u32x4* dst = reinterpret_cast<u32x4*>(w_qdq + base);
+  dst[0] = o0;
+  dst[1] = o1;
+  if (codes) *reinterpret_cast<u32x2*>(codes + base / 2) = u32x2{w0, w1};
+  if (scales) scales[base / kBlock] = (uint8_t)sb;
 }
 
 // grid: x over the matrix's 16-blocks (grid-stride), y = matrix in the group
@@ -59,65 +102,39 @@ __global__ __launch_bounds__(256) void qdq_kernel(const __bf16* __restrict__ w, 
        b += (int64_t)gridDim.x * blockDim.x) {
     const int64_t base = mat * N * K + b * kBlock;      // blocks are contiguous in row-major order
     const u32x4* src = reinterpret_cast<const u32x4*>(w + base);
-    u32x4 a = src[0], c = src[1];
-    float v[16];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      v[2 * i] = bf16_lo(a[i]);
-      v[2 * i + 1] = bf16_hi(a[i]);
-      v[8 + 2 * i] = bf16_lo(c[i]);
-      v[8 + 2 * i + 1] = bf16_hi(c[i]);
-    }
-    uint32_t sb, w0, w1;
-    const float S = quantize_block16(v, g, six_g, &sb, &w0, &w1);
-    u32x4 o0, o1;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t c0 = ((i < 4 ? w0 : w1) >> (8 * (i & 3))) & 15u;
-      const uint32_t c1 = ((i < 4 ? w0 : w1) >> (8 * (i & 3) + 4)) & 15u;
-      const uint32_t lo = f32_to_bf16_rne(dq(c0, S)), hi = f32_to_bf16_rne(dq(c1, S));
-      const uint32_t word = lo | (hi << 16);
-      if (i < 4) o0[i] = word; else o1[i - 4] = word;
-    }
-    u32x4* dst = reinterpret_cast<u32x4*>(w_qdq + base);
-    dst[0] = o0;
-    dst[1] = o1;
-    if (codes) *reinterpret_cast<u32x2*>(codes + base / 2) = u32x2{w0, w1};
-    if (scales) scales[base / kBlock] = (uint8_t)sb;
+    qdq_block(src[0], src[1], g, six_g, base, w_qdq, codes, scales);
   }
 }
 
-// All matrices in one amax launch, then one quantize launch.  Measured
-// alternatives on the 256-expert weights (9.66 GB bf16): groups of matrices
-// small enough for the second read to come from the MALL took 6.9-13.1 ms
-// (64-200 MB groups) against 5.7 ms; a cooperative single-read kernel that
-// holds each matrix in registers across a grid-wide amax gather took 6.8 ms
-// (its workgroups move in lockstep between loading, gathering and writing).
-// The quantize pass already moves data faster than a plain device copy.
-constexpr int64_t kQdqGroupBytes = 1ll << 62;
+// All matrices in one amax launch, then one quantize launch; both stream at
+// about 5 TB/s.  Single-read alternatives measured on the 256-expert weights
+// (W_gu 3072 x 4096 and W_d 4096 x 1536 per expert; two-pass 4.2 + 2.1 ms):
+//  - groups of matrices small enough for the second read to come from the
+//    MALL: 6.9-13.1 ms (the MALL re-read runs at about 7 TB/s, hardly above
+//    HBM);
+//  - a cooperative kernel holding one matrix in registers across a grid-wide
+//    amax gather: 6.8 ms (load, gather and write in lockstep);
+//  - the same with the next matrix's loads issued before the gather (two or
+//    three matrices in registers, slot-based gathers, LDS-only barriers):
+//    3.8 + 2.6 ms; with two teams of workgroups a CU apart in phase:
+//    5.1 + 2.2 ms.  Each step waits for its gather and its stores drain into
+//    a busy memory system, which costs about what the second read saves.
+size_t qdq_workspace_bytes(int64_t nmat) { return ((size_t)(nmat > 0 ? nmat : 0) * 4 + 255) / 256 * 256; }
 
 hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
-                      uint8_t* codes, uint8_t* scales, float* g, float* ws_amax,
-                      hipStream_t stream) {
+                      uint8_t* codes, uint8_t* scales, float* g, void* ws, hipStream_t stream) {
+  float* ws_amax = static_cast<float*>(ws);
   hipError_t err = launch_fill_f32(ws_amax, nmat, 0.0f, stream);
   if (err != hipSuccess) return err;
   const int64_t per_mat = N * K;
-  int64_t group = kQdqGroupBytes / (per_mat * 2);
-  group = group < 1 ? 1 : (group > 65535 ? 65535 : group);
   const int64_t nb = N * (K / kBlock);
-  for (int64_t m0 = 0; m0 < nmat; m0 += group) {
-    const int64_t gm = nmat - m0 < group ? nmat - m0 : group;
-    int64_t ga = (per_mat / 8 + 255) / 256;              // about 4096 workgroups in all
-    ga = ga > 4096 / gm + 1 ? 4096 / gm + 1 : (ga < 1 ? 1 : ga);
-    qdq_amax_kernel<<<dim3((unsigned)ga, (unsigned)gm), 256, 0, stream>>>(w + m0 * per_mat, per_mat,
-                                                                           ws_amax + m0);
-    int64_t gq = (nb + 255) / 256;                       // about 16384 workgroups in all
-    gq = gq > 16384 / gm + 1 ? 16384 / gm + 1 : gq;
-    qdq_kernel<<<dim3((unsigned)gq, (unsigned)gm), 256, 0, stream>>>(
-        w + m0 * per_mat, N, K, ws_amax + m0, w_qdq + m0 * per_mat,
-        codes ? codes + m0 * per_mat / 2 : nullptr, scales ? scales + m0 * per_mat / kBlock : nullptr,
-        g ? g + m0 : nullptr);
-  }
+  int64_t ga = (per_mat / 8 + 255) / 256;                // about 4096 workgroups in all
+  ga = ga > 4096 / nmat + 1 ? 4096 / nmat + 1 : (ga < 1 ? 1 : ga);
+  qdq_amax_kernel<<<dim3((unsigned)ga, (unsigned)nmat), 256, 0, stream>>>(w, per_mat, ws_amax);
+  int64_t gq = (nb + 255) / 256;                         // about 16384 workgroups in all
+  gq = gq > 16384 / nmat + 1 ? 16384 / nmat + 1 : gq;
+  qdq_kernel<<<dim3((unsigned)gq, (unsigned)nmat), 256, 0, stream>>>(w, N, K, ws_amax, w_qdq, codes,
+                                                                     scales, g);
   return hipGetLastError();
 }
 
@@ -200,13 +217,15 @@ __global__ __launch_bounds__(256) void guided_kernel(
       uint32_t code = (uint32_t)(s_pick < 0 ? -s_pick : s_pick);
       if (s_pick < 0 || (s_pick == 0 && (__float_as_uint(v[j]) >> 31))) code |= 8u;
       if (j < 8) g0 |= code << (4 * j); else g1 |= code << (4 * (j - 8));
-      if (x_fq) {
-        const uint32_t hb = f32_to_bf16_rne(dq(code, S));
-        if (j & 1) fq[j >> 1] |= hb << 16; else fq[j >> 1] = hb;
-      }
     }
     *reinterpret_cast<u32x2*>(guided + (int64_t)b * 8) = u32x2{g0, g1};
     if (x_fq) {
+      // bf16(RNE32(value * S)) two elements at a time, as in the weight QDQ
+      float d[16];
+      e2m1_unpack8(g0, d);
+      e2m1_unpack8(g1, d + 8);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) fq[i] = pack_bf16x2_rne(d[2 * i] * S, d[2 * i + 1] * S);
       u32x4* dst = reinterpret_cast<u32x4*>(x_fq + (int64_t)b * kBlock);
       dst[0] = u32x4{fq[0], fq[1], fq[2], fq[3]};
       dst[1] = u32x4{fq[4], fq[5], fq[6], fq[7]};

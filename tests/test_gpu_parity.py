@@ -271,15 +271,44 @@ def test_grouped_gemm_swiglu_and_scatter(gpu_lib, comp):
 # trainer side
 # ---------------------------------------------------------------------------
 
+def _check_qdq(P, w, want_codes=True):
+    wq, c, s, g = P.qdq_weights(w.cuda(), want_codes=want_codes)
+    wq_r, c_r, s_r, g_r = OQ.qdq_weights(w.float().numpy())
+    assert np.array_equal(np32(g), g_r)
+    if want_codes:
+        assert np.array_equal(npu8(c), c_r) and np.array_equal(npu8(s), s_r)
+    assert np.array_equal(wq.cpu().view(torch.int16).numpy().view(np.uint16), wq_r)
+
+
 def test_qdq_weights(gpu_lib):
     P = gpu_lib
     w = synth.weights(3, 96, 256, seed=10, tensor_id=synth.WGU_ID)
     w[1, 5, 7] = 3.0                      # one outlier per matrix changes g
-    wq, c, s, g = P.qdq_weights(w.cuda())
-    wq_r, c_r, s_r, g_r = OQ.qdq_weights(w.float().numpy())
-    assert np.array_equal(np32(g), g_r)
-    assert np.array_equal(npu8(c), c_r) and np.array_equal(npu8(s), s_r)
-    assert np.array_equal(wq.cpu().view(torch.int16).numpy().view(np.uint16), wq_r)
+    _check_qdq(P, w)
+
+
+@pytest.mark.parametrize("nmat,n,k,mag,want_codes", [
+    (5, 40, 160, 1e-36, True),    # g, S and the outputs are fp32 subnormals
+    (2, 64, 128, 1e30, True),     # large values
+    (7, 33, 96, 1.0, False),      # odd sizes, no codes out
+    (4, 300, 512, 1.0, True),     # several blocks per thread
+])
+def test_qdq_weights_magnitudes(gpu_lib, nmat, n, k, mag, want_codes):
+    """Weight QDQ bit-exact at extreme magnitudes (subnormal global and block
+    scales and subnormal bf16 outputs), with zero matrices and zero blocks."""
+    P = gpu_lib
+    w = synth.weights(nmat, n, k, seed=12, tensor_id=synth.WGU_ID).float() * (mag / 0.02)
+    w[0] = 0.0                            # all-zero matrix: g = 1
+    w[-1, :, :16] = 0.0                   # zero blocks next to nonzero ones
+    _check_qdq(P, w.to(torch.bfloat16), want_codes)
+
+
+def test_qdq_weights_two_pass_size(gpu_lib):
+    """A matrix of 787456 16-blocks (512 x 24608): more than one resident
+    grid holds at once on a 256-CU GPU, so the two-pass path quantizes it."""
+    P = gpu_lib
+    w = synth.weights(1, 512, 24608, seed=13, tensor_id=synth.WD_ID)
+    _check_qdq(P, w)
 
 
 @pytest.mark.parametrize("rel", [1e-3, 8e-3, 0.2])
