@@ -303,9 +303,9 @@ def test_qdq_weights_magnitudes(gpu_lib, nmat, n, k, mag, want_codes):
     _check_qdq(P, w.to(torch.bfloat16), want_codes)
 
 
-def test_qdq_weights_two_pass_size(gpu_lib):
-    """A matrix of 787456 16-blocks (512 x 24608): more than one resident
-    grid holds at once on a 256-CU GPU, so the two-pass path quantizes it."""
+def test_qdq_weights_large_matrix(gpu_lib):
+    """One large matrix (512 x 24608, 12.6M elements): its amax is gathered
+    from many workgroups and its blocks are quantized by many more."""
     P = gpu_lib
     w = synth.weights(1, 512, 24608, seed=13, tensor_id=synth.WD_ID)
     _check_qdq(P, w)
