@@ -9,9 +9,10 @@
 //   scores    per (128-row tile, 64 channels): fp32 sum of |R| over the tile's
 //             rows in increasing row order          (skipped when nvfp4_quantize
 //                                                    already produced them)
-//   select    per unit: tile sums added in tile order -> LDS; the k-th largest
-//             score found bit by bit (31 block-wide counts); ties to the lower
-//             channel; compaction in ascending channel order (block scans)
+//   select    per unit: tile sums added in tile order; the k-th largest score
+//             found two bits per pass (keys in registers for K <= 8192,
+//             else in LDS one bit per pass); ties to the lower channel;
+//             compaction in ascending channel order (block scans)
 //   gather    per 32-row slot: R_S = x[:, sel] - DQ(codes, scales)[:, sel] ->
 //             workspace, with the slot's max |R_S|
 //   requant   per 32-row slot: unit amax -> g_R, NVFP4 of R_S rows (16-blocks
@@ -233,6 +234,166 @@ __device__ __forceinline__ uint32_t block_sum256(uint32_t v, uint32_t* sh4) {
   return sh4[0] + sh4[1] + sh4[2] + sh4[3];
 }
 
+// Wave-level sum and exclusive prefix of small counts (0 <= v < 2^BITS) from
+// bit-plane ballots: no lane shuffles, each bit plane is one ballot, its
+// population count and mbcnt (the set bits below this lane).
+template <int BITS>
+__device__ __forceinline__ uint32_t wave_scan_small(uint32_t v, uint32_t* total) {
+  uint32_t pre = 0, tot = 0;
+#pragma unroll
+  for (int b = 0; b < BITS; ++b) {
+    const unsigned long long m = __ballot((v >> b) & 1u);
+    pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u)) << b;
+    tot += (uint32_t)__popcll(m) << b;
+  }
+  *total = tot;
+  return pre;
+}
+
+// Workgroup (4 waves) sums of three small counts with one barrier: the wave
+// sums go to sh[parity], and callers alternate the parity, so a slot is
+// rewritten only after the next call's barrier, which every reader of it has
+// passed.
+template <int BITS>
+__device__ __forceinline__ void block_sum3_small(uint32_t& a, uint32_t& b, uint32_t& c,
+                                                 uint32_t (*sh)[3][4], int parity) {
+  uint32_t ta, tb, tc;
+  wave_scan_small<BITS>(a, &ta);
+  wave_scan_small<BITS>(b, &tb);
+  wave_scan_small<BITS>(c, &tc);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sh[parity][0][w] = ta;
+    sh[parity][1][w] = tb;
+    sh[parity][2][w] = tc;
+  }
+  __syncthreads();
+  a = sh[parity][0][0] + sh[parity][0][1] + sh[parity][0][2] + sh[parity][0][3];
+  b = sh[parity][1][0] + sh[parity][1][1] + sh[parity][1][2] + sh[parity][1][3];
+  c = sh[parity][2][0] + sh[parity][2][1] + sh[parity][2][2] + sh[parity][2][3];
+}
+
+// Workgroup (4 waves) exclusive prefix and total of a small count, with the
+// same alternating-parity slots (sh[parity][0..3]).
+template <int BITS>
+__device__ __forceinline__ uint32_t block_scan_small(uint32_t v, uint32_t* total, uint32_t (*sh)[3][4],
+                                                     int parity) {
+  uint32_t wt;
+  const uint32_t pre = wave_scan_small<BITS>(v, &wt);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) sh[parity][0][w] = wt;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = sh[parity][0][i];
+    base += i < w ? t : 0u;
+    tot += t;
+  }
+  *total = tot;
+  return base + pre;
+}
+
+// Selection with the keys in registers (K <= 256 CH): thread t owns channels
+// [t CH, t CH + CH).  The k-th largest key T is found two bits per pass: the
+// three candidates T | d << lo (d = 1..3) are counted together and the
+// largest with at least k keys >= it is kept (16 passes for the 31 bits of a
+// non-negative float).  The rest is as in the LDS kernel below: keys > T,
+// then keys == T in channel order up to k, written in ascending channel order.
+template <int CH>
+__global__ __launch_bounds__(256) void resq_select_reg_kernel(
+    const float* __restrict__ partials, int64_t K, Units units,
+    const int32_t* __restrict__ tile_start, int32_t k, int32_t* __restrict__ sel_idx,
+    float* __restrict__ r_global) {
+  __shared__ uint32_t sh[2][3][4];
+  const int64_t u = blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t b, e;
+  units.range(u, b, e);
+  int32_t* out = sel_idx + u * k;
+  if (e == b) {                               // empty unit: channels 0..k-1, g_R = 1
+    for (int j = tid; j < k; j += blockDim.x) out[j] = j;
+    if (tid == 0) r_global[u] = 1.0f;
+    return;
+  }
+  const int64_t t0 = tile_start[u], t1 = tile_start[u + 1];
+  const int64_t c0 = (int64_t)tid * CH;
+  const int n_my = (int)(c0 >= K ? 0 : (c0 + CH <= K ? CH : K - c0));
+  float acc[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) acc[j] = 0.0f;
+  if (n_my == CH) {                           // K % 16 == 0: whole 16-byte groups
+    for (int64_t t = t0; t < t1; ++t) {       // tile order
+      const f32x4* src = reinterpret_cast<const f32x4*>(partials + t * K + c0);
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q) {
+        const f32x4 v = src[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * q + i] = acc[4 * q + i] + v[i];
+      }
+    }
+  } else {
+    for (int64_t t = t0; t < t1; ++t)
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        if (j < n_my) acc[j] = acc[j] + partials[t * K + c0 + j];
+  }
+  uint32_t key[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) key[j] = __float_as_uint(acc[j]);
+
+  // per-thread counts are at most CH (<= 32): 6 bit planes
+  constexpr int kBits = 6;
+  uint32_t T = 0;
+  int parity = 0;
+  for (int hi = 30; hi >= 0; hi -= 2) {       // bits hi and hi - 1; the last pass bit 0 alone
+    const int lo = hi > 0 ? hi - 1 : 0;
+    const uint32_t c1 = T | (1u << lo), c2 = T | (2u << lo), c3 = T | (3u << lo);
+    uint32_t n1 = 0, n2 = 0, n3 = 0;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {            // padding keys (0) are below every candidate
+      n1 += (uint32_t)(key[j] >= c1);
+      n2 += (uint32_t)(key[j] >= c2);
+      n3 += (uint32_t)(key[j] >= c3);
+    }
+    block_sum3_small<kBits>(n1, n2, n3, sh, parity);
+    parity ^= 1;
+    if (hi > 0 && n3 >= (uint32_t)k) T = c3;
+    else if (hi > 0 && n2 >= (uint32_t)k) T = c2;
+    else if (n1 >= (uint32_t)k) T = c1;
+  }
+  uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {              // branch-free: padding keys are not channels
+    const uint32_t valid = (uint32_t)(j < n_my);
+    n_gt += valid & (uint32_t)(key[j] > T);
+    n_eq += valid & (uint32_t)(key[j] == T);
+  }
+  uint32_t tot_gt, tot_eq;
+  block_scan_small<kBits>(n_gt, &tot_gt, sh, parity);
+  parity ^= 1;
+  const uint32_t remaining = (uint32_t)k - tot_gt;            // keys == T to take
+  const uint32_t eq_before = block_scan_small<kBits>(n_eq, &tot_eq, sh, parity);
+  parity ^= 1;
+  uint32_t take = 0, n_sel = 0, eq_seen = eq_before;   // take: bit j = channel c0 + j selected
+#pragma unroll
+  for (int j = 0; j < CH; ++j) {
+    const uint32_t valid = (uint32_t)(j < n_my);
+    const uint32_t is_eq = valid & (uint32_t)(key[j] == T);
+    const uint32_t t = valid & ((uint32_t)(key[j] > T) | (is_eq & (uint32_t)(eq_seen < remaining)));
+    eq_seen += is_eq;
+    take |= t << j;
+    n_sel += t;
+  }
+  uint32_t tot;
+  uint32_t pos = block_scan_small<kBits>(n_sel, &tot, sh, parity);
+  while (take) {                              // ascending channel order
+    const int j = __builtin_ctz(take);
+    take &= take - 1;
+    if (pos < (uint32_t)k) out[pos++] = (int32_t)(c0 + j);
+  }
+}
+
 // Keys live in LDS chunk by chunk: thread t owns channels [t*chunk, (t+1)*chunk)
 // stored at t*(chunk+1) + j, one pad word per chunk so that the 64 lanes of a
 // wave reading "their" j-th key hit different banks.
@@ -419,14 +580,28 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
                                                     units, ws.tile_start, ws.partials);
     partials = ws.partials;
   }
-  const size_t sel_lds = (size_t)256 * ((K + 255) / 256 + 1) * 4;
-  if (sel_lds > 65536) {
-    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&resq_select_kernel),
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
-    if (err != hipSuccess) return err;
+  if (K <= 256 * 4) {
+    resq_select_reg_kernel<4><<<(unsigned)U, 256, 0, stream>>>(partials, K, units, ws.tile_start, k,
+                                                               sel_idx, r_global);
+  } else if (K <= 256 * 8) {
+    resq_select_reg_kernel<8><<<(unsigned)U, 256, 0, stream>>>(partials, K, units, ws.tile_start, k,
+                                                               sel_idx, r_global);
+  } else if (K <= 256 * 16) {
+    resq_select_reg_kernel<16><<<(unsigned)U, 256, 0, stream>>>(partials, K, units, ws.tile_start, k,
+                                                                sel_idx, r_global);
+  } else if (K <= 256 * 32) {
+    resq_select_reg_kernel<32><<<(unsigned)U, 256, 0, stream>>>(partials, K, units, ws.tile_start, k,
+                                                                sel_idx, r_global);
+  } else {
+    const size_t sel_lds = (size_t)256 * ((K + 255) / 256 + 1) * 4;
+    if (sel_lds > 65536) {
+      hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&resq_select_kernel),
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sel_lds);
+      if (err != hipSuccess) return err;
+    }
+    resq_select_kernel<<<(unsigned)U, 256, sel_lds, stream>>>(partials, K, units, ws.tile_start, k,
+                                                              sel_idx, r_global);
   }
-  resq_select_kernel<<<(unsigned)U, 256, sel_lds, stream>>>(partials, K, units, ws.tile_start, k,
-                                                            sel_idx, r_global);
   if (gslots > 0) {
     resq_gather_kernel<T><<<(unsigned)gslots, 256, (size_t)k * 4, stream>>>(
         x, x_rows, K, ldx, row_index, codes, scales, g, units, ws.slot_start, sel_idx, k, ws.r_s,

@@ -129,6 +129,31 @@ def test_resq_tile_units(gpu_lib):
     assert np.array_equal(npu8(rc), rc_r)
 
 
+@pytest.mark.parametrize("k_dim,k", [(512, 400), (1536, 128), (4096, 128), (6144, 64), (8208, 128)])
+def test_resq_select_widths_and_ties(gpu_lib, k_dim, k):
+    """Selection at each channel count the select kernel distinguishes (keys
+    in registers up to 8192 channels, in LDS beyond), with exact score ties:
+    all-zero 16-blocks (score +0) and copied 16-blocks (equal scores); ties
+    go to the lower channel.  With k = 400 of 512 the threshold itself is +0."""
+    P = gpu_lib
+    m = 200
+    x = synth.activations(m, k_dim, seed=14, heavy_frac=0.01).float()
+    x[:, 16:176] = 0.0                    # ten zero blocks
+    x[:, 192:256] = x[:, 320:384]         # four copied blocks
+    x = x.to(torch.bfloat16)
+    xc = x.cuda()
+    codes, scales, g, tp = P.nvfp4_quantize(xc, tile_partials=True)
+    sel, rc, rs, rg = P.resq_select_and_requant(xc, codes, scales, g, k, tile_partials=tp)
+    x_np = x.float().numpy()
+    c_ref, s_ref, g_ref = OQ.quantize(x_np)
+    offs = list(range(0, m, 128)) + [m]
+    sel_r, rc_r, rs_r, rg_r = OQ.resq_select_and_requant(x_np, c_ref, s_ref, g_ref, offs, k)
+    assert np.array_equal(npu8(sel), sel_r)
+    assert np.array_equal(np32(rg), rg_r)
+    assert np.array_equal(npu8(rs), rs_r)
+    assert np.array_equal(npu8(rc), rc_r)
+
+
 @pytest.mark.parametrize("k", [16, 64])
 def test_resq_gathered_expert_units(gpu_lib, k):
     """Units = experts' routed tokens (gather through the slot->token map),
