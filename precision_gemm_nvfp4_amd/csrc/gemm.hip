@@ -131,7 +131,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   using L = StageLayout<BM>;
   constexpr int A_CODES = L::A_CODES, A_SC = L::A_SC, B_CODES = L::B_CODES, B_SC = L::B_SC;
   constexpr int STAGE = L::BYTES;
-  static_assert(4 * BM * 18 <= NSTAGE * STAGE, "compensation chunks fit in the stages");
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16* WS = reinterpret_cast<_Float16*>(smem + NSTAGE * STAGE);   // [BN][ws_stride]
 
@@ -160,6 +159,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   const int ws_stride = kcp + 8;
   int32_t* sel = reinterpret_cast<int32_t*>(WS + (comp ? BN * ws_stride : 0));   // [MAX_KC]
   int32_t* jr = sel + MAX_KC;                                                   // [nsteps + 1]
+  // Q(R_S) rows of the tile: chunk c of 32 compact channels at c * BM * 18
+  // bytes, codes [BM][16 B] then scales [BM][2 B]
+  unsigned char* RS = reinterpret_cast<unsigned char*>(
+      (reinterpret_cast<uintptr_t>(jr + nsteps + 1) + 15) & ~static_cast<uintptr_t>(15));
 
 
   // ---- this thread's rows: A row tid (if < BM), W row tid ------------------
@@ -290,10 +293,45 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   // a fixed LDS offset.
   RowLoad ra[2], rb[2];
   const int last = nsteps - 1;
+  // The Q(R_S) rows are loaded with the first K-steps (loads complete in
+  // order, so they are in once steps 0 and 1 are) and parked in LDS before
+  // the K loop: the compensation chunk after it waits for no global memory.
+  constexpr int kMaxChunks = MAX_KC / BK;
+  const int nchunk = kcp / BK;
+  u32x4 rq_codes[kMaxChunks];
+  uint32_t rq_sc[kMaxChunks];
+  if (comp) {
+    const bool ok = tid < rows_valid;
+    const int64_t ur = row0 + (ok ? tid : 0);
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      rq_codes[c] = u32x4{0, 0, 0, 0};
+      rq_sc[c] = 0;
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int j = c * BK + q * 16;
+        if (ok && j < kc) {
+          const u32x2 w = *reinterpret_cast<const u32x2*>(p.r_codes + ur * (kc / 2) + j / 2);
+          rq_codes[c][2 * q] = w[0];
+          rq_codes[c][2 * q + 1] = w[1];
+          rq_sc[c] |= (uint32_t)p.r_scales[ur * (kc / 16) + j / 16] << (8 * q);
+        }
+      }
+    }
+  }
   load_step(0, ra[0], rb[0]);
   load_step(1, ra[1], rb[1]);
   stage_write(0, ra[0], rb[0]);
   stage_write(1, ra[1], rb[1]);
+  if (comp && tid < BM) {
+#pragma unroll
+    for (int c = 0; c < kMaxChunks; ++c) {
+      if (c < nchunk) {
+        *reinterpret_cast<u32x4*>(RS + c * (BM * 18) + tid * 16) = rq_codes[c];
+        *reinterpret_cast<uint16_t*>(RS + c * (BM * 18) + BM * 16 + tid * 2) = (uint16_t)rq_sc[c];
+      }
+    }
+  }
   load_step(2 < last ? 2 : last, ra[0], rb[0]);
   __builtin_amdgcn_sched_barrier(0);          // keep the loop's load order in the prologue
   load_step(3 < last ? 3 : last, ra[1], rb[1]);
@@ -431,34 +469,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = acc[i][j][q] * ratio;
     scale = gr * p.w_global[e];
-    // Q(R_S) rows of the tile into LDS (chunk c of 32 compact channels at
-    // c * BM * 18 bytes: codes [BM][16 B], then scales [BM][2 B]; four chunks
-    // fit in the space of the three stages), all chunks before one barrier.
-    const int nchunk = kcp / BK;
-    if (tid < BM) {
-      const int64_t ur = row0 + tid;
-      const bool ok = tid < rows_valid;
-      for (int c = 0; c < nchunk; ++c) {
-        u32x4 codes = u32x4{0, 0, 0, 0};
-        uint32_t sc = 0;
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
-          const int j = c * BK + q * 16;
-          if (ok && j < kc) {
-            const u32x2 w = *reinterpret_cast<const u32x2*>(p.r_codes + ur * (kc / 2) + j / 2);
-            codes[2 * q] = w[0];
-            codes[2 * q + 1] = w[1];
-            sc |= (uint32_t)p.r_scales[ur * (kc / 16) + j / 16] << (8 * q);
-          }
-        }
-        unsigned char* base = smem + c * (BM * 18);
-        *reinterpret_cast<u32x4*>(base + tid * 16) = codes;
-        *reinterpret_cast<uint16_t*>(base + BM * 16 + tid * 2) = (uint16_t)sc;
-      }
-    }
-    lds_barrier();
+    // Q(R_S) x W_S over the compact channels (Q(R_S) parked in RS before
+    // the K loop, W_S gathered during it)
     for (int c = 0; c < nchunk; ++c) {
-      const unsigned char* base = smem + c * (BM * 18);
+      const unsigned char* base = RS + c * (BM * 18);
       Frags f;
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
@@ -490,7 +504,8 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int kcp = a.sel_idx ? (a.kc + BK - 1) / BK * BK : 0;
   const size_t stage = StageLayout<BM>::BYTES;
   const size_t loop_lds = NSTAGE * stage + (a.sel_idx ? (size_t)BN * (kcp + 8) * 2 : 0) +
-                          (size_t)(MAX_KC + a.K / BK + 1) * 4;
+                          ((size_t)(MAX_KC + a.K / BK + 1) * 4 + 15) / 16 * 16 +
+                          (a.sel_idx ? (size_t)(kcp / BK) * BM * 18 : 0);
   const size_t epi_lds = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
   const size_t lds = loop_lds > epi_lds ? loop_lds : epi_lds;
   auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, EPI>;

@@ -11,7 +11,11 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
   return v < lo ? lo : (v > hi ? hi : v);
 }
 
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
+// silu(z) = z / (1 + e^-z), with the hardware reciprocal (about 1 ulp) in
+// place of a correctly rounded division; z -> -inf gives -0.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 struct TileCoord {
   int e;            // expert
@@ -173,7 +177,10 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&
     }
   } else {
     // SwiGLU: block j (even) is gate, j+1 is up, for the same 32 channels;
-    // h = bf16(silu(gate) * up) staged as 16-bit values.
+    // h = bf16(silu(gate) * up) staged as 16-bit values.  Rows q and q + 1 of
+    // a lane are rounded by one packed convert.  The amax is taken over the
+    // fp32 values and rounded once at the end: rounding to nearest is
+    // monotonic, so that equals the largest |h| of the bf16 outputs.
     const int64_t inter = p.N / 2;
     uint16_t* out = static_cast<uint16_t*>(p.out);
     uint16_t* lh = reinterpret_cast<uint16_t*>(lds);
@@ -187,16 +194,21 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
 #pragma unroll
-      for (int j = 0; j < NJ; j += 2)
+      for (int j = 0; j < NJ; j += 2) {
+        const float col_ok = c0 + (j / 2) * 32 + l32 < inter ? 1.0f : 0.0f;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int rl = (q >> 2) * 8 + half * 4 + (q & 3);
-          const float gte = acc[i][j][q] * scale, up = acc[i][j + 1][q] * scale;
-          const uint32_t hb = f32_to_bf16_rne(silu_f32(gte) * up);
-          const bool valid = wr0 + i * 32 + rl < t.rows_valid && c0 + (j / 2) * 32 + l32 < inter;
-          if (valid) m = fmaxf(m, fabsf(__uint_as_float(hb << 16)));
+        for (int q = 0; q < 16; q += 2) {
+          const int rl = (q >> 2) * 8 + half * 4 + (q & 3);        // rows rl and rl + 1
+          const float v0 = silu_f32(acc[i][j][q] * scale) * (acc[i][j + 1][q] * scale);
+          const float v1 = silu_f32(acc[i][j][q + 1] * scale) * (acc[i][j + 1][q + 1] * scale);
+          const uint32_t hb = pack_bf16x2_rne(v0, v1);
           lh[rl * HS + (j / 2) * 32 + l32] = (uint16_t)hb;
+          lh[(rl + 1) * HS + (j / 2) * 32 + l32] = (uint16_t)(hb >> 16);
+          const float ok0 = wr0 + i * 32 + rl < t.rows_valid ? col_ok : 0.0f;
+          const float ok1 = wr0 + i * 32 + rl + 1 < t.rows_valid ? col_ok : 0.0f;
+          m = fmaxf(m, fmaxf(fabsf(v0 * ok0), fabsf(v1 * ok1)));
         }
+      }
       __builtin_amdgcn_s_waitcnt(0xc07f);
 #pragma unroll
       for (int rr = 0; rr < 32; rr += RPI) {
@@ -216,6 +228,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&
       }
       __builtin_amdgcn_s_waitcnt(0xc07f);
     }
+    m = __uint_as_float(f32_to_bf16_rne(m) << 16);
     if (p.out_amax) {
       m = wave_max(m);
       if (lane == 0) atomic_max_nonneg(p.out_amax, m);
