@@ -69,6 +69,18 @@ namespace nvfp4 {
 
 constexpr int BN = 256, BK = 32;
 
+// 32-channel chunks of a padded compensation width
+__host__ __device__ constexpr int nchunk_of(int kcp) { return kcp / 32; }
+
+// LDS bytes of the epilogue staging (four waves), and the offset of the
+// scatter epilogue's row weights: past the K-loop region (loop_end bytes) and
+// the staging.
+template <int NJ>
+__host__ __device__ constexpr size_t epilogue_lds_bytes() { return (size_t)4 * epilogue_wave_floats<NJ>() * 4; }
+__host__ __device__ constexpr size_t rw_offset(size_t loop_end, size_t epi_end) {
+  return ((loop_end > epi_end ? loop_end : epi_end) + 15) / 16 * 16;
+}
+
 template <int V>
 struct IntC {
   static constexpr int value = V;
@@ -163,6 +175,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   // bytes, codes [BM][16 B] then scales [BM][2 B]
   unsigned char* RS = reinterpret_cast<unsigned char*>(
       (reinterpret_cast<uintptr_t>(jr + nsteps + 1) + 15) & ~static_cast<uintptr_t>(15));
+  // scatter epilogue: row_weight of the tile's rows [BM] (0 past the group),
+  // past both the K-loop region and the epilogue's staging (which it outlives)
+  float* RW = reinterpret_cast<float*>(
+      smem + rw_offset((size_t)(RS - smem) + (comp ? (size_t)nchunk_of(kcp) * BM * 18 : 0),
+                       epilogue_lds_bytes<NJ>()));
 
 
   // ---- this thread's rows: A row tid (if < BM), W row tid ------------------
@@ -297,7 +314,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   // order, so they are in once steps 0 and 1 are) and parked in LDS before
   // the K loop: the compensation chunk after it waits for no global memory.
   constexpr int kMaxChunks = MAX_KC / BK;
-  const int nchunk = kcp / BK;
+  const int nchunk = nchunk_of(kcp);
   u32x4 rq_codes[kMaxChunks];
   uint32_t rq_sc[kMaxChunks];
   if (comp) {
@@ -319,10 +336,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
       }
     }
   }
+  float rw = 0.0f;
+  if (EPI == 2 && tid < rows_valid) rw = p.row_weight[row0 + tid];
   load_step(0, ra[0], rb[0]);
   load_step(1, ra[1], rb[1]);
   stage_write(0, ra[0], rb[0]);
   stage_write(1, ra[1], rb[1]);
+  if (EPI == 2 && tid < BM) RW[tid] = rw;
   if (comp && tid < BM) {
 #pragma unroll
     for (int c = 0; c < kMaxChunks; ++c) {
@@ -492,7 +512,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 
   __syncthreads();                             // LDS free for the epilogue staging
   gemm_epilogue<MI, NJ, BN, EPI>(p, acc, tc, wm * MI * 32, wn * NJ * 32, scale,
-                            reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>());
+                            reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>(), RW);
 }
 
 template <int MI, int NJ, int WM, int WN, int EPI>
@@ -505,9 +525,10 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const size_t stage = StageLayout<BM>::BYTES;
   const size_t loop_lds = NSTAGE * stage + (a.sel_idx ? (size_t)BN * (kcp + 8) * 2 : 0) +
                           ((size_t)(MAX_KC + a.K / BK + 1) * 4 + 15) / 16 * 16 +
-                          (a.sel_idx ? (size_t)(kcp / BK) * BM * 18 : 0);
-  const size_t epi_lds = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
-  const size_t lds = loop_lds > epi_lds ? loop_lds : epi_lds;
+                          (a.sel_idx ? (size_t)nchunk_of(kcp) * BM * 18 : 0);
+  const size_t epi_lds = epilogue_lds_bytes<NJ>();
+  const size_t lds = EPI == 2 ? rw_offset(loop_lds, epi_lds) + (size_t)BM * 4
+                              : (loop_lds > epi_lds ? loop_lds : epi_lds);
   auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, EPI>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -132,11 +132,11 @@ constexpr int epilogue_wave_floats() { return 32 * (NJ * 32 + 8); }
 // epilogue_wave_floats<NJ>() floats) so that it leaves as whole row segments
 // with 16-byte stores (a store per element would write 4 bytes per lane
 // into rows far apart).  The caller has synchronized the workgroup, so the
-// region is free.
+// region is free.  rw_lds: the tile's row weights (scatter epilogue).
 template <int MI, int NJ, int BN, int EPI>
 __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&acc)[MI][NJ],
                                               const TileCoord& t, int wr0, int wc0, float scale,
-                                              float* lds) {
+                                              float* lds, const float* rw_lds) {
   constexpr int CS = NJ * 32 + 8;               // LDS row stride (floats)
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   if constexpr (EPI == 0 || EPI == 2) {
@@ -162,7 +162,7 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&
         const f32x4 v = *reinterpret_cast<const f32x4*>(lds + rl * CS + c4);
         if (r < t.rows_valid) {
           const int64_t s2 = t.row0 + r;
-          const float w = scatter ? p.row_weight[s2] : 1.0f;
+          const float w = scatter ? rw_lds[r] : 1.0f;      // row_weight[s2], staged in LDS
           float* dst = out + s2 * ld + n0 + c4;
           if (vec && n0 + c4 + 4 <= p.N) {
             *reinterpret_cast<f32x4*>(dst) = f32x4{v[0] * w, v[1] * w, v[2] * w, v[3] * w};
