@@ -34,7 +34,9 @@
 // fragment per MFMA.  One barrier per step.  On gfx950 a SIMD does not run
 // VALU instructions while an MFMA executes, so the dequantization adds to the
 // MFMA time (about 4.5 VALU instructions per MFMA for a 128 x 128 wave tile);
-// the schedule keeps the MFMA pipe from also waiting on LDS or memory.
+// the schedule keeps the MFMA pipe from also waiting on LDS or memory.  The
+// 32-row tile, bound by memory rather than MFMA, uses 128-K stages with
+// coalesced loads instead (MacroTile below).
 //
 // The compensation term is an extra chunk of kc: while the main loop streams
 // the expert's weight tile through LDS, the elements of the selected columns
@@ -130,6 +132,31 @@ struct StageLayout {
   static constexpr int BYTES = (B_SC + BN * 2 + 15) / 16 * 16;
 };
 
+// The 32-row tile (MI = WM = 1) streams W with little reuse (a decode batch
+// gives each expert a few rows), so it is bound by the memory system rather
+// than the matrix cores, and it moves 128 K per pipeline stage instead of 32:
+// four lanes load one row's 64 contiguous code bytes (one 64-byte request
+// where the 32-wide stage needs four 16-byte ones, plus as many for the scale
+// bytes), and there is one barrier per 128 K.  LDS row: 64 code bytes then
+// the 8 scale bytes of its blocks; the 72-byte row stride makes the 8-byte
+// fragment reads of 32 consecutive rows conflict-free.
+template <int MI, int WM>
+struct MacroTile {
+  static constexpr bool on = MI == 1 && WM == 1;
+};
+template <int BM>
+struct MacroLayout {
+  static constexpr int KM = 128;              // K per stage
+  static constexpr int ROW = 72;
+  static constexpr int A_OFF = 0;             // A rows [BM + 1] (row BM: the spare)
+  static constexpr int B_OFF = (BM + 1) * ROW;
+  static constexpr int BYTES = (B_OFF + BN * ROW + 15) / 16 * 16;
+};
+template <int MI, int WM>
+__host__ __device__ constexpr int stage_bytes() {
+  return MacroTile<MI, WM>::on ? MacroLayout<WM * MI * 32>::BYTES : StageLayout<WM * MI * 32>::BYTES;
+}
+
 // EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows), fixed per kernel.
 template <int MI, int NJ, int WM, int WN, int EPI>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles) {
@@ -142,7 +169,8 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   // their A data into the spare row, so staging has no branch.
   using L = StageLayout<BM>;
   constexpr int A_CODES = L::A_CODES, A_SC = L::A_SC, B_CODES = L::B_CODES, B_SC = L::B_SC;
-  constexpr int STAGE = L::BYTES;
+  constexpr bool kMacro = MacroTile<MI, WM>::on;
+  constexpr int STAGE = stage_bytes<MI, WM>();
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   _Float16* WS = reinterpret_cast<_Float16*>(smem + NSTAGE * STAGE);   // [BN][ws_stride]
 
@@ -230,11 +258,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     for (int i = tid; i < BN * ws_stride / 8; i += 256)
       reinterpret_cast<u32x4*>(WS)[i] = u32x4{0, 0, 0, 0};
     __syncthreads();
-    for (int s = tid; s <= nsteps; s += 256) {
-      int lo = 0, hi = kc;                    // first j with sel[j] >= s * BK
+    // jr[s]: the first j with sel[j] in pipeline stage s or later
+    constexpr int KSTEP = kMacro ? MacroLayout<BM>::KM : BK;
+    const int nst = kMacro ? (int)((K + KSTEP - 1) / KSTEP) : nsteps;
+    for (int s = tid; s <= nst; s += 256) {
+      int lo = 0, hi = kc;
       while (lo < hi) {
         int mid = (lo + hi) >> 1;
-        if (sel[mid] < s * BK) lo = mid + 1; else hi = mid;
+        if (sel[mid] < s * KSTEP) lo = mid + 1; else hi = mid;
       }
       jr[s] = lo;
     }
@@ -296,19 +327,165 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     }
   };
 
+  // ---- 128-K pipeline of the 32-row tile (MacroTile) -----------------------
+  // Stage m covers K [128 m, 128 m + 128): code bytes [64 m, 64 m + 64) and
+  // scale bytes [8 m, 8 m + 8) of every row.  Thread t loads the 16 code bytes
+  // 16 (t % 4) .. of W rows t / 4 + 64 i (i = 0..3) and of A row t / 4, and
+  // the 8 scale bytes of W row t and A row t; threads past the tile's A rows
+  // load row 0 and write the spare LDS row.  When K is not a multiple of 128
+  // the last stage is half full: its missing code bytes are read from the
+  // row's start and its missing blocks get scale 0 in A and W, so they add
+  // nothing.  Two LDS stages and two register sets: in stage m a wave reads
+  // its raw fragments of stage m, writes the data of stage m + 1 into the
+  // other LDS stage and issues the loads of stage m + 3 into the register set
+  // just written, so loads have two stages (256 K) to arrive.
+  //
+  // K order of one stage: MFMA substep q (0..7) takes, in lane half h, the 8
+  // codes 8 (q % 4) .. of 16-byte granule 2 (q / 4) + h (granule G holds
+  // blocks 2G and 2G + 1), the same in A and W, so every k of the stage is
+  // summed once.
+  auto macro_loop = [&](auto&& park) {
+    using ML = MacroLayout<BM>;
+    constexpr int KM = ML::KM, ROW = ML::ROW, AO = ML::A_OFF, BO = ML::B_OFF;
+    typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
+    const int nmac = (int)((K + KM - 1) / KM);
+    const int mlast = nmac - 1;
+    const bool half_last = (K % KM) != 0;
+    const int g4 = tid & 3;
+    const int64_t rbytes = K / 2;
+    int64_t ac = 0;                            // A row of the code loads: tile row tid / 4
+    if ((tid >> 2) < rows_valid) {
+      const int64_t ur = row0 + (tid >> 2);
+      ac = p.a_row_index ? (int64_t)p.a_row_index[ur] : ur;
+      if (ac < 0 || ac >= p.a_rows) ac = 0;    // its scales (row tid / 4's) are zero
+    }
+    const uint8_t* a_cm = p.a_codes + ac * rbytes + g4 * 16;
+    const uint8_t* b_cm[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t br = weight_row<BN>(p, n_tile, i * 64 + (tid >> 2));
+      b_cm[i] = p.w_codes + ((int64_t)e * p.N + (br >= 0 ? br : 0)) * rbytes + g4 * 16;
+    }
+    const uint32_t am32 = a_mask ? 0xFFFFFFFFu : 0u;
+
+    struct MacLoad {
+      u32x4 wc[4], ac;
+      u32x2 ws, as;
+    };
+    auto mload = [&](int m, MacLoad& r) {
+      const int64_t cb = (int64_t)m * 64;
+      const int64_t co = cb + g4 * 16 < rbytes ? cb : -(int64_t)g4 * 16;   // past K: row start
+      const bool part = half_last && m == mlast;
+      const int64_t so = part ? (int64_t)m * 8 - 4 : (int64_t)m * 8;      // 4 valid bytes: the high half
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r.wc[i] = *reinterpret_cast<const u32x4*>(b_cm[i] + co);
+      r.ac = *reinterpret_cast<const u32x4*>(a_cm + co);
+      const u32x2a ws = *reinterpret_cast<const u32x2a*>(b_sp + so);
+      const u32x2a as = *reinterpret_cast<const u32x2a*>(a_sp + so);
+      r.ws = part ? u32x2{ws[1], 0u} : u32x2{ws[0], ws[1]};
+      r.as = part ? u32x2{as[1] & am32, 0u} : u32x2{as[0] & am32, as[1] & am32};
+    };
+    auto mwrite = [&](int st, const MacLoad& r) {
+      unsigned char* base = smem + st * STAGE;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        unsigned char* d = base + BO + (i * 64 + (tid >> 2)) * ROW + g4 * 16;
+        *reinterpret_cast<u32x2*>(d) = u32x2{r.wc[i][0], r.wc[i][1]};
+        *reinterpret_cast<u32x2*>(d + 8) = u32x2{r.wc[i][2], r.wc[i][3]};
+      }
+      *reinterpret_cast<u32x2*>(base + BO + tid * ROW + 64) = r.ws;
+      unsigned char* da = base + AO + ((tid >> 2) < BM ? (tid >> 2) : BM) * ROW + g4 * 16;
+      *reinterpret_cast<u32x2*>(da) = u32x2{r.ac[0], r.ac[1]};
+      *reinterpret_cast<u32x2*>(da + 8) = u32x2{r.ac[2], r.ac[3]};
+      *reinterpret_cast<u32x2*>(base + AO + (tid < BM ? tid : BM) * ROW + 64) = r.as;
+    };
+    // A fragment row's raw data of a stage: granules h and 2 + h, and the
+    // scale pairs of their blocks as fp16 ({2h, 2h+1} and {4+2h, 5+2h})
+    struct RawRow {
+      u32x2 g0a, g0b, g1a, g1b;
+      f16x2 s0, s1;
+    };
+    auto read_raw = [&](const unsigned char* row, RawRow& o) {
+      o.g0a = *reinterpret_cast<const u32x2*>(row + half * 16);
+      o.g0b = *reinterpret_cast<const u32x2*>(row + half * 16 + 8);
+      o.g1a = *reinterpret_cast<const u32x2*>(row + 32 + half * 16);
+      o.g1b = *reinterpret_cast<const u32x2*>(row + 32 + half * 16 + 8);
+      const u32x2 sc = *reinterpret_cast<const u32x2*>(row + 64);
+      o.s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[0] >> (16 * half), 1.0f, false);
+      o.s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[1] >> (16 * half), 1.0f, false);
+    };
+    auto frag_q = [&](const RawRow& o, int q) {
+      const u32x2 g = q < 4 ? ((q & 2) ? o.g0b : o.g0a) : ((q & 2) ? o.g1b : o.g1a);
+      const f16x2 sp = q < 4 ? o.s0 : o.s1;
+      const _Float16 sv = (q & 2) ? sp[1] : sp[0];
+      return dequant8(g[q & 1], f16x2{sv, sv});
+    };
+    auto gather_ws_m = [&](int m, int st) {
+      const unsigned char* row = smem + st * STAGE + BO + tid * ROW;
+      const int j1 = jr[m + 1];
+      for (int jj = jr[m]; jj < j1; ++jj) {
+        const int kk = sel[jj] - m * KM;                      // 0..127 inside the stage
+        const uint32_t byte = row[kk >> 1] >> (4 * (kk & 1));
+        const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(byte, 1.0f, 0);
+        const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(row[64 + (kk >> 4)], 1.0f, false);
+        WS[tid * ws_stride + jj] = v[0] * sc[0];
+      }
+    };
+    auto mstep = [&](int m, int st, MacLoad& rset) {
+      const unsigned char* base = smem + st * STAGE;
+      RawRow ra_, rb_[NJ];
+      read_raw(base + AO + l32 * ROW, ra_);
+#pragma unroll
+      for (int j = 0; j < NJ; ++j) read_raw(base + BO + (wn * NJ * 32 + j * 32 + l32) * ROW, rb_[j]);
+      if (comp) gather_ws_m(m, st);
+      mwrite(st ^ 1, rset);                     // data of stage m + 1
+      mload(m + 3 < nmac ? m + 3 : mlast, rset);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        const f16x8 fa = frag_q(ra_, q);
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, frag_q(rb_[j], q), acc[0][j], 0, 0, 0);
+      }
+    };
+
+    MacLoad R0, R1;
+    mload(0, R0);
+    mload(1 < nmac ? 1 : mlast, R1);
+    park();
+    mwrite(0, R0);
+    mload(2 < nmac ? 2 : mlast, R0);
+    lds_barrier();
+    int m = 0;
+    for (; m + 2 <= nmac; m += 2) {
+      mstep(m, 0, R1);
+      lds_barrier();
+      mstep(m + 1, 1, R0);
+      lds_barrier();
+    }
+    if (m < nmac) {
+      mstep(m, 0, R1);
+      lds_barrier();
+    }
+  };
+
   // ---- main K loop ----------------------------------------------------------
   // Step s: MFMAs on the fragments of step s (registers), while the fragments
   // of step s+1 are read from LDS stage (s+1)%2 and dequantized (and the
   // selected W columns of step s+1 copied into W_S), the raw data of step s+2
-  // goes from registers into stage s%2 and the loads of step s+4 are issued.
+  // goes from register set s%PD into stage s%2 and the loads of step s+2+PD
+  // are issued into that set: PD K-steps between a load and its use.  Small
+  // tiles (BM <= 64) have short K-steps, so they keep more loads in flight
+  // (PD = 4) to cover the memory latency; large tiles use PD = 2.
   // One barrier per step: it orders this step's writes of stage s%2 before
   // the next step's reads of it, and this step's reads of stage (s+1)%2
   // before the next step's writes.  Every load is issued unconditionally (a step past
   // the end re-reads the last step; its stage is never read), so the compiler
   // waits only for the older step's loads.  K is a multiple of 64, so nsteps
-  // is even and at least 2, and the loop, unrolled by two, sees each stage at
-  // a fixed LDS offset.
-  RowLoad ra[2], rb[2];
+  // is even and at least 2, and the loop, unrolled by PD (plus two steps when
+  // nsteps % PD == 2), sees each stage and register set at a fixed place.
+  constexpr int PD = BM <= 64 ? 4 : 2;
+  RowLoad ra[PD], rb[PD];
   const int last = nsteps - 1;
   // The Q(R_S) rows are loaded with the first K-steps (loads complete in
   // order, so they are in once steps 0 and 1 are) and parked in LDS before
@@ -338,23 +515,32 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   }
   float rw = 0.0f;
   if (EPI == 2 && tid < rows_valid) rw = p.row_weight[row0 + tid];
+  auto park_rows = [&]() {                    // row weights and Q(R_S) rows into LDS
+    if (EPI == 2 && tid < BM) RW[tid] = rw;
+    if (comp && tid < BM) {
+#pragma unroll
+      for (int c = 0; c < kMaxChunks; ++c) {
+        if (c < nchunk) {
+          *reinterpret_cast<u32x4*>(RS + c * (BM * 18) + tid * 16) = rq_codes[c];
+          *reinterpret_cast<uint16_t*>(RS + c * (BM * 18) + BM * 16 + tid * 2) = (uint16_t)rq_sc[c];
+        }
+      }
+    }
+  };
+  if constexpr (kMacro) {
+    macro_loop(park_rows);
+  } else {
   load_step(0, ra[0], rb[0]);
   load_step(1, ra[1], rb[1]);
   stage_write(0, ra[0], rb[0]);
   stage_write(1, ra[1], rb[1]);
-  if (EPI == 2 && tid < BM) RW[tid] = rw;
-  if (comp && tid < BM) {
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      if (c < nchunk) {
-        *reinterpret_cast<u32x4*>(RS + c * (BM * 18) + tid * 16) = rq_codes[c];
-        *reinterpret_cast<uint16_t*>(RS + c * (BM * 18) + BM * 16 + tid * 2) = (uint16_t)rq_sc[c];
-      }
-    }
-  }
+  park_rows();
   load_step(2 < last ? 2 : last, ra[0], rb[0]);
-  __builtin_amdgcn_sched_barrier(0);          // keep the loop's load order in the prologue
-  load_step(3 < last ? 3 : last, ra[1], rb[1]);
+#pragma unroll
+  for (int i = 1; i < PD; ++i) {
+    __builtin_amdgcn_sched_barrier(0);        // keep the loop's load order in the prologue
+    load_step(2 + i < last ? 2 + i : last, ra[i], rb[i]);
+  }
   lds_barrier();
   if (comp) gather_ws(0, 0);
 
@@ -420,7 +606,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
         }
       }
       if (m == 1) stage_write(st, ta, tb);                    // data of step s+2
-      if (m == 2) load_step(s + 4 < last ? s + 4 : last, ta, tb);
+      if (m == 2) load_step(s + 2 + PD < last ? s + 2 + PD : last, ta, tb);
       if (m >= kDeq0 || kMf <= kDeq0) {
 #pragma unroll
         for (int hf = 0; hf < 2 * kFr; ++hf) {
@@ -452,11 +638,26 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     __builtin_amdgcn_sched_barrier(0);
     if (comp && s + 1 < nsteps) gather_ws(s + 1, st ^ 1);
   };
-  for (int s = 0; s < nsteps; s += 2) {
+  int s = 0;
+  for (; s + PD <= nsteps; s += PD) {
     step(s, 0, fr[0], fr[1], ra[0], rb[0]);
     lds_barrier();
     step(s + 1, 1, fr[1], fr[0], ra[1], rb[1]);
     lds_barrier();
+    if constexpr (PD == 4) {
+      step(s + 2, 0, fr[0], fr[1], ra[2], rb[2]);
+      lds_barrier();
+      step(s + 3, 1, fr[1], fr[0], ra[3], rb[3]);
+      lds_barrier();
+    }
+  }
+  if constexpr (PD == 4) {
+    if (s < nsteps) {                          // nsteps % 4 == 2
+      step(s, 0, fr[0], fr[1], ra[0], rb[0]);
+      lds_barrier();
+      step(s + 1, 1, fr[1], fr[0], ra[1], rb[1]);
+      lds_barrier();
+    }
   }
   };
   // The number of this wave's 32-row A fragments that hold rows of the tile
@@ -475,6 +676,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     case 2: if constexpr (MI >= 2) main_loop(IntC<2>{}); break;
     case 3: if constexpr (MI >= 3) main_loop(IntC<3>{}); break;
     default: main_loop(IntC<MI>{}); break;
+  }
   }
 
   // ---- compensation chunk ---------------------------------------------------
@@ -522,7 +724,7 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int64_t ntiles = a.epilogue == 1 ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const int64_t total = mtiles * ntiles;
   const int kcp = a.sel_idx ? (a.kc + BK - 1) / BK * BK : 0;
-  const size_t stage = StageLayout<BM>::BYTES;
+  const size_t stage = stage_bytes<MI, WM>();
   const size_t loop_lds = NSTAGE * stage + (a.sel_idx ? (size_t)BN * (kcp + 8) * 2 : 0) +
                           ((size_t)(MAX_KC + a.K / BK + 1) * 4 + 15) / 16 * 16 +
                           (a.sel_idx ? (size_t)nchunk_of(kcp) * BM * 18 : 0);
@@ -571,7 +773,8 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
     case 256: err = launch_epi<4, 4, 2, 2>(a, stream); break;
     case 128: err = launch_epi<2, 4, 2, 2>(a, stream); break;
     case 64: err = launch_epi<1, 4, 2, 2>(a, stream); break;
-    default: err = launch_epi<1, 2, 1, 4>(a, stream); break;
+    // the 32-row tile moves 128 K per stage: K = 64 takes the 64-row tile
+    default: err = a.K >= 128 ? launch_epi<1, 2, 1, 4>(a, stream) : launch_epi<1, 4, 2, 2>(a, stream); break;
   }
   if (err != hipSuccess || a.epilogue != 2) return err;
   return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,

@@ -231,10 +231,23 @@ def _moe_setup(P, tokens, hidden, n_exp, inter, k, seed, zipf=0.0, top_k=8, empt
 
 @pytest.mark.parametrize("comp", [True, False])
 def test_grouped_gemm_swiglu_and_scatter(gpu_lib, comp):
-    P = gpu_lib
-    tokens, hidden, n_exp, inter, k = 200, 256, 8, 192, 32
-    x, rt, offs, wgu, wd = _moe_setup(P, tokens, hidden, n_exp, inter, k, seed=9, zipf=1.2,
-                                      top_k=4, empty_expert=5)
+    _check_moe_layer(gpu_lib, 200, 256, 8, 192, 32, seed=9, zipf=1.2, top_k=4, empty_expert=5,
+                     comp=comp)
+
+
+@pytest.mark.parametrize("hidden,inter", [(64, 64), (128, 192), (192, 128), (1024, 320)])
+def test_grouped_gemm_32row_tiles(gpu_lib, hidden, inter):
+    """16 rows per expert (the 32-row tile, which moves 128 K per stage): K a
+    multiple of 128, K with a half-full last stage (192, 320), and K = 64
+    (served by the 64-row tile); gate/up with SwiGLU, down with scatter-add,
+    both compensated."""
+    _check_moe_layer(gpu_lib, 64, hidden, 16, inter, 32, seed=23, zipf=0.0, top_k=4,
+                     empty_expert=3, comp=True)
+
+
+def _check_moe_layer(P, tokens, hidden, n_exp, inter, k, seed, zipf, top_k, empty_expert, comp):
+    x, rt, offs, wgu, wd = _moe_setup(P, tokens, hidden, n_exp, inter, k, seed=seed, zipf=zipf,
+                                      top_k=top_k, empty_expert=empty_expert)
     xc = x.cuda()
     rows = int(offs[-1])
     offs_t = torch.from_numpy(offs).cuda()
