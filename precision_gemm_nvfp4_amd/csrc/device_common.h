@@ -93,10 +93,54 @@ __device__ __forceinline__ uint32_t e4m3_nearest(double q) {
   return byte > 0x7Eu ? 0x7Eu : byte;
 }
 
+// Per-tensor constants of the block-scale choice for global scale g.
+struct BlockScaler {
+  float g;
+  float inv_up, inv_dn;                      // 1/(6g) times (1 + 2^-20), (1 - 2^-20)
+  double six_g;
+  bool fast;                                 // g >= 2^-100: the fp32 path below is exact
+};
+__device__ __forceinline__ BlockScaler make_block_scaler(float g) {
+  BlockScaler b;
+  b.g = g;
+  b.six_g = 6.0 * (double)g;
+  b.fast = g >= 0x1p-100f;
+  const float inv = __builtin_amdgcn_rcpf(6.0f * g);
+  b.inv_up = inv * (1.0f + 0x1p-20f);
+  b.inv_dn = inv * (1.0f - 0x1p-20f);
+  return b;
+}
+
 // Block scale byte and effective fp32 scale S_b for a block amax.
-__device__ __forceinline__ uint32_t block_scale(float amax_b, double six_g, float g, float& S) {
-  uint32_t sb = e4m3_nearest((double)amax_b / six_g);
-  S = e4m3_value(sb) * g;                    // RNE32(s_b * g): one rounding
+// The byte is the E4M3 value nearest to the exact quotient q = amax_b / (6g)
+// (ties to even, saturating at 448), as e4m3_nearest decides it.  Fast path:
+// amax_b * inv_up and amax_b * inv_dn bracket q (1/(6g) is within 2^-22 of
+// exact after the rounding of 6g, the reciprocal and the two products, well
+// inside the 2^-20 margins), and the hardware FP8 convert (round to nearest
+// even) of both, clamped to 448, gives the byte wherever they agree.  Where
+// they differ, exactly one rounding boundary m (the midpoint of the two
+// adjacent values, at most 5 significant bits) lies between them, and the sign
+// of fma(6m, g, -amax_b) -- 6m is exact, so this is 6mg - amax_b rounded once,
+// which keeps its sign and is zero only on a tie (no underflow to zero for
+// g >= 2^-100) -- picks the side; a tie goes to the even byte.
+__device__ __forceinline__ uint32_t block_scale(float amax_b, const BlockScaler& bs, float& S) {
+  uint32_t sb;
+  if (bs.fast) {
+    const float qu = fminf(amax_b * bs.inv_up, 448.0f), qd = fminf(amax_b * bs.inv_dn, 448.0f);
+    typedef short s16x2 __attribute__((ext_vector_type(2)));
+    const s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2{0, 0}, qu, qd, 1.0f, false);
+    const uint32_t w = (uint16_t)r[0];
+    const uint32_t bu = w & 0xFFu, bd = w >> 8;
+    sb = bu;
+    if (bu != bd) {                            // rare: q near a rounding boundary
+      const float m = 0.5f * (e4m3_value(bd) + e4m3_value(bu));   // exact
+      const float d = __builtin_fmaf(6.0f * m, bs.g, -amax_b);
+      sb = d < 0.0f ? bu : (d > 0.0f ? bd : ((bd & 1u) ? bu : bd));
+    }
+  } else {
+    sb = e4m3_nearest((double)amax_b / bs.six_g);
+  }
+  S = e4m3_value(sb) * bs.g;                 // RNE32(s_b * g): one rounding
   return sb;
 }
 
@@ -131,25 +175,27 @@ __device__ __forceinline__ uint32_t e2m1_code_exact(float x, float S) {
   return (sign << 3) | idx;
 }
 
-// Fast path for 8 elements sharing a scale.  v = x * (1/S) is within 2^-22
-// (relative) of the exact quotient; the hardware FP4 convert (round to
-// nearest even, saturating, sign kept) of v * (1 + 2^-20) and v * (1 - 2^-20)
-// brackets that error band.  Where the two agree, no rounding boundary lies in
-// the band and the code is exact.  Where they differ, exactly one midpoint m
+// Fast path for 8 elements sharing a scale.  iu and id are 1/S (within 1 ulp)
+// times (1 + 2^-20) and (1 - 2^-20), each rounded once (e2m1_brackets), so
+// x * iu and x * id lie above and below the exact quotient x / S (the three
+// roundings stay within 2^-22); the hardware FP4 convert (round to nearest
+// even, saturating, sign kept) of both brackets the exact code.  Where the
+// two agree, no rounding boundary lies in the band and the code is exact.  Where they differ, exactly one midpoint m
 // lies in the band, between the two (adjacent) magnitudes the brackets gave;
 // the sign of fma(m, S, -|x|) -- the exact m*S - |x| rounded once -- decides
 // the side, and a zero (an exact tie, common when S has few significant bits)
 // goes to the even index.  Returns the packed codes (element 2j in the low
 // nibble of byte j).
-__device__ __forceinline__ uint32_t e2m1_pack8_fast(const float* x, float inv, float S) {
-  const float up = 1.0f + 0x1p-20f, dn = 1.0f - 0x1p-20f;
+__device__ __forceinline__ void e2m1_brackets(float S, float& iu, float& id) {
+  const float inv = __builtin_amdgcn_rcpf(S);   // within 1 ulp
+  iu = inv * (1.0f + 0x1p-20f);
+  id = inv * (1.0f - 0x1p-20f);
+}
+__device__ __forceinline__ uint32_t e2m1_pack8_fast(const float* x, float iu, float id, float S) {
   uint32_t wu = 0, wd = 0;
-  float a[8];
-#pragma unroll
-  for (int i = 0; i < 8; ++i) a[i] = x[i] * inv;
 #define NVFP4_CVT_PAIR(P)                                                                   \
-  wu = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wu, a[2 * P] * up, a[2 * P + 1] * up, 1.0f, P); \
-  wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, a[2 * P] * dn, a[2 * P + 1] * dn, 1.0f, P);
+  wu = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wu, x[2 * P] * iu, x[2 * P + 1] * iu, 1.0f, P); \
+  wd = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(wd, x[2 * P] * id, x[2 * P + 1] * id, 1.0f, P);
   NVFP4_CVT_PAIR(0)
   NVFP4_CVT_PAIR(1)
   NVFP4_CVT_PAIR(2)
@@ -181,18 +227,19 @@ __device__ __forceinline__ uint32_t e2m1_pack8_exact(const float* x, float S) {
 
 // Quantize one 16-element block held in registers.  Writes the scale byte and
 // two packed code words; returns S_b.
-__device__ __forceinline__ float quantize_block16(const float* v, float g, double six_g,
+__device__ __forceinline__ float quantize_block16(const float* v, const BlockScaler& bs,
                                                   uint32_t* sbyte, uint32_t* w0, uint32_t* w1) {
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(v[i]));
   float S;
-  *sbyte = block_scale(amax, six_g, g, S);
+  *sbyte = block_scale(amax, bs, S);
   // The fast path needs 1/S finite and accurate: S >= 2^-100 (a normal number).
   if (S >= 0x1p-100f) {
-    const float inv = __builtin_amdgcn_rcpf(S);    // within 1 ulp
-    *w0 = e2m1_pack8_fast(v, inv, S);
-    *w1 = e2m1_pack8_fast(v + 8, inv, S);
+    float iu, id;
+    e2m1_brackets(S, iu, id);
+    *w0 = e2m1_pack8_fast(v, iu, id, S);
+    *w1 = e2m1_pack8_fast(v + 8, iu, id, S);
   } else {
     *w0 = e2m1_pack8_exact(v, S);
     *w1 = e2m1_pack8_exact(v + 8, S);

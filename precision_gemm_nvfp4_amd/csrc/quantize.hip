@@ -100,7 +100,14 @@ __global__ __launch_bounds__(256) void amax_fold_kernel(float* __restrict__ part
 // ---------------------------------------------------------------------------
 // pass 2: block quantization (+ optional residual-score partials)
 // ---------------------------------------------------------------------------
-// One workgroup (256 threads) owns a tile of 128 rows x 64 columns.  Thread t
+// One workgroup (256 threads) owns a tile of 128 rows x 64 columns.  The
+// tiles (row bands outer, column tiles inner) are dealt to the 8 XCDs in
+// contiguous eighths -- hardware workgroup h runs on XCD h % 8 and takes tile
+// (h % 8) * ceil(T / 8) + h / 8 -- because neighbouring column tiles share
+// output lines (4 tiles per 128-byte line of codes, 32 per line of scales):
+// written from one XCD, a line is completed in that XCD's L2 and leaves as one
+// write; spread over XCDs, each L2 writes its pieces back separately (1.7x the
+// output bytes in HBM writes, measured).  Thread t
 // quantizes the 16-element block column t % 4 of rows t / 4 and t / 4 + 64:
 // both rows are loaded before any arithmetic, so every thread has two loads in
 // flight.  With SCORES, each thread also writes |x - DQ| of its blocks into LDS
@@ -120,13 +127,19 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
   __shared__ float absr[SCORES ? kScoreTileRows * kAbsStride : 1];
   const int tid = threadIdx.x;
   const float g = global_scale_from_amax(*amax);
-  const double six_g = 6.0 * (double)g;
-  if (g_out && blockIdx.x == 0 && blockIdx.y == 0 && tid == 0) *g_out = g;
+  const BlockScaler bsc = make_block_scaler(g);
+  if (g_out && blockIdx.x == 0 && tid == 0) *g_out = g;
 
   const int64_t nb = K / kBlock;
+  const int64_t tiles_x = (nb + kTileBlocks - 1) / kTileBlocks;
+  const int64_t ntiles = tiles_x * ((M + kScoreTileRows - 1) / kScoreTileRows);
+  const int64_t per_xcd = (ntiles + 7) / 8;
+  const int64_t tile = (int64_t)(blockIdx.x % 8) * per_xcd + blockIdx.x / 8;
+  if ((int64_t)(blockIdx.x / 8) >= per_xcd || tile >= ntiles) return;   // uniform
+  const int64_t tx = tile % tiles_x, ty = tile / tiles_x;
   const int bl = tid % kTileBlocks, rsub = tid / kTileBlocks;
-  const int64_t bc = (int64_t)blockIdx.x * kTileBlocks + bl;
-  const int64_t r0 = (int64_t)blockIdx.y * kScoreTileRows;
+  const int64_t bc = tx * kTileBlocks + bl;
+  const int64_t r0 = ty * kScoreTileRows;
   float v[kRowsPerThread][16];
   bool live[kRowsPerThread];
 #pragma unroll
@@ -142,7 +155,7 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     float res[16];
     if (live[j]) {
       uint32_t sb, w0, w1;
-      const float S = quantize_block16(v[j], g, six_g, &sb, &w0, &w1);
+      const float S = quantize_block16(v[j], bsc, &sb, &w0, &w1);
       *reinterpret_cast<u32x2*>(codes + r * (K / 2) + bc * 8) = u32x2{w0, w1};
       scales[r * nb + bc] = (uint8_t)sb;
       if constexpr (SCORES) {
@@ -164,12 +177,12 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
   }
   if constexpr (SCORES) {
     __syncthreads();
-    const int64_t c = (int64_t)blockIdx.x * kTileCols + tid;
+    const int64_t c = tx * kTileCols + tid;
     if (tid < kTileCols && c < K) {
       float sum = 0.0f;
 #pragma unroll 16
       for (int rl = 0; rl < kScoreTileRows; ++rl) sum = sum + absr[rl * kAbsStride + tid];
-      tile_partials[(int64_t)blockIdx.y * K + c] = sum;
+      tile_partials[ty * K + c] = sum;
     }
   }
 }
@@ -195,8 +208,9 @@ static hipError_t launch_quantize_t(const T* x, int64_t M, int64_t K, int64_t ld
     amax_fold_kernel<<<1, 256, 0, stream>>>(ws_partials, np);
     amax = ws_partials + np;
   }
-  dim3 grid((unsigned)((K + kTileCols - 1) / kTileCols),
-            (unsigned)((M + kScoreTileRows - 1) / kScoreTileRows));
+  const int64_t ntiles = ((K / kBlock + kTileBlocks - 1) / kTileBlocks) *
+                         ((M + kScoreTileRows - 1) / kScoreTileRows);
+  const unsigned grid = (unsigned)(ntiles > 0 ? (ntiles + 7) / 8 * 8 : 8);   // whole eighths, one per XCD
   if (tile_partials)
     quantize_tile_kernel<T, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, amax, codes, scales,
                                                             g_out, tile_partials);

@@ -540,7 +540,7 @@ __global__ __launch_bounds__(256) void resq_requant_kernel(
   }
   __syncthreads();
   const float g = sh_g;
-  const double six_g = 6.0 * (double)g;
+  const BlockScaler bsc = make_block_scaler(g);
   if (slot == slot_start[u] && threadIdx.x == 0) r_global[u] = g;
   const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
   const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
@@ -552,7 +552,7 @@ __global__ __launch_bounds__(256) void resq_requant_kernel(
     float v[16];
     load16<float>(r_s + r * k + bl * kBlock, v);
     uint32_t sb, w0, w1;
-    quantize_block16(v, g, six_g, &sb, &w0, &w1);
+    quantize_block16(v, bsc, &sb, &w0, &w1);
     *reinterpret_cast<u32x2*>(r_codes + r * (k / 2) + bl * 8) = u32x2{w0, w1};
     r_scales[r * kb + bl] = (uint8_t)sb;
   }

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256) void qdq_amax_kernel(const __bf16* __restrict_
 
 // One 16-block (elements a, c as bf16 pairs) quantized under g: writes
 // bf16(DQ) at w_qdq + base and, when asked, the codes and the block scale.
-__device__ __forceinline__ void qdq_block(const u32x4& a, const u32x4& c, float g, double six_g,
+__device__ __forceinline__ void qdq_block(const u32x4& a, const u32x4& c, const BlockScaler& bsc,
                                           int64_t base, __bf16* __restrict__ w_qdq,
                                           uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   float v[16];
@@ -68,7 +68,7 @@ __device__ __forceinline__ void qdq_block(const u32x4& a, const u32x4& c, float 
     v[8 + 2 * i + 1] = bf16_hi(c[i]);
   }
   uint32_t sb, w0, w1;
-  const float S = quantize_block16(v, g, six_g, &sb, &w0, &w1);
+  const float S = quantize_block16(v, bsc, &sb, &w0, &w1);
   // bf16(DQ) two elements at a time: the hardware FP4 convert gives the codes'
   // exact values, one fp32 multiply each rounds value * S, one packed convert
   // rounds both to bf16.
@@ -95,14 +95,14 @@ __global__ __launch_bounds__(256) void qdq_kernel(const __bf16* __restrict__ w, 
                                                   uint8_t* __restrict__ scales, float* __restrict__ g_out) {
   const int64_t mat = blockIdx.y;
   const float g = global_scale_from_amax(amax[mat]);
-  const double six_g = 6.0 * (double)g;
+  const BlockScaler bsc = make_block_scaler(g);
   if (g_out && blockIdx.x == 0 && threadIdx.x == 0) g_out[mat] = g;
   const int64_t nb = N * (K / kBlock);                  // blocks in this matrix
   for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nb;
        b += (int64_t)gridDim.x * blockDim.x) {
     const int64_t base = mat * N * K + b * kBlock;      // blocks are contiguous in row-major order
     const u32x4* src = reinterpret_cast<const u32x4*>(w + base);
-    qdq_block(src[0], src[1], g, six_g, base, w_qdq, codes, scales);
+    qdq_block(src[0], src[1], bsc, base, w_qdq, codes, scales);
   }
 }
 
@@ -186,9 +186,10 @@ __global__ __launch_bounds__(256) void guided_kernel(
     // round-to-nearest codes under S (fast path, exact fallback)
     uint32_t w0, w1;
     if (S >= 0x1p-100f) {
-      const float inv = __builtin_amdgcn_rcpf(S);
-      w0 = e2m1_pack8_fast(v, inv, S);
-      w1 = e2m1_pack8_fast(v + 8, inv, S);
+      float iu, id;
+      e2m1_brackets(S, iu, id);
+      w0 = e2m1_pack8_fast(v, iu, id, S);
+      w1 = e2m1_pack8_fast(v + 8, iu, id, S);
     } else {
       w0 = e2m1_pack8_exact(v, S);
       w1 = e2m1_pack8_exact(v + 8, S);

@@ -59,6 +59,37 @@ def test_quantize_exhaustive_bf16_many_scales(gpu_lib):
         assert np.array_equal(npu8(codes), c_ref), f"codes differ at amax={amax}"
 
 
+def _e4m3_midpoints():
+    v = F.e4m3_decode(np.arange(0x7F, dtype=np.uint8)).astype(np.float64)
+    return 0.5 * (v[:-1] + v[1:])                      # between bytes b and b + 1
+
+
+@pytest.mark.parametrize("amax", [2688.0, 2688.0 * 1.37, 2.0 ** -85, 2.0 ** -90])
+def test_quantize_scale_rounding_boundaries(gpu_lib, amax):
+    """Blocks whose amax sits on every E4M3 rounding boundary of amax_b / (6g)
+    and one fp32 ulp either side: exact ties (g = 1, so 6 m g is exact),
+    a g with a full mantissa, a tiny g, and a g below 2^-100."""
+    P = gpu_lib
+    g = OQ.global_scale(np.float32(amax))
+    targets = (6.0 * _e4m3_midpoints() * np.float64(g)).astype(np.float32)
+    block_amax = np.concatenate([targets, np.nextafter(targets, np.float32(0)),
+                                 np.nextafter(targets, np.float32(np.inf))])
+    block_amax = block_amax[block_amax <= np.float32(amax)]
+    rng = np.random.default_rng(31)
+    nblk = block_amax.size + (-(block_amax.size + 1)) % 32 + 1
+    x = np.zeros((nblk, 16), np.float32)
+    x[0, 0] = np.float32(amax)                         # fixes the global amax
+    x[1:block_amax.size + 1] = block_amax[:, None] * rng.uniform(0, 1, (block_amax.size, 16))
+    x[1:block_amax.size + 1, 0] = block_amax
+    x *= np.where(rng.uniform(size=x.shape) < 0.5, -1, 1).astype(np.float32)
+    x_np = x.reshape(-1, 32 * 16)
+    codes, scales, g_d, _ = P.nvfp4_quantize(torch.from_numpy(x_np).cuda())
+    c_ref, s_ref, g_ref = OQ.quantize(x_np)
+    assert np32(g_d)[0] == g_ref == g
+    assert np.array_equal(npu8(scales), s_ref)
+    assert np.array_equal(npu8(codes), c_ref)
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
 @pytest.mark.parametrize("m,k", [(128, 512), (300, 4096), (1, 16), (7, 48)])
 def test_quantize_random_with_tile_partials(gpu_lib, dtype, m, k):
