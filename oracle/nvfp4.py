@@ -334,3 +334,80 @@ def guided_round(x_train, roll_codes, roll_scales, roll_g):
         dist = np.abs(rtn_signed - signed_index(roll_nib[r0:r1]))
         hist += [(dist == 0).sum(), (dist == 1).sum(), (dist >= 2).sum()]
     return pack_nibbles(nib), x_fq, hist
+
+
+# ---------------------------------------------------------------------------
+# mantissa-only guidance record
+# ---------------------------------------------------------------------------
+
+def guidance_record(roll_codes):
+    """Mantissa-only guidance record of the rollout codes (TRACE summary, "Core
+    method", second innovation, and method step two).
+
+    One bit per element: the low bit of its 4-bit rollout code, which is the
+    low bit of the level's magnitude index (the E2M1 mantissa bit).
+    Neighbouring signed levels always differ in that bit, so together with
+    the candidates {q-, q+} of the training side it names the rollout level
+    whenever that level is one of them.  The rollout block scales (and g)
+    travel beside it unchanged, one byte per 16 elements, so the record costs
+    1 + 8/16 = 1.5 bits per element.
+
+    Layout (reading; the pages fix none): row-major [M, K/8] bytes; bit j of
+    byte i of a row is the bit of element 8i + j (low bit first, the order of
+    the code nibbles).
+    """
+    nib = unpack_nibbles(roll_codes).astype(np.uint32)
+    m, k = nib.shape
+    bits = (nib & 1).reshape(m, k // 8, 8)
+    weights = (1 << np.arange(8, dtype=np.uint32))[None, None, :]
+    return (bits * weights).sum(axis=2).astype(np.uint8)
+
+
+def guided_round_record(x_train, record, roll_scales, roll_g):
+    """Rollout-guided rounding from the mantissa-only record (TRACE summary,
+    method steps two and four).
+
+    S, v = x_train / S and the neighbouring levels q- <= v <= q+ (clamped to
+    +-6) are those of guided_round.  Only the low code bit b of q_roll is
+    known; q- and q+ differ in it, so the output is the candidate whose
+    magnitude index has low bit b, and q- when q- == q+.  When q_roll is q- or
+    q+ this is guided_round's choice (the pages find more than 99% of the
+    training/rollout mismatches one code apart).  A zero result takes
+    x_train's sign bit (reading, as in guided_round); S == 0 gives magnitude 0.
+
+    Returns (guided codes [M, K/2], x_fq bf16 bits [M, K] (the guided code's
+    value times S, RNE32 then bf16), moved int64[2] = numbers of elements
+    whose signed level index equals round-to-nearest's under S, and differs
+    from it).
+    """
+    x = np.asarray(x_train, dtype=np.float32)
+    m, k = x.shape
+    rec = np.asarray(record, dtype=np.uint8)
+    bits = ((rec[:, :, None] >> np.arange(8, dtype=np.uint8)[None, None, :]) & 1).reshape(m, k)
+    nib = np.empty((m, k), dtype=np.uint8)
+    x_fq = np.empty((m, k), dtype=np.uint16)
+    moved = np.zeros(2, dtype=np.int64)
+    S_all = np.repeat(effective_scales(roll_scales, roll_g), BLOCK, axis=1).astype(np.float64)
+    mag_of_pos = np.abs(np.arange(_SIGNED_LEVELS.size) - (_SIGNED_LEVELS.size // 2))
+    for r0 in range(0, m, 64):                  # row chunks bound the memory
+        r1 = min(r0 + 64, m)
+        xs = x[r0:r1]
+        xd = xs.astype(np.float64)
+        S = S_all[r0:r1]
+        t = _SIGNED_LEVELS[None, None, :] * S[..., None]          # exact
+        le = t <= xd[..., None]
+        ge = t >= xd[..., None]
+        lo = np.clip(le.sum(axis=2) - 1, 0, 14)                   # q-, clamped at -6
+        hi = np.where(ge.any(axis=2), ge.argmax(axis=2), 14)      # q+, clamped at +6
+        lo = np.minimum(lo, hi)
+        pick = np.where((mag_of_pos[hi] & 1) == bits[r0:r1], hi, lo)
+        q = np.where(S == 0, 0.0, _SIGNED_LEVELS[pick])
+        mag_idx = np.searchsorted(E2M1_LEVELS, np.abs(q))
+        neg = (q < 0) | ((q == 0) & np.signbit(xs))
+        nib[r0:r1] = (neg.astype(np.int64) << 3) | mag_idx
+        x_fq[r0:r1] = f32_to_bf16_bits((e2m1_decode(nib[r0:r1]) * S).astype(np.float32))
+        rtn_idx = e2m1_index_nearest(np.abs(xd), S)
+        rtn_signed = np.where(np.signbit(xs), -rtn_idx, rtn_idx)
+        same = signed_index(nib[r0:r1]) == rtn_signed
+        moved += [same.sum(), (~same).sum()]
+    return pack_nibbles(nib), x_fq, moved

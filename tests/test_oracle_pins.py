@@ -560,3 +560,101 @@ def test_guided_invariant_and_brute_force():
     # identical trainer input: guided == RTN == rollout codes
     gc, _, hist = Q.guided_round(xr, rc, rs, rg)
     assert np.array_equal(gc, rc) and hist[1] == 0 and hist[2] == 0
+
+
+# ---------------------------------------------------------------------------
+# mantissa-only guidance record
+# ---------------------------------------------------------------------------
+
+def test_guidance_record_layout_and_size():
+    """One bit per element (the low code bit), element 8i + j in bit j of
+    byte i; with the block scales that is the TRACE summary's 1.5 bits per
+    value: 61440 bits (7.5 KB) per token for 2048 values x 20 layers, about 6x
+    less than the full 4.5-bit codes and scales of all 40 layers (about 50 KB)."""
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 256, (5, 48), dtype=np.uint8)
+    rec = Q.guidance_record(codes)
+    nib = Q.unpack_nibbles(codes)
+    assert rec.shape == (5, 12)
+    for r in range(5):
+        for e in range(96):
+            assert (rec[r, e // 8] >> (e % 8)) & 1 == nib[r, e] & 1
+    k = 4096
+    assert (k // 8 + k // 16) * 8 / k == GOLDEN["record_arithmetic"]["bits_per_value"]
+    cmp = GOLDEN["record_compression"]
+    width = GOLDEN["record_arithmetic"]["width"]
+    rec_bytes = width * cmp["layers_kept"] * 1.5 / 8
+    full_bytes = width * cmp["layers_all"] * 4.5 / 8
+    assert rec_bytes * 8 == GOLDEN["record_arithmetic"]["bits_per_token"]
+    assert rec_bytes / 1024 == cmp["record_kb_per_token_about"]
+    assert abs(full_bytes / 1024 - cmp["full_kb_per_token_about"]) / cmp["full_kb_per_token_about"] < 0.15
+    assert round(full_bytes / rec_bytes) == cmp["compression_about"]
+
+
+def _guided_record_brute(xt, bit, S):
+    """Exact guided rounding of one element from the record bit (rationals)."""
+    levels = sorted(set([-v for v in E2M1_PAGE] + E2M1_PAGE))
+    if S == 0:
+        return (8 if np.signbit(np.float32(xt)) else 0)
+    v = Fraction(float(xt)) / Fraction(float(S))
+    lo = max([l for l in levels if l <= v], default=levels[0])
+    hi = min([l for l in levels if l >= v], default=levels[-1])
+    q = hi if E2M1_PAGE.index(abs(hi)) % 2 == bit else lo
+    neg = q < 0 or (q == 0 and np.signbit(np.float32(xt)))
+    return (8 if neg else 0) | E2M1_PAGE.index(abs(q))
+
+
+def test_guided_record_worked_example():
+    """TRACE research motivation: the rollout's 59.76 rounds to 2 (index 4,
+    low bit 0) under scale 24; the trainer's 60.24 has candidates 2 and 3,
+    and the record bit picks 2 where round-to-nearest gives 3."""
+    ex = GOLDEN["rounding_boundary_example"]
+    xr = np.zeros((1, 32), np.float32)
+    xr[0, 16] = 2688.0
+    xr[0, 0] = 144.0
+    xr[0, 1] = ex["x_rollout"]
+    xt = xr.copy()
+    xt[0, 1] = ex["x_train"]
+    rc, rs, rg = Q.quantize(xr)
+    rec = Q.guidance_record(rc)
+    assert (rec[0, 0] >> 1) & 1 == 0
+    gc, fq, moved = Q.guided_round_record(xt, rec, rs, rg)
+    assert F.e2m1_decode(Q.unpack_nibbles(gc)[0, 1]) == ex["code_rollout"]
+    assert F.bf16_bits_to_f32(fq)[0, 1] == 48.0
+    assert moved.tolist() == [31, 1]
+
+
+def test_guided_record_brute_force_and_agreement():
+    """Brute force on sampled elements; the output is always q- or q+ (one
+    code from round-to-nearest at most); wherever the rollout level is one of
+    the candidates it equals full-code guided rounding; identical inputs give
+    the rollout codes back."""
+    rng = np.random.default_rng(15)
+    xr = (rng.standard_normal((64, 64)) * 2).astype(np.float32)
+    xr[:, 9] *= 30
+    rc, rs, rg = Q.quantize(xr)
+    rec = Q.guidance_record(rc)
+    S = np.repeat(Q.effective_scales(rs, rg), 16, axis=1)
+    levels = sorted(set([-v for v in E2M1_PAGE] + E2M1_PAGE))
+    for rel in (1e-3, 8e-3, 0.1):
+        xt = (xr + rng.standard_normal(xr.shape).astype(np.float32) * rel * np.abs(xr)).astype(np.float32)
+        gc, fq, moved = Q.guided_round_record(xt, rec, rs, rg)
+        gfull, _, _ = Q.guided_round(xt, rc, rs, rg)
+        gn, fn, rn = Q.unpack_nibbles(gc), Q.unpack_nibbles(gfull), Q.unpack_nibbles(rc)
+        rtn = F.e2m1_index_nearest(np.abs(xt).astype(np.float64), S.astype(np.float64))
+        rtn_s = np.where(np.signbit(xt), -rtn, rtn)
+        assert np.all(np.abs(Q.signed_index(gn) - rtn_s) <= 1)
+        assert moved.sum() == xt.size and moved[1] == np.sum(Q.signed_index(gn) != rtn_s)
+        agree = 0
+        for (i, j) in zip(rng.integers(0, 64, 400), rng.integers(0, 64, 400)):
+            bit = (rec[i, j // 8] >> (j % 8)) & 1
+            assert gn[i, j] == _guided_record_brute(xt[i, j], bit, S[i, j])
+            v = Fraction(float(xt[i, j])) / Fraction(float(S[i, j]))
+            lo = max([l for l in levels if l <= v], default=levels[0])
+            hi = min([l for l in levels if l >= v], default=levels[-1])
+            if Fraction(float(F.e2m1_decode(rn[i, j]))) in (lo, hi):
+                assert gn[i, j] == fn[i, j]
+                agree += 1
+        assert agree > 300
+    gc, _, moved = Q.guided_round_record(xr, rec, rs, rg)
+    assert np.array_equal(gc, rc) and moved[1] == 0
