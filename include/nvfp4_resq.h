@@ -239,6 +239,43 @@ int guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t l
                  const float* roll_global, uint8_t* guided_codes, void* x_fq,
                  int64_t* dist_hist, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * guidance_record_pack -- the rollout side of the mantissa-only guidance
+ * record ([TRACE] core method, second innovation; method step two): one bit
+ * per element, the low bit of its E2M1 code (the level's mantissa bit).  With
+ * the rollout block scales, which travel beside it unchanged, the record
+ * costs 1.5 bits per element instead of 4.5.
+ *   roll_codes  [M, K/2] (rows contiguous)
+ *   record      out [M, K/8]: bit j of byte i of a row = low code bit of
+ *               element 8i + j
+ * Asynchronous on stream; writes nothing but record.
+ * Errors: EINVAL (K % 16 != 0, null or misaligned pointers).
+ * ------------------------------------------------------------------------ */
+int guidance_record_pack(const uint8_t* roll_codes, int64_t M, int64_t K, uint8_t* record,
+                         void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * guided_round_record -- rollout-guided rounding from the mantissa-only
+ * record ([TRACE] method steps two and four).  S, v = x_train / S and the
+ * neighbouring levels q- <= v <= q+ are those of guided_round; the output is
+ * the one whose magnitude index has the recorded low bit (neighbouring
+ * levels always differ in it), q- when q- == q+.  Wherever the rollout level
+ * is q- or q+ this equals guided_round.  A zero result takes x_train's sign
+ * bit; S == 0 gives magnitude 0.
+ *   x_train       bf16/fp32 [M, ldx]
+ *   record        [M, K/8] from guidance_record_pack
+ *   roll_scales   [M, K/16];  roll_global fp32 [1]
+ *   guided_codes  out [M, K/2]
+ *   x_fq          NULL or out bf16 [M, K] = bf16(RNE32(value * S))
+ *   moved         NULL or out int64 [2]: numbers of elements left at and
+ *                 moved from round-to-nearest (overwritten)
+ * Errors: EINVAL (shapes, null pointers), EUNSUPPORTED (over 2^31-1 blocks).
+ * ------------------------------------------------------------------------ */
+int guided_round_record(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                        const uint8_t* record, const uint8_t* roll_scales,
+                        const float* roll_global, uint8_t* guided_codes, void* x_fq,
+                        int64_t* moved, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -46,6 +46,8 @@ _SIGNATURES = {
     "qdq_weights_workspace_size": (_SZ, [_I64, _I64, _I64]),
     "qdq_weights": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P, _P, _SZ, _P]),
     "guided_round": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "guidance_record_pack": (_INT, [_P, _I64, _I64, _P, _P]),
+    "guided_round_record": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
 }
 
 
@@ -223,3 +225,30 @@ def guided_round(x_train, roll_codes, roll_scales, roll_global, want_fq=True, wa
                             _ptr(roll_codes), _ptr(roll_scales), _ptr(roll_global), _ptr(codes),
                             _ptr(fq), _ptr(hist), _stream()), "guided_round")
     return codes, fq, hist
+
+
+def guidance_record_pack(roll_codes):
+    """Mantissa-only guidance record of rollout codes [M, K/2]: returns [M, K/8]."""
+    lib = load()
+    _require_cuda(roll_codes)
+    m, kh = roll_codes.shape
+    record = torch.empty(m, kh // 4, dtype=torch.uint8, device=roll_codes.device)
+    _check(lib.guidance_record_pack(_ptr(roll_codes), m, kh * 2, _ptr(record), _stream()),
+           "guidance_record_pack")
+    return record
+
+
+def guided_round_record(x_train, record, roll_scales, roll_global, want_fq=True, want_moved=True):
+    """Rollout-guided rounding from the mantissa-only record.  Returns (codes
+    [M, K/2], x_fq bf16 or None, moved int64 [2] or None)."""
+    lib = load()
+    _require_cuda(x_train, record, roll_scales, roll_global)
+    m, kk = x_train.shape
+    dev = x_train.device
+    codes = torch.empty(m, kk // 2, dtype=torch.uint8, device=dev)
+    fq = torch.empty(m, kk, dtype=torch.bfloat16, device=dev) if want_fq else None
+    moved = torch.empty(2, dtype=torch.int64, device=dev) if want_moved else None
+    _check(lib.guided_round_record(_ptr(x_train), _dtype_code(x_train), m, kk, x_train.stride(0),
+                                   _ptr(record), _ptr(roll_scales), _ptr(roll_global), _ptr(codes),
+                                   _ptr(fq), _ptr(moved), _stream()), "guided_round_record")
+    return codes, fq, moved

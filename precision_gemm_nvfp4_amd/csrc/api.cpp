@@ -260,4 +260,36 @@ int guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t l
                     fn);
 }
 
+int guidance_record_pack(const uint8_t* roll_codes, int64_t M, int64_t K, uint8_t* record,
+                         void* stream) {
+  const char* fn = "guidance_record_pack";
+  if (M < 0 || K <= 0) return fail(NVFP4_EINVAL, "%s: M=%lld K=%lld", fn, (long long)M, (long long)K);
+  if (K % 16 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 16", fn, (long long)K);
+  if (M > 0 && (!roll_codes || !record)) return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if ((roll_codes && !aligned16(roll_codes)) || (record && !aligned16(record)))
+    return fail(NVFP4_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_guidance_pack(roll_codes, M, K, record,
+                                                static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int guided_round_record(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                        const uint8_t* record, const uint8_t* roll_scales, const float* roll_global,
+                        uint8_t* guided_codes, void* x_fq, int64_t* moved, void* stream) {
+  const char* fn = "guided_round_record";
+  if (int s = check_act(x_train, dtype, M, K, ldx, fn)) return s;
+  if (M * (K / 16) > 2147483647LL)
+    return fail(NVFP4_EUNSUPPORTED, "%s: more than 2^31-1 blocks", fn);
+  if (M > 0 && (!record || !roll_scales || !roll_global || !guided_codes))
+    return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if ((record && !aligned16(record)) || (guided_codes && !aligned16(guided_codes)) ||
+      (x_fq && !aligned16(x_fq)))
+    return fail(NVFP4_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_guided_record(x_train, dtype, M, K, ldx, record, roll_scales,
+                                                roll_global, guided_codes,
+                                                static_cast<__bf16*>(x_fq), moved,
+                                                static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

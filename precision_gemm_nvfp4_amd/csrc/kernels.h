@@ -78,5 +78,11 @@ hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t
                          const uint8_t* roll_codes, const uint8_t* roll_scales,
                          const float* roll_global, uint8_t* guided, __bf16* x_fq,
                          int64_t* hist, hipStream_t stream);
+hipError_t launch_guided_record(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                                const uint8_t* record, const uint8_t* roll_scales,
+                                const float* roll_global, uint8_t* guided, __bf16* x_fq,
+                                int64_t* moved, hipStream_t stream);
+hipError_t launch_guidance_pack(const uint8_t* codes, int64_t M, int64_t K, uint8_t* record,
+                                hipStream_t stream);
 
 }  // namespace nvfp4

@@ -151,9 +151,15 @@ __device__ __forceinline__ float level_of(int si) {      // value of signed inde
   return si < 0 ? -m : m;
 }
 
-template <typename T>
+// RECORD = false: roll holds the rollout codes [M, K/2], and hist counts the
+// elements whose round-to-nearest index is 0, 1 and >= 2 from the rollout's.
+// RECORD = true: roll holds the mantissa-only record [M, K/8] (the low code
+// bit of each element, element 8i + j in bit j of byte i); the output is the
+// neighbour whose magnitude index has that low bit (neighbouring levels differ
+// in it), and hist counts the elements kept at round-to-nearest and moved.
+template <typename T, bool RECORD>
 __global__ __launch_bounds__(256) void guided_kernel(
-    const T* __restrict__ x, uint32_t M, uint32_t K, int64_t ldx, const uint8_t* __restrict__ roll_codes,
+    const T* __restrict__ x, uint32_t M, uint32_t K, int64_t ldx, const uint8_t* __restrict__ roll,
     const uint8_t* __restrict__ roll_scales, const float* __restrict__ roll_global,
     uint8_t* __restrict__ guided, __bf16* __restrict__ x_fq, unsigned long long* __restrict__ hist) {
   const uint32_t nb = K / kBlock;
@@ -194,26 +200,41 @@ __global__ __launch_bounds__(256) void guided_kernel(
       w0 = e2m1_pack8_exact(v, S);
       w1 = e2m1_pack8_exact(v + 8, S);
     }
-    const u32x2 rw = *reinterpret_cast<const u32x2*>(roll_codes + (int64_t)b * 8);
+    u32x2 rw = u32x2{0u, 0u};
+    uint32_t rbits = 0;
+    if constexpr (RECORD) rbits = *reinterpret_cast<const uint16_t*>(roll + (int64_t)b * 2);
+    else rw = *reinterpret_cast<const u32x2*>(roll + (int64_t)b * 8);
     uint32_t g0 = 0, g1 = 0;
     uint32_t fq[8];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t c = ((j < 8 ? w0 : w1) >> (4 * (j & 7))) & 15u;
-      const uint32_t cr = (rw[j >> 3] >> (4 * (j & 7))) & 15u;
-      const int s_rtn = signed_index(c), s_roll = signed_index(cr);
-      const int dist = s_rtn > s_roll ? s_rtn - s_roll : s_roll - s_rtn;
-      h0 += dist == 0;
-      h1 += dist == 1;
-      h2 += dist >= 2;
+      const int s_rtn = signed_index(c);
+      int s_roll = 0;
+      if constexpr (!RECORD) {
+        s_roll = signed_index((rw[j >> 3] >> (4 * (j & 7))) & 15u);
+        const int dist = s_rtn > s_roll ? s_rtn - s_roll : s_roll - s_rtn;
+        h0 += dist == 0;
+        h1 += dist == 1;
+        h2 += dist >= 2;
+      }
       int s_pick = s_rtn;
       if (S != 0.0f) {
         const float L = level_of(s_rtn);
         const float d = __builtin_fmaf(L, S, -v[j]);    // sign of L*S - x, exact
         int s_other = d < 0.0f ? s_rtn + 1 : (d > 0.0f ? s_rtn - 1 : s_rtn);
         s_other = s_other > 7 ? 7 : (s_other < -7 ? -7 : s_other);
-        const float q_roll = level_of(s_roll);
-        if (fabsf(level_of(s_other) - q_roll) < fabsf(L - q_roll)) s_pick = s_other;
+        if constexpr (RECORD) {
+          const uint32_t bit = (rbits >> j) & 1u;
+          if ((uint32_t)(s_rtn < 0 ? -s_rtn : s_rtn) % 2u != bit) s_pick = s_other;
+        } else {
+          const float q_roll = level_of(s_roll);
+          if (fabsf(level_of(s_other) - q_roll) < fabsf(L - q_roll)) s_pick = s_other;
+        }
+      }
+      if constexpr (RECORD) {
+        h0 += s_pick == s_rtn;
+        h1 += s_pick != s_rtn;
       }
       uint32_t code = (uint32_t)(s_pick < 0 ? -s_pick : s_pick);
       if (s_pick < 0 || (s_pick == 0 && (__float_as_uint(v[j]) >> 31))) code |= 8u;
@@ -255,24 +276,73 @@ __global__ void zero_i64_kernel(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
-hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
-                         const uint8_t* roll_codes, const uint8_t* roll_scales,
-                         const float* roll_global, uint8_t* guided, __bf16* x_fq,
-                         int64_t* hist, hipStream_t stream) {
+template <bool RECORD>
+static hipError_t launch_guided_t(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                                  const uint8_t* roll, const uint8_t* roll_scales,
+                                  const float* roll_global, uint8_t* guided, __bf16* x_fq,
+                                  int64_t* hist, hipStream_t stream) {
   unsigned long long* h = reinterpret_cast<unsigned long long*>(hist);
-  if (h) zero_i64_kernel<<<1, 64, 0, stream>>>(h, 3);
+  if (h) zero_i64_kernel<<<1, 64, 0, stream>>>(h, RECORD ? 2 : 3);
   const int64_t nb = M * (K / kBlock);
   if (nb == 0) return hipGetLastError();
   int64_t grid = (nb + 255) / 256;
   if (grid > 2048) grid = 2048;
   if (dtype == 0)
-    guided_kernel<__bf16><<<(unsigned)grid, 256, 0, stream>>>(
-        static_cast<const __bf16*>(x), (uint32_t)M, (uint32_t)K, ldx, roll_codes, roll_scales,
+    guided_kernel<__bf16, RECORD><<<(unsigned)grid, 256, 0, stream>>>(
+        static_cast<const __bf16*>(x), (uint32_t)M, (uint32_t)K, ldx, roll, roll_scales,
         roll_global, guided, x_fq, h);
   else
-    guided_kernel<float><<<(unsigned)grid, 256, 0, stream>>>(
-        static_cast<const float*>(x), (uint32_t)M, (uint32_t)K, ldx, roll_codes, roll_scales,
+    guided_kernel<float, RECORD><<<(unsigned)grid, 256, 0, stream>>>(
+        static_cast<const float*>(x), (uint32_t)M, (uint32_t)K, ldx, roll, roll_scales,
         roll_global, guided, x_fq, h);
+  return hipGetLastError();
+}
+
+hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                         const uint8_t* roll_codes, const uint8_t* roll_scales,
+                         const float* roll_global, uint8_t* guided, __bf16* x_fq,
+                         int64_t* hist, hipStream_t stream) {
+  return launch_guided_t<false>(x, dtype, M, K, ldx, roll_codes, roll_scales, roll_global, guided,
+                                x_fq, hist, stream);
+}
+
+hipError_t launch_guided_record(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                                const uint8_t* record, const uint8_t* roll_scales,
+                                const float* roll_global, uint8_t* guided, __bf16* x_fq,
+                                int64_t* moved, hipStream_t stream) {
+  return launch_guided_t<true>(x, dtype, M, K, ldx, record, roll_scales, roll_global, guided,
+                               x_fq, moved, stream);
+}
+
+// ---------------------------------------------------------------------------
+// mantissa-only guidance record
+// ---------------------------------------------------------------------------
+// Thread i turns code bytes [8i, 8i + 8) (16 elements) into record bytes
+// [2i, 2i + 2): the low bit of each nibble, gathered by shift-and-mask steps
+// (nibble j's bit 4j goes to bit j).
+__device__ __forceinline__ uint32_t low_bits8(uint32_t w) {
+  uint32_t t = w & 0x11111111u;
+  t = (t | (t >> 3)) & 0x03030303u;
+  t = (t | (t >> 6)) & 0x000F000Fu;
+  return (t | (t >> 12)) & 0xFFu;
+}
+
+__global__ __launch_bounds__(256) void guidance_pack_kernel(const uint8_t* __restrict__ codes,
+                                                            int64_t n16, uint8_t* __restrict__ record) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(codes + i * 8);
+    *reinterpret_cast<uint16_t*>(record + i * 2) = (uint16_t)(low_bits8(w[0]) | (low_bits8(w[1]) << 8));
+  }
+}
+
+hipError_t launch_guidance_pack(const uint8_t* codes, int64_t M, int64_t K, uint8_t* record,
+                                hipStream_t stream) {
+  const int64_t n16 = M * (K / kBlock);
+  if (n16 == 0) return hipSuccess;
+  int64_t grid = (n16 + 255) / 256;
+  if (grid > 4096) grid = 4096;
+  guidance_pack_kernel<<<(unsigned)grid, 256, 0, stream>>>(codes, n16, record);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 11      # 5 operations, 4 workspace queries, version, last error
+    assert len(declared) == 13      # 7 operations, 4 workspace queries, version, last error
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(P.exported_symbols()) == declared
@@ -115,3 +115,16 @@ def test_qdq_and_guided_validation(lib):
                            None) == -3
     assert lib.guided_round(FAKE, 0, 4, 32, 32, None, FAKE, FAKE, FAKE, None, None, None) == -1
     assert lib.guided_round(FAKE, 0, 4, 24, 24, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
+
+
+def test_guidance_record_validation(lib):
+    assert lib.guidance_record_pack(None, 4, 32, FAKE, None) == -1
+    assert "NULL" in err(lib)
+    assert lib.guidance_record_pack(FAKE, 4, 24, FAKE, None) == -1
+    assert "multiple of 16" in err(lib)
+    assert lib.guidance_record_pack(FAKE, 4, 32, ctypes.c_void_p(0x1008), None) == -1
+    assert "aligned" in err(lib)
+    assert lib.guided_round_record(FAKE, 0, 4, 32, 32, None, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert lib.guided_round_record(FAKE, 0, 4, 24, 24, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert lib.guided_round_record(FAKE, 3, 4, 32, 32, FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
+

@@ -393,6 +393,39 @@ def test_guided_round(gpu_lib, rel):
     assert np.array_equal(hist.cpu().numpy(), hist_r)
 
 
+@pytest.mark.parametrize("rel", [1e-3, 8e-3, 0.2])
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+def test_guided_round_record(gpu_lib, rel, dtype):
+    """Mantissa-only record: the packed low code bits, then guided rounding
+    from them (codes, fake-quant values, kept/moved counts), bit-exact."""
+    P = gpu_lib
+    x_roll = synth.activations(257, 1024, seed=12, heavy_frac=0.01)
+    x_train = synth.guided_noise(x_roll, seed=12, rel=rel).to(dtype)
+    if dtype == torch.float32:
+        x_train = x_train + torch.randn(x_train.shape, generator=torch.Generator().manual_seed(2)) * 1e-4
+    rc, rs, rg, _ = P.nvfp4_quantize(x_roll.cuda())
+    rec = P.guidance_record_pack(rc)
+    rec_r = OQ.guidance_record(npu8(rc))
+    assert np.array_equal(npu8(rec), rec_r)
+    gc, fq, moved = P.guided_round_record(x_train.cuda(), rec, rs, rg)
+    gc_r, fq_r, moved_r = OQ.guided_round_record(x_train.float().numpy(), rec_r, npu8(rs),
+                                                 np32(rg)[0])
+    assert np.array_equal(npu8(gc), gc_r)
+    assert np.array_equal(fq.cpu().view(torch.int16).numpy().view(np.uint16), fq_r)
+    assert np.array_equal(moved.cpu().numpy(), moved_r)
+    if rel < 0.1:
+        assert moved_r[1] > 0
+
+
+def test_guidance_record_pack_exhaustive_bytes(gpu_lib):
+    """Every code byte value in every position of a 16-element group."""
+    P = gpu_lib
+    codes = torch.arange(256, dtype=torch.int32).repeat(8 * 16).reshape(-1, 64).to(torch.uint8)
+    codes = codes[torch.randperm(codes.shape[0], generator=torch.Generator().manual_seed(4))]
+    rec = P.guidance_record_pack(codes.cuda())
+    assert np.array_equal(npu8(rec), OQ.guidance_record(codes.numpy()))
+
+
 @pytest.mark.parametrize("tokens,n_exp,top_k,zipf", [
     (600, 2, 2, 0.0),     # 600 rows per expert: 256-row tiles, last one 88 rows
     (340, 4, 2, 0.3),     # ~170 rows per expert: one 256-row tile, waves with 2-4 live fragments
