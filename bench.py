@@ -316,6 +316,79 @@ def quant_select_bench(args, torch, P, synth, wl, dev):
         frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
 
 
+def guidance_bench(args, torch, P, synth, wl, dev):
+    """Mantissa-only guidance record (bandwidth-bound): per step, the rollout
+    side packs the low code bits of Q(X_roll) (guidance_record_pack), and the
+    trainer side rounds X_train from that record (guided_round_record, with the
+    bf16 fake-quant output).  Q(X_roll) itself belongs to the rollout forward and
+    is made once outside the timed region.  value = algorithmic GB/s."""
+    x_roll = synth.activations(wl.tokens, wl.hidden, seed=wl.seed, device=dev.type,
+                               heavy_frac=wl.heavy_frac)
+    x_train = synth.guided_noise(x_roll, seed=wl.seed, rel=wl.guided_rel)
+    rc, rs, rg, _ = P.nvfp4_quantize(x_roll)
+    torch.cuda.synchronize()
+
+    def step(tl):
+        tl.mark("start")
+        rec = P.guidance_record_pack(rc)
+        tl.mark("pack")
+        out = P.guided_round_record(x_train, rec, rs, rg, want_fq=True)
+        tl.mark("guided_record")
+        return out
+
+    for _ in range(args.warmup):
+        step(Timeline(torch))
+    torch.cuda.synchronize()
+    tls = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        tl = Timeline(torch)
+        step(tl)
+        tls.append(tl)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    n = wl.tokens * wl.hidden
+    b_pack = n * (0.5 + 0.125)                              # codes in, record out
+    b_guided = n * (2 + 0.125 + 1 / 16 + 0.5 + 2)           # x, record, scales in; codes, x_fq out
+    parts_ms = {}
+    for tl in tls:
+        for name, v in tl.durations().items():
+            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
+    parts = {nm: dict(ms=round(v, 4)) for nm, v in parts_ms.items()}
+    for nm, b in (("pack", b_pack), ("guided_record", b_guided)):
+        gbs = b / (parts_ms[nm] * 1e-3) / 1e9
+        parts[nm].update(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+    value = (b_pack + b_guided) / (ms * 1e-3) / 1e9
+    ach = b_guided / (parts_ms["guided_record"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import nvfp4 as OQ
+        rows = 256
+        xr = x_roll[:rows].float().cpu().numpy()
+        xt = x_train[:rows].float().cpu().numpy()
+        c, sc, g = OQ.quantize(xr)
+        t0 = time.time()
+        rec = OQ.guidance_record(c)
+        OQ.guided_round_record(xt, rec, sc, g)
+        dt = time.time() - t0
+        cpu = dict(value=round(rows * wl.hidden * (0.625 + 4.6875) / dt / 1e9, 4), unit="GB/s",
+                   cores=1, kind="oracle",
+                   sample=f"first {rows} of {wl.tokens} rows: record pack + guided rounding from "
+                          f"the record, {dt:.1f} s")
+    return dict(
+        metric="compensated W4A4 MoE GEMM TFLOPS (% FP4 peak); quantizer GB/s (% HBM)",
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 4),
+        config={"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden,
+                "record_bits_per_value": 1.5, "parallelism": "single GPU"},
+        algorithmic_bytes=int(b_pack + b_guided), parts=parts,
+        roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                      kernel="guided_kernel<bf16, record>"),
+        frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -335,8 +408,9 @@ def main():
     P.load()
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
-    if wl.kind == "quant_select":
-        res = quant_select_bench(args, torch, P, synth, wl, dev)
+    if wl.kind in ("quant_select", "guidance"):
+        fn = quant_select_bench if wl.kind == "quant_select" else guidance_bench
+        res = fn(args, torch, P, synth, wl, dev)
         line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
                 "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
                 "ms_per_step": res.pop("ms_per_step"), "higher_is_better": True,
@@ -345,7 +419,7 @@ def main():
         line.update(res)
         print(json.dumps(line))
         return
-    assert wl.kind == "moe", "bench.py runs MoE and quantizer workloads"
+    assert wl.kind == "moe", "bench.py runs MoE, quantizer and guidance-record workloads"
     print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
     inp, gen_s = build_inputs(torch, P, synth, wl, dev)
     print(f"[bench] inputs ready in {gen_s:.1f}s; rows={inp['rows']}; warmup {args.warmup}",

@@ -163,32 +163,46 @@ __global__ __launch_bounds__(256) void guided_kernel(
     const uint8_t* __restrict__ roll_scales, const float* __restrict__ roll_global,
     uint8_t* __restrict__ guided, __bf16* __restrict__ x_fq, unsigned long long* __restrict__ hist) {
   const uint32_t nb = K / kBlock;
-  const uint32_t total = M * nb;
+  const uint32_t total = M * nb;                  // >= 1: the launcher skips empty inputs
   const float g_roll = *roll_global;
   uint32_t h0 = 0, h1 = 0, h2 = 0;
-  for (uint32_t b = blockIdx.x * blockDim.x + threadIdx.x; b < total; b += gridDim.x * blockDim.x) {
-    const uint32_t r = b / nb, bc = b - r * nb;
+  // The inputs of a thread's next block are loaded before the current one is
+  // rounded (from a clamped index, unconditionally), so each trip of the
+  // grid-stride loop has its loads in flight during the previous trip.
+  struct In {
+    u32x4 q[sizeof(T)];                           // 16 elements
+    uint32_t sc;                                  // rollout scale byte
+    u32x2 roll;                                   // codes (8 bytes) or record bits (low 16)
+  };
+  auto fetch = [&](uint32_t bb, In& in) {
+    const uint32_t r = bb / nb, bc = bb - r * nb;
+    const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)r * ldx + bc * kBlock);
+#pragma unroll
+    for (int i = 0; i < (int)sizeof(T); ++i) in.q[i] = src[i];
+    in.sc = roll_scales[bb];
+    if constexpr (RECORD) in.roll = u32x2{*reinterpret_cast<const uint16_t*>(roll + (int64_t)bb * 2), 0u};
+    else in.roll = *reinterpret_cast<const u32x2*>(roll + (int64_t)bb * 8);
+  };
+  const uint32_t stride = gridDim.x * blockDim.x;
+  uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  In cur, nxt;
+  fetch(b < total ? b : total - 1, cur);
+  for (; b < total; b += stride) {
+    fetch(b + stride < total ? b + stride : b, nxt);
     float v[16];
-    const T* src = x + (int64_t)r * ldx + bc * kBlock;
     if constexpr (sizeof(T) == 2) {
-      const u32x4* q = reinterpret_cast<const u32x4*>(src);
-      u32x4 a = q[0], c = q[1];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_lo(a[i]);
-        v[2 * i + 1] = bf16_hi(a[i]);
-        v[8 + 2 * i] = bf16_lo(c[i]);
-        v[8 + 2 * i + 1] = bf16_hi(c[i]);
+        v[2 * i] = bf16_lo(cur.q[0][i]);
+        v[2 * i + 1] = bf16_hi(cur.q[0][i]);
+        v[8 + 2 * i] = bf16_lo(cur.q[1][i]);
+        v[8 + 2 * i + 1] = bf16_hi(cur.q[1][i]);
       }
     } else {
-      const f32x4* q = reinterpret_cast<const f32x4*>(src);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        f32x4 a = q[i];
-        v[4 * i] = a[0]; v[4 * i + 1] = a[1]; v[4 * i + 2] = a[2]; v[4 * i + 3] = a[3];
-      }
+      for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(cur.q[i >> 2][i & 3]);
     }
-    const float S = e4m3_value(roll_scales[b]) * g_roll;
+    const float S = e4m3_value(cur.sc) * g_roll;
     // round-to-nearest codes under S (fast path, exact fallback)
     uint32_t w0, w1;
     if (S >= 0x1p-100f) {
@@ -200,10 +214,8 @@ __global__ __launch_bounds__(256) void guided_kernel(
       w0 = e2m1_pack8_exact(v, S);
       w1 = e2m1_pack8_exact(v + 8, S);
     }
-    u32x2 rw = u32x2{0u, 0u};
-    uint32_t rbits = 0;
-    if constexpr (RECORD) rbits = *reinterpret_cast<const uint16_t*>(roll + (int64_t)b * 2);
-    else rw = *reinterpret_cast<const u32x2*>(roll + (int64_t)b * 8);
+    const u32x2 rw = cur.roll;
+    const uint32_t rbits = cur.roll[0];
     uint32_t g0 = 0, g1 = 0;
     uint32_t fq[8];
 #pragma unroll
@@ -252,6 +264,7 @@ __global__ __launch_bounds__(256) void guided_kernel(
       dst[0] = u32x4{fq[0], fq[1], fq[2], fq[3]};
       dst[1] = u32x4{fq[4], fq[5], fq[6], fq[7]};
     }
+    cur = nxt;
   }
   if (hist) {                                // one atomic per bin per workgroup
     __shared__ uint32_t sh[3][4];

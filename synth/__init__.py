@@ -112,7 +112,7 @@ def route(n_tokens, n_experts, seed, top_k=8, zipf_s=0.0):
 class Workload:
     """One synthetic workload: its name, sizes and generator settings."""
     name: str
-    kind: str                 # "dense", "quant_select", "moe"
+    kind: str                 # "dense", "quant_select", "moe", "guidance"
     seed: int
     tokens: int
     hidden: int
@@ -141,5 +141,7 @@ WORKLOADS = {
                  hidden=2048, experts=128, inter=768, k=64, heavy_frac=0.01, zipf_s=1.1),
         Workload("moe_T8192_H4096_E256_I1536_k64_trainer", "moe", seed=4, tokens=8192,
                  hidden=4096, experts=256, inter=1536, k=64, heavy_frac=0.01, trainer=True),
+        Workload("guidance_record_T8192_K4096", "guidance", seed=4, tokens=8192, hidden=4096,
+                 k=0, heavy_frac=0.01),
     ]
 }
