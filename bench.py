@@ -389,6 +389,88 @@ def guidance_bench(args, torch, P, synth, wl, dev):
         frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
 
 
+def kv_bench(args, torch, P, synth, wl, dev):
+    """NVFP4 KV cache with guided KV rounding (bandwidth-bound): per step, for
+    the key and the value cache [tokens, heads, head_dim] (blocks along
+    head_dim, one calibrated global scale per cache passed as amax), the
+    rollout side quantizes the cache and packs its mantissa-only record, and
+    the trainer side rounds its own cache from that record (with the bf16
+    fake-quant output).  The calibration amax is taken once outside the timed
+    region.  value = algorithmic GB/s."""
+    T, H, D = wl.tokens, wl.extra["heads"], wl.hidden
+    roll = [synth.kv_cache(T, H, D, seed=wl.seed + i, device=dev.type, heavy_frac=wl.heavy_frac)
+            for i in range(2)]
+    train = [synth.guided_noise(r, seed=wl.seed + i, rel=wl.guided_rel) for i, r in enumerate(roll)]
+    rows = [r.reshape(T * H, D) for r in roll]
+    trows = [t.reshape(T * H, D) for t in train]
+    amax = [r.abs().max().float().reshape(1) for r in rows]
+    torch.cuda.synchronize()
+
+    def step(tl):
+        tl.mark("start")
+        q = [P.nvfp4_quantize(rows[i], amax_in=amax[i]) for i in range(2)]
+        tl.mark("quantize_kv")
+        rec = [P.guidance_record_pack(q[i][0]) for i in range(2)]
+        tl.mark("record_pack")
+        out = [P.guided_round_record(trows[i], rec[i], q[i][1], q[i][2], want_fq=True)
+               for i in range(2)]
+        tl.mark("guided_kv")
+        return out
+
+    for _ in range(args.warmup):
+        step(Timeline(torch))
+    torch.cuda.synchronize()
+    tls = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        tl = Timeline(torch)
+        step(tl)
+        tls.append(tl)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    n = 2 * T * H * D                                      # key and value elements
+    b = {"quantize_kv": n * (2 + 0.5625), "record_pack": n * (0.5 + 0.125),
+         "guided_kv": n * (2 + 0.125 + 1 / 16 + 0.5 + 2)}
+    parts_ms = {}
+    for tl in tls:
+        for name, v in tl.durations().items():
+            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
+    parts = {nm: dict(ms=round(v, 4)) for nm, v in parts_ms.items()}
+    for nm, nb in b.items():
+        gbs = nb / (parts_ms[nm] * 1e-3) / 1e9
+        parts[nm].update(gbs=round(gbs, 1), frac_hbm=round(gbs / HBM_PEAK_GBS, 4))
+    total = sum(b.values())
+    value = total / (ms * 1e-3) / 1e9
+    ach = b["guided_kv"] / (parts_ms["guided_kv"] * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import nvfp4 as OQ
+        r_n = 4096
+        xr = rows[0][:r_n].float().cpu().numpy()
+        xt = trows[0][:r_n].float().cpu().numpy()
+        t0 = time.time()
+        c, sc, g = OQ.quantize(xr, g=OQ.global_scale(amax[0].cpu().numpy()[0]))
+        rec = OQ.guidance_record(c)
+        OQ.guided_round_record(xt, rec, sc, g)
+        dt = time.time() - t0
+        cpu = dict(value=round(r_n * D * (2.5625 + 0.625 + 4.6875) / dt / 1e9, 4), unit="GB/s",
+                   cores=1, kind="oracle",
+                   sample=f"first {r_n} of {T * H} key rows: quantize + record pack + guided "
+                          f"rounding from the record, {dt:.1f} s")
+    return dict(
+        metric="compensated W4A4 MoE GEMM TFLOPS (% FP4 peak); quantizer GB/s (% HBM)",
+        value=round(value, 1), unit="GB/s", ms_per_step=round(ms, 4),
+        config={"workload": wl.name, "tokens": T, "kv_heads": H, "head_dim": D,
+                "caches": "key and value", "parallelism": "single GPU"},
+        algorithmic_bytes=int(total), parts=parts,
+        roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                      kernel="guided_kernel<bf16, record>"),
+        frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -408,8 +490,9 @@ def main():
     P.load()
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
-    if wl.kind in ("quant_select", "guidance"):
-        fn = quant_select_bench if wl.kind == "quant_select" else guidance_bench
+    if wl.kind in ("quant_select", "guidance", "kv"):
+        fn = {"quant_select": quant_select_bench, "guidance": guidance_bench,
+              "kv": kv_bench}[wl.kind]
         res = fn(args, torch, P, synth, wl, dev)
         line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
                 "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -419,7 +502,7 @@ def main():
         line.update(res)
         print(json.dumps(line))
         return
-    assert wl.kind == "moe", "bench.py runs MoE, quantizer and guidance-record workloads"
+    assert wl.kind == "moe", "bench.py runs MoE, quantizer, guidance-record and KV workloads"
     print(f"[bench] workload {wl.name}: generating inputs", file=sys.stderr, flush=True)
     inp, gen_s = build_inputs(torch, P, synth, wl, dev)
     print(f"[bench] inputs ready in {gen_s:.1f}s; rows={inp['rows']}; warmup {args.warmup}",

@@ -55,6 +55,16 @@ def activations(rows, cols, seed, device="cpu", heavy_frac=0.0, heavy_scale=8.0,
     return x.to(torch.bfloat16)
 
 
+def kv_cache(tokens, heads, head_dim, seed, device="cpu", heavy_frac=0.01):
+    """bf16 [tokens, heads, head_dim] key or value cache: the activations
+    recipe over the tokens x (heads * head_dim) matrix (N(0, 1) bulk with
+    round(heavy_frac * heads * head_dim) Student-t(3) x 8 channels).  Rows of
+    the [tokens * heads, head_dim] view are the NVFP4 rows, so blocks run along
+    head_dim."""
+    return activations(tokens, heads * head_dim, seed, device=device,
+                       heavy_frac=heavy_frac).reshape(tokens, heads, head_dim)
+
+
 def weights(n_mat, rows, cols, seed, tensor_id, device="cpu", std=0.02):
     """bf16 [n_mat, rows, cols] with N(0, std^2) entries, drawn one matrix at
     a time (bounded fp32 scratch for large expert stacks)."""
@@ -112,7 +122,7 @@ def route(n_tokens, n_experts, seed, top_k=8, zipf_s=0.0):
 class Workload:
     """One synthetic workload: its name, sizes and generator settings."""
     name: str
-    kind: str                 # "dense", "quant_select", "moe", "guidance"
+    kind: str                 # "dense", "quant_select", "moe", "guidance", "kv"
     seed: int
     tokens: int
     hidden: int
@@ -143,5 +153,7 @@ WORKLOADS = {
                  hidden=4096, experts=256, inter=1536, k=64, heavy_frac=0.01, trainer=True),
         Workload("guidance_record_T8192_K4096", "guidance", seed=4, tokens=8192, hidden=4096,
                  k=0, heavy_frac=0.01),
+        Workload("kv_T65536_H4_D128", "kv", seed=5, tokens=65536, hidden=128, k=0,
+                 heavy_frac=0.01, extra={"heads": 4}),
     ]
 }

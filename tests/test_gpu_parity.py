@@ -417,6 +417,46 @@ def test_guided_round_record(gpu_lib, rel, dtype):
         assert moved_r[1] > 0
 
 
+@pytest.mark.parametrize("padded", [False, True])
+def test_kv_cache_quantize_and_guided(gpu_lib, padded):
+    """KV-cache shapes: a key cache [300 tokens, 4 heads, 128] viewed as 1200
+    rows of head_dim (blocks along head_dim), quantized under a calibrated
+    global scale (amax_in above the data's amax), then guided rounding of the
+    trainer's cache from the full codes and from the mantissa-only record; with
+    and without a padded row stride (a cache laid out [tokens, heads, 136])."""
+    P = gpu_lib
+    t, h, d = 300, 4, 128
+    k_roll = synth.kv_cache(t, h, d, seed=31)
+    k_train = synth.guided_noise(k_roll, seed=31, rel=8e-3)
+    amax = np.float32(float(k_roll.float().abs().max()) * 1.25)
+    g_ref = OQ.global_scale(amax)
+
+    def dev_rows(x):
+        if not padded:
+            return x.reshape(t * h, d).cuda()
+        buf = torch.zeros(t, h, d + 8, dtype=x.dtype)
+        buf[:, :, :d] = x
+        return buf.cuda().reshape(t * h, d + 8)[:, :d]
+
+    xr, xt = dev_rows(k_roll), dev_rows(k_train)
+    assert xr.stride(0) == (d + 8 if padded else d)
+    rc, rs, rg, _ = P.nvfp4_quantize(xr, amax_in=torch.tensor([amax], device="cuda"))
+    xr_np = k_roll.reshape(t * h, d).float().numpy()
+    xt_np = k_train.reshape(t * h, d).float().numpy()
+    c_ref, s_ref, _ = OQ.quantize(xr_np, g=g_ref)
+    assert np32(rg)[0] == g_ref
+    assert np.array_equal(npu8(rc), c_ref) and np.array_equal(npu8(rs), s_ref)
+    gc, fq, hist = P.guided_round(xt, rc, rs, rg)
+    gc_r, fq_r, hist_r = OQ.guided_round(xt_np, c_ref, s_ref, g_ref)
+    assert np.array_equal(npu8(gc), gc_r) and np.array_equal(hist.cpu().numpy(), hist_r)
+    assert np.array_equal(fq.cpu().view(torch.int16).numpy().view(np.uint16), fq_r)
+    rec = P.guidance_record_pack(rc)
+    gc2, fq2, moved = P.guided_round_record(xt, rec, rs, rg)
+    gc2_r, fq2_r, moved_r = OQ.guided_round_record(xt_np, OQ.guidance_record(c_ref), s_ref, g_ref)
+    assert np.array_equal(npu8(gc2), gc2_r) and np.array_equal(moved.cpu().numpy(), moved_r)
+    assert np.array_equal(fq2.cpu().view(torch.int16).numpy().view(np.uint16), fq2_r)
+
+
 def test_guidance_record_pack_exhaustive_bytes(gpu_lib):
     """Every code byte value in every position of a 16-element group."""
     P = gpu_lib
