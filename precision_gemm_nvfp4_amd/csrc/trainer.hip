@@ -146,10 +146,6 @@ __device__ __forceinline__ int signed_index(uint32_t c) {
   const int i = (int)(c & 7u);
   return (c & 8u) ? -i : i;
 }
-__device__ __forceinline__ float level_of(int si) {      // value of signed index
-  const float m = e2m1_mag((uint32_t)(si < 0 ? -si : si));
-  return si < 0 ? -m : m;
-}
 
 // RECORD = false: roll holds the rollout codes [M, K/2], and hist counts the
 // elements whose round-to-nearest index is 0, 1 and >= 2 from the rollout's.
@@ -216,41 +212,59 @@ __global__ __launch_bounds__(256) void guided_kernel(
     }
     const u32x2 rw = cur.roll;
     const uint32_t rbits = cur.roll[0];
+    // Candidates in magnitude space: the round-to-nearest index i and, by the
+    // exact sign of i's level * S - |x|, its neighbour on x's side (i + 1 up
+    // to 7, i - 1, or none when x sits on the level).  Both carry x's sign
+    // bit (neighbours never straddle zero with opposite signs, and a zero
+    // takes x's sign).  The full-code rule picks the candidate on the rollout
+    // level's side in signed index order, which for two adjacent levels is
+    // the one closer to it; the record rule picks the one whose index has the
+    // recorded low bit.
+    float Lm[16];
+    e2m1_unpack8(w0 & 0x77777777u, Lm);
+    e2m1_unpack8(w1 & 0x77777777u, Lm + 8);
+    const bool live = S != 0.0f;                  // S == 0: every code stays at magnitude 0
     uint32_t g0 = 0, g1 = 0;
+    uint32_t e0 = 0, e1 = 0;                      // full-code rule: index distance 0, 1 masks
     uint32_t fq[8];
 #pragma unroll
     for (int j = 0; j < 16; ++j) {
       const uint32_t c = ((j < 8 ? w0 : w1) >> (4 * (j & 7))) & 15u;
-      const int s_rtn = signed_index(c);
-      int s_roll = 0;
-      if constexpr (!RECORD) {
-        s_roll = signed_index((rw[j >> 3] >> (4 * (j & 7))) & 15u);
-        const int dist = s_rtn > s_roll ? s_rtn - s_roll : s_roll - s_rtn;
-        h0 += dist == 0;
-        h1 += dist == 1;
-        h2 += dist >= 2;
-      }
-      int s_pick = s_rtn;
-      if (S != 0.0f) {
-        const float L = level_of(s_rtn);
-        const float d = __builtin_fmaf(L, S, -v[j]);    // sign of L*S - x, exact
-        int s_other = d < 0.0f ? s_rtn + 1 : (d > 0.0f ? s_rtn - 1 : s_rtn);
-        s_other = s_other > 7 ? 7 : (s_other < -7 ? -7 : s_other);
-        if constexpr (RECORD) {
-          const uint32_t bit = (rbits >> j) & 1u;
-          if ((uint32_t)(s_rtn < 0 ? -s_rtn : s_rtn) % 2u != bit) s_pick = s_other;
-        } else {
-          const float q_roll = level_of(s_roll);
-          if (fabsf(level_of(s_other) - q_roll) < fabsf(L - q_roll)) s_pick = s_other;
-        }
-      }
+      const uint32_t i = c & 7u, sgn = c & 8u;
+      const float d = __builtin_fmaf(Lm[j], S, -fabsf(v[j]));     // exact sign
+      const uint32_t other = d < 0.0f ? (i < 7u ? i + 1u : 7u) : (d > 0.0f ? i - 1u : i);
+      uint32_t pick;
       if constexpr (RECORD) {
-        h0 += s_pick == s_rtn;
-        h1 += s_pick != s_rtn;
+        pick = (live && ((i ^ (rbits >> j)) & 1u)) ? other : i;
+      } else {
+        // In magnitude space: r = the rollout index, negated when its sign
+        // differs from x's (a rollout zero is on either side).  The candidate
+        // on the rollout level's side is the larger magnitude when r reaches
+        // it.  (Checked against the signed-index rule for every index,
+        // neighbour, sign and rollout code.)
+        const uint32_t cr = (rw[j >> 3] >> (4 * (j & 7))) & 15u;
+        const int ir = (int)(cr & 7u);
+        const bool same = (cr & 8u) == sgn || ir == 0;
+        const int r = same ? ir : -ir;
+        const int mx = (int)(other > i ? other : i), mn = (int)(other > i ? i : other);
+        pick = (live && r >= mx) ? (uint32_t)mx : (live ? (uint32_t)mn : i);
+        const int dist = same ? (ir > (int)i ? ir - (int)i : (int)i - ir) : ir + (int)i;
+        e0 |= (uint32_t)(dist == 0) << j;
+        e1 |= (uint32_t)(dist == 1) << j;
       }
-      uint32_t code = (uint32_t)(s_pick < 0 ? -s_pick : s_pick);
-      if (s_pick < 0 || (s_pick == 0 && (__float_as_uint(v[j]) >> 31))) code |= 8u;
+      const uint32_t code = sgn | pick;
       if (j < 8) g0 |= code << (4 * j); else g1 |= code << (4 * (j - 8));
+    }
+    if constexpr (RECORD) {                       // moved = nibbles that left round-to-nearest
+      auto nz = [](uint32_t x) { return (x | (x >> 1) | (x >> 2) | (x >> 3)) & 0x11111111u; };
+      const uint32_t moved = __builtin_popcount(nz(g0 ^ w0)) + __builtin_popcount(nz(g1 ^ w1));
+      h0 += 16u - moved;
+      h1 += moved;
+    } else {
+      const uint32_t n0 = __builtin_popcount(e0), n1 = __builtin_popcount(e1);
+      h0 += n0;
+      h1 += n1;
+      h2 += 16u - n0 - n1;
     }
     *reinterpret_cast<u32x2*>(guided + (int64_t)b * 8) = u32x2{g0, g1};
     if (x_fq) {
