@@ -27,9 +27,12 @@ Modules:
               scores, top-k selection, residual requantization, weight QDQ,
               rollout-guided rounding.
   gemm     -- compensated W4A4 GEMM and the MoE FFN layer stages.
+  mxfp4    -- the MXFP4 variant (32-element blocks, E8M0 power-of-two
+              scales): quantize, dequantize, residual selection and
+              requantization, compensated GEMM.
 
 Every function states which passage of the pages it follows.  Functions with
 no independent pin say "parity unpinned" (none at present).
 """
 
-from . import formats, nvfp4, gemm  # noqa: F401
+from . import formats, nvfp4, gemm, mxfp4  # noqa: F401

@@ -1,0 +1,238 @@
+"""Pins of the MXFP4 oracle against what the pages and the format fix.
+
+The TRACE summary validates rollout-guided training in MXFP4 as well as NVFP4
+(Table 4 and the results paragraph), without stating the format's rules; the
+oracle reads them as the OCP MX format (32-element blocks, E8M0 power-of-two
+scales, X = floor(log2 amax) - 2).  These tests check the oracle against a
+library decoder (torch.float8_e8m0fnu), brute force with exact rationals,
+hand-derived closed forms and the pages' worked-example quotients.
+"""
+
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+from oracle import formats as F
+from oracle import mxfp4 as MX
+from oracle import nvfp4 as Q
+
+GOLDEN = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "worked_example.json")))
+E2M1_PAGE = [Fraction(v) for v in GOLDEN["e2m1_levels"]["value"]]
+
+
+def _nearest_even(q, table):
+    return min(range(len(table)), key=lambda i: (abs(table[i] - q), i % 2))
+
+
+def brute_mx_block(xs):
+    """One 32-element block by brute force: the exponent X is the largest
+    integer with 2^(X + 2) <= amax (found by stepping), clamped to
+    [-127, 127]; codes are nearest-even E2M1 levels of |x| / 2^X, saturating."""
+    amax = max(abs(Fraction(float(v))) for v in xs)
+    if amax == 0:
+        X = -127
+    else:
+        X = 0
+        while Fraction(2) ** (X + 2) > amax:
+            X -= 1
+        while Fraction(2) ** (X + 3) <= amax:
+            X += 1
+        X = max(-127, min(127, X))
+    d = Fraction(2) ** X
+    codes = []
+    for v in xs:
+        q = abs(Fraction(float(v))) / d
+        idx = 7 if q > 6 else _nearest_even(q, E2M1_PAGE)
+        codes.append((1 if np.signbit(np.float32(v)) else 0) << 3 | idx)
+    return X + 127, codes
+
+
+def test_e8m0_decode_matches_library():
+    b = torch.arange(255, dtype=torch.uint8)
+    lib = b.view(torch.float8_e8m0fnu).double().numpy()
+    assert np.array_equal(MX.e8m0_decode(np.arange(255)), lib)
+    assert np.isnan(MX.e8m0_decode(np.array([255])))[0]
+
+
+def test_shared_exponent_closed_forms():
+    # amax -> X = floor(log2 amax) - 2, by hand
+    cases = [(6.0, 0), (4.0, 0), (7.99, 0), (8.0, 1), (3.99, -1), (0.5, -3), (1.0, -2),
+             (2.0 ** -149, -127), (0.0, -127), (1.5 * 2.0 ** 127, 125), (448.0, 6)]
+    x = np.zeros((len(cases), 32), dtype=np.float32)
+    for i, (a, _) in enumerate(cases):
+        x[i, 7] = -a if i % 2 else a
+    xe = MX.shared_exponents(x)[:, 0]
+    assert list(xe) == [c[1] for c in cases]
+
+
+def test_worked_example_quotients():
+    """The pages' scaled values 2.51 and 2.49 round to 3 and 2 (TRACE
+    summary, research motivation); in MX they are the quotients of a block
+    whose scale is 2^0 (amax in [4, 8)) or, scaled by 2^5, of one at 2^5."""
+    ex = GOLDEN["rounding_boundary_example"]
+    for shift in (0, 5, -9):
+        x = np.zeros((1, 32), dtype=np.float32)
+        x[0, 0] = np.float32(6.0 * 2.0 ** shift)
+        x[0, 1] = np.float32(ex["scaled_train"] * 2.0 ** shift)
+        x[0, 2] = np.float32(ex["scaled_rollout"] * 2.0 ** shift)
+        codes, scales = MX.quantize(x)
+        assert scales[0, 0] == 127 + shift
+        vals = F.e2m1_decode(Q.unpack_nibbles(codes)[0, :3])
+        assert list(vals) == [6.0, ex["code_train"], ex["code_rollout"]]
+
+
+def test_saturation_and_ties():
+    # one block at X = 0: 7.9 saturates to 6; ties 0.25 -> 0, 0.75 -> 1,
+    # 1.25 -> 1, 1.75 -> 2, 2.5 -> 2, 3.5 -> 4, 5 -> 4 (even index)
+    vals = [7.9, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, -0.1, -0.0, 6.5]
+    x = np.zeros((1, 32), dtype=np.float32)
+    x[0, :len(vals)] = vals
+    codes, scales = MX.quantize(x)
+    assert scales[0, 0] == 127
+    nib = Q.unpack_nibbles(codes)[0, :len(vals)]
+    assert list(nib) == [7, 0, 2, 2, 4, 4, 6, 6, 8, 8, 7]
+
+
+def test_quantize_brute_force():
+    rng = np.random.default_rng(21)
+    for trial in range(16):
+        x = (rng.standard_normal((3, 64)) * np.exp(rng.uniform(-20, 20))).astype(np.float32)
+        if trial % 4 == 0:
+            x[0, :32] = 0
+            x[1, 5] = -0.0
+        if trial % 4 == 1:                      # exact ties at the block's own scale
+            X = int(np.floor(np.log2(np.abs(x[2, :32]).max()))) - 2
+            x[2, 1:8] = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32) * np.float32(2.0 ** X)
+        codes, scales = MX.quantize(x)
+        nib = Q.unpack_nibbles(codes)
+        for r in range(3):
+            for b in range(2):
+                sb, cs = brute_mx_block(x[r, 32 * b:32 * b + 32])
+                assert scales[r, b] == sb
+                assert list(nib[r, 32 * b:32 * b + 32]) == cs
+
+
+def test_exhaustive_bf16_against_brute_force():
+    """Every finite bf16 value, in blocks whose amax fixes X = 0, 7 and -12,
+    against the brute-force nearest-even rule."""
+    bits = np.arange(65536, dtype=np.uint32)
+    v = F.bf16_bits_to_f32(bits.astype(np.uint16))
+    v = v[np.isfinite(v)]
+    levels = [float(t) for t in E2M1_PAGE]
+    for X in (0, 7, -12):
+        d = 2.0 ** X
+        mag = np.abs(v.astype(np.float64)) / d
+        keep = mag < 6.0                               # the block amax sets X
+        vv = v[keep]
+        n = (vv.size + 30) // 31 * 31
+        blocks = np.zeros((n // 31, 32), dtype=np.float32)
+        blocks[:, 0] = np.float32(6.0 * d)
+        blocks[:, 1:] = np.pad(vv, (0, n - vv.size)).reshape(-1, 31)
+        codes, scales = MX.quantize(blocks)
+        assert np.all(scales == 127 + X)
+        nib = Q.unpack_nibbles(codes)[:, 1:].reshape(-1)[:vv.size]
+        q = np.abs(vv.astype(np.float64)) / d            # exact: a power-of-two division
+        dist = np.abs(q[:, None] - np.array(levels)[None, :])
+        best = dist.min(axis=1)
+        cand = dist == best[:, None]
+        # nearest, ties to the even index
+        idx = np.where(cand.sum(1) > 1, np.argmax(cand & (np.arange(8) % 2 == 0), axis=1), np.argmin(dist, axis=1))
+        ref = idx | (np.signbit(vv).astype(np.int64) << 3)
+        assert np.array_equal(nib.astype(np.int64), ref)
+
+
+def test_residual_exact_and_bound():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((8, 128)) * 3).astype(np.float32)
+    x[:, 9] *= 40
+    codes, scales = MX.quantize(x)
+    r = MX.residual(x, codes, scales)                   # asserts exactness
+    dq = MX.dequantize(codes, scales)
+    s = np.repeat(MX.e8m0_decode(scales), 32, axis=1)
+    # |R| <= half the local level spacing, i.e. <= 1 * 2^X (spacing 2 between 4 and 6),
+    # plus saturation of (6, 8) * 2^X: at most 2 * 2^X
+    assert np.all(np.abs(r.astype(np.float64)) <= 2.0 * s)
+    nib = Q.unpack_nibbles(codes)
+    z = (nib & 7) == 0
+    assert np.array_equal(r[z], x[z])
+    assert np.array_equal(dq[z], np.zeros(z.sum(), np.float32))
+
+
+def test_resq_brute_force_small():
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((7, 96)).astype(np.float32)
+    x[:, [3, 40, 77]] *= 12
+    codes, scales = MX.quantize(x)
+    offs = [0, 3, 3, 7]
+    row_index = np.array([6, 0, 2, 1, 5, 4, 3])
+    sel, rc, rs = MX.resq_select_and_requant(x, codes, scales, offs, 32, row_index=row_index)
+    # brute force: residual from brute-force quantization, scores in fp64
+    # (units of <= 128 rows: the fp32 sequential sum ranks identically here)
+    nib_b = np.zeros((7, 96), np.int64)
+    xe_b = np.zeros((7, 3), np.int64)
+    for r in range(7):
+        for b in range(3):
+            sb, cs = brute_mx_block(x[r, 32 * b:32 * b + 32])
+            nib_b[r, 32 * b:32 * b + 32] = cs
+            xe_b[r, b] = sb - 127
+    dq = F.e2m1_decode(nib_b) * np.repeat(np.ldexp(1.0, xe_b), 32, axis=1)
+    R = x.astype(np.float64) - dq
+    assert np.array_equal(sel[1], np.arange(32))            # the empty unit
+    for u, (a, b) in enumerate([(0, 3), (3, 7)]):
+        uu = 0 if u == 0 else 2
+        rows = row_index[a:b]
+        score = np.abs(R[rows]).sum(axis=0)
+        order = sorted(range(96), key=lambda c: (-score[c], c))
+        assert list(sel[uu]) == sorted(order[:32])
+        rq_c, rq_s = MX.quantize(R[rows][:, sel[uu]].astype(np.float32))
+        assert np.array_equal(rc[a:b], rq_c) and np.array_equal(rs[a:b], rq_s)
+
+
+def _exact(codes, scales):
+    nib = Q.unpack_nibbles(codes)
+    return [[Fraction(float(F.e2m1_decode(nib[i, j]))) * Fraction(2) ** (int(scales[i, j // 32]) - 127)
+             for j in range(nib.shape[1])] for i in range(nib.shape[0])]
+
+
+def test_gemm_brute_force_tiny():
+    rng = np.random.default_rng(9)
+    x = rng.standard_normal((2, 64)).astype(np.float32)
+    w = (rng.standard_normal((3, 64)) * 0.02).astype(np.float32)
+    xc, xs = MX.quantize(x)
+    wc, ws = MX.quantize(w)
+    sel, rc, rs = MX.resq_select_and_requant(x, xc, xs, [0, 2], 32)
+    y = MX.gemm_comp(xc, xs, wc, ws, sel[0], rc, rs)
+    A, W, R = _exact(xc, xs), _exact(wc, ws), _exact(rc, rs)
+    for i in range(2):
+        for n in range(3):
+            ref = sum(A[i][j] * W[n][j] for j in range(64))
+            ref += sum(R[i][j] * W[n][int(sel[0][j])] for j in range(32))
+            assert abs(float(ref) - y[i, n]) <= 1e-12 * max(1.0, abs(float(ref)))
+    assert not np.array_equal(MX.gemm_comp(xc, xs, wc, ws), y)
+
+
+def test_compensation_linearity_identity():
+    """Adding the correction to the output equals adding the scattered
+    Q(R_S) to the quantized activation (the weight side is the stored
+    MXFP4 weight at the selected channels)."""
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((16, 128)).astype(np.float32)
+    x[:, [1, 50]] *= 20
+    w = (rng.standard_normal((24, 128)) * 0.02).astype(np.float32)
+    xc, xs = MX.quantize(x)
+    wc, ws = MX.quantize(w)
+    sel, rc, rs = MX.resq_select_and_requant(x, xc, xs, [0, 16], 64)
+    y = MX.gemm_comp(xc, xs, wc, ws, sel[0], rc, rs)
+    a = MX.dequantize(xc, xs).astype(np.float64)
+    a[:, sel[0]] += MX.dequantize(rc, rs)
+    y2 = a @ MX.dequantize(wc, ws).astype(np.float64).T
+    assert np.allclose(y, y2, rtol=1e-12, atol=1e-12)
+    # with every channel selected the compensated product is closer to the exact one
+    sel_all, rca, rsa = MX.resq_select_and_requant(x, xc, xs, [0, 16], 128)
+    exact = x.astype(np.float64) @ MX.dequantize(wc, ws).astype(np.float64).T
+    e0 = np.abs(MX.gemm_comp(xc, xs, wc, ws) - exact).max()
+    e1 = np.abs(MX.gemm_comp(xc, xs, wc, ws, sel_all[0], rca, rsa) - exact).max()
+    assert e1 < e0
