@@ -276,6 +276,83 @@ int guided_round_record(const void* x_train, int dtype, int64_t M, int64_t K, in
                         const float* roll_global, uint8_t* guided_codes, void* x_fq,
                         int64_t* moved, void* stream);
 
+/* ======================================================================== *
+ * MXFP4 variant.  [TRACE] validates its method in MXFP4 rollouts as well as
+ * NVFP4 (results paragraph and Table 4, MXFP4 W4A8 and W4A4) without stating
+ * the format; it is read as the OCP MX format:
+ *   - block: 32 consecutive elements of a row share one E8M0 scale byte
+ *     b = X + 127, value 2^X; X = floor(log2 amax_b) - 2 clamped to
+ *     [-127, 127], -127 for an all-zero block; no global scale;
+ *   - element: E2M1 index nearest to |x| / 2^X (ties to the even index,
+ *     above 6 gives 6), sign bit of x; DQ = value * 2^X (exact in fp32).
+ *   Storage: codes [rows, K/2] as for NVFP4; scales [rows, K/32] bytes,
+ *   row-major.  4.25 bit per element.
+ * ======================================================================== */
+
+/* ------------------------------------------------------------------------ *
+ * mxfp4_quantize -- online MXFP4 quantization of an activation tensor
+ * ([QUADS] sec. 2.1: activations are quantized online every forward).
+ *   x              bf16 or fp32 [M, ldx]
+ *   codes          out [M, K/2];  scales out [M, K/32]
+ *   tile_partials  NULL or out fp32 [ceil(M/128), K]: per 128-row tile, the
+ *                  fp32 sum of |x - DQ| of each channel in increasing row
+ *                  order (the residual channel scores, [QUADS] sec. 2.2B)
+ * Errors: EINVAL for null required pointers, K % 32 != 0, ldx < K, M < 0.
+ * Needs no workspace.  M == 0 writes nothing.
+ * ------------------------------------------------------------------------ */
+int mxfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                   uint8_t* scales, float* tile_partials, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * mxfp4_resq_select_and_requant -- residual activation compensation in MXFP4
+ * ([QUADS] sec. 2.2B): as resq_select_and_requant (units, row_index, the
+ * channel scores of |x - DQ| in the fixed 128-row tile order, top-k with
+ * ties to the lower channel, sel_idx ascending), with x's codes and scales
+ * in MXFP4 and the compact residual R_S quantized to MXFP4 with 32-blocks
+ * along the compact axis.  No global scales.
+ *   k              multiple of 32 in [32, K]
+ *   sel_idx        out int32 [U, k];  r_codes out [rows_total, k/2];
+ *   r_scales       out [rows_total, k/32]
+ * Errors: as resq_select_and_requant; K % 32 != 0 or k % 32 != 0 give EINVAL.
+ * ------------------------------------------------------------------------ */
+size_t mxfp4_resq_select_and_requant_workspace_size(int64_t K, int64_t rows_total, int64_t U,
+                                                    int32_t k);
+int mxfp4_resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+                                  const int32_t* row_index, const uint8_t* codes,
+                                  const uint8_t* scales, const int64_t* unit_offsets, int64_t U,
+                                  int64_t rows_total, int32_t k, const float* tile_partials,
+                                  int32_t* sel_idx, uint8_t* r_codes, uint8_t* r_scales, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * moe_mxfp4_grouped_gemm -- the routed grouped expert GEMM over MXFP4
+ * activations and weights with the residual compensation term ([QUADS]
+ * sec. 1: native W4A4 GEMM on the rollout; sec. 2.2B: the second FP4
+ * quantization of the selected channels added back into the result):
+ *   Y[r, n] = sum_k A[r, k] W_e[n, k] + sum_j R_S[r, j] W_e[n, sel_e[j]]
+ * with every operand element its MXFP4 value (no global scales).  Arguments
+ * as moe_w4a4_grouped_gemm without a_global, w_global and r_global:
+ *   a_scales       [a_rows, K/32];  w_scales [E, N, K/32]; both 4-byte aligned
+ *   r_scales       [rows_total, kc/32];  kc multiple of 32 in [32, min(K, 128)]
+ *   K              multiple of 128
+ * The compensation's weight side is computed on the matrix cores in FP8 E4M3
+ * against the largest block scale of each weight row: exact when a row's block
+ * scales span at most 8 binades, else the smaller elements of W at the selected
+ * channels are rounded to E4M3.
+ * Errors: EINVAL (shapes, pointers, alignment, epilogue arguments, kc),
+ *         EWORKSPACE (scatter epilogue).
+ * ------------------------------------------------------------------------ */
+size_t moe_mxfp4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K,
+                                             int epilogue, int64_t out_rows);
+int moe_mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                           const int32_t* a_row_index, int64_t a_rows,
+                           const int64_t* group_offsets, int32_t E, int64_t rows_total, int64_t K,
+                           const uint8_t* w_codes, const uint8_t* w_scales, int64_t N,
+                           const int32_t* sel_idx, const uint8_t* r_codes, const uint8_t* r_scales,
+                           int32_t kc, int epilogue, const float* row_weight,
+                           const int32_t* scatter_index, int64_t out_rows, void* out, int64_t ldo,
+                           float* out_amax, void* ws, size_t ws_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

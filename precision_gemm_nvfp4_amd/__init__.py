@@ -48,6 +48,14 @@ _SIGNATURES = {
     "guided_round": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
     "guidance_record_pack": (_INT, [_P, _I64, _I64, _P, _P]),
     "guided_round_record": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _P]),
+    "mxfp4_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "mxfp4_resq_select_and_requant_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
+    "mxfp4_resq_select_and_requant": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _I64,
+                                             _I64, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_mxfp4_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _INT, _I64]),
+    "moe_mxfp4_grouped_gemm": (_INT, [_P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _I64,
+                                      _P, _P, _P, _I32, _INT, _P, _P, _I64, _P, _I64, _P, _P,
+                                      _SZ, _P]),
 }
 
 
@@ -252,3 +260,83 @@ def guided_round_record(x_train, record, roll_scales, roll_global, want_fq=True,
                                    _ptr(record), _ptr(roll_scales), _ptr(roll_global), _ptr(codes),
                                    _ptr(fq), _ptr(moved), _stream()), "guided_round_record")
     return codes, fq, moved
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 variant
+# ---------------------------------------------------------------------------
+def mxfp4_quantize(x, tile_partials=False):
+    """MXFP4 quantization of x [M, K] (bf16/fp32, GPU).
+
+    Returns (codes uint8 [M, K/2], scales uint8 [M, K/32] (E8M0),
+    tile_partials fp32 [ceil(M/128), K] or None)."""
+    lib = load()
+    _require_cuda(x)
+    m, k = x.shape
+    dev = x.device
+    codes = torch.empty(m, k // 2, dtype=torch.uint8, device=dev)
+    scales = torch.empty(m, k // 32, dtype=torch.uint8, device=dev)
+    tp = torch.empty((m + 127) // 128, k, dtype=torch.float32, device=dev) if tile_partials else None
+    _check(lib.mxfp4_quantize(_ptr(x), _dtype_code(x), m, k, x.stride(0), _ptr(codes),
+                              _ptr(scales), _ptr(tp), _stream()), "mxfp4_quantize")
+    return codes, scales, tp
+
+
+def mxfp4_resq_select_and_requant(x, codes, scales, k, unit_offsets=None, rows_total=None,
+                                  row_index=None, tile_partials=None):
+    """MXFP4 residual selection and requantization (see resq_select_and_requant).
+    Returns (sel_idx int32 [U, k], r_codes [rows, k/2], r_scales [rows, k/32])."""
+    lib = load()
+    _require_cuda(x, codes, scales, unit_offsets, row_index, tile_partials)
+    x_rows, kk = x.shape
+    dev = x.device
+    if tile_partials is not None:
+        n_units = (x_rows + 127) // 128
+        rows_total = x_rows
+    else:
+        n_units = unit_offsets.numel() - 1
+        if rows_total is None:
+            raise ValueError("rows_total (host int) is required with unit_offsets")
+    sel = torch.empty(n_units, k, dtype=torch.int32, device=dev)
+    rc = torch.empty(rows_total, k // 2, dtype=torch.uint8, device=dev)
+    rs = torch.empty(rows_total, k // 32, dtype=torch.uint8, device=dev)
+    ws = _workspace(lib.mxfp4_resq_select_and_requant_workspace_size(kk, rows_total, n_units, k), dev)
+    _check(lib.mxfp4_resq_select_and_requant(
+        _ptr(x), _dtype_code(x), x_rows, kk, x.stride(0), _ptr(row_index), _ptr(codes),
+        _ptr(scales), _ptr(unit_offsets), n_units, rows_total, k, _ptr(tile_partials),
+        _ptr(sel), _ptr(rc), _ptr(rs), _ptr(ws), ws.numel(), _stream()),
+        "mxfp4_resq_select_and_requant")
+    return sel, rc, rs
+
+
+def moe_mxfp4_grouped_gemm(a_codes, a_scales, group_offsets, rows_total, w_codes, w_scales,
+                           epilogue=EPI_F32, a_row_index=None, sel_idx=None, r_codes=None,
+                           r_scales=None, row_weight=None, scatter_index=None, out=None,
+                           out_rows=None, out_amax=None):
+    """Grouped MXFP4 W4A4 GEMM with the fused compensation term (outputs as
+    moe_w4a4_grouped_gemm)."""
+    lib = load()
+    _require_cuda(a_codes, a_scales, group_offsets, w_codes, w_scales, a_row_index, sel_idx,
+                  r_codes, r_scales, row_weight, scatter_index, out, out_amax)
+    n_exp, n, k_half = w_codes.shape
+    kk = k_half * 2
+    dev = w_codes.device
+    if out is None:
+        if epilogue == EPI_F32:
+            out = torch.empty(rows_total, n, dtype=torch.float32, device=dev)
+        elif epilogue == EPI_SWIGLU_BF16:
+            out = torch.empty(rows_total, n // 2, dtype=torch.bfloat16, device=dev)
+        else:
+            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor")
+    if out_rows is None:
+        out_rows = out.shape[0]
+    kc = 0 if sel_idx is None else sel_idx.shape[1]
+    ws = _workspace(lib.moe_mxfp4_grouped_gemm_workspace_size(n_exp, rows_total, n, kk, epilogue,
+                                                              out_rows), dev)
+    a_rows = a_codes.shape[0] if a_codes is not None else 0
+    _check(lib.moe_mxfp4_grouped_gemm(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_row_index), a_rows, _ptr(group_offsets), n_exp,
+        rows_total, kk, _ptr(w_codes), _ptr(w_scales), n, _ptr(sel_idx), _ptr(r_codes),
+        _ptr(r_scales), kc, epilogue, _ptr(row_weight), _ptr(scatter_index), out_rows, _ptr(out),
+        out.stride(0), _ptr(out_amax), _ptr(ws), ws.numel(), _stream()), "moe_mxfp4_grouped_gemm")
+    return out

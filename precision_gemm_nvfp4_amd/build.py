@@ -22,7 +22,7 @@ LIB = os.path.join(HERE, "libnvfp4_resq.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
-SOURCES = ["quantize.hip", "resq.hip", "gemm.hip", "combine.hip", "trainer.hip", "api.cpp"]
+SOURCES = ["quantize.hip", "resq.hip", "gemm.hip", "mxfp4.hip", "combine.hip", "trainer.hip", "api.cpp"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",

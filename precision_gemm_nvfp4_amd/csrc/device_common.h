@@ -260,6 +260,45 @@ __device__ __forceinline__ void e2m1_unpack8(uint32_t w, float* f) {
 // Dequantized value of 4-bit code c under S: RNE32(value * S).
 __device__ __forceinline__ float dq(uint32_t c, float S) { return e2m1_value(c) * S; }
 
+// ---------------------------------------------------------------------------
+// MXFP4 (32-element blocks, E8M0 power-of-two scales)
+// ---------------------------------------------------------------------------
+// Shared scale 2^X of a block with largest magnitude amax: X = floor(log2
+// amax) - 2 (2 is the exponent of the largest E2M1 level), clamped to
+// [-127, 127], and -127 for amax == 0.  With E the fp32 exponent field of
+// amax, floor(log2 amax) = E - 127 for normal amax; a subnormal or zero amax
+// (E == 0) lies below 2^-126 and clamps to -127 as well, as does E == 1.
+// The stored byte is X + 127 = max(E - 2, 0); finite fp32 inputs give at most
+// 252 (X = 125).
+constexpr int kMxBlock = 32;
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  const int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return (uint32_t)(E > 2 ? E - 2 : 0);
+}
+// 2^X of a scale byte b = X + 127 (b <= 254): a normal fp32 for b >= 1,
+// 2^-127 (an fp32 subnormal) for b == 0.
+__device__ __forceinline__ float e8m0_value(uint32_t b) {
+  return b ? __uint_as_float(b << 23) : __uint_as_float(0x00400000u);
+}
+// 2^-X, always a normal fp32 (X in [-127, 125]).
+__device__ __forceinline__ float e8m0_inverse(uint32_t b) {
+  return __uint_as_float((254u - b) << 23);
+}
+
+// MXFP4 codes of 32 elements sharing scale byte b, packed 8 to a word.
+// |x| * 2^-X is exact (a power-of-two multiply; results small enough to
+// underflow lie far below the first rounding midpoint), so the E2M1 rounding
+// of the NVFP4 fast path applies with brackets 2^-X (1 +- 2^-20): the
+// hardware convert of both brackets agrees except where an exact midpoint
+// lies between them, and there the sign of fma(m, 2^X, -|x|) -- exact, also
+// when 2^X is subnormal -- decides, a tie going to the even index.
+__device__ __forceinline__ void mx_pack32(const float* v, uint32_t b, uint32_t* w) {
+  const float inv = e8m0_inverse(b), S = e8m0_value(b);
+  const float iu = inv * (1.0f + 0x1p-20f), id = inv * (1.0f - 0x1p-20f);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) w[q] = e2m1_pack8_fast(v + 8 * q, iu, id, S);
+}
+
 // Workgroup barrier for LDS hand-offs only: waits for this wave's LDS
 // operations, then meets the other waves.  Unlike __syncthreads() it does not
 // wait for outstanding global loads, so loads issued ahead for later K-steps

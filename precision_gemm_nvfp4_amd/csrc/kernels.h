@@ -29,7 +29,7 @@ hipError_t launch_resq(const void* x, int dtype, int64_t x_rows, int64_t K, int6
                        const float* g, const int64_t* unit_offsets, int64_t U, int64_t rows_total,
                        int32_t k, const float* tile_partials, int32_t* sel_idx, uint8_t* r_codes,
                        uint8_t* r_scales, float* r_global, const ResqWorkspace& ws,
-                       hipStream_t stream);
+                       hipStream_t stream, bool mx = false);
 
 // gemm.hip
 struct GemmArgs {
@@ -60,9 +60,17 @@ struct GemmArgs {
   float* out_amax;
   float* y_rows;         // scatter epilogue: row_weight * Y rows [rows_total, N] (workspace)
   int block_m;           // rows per tile: 256, 128, 64, 32, or 0 to pick from the average group size
+  int rw_lds_offset;     // set by the launcher: LDS byte offset of the scatter epilogue's row weights
 };
 int grouped_gemm_block_m(int64_t rows_total, int32_t E);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+
+// mxfp4.hip
+hipError_t launch_mx_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                              uint8_t* codes, uint8_t* scales, float* tile_partials,
+                              hipStream_t stream);
+size_t mx_gemm_max_lds(int64_t K);
+hipError_t launch_mx_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 
 // combine.hip
 size_t combine_workspace_bytes(int64_t rows, int64_t N, int64_t out_rows);

@@ -161,7 +161,9 @@ constexpr int kScoreCols = 64;
 constexpr int kScoreBlocks = kScoreCols / kBlock;
 constexpr int kAbsStride = kScoreCols + 4;
 
-template <typename T>
+// MX: the operand is MXFP4 (E8M0 scale per 32-block, no global scale; gp
+// unused), else NVFP4 (E4M3 per 16-block times *gp).
+template <typename T, bool MX>
 __global__ __launch_bounds__(256) void resq_scores_kernel(
     const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
     const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
@@ -178,7 +180,8 @@ __global__ __launch_bounds__(256) void resq_scores_kernel(
   int64_t b, e;
   units.range(u, b, e);
   const int64_t r0 = b + (slot - tile_start[u]) * kScoreTileRows;
-  const float g = *gp;
+  const float g = MX ? 1.0f : *gp;
+  const int64_t nsb = MX ? K / kMxBlock : nb;           // scale bytes per row
   float v[2][16];
   u32x2 w[2];
   uint32_t sb[2];
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(256) void resq_scores_kernel(
     if (live[j]) {
       load16<T>(x + xr * ldx + bc * kBlock, v[j]);
       w[j] = *reinterpret_cast<const u32x2*>(codes + xr * (K / 2) + bc * 8);
-      sb[j] = scales[xr * nb + bc];
+      sb[j] = scales[xr * nsb + (MX ? bc >> 1 : bc)];
     }
   }
 #pragma unroll
@@ -201,7 +204,7 @@ __global__ __launch_bounds__(256) void resq_scores_kernel(
 #pragma unroll
     for (int i = 0; i < 16; ++i) res[i] = 0.0f;
     if (live[j]) {
-      const float S = e4m3_value(sb[j]) * g;
+      const float S = MX ? e8m0_value(sb[j]) : e4m3_value(sb[j]) * g;
       float f[16];
       e2m1_unpack8(w[j][0], f);
       e2m1_unpack8(w[j][1], f + 8);
@@ -313,7 +316,7 @@ __global__ __launch_bounds__(256) void resq_select_reg_kernel(
   int32_t* out = sel_idx + u * k;
   if (e == b) {                               // empty unit: channels 0..k-1, g_R = 1
     for (int j = tid; j < k; j += blockDim.x) out[j] = j;
-    if (tid == 0) r_global[u] = 1.0f;
+    if (tid == 0 && r_global) r_global[u] = 1.0f;   // NULL for MXFP4 (no global scale)
     return;
   }
   const int64_t t0 = tile_start[u], t1 = tile_start[u + 1];
@@ -410,7 +413,7 @@ __global__ __launch_bounds__(256) void resq_select_kernel(
   int32_t* out = sel_idx + u * k;
   if (e == b) {                               // empty unit: channels 0..k-1, g_R = 1
     for (int j = tid; j < k; j += blockDim.x) out[j] = j;
-    if (tid == 0) r_global[u] = 1.0f;
+    if (tid == 0 && r_global) r_global[u] = 1.0f;   // NULL for MXFP4 (no global scale)
     return;
   }
   const int chunk = (int)((K + blockDim.x - 1) / blockDim.x);
@@ -468,7 +471,7 @@ __global__ __launch_bounds__(256) void resq_select_kernel(
 // ---------------------------------------------------------------------------
 // gather R_S and per-slot max |R_S|
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool MX>
 __global__ __launch_bounds__(256) void resq_gather_kernel(
     const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
     const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
@@ -489,8 +492,8 @@ __global__ __launch_bounds__(256) void resq_gather_kernel(
     sel[j] = c < 0 ? 0 : (c >= K ? (int32_t)(K - 1) : c);
   }
   __syncthreads();
-  const float g = *gp;
-  const int64_t nb = K / kBlock;
+  const float g = MX ? 1.0f : *gp;
+  const int64_t nb = K / (MX ? kMxBlock : kBlock);
   float m = 0.0f;
   const int64_t n = (r1 - r0) * k;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
@@ -502,7 +505,8 @@ __global__ __launch_bounds__(256) void resq_gather_kernel(
       const int64_t c = sel[j];
       const float xv = load1<T>(x + xr * ldx + c);
       const uint32_t code = (codes[xr * (K / 2) + (c >> 1)] >> (4 * (c & 1))) & 15u;
-      const float S = e4m3_value(scales[xr * nb + (c >> 4)]) * g;
+      const float S = MX ? e8m0_value(scales[xr * nb + (c >> 5)])
+                         : e4m3_value(scales[xr * nb + (c >> 4)]) * g;
       res = xv - dq(code, S);
     }
     r_s[r * k + j] = res;
@@ -558,10 +562,41 @@ __global__ __launch_bounds__(256) void resq_requant_kernel(
   }
 }
 
+// MXFP4 of R_S: 32-blocks along the compact axis, each with its own E8M0
+// scale; no global scale.
+__global__ __launch_bounds__(256) void resq_requant_mx_kernel(
+    const float* __restrict__ r_s, Units units, const int32_t* __restrict__ slot_start, int32_t k,
+    uint8_t* __restrict__ r_codes, uint8_t* __restrict__ r_scales) {
+  const int64_t slot = blockIdx.x;
+  const int64_t u = unit_of_slot(slot_start, units.U, slot);
+  if (u < 0) return;
+  int64_t b, e;
+  units.range(u, b, e);
+  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
+  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
+  const int kb = k / kMxBlock;
+  const int64_t n = (r1 - r0) * kb;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t r = r0 + i / kb;
+    const int bl = (int)(i % kb);
+    float v[32];
+    load16<float>(r_s + r * k + bl * kMxBlock, v);
+    load16<float>(r_s + r * k + bl * kMxBlock + 16, v + 16);
+    float amax = 0.0f;
+#pragma unroll
+    for (int q = 0; q < 32; ++q) amax = fmaxf(amax, fabsf(v[q]));
+    const uint32_t sb = mx_scale_byte(amax);
+    uint32_t w[4];
+    mx_pack32(v, sb, w);
+    *reinterpret_cast<u32x4*>(r_codes + r * (k / 2) + bl * 16) = u32x4{w[0], w[1], w[2], w[3]};
+    r_scales[r * kb + bl] = (uint8_t)sb;
+  }
+}
+
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, bool MX>
 static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t ldx,
                                 const int32_t* row_index, const uint8_t* codes,
                                 const uint8_t* scales, const float* g,
@@ -576,7 +611,7 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
   const float* partials = tile_partials;
   if (!tile_partials) {
     dim3 grid((unsigned)((K + kScoreCols - 1) / kScoreCols), (unsigned)slots);
-    resq_scores_kernel<T><<<grid, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
+    resq_scores_kernel<T, MX><<<grid, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
                                                     units, ws.tile_start, ws.partials);
     partials = ws.partials;
   }
@@ -603,12 +638,16 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
                                                               sel_idx, r_global);
   }
   if (gslots > 0) {
-    resq_gather_kernel<T><<<(unsigned)gslots, 256, (size_t)k * 4, stream>>>(
+    resq_gather_kernel<T, MX><<<(unsigned)gslots, 256, (size_t)k * 4, stream>>>(
         x, x_rows, K, ldx, row_index, codes, scales, g, units, ws.slot_start, sel_idx, k, ws.r_s,
         ws.amax_part);
-    resq_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start,
-                                                              ws.amax_part, k, r_codes, r_scales,
-                                                              r_global);
+    if constexpr (MX)
+      resq_requant_mx_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start, k,
+                                                                   r_codes, r_scales);
+    else
+      resq_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start,
+                                                                ws.amax_part, k, r_codes, r_scales,
+                                                                r_global);
   }
   return hipGetLastError();
 }
@@ -618,14 +657,14 @@ hipError_t launch_resq(const void* x, int dtype, int64_t x_rows, int64_t K, int6
                        const float* g, const int64_t* unit_offsets, int64_t U, int64_t rows_total,
                        int32_t k, const float* tile_partials, int32_t* sel_idx, uint8_t* r_codes,
                        uint8_t* r_scales, float* r_global, const ResqWorkspace& ws,
-                       hipStream_t stream) {
-  if (dtype == 0)
-    return launch_resq_t(static_cast<const __bf16*>(x), x_rows, K, ldx, row_index, codes, scales, g,
-                         unit_offsets, U, rows_total, k, tile_partials, sel_idx, r_codes, r_scales,
-                         r_global, ws, stream);
-  return launch_resq_t(static_cast<const float*>(x), x_rows, K, ldx, row_index, codes, scales, g,
-                       unit_offsets, U, rows_total, k, tile_partials, sel_idx, r_codes, r_scales,
-                       r_global, ws, stream);
+                       hipStream_t stream, bool mx) {
+#define RESQ_ARGS x_rows, K, ldx, row_index, codes, scales, g, unit_offsets, U, rows_total, k, \
+                  tile_partials, sel_idx, r_codes, r_scales, r_global, ws, stream
+  const __bf16* xb = static_cast<const __bf16*>(x);
+  const float* xf = static_cast<const float*>(x);
+  if (mx) return dtype == 0 ? launch_resq_t<__bf16, true>(xb, RESQ_ARGS) : launch_resq_t<float, true>(xf, RESQ_ARGS);
+  return dtype == 0 ? launch_resq_t<__bf16, false>(xb, RESQ_ARGS) : launch_resq_t<float, false>(xf, RESQ_ARGS);
+#undef RESQ_ARGS
 }
 
 }  // namespace nvfp4

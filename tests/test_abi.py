@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 13      # 7 operations, 4 workspace queries, version, last error
+    assert len(declared) == 18      # 10 operations, 6 workspace queries, version, last error
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(P.exported_symbols()) == declared
@@ -128,3 +128,28 @@ def test_guidance_record_validation(lib):
     assert lib.guided_round_record(FAKE, 0, 4, 24, 24, FAKE, FAKE, FAKE, FAKE, None, None, None) == -1
     assert lib.guided_round_record(FAKE, 3, 4, 32, 32, FAKE, FAKE, FAKE, FAKE, None, None, None) == -2
 
+
+
+def test_mxfp4_validation(lib):
+    assert lib.mxfp4_quantize(FAKE, 0, 4, 48, 48, FAKE, FAKE, None, None) == -1
+    assert "multiple of 32" in err(lib)
+    assert lib.mxfp4_quantize(None, 0, 4, 64, 64, FAKE, FAKE, None, None) == -1
+    ws = lib.mxfp4_resq_select_and_requant_workspace_size(128, 8, 1, 32)
+    assert ws == lib.resq_select_and_requant_workspace_size(128, 8, 1, 32)
+    # k must be a multiple of 32 in MXFP4
+    assert lib.mxfp4_resq_select_and_requant(FAKE, 0, 8, 128, 128, None, FAKE, FAKE, FAKE, 1, 8, 16,
+                                             None, FAKE, FAKE, FAKE, FAKE, ws, None) == -1
+    assert "multiple of 32" in err(lib)
+    # the GEMM needs K % 128 == 0, kc % 32 == 0 and 4-byte aligned scales
+    args = [FAKE, FAKE, None, 8, FAKE, 1, 8, 192, FAKE, FAKE, 256, None, None, None, 0, 0,
+            None, None, 0, FAKE, 256, None, None, 0, None]
+    assert lib.moe_mxfp4_grouped_gemm(*args) == -1
+    assert "multiple of 128" in err(lib)
+    args[7] = 256
+    args[11], args[12], args[13], args[14] = FAKE, FAKE, FAKE, 48
+    assert lib.moe_mxfp4_grouped_gemm(*args) == -1
+    assert "kc=48" in err(lib)
+    args[11], args[12], args[13], args[14] = None, None, None, 0
+    args[9] = ctypes.c_void_p(0x1002)
+    assert lib.moe_mxfp4_grouped_gemm(*args) == -1
+    assert "4-byte aligned" in err(lib)

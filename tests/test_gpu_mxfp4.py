@@ -1,0 +1,318 @@
+"""GPU parity of the MXFP4 variant: the HIP library (through its C ABI)
+against the MXFP4 oracle on identical seeded inputs.
+
+Bar: codes, E8M0 scales, tile partials, selected channels and requantized
+residuals bit-exact; GEMM outputs within max|Y_gpu - Y_ref| / max|Y_ref| <=
+1e-3 per output tensor (per expert for grouped GEMMs) against the float64
+product of the same quantized operands.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import formats as F
+from oracle import mxfp4 as MX
+from oracle import nvfp4 as OQ
+
+pytestmark = pytest.mark.gpu
+
+GEMM_TOL = 1e-3
+
+
+def np32(t):
+    return t.detach().float().cpu().numpy()
+
+
+def npu8(t):
+    return t.detach().cpu().numpy()
+
+
+def rel_err(y, ref):
+    den = np.abs(ref).max()
+    return float(np.abs(y - ref).max() / (den if den > 0 else 1.0))
+
+
+# ---------------------------------------------------------------------------
+# quantize
+# ---------------------------------------------------------------------------
+
+def test_mx_quantize_exhaustive_bf16(gpu_lib):
+    """Every finite bf16 value in blocks of mixed magnitudes, and every value
+    again in blocks whose scale is fixed (amax 6 * 2^X) so that each one is
+    rounded at X = 0, 9 and -20, ties included."""
+    P = gpu_lib
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = F.bf16_bits_to_f32(bits)
+    vals = vals[np.isfinite(vals)]
+    rng = np.random.default_rng(0)
+    mixed = np.concatenate([vals, np.zeros((-vals.size) % 128, np.float32)])
+    x_np = mixed[rng.permutation(mixed.size)].reshape(-1, 128)
+    codes, scales, _ = P.mxfp4_quantize(torch.from_numpy(x_np).to(torch.bfloat16).cuda())
+    c_ref, s_ref = MX.quantize(x_np)
+    assert np.array_equal(npu8(scales), s_ref)
+    assert np.array_equal(npu8(codes), c_ref)
+    for X in (0, 9, -20):
+        d = np.float32(2.0 ** X)
+        v = vals[np.abs(vals.astype(np.float64)) < 6.0 * 2.0 ** X]
+        n = (v.size + 30) // 31 * 31
+        blocks = np.zeros((n // 31, 32), np.float32)
+        blocks[:, 0] = 6 * d
+        blocks[:, 1:] = np.pad(v, (0, n - v.size)).reshape(-1, 31)
+        blocks = np.concatenate([blocks, np.zeros(((-blocks.shape[0]) % 4, 32), np.float32)])
+        xb = blocks.reshape(-1, 128)
+        codes, scales, _ = P.mxfp4_quantize(torch.from_numpy(xb).to(torch.bfloat16).cuda())
+        c_ref, s_ref = MX.quantize(xb)
+        assert np.array_equal(npu8(scales), s_ref), f"X={X}"
+        assert np.array_equal(npu8(codes), c_ref), f"X={X}"
+
+
+def test_mx_quantize_scale_boundaries(gpu_lib):
+    """Block maxima on and one fp32 ulp either side of every power of two the
+    shared exponent changes at, from the subnormal range to 2^127, in fp32."""
+    P = gpu_lib
+    p2 = np.ldexp(np.float32(1.0), np.arange(-149, 128)).astype(np.float32)
+    amax = np.concatenate([p2, np.nextafter(p2, np.float32(0)), np.nextafter(p2, np.float32(np.inf))])
+    amax = amax[np.isfinite(amax) & (amax > 0)]
+    amax = np.concatenate([amax, np.zeros((-amax.size) % 4, np.float32)])
+    rng = np.random.default_rng(4)
+    x = (amax[:, None] * rng.uniform(-1, 1, (amax.size, 32))).astype(np.float32)
+    x[:, 5] = amax
+    x_np = x.reshape(-1, 128)
+    codes, scales, _ = P.mxfp4_quantize(torch.from_numpy(x_np).cuda())
+    c_ref, s_ref = MX.quantize(x_np)
+    assert np.array_equal(npu8(scales), s_ref)
+    assert np.array_equal(npu8(codes), c_ref)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("m,k", [(128, 512), (300, 4096), (1, 32), (7, 96)])
+def test_mx_quantize_random_with_tile_partials(gpu_lib, dtype, m, k):
+    P = gpu_lib
+    x = synth.activations(m, k, seed=5, heavy_frac=0.01).to(dtype)
+    if dtype == torch.float32:
+        x = x + torch.randn(x.shape, generator=torch.Generator().manual_seed(1)) * 1e-3
+    x_np = x.float().numpy()
+    codes, scales, tp = P.mxfp4_quantize(x.cuda(), tile_partials=True)
+    c_ref, s_ref = MX.quantize(x_np)
+    assert np.array_equal(npu8(scales), s_ref)
+    assert np.array_equal(npu8(codes), c_ref)
+    r = np.abs(MX.residual(x_np, c_ref, s_ref))
+    tp_ref = np.stack([OQ.channel_scores(r[t:t + 128]) for t in range(0, m, 128)])
+    assert np.array_equal(np32(tp), tp_ref)
+
+
+# ---------------------------------------------------------------------------
+# residual selection
+# ---------------------------------------------------------------------------
+
+def test_mx_resq_tile_units(gpu_lib):
+    """Units = 128-token tiles with the quantizer's fused tile partials."""
+    P = gpu_lib
+    x = synth.activations(300, 1024, seed=7, heavy_frac=0.01)
+    xc = x.cuda()
+    codes, scales, tp = P.mxfp4_quantize(xc, tile_partials=True)
+    sel, rc, rs = P.mxfp4_resq_select_and_requant(xc, codes, scales, 128, tile_partials=tp)
+    x_np = x.float().numpy()
+    c_ref, s_ref = MX.quantize(x_np)
+    offs = [0, 128, 256, 300]
+    sel_r, rc_r, rs_r = MX.resq_select_and_requant(x_np, c_ref, s_ref, offs, 128)
+    assert np.array_equal(npu8(sel), sel_r)
+    assert np.array_equal(npu8(rs), rs_r)
+    assert np.array_equal(npu8(rc), rc_r)
+
+
+@pytest.mark.parametrize("k", [32, 64])
+def test_mx_resq_gathered_expert_units(gpu_lib, k):
+    """Units = experts' routed tokens through the slot->token map, with skewed
+    loads, an empty expert and units longer than one 128-row tile."""
+    P = gpu_lib
+    tokens, hidden, n_exp = 400, 256, 6
+    x = synth.activations(tokens, hidden, seed=8, heavy_frac=0.02)
+    rt = synth.route(tokens, n_exp, seed=8, top_k=2, zipf_s=1.5)
+    offs = rt["offsets"].copy()
+    offs[4] = offs[3]
+    xc = x.cuda()
+    codes, scales, _ = P.mxfp4_quantize(xc)
+    sel, rc, rs = P.mxfp4_resq_select_and_requant(
+        xc, codes, scales, k, unit_offsets=torch.from_numpy(offs).cuda(), rows_total=int(offs[-1]),
+        row_index=torch.from_numpy(rt["slot_token"]).cuda())
+    x_np = x.float().numpy()
+    c_ref, s_ref = MX.quantize(x_np)
+    sel_r, rc_r, rs_r = MX.resq_select_and_requant(x_np, c_ref, s_ref, offs, k,
+                                                   row_index=rt["slot_token"])
+    assert np.diff(offs).max() > 128
+    assert np.array_equal(npu8(sel), sel_r)
+    assert np.array_equal(npu8(rs), rs_r)
+    assert np.array_equal(npu8(rc), rc_r)
+
+
+# ---------------------------------------------------------------------------
+# GEMM
+# ---------------------------------------------------------------------------
+
+def _mx_weights(P, w):
+    """MXFP4 codes and scales of w [E, N, K] (each row independently)."""
+    e, n, k = w.shape
+    c, s, _ = P.mxfp4_quantize(w.reshape(e * n, k).cuda())
+    return c.reshape(e, n, k // 2), s.reshape(e, n, k // 32)
+
+
+def _gemm_ref(a_c, a_s, w_c, w_s, sel=None, rc=None, rs=None):
+    return MX.gemm_comp(a_c, a_s, w_c, w_s, sel, rc, rs)
+
+
+@pytest.mark.parametrize("spread", [False, True])
+def test_mx_dense_linear_compensated(gpu_lib, spread):
+    """Single dense linear 128 x 512 -> 1024 with top-32 compensation over all
+    128 tokens (E = 1).  With spread, some weight blocks are scaled by 2^-12, so
+    weight rows span more than 8 binades and the compensation's smallest W_S
+    elements are rounded to E4M3 on the GPU."""
+    P = gpu_lib
+    wl = synth.WORKLOADS["dense_T128_K512_N1024_k32"]
+    x = synth.activations(wl.tokens, wl.hidden, seed=wl.seed, outlier_channels=wl.outliers)
+    w = synth.weights(1, wl.n_out, wl.hidden, seed=wl.seed, tensor_id=synth.WDENSE_ID)
+    if spread:
+        w = w.clone()
+        w[0, :, 32:96] *= 2.0 ** -12
+    xc = x.cuda()
+    codes, scales, _ = P.mxfp4_quantize(xc)
+    offs = torch.tensor([0, wl.tokens], dtype=torch.int64, device="cuda")
+    sel, rc, rs = P.mxfp4_resq_select_and_requant(xc, codes, scales, wl.k, unit_offsets=offs,
+                                                  rows_total=wl.tokens)
+    wc, ws_ = _mx_weights(P, w)
+    y = P.moe_mxfp4_grouped_gemm(codes, scales, offs, wl.tokens, wc, ws_, sel_idx=sel, r_codes=rc,
+                                 r_scales=rs)
+    y0 = P.moe_mxfp4_grouped_gemm(codes, scales, offs, wl.tokens, wc, ws_)
+    ref = _gemm_ref(npu8(codes), npu8(scales), npu8(wc)[0], npu8(ws_)[0], npu8(sel)[0], npu8(rc),
+                    npu8(rs))
+    ref0 = _gemm_ref(npu8(codes), npu8(scales), npu8(wc)[0], npu8(ws_)[0])
+    e_comp, e_plain = rel_err(np32(y), ref), rel_err(np32(y0), ref0)
+    assert e_comp <= GEMM_TOL and e_plain <= GEMM_TOL, (e_comp, e_plain)
+    if not spread:
+        exact = x.float().numpy().astype(np.float64) @ MX.dequantize(
+            npu8(wc)[0], npu8(ws_)[0]).astype(np.float64).T
+        assert np.linalg.norm(np32(y) - exact) < np.linalg.norm(np32(y0) - exact)
+
+
+def _route_setup(tokens, hidden, n_exp, inter, seed, zipf, top_k, empty_expert=None):
+    x = synth.activations(tokens, hidden, seed=seed, heavy_frac=0.01)
+    rt = synth.route(tokens, n_exp, seed=seed, top_k=top_k, zipf_s=zipf)
+    offs = rt["offsets"].copy()
+    if empty_expert is not None:
+        offs[empty_expert + 1] = offs[empty_expert]
+    wgu = synth.weights(n_exp, 2 * inter, hidden, seed=seed, tensor_id=synth.WGU_ID)
+    wd = synth.weights(n_exp, hidden, inter, seed=seed, tensor_id=synth.WD_ID)
+    return x, rt, offs, wgu, wd
+
+
+def _gate_up_ref(codes, scales, slot_token, offs, gc, gs, sel=None, rc=None, rs=None):
+    rows = int(offs[-1])
+    out = np.zeros((rows, gc.shape[1]), np.float64)
+    for e in range(len(offs) - 1):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        tok = slot_token[a:b]
+        comp = (sel[e], rc[a:b], rs[a:b]) if sel is not None else (None, None, None)
+        out[a:b] = _gemm_ref(codes[tok], scales[tok], gc[e], gs[e], *comp)
+    return out
+
+
+@pytest.mark.parametrize("tokens,n_exp,top_k,zipf", [
+    (600, 2, 2, 0.0),     # 600 rows per expert: 256-row tiles, last one 88 rows
+    (340, 4, 2, 0.3),     # ~170 rows per expert: one 256-row tile
+    (300, 4, 2, 0.5),     # 150 rows per expert: 128-row tiles
+    (200, 8, 2, 1.0),     # 50 rows per expert: 64-row tiles
+    (64, 16, 4, 0.0),     # 16 rows per expert: 32-row tiles
+])
+def test_mx_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
+    """Every tile shape (chosen from the average rows per expert) with
+    compensation, F32 and SwiGLU epilogues, K = 384 (three 128-K stages) and
+    N = 2 x 160 (a partial N tile)."""
+    P = gpu_lib
+    hidden, inter, k = 384, 160, 64
+    x, rt, offs, wgu, _ = _route_setup(tokens, hidden, n_exp, inter, 21, zipf, top_k)
+    xc = x.cuda()
+    rows = int(offs[-1])
+    offs_t = torch.from_numpy(offs).cuda()
+    slot_tok = torch.from_numpy(rt["slot_token"]).cuda()
+    codes, scales, _ = P.mxfp4_quantize(xc)
+    sel, rc, rs = P.mxfp4_resq_select_and_requant(xc, codes, scales, k, unit_offsets=offs_t,
+                                                  rows_total=rows, row_index=slot_tok)
+    gc, gs = _mx_weights(P, wgu)
+    comp = dict(sel_idx=sel, r_codes=rc, r_scales=rs)
+    gu = P.moe_mxfp4_grouped_gemm(codes, scales, offs_t, rows, gc, gs, a_row_index=slot_tok, **comp)
+    h = P.moe_mxfp4_grouped_gemm(codes, scales, offs_t, rows, gc, gs, a_row_index=slot_tok,
+                                 epilogue=P.EPI_SWIGLU_BF16, **comp)
+    gu_ref = _gate_up_ref(npu8(codes), npu8(scales), rt["slot_token"], offs, npu8(gc), npu8(gs),
+                          npu8(sel), npu8(rc), npu8(rs))
+    gu_np = np32(gu)
+    for e in range(n_exp):
+        a, b = offs[e], offs[e + 1]
+        if a < b:
+            assert rel_err(gu_np[a:b], gu_ref[a:b]) <= GEMM_TOL, f"expert {e}"
+    g_, u_ = gu_ref[:, :inter], gu_ref[:, inter:]
+    h_r = F.bf16_bits_to_f32(F.f64_to_bf16_bits(g_ / (1 + np.exp(-g_)) * u_))
+    tol = np.abs(h_r) * 2.0 ** -7 + GEMM_TOL * np.abs(h_r).max()
+    assert np.all(np.abs(np32(h) - h_r) <= tol)
+
+
+@pytest.mark.parametrize("comp", [True, False])
+def test_mx_moe_layer(gpu_lib, comp):
+    """The MXFP4 MoE layer stage by stage on the GPU's own intermediates:
+    quantize X, select + requantize per expert, gate/up with SwiGLU and the
+    amax of h, quantize h, select per expert, down with the scatter-add."""
+    P = gpu_lib
+    tokens, hidden, n_exp, inter, k = 200, 256, 8, 256, 64
+    x, rt, offs, wgu, wd = _route_setup(tokens, hidden, n_exp, inter, 9, 1.2, 4, empty_expert=5)
+    xc = x.cuda()
+    rows = int(offs[-1])
+    offs_t = torch.from_numpy(offs).cuda()
+    slot_tok = torch.from_numpy(rt["slot_token"]).cuda()
+    codes, scales, _ = P.mxfp4_quantize(xc)
+    comp1, comp1_ref = {}, (None, None, None)
+    if comp:
+        sel, rc, rs = P.mxfp4_resq_select_and_requant(xc, codes, scales, k, unit_offsets=offs_t,
+                                                      rows_total=rows, row_index=slot_tok)
+        comp1 = dict(sel_idx=sel, r_codes=rc, r_scales=rs)
+        comp1_ref = (npu8(sel), npu8(rc), npu8(rs))
+    gc, gs = _mx_weights(P, wgu)
+    amax = torch.empty(1, dtype=torch.float32, device="cuda")
+    h = P.moe_mxfp4_grouped_gemm(codes, scales, offs_t, rows, gc, gs, a_row_index=slot_tok,
+                                 epilogue=P.EPI_SWIGLU_BF16, out_amax=amax, **comp1)
+    gu_ref = _gate_up_ref(npu8(codes), npu8(scales), rt["slot_token"], offs, npu8(gc), npu8(gs),
+                          *comp1_ref)
+    g_, u_ = gu_ref[:, :inter], gu_ref[:, inter:]
+    h_r = F.bf16_bits_to_f32(F.f64_to_bf16_bits(g_ / (1 + np.exp(-g_)) * u_))
+    h_np = np32(h)
+    tol = np.abs(h_r) * 2.0 ** -7 + GEMM_TOL * np.abs(h_r).max()
+    assert np.all(np.abs(h_np - h_r) <= tol)
+    assert np32(amax)[0] == np.abs(h_np).max()
+    hq_c, hq_s, _ = P.mxfp4_quantize(h)
+    hc_r, hs_r = MX.quantize(h_np)
+    assert np.array_equal(npu8(hq_c), hc_r) and np.array_equal(npu8(hq_s), hs_r)
+    comp2, comp2_ref = {}, None
+    if comp:
+        sel2, rc2, rs2 = P.mxfp4_resq_select_and_requant(h, hq_c, hq_s, k, unit_offsets=offs_t,
+                                                         rows_total=rows)
+        s2r = MX.resq_select_and_requant(h_np, hc_r, hs_r, offs, k)
+        assert np.array_equal(npu8(sel2), s2r[0]) and np.array_equal(npu8(rc2), s2r[1])
+        assert np.array_equal(npu8(rs2), s2r[2])
+        comp2, comp2_ref = dict(sel_idx=sel2, r_codes=rc2, r_scales=rs2), s2r
+    dc, ds = _mx_weights(P, wd)
+    y = torch.zeros(tokens, hidden, dtype=torch.float32, device="cuda")
+    P.moe_mxfp4_grouped_gemm(hq_c, hq_s, offs_t, rows, dc, ds, epilogue=P.EPI_SCATTER_ADD_F32,
+                             row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
+                             scatter_index=slot_tok, out=y, **comp2)
+    y_ref = np.zeros((tokens, hidden), np.float64)
+    dc_n, ds_n = npu8(dc), npu8(ds)
+    for e in range(n_exp):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a == b:
+            continue
+        c2 = (comp2_ref[0][e], comp2_ref[1][a:b], comp2_ref[2][a:b]) if comp else (None, None, None)
+        out = _gemm_ref(hc_r[a:b], hs_r[a:b], dc_n[e], ds_n[e], *c2)
+        np.add.at(y_ref, rt["slot_token"][a:b], out * rt["slot_weight"][a:b, None].astype(np.float64))
+    assert rel_err(np32(y), y_ref) <= GEMM_TOL
