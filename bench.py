@@ -56,13 +56,15 @@ def profiled_traffic(workload, kernel):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def gemm_kernel_name(rows, experts, epilogue):
+def gemm_kernel_name(rows, experts, epilogue, fmt="nvfp4"):
     """Name of the grouped-GEMM kernel instance the library picks: rows per
     tile from the average rows per expert (>= 160: 256, >= 64: 128,
     >= 24: 64, else 32), epilogue 1 = SwiGLU, 2 = scatter."""
     avg = rows // max(experts, 1)
     cfg = "4, 4, 2, 2" if avg >= 160 else "2, 4, 2, 2" if avg >= 64 else \
           "1, 4, 2, 2" if avg >= 24 else "1, 2, 1, 4"
+    if fmt == "mxfp4":
+        return f"nvfp4::mxg::mx_grouped_gemm_kernel<{cfg}, {epilogue}>"
     return f"nvfp4::grouped_gemm_kernel<{cfg}, {epilogue}>"
 
 
@@ -134,9 +136,17 @@ def build_inputs(torch, P, synth, wl, dev):
     wd = synth.weights(wl.experts, wl.hidden, wl.inter, seed=wl.seed, tensor_id=synth.WD_ID,
                        device=dev.type)
     x_train = synth.guided_noise(x, seed=wl.seed, rel=wl.guided_rel) if wl.trainer else None
-    # rollout-side NVFP4 weights (pre-quantized outside the timed region)
-    _, gc, gs, gg = P.qdq_weights(wgu)
-    _, dc, ds, dg = P.qdq_weights(wd)
+    # rollout-side FP4 weights (pre-quantized outside the timed region)
+    if wl.fmt == "mxfp4":
+        E = wl.experts
+        gc, gs, _ = P.mxfp4_quantize(wgu.reshape(E * 2 * wl.inter, wl.hidden))
+        dc, ds, _ = P.mxfp4_quantize(wd.reshape(E * wl.hidden, wl.inter))
+        gc, gs = gc.reshape(E, 2 * wl.inter, -1), gs.reshape(E, 2 * wl.inter, -1)
+        dc, ds = dc.reshape(E, wl.hidden, -1), ds.reshape(E, wl.hidden, -1)
+        gg = dg = None
+    else:
+        _, gc, gs, gg = P.qdq_weights(wgu)
+        _, dc, ds, dg = P.qdq_weights(wd)
     torch.cuda.synchronize()
     inp = dict(
         x=x, x_train=x_train, wgu=wgu, wd=wd, gc=gc, gs=gs, gg=gg, dc=dc, ds=ds, dg=dg,
@@ -150,7 +160,37 @@ def build_inputs(torch, P, synth, wl, dev):
     return inp, time.time() - t_gen
 
 
+def run_step_mx(P, inp, wl, tl):
+    """One pass of the MXFP4 rollout path (same steps as run_step)."""
+    tl.mark("start")
+    xq_c, xq_s, _ = P.mxfp4_quantize(inp["x"])
+    tl.mark("quantize_x")
+    sel1, rc1, rs1 = P.mxfp4_resq_select_and_requant(
+        inp["x"], xq_c, xq_s, wl.k, unit_offsets=inp["offs"], rows_total=inp["rows"],
+        row_index=inp["slot_token"])
+    tl.mark("resq_x")
+    h = P.moe_mxfp4_grouped_gemm(xq_c, xq_s, inp["offs"], inp["rows"], inp["gc"], inp["gs"],
+                                 epilogue=P.EPI_SWIGLU_BF16, a_row_index=inp["slot_token"],
+                                 sel_idx=sel1, r_codes=rc1, r_scales=rs1, out_amax=inp["amax"])
+    tl.mark("gemm_gate_up")
+    hq_c, hq_s, _ = P.mxfp4_quantize(h)
+    tl.mark("quantize_h")
+    sel2, rc2, rs2 = P.mxfp4_resq_select_and_requant(h, hq_c, hq_s, wl.k, unit_offsets=inp["offs"],
+                                                     rows_total=inp["rows"])
+    tl.mark("resq_h")
+    inp["y"].zero_()
+    tl.mark("zero_y")
+    P.moe_mxfp4_grouped_gemm(hq_c, hq_s, inp["offs"], inp["rows"], inp["dc"], inp["ds"],
+                             epilogue=P.EPI_SCATTER_ADD_F32, sel_idx=sel2, r_codes=rc2,
+                             r_scales=rs2, row_weight=inp["slot_weight"],
+                             scatter_index=inp["slot_token"], out=inp["y"])
+    tl.mark("gemm_down")
+    return dict(xq=(xq_c, xq_s), sel1=(sel1, rc1, rs1), h=h, hq=(hq_c, hq_s), sel2=(sel2, rc2, rs2))
+
+
 def run_step(P, inp, wl, tl, trainer=True):
+    if wl.fmt == "mxfp4":
+        return run_step_mx(P, inp, wl, tl)
     tl.mark("start")
     xq_c, xq_s, xq_g, _ = P.nvfp4_quantize(inp["x"])
     tl.mark("quantize_x")
@@ -189,7 +229,8 @@ def run_step(P, inp, wl, tl, trainer=True):
 def part_work(wl, rows):
     """Algorithmic bytes / flops of each part of one step."""
     T, H, I, E, k = wl.tokens, wl.hidden, wl.inter, wl.experts, wl.k
-    nv = lambda n: n * (0.5 + 1 / 16)                       # NVFP4 bytes of n elements
+    sb = 32 if wl.fmt == "mxfp4" else 16
+    nv = lambda n: n * (0.5 + 1 / sb)                       # FP4 bytes of n elements (codes + scales)
     w = {}
     w["quantize_x"] = dict(bytes=T * H * 2 + nv(T * H), unit="GB/s")
     w["resq_x"] = dict(bytes=rows * H * 2 + nv(rows * H) + nv(rows * k) + E * k * 4, unit="GB/s")
@@ -214,6 +255,7 @@ def cpu_baseline(wl, inp, budget_s):
     until the time budget is spent.  Returns GEMM TFLOP/s on the host."""
     import torch
     from oracle import gemm as OG
+    from oracle import mxfp4 as OM
     from oracle import nvfp4 as OQ
     try:
         from threadpoolctl import threadpool_info
@@ -226,24 +268,32 @@ def cpu_baseline(wl, inp, budget_s):
     flops = 0.0
     done = 0
     t0 = time.time()
-    xc, xsc, xg = OQ.quantize(xs)
+    mx = wl.fmt == "mxfp4"
+    if mx:
+        xc, xsc = OM.quantize(xs)
+    else:
+        xc, xsc, xg = OQ.quantize(xs)
     for e in range(wl.experts):
         a, b = int(offs[e]), int(offs[e + 1])
         if b == a:
             continue
-        rows_x = xs[tok[a:b]]
-        sel, rc, rs, rg = OQ.resq_select_and_requant(xs, xc, xsc, xg, [0, b - a], wl.k, row_index=tok[a:b])
         wgu = inp["wgu"][e:e + 1].float().cpu().numpy()
-        _, gc, gs, gg = OQ.qdq_weights(wgu)
-        OG.gemm_comp(xc[tok[a:b]], xsc[tok[a:b]], xg, gc[0], gs[0], gg[0], sel[0], rc, rs, rg[0])
+        if mx:
+            sel, rc, rs = OM.resq_select_and_requant(xs, xc, xsc, [0, b - a], wl.k, row_index=tok[a:b])
+            gc, gs = OM.quantize_weights(wgu)
+            OM.gemm_comp(xc[tok[a:b]], xsc[tok[a:b]], gc[0], gs[0], sel[0], rc, rs)
+        else:
+            sel, rc, rs, rg = OQ.resq_select_and_requant(xs, xc, xsc, xg, [0, b - a], wl.k,
+                                                         row_index=tok[a:b])
+            _, gc, gs, gg = OQ.qdq_weights(wgu)
+            OG.gemm_comp(xc[tok[a:b]], xsc[tok[a:b]], xg, gc[0], gs[0], gg[0], sel[0], rc, rs, rg[0])
         flops += gemm_flops(b - a, 2 * wl.inter, wl.hidden, wl.k)
         done += 1
-        del rows_x
         if time.time() - t0 > budget_s:
             break
     dt = time.time() - t0
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
-                sample=f"NVFP4 quantization of X, then {done} expert(s) of the gate/up projection "
+                sample=f"{wl.fmt.upper()} quantization of X, then {done} expert(s) of the gate/up projection "
                        f"({wl.hidden}->{2 * wl.inter}, k={wl.k}) in expert order, each with residual "
                        f"selection, weight quantization and the fp64 compensated GEMM; {dt:.1f} s",
                 seconds=round(dt, 2))
@@ -555,12 +605,14 @@ def main():
     # largest single kernel of the step).  Its part also holds the 1-thread
     # fill that zeroes out_amax (about 2 us).
     ach = work["gemm_gate_up"]["flops"] / (parts_ms["gemm_gate_up"] * 1e-3) / 1e12
-    kname = gemm_kernel_name(inp["rows"], wl.experts, 1)
+    kname = gemm_kernel_name(inp["rows"], wl.experts, 1, wl.fmt)
     traffic = profiled_traffic(wl.name, kname)
-    roofline = dict(bound="mfma", achieved=round(ach, 2), peak=FP16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=round(ach / FP16_PEAK_TFLOPS, 4),
+    mx = wl.fmt == "mxfp4"
+    peak = FP4_PEAK_TFLOPS if mx else FP16_PEAK_TFLOPS
+    roofline = dict(bound="mfma", achieved=round(ach, 2), peak=peak, unit="TFLOP/s",
+                    frac=round(ach / peak, 4),
                     traffic=None if traffic is None else int(traffic),
-                    kernel=kname, mfma_dtype="fp16",
+                    kernel=kname, mfma_dtype="fp4 (block-scaled)" if mx else "fp16",
                     launch_ms=round(parts_ms["gemm_gate_up"], 4),
                     flops_per_launch=work["gemm_gate_up"]["flops"],
                     frac_fp4_peak=round(ach / FP4_PEAK_TFLOPS, 4))
@@ -581,7 +633,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "nvfp4 (e2m1 + e4m3 scales) operands, fp16 MFMA (exact products), fp32 accumulate",
+        "dtype": ("mxfp4 (e2m1 + e8m0 scales) operands, block-scaled fp4 MFMA, fp32 accumulate"
+                  if mx else
+                  "nvfp4 (e2m1 + e4m3 scales) operands, fp16 MFMA (exact products), fp32 accumulate"),
         "data": "synthetic (seeded; Gaussian activations with 1% Student-t(3) x8 channels, "
                 "N(0,0.02) weights, top-8 softmax routing)",
         "config": {"workload": wl.name, "tokens": wl.tokens, "hidden": wl.hidden,

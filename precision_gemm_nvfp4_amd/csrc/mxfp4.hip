@@ -179,6 +179,12 @@ constexpr int KS = 128;                    // K per pipeline stage
 constexpr int ROW = 80;                    // LDS bytes per row
 constexpr int MAX_KC = 128;
 
+// Bytes per W_S row in LDS for kc compensated channels: one byte per channel
+// of the padded width plus 16 of padding (0 without compensation).
+__host__ __device__ constexpr int ws_stride(int kc) {
+  return kc > 0 ? (kc + 63) / 64 * 64 + 16 : 0;
+}
+
 template <int BM>
 struct Layout {
   static constexpr int AR = BM + 1;                  // row BM: spare for threads past the tile
@@ -220,12 +226,15 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   using L = Layout<BM>;
   constexpr int STAGE = L::STAGE, B_OFF = L::B_OFF, NA = L::NA;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // LDS: 2 stages | W_S [BN][WSS] fp8 | Xmax bytes [BN] | sel [MAX_KC] | jr [nst + 1]
-  constexpr int WSS = MAX_KC + 16;
+  // LDS: 2 stages | W_S [BN][wss] bytes | Xmax bytes [BN] | sel [MAX_KC] |
+  // gather table [nst] (u32x2 per stage).  W_S row t holds, for each selected
+  // channel j, code | min(xmax - scale byte, 15) << 4 during the K loop, and
+  // the E4M3 byte of W[t, sel[j]] / 2^(xmax - 127) after it (convert_ws).
+  const int wss = ws_stride(p.sel_idx ? p.kc : 0);
   unsigned char* WS = smem + 2 * STAGE;
-  unsigned char* WX = WS + BN * WSS;
+  unsigned char* WX = WS + BN * wss;
   int32_t* sel = reinterpret_cast<int32_t*>(WX + BN);
-  int32_t* jr = sel + MAX_KC;
+  u32x2* tab = reinterpret_cast<u32x2*>(sel + MAX_KC);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -295,6 +304,15 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
     r.as = *reinterpret_cast<const uint32_t*>(a_sp + (int64_t)m * 4);
     r.bs = *reinterpret_cast<const uint32_t*>(b_sp + (int64_t)m * 4);
   };
+  // xmax: the largest scale byte of weight row tid (read in the prologue).
+  uint32_t xmax = 0;
+  auto max_bytes = [&](uint32_t w) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t b = (w >> (8 * q)) & 0xFFu;
+      xmax = b > xmax ? b : xmax;
+    }
+  };
   auto swrite = [&](int st, const Ld& r) {
     unsigned char* base = smem + st * STAGE;
 #pragma unroll
@@ -311,31 +329,64 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   };
 
   // ---- prologue: compensation set-up, row weights -----------------------------
-  uint32_t xmax = 0;                          // largest scale byte of weight row tid
+  // Q(R_S) of this wave's rows for one 64-wide K-step: codes of lane half
+  // `half` and the scale bytes of both halves.  Step 0 is loaded ahead of
+  // the K loop, step 1 (kc > 64) after it.
+  const int rb = kc / 2, sbr = kc / kMxBlock;
+  u32x4 rq[MI];
+  uint32_t rsc[MI];
+  auto load_rs = [&](int ks) {
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm * MI * 32 + i * 32 + l32;
+      rq[i] = u32x4{0, 0, 0, 0};
+      rsc[i] = 0;
+      if (r < rows_valid) {
+        const int64_t ur = row0 + r;
+        if (ks * 64 + half * 32 < kc)
+          rq[i] = *reinterpret_cast<const u32x4*>(p.r_codes + ur * rb + ks * 32 + half * 16);
+        const uint32_t s0 = p.r_scales[ur * sbr + ks * 2];
+        const uint32_t s1 = ks * 64 + 32 < kc ? p.r_scales[ur * sbr + ks * 2 + 1] : 0u;
+        rsc[i] = s0 | (s1 << 8);
+      }
+    }
+  };
+  // First selected channel at or after channel c (binary search in LDS).
+  auto lower = [&](int c) {
+    int lo = 0, hi = kc;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (sel[mid] < c) lo = mid + 1; else hi = mid;
+    }
+    return lo;
+  };
   if (comp) {
     for (int j = tid; j < kc; j += 256) {
       int32_t c = p.sel_idx[(int64_t)e * kc + j];
       sel[j] = c < 0 ? 0 : (c >= K ? (int32_t)(K - 1) : c);
     }
-    for (int i = tid; i < BN * WSS / 16; i += 256) reinterpret_cast<u32x4*>(WS)[i] = u32x4{0, 0, 0, 0};
-    for (int64_t q = 0; q < sbytes; q += 4) {
-      const uint32_t w = *reinterpret_cast<const uint32_t*>(b_sp + q);
+    load_rs(0);
+    // the row's scale bytes, all loads in flight together (K <= 4096 takes one pass)
+    const int n16 = (int)(sbytes / 16), n4 = (int)(sbytes / 4);
+    for (int q = 0; q < n16; q += 8) {
+      u32x4 w[8];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint32_t b = (w >> (8 * s)) & 0xFFu;
-        xmax = b > xmax ? b : xmax;
-      }
+      for (int u = 0; u < 8; ++u)
+        w[u] = q + u < n16 ? *reinterpret_cast<const u32x4*>(b_sp + 16 * (q + u)) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int u = 0; u < 8; ++u) { max_bytes(w[u][0]); max_bytes(w[u][1]); max_bytes(w[u][2]); max_bytes(w[u][3]); }
     }
-    WX[tid] = (uint8_t)xmax;
+    for (int q = 4 * n16; q < n4; ++q) max_bytes(*reinterpret_cast<const uint32_t*>(b_sp + 4 * q));
+    // padding channels kc .. kcp-1 of W_S are zero (entry 0 converts to +0)
+    for (int j = kc; j < kcp; ++j) WS[tid * wss + j] = 0;
     __syncthreads();
-    // jr[m]: the first j with sel[j] in stage m or later
-    for (int m = tid; m <= nst; m += 256) {
-      int lo = 0, hi = kc;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (sel[mid] < m * KS) lo = mid + 1; else hi = mid;
-      }
-      jr[m] = lo;
+    // gather table of stage m: first selected channel j0 and count n, and the
+    // in-stage offsets of its first four channels
+    for (int m = tid; m < nst; m += 256) {
+      const int j0 = lower(m * KS), n = lower((m + 1) * KS) - j0;
+      uint32_t kk = 0;
+      for (int q = 0; q < 4 && q < n; ++q) kk |= (uint32_t)((sel[j0 + q] - m * KS) & 0x7F) << (8 * q);
+      tab[m] = u32x2{(uint32_t)j0 | ((uint32_t)n << 8), kk};
     }
   }
   if constexpr (EPI == 2) {
@@ -350,21 +401,46 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // W_S bytes of the selected channels inside stage m (LDS stage st) for
-  // weight row tid: the loop count depends on m only.
-  auto gather_ws = [&](int m, int st) {
-    const unsigned char* row = smem + st * STAGE + B_OFF + tid * ROW;
-    const int j1 = jr[m + 1];
-    for (int jj = jr[m]; jj < j1; ++jj) {
-      const int kk = sel[jj] - m * KS;                       // 0..127 inside the stage
-      if ((unsigned)kk >= (unsigned)KS) continue;            // only if sel is not ascending
-      const uint32_t code = (row[kk >> 1] >> (4 * (kk & 1))) & 15u;
-      const int d = (int)row[64 + (kk >> 5)] - (int)xmax;   // <= 0
-      const float f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(code, 1.0f, 0)[0];
-      WS[tid * WSS + jj] = (uint8_t)__builtin_amdgcn_cvt_pk_fp8_f32(f * pow2_nonpos(d), 0.0f, 0, false);
+  // W_S entry of weight row tid for a selected channel at offset kk inside
+  // the stage held in LDS row `row`: code | min(xmax - scale byte, 15) << 4
+  // (E2M1 times 2^-15 or less is below half of E4M3's smallest subnormal,
+  // so the clamp changes no E4M3 rounding).
+  unsigned char* WSt = WS + tid * wss;
+  auto ws_entry = [&](uint32_t code_byte, uint32_t scale, int kk) {
+    const uint32_t code = (code_byte >> (4 * (kk & 1))) & 15u;
+    const uint32_t d = xmax - scale;                          // >= 0
+    return code | ((d < 15u ? d : 15u) << 4);
+  };
+  // Stage m's selected channels beyond the first four (rare): a plain loop.
+  auto gather_rest = [&](const unsigned char* row, int m, int j0, int n) {
+    for (int jj = j0 + 4; jj < j0 + n; ++jj) {
+      const int kk = sel[jj] - m * KS;
+      if ((unsigned)kk < (unsigned)KS)                        // false only if sel is not ascending
+        WSt[jj] = (uint8_t)ws_entry(row[kk >> 1], row[64 + (kk >> 5)], kk);
     }
   };
+  // After the K loop: W_S row tid in E4M3 against 2^xmax, in place.
+  auto convert_ws = [&]() {
+#pragma unroll 4
+    for (int q = 0; q < kcp / 8; ++q) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(WSt + 8 * q);
+      float f[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const uint32_t b = (v[u >> 2] >> (8 * (u & 3))) & 0xFFu;
+        f[u] = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(b & 15u, 1.0f, 0)[0] * pow2_nonpos(-(int)(b >> 4));
+      }
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+      int hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[4], f[5], 0, false);
+      hi = __builtin_amdgcn_cvt_pk_fp8_f32(f[6], f[7], hi, true);
+      *reinterpret_cast<u32x2*>(WSt + 8 * q) = u32x2{(uint32_t)lo, (uint32_t)hi};
+    }
+    WX[tid] = (uint8_t)xmax;
+  };
 
+  // tm: gather table entry of the current stage (uniform; read one stage ahead)
+  u32x2 tm = u32x2{0, 0};
   auto stage = [&](int m, int st, Ld& rset) {
     const unsigned char* base = smem + st * STAGE;
     u32x4 fa[2][MI], fb[2][NJ];
@@ -383,7 +459,28 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
       fb[1][j] = *reinterpret_cast<const u32x4*>(row + 32 + half * 16);
       sb[j] = *reinterpret_cast<const uint32_t*>(row + 64) >> (8 * half);
     }
-    if (comp) gather_ws(m, st);
+    // the gather's LDS reads go out now and are consumed after the MFMAs
+    const unsigned char* grow = base + B_OFF + tid * ROW;
+    int j0 = 0, n = 0;
+    uint32_t gcb[4], gsb[4];
+    u32x2 tnext = u32x2{0, 0};
+    if (comp) {
+      j0 = __builtin_amdgcn_readfirstlane((int)(tm[0] & 0xFFu));
+      n = __builtin_amdgcn_readfirstlane((int)(tm[0] >> 8));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int kk = (int)((tm[1] >> (8 * q)) & 0x7Fu);
+        gcb[q] = q < n ? grow[kk >> 1] : 0u;
+        gsb[q] = q < n ? grow[64 + (kk >> 5)] : 0u;
+      }
+      if (m + 1 < nst) tnext = tab[m + 1];
+    }
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int i = 0; i < MI; ++i)
+        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+            as_v8i(fa[0][i]), as_v8i(fb[0][j]), acc[i][j], 4, 4, 0, (int)sa[i], 0, (int)sb[j]);
     swrite(st ^ 1, rset);                                    // data of stage m + 1
     if (m + 3 < nst) gload(m + 3, rset);
 #pragma unroll
@@ -391,13 +488,14 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_v8i(fa[0][i]), as_v8i(fb[0][j]), acc[i][j], 4, 4, 0, (int)sa[i], 0, (int)sb[j]);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
             as_v8i(fa[1][i]), as_v8i(fb[1][j]), acc[i][j], 4, 4, 2, (int)sa[i], 2, (int)sb[j]);
+    if (comp) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (q < n) WSt[j0 + q] = (uint8_t)ws_entry(gcb[q], gsb[q], (int)((tm[1] >> (8 * q)) & 0x7Fu));
+      if (n > 4) gather_rest(grow, m, j0, n);
+      tm = tnext;
+    }
     lds_barrier();
   };
 
@@ -408,6 +506,7 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
     swrite(0, R0);
     if (nst > 2) gload(2, R0);
     __syncthreads();
+    if (comp) tm = tab[0];
     for (int m = 0; m < nst; m += 2) {
       stage(m, 0, R1);
       if (m + 1 < nst) stage(m + 1, 1, R0);
@@ -416,28 +515,22 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 
   // ---- compensation: Q(R_S) (widened to E4M3) x W_S (E4M3, row scale) -----
   if (comp) {
-    const int rb = kc / 2, sbr = kc / kMxBlock;
-    for (int ks = 0; ks < kcp / 64; ++ks) {
-      const bool live_h = ks * 64 + half * 32 < kc;        // lane half inside kc
+    convert_ws();
+    __syncthreads();
+    for (int ks = 0; ks < 2; ++ks) {
+      if (ks * 64 >= kc) break;                               // uniform
+      if (ks == 1) load_rs(1);
       v8i fa[MI], fb[NJ];
       uint32_t sa[MI], sb[NJ];
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const int r = wm * MI * 32 + i * 32 + l32;
         // Both lane halves of a row take one scale, the larger of the row's
         // two blocks in this K-step (the FP8 form of the MFMA is only used
         // with a scale shared by all 64 K-values of a row or column, so the
         // order in which it pairs K-values and scales does not matter).
-        u32x4 w = u32x4{0, 0, 0, 0};
-        uint32_t s_own = 0, s_max = 127u;
-        if (r < rows_valid) {
-          const int64_t ur = row0 + r;
-          const uint32_t s0 = p.r_scales[ur * sbr + ks * 2];
-          const uint32_t s1 = ks * 64 + 32 < kc ? p.r_scales[ur * sbr + ks * 2 + 1] : 0u;
-          s_max = s0 > s1 ? s0 : s1;
-          s_own = half ? s1 : s0;
-          if (live_h) w = *reinterpret_cast<const u32x4*>(p.r_codes + ur * rb + ks * 32 + half * 16);
-        }
+        const u32x4 w = rq[i];
+        const uint32_t s0 = rsc[i] & 0xFFu, s1 = rsc[i] >> 8;
+        const uint32_t s_max = s0 > s1 ? s0 : s1, s_own = half ? s1 : s0;
         const float f = pow2_nonpos((int)s_own - (int)s_max);
         u32x2 q[4];
 #pragma unroll
@@ -449,8 +542,8 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const int r = wn * NJ * 32 + j * 32 + l32;
-        const u32x4 lo = *reinterpret_cast<const u32x4*>(WS + r * WSS + ks * 64 + half * 32);
-        const u32x4 hi = *reinterpret_cast<const u32x4*>(WS + r * WSS + ks * 64 + half * 32 + 16);
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(WS + r * wss + ks * 64 + half * 32);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(WS + r * wss + ks * 64 + half * 32 + 16);
         fb[j] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                     (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         sb[j] = WX[r];
@@ -470,9 +563,9 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 }
 
 template <int MI, int NJ, int WM, int WN>
-__host__ constexpr size_t loop_lds_bytes(int64_t K) {
-  return 2 * (size_t)Layout<WM * MI * 32>::STAGE + (size_t)BN * (MAX_KC + 16) + BN +
-         (size_t)(MAX_KC + K / KS + 1) * 4;
+__host__ constexpr size_t loop_lds_bytes(int64_t K, int kc) {
+  return 2 * (size_t)Layout<WM * MI * 32>::STAGE + (size_t)BN * ws_stride(kc) + BN +
+         (size_t)MAX_KC * 4 + (size_t)(K / KS) * 8;
 }
 
 template <int MI, int NJ, int WM, int WN, int EPI>
@@ -481,7 +574,7 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   const int64_t mtiles = (a.rows_total + BM - 1) / BM + a.E;
   const int64_t ntiles = a.epilogue == 1 ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const int64_t total = mtiles * ntiles;
-  const size_t loop = (loop_lds_bytes<MI, NJ, WM, WN>(a.K) + 15) / 16 * 16;
+  const size_t loop = (loop_lds_bytes<MI, NJ, WM, WN>(a.K, a.sel_idx ? a.kc : 0) + 15) / 16 * 16;
   const size_t epi = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
   const size_t body = loop > epi ? loop : epi;
   a.rw_lds_offset = (int)body;
@@ -507,7 +600,7 @@ static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
 }  // namespace mxg
 
 size_t mx_gemm_max_lds(int64_t K) {
-  return mxg::loop_lds_bytes<4, 4, 2, 2>(K) + 16 + 256 * 4;
+  return mxg::loop_lds_bytes<4, 4, 2, 2>(K, mxg::MAX_KC) + 16 + 256 * 4;
 }
 
 hipError_t launch_mx_grouped_gemm(const GemmArgs& a, hipStream_t stream) {

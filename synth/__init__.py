@@ -136,6 +136,7 @@ class Workload:
     outliers: tuple = ()
     trainer: bool = False     # also run weight QDQ and guided rounding
     guided_rel: float = 1e-3
+    fmt: str = "nvfp4"        # FP4 format of the rollout path: "nvfp4" or "mxfp4"
     extra: dict = field(default_factory=dict)
 
 
@@ -151,6 +152,13 @@ WORKLOADS = {
                  hidden=2048, experts=128, inter=768, k=64, heavy_frac=0.01, zipf_s=1.1),
         Workload("moe_T8192_H4096_E256_I1536_k64_trainer", "moe", seed=4, tokens=8192,
                  hidden=4096, experts=256, inter=1536, k=64, heavy_frac=0.01, trainer=True),
+        Workload("mx_moe_decode_T256_H2048_E128_I768_k64", "moe", seed=2, tokens=256,
+                 hidden=2048, experts=128, inter=768, k=64, heavy_frac=0.01, fmt="mxfp4"),
+        Workload("mx_moe_prefill_T16384_H2048_E128_I768_zipf1.1_k64", "moe", seed=3,
+                 tokens=16384, hidden=2048, experts=128, inter=768, k=64, heavy_frac=0.01,
+                 zipf_s=1.1, fmt="mxfp4"),
+        Workload("mx_moe_T8192_H4096_E256_I1536_k64", "moe", seed=4, tokens=8192, hidden=4096,
+                 experts=256, inter=1536, k=64, heavy_frac=0.01, fmt="mxfp4"),
         Workload("guidance_record_T8192_K4096", "guidance", seed=4, tokens=8192, hidden=4096,
                  k=0, heavy_frac=0.01),
         Workload("kv_T65536_H4_D128", "kv", seed=5, tokens=65536, hidden=128, k=0,
