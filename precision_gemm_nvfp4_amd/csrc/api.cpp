@@ -306,6 +306,8 @@ int moe_mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                 (long long)N, (long long)rows_total);
   if (K % 128 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 128", fn, (long long)K);
   if (K > 65536) return fail(NVFP4_EUNSUPPORTED, "%s: K=%lld > 65536", fn, (long long)K);
+  if (a_rows * (K / 2) >= (1LL << 32) || N * (K / 2) >= (1LL << 32))   // 32-bit lane offsets
+    return fail(NVFP4_EUNSUPPORTED, "%s: A or one expert's W spans 4 GiB or more", fn);
   if (rows_total > 2147483647LL) return fail(NVFP4_EUNSUPPORTED, "%s: rows_total above 2^31-1", fn);
   if (!group_offsets || !w_codes || !w_scales || !out)
     return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);

@@ -149,14 +149,22 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t M, int64_t K, in
 // Tiles: BM (256/128/64/32) rows x 256 weight rows, four waves each owning
 // MI x NJ blocks of 32 x 32; the (expert, m-tile, n-tile) decomposition, the
 // XCD-aware tile order and the epilogues are the NVFP4 GEMM's
-// (gemm_common.h).  K moves 128 per pipeline stage: an LDS row is 64 code
-// bytes, the 4 scale bytes of the stage's blocks and 12 bytes of padding
-// (an 80-byte stride keeps the 16-byte fragment reads of 8 consecutive rows
-// on distinct banks).  Thread t loads 16-byte chunk t % 4 of rows t / 4 + 64 i
-// of both operands and the scale word of row t.  Two LDS stages and two
-// register sets: in stage m a wave reads its fragments of stage m, writes
-// the data of stage m + 1 into the other LDS stage and issues the loads of
-// stage m + 3, then runs its 2 MI NJ MFMAs; one barrier per stage.
+// (gemm_common.h).  K moves 128 per pipeline stage through a ring of LDS
+// slots (four for tiles of 128 rows or more, else three), filled by direct
+// global-to-LDS loads (global_load_lds_dwordx4:
+// lane l of the instruction writes 16 bytes at base + 16 l, so no registers
+// carry the tiles).  A slot holds the stage's 64 code bytes of every A and W
+// row, 16-byte chunks swizzled within a row (chunk c of row r at position
+// c ^ ((r >> 1) & 3), so that the fragment reads of 8 consecutive rows hit
+// distinct banks), then the 4 scale bytes of every row.  Each wave issues the
+// same number of load instructions per stage (padding ones go to a dummy
+// area), so one vmcnt wait tells it its share of a stage has landed.
+// Iteration m: run the first half of the stage-m MFMAs from registers, wait
+// for stage m + 1 and meet at the one barrier, issue the loads of stage
+// m + PD (PD = slots - 1) into the slot stage m - 1 used, and read the
+// stage-(m + 1) fragments while the second half of the stage-m MFMAs runs.
+// So LDS reads and loads overlap the matrix cores, and a slot is refilled
+// only after every wave has passed the barrier that followed its last read.
 //
 // Compensation.  A lane of the MFMA applies one scale to its 32 K-values,
 // but the selected channels W[n, sel[j]] keep the scales of the blocks they
@@ -176,8 +184,8 @@ namespace mxg {
 
 constexpr int BN = 256;
 constexpr int KS = 128;                    // K per pipeline stage
-constexpr int ROW = 80;                    // LDS bytes per row
 constexpr int MAX_KC = 128;
+constexpr int DUMMY_BYTES = 1024;          // target of the padding loads
 
 // Bytes per W_S row in LDS for kc compensated channels: one byte per channel
 // of the padded width plus 16 of padding (0 without compensation).
@@ -185,13 +193,48 @@ __host__ __device__ constexpr int ws_stride(int kc) {
   return kc > 0 ? (kc + 63) / 64 * 64 + 16 : 0;
 }
 
+// One LDS slot: A codes [BM][64], W codes [BN][64], A scale words
+// [max(BM, 64)], W scale words [BN].  Load instructions per wave and stage:
+// NAI A-code blocks of 16 rows, 4 W-code blocks, one A-scale and one W-scale
+// block of 64 rows.
 template <int BM>
 struct Layout {
-  static constexpr int AR = BM + 1;                  // row BM: spare for threads past the tile
-  static constexpr int NA = BM < 64 ? 1 : BM / 64;   // A chunk loads per thread
-  static constexpr int STAGE = (AR + BN) * ROW;
-  static constexpr int B_OFF = AR * ROW;
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = BM * 64;
+  static constexpr int AS_OFF = (BM + BN) * 64;
+  static constexpr int ASR = BM < 64 ? 64 : BM;
+  static constexpr int BS_OFF = AS_OFF + ASR * 4;
+  static constexpr int STAGE = BS_OFF + BN * 4;
+  static constexpr int NAI = BM < 64 ? 1 : BM / 64;
+  static constexpr int LPW = NAI + 6;                  // load instructions per wave and stage
+  // LDS ring: four slots (three stages in flight) for the tall tiles, whose
+  // time per stage is set by how many bytes a CU keeps in flight; three for
+  // the short ones, so that two of them still share a CU
+  static constexpr int NSLOT = BM >= 128 ? 4 : 3;
+  static constexpr int PD = NSLOT - 1;                 // prefetch distance in stages
 };
+
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+
+template <int V>
+struct KC {                                 // a compile-time count
+  static constexpr int value = V;
+};
+
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+__device__ __forceinline__ void load_lds16(const void* g, unsigned char* l) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const void* g, unsigned char* l) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 0-3 and 14-15)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | ((N >> 4) << 14));
+}
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
@@ -218,26 +261,28 @@ __device__ __forceinline__ float pow2_nonpos(int d) {
   return d >= -126 ? __uint_as_float((uint32_t)(127 + d) << 23) : 0.0f;
 }
 
-template <int MI, int NJ, int WM, int WN, int EPI>
+template <int MI, int NJ, int WM, int WN, int EPI, bool COMP>
 __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int ntiles) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
   static_assert(WM * WN == 4, "four waves");
   using L = Layout<BM>;
-  constexpr int STAGE = L::STAGE, B_OFF = L::B_OFF, NA = L::NA;
+  constexpr int STAGE = L::STAGE, NAI = L::NAI, LPW = L::LPW, NSLOT = L::NSLOT, PD = L::PD;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // LDS: 2 stages | W_S [BN][wss] bytes | Xmax bytes [BN] | sel [MAX_KC] |
-  // gather table [nst] (u32x2 per stage).  W_S row t holds, for each selected
-  // channel j, code | min(xmax - scale byte, 15) << 4 during the K loop, and
-  // the E4M3 byte of W[t, sel[j]] / 2^(xmax - 127) after it (convert_ws).
+  // LDS: NSLOT slots | dummy | W_S [BN][wss] bytes | Xmax bytes [BN] |
+  // sel [MAX_KC] | gather table [nst] (u32x2 per stage).  W_S row t holds, for
+  // each selected channel j, code | min(xmax - scale byte, 15) << 4 during the
+  // K loop, and the E4M3 byte of W[t, sel[j]] / 2^(xmax - 127) after it.
   const int wss = ws_stride(p.sel_idx ? p.kc : 0);
-  unsigned char* WS = smem + 2 * STAGE;
+  unsigned char* DUMMY = smem + NSLOT * STAGE;
+  unsigned char* WS = DUMMY + DUMMY_BYTES;
   unsigned char* WX = WS + BN * wss;
   int32_t* sel = reinterpret_cast<int32_t*>(WX + BN);
   u32x2* tab = reinterpret_cast<u32x2*>(sel + MAX_KC);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
@@ -252,58 +297,72 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   const int64_t K = p.K;
   const int nst = (int)(K / KS);
   const int64_t rbytes = K / 2, sbytes = K / kMxBlock;
-  const bool comp = p.sel_idx != nullptr;
+  constexpr bool comp = COMP;
   const int kc = comp ? p.kc : 0;
   const int kcp = (kc + 63) / 64 * 64;
   float* RW = reinterpret_cast<float*>(smem + p.rw_lds_offset);
 
-  // ---- row pointers (branch-free loads: rows outside the tile read row 0) --
-  const int g4 = tid & 3;
-  const uint8_t* a_cp[NA];
-  uint32_t a_keep[NA];
+  // ---- load addressing ---------------------------------------------------------
+  // Lane l of a 16-row block instruction loads row 16 b + l / 4, position
+  // l % 4, i.e. logical chunk (l % 4) ^ swz(row).  Rows outside the tile, and
+  // A rows whose index lies outside [0, a_rows), read row 0 (their results are
+  // never stored, or unspecified for a bad index).
+  auto a_row = [&](int r) -> int64_t {
+    if (r >= rows_valid) return 0;
+    const int64_t ur = row0 + r;
+    const int64_t ar = p.a_row_index ? (int64_t)p.a_row_index[ur] : ur;
+    return ar >= 0 && ar < p.a_rows ? ar : 0;
+  };
+  // weight row of tile row r inside expert e's matrix (row 0 past N)
+  auto w_row = [&](int r) -> int64_t {
+    const int64_t br = weight_row<BN>(p, n_tile, r);
+    return br >= 0 ? br : 0;
+  };
+  // Global addresses are a uniform base (kernel argument plus the expert's
+  // and the stage's offsets, kept in SGPRs) plus a 32-bit per-lane offset
+  // (the host checks that each operand spans less than 4 GiB).
+  const uint8_t* wc_e = p.w_codes + (int64_t)e * p.N * rbytes;
+  const uint8_t* ws_e = p.w_scales + (int64_t)e * p.N * sbytes;
+  const int lr = lane >> 2, lp = lane & 3;
+  uint32_t a_off[NAI];
 #pragma unroll
-  for (int i = 0; i < NA; ++i) {
-    const int r = (tid >> 2) + 64 * i;
-    int64_t ar = 0;
-    bool ok = false;
-    if (r < rows_valid) {
-      const int64_t ur = row0 + r;
-      ar = p.a_row_index ? (int64_t)p.a_row_index[ur] : ur;
-      ok = ar >= 0 && ar < p.a_rows;
-      if (!ok) ar = 0;
-    }
-    a_keep[i] = ok ? 0xFFFFFFFFu : 0u;       // a row index outside [0, a_rows) reads as zeros
-    a_cp[i] = p.a_codes + ar * rbytes + g4 * 16;
+  for (int i = 0; i < NAI; ++i) {
+    const int b = wave * NAI + i, r = b * 16 + lr;
+    a_off[i] = (uint32_t)(a_row(b < BM / 16 ? r : BM) * rbytes) + ((lp ^ swz(r)) << 4);
   }
-  int64_t as_row = 0;
-  if (tid < rows_valid) {
-    const int64_t ur = row0 + tid;
-    as_row = p.a_row_index ? (int64_t)p.a_row_index[ur] : ur;
-    if (as_row < 0 || as_row >= p.a_rows) as_row = 0;
-  }
-  const uint8_t* a_sp = p.a_scales + as_row * sbytes;
-  const uint8_t* b_cp[4];
+  uint32_t b_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int64_t br = weight_row<BN>(p, n_tile, (tid >> 2) + 64 * i);
-    b_cp[i] = p.w_codes + ((int64_t)e * p.N + (br >= 0 ? br : 0)) * rbytes + g4 * 16;
+    const int r = (wave * 4 + i) * 16 + lr;
+    b_off[i] = (uint32_t)(w_row(r) * rbytes) + ((lp ^ swz(r)) << 4);
   }
-  const int64_t b_own = weight_row<BN>(p, n_tile, tid);
-  const uint8_t* b_sp = p.w_scales + ((int64_t)e * p.N + (b_own >= 0 ? b_own : 0)) * sbytes;
+  // Scale words are stored in the order the fragment reads want them: the
+  // word of A row wm MI 32 + 32 i + l32 at position (wm 32 + l32) MI + i, so
+  // a lane reads its MI words (likewise NJ for W) with one LDS instruction.
+  // Lane l of the scale instruction of wave w fills position 64 w + l.
+  const int rs_pos = 64 * wave + lane;
+  const int ra_s = (rs_pos / (32 * MI)) * (32 * MI) + (rs_pos % MI) * 32 + (rs_pos / MI) % 32;
+  const int rb_s = (rs_pos / (32 * NJ)) * (32 * NJ) + (rs_pos % NJ) * 32 + (rs_pos / NJ) % 32;
+  const uint32_t as_off = (uint32_t)(a_row(rs_pos < BM ? ra_s : BM) * sbytes);
+  const uint32_t bs_off = (uint32_t)(w_row(rb_s) * sbytes);
+  const uint8_t* b_sp = ws_e + w_row(tid) * sbytes;   // weight row tid (compensation)
 
-  struct Ld {
-    u32x4 a[NA], b[4];
-    uint32_t as, bs;
-  };
-  auto gload = [&](int m, Ld& r) {
-    const int64_t co = (int64_t)m * 64;
+  // the LPW load instructions of stage m into slot `slot`
+  auto issue = [&](int m, int slot) {
+    unsigned char* base = smem + slot * STAGE;
+    const uint8_t* ac = p.a_codes + (int64_t)m * 64;
+    const uint8_t* wcm = wc_e + (int64_t)m * 64;
 #pragma unroll
-    for (int i = 0; i < NA; ++i) r.a[i] = *reinterpret_cast<const u32x4*>(a_cp[i] + co);
+    for (int i = 0; i < NAI; ++i) {
+      const int b = wave * NAI + i;
+      load_lds16(ac + a_off[i], b < BM / 16 ? base + L::A_OFF + b * 1024 : DUMMY);
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r.b[i] = *reinterpret_cast<const u32x4*>(b_cp[i] + co);
-    r.as = *reinterpret_cast<const uint32_t*>(a_sp + (int64_t)m * 4);
-    r.bs = *reinterpret_cast<const uint32_t*>(b_sp + (int64_t)m * 4);
+    for (int i = 0; i < 4; ++i) load_lds16(wcm + b_off[i], base + L::B_OFF + (wave * 4 + i) * 1024);
+    load_lds4(p.a_scales + (int64_t)m * 4 + as_off, 64 * wave < BM ? base + L::AS_OFF + wave * 256 : DUMMY);
+    load_lds4(ws_e + (int64_t)m * 4 + bs_off, base + L::BS_OFF + wave * 256);
   };
+
   // xmax: the largest scale byte of weight row tid (read in the prologue).
   uint32_t xmax = 0;
   auto max_bytes = [&](uint32_t w) {
@@ -313,20 +372,11 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
       xmax = b > xmax ? b : xmax;
     }
   };
-  auto swrite = [&](int st, const Ld& r) {
-    unsigned char* base = smem + st * STAGE;
+
+  // the first two stages go out first, so that their latency overlaps the
+  // compensation set-up below
 #pragma unroll
-    for (int i = 0; i < NA; ++i) {
-      const int row = (tid >> 2) + 64 * i;
-      const u32x4 v = r.a[i] & a_keep[i];
-      *reinterpret_cast<u32x4*>(base + (row < BM ? row : BM) * ROW + g4 * 16) = v;
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<u32x4*>(base + B_OFF + ((tid >> 2) + 64 * i) * ROW + g4 * 16) = r.b[i];
-    *reinterpret_cast<uint32_t*>(base + (tid < BM ? tid : BM) * ROW + 64) = r.as;
-    *reinterpret_cast<uint32_t*>(base + B_OFF + tid * ROW + 64) = r.bs;
-  };
+  for (int q = 0; q < PD; ++q) issue(q < nst ? q : nst - 1, q);
 
   // ---- prologue: compensation set-up, row weights -----------------------------
   // Q(R_S) of this wave's rows for one 64-wide K-step: codes of lane half
@@ -401,8 +451,8 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // W_S entry of weight row tid for a selected channel at offset kk inside
-  // the stage held in LDS row `row`: code | min(xmax - scale byte, 15) << 4
+  // W_S entry of weight row tid for a selected channel at K-offset kk of a
+  // stage, from its code byte and scale byte: code | min(xmax - scale, 15) << 4
   // (E2M1 times 2^-15 or less is below half of E4M3's smallest subnormal,
   // so the clamp changes no E4M3 rounding).
   unsigned char* WSt = WS + tid * wss;
@@ -410,14 +460,6 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
     const uint32_t code = (code_byte >> (4 * (kk & 1))) & 15u;
     const uint32_t d = xmax - scale;                          // >= 0
     return code | ((d < 15u ? d : 15u) << 4);
-  };
-  // Stage m's selected channels beyond the first four (rare): a plain loop.
-  auto gather_rest = [&](const unsigned char* row, int m, int j0, int n) {
-    for (int jj = j0 + 4; jj < j0 + n; ++jj) {
-      const int kk = sel[jj] - m * KS;
-      if ((unsigned)kk < (unsigned)KS)                        // false only if sel is not ascending
-        WSt[jj] = (uint8_t)ws_entry(row[kk >> 1], row[64 + (kk >> 5)], kk);
-    }
   };
   // After the K loop: W_S row tid in E4M3 against 2^xmax, in place.
   auto convert_ws = [&]() {
@@ -439,78 +481,143 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
     WX[tid] = (uint8_t)xmax;
   };
 
-  // tm: gather table entry of the current stage (uniform; read one stage ahead)
+  // A wave's fragments: A0/B0 feed the stage's first 64-wide K-step, A1/B1
+  // its second (lane half h takes logical chunk 2 ks + h), SA/SB the scale
+  // words shifted so that op_sel 0 / 2 picks the lane's block of step 0 / 1.
+  // A0/B0 of stage m + 1 are read as soon as the step-0 MFMAs of stage m have
+  // been issued, A1/B1 and the scale words after the step-1 ones.
+  u32x4 A0[MI], B0[NJ], A1[MI], B1[NJ];
+  uint32_t SA[MI], SB[NJ];
+  // Per-lane LDS offsets: the swizzle of rows r = 32 i + l32 (+ a multiple of
+  // 32) depends on l32 only, so the row blocks are immediate offsets.
+  const int sw = swz(l32);
+  const uint32_t fa_off[2] = {(uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 64 + ((half ^ sw) << 4)),
+                              (uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 64 + (((2 + half) ^ sw) << 4))};
+  const uint32_t fb_off[2] = {(uint32_t)(L::B_OFF + (wn * NJ * 32 + l32) * 64 + ((half ^ sw) << 4)),
+                              (uint32_t)(L::B_OFF + (wn * NJ * 32 + l32) * 64 + (((2 + half) ^ sw) << 4))};
+  const uint32_t sa_off = (uint32_t)(L::AS_OFF + (wm * 32 + l32) * MI * 4);
+  const uint32_t sb_off = (uint32_t)(L::BS_OFF + (wn * 32 + l32) * NJ * 4);
+  auto read_half = [&](int slot, int ks, u32x4* A, u32x4* B) {
+    const unsigned char* base = smem + slot * STAGE;
+#pragma unroll
+    for (int i = 0; i < MI; ++i) A[i] = *reinterpret_cast<const u32x4*>(base + fa_off[ks] + i * 2048);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) B[j] = *reinterpret_cast<const u32x4*>(base + fb_off[ks] + j * 2048);
+  };
+  auto read_words = [&](const unsigned char* p_, uint32_t* w, auto NW) {
+    constexpr int n = decltype(NW)::value;
+    if constexpr (n == 4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(p_);
+      w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+    } else if constexpr (n == 2) {
+      const u32x2 v = *reinterpret_cast<const u32x2*>(p_);
+      w[0] = v[0]; w[1] = v[1];
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(p_);
+    }
+  };
+  auto read_scales = [&](int slot) {
+    const unsigned char* base = smem + slot * STAGE;
+    read_words(base + sa_off, SA, KC<MI>{});
+    read_words(base + sb_off, SB, KC<NJ>{});
+#pragma unroll
+    for (int i = 0; i < MI; ++i) SA[i] >>= 8 * half;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) SB[j] >>= 8 * half;
+  };
+
+  // gather table entry of the current stage (uniform; read one stage ahead)
   u32x2 tm = u32x2{0, 0};
-  auto stage = [&](int m, int st, Ld& rset) {
-    const unsigned char* base = smem + st * STAGE;
-    u32x4 fa[2][MI], fb[2][NJ];
-    uint32_t sa[MI], sb[NJ];
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const unsigned char* row = base + (wm * MI * 32 + i * 32 + l32) * ROW;
-      fa[0][i] = *reinterpret_cast<const u32x4*>(row + half * 16);
-      fa[1][i] = *reinterpret_cast<const u32x4*>(row + 32 + half * 16);
-      sa[i] = *reinterpret_cast<const uint32_t*>(row + 64) >> (8 * half);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const unsigned char* row = base + B_OFF + (wn * NJ * 32 + j * 32 + l32) * ROW;
-      fb[0][j] = *reinterpret_cast<const u32x4*>(row + half * 16);
-      fb[1][j] = *reinterpret_cast<const u32x4*>(row + 32 + half * 16);
-      sb[j] = *reinterpret_cast<const uint32_t*>(row + 64) >> (8 * half);
-    }
-    // the gather's LDS reads go out now and are consumed after the MFMAs
-    const unsigned char* grow = base + B_OFF + tid * ROW;
+  // The byte holding K-offset kk of weight row tid in a slot, and its scale byte.
+  // (the row is 64-byte aligned; the in-row byte (kk >> 5) << 4 | (kk & 31) >> 1
+  // is uniform, the chunk swizzle of row tid is an XOR on bits 4-5)
+  const uint32_t g_row = (uint32_t)(L::B_OFF + tid * 64), g_sw = (uint32_t)(swz(tid) << 4);
+  const uint32_t g_srow = (uint32_t)(L::BS_OFF +
+      (((tid / (32 * NJ)) * 32 + tid % 32) * NJ + (tid % (32 * NJ)) / 32) * 4);
+  auto w_byte = [&](const unsigned char* base, int kk) {
+    return base + (g_row | ((uint32_t)(((kk >> 5) << 4) | ((kk & 31) >> 1)) ^ g_sw));
+  };
+  auto w_scale = [&](const unsigned char* base, int kk) {
+    return base + g_srow + (kk >> 5);
+  };
+
+  // Iteration m, the same straight-line code for every m (so the
+  // accumulators keep their registers): the loads of stage m + PD -- for the
+  // last PD iterations a repeat of the last stage into a slot nobody reads,
+  // which keeps every wave's count of loads in flight the same -- then the
+  // stage-m MFMAs with the stage-(m + 1) fragment reads between and after
+  // them (in the last iteration those read a slot whose contents go unused).
+  auto body = [&](int m, int slot) {
+    const unsigned char* base = smem + slot * STAGE;
+    const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
     int j0 = 0, n = 0;
     uint32_t gcb[4], gsb[4];
     u32x2 tnext = u32x2{0, 0};
-    if (comp) {
+    if constexpr (COMP) {             // the gather's LDS reads go out first
       j0 = __builtin_amdgcn_readfirstlane((int)(tm[0] & 0xFFu));
       n = __builtin_amdgcn_readfirstlane((int)(tm[0] >> 8));
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int kk = (int)((tm[1] >> (8 * q)) & 0x7Fu);
-        gcb[q] = q < n ? grow[kk >> 1] : 0u;
-        gsb[q] = q < n ? grow[64 + (kk >> 5)] : 0u;
+        const int kk = __builtin_amdgcn_readfirstlane((int)((tm[1] >> (8 * q)) & 0x7Fu));
+        gcb[q] = *w_byte(base, kk);
+        gsb[q] = *w_scale(base, kk);
       }
-      if (m + 1 < nst) tnext = tab[m + 1];
+      tnext = tab[m + 1 < nst ? m + 1 : m];
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_v8i(fa[0][i]), as_v8i(fb[0][j]), acc[i][j], 4, 4, 0, (int)sa[i], 0, (int)sb[j]);
-    swrite(st ^ 1, rset);                                    // data of stage m + 1
-    if (m + 3 < nst) gload(m + 3, rset);
+            as_v8i(A0[i]), as_v8i(B0[j]), acc[i][j], 4, 4, 0, (int)SA[i], 0, (int)SB[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's loads of stage m + 1 have landed (only those of stages
+    // m + 2 .. m + PD - 1 may be outstanding); after the barrier every wave's
+    // have.  The loads of stage m + PD go out here, where no LDS access is in
+    // flight (setting M0 for them waits for those).
+    wait_vm_lgkm0<(PD - 2) * LPW>();
+    asm volatile("s_barrier" ::: "memory");
+    issue(m + PD < nst ? m + PD : nst - 1, slot == 0 ? NSLOT - 1 : slot - 1);   // slot (m + PD) % NSLOT
+    read_half(nslot, 0, A0, B0);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j)
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_v8i(fa[1][i]), as_v8i(fb[1][j]), acc[i][j], 4, 4, 2, (int)sa[i], 2, (int)sb[j]);
-    if (comp) {
+            as_v8i(A1[i]), as_v8i(B1[j]), acc[i][j], 4, 4, 2, (int)SA[i], 2, (int)SB[j]);
+    __builtin_amdgcn_sched_barrier(0);
+    read_half(nslot, 1, A1, B1);
+    read_scales(nslot);
+    if constexpr (COMP) {
+      // entries past the stage's count go to the row's padding bytes
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if (q < n) WSt[j0 + q] = (uint8_t)ws_entry(gcb[q], gsb[q], (int)((tm[1] >> (8 * q)) & 0x7Fu));
-      if (n > 4) gather_rest(grow, m, j0, n);
+        WSt[q < n ? j0 + q : kcp + q] =
+            (uint8_t)ws_entry(gcb[q], gsb[q], (int)((tm[1] >> (8 * q)) & 0x7Fu));
+      for (int jj = j0 + 4; jj < j0 + n; ++jj) {               // more than four: rare
+        const int kk = sel[jj] - m * KS;
+        if ((unsigned)kk < (unsigned)KS)                        // false only if sel is not ascending
+          WSt[jj] = (uint8_t)ws_entry(*w_byte(base, kk), *w_scale(base, kk), kk);
+      }
       tm = tnext;
     }
-    lds_barrier();
   };
 
   {
-    Ld R0, R1;
-    gload(0, R0);
-    if (nst > 1) gload(1, R1); else R1 = R0;
-    swrite(0, R0);
-    if (nst > 2) gload(2, R0);
-    __syncthreads();
-    if (comp) tm = tab[0];
-    for (int m = 0; m < nst; m += 2) {
-      stage(m, 0, R1);
-      if (m + 1 < nst) stage(m + 1, 1, R0);
+    wait_vm_lgkm0<(PD - 1) * LPW>();  // stage 0 has landed (stages 1 .. PD - 1 may be in flight)
+    asm volatile("s_barrier" ::: "memory");
+    read_half(0, 0, A0, B0);
+    read_half(0, 1, A1, B1);
+    read_scales(0);
+    if constexpr (COMP) tm = tab[0];
+    int slot = 0;                     // uniform: the slot offsets are scalar adds
+    for (int m = 0; m < nst; ++m) {
+      body(m, slot);
+      slot = slot == NSLOT - 1 ? 0 : slot + 1;
     }
+    wait_vm_lgkm0<0>();               // the repeat loads of the last iterations
   }
 
   // ---- compensation: Q(R_S) (widened to E4M3) x W_S (E4M3, row scale) -----
@@ -564,11 +671,20 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 
 template <int MI, int NJ, int WM, int WN>
 __host__ constexpr size_t loop_lds_bytes(int64_t K, int kc) {
-  return 2 * (size_t)Layout<WM * MI * 32>::STAGE + (size_t)BN * ws_stride(kc) + BN +
-         (size_t)MAX_KC * 4 + (size_t)(K / KS) * 8;
+  return Layout<WM * MI * 32>::NSLOT * (size_t)Layout<WM * MI * 32>::STAGE + DUMMY_BYTES + (size_t)BN * ws_stride(kc) +
+         BN + (size_t)MAX_KC * 4 + (size_t)(K / KS) * 8;
 }
 
-template <int MI, int NJ, int WM, int WN, int EPI>
+// LDS bytes a tile configuration needs (0 if over the 160 KB of a CU).
+template <int MI, int NJ, int WM, int WN>
+static size_t cfg_lds(const GemmArgs& a) {
+  const size_t loop = (loop_lds_bytes<MI, NJ, WM, WN>(a.K, a.sel_idx ? a.kc : 0) + 15) / 16 * 16;
+  const size_t epi = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
+  const size_t lds = (loop > epi ? loop : epi) + (size_t)WM * MI * 32 * 4 + 256;   // + row weights, static
+  return lds <= 160 * 1024 ? lds : 0;
+}
+
+template <int MI, int NJ, int WM, int WN, int EPI, bool COMP>
 static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   constexpr int BM = WM * MI * 32;
   const int64_t mtiles = (a.rows_total + BM - 1) / BM + a.E;
@@ -579,7 +695,7 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   const size_t body = loop > epi ? loop : epi;
   a.rw_lds_offset = (int)body;
   const size_t lds = body + (EPI == 2 ? (size_t)BM * 4 : 0);
-  auto kern = mx_grouped_gemm_kernel<MI, NJ, WM, WN, EPI>;
+  auto kern = mx_grouped_gemm_kernel<MI, NJ, WM, WN, EPI, COMP>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -590,10 +706,11 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
 
 template <int MI, int NJ, int WM, int WN>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
+  const bool c = a.sel_idx != nullptr;
   switch (a.epilogue) {
-    case 0: return launch_cfg<MI, NJ, WM, WN, 0>(a, stream);
-    case 1: return launch_cfg<MI, NJ, WM, WN, 1>(a, stream);
-    default: return launch_cfg<MI, NJ, WM, WN, 2>(a, stream);
+    case 0: return c ? launch_cfg<MI, NJ, WM, WN, 0, true>(a, stream) : launch_cfg<MI, NJ, WM, WN, 0, false>(a, stream);
+    case 1: return c ? launch_cfg<MI, NJ, WM, WN, 1, true>(a, stream) : launch_cfg<MI, NJ, WM, WN, 1, false>(a, stream);
+    default: return c ? launch_cfg<MI, NJ, WM, WN, 2, true>(a, stream) : launch_cfg<MI, NJ, WM, WN, 2, false>(a, stream);
   }
 }
 
@@ -610,7 +727,10 @@ hipError_t launch_mx_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   }
   if (a.rows_total == 0) return hipSuccess;
   hipError_t err;
-  const int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
+  int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
+  // a long K (a long gather table) can push the tallest tile past the LDS
+  if (bm == 256 && mxg::cfg_lds<4, 4, 2, 2>(a) == 0) bm = 128;
+  if (bm == 128 && mxg::cfg_lds<2, 4, 2, 2>(a) == 0) bm = 64;
   switch (bm) {
     case 256: err = mxg::launch_epi<4, 4, 2, 2>(a, stream); break;
     case 128: err = mxg::launch_epi<2, 4, 2, 2>(a, stream); break;
