@@ -35,7 +35,7 @@ to the selected channels, each element keeping its own block scale.
 
 import numpy as np
 
-from .formats import E2M1_LEVELS, e2m1_decode, e2m1_index_nearest
+from .formats import E2M1_LEVELS, E4M3_VALUES, e2m1_decode, e2m1_index_nearest, e4m3_code_nearest
 from .nvfp4 import channel_scores, pack_nibbles, topk_channels, unpack_nibbles
 
 BLOCK = 32
@@ -167,5 +167,56 @@ def quantize_weights(w):
     return c.reshape(nmat, n, k // 2), s.reshape(nmat, n, k // BLOCK)
 
 
-__all__ = ["BLOCK", "E2M1_LEVELS", "e8m0_decode", "shared_exponents", "quantize", "dequantize",
+# ---------------------------------------------------------------------------
+# W4A8: MXFP8 activations (the TRACE summary's MXFP4 W4A8 rollout, Table 4)
+# ---------------------------------------------------------------------------
+#: Exponent of the largest E4M3 value: 448 = 1.75 * 2^8.
+E4M3_EMAX = 8
+
+
+def shared_exponents_fp8(x):
+    """X of every 32-block for MXFP8 elements: floor(log2 amax) - 8, clamped
+    to [-127, 127]; -127 for an all-zero block (OCP MX, read as for MXFP4)."""
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    amax = np.abs(x.reshape(m, k // BLOCK, BLOCK)).max(axis=2).astype(np.float64)
+    _, e = np.frexp(amax)
+    xe = np.where(amax > 0, e - 1 - E4M3_EMAX, E8M0_XMIN)
+    return np.clip(xe, E8M0_XMIN, E8M0_XMAX).astype(np.int64)
+
+
+def quantize_fp8(x):
+    """MXFP8 quantization of activations x [M, K]: per 32-block the shared
+    exponent above; per element the E4M3 value nearest to |x| / 2^X (exact
+    real quotient, ties to the even byte, values above 448 saturating to 448),
+    sign bit from x.  Returns (codes [M, K] uint8 E4M3 bytes, scales [M, K/32])."""
+    x = np.asarray(x, dtype=np.float32)
+    m, k = x.shape
+    assert k % BLOCK == 0
+    xe = shared_exponents_fp8(x)
+    codes = np.zeros((m, k), dtype=np.uint8)
+    for b in range(k // BLOCK):
+        cols = slice(BLOCK * b, BLOCK * b + BLOCK)
+        blk = x[:, cols]
+        for r in range(m):
+            mag = e4m3_code_nearest(np.abs(blk[r]).astype(np.float64), np.ldexp(1.0, int(xe[r, b])))
+            codes[r, cols] = mag | (np.signbit(blk[r]).astype(np.uint8) << 7)
+    return codes, (xe + E8M0_BIAS).astype(np.uint8)
+
+
+def dequantize_fp8(codes, scales):
+    """value(E4M3 byte) * 2^X as float64 (exact)."""
+    c = np.asarray(codes).astype(np.int64)
+    mag = E4M3_VALUES[c & 0x7F]
+    v = np.where(c & 0x80, -mag, mag)
+    return v * np.repeat(e8m0_decode(scales), BLOCK, axis=1)
+
+
+def gemm_w4a8(a_codes, a_scales, w_codes, w_scales):
+    """Y = DQ(A8) DQ(W4)^T in float64: MXFP8 activations times MXFP4 weights."""
+    return dequantize_fp8(a_codes, a_scales) @ dequantize(w_codes, w_scales).astype(np.float64).T
+
+
+__all__ = ["shared_exponents_fp8", "quantize_fp8", "dequantize_fp8", "gemm_w4a8",
+           "BLOCK", "E2M1_LEVELS", "e8m0_decode", "shared_exponents", "quantize", "dequantize",
            "residual", "resq_select_and_requant", "gemm_comp", "quantize_weights"]

@@ -236,3 +236,69 @@ def test_compensation_linearity_identity():
     e0 = np.abs(MX.gemm_comp(xc, xs, wc, ws) - exact).max()
     e1 = np.abs(MX.gemm_comp(xc, xs, wc, ws, sel_all[0], rca, rsa) - exact).max()
     assert e1 < e0
+
+
+# ---------------------------------------------------------------------------
+# W4A8: MXFP8 activations
+# ---------------------------------------------------------------------------
+
+def test_fp8_shared_exponent_closed_forms():
+    # amax -> X = floor(log2 amax) - 8
+    cases = [(448.0, 0), (256.0, 0), (511.0, 0), (512.0, 1), (255.9, -1), (1.0, -8), (0.0, -127),
+             (2.0 ** -149, -127), (1.5 * 2.0 ** 127, 119)]
+    x = np.zeros((len(cases), 32), dtype=np.float32)
+    for i, (a, _) in enumerate(cases):
+        x[i, 3] = a
+    assert list(MX.shared_exponents_fp8(x)[:, 0]) == [c[1] for c in cases]
+
+
+def test_fp8_quantize_matches_library_cast():
+    """Elements: torch's float8_e4m3fn cast (round to nearest even) of the
+    exactly scaled value, after clamping to +-448 (the format saturates)."""
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((6, 128)) * np.exp(rng.uniform(-15, 15, (6, 1)))).astype(np.float32)
+    x[0, :32] = 0
+    x[1, 7] = -0.0
+    x[2, 40] = np.float32(480.0 * 2.0 ** -3)              # saturates: 480 > 448 at its block's scale
+    x[2, 32:64] = np.clip(x[2, 32:64], -50, 50)
+    x[2, 40] = 61.0                                          # block amax 61 -> X = -3, 61 * 8 = 488 -> 448
+    codes, scales = MX.quantize_fp8(x)
+    xe = scales.astype(np.int64) - 127
+    v = x.astype(np.float64) / np.repeat(np.ldexp(1.0, xe), 32, axis=1)
+    lib = torch.from_numpy(np.clip(v, -448, 448).astype(np.float32)).to(torch.float8_e4m3fn)
+    assert np.array_equal(codes, lib.view(torch.uint8).numpy())
+    assert F.e4m3_decode(codes[2, 40]) == 448.0
+
+
+def test_fp8_quantize_brute_force_and_error():
+    rng = np.random.default_rng(32)
+    x = (rng.standard_normal((3, 64)) * 3).astype(np.float32)
+    codes, scales = MX.quantize_fp8(x)
+    vals = [Fraction(float(v)) for v in F.E4M3_VALUES]
+    for r in range(3):
+        for c in range(64):
+            X = int(scales[r, c // 32]) - 127
+            q = abs(Fraction(float(x[r, c]))) / Fraction(2) ** X
+            best = min(range(len(vals)), key=lambda i: (abs(vals[i] - q), i % 2)) if q <= 448 else 0x7E
+            assert (codes[r, c] & 0x7F) == best
+    # relative error of E4M3 (3 mantissa bits): at most 2^-4 of the value for normal results
+    dq = MX.dequantize_fp8(codes, scales)
+    assert np.all(np.abs(dq - x) <= np.abs(x) * 2.0 ** -4 + 2.0 ** -9 * np.repeat(np.ldexp(1.0, scales.astype(np.int64) - 127), 32, axis=1))
+
+
+def test_w4a8_gemm_brute_force():
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((2, 64)).astype(np.float32)
+    w = (rng.standard_normal((3, 64)) * 0.02).astype(np.float32)
+    ac, asc = MX.quantize_fp8(x)
+    wc, ws = MX.quantize(w)
+    y = MX.gemm_w4a8(ac, asc, wc, ws)
+    W = _exact(wc, ws)
+    for i in range(2):
+        for n in range(3):
+            ref = Fraction(0)
+            for j in range(64):
+                b = int(ac[i, j])
+                v = Fraction(float(F.E4M3_VALUES[b & 0x7F])) * (-1 if b & 0x80 else 1)
+                ref += v * Fraction(2) ** (int(asc[i, j // 32]) - 127) * W[n][j]
+            assert abs(float(ref) - y[i, n]) <= 1e-12 * max(1.0, abs(float(ref)))
