@@ -353,6 +353,40 @@ int moe_mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                            const int32_t* scatter_index, int64_t out_rows, void* out, int64_t ldo,
                            float* out_amax, void* ws, size_t ws_bytes, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * mxfp8_quantize -- MXFP8 quantization of activations for the W4A8 GEMM
+ * ([TRACE] results and Table 4: MXFP4 W4A8 rollouts, FP8 activations with FP4
+ * weights).  Read as OCP MXFP8: 32-element blocks, E8M0 scale byte X + 127
+ * with X = floor(log2 amax_b) - 8 clamped to [-127, 127] (-127 for an
+ * all-zero block); element = E4M3FN byte nearest to |x| / 2^X (ties to the
+ * even byte, above 448 gives 448), sign of x.
+ *   codes  out [M, K] E4M3 bytes;  scales out [M, K/32]
+ * Errors: EINVAL for null required pointers, K % 32 != 0, ldx < K, M < 0.
+ * ------------------------------------------------------------------------ */
+int mxfp8_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                   uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * moe_mxfp4_w4a8_grouped_gemm -- the routed grouped expert GEMM with MXFP8
+ * activations and MXFP4 weights (W4A8), on the matrix cores' mixed FP8 x FP4
+ * form:  Y[r, n] = sum_k A[r, k] W_e[n, k]  (no residual compensation: that
+ * step corrects FP4 activations).  Arguments as moe_mxfp4_grouped_gemm
+ * without the compensation ones; a_codes are [a_rows, K] E4M3 bytes.
+ * Errors: EINVAL (shapes, pointers, alignment, epilogue arguments),
+ *         EUNSUPPORTED (A or one expert's W of 4 GiB or more),
+ *         EWORKSPACE (scatter epilogue).
+ * ------------------------------------------------------------------------ */
+size_t moe_mxfp4_w4a8_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N,
+                                                  int64_t K, int epilogue, int64_t out_rows);
+int moe_mxfp4_w4a8_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const int32_t* a_row_index, int64_t a_rows,
+                                const int64_t* group_offsets, int32_t E, int64_t rows_total,
+                                int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                int64_t N, int epilogue, const float* row_weight,
+                                const int32_t* scatter_index, int64_t out_rows, void* out,
+                                int64_t ldo, float* out_amax, void* ws, size_t ws_bytes,
+                                void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,10 @@ _SIGNATURES = {
     "moe_mxfp4_grouped_gemm": (_INT, [_P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _I64,
                                       _P, _P, _P, _I32, _INT, _P, _P, _I64, _P, _I64, _P, _P,
                                       _SZ, _P]),
+    "mxfp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P]),
+    "moe_mxfp4_w4a8_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _INT, _I64]),
+    "moe_mxfp4_w4a8_grouped_gemm": (_INT, [_P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _I64,
+                                           _INT, _P, _P, _I64, _P, _I64, _P, _P, _SZ, _P]),
 }
 
 
@@ -339,4 +343,48 @@ def moe_mxfp4_grouped_gemm(a_codes, a_scales, group_offsets, rows_total, w_codes
         rows_total, kk, _ptr(w_codes), _ptr(w_scales), n, _ptr(sel_idx), _ptr(r_codes),
         _ptr(r_scales), kc, epilogue, _ptr(row_weight), _ptr(scatter_index), out_rows, _ptr(out),
         out.stride(0), _ptr(out_amax), _ptr(ws), ws.numel(), _stream()), "moe_mxfp4_grouped_gemm")
+    return out
+
+
+def mxfp8_quantize(x):
+    """MXFP8 quantization of activations x [M, K] (bf16/fp32, GPU).
+    Returns (codes uint8 [M, K] E4M3 bytes, scales uint8 [M, K/32] E8M0)."""
+    lib = load()
+    _require_cuda(x)
+    m, k = x.shape
+    codes = torch.empty(m, k, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(m, k // 32, dtype=torch.uint8, device=x.device)
+    _check(lib.mxfp8_quantize(_ptr(x), _dtype_code(x), m, k, x.stride(0), _ptr(codes), _ptr(scales),
+                              _stream()), "mxfp8_quantize")
+    return codes, scales
+
+
+def moe_mxfp4_w4a8_grouped_gemm(a_codes, a_scales, group_offsets, rows_total, w_codes, w_scales,
+                                epilogue=EPI_F32, a_row_index=None, row_weight=None,
+                                scatter_index=None, out=None, out_rows=None, out_amax=None):
+    """Grouped W4A8 GEMM: MXFP8 activations [rows, K] x MXFP4 weights [E, N, K/2]
+    (outputs as moe_w4a4_grouped_gemm)."""
+    lib = load()
+    _require_cuda(a_codes, a_scales, group_offsets, w_codes, w_scales, a_row_index, row_weight,
+                  scatter_index, out, out_amax)
+    n_exp, n, k_half = w_codes.shape
+    kk = k_half * 2
+    dev = w_codes.device
+    if out is None:
+        if epilogue == EPI_F32:
+            out = torch.empty(rows_total, n, dtype=torch.float32, device=dev)
+        elif epilogue == EPI_SWIGLU_BF16:
+            out = torch.empty(rows_total, n // 2, dtype=torch.bfloat16, device=dev)
+        else:
+            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor")
+    if out_rows is None:
+        out_rows = out.shape[0]
+    ws = _workspace(lib.moe_mxfp4_w4a8_grouped_gemm_workspace_size(n_exp, rows_total, n, kk,
+                                                                   epilogue, out_rows), dev)
+    a_rows = a_codes.shape[0] if a_codes is not None else 0
+    _check(lib.moe_mxfp4_w4a8_grouped_gemm(
+        _ptr(a_codes), _ptr(a_scales), _ptr(a_row_index), a_rows, _ptr(group_offsets), n_exp,
+        rows_total, kk, _ptr(w_codes), _ptr(w_scales), n, epilogue, _ptr(row_weight),
+        _ptr(scatter_index), out_rows, _ptr(out), out.stride(0), _ptr(out_amax), _ptr(ws),
+        ws.numel(), _stream()), "moe_mxfp4_w4a8_grouped_gemm")
     return out

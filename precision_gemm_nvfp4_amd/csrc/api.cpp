@@ -356,6 +356,81 @@ int moe_mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 W4A8: MXFP8 activations x MXFP4 weights
+// ---------------------------------------------------------------------------
+int mxfp8_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx, uint8_t* codes,
+                   uint8_t* scales, void* stream) {
+  const char* fn = "mxfp8_quantize";
+  if (int s = check_act(x, dtype, M, K, ldx, fn)) return s;
+  if (K % 32 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+  if (M > 0 && (!codes || !scales)) return fail(NVFP4_EINVAL, "%s: codes/scales are NULL", fn);
+  if (codes && !aligned16(codes)) return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_mx8_quantize(x, dtype, M, K, ldx, codes, scales,
+                                               static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t moe_mxfp4_w4a8_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N,
+                                                  int64_t K, int epilogue, int64_t out_rows) {
+  return moe_w4a4_grouped_gemm_workspace_size(E, rows_total, N, K, epilogue, out_rows);
+}
+
+int moe_mxfp4_w4a8_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
+                                const int32_t* a_row_index, int64_t a_rows,
+                                const int64_t* group_offsets, int32_t E, int64_t rows_total,
+                                int64_t K, const uint8_t* w_codes, const uint8_t* w_scales,
+                                int64_t N, int epilogue, const float* row_weight,
+                                const int32_t* scatter_index, int64_t out_rows, void* out,
+                                int64_t ldo, float* out_amax, void* ws, size_t ws_bytes,
+                                void* stream) {
+  const char* fn = "moe_mxfp4_w4a8_grouped_gemm";
+  if (E <= 0 || K <= 0 || N <= 0 || rows_total < 0 || a_rows < 0)
+    return fail(NVFP4_EINVAL, "%s: E=%d K=%lld N=%lld rows_total=%lld", fn, E, (long long)K,
+                (long long)N, (long long)rows_total);
+  if (K % 128 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 128", fn, (long long)K);
+  if (K > 65536) return fail(NVFP4_EUNSUPPORTED, "%s: K=%lld > 65536", fn, (long long)K);
+  if (a_rows * K >= (1LL << 32) || N * (K / 2) >= (1LL << 32))   // 32-bit lane offsets
+    return fail(NVFP4_EUNSUPPORTED, "%s: A or one expert's W spans 4 GiB or more", fn);
+  if (rows_total > 2147483647LL) return fail(NVFP4_EUNSUPPORTED, "%s: rows_total above 2^31-1", fn);
+  if (!group_offsets || !w_codes || !w_scales || !out)
+    return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if (rows_total > 0 && (!a_codes || !a_scales)) return fail(NVFP4_EINVAL, "%s: a_codes/a_scales NULL", fn);
+  if (rows_total > 0 && a_rows < 1)
+    return fail(NVFP4_EINVAL, "%s: a_rows must be at least 1 when rows_total > 0", fn);
+  if (!aligned16(w_codes) || (a_codes && !aligned16(a_codes)))
+    return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
+  if ((reinterpret_cast<uintptr_t>(w_scales) & 3u) || (reinterpret_cast<uintptr_t>(a_scales) & 3u))
+    return fail(NVFP4_EINVAL, "%s: scales not 4-byte aligned", fn);
+  if (epilogue == NVFP4_EPI_F32) {
+    if (ldo < N) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N", fn, (long long)ldo);
+  } else if (epilogue == NVFP4_EPI_SWIGLU_BF16) {
+    if (N % 2 != 0) return fail(NVFP4_EINVAL, "%s: SwiGLU needs N even", fn);
+    if (ldo < N / 2) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N/2", fn, (long long)ldo);
+  } else if (epilogue == NVFP4_EPI_SCATTER_ADD_F32) {
+    if (ldo < N) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N", fn, (long long)ldo);
+    if (!row_weight || !scatter_index) return fail(NVFP4_EINVAL, "%s: scatter needs row_weight and scatter_index", fn);
+    if (out_rows < 0 || out_rows > 2147483647LL)
+      return fail(NVFP4_EINVAL, "%s: out_rows must be in [0, 2^31-1]", fn);
+    const size_t need = moe_mxfp4_w4a8_grouped_gemm_workspace_size(E, rows_total, N, K, epilogue, out_rows);
+    if (!ws || ws_bytes < need)
+      return fail(NVFP4_EWORKSPACE, "%s: scatter epilogue needs a %zu-byte workspace", fn, need);
+  } else {
+    return fail(NVFP4_EINVAL, "%s: unknown epilogue %d", fn, epilogue);
+  }
+  nvfp4::GemmArgs a = {};
+  a.a_codes = a_codes; a.a_scales = a_scales;
+  a.a_row_index = a_row_index; a.a_rows = a_rows;
+  a.group_offsets = group_offsets; a.E = E; a.rows_total = rows_total; a.K = K;
+  a.w_codes = w_codes; a.w_scales = w_scales; a.N = N;
+  a.epilogue = epilogue; a.row_weight = row_weight; a.scatter_index = scatter_index;
+  a.out_rows = out_rows; a.out = out; a.ldo = ldo;
+  a.out_amax = epilogue == NVFP4_EPI_SWIGLU_BF16 ? out_amax : nullptr;
+  a.block_m = 0;
+  a.y_rows = epilogue == NVFP4_EPI_SCATTER_ADD_F32 ? static_cast<float*>(ws) : nullptr;
+  return hip_status(nvfp4::launch_mx_w4a8_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ---------------------------------------------------------------------------
 size_t qdq_weights_workspace_size(int64_t nmat, int64_t N, int64_t K) {
   (void)N; (void)K;
   return nvfp4::qdq_workspace_bytes(nmat);

@@ -71,6 +71,9 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t M, int64_t K, in
                               hipStream_t stream);
 size_t mx_gemm_max_lds(int64_t K);
 hipError_t launch_mx_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_mx_w4a8_grouped_gemm(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_mx8_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 // combine.hip
 size_t combine_workspace_bytes(int64_t rows, int64_t N, int64_t out_rows);

@@ -17,6 +17,8 @@
 // 32 x 32 fp32 result sits in lane l, element q at row (q / 4) * 8 +
 // (l / 32) * 4 + q % 4, column l % 32 (the layout of the fp16 MFMA the shared
 // epilogues assume).
+#include <type_traits>
+
 #include "gemm_common.h"
 
 namespace nvfp4 {
@@ -197,20 +199,25 @@ __host__ __device__ constexpr int ws_stride(int kc) {
 // [max(BM, 64)], W scale words [BN].  Load instructions per wave and stage:
 // NAI A-code blocks of 16 rows, 4 W-code blocks, one A-scale and one W-scale
 // block of 64 rows.
-template <int BM>
+// A8: the activations are MXFP8 (one byte per element, 128 bytes a row per
+// stage, 8 rows per 1 KB load instruction) instead of MXFP4.
+template <int BM, bool A8 = false>
 struct Layout {
+  static constexpr int AROW = A8 ? 128 : 64;           // A bytes per row and stage
   static constexpr int A_OFF = 0;
-  static constexpr int B_OFF = BM * 64;
-  static constexpr int AS_OFF = (BM + BN) * 64;
+  static constexpr int B_OFF = BM * AROW;
+  static constexpr int AS_OFF = B_OFF + BN * 64;
   static constexpr int ASR = BM < 64 ? 64 : BM;
   static constexpr int BS_OFF = AS_OFF + ASR * 4;
   static constexpr int STAGE = BS_OFF + BN * 4;
-  static constexpr int NAI = BM < 64 ? 1 : BM / 64;
+  static constexpr int ABLK = BM * AROW / 1024;        // A-code load instructions per stage
+  static constexpr int NAI = ABLK < 4 ? 1 : ABLK / 4;  // ... per wave (padding ones included)
   static constexpr int LPW = NAI + 6;                  // load instructions per wave and stage
   // LDS ring: four slots (three stages in flight) for the tall tiles, whose
   // time per stage is set by how many bytes a CU keeps in flight; three for
-  // the short ones, so that two of them still share a CU
-  static constexpr int NSLOT = BM >= 128 ? 4 : 3;
+  // the short ones, so that two of them still share a CU, and for the
+  // 256-row MXFP8 tile, whose slots are larger
+  static constexpr int NSLOT = BM >= 128 && STAGE * 4 <= 144 * 1024 ? 4 : 3;
   static constexpr int PD = NSLOT - 1;                 // prefetch distance in stages
 };
 
@@ -241,6 +248,8 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ v8i as_v8i(const u32x4& w) {
   return v8i{(int)w[0], (int)w[1], (int)w[2], (int)w[3], 0, 0, 0, 0};
 }
+__device__ __forceinline__ v8i a_v8i(const u32x4& w) { return as_v8i(w); }
+__device__ __forceinline__ v8i a_v8i(const v8i& w) { return w; }
 
 // E4M3 bytes of the 8 E2M1 codes of w times the power of two f (exact when
 // the products stay at or above 2^-9, E4M3's smallest subnormal).
@@ -261,12 +270,13 @@ __device__ __forceinline__ float pow2_nonpos(int d) {
   return d >= -126 ? __uint_as_float((uint32_t)(127 + d) << 23) : 0.0f;
 }
 
-template <int MI, int NJ, int WM, int WN, int EPI, bool COMP>
+template <int MI, int NJ, int WM, int WN, int EPI, bool COMP, bool A8>
 __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int ntiles) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
   static_assert(WM * WN == 4, "four waves");
-  using L = Layout<BM>;
+  static_assert(!(A8 && COMP), "the MXFP8-activation GEMM has no compensation");
+  using L = Layout<BM, A8>;
   constexpr int STAGE = L::STAGE, NAI = L::NAI, LPW = L::LPW, NSLOT = L::NSLOT, PD = L::PD;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // LDS: NSLOT slots | dummy | W_S [BN][wss] bytes | Xmax bytes [BN] |
@@ -324,11 +334,19 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   const uint8_t* wc_e = p.w_codes + (int64_t)e * p.N * rbytes;
   const uint8_t* ws_e = p.w_scales + (int64_t)e * p.N * sbytes;
   const int lr = lane >> 2, lp = lane & 3;
+  // MXFP8 rows: 8 chunks of 16 bytes a stage, chunk c at position c ^ (r & 7)
+  const int64_t arbytes = A8 ? K : rbytes;
   uint32_t a_off[NAI];
 #pragma unroll
   for (int i = 0; i < NAI; ++i) {
-    const int b = wave * NAI + i, r = b * 16 + lr;
-    a_off[i] = (uint32_t)(a_row(b < BM / 16 ? r : BM) * rbytes) + ((lp ^ swz(r)) << 4);
+    const int b = wave * NAI + i;
+    if constexpr (A8) {
+      const int r = b * 8 + (lane >> 3), q = lane & 7;
+      a_off[i] = (uint32_t)(a_row(b < L::ABLK ? r : BM) * arbytes) + ((q ^ (r & 7)) << 4);
+    } else {
+      const int r = b * 16 + lr;
+      a_off[i] = (uint32_t)(a_row(b < L::ABLK ? r : BM) * arbytes) + ((lp ^ swz(r)) << 4);
+    }
   }
   uint32_t b_off[4];
 #pragma unroll
@@ -350,12 +368,12 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   // the LPW load instructions of stage m into slot `slot`
   auto issue = [&](int m, int slot) {
     unsigned char* base = smem + slot * STAGE;
-    const uint8_t* ac = p.a_codes + (int64_t)m * 64;
+    const uint8_t* ac = p.a_codes + (int64_t)m * L::AROW;
     const uint8_t* wcm = wc_e + (int64_t)m * 64;
 #pragma unroll
     for (int i = 0; i < NAI; ++i) {
       const int b = wave * NAI + i;
-      load_lds16(ac + a_off[i], b < BM / 16 ? base + L::A_OFF + b * 1024 : DUMMY);
+      load_lds16(ac + a_off[i], b < L::ABLK ? base + L::A_OFF + b * 1024 : DUMMY);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) load_lds16(wcm + b_off[i], base + L::B_OFF + (wave * 4 + i) * 1024);
@@ -486,7 +504,9 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   // words shifted so that op_sel 0 / 2 picks the lane's block of step 0 / 1.
   // A0/B0 of stage m + 1 are read as soon as the step-0 MFMAs of stage m have
   // been issued, A1/B1 and the scale words after the step-1 ones.
-  u32x4 A0[MI], B0[NJ], A1[MI], B1[NJ];
+  using AFrag = typename std::conditional<A8, v8i, u32x4>::type;
+  AFrag A0[MI], A1[MI];
+  u32x4 B0[NJ], B1[NJ];
   uint32_t SA[MI], SB[NJ];
   // Per-lane LDS offsets: the swizzle of rows r = 32 i + l32 (+ a multiple of
   // 32) depends on l32 only, so the row blocks are immediate offsets.
@@ -497,10 +517,26 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
                               (uint32_t)(L::B_OFF + (wn * NJ * 32 + l32) * 64 + (((2 + half) ^ sw) << 4))};
   const uint32_t sa_off = (uint32_t)(L::AS_OFF + (wm * 32 + l32) * MI * 4);
   const uint32_t sb_off = (uint32_t)(L::BS_OFF + (wn * 32 + l32) * NJ * 4);
-  auto read_half = [&](int slot, int ks, u32x4* A, u32x4* B) {
+  // MXFP8 A: lane half h of K-step ks takes chunks 4 ks + h and 4 ks + 2 + h
+  // (the FP8 form of the MFMA holds K 16 h .. and 32 + 16 h .. of the step in
+  // a lane, checked on the GPU), each at position c ^ (r & 7); r & 7 = l32 & 7
+  const uint32_t fa8_off[2][2] = {
+      {(uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 128 + ((half ^ (l32 & 7)) << 4)),
+       (uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 128 + (((2 + half) ^ (l32 & 7)) << 4))},
+      {(uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 128 + (((4 + half) ^ (l32 & 7)) << 4)),
+       (uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 128 + (((6 + half) ^ (l32 & 7)) << 4))}};
+  auto read_half = [&](int slot, int ks, AFrag* A, u32x4* B) {
     const unsigned char* base = smem + slot * STAGE;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) A[i] = *reinterpret_cast<const u32x4*>(base + fa_off[ks] + i * 2048);
+    for (int i = 0; i < MI; ++i) {
+      if constexpr (A8) {
+        const u32x4 lo = *reinterpret_cast<const u32x4*>(base + fa8_off[ks][0] + i * 4096);
+        const u32x4 hi = *reinterpret_cast<const u32x4*>(base + fa8_off[ks][1] + i * 4096);
+        A[i] = v8i{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+      } else {
+        A[i] = *reinterpret_cast<const u32x4*>(base + fa_off[ks] + i * 2048);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) B[j] = *reinterpret_cast<const u32x4*>(base + fb_off[ks] + j * 2048);
   };
@@ -570,7 +606,7 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_v8i(A0[i]), as_v8i(B0[j]), acc[i][j], 4, 4, 0, (int)SA[i], 0, (int)SB[j]);
+            a_v8i(A0[i]), as_v8i(B0[j]), acc[i][j], A8 ? 0 : 4, 4, 0, (int)SA[i], 0, (int)SB[j]);
     __builtin_amdgcn_sched_barrier(0);
     // this wave's loads of stage m + 1 have landed (only those of stages
     // m + 2 .. m + PD - 1 may be outstanding); after the barrier every wave's
@@ -586,7 +622,7 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
 #pragma unroll
       for (int i = 0; i < MI; ++i)
         acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-            as_v8i(A1[i]), as_v8i(B1[j]), acc[i][j], 4, 4, 2, (int)SA[i], 2, (int)SB[j]);
+            a_v8i(A1[i]), as_v8i(B1[j]), acc[i][j], A8 ? 0 : 4, 4, 2, (int)SA[i], 2, (int)SB[j]);
     __builtin_amdgcn_sched_barrier(0);
     read_half(nslot, 1, A1, B1);
     read_scales(nslot);
@@ -669,33 +705,34 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
                                  reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>(), RW);
 }
 
-template <int MI, int NJ, int WM, int WN>
+template <int MI, int NJ, int WM, int WN, bool A8 = false>
 __host__ constexpr size_t loop_lds_bytes(int64_t K, int kc) {
-  return Layout<WM * MI * 32>::NSLOT * (size_t)Layout<WM * MI * 32>::STAGE + DUMMY_BYTES + (size_t)BN * ws_stride(kc) +
-         BN + (size_t)MAX_KC * 4 + (size_t)(K / KS) * 8;
+  using L = Layout<WM * MI * 32, A8>;
+  return L::NSLOT * (size_t)L::STAGE + DUMMY_BYTES + (size_t)BN * ws_stride(kc) + BN +
+         (size_t)MAX_KC * 4 + (size_t)(K / KS) * 8;
 }
 
 // LDS bytes a tile configuration needs (0 if over the 160 KB of a CU).
-template <int MI, int NJ, int WM, int WN>
+template <int MI, int NJ, int WM, int WN, bool A8 = false>
 static size_t cfg_lds(const GemmArgs& a) {
-  const size_t loop = (loop_lds_bytes<MI, NJ, WM, WN>(a.K, a.sel_idx ? a.kc : 0) + 15) / 16 * 16;
+  const size_t loop = (loop_lds_bytes<MI, NJ, WM, WN, A8>(a.K, a.sel_idx ? a.kc : 0) + 15) / 16 * 16;
   const size_t epi = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
   const size_t lds = (loop > epi ? loop : epi) + (size_t)WM * MI * 32 * 4 + 256;   // + row weights, static
   return lds <= 160 * 1024 ? lds : 0;
 }
 
-template <int MI, int NJ, int WM, int WN, int EPI, bool COMP>
+template <int MI, int NJ, int WM, int WN, int EPI, bool COMP, bool A8>
 static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   constexpr int BM = WM * MI * 32;
   const int64_t mtiles = (a.rows_total + BM - 1) / BM + a.E;
   const int64_t ntiles = a.epilogue == 1 ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const int64_t total = mtiles * ntiles;
-  const size_t loop = (loop_lds_bytes<MI, NJ, WM, WN>(a.K, a.sel_idx ? a.kc : 0) + 15) / 16 * 16;
+  const size_t loop = (loop_lds_bytes<MI, NJ, WM, WN, A8>(a.K, a.sel_idx ? a.kc : 0) + 15) / 16 * 16;
   const size_t epi = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
   const size_t body = loop > epi ? loop : epi;
   a.rw_lds_offset = (int)body;
   const size_t lds = body + (EPI == 2 ? (size_t)BM * 4 : 0);
-  auto kern = mx_grouped_gemm_kernel<MI, NJ, WM, WN, EPI, COMP>;
+  auto kern = mx_grouped_gemm_kernel<MI, NJ, WM, WN, EPI, COMP, A8>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -704,14 +741,45 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MI, int NJ, int WM, int WN>
+template <int MI, int NJ, int WM, int WN, bool A8>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
-  const bool c = a.sel_idx != nullptr;
-  switch (a.epilogue) {
-    case 0: return c ? launch_cfg<MI, NJ, WM, WN, 0, true>(a, stream) : launch_cfg<MI, NJ, WM, WN, 0, false>(a, stream);
-    case 1: return c ? launch_cfg<MI, NJ, WM, WN, 1, true>(a, stream) : launch_cfg<MI, NJ, WM, WN, 1, false>(a, stream);
-    default: return c ? launch_cfg<MI, NJ, WM, WN, 2, true>(a, stream) : launch_cfg<MI, NJ, WM, WN, 2, false>(a, stream);
+  if constexpr (A8) {                          // no compensation with MXFP8 activations
+    switch (a.epilogue) {
+      case 0: return launch_cfg<MI, NJ, WM, WN, 0, false, true>(a, stream);
+      case 1: return launch_cfg<MI, NJ, WM, WN, 1, false, true>(a, stream);
+      default: return launch_cfg<MI, NJ, WM, WN, 2, false, true>(a, stream);
+    }
+  } else {
+    const bool c = a.sel_idx != nullptr;
+    switch (a.epilogue) {
+      case 0: return c ? launch_cfg<MI, NJ, WM, WN, 0, true, false>(a, stream) : launch_cfg<MI, NJ, WM, WN, 0, false, false>(a, stream);
+      case 1: return c ? launch_cfg<MI, NJ, WM, WN, 1, true, false>(a, stream) : launch_cfg<MI, NJ, WM, WN, 1, false, false>(a, stream);
+      default: return c ? launch_cfg<MI, NJ, WM, WN, 2, true, false>(a, stream) : launch_cfg<MI, NJ, WM, WN, 2, false, false>(a, stream);
+    }
   }
+}
+
+template <bool A8>
+static hipError_t launch_any(const GemmArgs& a, hipStream_t stream) {
+  if (a.epilogue == 1 && a.out_amax) {
+    hipError_t err = launch_fill_f32(a.out_amax, 1, 0.0f, stream);
+    if (err != hipSuccess) return err;
+  }
+  if (a.rows_total == 0) return hipSuccess;
+  hipError_t err;
+  int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
+  // a long K (a long gather table) can push the tallest tile past the LDS
+  if (bm == 256 && cfg_lds<4, 4, 2, 2, A8>(a) == 0) bm = 128;
+  if (bm == 128 && cfg_lds<2, 4, 2, 2, A8>(a) == 0) bm = 64;
+  switch (bm) {
+    case 256: err = launch_epi<4, 4, 2, 2, A8>(a, stream); break;
+    case 128: err = launch_epi<2, 4, 2, 2, A8>(a, stream); break;
+    case 64: err = launch_epi<1, 4, 2, 2, A8>(a, stream); break;
+    default: err = launch_epi<1, 2, 1, 4, A8>(a, stream); break;
+  }
+  if (err != hipSuccess || a.epilogue != 2) return err;
+  return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
+                        static_cast<float*>(a.out), a.ldo, a.y_rows, stream);
 }
 
 }  // namespace mxg
@@ -721,25 +789,72 @@ size_t mx_gemm_max_lds(int64_t K) {
 }
 
 hipError_t launch_mx_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
-  if (a.epilogue == 1 && a.out_amax) {
-    hipError_t err = launch_fill_f32(a.out_amax, 1, 0.0f, stream);
-    if (err != hipSuccess) return err;
+  return mxg::launch_any<false>(a, stream);
+}
+
+hipError_t launch_mx_w4a8_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
+  return mxg::launch_any<true>(a, stream);
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 quantizer (activations of the W4A8 GEMM)
+// ---------------------------------------------------------------------------
+// Scale byte X + 127 with X = floor(log2 amax) - 8 (8 is the exponent of
+// E4M3's largest value 448), clamped: from the fp32 exponent field E of amax
+// it is max(E - 8, 0).  Elements: |x| 2^-X is exact (a power-of-two multiply;
+// results small enough to underflow lie far below E4M3's smallest subnormal),
+// clamped to 448 (MX saturates), then the hardware convert rounds to nearest
+// even; the sign stays with the value.
+__device__ __forceinline__ uint32_t mx8_scale_byte(float amax) {
+  const int E = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  return (uint32_t)(E > 8 ? E - 8 : 0);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void mx8_quantize_kernel(const T* __restrict__ x, int64_t M,
+                                                           int64_t K, int64_t ldx,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+  const int64_t nb = K / kMxBlock;
+  const int64_t total = M * nb;
+  for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t r = t / nb, bc = t % nb;
+    float v[32];
+    mx_load32<T>(x + r * ldx + bc * kMxBlock, v);
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+    const uint32_t sb = mx8_scale_byte(amax);
+    const float inv = __uint_as_float((254u - sb) << 23);   // 2^-X, a normal fp32
+    uint32_t w[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      float f[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) f[u] = fminf(fmaxf(v[4 * q + u] * inv, -448.0f), 448.0f);
+      int lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[0], f[1], 0, false);
+      lo = __builtin_amdgcn_cvt_pk_fp8_f32(f[2], f[3], lo, true);
+      w[q] = (uint32_t)lo;
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(codes + r * K + bc * kMxBlock);
+    dst[0] = u32x4{w[0], w[1], w[2], w[3]};
+    dst[1] = u32x4{w[4], w[5], w[6], w[7]};
+    scales[r * nb + bc] = (uint8_t)sb;
   }
-  if (a.rows_total == 0) return hipSuccess;
-  hipError_t err;
-  int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
-  // a long K (a long gather table) can push the tallest tile past the LDS
-  if (bm == 256 && mxg::cfg_lds<4, 4, 2, 2>(a) == 0) bm = 128;
-  if (bm == 128 && mxg::cfg_lds<2, 4, 2, 2>(a) == 0) bm = 64;
-  switch (bm) {
-    case 256: err = mxg::launch_epi<4, 4, 2, 2>(a, stream); break;
-    case 128: err = mxg::launch_epi<2, 4, 2, 2>(a, stream); break;
-    case 64: err = mxg::launch_epi<1, 4, 2, 2>(a, stream); break;
-    default: err = mxg::launch_epi<1, 2, 1, 4>(a, stream); break;
-  }
-  if (err != hipSuccess || a.epilogue != 2) return err;
-  return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
-                        static_cast<float*>(a.out), a.ldo, a.y_rows, stream);
+}
+
+hipError_t launch_mx8_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                               uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (M == 0) return hipSuccess;
+  const int64_t total = M * (K / kMxBlock);
+  const int64_t blocks = (total + 255) / 256;
+  const unsigned grid = (unsigned)(blocks < 8192 ? blocks : 8192);
+  if (dtype == 0)
+    mx8_quantize_kernel<__bf16><<<grid, 256, 0, stream>>>(static_cast<const __bf16*>(x), M, K, ldx, codes, scales);
+  else
+    mx8_quantize_kernel<float><<<grid, 256, 0, stream>>>(static_cast<const float*>(x), M, K, ldx, codes, scales);
+  return hipGetLastError();
 }
 
 }  // namespace nvfp4

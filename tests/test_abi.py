@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 18      # 10 operations, 6 workspace queries, version, last error
+    assert len(declared) == 21      # 12 operations, 7 workspace queries, version, last error
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(P.exported_symbols()) == declared
@@ -153,3 +153,16 @@ def test_mxfp4_validation(lib):
     args[9] = ctypes.c_void_p(0x1002)
     assert lib.moe_mxfp4_grouped_gemm(*args) == -1
     assert "4-byte aligned" in err(lib)
+
+
+def test_w4a8_validation(lib):
+    assert lib.mxfp8_quantize(FAKE, 0, 4, 48, 48, FAKE, FAKE, None) == -1
+    assert "multiple of 32" in err(lib)
+    args = [FAKE, FAKE, None, 8, FAKE, 1, 8, 192, FAKE, FAKE, 256, 0, None, None, 0, FAKE, 256,
+            None, None, 0, None]
+    assert lib.moe_mxfp4_w4a8_grouped_gemm(*args) == -1
+    assert "multiple of 128" in err(lib)
+    args[7] = 256
+    args[11] = 2                    # scatter without row weights
+    assert lib.moe_mxfp4_w4a8_grouped_gemm(*args) == -1
+    assert "scatter" in err(lib)

@@ -316,3 +316,105 @@ def test_mx_moe_layer(gpu_lib, comp):
         out = _gemm_ref(hc_r[a:b], hs_r[a:b], dc_n[e], ds_n[e], *c2)
         np.add.at(y_ref, rt["slot_token"][a:b], out * rt["slot_weight"][a:b, None].astype(np.float64))
     assert rel_err(np32(y), y_ref) <= GEMM_TOL
+
+
+# ---------------------------------------------------------------------------
+# W4A8: MXFP8 activations x MXFP4 weights
+# ---------------------------------------------------------------------------
+
+def test_mx8_quantize_exhaustive_bf16(gpu_lib):
+    """Every finite bf16 value in mixed-magnitude blocks, and again in blocks
+    whose scale is fixed at X = 0, 5 and -20 (amax 448 * 2^X), so that every
+    value is rounded (ties and saturation included) at those scales."""
+    P = gpu_lib
+    bits = np.arange(65536, dtype=np.uint16)
+    vals = F.bf16_bits_to_f32(bits)
+    vals = vals[np.isfinite(vals)]
+    rng = np.random.default_rng(2)
+    mixed = np.concatenate([vals, np.zeros((-vals.size) % 128, np.float32)])
+    x_np = mixed[rng.permutation(mixed.size)].reshape(-1, 128)
+    codes, scales = P.mxfp8_quantize(torch.from_numpy(x_np).to(torch.bfloat16).cuda())
+    c_ref, s_ref = MX.quantize_fp8(x_np)
+    assert np.array_equal(npu8(scales), s_ref)
+    assert np.array_equal(npu8(codes), c_ref)
+    for X in (0, 5, -20):
+        v = vals[np.abs(vals.astype(np.float64)) <= 480.0 * 2.0 ** X]
+        n = (v.size + 30) // 31 * 31
+        blocks = np.zeros((n // 31, 32), np.float32)
+        blocks[:, 0] = np.float32(448.0 * 2.0 ** X)
+        blocks[:, 1:] = np.pad(v, (0, n - v.size)).reshape(-1, 31)
+        blocks = np.concatenate([blocks, np.zeros(((-blocks.shape[0]) % 4, 32), np.float32)])
+        xb = blocks.reshape(-1, 128)
+        codes, scales = P.mxfp8_quantize(torch.from_numpy(xb).to(torch.bfloat16).cuda())
+        c_ref, s_ref = MX.quantize_fp8(xb)
+        assert np.array_equal(npu8(scales), s_ref), f"X={X}"
+        assert np.array_equal(npu8(codes), c_ref), f"X={X}"
+
+
+@pytest.mark.parametrize("m,k", [(300, 4096), (7, 96)])
+def test_mx8_quantize_random_f32(gpu_lib, m, k):
+    P = gpu_lib
+    x = synth.activations(m, k, seed=6, heavy_frac=0.01).float()
+    x = x + torch.randn(x.shape, generator=torch.Generator().manual_seed(3)) * 1e-3
+    codes, scales = P.mxfp8_quantize(x.cuda())
+    c_ref, s_ref = MX.quantize_fp8(x.numpy())
+    assert np.array_equal(npu8(scales), s_ref)
+    assert np.array_equal(npu8(codes), c_ref)
+
+
+@pytest.mark.parametrize("tokens,n_exp,top_k,zipf", [
+    (600, 2, 2, 0.0),     # 256-row tiles
+    (300, 4, 2, 0.5),     # 128-row tiles
+    (200, 8, 2, 1.0),     # 64-row tiles
+    (64, 16, 4, 0.0),     # 32-row tiles
+])
+def test_w4a8_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
+    """Every tile shape of the W4A8 GEMM against the float64 product of the
+    same quantized operands: F32 and SwiGLU epilogues, K = 384, N = 2 x 160."""
+    P = gpu_lib
+    hidden, inter = 384, 160
+    x, rt, offs, wgu, _ = _route_setup(tokens, hidden, n_exp, inter, 22, zipf, top_k)
+    rows = int(offs[-1])
+    offs_t = torch.from_numpy(offs).cuda()
+    slot_tok = torch.from_numpy(rt["slot_token"]).cuda()
+    ac, asc = P.mxfp8_quantize(x.cuda())
+    gc, gs = _mx_weights(P, wgu)
+    gu = P.moe_mxfp4_w4a8_grouped_gemm(ac, asc, offs_t, rows, gc, gs, a_row_index=slot_tok)
+    h = P.moe_mxfp4_w4a8_grouped_gemm(ac, asc, offs_t, rows, gc, gs, a_row_index=slot_tok,
+                                      epilogue=P.EPI_SWIGLU_BF16)
+    ac_n, as_n, gc_n, gs_n = npu8(ac), npu8(asc), npu8(gc), npu8(gs)
+    ref = np.zeros((rows, 2 * inter))
+    for e in range(n_exp):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a < b:
+            tok = rt["slot_token"][a:b]
+            ref[a:b] = MX.gemm_w4a8(ac_n[tok], as_n[tok], gc_n[e], gs_n[e])
+            assert rel_err(np32(gu)[a:b], ref[a:b]) <= GEMM_TOL, f"expert {e}"
+    g_, u_ = ref[:, :inter], ref[:, inter:]
+    h_r = F.bf16_bits_to_f32(F.f64_to_bf16_bits(g_ / (1 + np.exp(-g_)) * u_))
+    tol = np.abs(h_r) * 2.0 ** -7 + GEMM_TOL * np.abs(h_r).max()
+    assert np.all(np.abs(np32(h) - h_r) <= tol)
+
+
+def test_w4a8_down_scatter(gpu_lib):
+    """Down projection with the scatter-add epilogue (K = 256)."""
+    P = gpu_lib
+    tokens, hidden, n_exp, inter = 160, 256, 8, 256
+    _, rt, offs, _, wd = _route_setup(tokens, hidden, n_exp, inter, 24, 1.0, 4)
+    rows = int(offs[-1])
+    hrows = torch.from_numpy(np.random.default_rng(4).standard_normal((rows, inter)).astype(np.float32))
+    hc, hs = P.mxfp8_quantize(hrows.to(torch.bfloat16).cuda())
+    dc, ds = _mx_weights(P, wd)
+    y = torch.zeros(tokens, hidden, dtype=torch.float32, device="cuda")
+    P.moe_mxfp4_w4a8_grouped_gemm(hc, hs, torch.from_numpy(offs).cuda(), rows, dc, ds,
+                                  epilogue=P.EPI_SCATTER_ADD_F32,
+                                  row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
+                                  scatter_index=torch.from_numpy(rt["slot_token"]).cuda(), out=y)
+    y_ref = np.zeros((tokens, hidden))
+    hc_n, hs_n, dc_n, ds_n = npu8(hc), npu8(hs), npu8(dc), npu8(ds)
+    for e in range(n_exp):
+        a, b = int(offs[e]), int(offs[e + 1])
+        if a < b:
+            out = MX.gemm_w4a8(hc_n[a:b], hs_n[a:b], dc_n[e], ds_n[e])
+            np.add.at(y_ref, rt["slot_token"][a:b], out * rt["slot_weight"][a:b, None].astype(np.float64))
+    assert rel_err(np32(y), y_ref) <= GEMM_TOL
