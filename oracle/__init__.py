@@ -24,9 +24,11 @@ fixed, documented order.  Reference GEMM results are accumulated in float64.
 Modules:
   formats  -- E2M1 (FP4) and E4M3 codebooks and exact nearest rounding.
   nvfp4    -- global/block scales, quantize, dequantize, residual, channel
-              scores, top-k selection, residual requantization, weight QDQ,
-              rollout-guided rounding.
-  gemm     -- compensated W4A4 GEMM and the MoE FFN layer stages.
+              scores, top-k selection, residual requantization (compact, and
+              the dense binary-mask form), weight QDQ, rollout-guided
+              rounding.
+  gemm     -- compensated W4A4 GEMM (compact and dense-mask correction) and
+              the MoE FFN layer stages.
   mxfp4    -- the MXFP4 variant (32-element blocks, E8M0 power-of-two
               scales): quantize, dequantize, residual selection and
               requantization, compensated GEMM.

@@ -40,6 +40,17 @@ def gemm_comp(a_codes, a_scales, a_g, w_codes, w_scales, w_g,
     return y
 
 
+
+def gemm_masked_comp(a_codes, a_scales, a_g, w_codes, w_scales, w_g, m_codes, m_scales, m_g):
+    """Y = DQ(A) DQ(W)^T + DQ(Q(R * M)) DQ(W)^T in float64: the dense-mask
+    compensation of QUADS section 2.2B as a second GEMM of the same shape over
+    the masked, requantized residual (m_* [M, K] from
+    nvfp4.resq_mask_select_and_requant, global scale m_g)."""
+    w = dequantize(w_codes, w_scales, w_g).astype(np.float64)
+    a = dequantize(a_codes, a_scales, a_g).astype(np.float64)
+    m = dequantize(m_codes, m_scales, m_g).astype(np.float64)
+    return a @ w.T + m @ w.T
+
 def silu(z):
     """z / (1 + exp(-z)) in float64 (SwiGLU gate activation)."""
     z = np.asarray(z, dtype=np.float64)

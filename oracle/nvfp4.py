@@ -244,6 +244,50 @@ def resq_select_and_requant(x, codes, scales, g, unit_offsets, k, row_index=None
     return sel, r_codes, r_scales, r_global
 
 
+def resq_mask_select_and_requant(x, codes, scales, g, unit_offsets, k, row_index=None):
+    """Dense-mask form of the residual compensation (QUADS section 2.2B: a
+    binary channel mask keeps the top k% of channels by residual magnitude,
+    50% in the pages' example, and those channels are quantized a second
+    time).
+
+    Reading: the mask M_u of unit u is 1 on the k channels that
+    resq_select_and_requant selects (same scores, same tie rule) and 0
+    elsewhere; the correction is Q(R * M_u), an ordinary NVFP4 tensor of the
+    full width K (blocks of 16 consecutive input channels, zeros outside the
+    mask), with one global scale per unit from the largest |R * M_u| of the
+    unit's rows.  Its GEMM term is Q(R * M) Q(W)^T over all K channels, the
+    masked channels contributing nothing.
+
+    Returns (sel_idx [U, k] int32, m_codes [rows, K/2], m_scales [rows, K/16],
+    m_global [U] float32); a unit without rows gets sel_idx = 0..k-1,
+    m_global = 1 and no rows.
+    """
+    x = np.asarray(x, dtype=np.float32)
+    unit_offsets = np.asarray(unit_offsets, dtype=np.int64)
+    n_units = unit_offsets.size - 1
+    rows_total = int(unit_offsets[-1])
+    kdim = x.shape[1]
+    if row_index is None:
+        row_index = np.arange(rows_total)
+    row_index = np.asarray(row_index, dtype=np.int64)
+    r_full = residual(x, codes, scales, g)
+    sel = np.zeros((n_units, k), dtype=np.int32)
+    m_codes = np.zeros((rows_total, kdim // 2), dtype=np.uint8)
+    m_scales = np.zeros((rows_total, kdim // BLOCK), dtype=np.uint8)
+    m_global = np.ones(n_units, dtype=np.float32)
+    for u in range(n_units):
+        a, b = int(unit_offsets[u]), int(unit_offsets[u + 1])
+        if b == a:
+            sel[u] = np.arange(k, dtype=np.int32)
+            continue
+        r_unit = r_full[row_index[a:b]]
+        sel[u] = topk_channels(channel_scores(np.abs(r_unit)), k)
+        masked = np.zeros_like(r_unit)
+        masked[:, sel[u]] = r_unit[:, sel[u]]
+        m_codes[a:b], m_scales[a:b], m_global[u] = quantize(masked)
+    return sel, m_codes, m_scales, m_global
+
+
 # ---------------------------------------------------------------------------
 # trainer side
 # ---------------------------------------------------------------------------
