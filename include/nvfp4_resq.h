@@ -152,6 +152,31 @@ int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K,
                             float* r_global, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * resq_mask_select_and_requant -- the dense binary-mask form of the same
+ * compensation ([QUADS] sec. 2.2B: a binary channel mask keeps the top k% of
+ * channels by residual magnitude, 50% in the pages' example, and those
+ * channels are quantized a second time).
+ *
+ * Arguments, selection (scores, top-k, ties, empty units) and workspace
+ * (resq_select_and_requant_workspace_size with the same K, rows_total, U, k)
+ * are those of resq_select_and_requant.  The output differs: per unit,
+ *   R * M  = R on the channels of sel_idx[u], 0 on the others (full width K),
+ *   quantized to NVFP4 with its own global scale m_global[u] (the largest
+ *   |R * M| of the unit's rows), blocks of 16 along K
+ *   -> m_codes [rows_total, K/2] (16-byte aligned), m_scales [rows_total, K/16].
+ * Blocks with no selected channel get codes 0 and scale 0.  The GEMM term is
+ * moe_w4a4_masked_comp_gemm below.  K <= 16384.
+ * Errors: as resq_select_and_requant.
+ * ------------------------------------------------------------------------ */
+int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+                                 const int32_t* row_index, const uint8_t* codes,
+                                 const uint8_t* scales, const float* g,
+                                 const int64_t* unit_offsets, int64_t U, int64_t rows_total,
+                                 int32_t k, const float* tile_partials, int32_t* sel_idx,
+                                 uint8_t* m_codes, uint8_t* m_scales, float* m_global, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * moe_w4a4_grouped_gemm -- routed grouped expert GEMM over NVFP4 weights and
  * NVFP4 activations, with the compensation term fused in ([QUADS] sec. 1:
  * native W4A4 GEMM; sec. 2.2B: the residual correction of the selected
@@ -199,6 +224,29 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int epilogue, const float* row_weight, const int32_t* scatter_index,
                           int64_t out_rows, void* out, int64_t ldo, float* out_amax,
                           void* ws, size_t ws_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * moe_w4a4_masked_comp_gemm -- the dense-mask compensation's GEMM term, a
+ * second grouped GEMM of the main one's shape ([QUADS] sec. 2.2B: the
+ * correction of the masked residual is added back into the result).
+ *
+ * For every unit row r of group e (group_offsets as in moe_w4a4_grouped_gemm;
+ * no row index: row r of m_codes) and output n < N:
+ *   out[r * ldo + n] += sum_k DQM[r, k] * DQW[e, n, k]
+ * where DQM dequantizes m_codes / m_scales with m_global[e] (one global scale
+ * per group, as resq_mask_select_and_requant writes them).  Run it after
+ * moe_w4a4_grouped_gemm (EPI_F32) wrote the main product into out on the same
+ * stream: out then holds Q(X) Q(W)^T + Q(R * M) Q(W)^T.
+ *   m_codes/m_scales   [rows_total, K/2] / [rows_total, K/16]; m_global fp32 [E]
+ *   w_*                as moe_w4a4_grouped_gemm; K multiple of 64
+ *   out                fp32 [rows_total, ldo], read and written; ldo >= N
+ * Errors: EINVAL (shapes, pointers, alignment), EUNSUPPORTED (K > 65536).
+ * ------------------------------------------------------------------------ */
+int moe_w4a4_masked_comp_gemm(const uint8_t* m_codes, const uint8_t* m_scales,
+                              const float* m_global, const int64_t* group_offsets, int32_t E,
+                              int64_t rows_total, int64_t K, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const float* w_global, int64_t N,
+                              float* out, int64_t ldo, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * qdq_weights -- trainer-side weight quantize-dequantize of the asymmetric

@@ -39,6 +39,10 @@ _SIGNATURES = {
     "resq_select_and_requant_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "resq_select_and_requant": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64,
                                        _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "resq_mask_select_and_requant": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P,
+                                            _I64, _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "moe_w4a4_masked_comp_gemm": (_INT, [_P, _P, _P, _P, _I32, _I64, _I64, _P, _P, _P, _I64, _P,
+                                         _I64, _P]),
     "moe_w4a4_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _INT, _I64]),
     "moe_w4a4_grouped_gemm": (_INT, [_P, _P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _P,
                                      _I64, _P, _P, _P, _P, _I32, _INT, _P, _P, _I64, _P, _I64,
@@ -166,6 +170,53 @@ def resq_select_and_requant(x, codes, scales, g, k, unit_offsets=None, rows_tota
         _ptr(sel), _ptr(rc), _ptr(rs), _ptr(rg), _ptr(ws), ws.numel(), _stream()),
         "resq_select_and_requant")
     return sel, rc, rs, rg
+
+
+def resq_mask_select_and_requant(x, codes, scales, g, k, unit_offsets=None, rows_total=None,
+                                 row_index=None, tile_partials=None):
+    """Dense-mask form: the top-k residual channels of each unit (as
+    resq_select_and_requant) kept at their own positions, the rest zero, and
+    that full-width residual requantized.  Returns (sel_idx int32 [U, k],
+    m_codes [rows, K/2], m_scales [rows, K/16], m_global fp32 [U])."""
+    lib = load()
+    _require_cuda(x, codes, scales, g, unit_offsets, row_index, tile_partials)
+    x_rows, kk = x.shape
+    dev = x.device
+    if tile_partials is not None:
+        n_units = (x_rows + 127) // 128
+        rows_total = x_rows
+    else:
+        n_units = unit_offsets.numel() - 1
+        if rows_total is None:
+            raise ValueError("rows_total (host int) is required with unit_offsets")
+    sel = torch.empty(n_units, k, dtype=torch.int32, device=dev)
+    mc = torch.empty(rows_total, kk // 2, dtype=torch.uint8, device=dev)
+    ms = torch.empty(rows_total, kk // 16, dtype=torch.uint8, device=dev)
+    mg = torch.empty(n_units, dtype=torch.float32, device=dev)
+    ws = _workspace(lib.resq_select_and_requant_workspace_size(kk, rows_total, n_units, k), dev)
+    _check(lib.resq_mask_select_and_requant(
+        _ptr(x), _dtype_code(x), x_rows, kk, x.stride(0), _ptr(row_index), _ptr(codes),
+        _ptr(scales), _ptr(g), _ptr(unit_offsets), n_units, rows_total, k, _ptr(tile_partials),
+        _ptr(sel), _ptr(mc), _ptr(ms), _ptr(mg), _ptr(ws), ws.numel(), _stream()),
+        "resq_mask_select_and_requant")
+    return sel, mc, ms, mg
+
+
+def moe_w4a4_masked_comp_gemm(m_codes, m_scales, m_global, group_offsets, rows_total,
+                              w_codes, w_scales, w_global, out):
+    """out [rows_total, N] fp32 += Q(R * M) Q(W)^T per group (the dense-mask
+    compensation term); out already holds the main product.  Returns out."""
+    lib = load()
+    _require_cuda(m_codes, m_scales, m_global, group_offsets, w_codes, w_scales, w_global, out)
+    n_exp, n, k_half = w_codes.shape
+    if out.dtype != torch.float32 or out.dim() != 2 or out.shape[0] < rows_total \
+            or out.shape[1] < n or out.stride(1) != 1:
+        raise ValueError("out must be fp32 [rows_total, >= N] with unit column stride")
+    _check(lib.moe_w4a4_masked_comp_gemm(
+        _ptr(m_codes), _ptr(m_scales), _ptr(m_global), _ptr(group_offsets), n_exp, rows_total,
+        k_half * 2, _ptr(w_codes), _ptr(w_scales), _ptr(w_global), n, _ptr(out), out.stride(0),
+        _stream()), "moe_w4a4_masked_comp_gemm")
+    return out
 
 
 def moe_w4a4_grouped_gemm(a_codes, a_scales, a_global, group_offsets, rows_total,

@@ -99,13 +99,17 @@ size_t resq_select_and_requant_workspace_size(int64_t K, int64_t rows_total, int
          align256((size_t)rows_total * k * 4) + align256((size_t)gslots * 4);
 }
 
-int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
-                            const int32_t* row_index, const uint8_t* codes, const uint8_t* scales,
-                            const float* g, const int64_t* unit_offsets, int64_t U,
-                            int64_t rows_total, int32_t k, const float* tile_partials,
-                            int32_t* sel_idx, uint8_t* r_codes, uint8_t* r_scales,
-                            float* r_global, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "resq_select_and_requant";
+}  // extern "C"
+
+namespace {
+// The compact (masked = false) and dense-mask residual steps share validation,
+// workspace and the selection; they differ in the requantized output.
+int resq_entry(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+               const int32_t* row_index, const uint8_t* codes, const uint8_t* scales,
+               const float* g, const int64_t* unit_offsets, int64_t U, int64_t rows_total,
+               int32_t k, const float* tile_partials, int32_t* sel_idx, uint8_t* r_codes,
+               uint8_t* r_scales, float* r_global, void* ws, size_t ws_bytes, void* stream,
+               bool masked, const char* fn) {
   if (int s = check_act(x, dtype, x_rows, K, ldx, fn)) return s;
   if (K > 16384) return fail(NVFP4_EUNSUPPORTED, "%s: K=%lld > 16384", fn, (long long)K);
   if (k < 16 || k % 16 != 0 || k > K)
@@ -144,8 +148,34 @@ int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K,
   return hip_status(nvfp4::launch_resq(x, dtype, x_rows, K, ldx, row_index, codes, scales, g,
                                        unit_offsets, U, rows_total, k, tile_partials, sel_idx,
                                        r_codes, r_scales, r_global, rw,
-                                       static_cast<hipStream_t>(stream)),
+                                       static_cast<hipStream_t>(stream), false, masked),
                     fn);
+}
+}  // namespace
+
+extern "C" {
+
+int resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+                            const int32_t* row_index, const uint8_t* codes, const uint8_t* scales,
+                            const float* g, const int64_t* unit_offsets, int64_t U,
+                            int64_t rows_total, int32_t k, const float* tile_partials,
+                            int32_t* sel_idx, uint8_t* r_codes, uint8_t* r_scales,
+                            float* r_global, void* ws, size_t ws_bytes, void* stream) {
+  return resq_entry(x, dtype, x_rows, K, ldx, row_index, codes, scales, g, unit_offsets, U,
+                    rows_total, k, tile_partials, sel_idx, r_codes, r_scales, r_global, ws,
+                    ws_bytes, stream, false, "resq_select_and_requant");
+}
+
+int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
+                                 const int32_t* row_index, const uint8_t* codes,
+                                 const uint8_t* scales, const float* g,
+                                 const int64_t* unit_offsets, int64_t U, int64_t rows_total,
+                                 int32_t k, const float* tile_partials, int32_t* sel_idx,
+                                 uint8_t* m_codes, uint8_t* m_scales, float* m_global, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  return resq_entry(x, dtype, x_rows, K, ldx, row_index, codes, scales, g, unit_offsets, U,
+                    rows_total, k, tile_partials, sel_idx, m_codes, m_scales, m_global, ws,
+                    ws_bytes, stream, true, "resq_mask_select_and_requant");
 }
 
 // ---------------------------------------------------------------------------
@@ -213,6 +243,40 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
   a.out_amax = epilogue == NVFP4_EPI_SWIGLU_BF16 ? out_amax : nullptr;
   a.block_m = 0;
   a.y_rows = epilogue == NVFP4_EPI_SCATTER_ADD_F32 ? static_cast<float*>(ws) : nullptr;
+  return hip_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
+}
+
+int moe_w4a4_masked_comp_gemm(const uint8_t* m_codes, const uint8_t* m_scales,
+                              const float* m_global, const int64_t* group_offsets, int32_t E,
+                              int64_t rows_total, int64_t K, const uint8_t* w_codes,
+                              const uint8_t* w_scales, const float* w_global, int64_t N,
+                              float* out, int64_t ldo, void* stream) {
+  const char* fn = "moe_w4a4_masked_comp_gemm";
+  if (E <= 0 || K <= 0 || N <= 0 || rows_total < 0)
+    return fail(NVFP4_EINVAL, "%s: E=%d K=%lld N=%lld rows_total=%lld", fn, E, (long long)K,
+                (long long)N, (long long)rows_total);
+  if (K % 64 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 64", fn, (long long)K);
+  if (K > 65536) return fail(NVFP4_EUNSUPPORTED, "%s: K=%lld > 65536", fn, (long long)K);
+  if (rows_total > 2147483647LL) return fail(NVFP4_EUNSUPPORTED, "%s: rows_total above 2^31-1", fn);
+  if (!group_offsets || !w_codes || !w_scales || !w_global || !m_global || !out)
+    return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if (rows_total > 0 && (!m_codes || !m_scales)) return fail(NVFP4_EINVAL, "%s: m_codes/m_scales NULL", fn);
+  if (!aligned16(w_codes) || (m_codes && !aligned16(m_codes)))
+    return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
+  if (ldo < N) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N", fn, (long long)ldo);
+  if (rows_total == 0) return ok();
+  nvfp4::GemmArgs a;
+  a.a_codes = m_codes; a.a_scales = m_scales; a.a_global = m_global;
+  a.a_global_per_group = 1;
+  a.a_row_index = nullptr; a.a_rows = rows_total;
+  a.group_offsets = group_offsets; a.E = E; a.rows_total = rows_total; a.K = K;
+  a.w_codes = w_codes; a.w_scales = w_scales; a.w_global = w_global; a.N = N;
+  a.sel_idx = nullptr; a.r_codes = nullptr; a.r_scales = nullptr; a.r_global = nullptr;
+  a.kc = 0;
+  a.epilogue = NVFP4_EPI_F32; a.row_weight = nullptr; a.scatter_index = nullptr;
+  a.out_rows = 0; a.out = out; a.ldo = ldo; a.out_amax = nullptr;
+  a.block_m = 0; a.y_rows = nullptr;
+  a.accumulate = 1;
   return hip_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }
 

@@ -680,9 +680,10 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   }
 
   // ---- compensation chunk ---------------------------------------------------
-  float scale = *p.a_global * p.w_global[e];
+  const float ga = p.a_global[p.a_global_per_group ? e : 0];
+  float scale = ga * p.w_global[e];
   if (comp) {
-    const float ga = *p.a_global, gr = p.r_global[e];
+    const float gr = p.r_global[e];
     const float ratio = ga / gr;
 #pragma unroll
     for (int i = 0; i < MI; ++i)

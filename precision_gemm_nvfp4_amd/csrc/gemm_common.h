@@ -165,11 +165,16 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&
           const float w = scatter ? rw_lds[r] : 1.0f;      // row_weight[s2], staged in LDS
           float* dst = out + s2 * ld + n0 + c4;
           if (vec && n0 + c4 + 4 <= p.N) {
-            *reinterpret_cast<f32x4*>(dst) = f32x4{v[0] * w, v[1] * w, v[2] * w, v[3] * w};
+            f32x4 o = f32x4{v[0] * w, v[1] * w, v[2] * w, v[3] * w};
+            if (!scatter && p.accumulate) {
+              const f32x4 old = *reinterpret_cast<const f32x4*>(dst);
+              o = f32x4{old[0] + o[0], old[1] + o[1], old[2] + o[2], old[3] + o[3]};
+            }
+            *reinterpret_cast<f32x4*>(dst) = o;
           } else {
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-              if (n0 + c4 + u < p.N) dst[u] = v[u] * w;
+              if (n0 + c4 + u < p.N) dst[u] = !scatter && p.accumulate ? dst[u] + v[u] * w : v[u] * w;
           }
         }
       }

@@ -29,7 +29,7 @@ hipError_t launch_resq(const void* x, int dtype, int64_t x_rows, int64_t K, int6
                        const float* g, const int64_t* unit_offsets, int64_t U, int64_t rows_total,
                        int32_t k, const float* tile_partials, int32_t* sel_idx, uint8_t* r_codes,
                        uint8_t* r_scales, float* r_global, const ResqWorkspace& ws,
-                       hipStream_t stream, bool mx = false);
+                       hipStream_t stream, bool mx = false, bool masked = false);
 
 // gemm.hip
 struct GemmArgs {
@@ -61,6 +61,8 @@ struct GemmArgs {
   float* y_rows;         // scatter epilogue: row_weight * Y rows [rows_total, N] (workspace)
   int block_m;           // rows per tile: 256, 128, 64, 32, or 0 to pick from the average group size
   int rw_lds_offset;     // set by the launcher: LDS byte offset of the scatter epilogue's row weights
+  int a_global_per_group = 0;  // a_global holds one scale per group (else one for all)
+  int accumulate = 0;          // F32 epilogue: out += Y instead of out = Y
 };
 int grouped_gemm_block_m(int64_t rows_total, int32_t E);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);

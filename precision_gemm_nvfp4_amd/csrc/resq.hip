@@ -562,6 +562,61 @@ __global__ __launch_bounds__(256) void resq_requant_kernel(
   }
 }
 
+// Dense-mask form: Q(R * M), the residual of the selected channels at their
+// own positions and zeros elsewhere, quantized along K with the unit's own
+// global scale.  R * M has the same nonzero entries as R_S, so the slots'
+// amax of |R_S| give its global scale.  pos[c] is the compact index of
+// channel c, or -1 outside the mask (K <= kMaskMaxK).
+constexpr int kMaskMaxK = 16384;
+__global__ __launch_bounds__(256) void resq_mask_requant_kernel(
+    const float* __restrict__ r_s, Units units, const int32_t* __restrict__ slot_start,
+    const float* __restrict__ amax_part, const int32_t* __restrict__ sel_idx, int32_t k, int64_t K,
+    uint8_t* __restrict__ m_codes, uint8_t* __restrict__ m_scales, float* __restrict__ m_global) {
+  __shared__ int16_t pos[kMaskMaxK];
+  __shared__ float sh_g;
+  const int64_t slot = blockIdx.x;
+  const int64_t u = unit_of_slot(slot_start, units.U, slot);
+  if (u < 0) return;
+  int64_t b, e;
+  units.range(u, b, e);
+  for (int64_t c = threadIdx.x; c < K; c += blockDim.x) pos[c] = -1;
+  __syncthreads();
+  for (int j = threadIdx.x; j < k; j += blockDim.x) {
+    int32_t c = sel_idx[u * k + j];
+    c = c < 0 ? 0 : (c >= K ? (int32_t)(K - 1) : c);
+    pos[c] = (int16_t)j;
+  }
+  if (threadIdx.x < 64) {
+    float m = 0.0f;
+    for (int64_t t = slot_start[u] + threadIdx.x; t < slot_start[u + 1]; t += 64)
+      m = fmaxf(m, amax_part[t]);
+    m = wave_max(m);
+    if (threadIdx.x == 0) sh_g = global_scale_from_amax(m);
+  }
+  __syncthreads();
+  const float g = sh_g;
+  const BlockScaler bsc = make_block_scaler(g);
+  if (slot == slot_start[u] && threadIdx.x == 0) m_global[u] = g;
+  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
+  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
+  const int64_t kb = K / kBlock;
+  const int64_t n = (r1 - r0) * kb;
+  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
+    const int64_t r = r0 + i / kb;
+    const int64_t bl = i % kb;
+    float v[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int j = pos[bl * kBlock + q];
+      v[q] = j >= 0 ? r_s[r * k + j] : 0.0f;
+    }
+    uint32_t sb, w0, w1;
+    quantize_block16(v, bsc, &sb, &w0, &w1);
+    *reinterpret_cast<u32x2*>(m_codes + r * (K / 2) + bl * 8) = u32x2{w0, w1};
+    m_scales[r * kb + bl] = (uint8_t)sb;
+  }
+}
+
 // MXFP4 of R_S: 32-blocks along the compact axis, each with its own E8M0
 // scale; no global scale.
 __global__ __launch_bounds__(256) void resq_requant_mx_kernel(
@@ -603,7 +658,7 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
                                 const int64_t* unit_offsets, int64_t U, int64_t rows_total,
                                 int32_t k, const float* tile_partials, int32_t* sel_idx,
                                 uint8_t* r_codes, uint8_t* r_scales, float* r_global,
-                                const ResqWorkspace& ws, hipStream_t stream) {
+                                const ResqWorkspace& ws, hipStream_t stream, bool masked) {
   Units units{tile_partials ? nullptr : unit_offsets, U, rows_total};
   const int64_t slots = tile_partials ? U : resq_max_slots(rows_total, U);
   const int64_t gslots = resq_max_gather_slots(rows_total, U);
@@ -644,6 +699,9 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
     if constexpr (MX)
       resq_requant_mx_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start, k,
                                                                    r_codes, r_scales);
+    else if (masked)
+      resq_mask_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(
+          ws.r_s, units, ws.slot_start, ws.amax_part, sel_idx, k, K, r_codes, r_scales, r_global);
     else
       resq_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start,
                                                                 ws.amax_part, k, r_codes, r_scales,
@@ -657,9 +715,10 @@ hipError_t launch_resq(const void* x, int dtype, int64_t x_rows, int64_t K, int6
                        const float* g, const int64_t* unit_offsets, int64_t U, int64_t rows_total,
                        int32_t k, const float* tile_partials, int32_t* sel_idx, uint8_t* r_codes,
                        uint8_t* r_scales, float* r_global, const ResqWorkspace& ws,
-                       hipStream_t stream, bool mx) {
+                       hipStream_t stream, bool mx, bool masked) {
+  if (masked && (mx || K > kMaskMaxK)) return hipErrorInvalidValue;
 #define RESQ_ARGS x_rows, K, ldx, row_index, codes, scales, g, unit_offsets, U, rows_total, k, \
-                  tile_partials, sel_idx, r_codes, r_scales, r_global, ws, stream
+                  tile_partials, sel_idx, r_codes, r_scales, r_global, ws, stream, masked
   const __bf16* xb = static_cast<const __bf16*>(x);
   const float* xf = static_cast<const float*>(x);
   if (mx) return dtype == 0 ? launch_resq_t<__bf16, true>(xb, RESQ_ARGS) : launch_resq_t<float, true>(xf, RESQ_ARGS);

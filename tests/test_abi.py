@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 21      # 12 operations, 7 workspace queries, version, last error
+    assert len(declared) == 23      # 14 operations, 7 workspace queries, version, last error
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(P.exported_symbols()) == declared
@@ -166,3 +166,26 @@ def test_w4a8_validation(lib):
     args[11] = 2                    # scatter without row weights
     assert lib.moe_mxfp4_w4a8_grouped_gemm(*args) == -1
     assert "scatter" in err(lib)
+
+
+def test_masked_validation(lib):
+    # the dense-mask residual step shares the compact one's checks
+    args = [FAKE, 0, 8, 64, 64, None, FAKE, FAKE, FAKE, FAKE, 1, 8, 24, None, FAKE, FAKE, FAKE,
+            FAKE, FAKE, 1 << 20, None]
+    assert lib.resq_mask_select_and_requant(*args) == -1
+    assert "multiple of 16" in err(lib)
+    args[3], args[4] = 32768, 32768
+    args[12] = 32
+    assert lib.resq_mask_select_and_requant(*args) == -2
+    assert "16384" in err(lib)
+    g = [FAKE, FAKE, FAKE, FAKE, 1, 8, 96, FAKE, FAKE, FAKE, 64, FAKE, 64, None]
+    assert lib.moe_w4a4_masked_comp_gemm(*g) == -1
+    assert "multiple of 64" in err(lib)
+    g[6] = 128
+    g[12] = 32                      # ldo < N
+    assert lib.moe_w4a4_masked_comp_gemm(*g) == -1
+    assert "ldo" in err(lib)
+    g[12] = 64
+    g[2] = None
+    assert lib.moe_w4a4_masked_comp_gemm(*g) == -1
+    assert "NULL" in err(lib)
