@@ -31,7 +31,8 @@ Modules:
               the MoE FFN layer stages.
   mxfp4    -- the MXFP4 variant (32-element blocks, E8M0 power-of-two
               scales): quantize, dequantize, residual selection and
-              requantization, compensated GEMM.
+              requantization, compensated GEMM, weight QDQ and guided
+              rounding; MXFP8 activations and the W4A8 GEMM.
 
 Every function states which passage of the pages it follows.  Functions with
 no independent pin say "parity unpinned" (none at present).

@@ -35,8 +35,9 @@ to the selected channels, each element keeping its own block scale.
 
 import numpy as np
 
-from .formats import E2M1_LEVELS, E4M3_VALUES, e2m1_decode, e2m1_index_nearest, e4m3_code_nearest
-from .nvfp4 import channel_scores, pack_nibbles, topk_channels, unpack_nibbles
+from .formats import (E2M1_LEVELS, E4M3_VALUES, bf16_bits_to_f32, e2m1_decode, e2m1_index_nearest,
+                      e4m3_code_nearest, f32_to_bf16_bits)
+from .nvfp4 import channel_scores, guided_round_under, pack_nibbles, topk_channels, unpack_nibbles
 
 BLOCK = 32
 #: Exponent of the largest E2M1 level: 6 = 1.5 * 2^2.
@@ -168,6 +169,40 @@ def quantize_weights(w):
 
 
 # ---------------------------------------------------------------------------
+# trainer side in MXFP4 (QUADS section 2.2A weight QDQ; TRACE core method and
+# method step four, guided rounding), with the MXFP4 scale rule above
+# ---------------------------------------------------------------------------
+
+def qdq_weights(w):
+    """MXFP4 fake quantization of weights w [nmat, N, K] (fp32 values, bf16
+    inputs): the trainer's forward sees the rollout's MXFP4 weights as BF16.
+    Blocks of 32 along K; there is no global scale, so the matrices are
+    independent.  DQ = value * 2^X is exact in fp32 and, having at most two
+    significant bits, also in bf16, so w_qdq is DQ itself.
+
+    Returns (w_qdq bf16 bits [nmat, N, K] uint16, codes [nmat, N, K/2],
+    scales [nmat, N, K/32])."""
+    w = np.asarray(w, dtype=np.float32)
+    nmat, n, k = w.shape
+    codes, scales = quantize(w.reshape(nmat * n, k))
+    dq = dequantize(codes, scales)
+    bits = f32_to_bf16_bits(dq)
+    assert np.array_equal(bf16_bits_to_f32(bits), dq), "MXFP4 DQ not exact in bf16"
+    return (bits.reshape(nmat, n, k), codes.reshape(nmat, n, k // 2),
+            scales.reshape(nmat, n, k // BLOCK))
+
+
+def guided_round(x_train, roll_codes, roll_scales):
+    """Rollout-guided rounding against MXFP4 rollout codes: the rule of the
+    NVFP4 oracle's guided_round (candidates q- <= x/S <= q+, the one closer
+    to the rollout level, zero keeps x's sign bit) with S = 2^X of the
+    element's 32-block.  Returns (guided codes [M, K/2], x_fq bf16 bits
+    [M, K], dist_hist int64[3])."""
+    S_all = np.repeat(e8m0_decode(roll_scales), BLOCK, axis=1).astype(np.float64)
+    return guided_round_under(x_train, unpack_nibbles(roll_codes), S_all)
+
+
+# ---------------------------------------------------------------------------
 # W4A8: MXFP8 activations (the TRACE summary's MXFP4 W4A8 rollout, Table 4)
 # ---------------------------------------------------------------------------
 #: Exponent of the largest E4M3 value: 448 = 1.75 * 2^8.
@@ -217,6 +252,6 @@ def gemm_w4a8(a_codes, a_scales, w_codes, w_scales):
     return dequantize_fp8(a_codes, a_scales) @ dequantize(w_codes, w_scales).astype(np.float64).T
 
 
-__all__ = ["shared_exponents_fp8", "quantize_fp8", "dequantize_fp8", "gemm_w4a8",
+__all__ = ["qdq_weights", "guided_round", "shared_exponents_fp8", "quantize_fp8", "dequantize_fp8", "gemm_w4a8",
            "BLOCK", "E2M1_LEVELS", "e8m0_decode", "shared_exponents", "quantize", "dequantize",
            "residual", "resq_select_and_requant", "gemm_comp", "quantize_weights"]

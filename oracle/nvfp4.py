@@ -345,13 +345,21 @@ def guided_round(x_train, roll_codes, roll_scales, roll_g):
     value times S, RNE32 then bf16 (the value of code 0x8 is -0, as in DQ), dist_hist int64[3] = counts of |signed index of RTN(v)
     - signed index of q_roll| equal to 0, 1 and >= 2).
     """
+    S_all = np.repeat(effective_scales(roll_scales, roll_g), BLOCK, axis=1).astype(np.float64)
+    return guided_round_under(x_train, unpack_nibbles(roll_codes), S_all)
+
+
+def guided_round_under(x_train, roll_nib, S_all):
+    """The guided rule of guided_round with the rollout scale of every
+    element given directly (S_all float64 [M, K], each an fp32 value):
+    candidates q- <= x/S <= q+ among the signed E2M1 levels, the one closer to
+    the rollout level, codes, x_fq = bf16(RNE32(value * S)) and the histogram.
+    Shared by the NVFP4 and MXFP4 forms, which differ only in S."""
     x = np.asarray(x_train, dtype=np.float32)
     m, k = x.shape
     nib = np.empty((m, k), dtype=np.uint8)
     x_fq = np.empty((m, k), dtype=np.uint16)
     hist = np.zeros(3, dtype=np.int64)
-    roll_nib = unpack_nibbles(roll_codes)
-    S_all = np.repeat(effective_scales(roll_scales, roll_g), BLOCK, axis=1).astype(np.float64)
     for r0 in range(0, m, 64):                  # row chunks bound the memory
         r1 = min(r0 + 64, m)
         xs = x[r0:r1]

@@ -302,3 +302,75 @@ def test_w4a8_gemm_brute_force():
                 v = Fraction(float(F.E4M3_VALUES[b & 0x7F])) * (-1 if b & 0x80 else 1)
                 ref += v * Fraction(2) ** (int(asc[i, j // 32]) - 127) * W[n][j]
             assert abs(float(ref) - y[i, n]) <= 1e-12 * max(1.0, abs(float(ref)))
+
+
+# ---------------------------------------------------------------------------
+# trainer side: weight QDQ and guided rounding in MXFP4
+# ---------------------------------------------------------------------------
+
+def test_qdq_weights_brute_force_and_idempotent():
+    """bf16(DQ) of each 32-block equals the brute-force block (exact
+    rationals), and QDQ is a projection: applied to its own output it
+    changes nothing (a wrong exponent or rounding would move values)."""
+    rng = np.random.default_rng(41)
+    w = (rng.standard_normal((2, 3, 64)) * np.exp(rng.standard_normal((2, 3, 1)) * 3)).astype(np.float32)
+    w[1, 2, 32:] = 0.0
+    w = F.bf16_bits_to_f32(F.f32_to_bf16_bits(w))
+    out, codes, scales = MX.qdq_weights(w)
+    vals = F.bf16_bits_to_f32(out)
+    for i in range(2):
+        for r in range(3):
+            for b in range(2):
+                blk = w[i, r, 32 * b:32 * b + 32]
+                sb, cs = brute_mx_block(blk)
+                X = sb - 127
+                assert scales[i, r, b] == sb
+                for j, c in enumerate(cs):
+                    ref = float(E2M1_PAGE[c & 7] * Fraction(2) ** X) * (-1.0 if c & 8 else 1.0)
+                    assert vals[i, r, 32 * b + j] == ref
+    out2, _, _ = MX.qdq_weights(vals)
+    assert np.array_equal(out2, out)
+
+
+def _guided_brute_mx(xt, roll_nib, X):
+    """Exact guided rounding of one element under S = 2^X (rationals)."""
+    levels = sorted(set([-v for v in E2M1_PAGE] + E2M1_PAGE))
+    v = Fraction(float(xt)) / Fraction(2) ** X
+    lo = max([l for l in levels if l <= v], default=levels[0])
+    hi = min([l for l in levels if l >= v], default=levels[-1])
+    qr = E2M1_PAGE[roll_nib & 7] * (-1 if roll_nib & 8 else 1)
+    q = hi if abs(hi - qr) < abs(lo - qr) else lo
+    neg = q < 0 or (q == 0 and np.signbit(np.float32(xt)))
+    return (8 if neg else 0) | E2M1_PAGE.index(abs(q))
+
+
+def test_guided_round_brute_force_and_invariants():
+    """Brute force on sampled elements; TRACE Eq. (3) (never farther from the
+    rollout level than round-to-nearest) everywhere; rollout codes that are
+    the trainer's own round-to-nearest codes leave them unchanged."""
+    rng = np.random.default_rng(42)
+    xr = (rng.standard_normal((48, 64)) * 3).astype(np.float32)
+    xr[:, 5] *= 40
+    rc, rs = MX.quantize(xr)
+    X = rs.astype(np.int64) - 127
+    lv = np.concatenate([-F.E2M1_LEVELS[:0:-1], F.E2M1_LEVELS])
+    for rel in (1e-3, 2e-2, 0.2):
+        xt = (xr + rng.standard_normal(xr.shape).astype(np.float32) * rel * np.abs(xr)).astype(np.float32)
+        gc, fq, hist = MX.guided_round(xt, rc, rs)
+        gn, rn = Q.unpack_nibbles(gc), Q.unpack_nibbles(rc)
+        S = np.repeat(np.ldexp(1.0, X), 32, axis=1)
+        rtn = F.e2m1_index_nearest(np.abs(xt).astype(np.float64), S)
+        rtn_s = np.where(np.signbit(xt), -rtn, rtn)
+        g_s, r_s = Q.signed_index(gn), Q.signed_index(rn)
+        assert np.all(np.abs(lv[g_s + 7] - lv[r_s + 7]) <= np.abs(lv[rtn_s + 7] - lv[r_s + 7]))
+        assert np.all(np.abs(g_s - rtn_s) <= 1)
+        assert hist.sum() == xt.size
+        for (i, j) in zip(rng.integers(0, 48, 300), rng.integers(0, 64, 300)):
+            assert gn[i, j] == _guided_brute_mx(xt[i, j], rn[i, j], int(X[i, j // 32]))
+        # x_fq is the guided level times 2^X, exact
+        vals = F.e2m1_decode(gn) * S
+        assert np.array_equal(F.bf16_bits_to_f32(fq).astype(np.float64), vals)
+    # guidance by the trainer's own codes is round-to-nearest
+    tc, ts = MX.quantize(xr)
+    gc, _, hist = MX.guided_round(xr, tc, ts)
+    assert np.array_equal(gc, tc) and hist.tolist() == [xr.size, 0, 0]
