@@ -373,6 +373,34 @@ int mxfp4_resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int6
                                   size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * mxfp4_qdq_weights -- trainer-side weight quantize-dequantize in MXFP4 (the
+ * asymmetric W4A16 QAT of [QUADS] sec. 2.2A with the rollout's MXFP4 weights;
+ * [TRACE] Table 4 trains MXFP4 rollouts).  Blocks of 32 along K, one E8M0
+ * scale each, no global scale; w_qdq = bf16(value * 2^X), which is exact.
+ *   w        bf16 [nmat, N, K];  w_qdq out bf16 [nmat, N, K] (not w itself)
+ *   codes    NULL or out [nmat, N, K/2];  scales NULL or out [nmat, N, K/32]
+ *   K multiple of 32; w, w_qdq, codes 16-byte aligned
+ * Errors: EINVAL (shape, null or aliased or misaligned pointers).
+ * ------------------------------------------------------------------------ */
+int mxfp4_qdq_weights(const void* w, int64_t nmat, int64_t N, int64_t K, void* w_qdq,
+                      uint8_t* codes, uint8_t* scales, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * mxfp4_guided_round -- rollout-guided rounding against MXFP4 rollout codes
+ * ([TRACE] core method and method step four, with the MXFP4 rollout of its
+ * Table 4): as guided_round, with S = 2^X of the element's rollout 32-block
+ * and no global scale.
+ *   x_train       bf16/fp32 [M, ldx];  K multiple of 32
+ *   roll_codes    [M, K/2];  roll_scales [M, K/32]
+ *   guided_codes  out [M, K/2];  x_fq NULL or out bf16 [M, K] = bf16(value * S)
+ *   dist_hist     NULL or out int64 [3], as guided_round
+ * Errors: EINVAL (shapes, null pointers), EUNSUPPORTED (M*K/16 >= 2^31).
+ * ------------------------------------------------------------------------ */
+int mxfp4_guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                       const uint8_t* roll_codes, const uint8_t* roll_scales,
+                       uint8_t* guided_codes, void* x_fq, int64_t* dist_hist, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * moe_mxfp4_grouped_gemm -- the routed grouped expert GEMM over MXFP4
  * activations and weights with the residual compensation term ([QUADS]
  * sec. 1: native W4A4 GEMM on the rollout; sec. 2.2B: the second FP4

@@ -60,6 +60,8 @@ _SIGNATURES = {
     "moe_mxfp4_grouped_gemm": (_INT, [_P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _I64,
                                       _P, _P, _P, _I32, _INT, _P, _P, _I64, _P, _I64, _P, _P,
                                       _SZ, _P]),
+    "mxfp4_qdq_weights": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
+    "mxfp4_guided_round": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "mxfp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P]),
     "moe_mxfp4_w4a8_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _INT, _I64]),
     "moe_mxfp4_w4a8_grouped_gemm": (_INT, [_P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _I64,
@@ -287,6 +289,37 @@ def guided_round(x_train, roll_codes, roll_scales, roll_global, want_fq=True, wa
     _check(lib.guided_round(_ptr(x_train), _dtype_code(x_train), m, kk, x_train.stride(0),
                             _ptr(roll_codes), _ptr(roll_scales), _ptr(roll_global), _ptr(codes),
                             _ptr(fq), _ptr(hist), _stream()), "guided_round")
+    return codes, fq, hist
+
+
+def mxfp4_qdq_weights(w, want_codes=True):
+    """MXFP4 weight QDQ of w bf16 [nmat, N, K] (K % 32 == 0).  Returns (w_qdq
+    bf16, codes [nmat, N, K/2] or None, scales [nmat, N, K/32] or None)."""
+    lib = load()
+    _require_cuda(w)
+    nmat, n, kk = w.shape
+    dev = w.device
+    w_qdq = torch.empty_like(w)
+    codes = torch.empty(nmat, n, kk // 2, dtype=torch.uint8, device=dev) if want_codes else None
+    scales = torch.empty(nmat, n, kk // 32, dtype=torch.uint8, device=dev) if want_codes else None
+    _check(lib.mxfp4_qdq_weights(_ptr(w), nmat, n, kk, _ptr(w_qdq), _ptr(codes), _ptr(scales),
+                                 _stream()), "mxfp4_qdq_weights")
+    return w_qdq, codes, scales
+
+
+def mxfp4_guided_round(x_train, roll_codes, roll_scales, want_fq=True, want_hist=True):
+    """Rollout-guided rounding against MXFP4 rollout codes [M, K/2] and E8M0
+    scales [M, K/32].  Returns (codes, x_fq bf16 or None, dist_hist or None)."""
+    lib = load()
+    _require_cuda(x_train, roll_codes, roll_scales)
+    m, kk = x_train.shape
+    dev = x_train.device
+    codes = torch.empty(m, kk // 2, dtype=torch.uint8, device=dev)
+    fq = torch.empty(m, kk, dtype=torch.bfloat16, device=dev) if want_fq else None
+    hist = torch.empty(3, dtype=torch.int64, device=dev) if want_hist else None
+    _check(lib.mxfp4_guided_round(_ptr(x_train), _dtype_code(x_train), m, kk, x_train.stride(0),
+                                  _ptr(roll_codes), _ptr(roll_scales), _ptr(codes), _ptr(fq),
+                                  _ptr(hist), _stream()), "mxfp4_guided_round")
     return codes, fq, hist
 
 

@@ -519,6 +519,41 @@ int qdq_weights(const void* w, int64_t nmat, int64_t N, int64_t K, void* w_qdq, 
                     fn);
 }
 
+int mxfp4_qdq_weights(const void* w, int64_t nmat, int64_t N, int64_t K, void* w_qdq,
+                      uint8_t* codes, uint8_t* scales, void* stream) {
+  const char* fn = "mxfp4_qdq_weights";
+  if (nmat < 0 || N < 0 || K <= 0) return fail(NVFP4_EINVAL, "%s: bad shape", fn);
+  if (K % 32 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld not a multiple of 32", fn, (long long)K);
+  if (nmat == 0 || N == 0) return ok();
+  if (!w || !w_qdq) return fail(NVFP4_EINVAL, "%s: w / w_qdq NULL", fn);
+  if (w == w_qdq) return fail(NVFP4_EINVAL, "%s: in-place operation is not supported", fn);
+  if (!aligned16(w) || !aligned16(w_qdq) || (codes && !aligned16(codes)))
+    return fail(NVFP4_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_mx_qdq(static_cast<const __bf16*>(w), nmat * N, K,
+                                         static_cast<__bf16*>(w_qdq), codes, scales,
+                                         static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int mxfp4_guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                       const uint8_t* roll_codes, const uint8_t* roll_scales,
+                       uint8_t* guided_codes, void* x_fq, int64_t* dist_hist, void* stream) {
+  const char* fn = "mxfp4_guided_round";
+  if (int s = check_act(x_train, dtype, M, K, ldx, fn)) return s;
+  if (K % 32 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+  if (M * (K / 16) > 2147483647LL)
+    return fail(NVFP4_EUNSUPPORTED, "%s: more than 2^31-1 blocks", fn);
+  if (M > 0 && (!roll_codes || !roll_scales || !guided_codes))
+    return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if ((roll_codes && !aligned16(roll_codes)) || (guided_codes && !aligned16(guided_codes)) ||
+      (x_fq && !aligned16(x_fq)))
+    return fail(NVFP4_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_mx_guided(x_train, dtype, M, K, ldx, roll_codes, roll_scales,
+                                            guided_codes, static_cast<__bf16*>(x_fq), dist_hist,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 // ---------------------------------------------------------------------------
 int guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
                  const uint8_t* roll_codes, const uint8_t* roll_scales, const float* roll_global,

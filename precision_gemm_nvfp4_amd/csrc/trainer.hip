@@ -138,6 +138,57 @@ hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf1
   return hipGetLastError();
 }
 
+// MXFP4 weight QDQ: blocks of 32 along K with their own E8M0 scale and no
+// global scale, so one pass suffices.  bf16(DQ) is DQ itself: value * 2^X has
+// at most two significant bits.  grid-stride over the 32-blocks of all rows.
+__global__ __launch_bounds__(256) void mx_qdq_kernel(const __bf16* __restrict__ w, int64_t nblk,
+                                                     __bf16* __restrict__ w_qdq,
+                                                     uint8_t* __restrict__ codes,
+                                                     uint8_t* __restrict__ scales) {
+  for (int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; b < nblk;
+       b += (int64_t)gridDim.x * blockDim.x) {
+    const u32x4* src = reinterpret_cast<const u32x4*>(w + b * kMxBlock);
+    u32x4 q[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) q[i] = src[i];
+    float v[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      v[2 * i] = bf16_lo(q[i >> 2][i & 3]);
+      v[2 * i + 1] = bf16_hi(q[i >> 2][i & 3]);
+      amax = fmaxf(amax, fmaxf(fabsf(v[2 * i]), fabsf(v[2 * i + 1])));
+    }
+    const uint32_t sb = mx_scale_byte(amax);
+    uint32_t cw[4];
+    mx_pack32(v, sb, cw);
+    const float S = e8m0_value(sb);
+    u32x4 o[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      float d[8];
+      e2m1_unpack8(cw[c], d);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[c][i] = pack_bf16x2_rne(d[2 * i] * S, d[2 * i + 1] * S);
+    }
+    u32x4* dst = reinterpret_cast<u32x4*>(w_qdq + b * kMxBlock);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[i] = o[i];
+    if (codes) *reinterpret_cast<u32x4*>(codes + b * 16) = u32x4{cw[0], cw[1], cw[2], cw[3]};
+    if (scales) scales[b] = (uint8_t)sb;
+  }
+}
+
+hipError_t launch_mx_qdq(const __bf16* w, int64_t rows, int64_t K, __bf16* w_qdq, uint8_t* codes,
+                         uint8_t* scales, hipStream_t stream) {
+  const int64_t nblk = rows * (K / kMxBlock);
+  if (nblk == 0) return hipGetLastError();
+  int64_t grid = (nblk + 255) / 256;
+  if (grid > 8192) grid = 8192;
+  mx_qdq_kernel<<<(unsigned)grid, 256, 0, stream>>>(w, nblk, w_qdq, codes, scales);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // guided rounding
 // ---------------------------------------------------------------------------
@@ -153,14 +204,17 @@ __device__ __forceinline__ int signed_index(uint32_t c) {
 // bit of each element, element 8i + j in bit j of byte i); the output is the
 // neighbour whose magnitude index has that low bit (neighbouring levels differ
 // in it), and hist counts the elements kept at round-to-nearest and moved.
-template <typename T, bool RECORD>
+// MX = true: MXFP4 rollout scales, one E8M0 byte per 32 elements (16-element
+// chunk b of a row takes byte b / 2, K being a multiple of 32), S = 2^X and no
+// global scale (roll_global unused).
+template <typename T, bool RECORD, bool MX = false>
 __global__ __launch_bounds__(256) void guided_kernel(
     const T* __restrict__ x, uint32_t M, uint32_t K, int64_t ldx, const uint8_t* __restrict__ roll,
     const uint8_t* __restrict__ roll_scales, const float* __restrict__ roll_global,
     uint8_t* __restrict__ guided, __bf16* __restrict__ x_fq, unsigned long long* __restrict__ hist) {
   const uint32_t nb = K / kBlock;
   const uint32_t total = M * nb;                  // >= 1: the launcher skips empty inputs
-  const float g_roll = *roll_global;
+  const float g_roll = MX ? 1.0f : *roll_global;
   uint32_t h0 = 0, h1 = 0, h2 = 0;
   // The inputs of a thread's next block are loaded before the current one is
   // rounded (from a clamped index, unconditionally), so each trip of the
@@ -175,7 +229,7 @@ __global__ __launch_bounds__(256) void guided_kernel(
     const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)r * ldx + bc * kBlock);
 #pragma unroll
     for (int i = 0; i < (int)sizeof(T); ++i) in.q[i] = src[i];
-    in.sc = roll_scales[bb];
+    in.sc = roll_scales[MX ? bb >> 1 : bb];
     if constexpr (RECORD) in.roll = u32x2{*reinterpret_cast<const uint16_t*>(roll + (int64_t)bb * 2), 0u};
     else in.roll = *reinterpret_cast<const u32x2*>(roll + (int64_t)bb * 8);
   };
@@ -198,7 +252,7 @@ __global__ __launch_bounds__(256) void guided_kernel(
 #pragma unroll
       for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(cur.q[i >> 2][i & 3]);
     }
-    const float S = e4m3_value(cur.sc) * g_roll;
+    const float S = MX ? e8m0_value(cur.sc) : e4m3_value(cur.sc) * g_roll;
     // round-to-nearest codes under S (fast path, exact fallback)
     uint32_t w0, w1;
     if (S >= 0x1p-100f) {
@@ -303,7 +357,7 @@ __global__ void zero_i64_kernel(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
-template <bool RECORD>
+template <bool RECORD, bool MX = false>
 static hipError_t launch_guided_t(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                                   const uint8_t* roll, const uint8_t* roll_scales,
                                   const float* roll_global, uint8_t* guided, __bf16* x_fq,
@@ -315,11 +369,11 @@ static hipError_t launch_guided_t(const void* x, int dtype, int64_t M, int64_t K
   int64_t grid = (nb + 255) / 256;
   if (grid > 2048) grid = 2048;
   if (dtype == 0)
-    guided_kernel<__bf16, RECORD><<<(unsigned)grid, 256, 0, stream>>>(
+    guided_kernel<__bf16, RECORD, MX><<<(unsigned)grid, 256, 0, stream>>>(
         static_cast<const __bf16*>(x), (uint32_t)M, (uint32_t)K, ldx, roll, roll_scales,
         roll_global, guided, x_fq, h);
   else
-    guided_kernel<float, RECORD><<<(unsigned)grid, 256, 0, stream>>>(
+    guided_kernel<float, RECORD, MX><<<(unsigned)grid, 256, 0, stream>>>(
         static_cast<const float*>(x), (uint32_t)M, (uint32_t)K, ldx, roll, roll_scales,
         roll_global, guided, x_fq, h);
   return hipGetLastError();
@@ -331,6 +385,13 @@ hipError_t launch_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t
                          int64_t* hist, hipStream_t stream) {
   return launch_guided_t<false>(x, dtype, M, K, ldx, roll_codes, roll_scales, roll_global, guided,
                                 x_fq, hist, stream);
+}
+
+hipError_t launch_mx_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                            const uint8_t* roll_codes, const uint8_t* roll_scales, uint8_t* guided,
+                            __bf16* x_fq, int64_t* hist, hipStream_t stream) {
+  return launch_guided_t<false, true>(x, dtype, M, K, ldx, roll_codes, roll_scales, nullptr,
+                                      guided, x_fq, hist, stream);
 }
 
 hipError_t launch_guided_record(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,

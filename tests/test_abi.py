@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 23      # 14 operations, 7 workspace queries, version, last error
+    assert len(declared) == 25      # 16 operations, 7 workspace queries, version, last error
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(P.exported_symbols()) == declared
@@ -188,4 +188,15 @@ def test_masked_validation(lib):
     g[12] = 64
     g[2] = None
     assert lib.moe_w4a4_masked_comp_gemm(*g) == -1
+    assert "NULL" in err(lib)
+
+
+def test_mxfp4_trainer_validation(lib):
+    assert lib.mxfp4_qdq_weights(FAKE, 2, 8, 48, FAKE, None, None, None) == -1
+    assert "multiple of 32" in err(lib)
+    assert lib.mxfp4_qdq_weights(FAKE, 2, 8, 64, FAKE, None, None, None) == -1
+    assert "in-place" in err(lib)
+    assert lib.mxfp4_guided_round(FAKE, 0, 4, 48, 48, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert "multiple of 32" in err(lib)
+    assert lib.mxfp4_guided_round(FAKE, 0, 4, 64, 64, None, FAKE, FAKE, None, None, None) == -1
     assert "NULL" in err(lib)

@@ -418,3 +418,78 @@ def test_w4a8_down_scatter(gpu_lib):
             out = MX.gemm_w4a8(hc_n[a:b], hs_n[a:b], dc_n[e], ds_n[e])
             np.add.at(y_ref, rt["slot_token"][a:b], out * rt["slot_weight"][a:b, None].astype(np.float64))
     assert rel_err(np32(y), y_ref) <= GEMM_TOL
+
+
+# ---------------------------------------------------------------------------
+# trainer side: MXFP4 weight QDQ and guided rounding
+# ---------------------------------------------------------------------------
+
+def _bits(t):
+    return t.cpu().view(torch.int16).numpy().view(np.uint16)
+
+
+def test_mx_qdq_weights_magnitudes(gpu_lib):
+    """bf16(DQ), codes and scales bit-exact, with rows spanning 2^-133 (bf16
+    subnormals, the E8M0 floor) to 2^120, zero rows and zero blocks."""
+    P = gpu_lib
+    g = torch.Generator().manual_seed(51)
+    nmat, n, k = 3, 64, 512
+    w = torch.randn(nmat, n, k, generator=g)
+    expo = torch.randint(-133, 121, (nmat, n, 1), generator=g).float()
+    w = (w * torch.exp2(expo)).to(torch.bfloat16)
+    w[1, 5] = 0
+    w[2, 7, 64:96] = 0
+    out, codes, scales = P.mxfp4_qdq_weights(w.cuda())
+    out_r, codes_r, scales_r = MX.qdq_weights(w.float().numpy())
+    assert np.array_equal(npu8(scales), scales_r)
+    assert np.array_equal(npu8(codes), codes_r)
+    assert np.array_equal(_bits(out), out_r)
+    out2, c2, s2 = P.mxfp4_qdq_weights(w.cuda(), want_codes=False)
+    assert c2 is None and s2 is None and torch.equal(out2, out)
+
+
+def test_mx_qdq_weights_expert_shapes(gpu_lib):
+    """Expert-shaped matrices (gate/up 2 x 192 by 256, down 256 by 192)."""
+    P = gpu_lib
+    for n, k, tid in [(384, 256, synth.WGU_ID), (256, 192, synth.WD_ID)]:
+        w = synth.weights(4, n, k, seed=52, tensor_id=tid)
+        out, codes, scales = P.mxfp4_qdq_weights(w.cuda())
+        out_r, codes_r, scales_r = MX.qdq_weights(w.float().numpy())
+        assert np.array_equal(npu8(scales), scales_r)
+        assert np.array_equal(npu8(codes), codes_r)
+        assert np.array_equal(_bits(out), out_r)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rel", [1e-3, 2e-2, 0.2])
+def test_mx_guided_round(gpu_lib, dtype, rel):
+    """Guided codes, x_fq and the distance histogram bit-exact against the
+    oracle, rollout codes from the MXFP4 quantizer."""
+    P = gpu_lib
+    x_roll = synth.activations(257, 512, seed=53, heavy_frac=0.01)
+    x_train = synth.guided_noise(x_roll, seed=53, rel=rel).to(dtype)
+    rc, rs, _ = P.mxfp4_quantize(x_roll.cuda())
+    gc, fq, hist = P.mxfp4_guided_round(x_train.cuda(), rc, rs)
+    gc_r, fq_r, hist_r = MX.guided_round(x_train.float().numpy(), npu8(rc), npu8(rs))
+    assert np.array_equal(npu8(gc), gc_r)
+    assert np.array_equal(_bits(fq), fq_r)
+    assert np.array_equal(hist.cpu().numpy(), hist_r)
+
+
+def test_mx_guided_round_tiny_scales(gpu_lib):
+    """Rollout blocks whose 2^X is subnormal or near the E8M0 floor (the exact
+    rounding path) and a padded row stride."""
+    P = gpu_lib
+    g = torch.Generator().manual_seed(54)
+    x_roll = (torch.randn(64, 256, generator=g)
+              * torch.exp2(torch.randint(-140, -100, (64, 1), generator=g).float())).to(torch.bfloat16)
+    x_train = (x_roll.float() * (1 + 0.05 * torch.randn(64, 256, generator=g))).to(torch.bfloat16)
+    rc, rs, _ = P.mxfp4_quantize(x_roll.cuda())
+    pad = torch.zeros(64, 320, dtype=torch.bfloat16)
+    pad[:, :256] = x_train
+    xt = pad.cuda()[:, :256]
+    gc, fq, hist = P.mxfp4_guided_round(xt, rc, rs)
+    gc_r, fq_r, hist_r = MX.guided_round(x_train.float().numpy(), npu8(rc), npu8(rs))
+    assert np.array_equal(npu8(gc), gc_r)
+    assert np.array_equal(_bits(fq), fq_r)
+    assert np.array_equal(hist.cpu().numpy(), hist_r)
