@@ -160,8 +160,8 @@ def build_inputs(torch, P, synth, wl, dev):
     return inp, time.time() - t_gen
 
 
-def run_step_mx(P, inp, wl, tl):
-    """One pass of the MXFP4 rollout path (same steps as run_step)."""
+def run_step_mx(P, inp, wl, tl, trainer=True):
+    """One pass of the MXFP4 path (same steps as run_step)."""
     tl.mark("start")
     xq_c, xq_s, _ = P.mxfp4_quantize(inp["x"])
     tl.mark("quantize_x")
@@ -185,12 +185,19 @@ def run_step_mx(P, inp, wl, tl):
                              r_scales=rs2, row_weight=inp["slot_weight"],
                              scatter_index=inp["slot_token"], out=inp["y"])
     tl.mark("gemm_down")
-    return dict(xq=(xq_c, xq_s), sel1=(sel1, rc1, rs1), h=h, hq=(hq_c, hq_s), sel2=(sel2, rc2, rs2))
+    out = dict(xq=(xq_c, xq_s), sel1=(sel1, rc1, rs1), h=h, hq=(hq_c, hq_s), sel2=(sel2, rc2, rs2))
+    if trainer and inp["x_train"] is not None:
+        P.mxfp4_qdq_weights(inp["wgu"], want_codes=False)
+        P.mxfp4_qdq_weights(inp["wd"], want_codes=False)
+        tl.mark("qdq")
+        out["guided"] = P.mxfp4_guided_round(inp["x_train"], xq_c, xq_s, want_fq=True)
+        tl.mark("guided")
+    return out
 
 
 def run_step(P, inp, wl, tl, trainer=True):
     if wl.fmt == "mxfp4":
-        return run_step_mx(P, inp, wl, tl)
+        return run_step_mx(P, inp, wl, tl, trainer)
     tl.mark("start")
     xq_c, xq_s, xq_g, _ = P.nvfp4_quantize(inp["x"])
     tl.mark("quantize_x")
