@@ -64,7 +64,7 @@ def gemm_kernel_name(rows, experts, epilogue, fmt="nvfp4"):
     cfg = "4, 4, 2, 2" if avg >= 160 else "2, 4, 2, 2" if avg >= 64 else \
           "1, 4, 2, 2" if avg >= 24 else "1, 2, 1, 4"
     if fmt == "mxfp4":     # compensated (the bench always compensates)
-        return f"nvfp4::mxg::mx_grouped_gemm_kernel<{cfg}, {epilogue}, true>"
+        return f"nvfp4::mxg::mx_grouped_gemm_kernel<{cfg}, {epilogue}, true, false>"
     return f"nvfp4::grouped_gemm_kernel<{cfg}, {epilogue}>"
 
 
