@@ -51,6 +51,7 @@ def gemm_masked_comp(a_codes, a_scales, a_g, w_codes, w_scales, w_g, m_codes, m_
     m = dequantize(m_codes, m_scales, m_g).astype(np.float64)
     return a @ w.T + m @ w.T
 
+
 def silu(z):
     """z / (1 + exp(-z)) in float64 (SwiGLU gate activation)."""
     z = np.asarray(z, dtype=np.float64)
