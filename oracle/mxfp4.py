@@ -37,7 +37,8 @@ import numpy as np
 
 from .formats import (E2M1_LEVELS, E4M3_VALUES, bf16_bits_to_f32, e2m1_decode, e2m1_index_nearest,
                       e4m3_code_nearest, f32_to_bf16_bits)
-from .nvfp4 import channel_scores, guided_round_under, pack_nibbles, topk_channels, unpack_nibbles
+from .nvfp4 import (channel_scores, guided_round_record_under, guided_round_under, pack_nibbles,
+                    topk_channels, unpack_nibbles)
 
 BLOCK = 32
 #: Exponent of the largest E2M1 level: 6 = 1.5 * 2^2.
@@ -202,6 +203,17 @@ def guided_round(x_train, roll_codes, roll_scales):
     return guided_round_under(x_train, unpack_nibbles(roll_codes), S_all)
 
 
+def guided_round_record(x_train, record, roll_scales):
+    """Guided rounding from the mantissa-only record of MXFP4 rollout codes
+    (TRACE method steps two and four): the record is the low code bit per
+    element (nvfp4.guidance_record, the same for both formats), with the E8M0
+    scales of the rollout beside it (1 + 8/32 = 1.25 bits per element); the
+    rule of the NVFP4 oracle's guided_round_record with S = 2^X.  Returns
+    (guided codes [M, K/2], x_fq bf16 bits [M, K], moved int64[2])."""
+    S_all = np.repeat(e8m0_decode(roll_scales), BLOCK, axis=1).astype(np.float64)
+    return guided_round_record_under(x_train, record, S_all)
+
+
 # ---------------------------------------------------------------------------
 # W4A8: MXFP8 activations (the TRACE summary's MXFP4 W4A8 rollout, Table 4)
 # ---------------------------------------------------------------------------
@@ -252,6 +264,6 @@ def gemm_w4a8(a_codes, a_scales, w_codes, w_scales):
     return dequantize_fp8(a_codes, a_scales) @ dequantize(w_codes, w_scales).astype(np.float64).T
 
 
-__all__ = ["qdq_weights", "guided_round", "shared_exponents_fp8", "quantize_fp8", "dequantize_fp8", "gemm_w4a8",
+__all__ = ["qdq_weights", "guided_round", "guided_round_record", "shared_exponents_fp8", "quantize_fp8", "dequantize_fp8", "gemm_w4a8",
            "BLOCK", "E2M1_LEVELS", "e8m0_decode", "shared_exponents", "quantize", "dequantize",
            "residual", "resq_select_and_requant", "gemm_comp", "quantize_weights"]

@@ -432,6 +432,14 @@ def guided_round_record(x_train, record, roll_scales, roll_g):
     whose signed level index equals round-to-nearest's under S, and differs
     from it).
     """
+    S_all = np.repeat(effective_scales(roll_scales, roll_g), BLOCK, axis=1).astype(np.float64)
+    return guided_round_record_under(x_train, record, S_all)
+
+
+def guided_round_record_under(x_train, record, S_all):
+    """The record rule of guided_round_record with the rollout scale of every
+    element given directly (S_all float64 [M, K], each an fp32 value); shared
+    by the NVFP4 and MXFP4 forms, which differ only in S."""
     x = np.asarray(x_train, dtype=np.float32)
     m, k = x.shape
     rec = np.asarray(record, dtype=np.uint8)
@@ -439,7 +447,6 @@ def guided_round_record(x_train, record, roll_scales, roll_g):
     nib = np.empty((m, k), dtype=np.uint8)
     x_fq = np.empty((m, k), dtype=np.uint16)
     moved = np.zeros(2, dtype=np.int64)
-    S_all = np.repeat(effective_scales(roll_scales, roll_g), BLOCK, axis=1).astype(np.float64)
     mag_of_pos = np.abs(np.arange(_SIGNED_LEVELS.size) - (_SIGNED_LEVELS.size // 2))
     for r0 in range(0, m, 64):                  # row chunks bound the memory
         r1 = min(r0 + 64, m)
