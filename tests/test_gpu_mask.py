@@ -110,16 +110,23 @@ def test_masked_comp_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
     y0 = y.clone()
     P.moe_w4a4_masked_comp_gemm(mc, ms, mg, offs_t, rows, gc, gs, gg, out=y)
     y_np, y0_np = np32(y), np32(y0)
-    c_np, s_np, mc_np, ms_np = npu8(codes), npu8(scales), npu8(mc), npu8(ms)
-    gc_np, gs_np, gg_np, mg_np = npu8(gc), npu8(gs), np32(gg), np32(mg)
+    # the oracle's own operands, after checking the GPU's are identical
+    x_np = x.float().numpy()
+    c_np, s_np, g_np = OQ.quantize(x_np)
+    assert np.array_equal(npu8(codes), c_np) and np32(g)[0] == g_np
+    _, mc_np, ms_np, mg_np = OQ.resq_mask_select_and_requant(x_np, c_np, s_np, g_np, offs, k,
+                                                             row_index=rt["slot_token"])
+    assert np.array_equal(npu8(mc), mc_np) and np.array_equal(np32(mg), mg_np)
+    _, gc_np, gs_np, gg_np = OQ.qdq_weights(wgu.float().numpy())
+    assert np.array_equal(npu8(gc), gc_np) and np.array_equal(np32(gg), gg_np)
     for e in range(n_exp):
         a, b = offs[e], offs[e + 1]
         if a == b:
             continue
         tok = rt["slot_token"][a:b]
-        ref = OG.gemm_masked_comp(c_np[tok], s_np[tok], np32(g)[0], gc_np[e], gs_np[e], gg_np[e],
+        ref = OG.gemm_masked_comp(c_np[tok], s_np[tok], g_np, gc_np[e], gs_np[e], gg_np[e],
                                   mc_np[a:b], ms_np[a:b], mg_np[e])
-        ref0 = OG.gemm_comp(c_np[tok], s_np[tok], np32(g)[0], gc_np[e], gs_np[e], gg_np[e])
+        ref0 = OG.gemm_comp(c_np[tok], s_np[tok], g_np, gc_np[e], gs_np[e], gg_np[e])
         assert rel_err(y_np[a:b], ref) <= GEMM_TOL, f"expert {e}"
         assert rel_err(y0_np[a:b], ref0) <= GEMM_TOL, f"expert {e}"
 
@@ -145,7 +152,9 @@ def test_masked_comp_moves_toward_exact(gpu_lib):
                                                    unit_offsets=offs, rows_total=tokens)
     ym = y0.clone()
     P.moe_w4a4_masked_comp_gemm(mc, ms, mg, offs, tokens, wc, ws_, wg, out=ym)
+    _, wc_r, ws_r, wg_r = OQ.qdq_weights(w.float().numpy())
+    assert np.array_equal(npu8(wc), wc_r)
     exact = x.float().numpy().astype(np.float64) @ OQ.dequantize(
-        npu8(wc)[0], npu8(ws_)[0], np32(wg)[0]).astype(np.float64).T
+        wc_r[0], ws_r[0], wg_r[0]).astype(np.float64).T
     e0, ec, em = (np.linalg.norm(np32(t) - exact) for t in (y0, yc, ym))
     assert em < ec < e0

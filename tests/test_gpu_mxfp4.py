@@ -163,6 +163,28 @@ def _gemm_ref(a_c, a_s, w_c, w_s, sel=None, rc=None, rs=None):
     return MX.gemm_comp(a_c, a_s, w_c, w_s, sel, rc, rs)
 
 
+# The oracle never takes an input from the GPU: each stage's oracle operands
+# are computed from the seeded inputs by the oracle itself, after checking
+# that the GPU's result of that stage is identical.
+def ref_mx(x_np, codes, scales, fp8=False):
+    c_r, s_r = (MX.quantize_fp8 if fp8 else MX.quantize)(x_np)
+    assert np.array_equal(npu8(codes), c_r) and np.array_equal(npu8(scales), s_r)
+    return c_r, s_r
+
+
+def ref_mx_weights(w, wc, ws):
+    c_r, s_r = MX.quantize_weights(w.float().numpy())
+    assert np.array_equal(npu8(wc), c_r) and np.array_equal(npu8(ws), s_r)
+    return c_r, s_r
+
+
+def ref_mx_resq(x_np, c_r, s_r, offs, k, row_index, sel, rc, rs):
+    out = MX.resq_select_and_requant(x_np, c_r, s_r, offs, k, row_index=row_index)
+    for got, want in zip((npu8(sel), npu8(rc), npu8(rs)), out):
+        assert np.array_equal(got, want)
+    return out
+
+
 @pytest.mark.parametrize("spread", [False, True])
 def test_mx_dense_linear_compensated(gpu_lib, spread):
     """Single dense linear 128 x 512 -> 1024 with top-32 compensation over all
@@ -185,14 +207,17 @@ def test_mx_dense_linear_compensated(gpu_lib, spread):
     y = P.moe_mxfp4_grouped_gemm(codes, scales, offs, wl.tokens, wc, ws_, sel_idx=sel, r_codes=rc,
                                  r_scales=rs)
     y0 = P.moe_mxfp4_grouped_gemm(codes, scales, offs, wl.tokens, wc, ws_)
-    ref = _gemm_ref(npu8(codes), npu8(scales), npu8(wc)[0], npu8(ws_)[0], npu8(sel)[0], npu8(rc),
-                    npu8(rs))
-    ref0 = _gemm_ref(npu8(codes), npu8(scales), npu8(wc)[0], npu8(ws_)[0])
+    x_np = x.float().numpy()
+    c_r, s_r = ref_mx(x_np, codes, scales)
+    sel_r, rc_r, rs_r = ref_mx_resq(x_np, c_r, s_r, [0, wl.tokens], wl.k, None, sel, rc, rs)
+    wc_r, ws_r = ref_mx_weights(w, wc, ws_)
+    ref = _gemm_ref(c_r, s_r, wc_r[0], ws_r[0], sel_r[0], rc_r, rs_r)
+    ref0 = _gemm_ref(c_r, s_r, wc_r[0], ws_r[0])
     e_comp, e_plain = rel_err(np32(y), ref), rel_err(np32(y0), ref0)
     assert e_comp <= GEMM_TOL and e_plain <= GEMM_TOL, (e_comp, e_plain)
     if not spread:
         exact = x.float().numpy().astype(np.float64) @ MX.dequantize(
-            npu8(wc)[0], npu8(ws_)[0]).astype(np.float64).T
+            wc_r[0], ws_r[0]).astype(np.float64).T
         assert np.linalg.norm(np32(y) - exact) < np.linalg.norm(np32(y0) - exact)
 
 
@@ -246,8 +271,11 @@ def test_mx_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
     gu = P.moe_mxfp4_grouped_gemm(codes, scales, offs_t, rows, gc, gs, a_row_index=slot_tok, **comp)
     h = P.moe_mxfp4_grouped_gemm(codes, scales, offs_t, rows, gc, gs, a_row_index=slot_tok,
                                  epilogue=P.EPI_SWIGLU_BF16, **comp)
-    gu_ref = _gate_up_ref(npu8(codes), npu8(scales), rt["slot_token"], offs, npu8(gc), npu8(gs),
-                          npu8(sel), npu8(rc), npu8(rs))
+    x_np = x.float().numpy()
+    c_r, s_r = ref_mx(x_np, codes, scales)
+    sel_r, rc_r, rs_r = ref_mx_resq(x_np, c_r, s_r, offs, k, rt["slot_token"], sel, rc, rs)
+    gc_r, gs_r = ref_mx_weights(wgu, gc, gs)
+    gu_ref = _gate_up_ref(c_r, s_r, rt["slot_token"], offs, gc_r, gs_r, sel_r, rc_r, rs_r)
     gu_np = np32(gu)
     for e in range(n_exp):
         a, b = offs[e], offs[e + 1]
@@ -261,7 +289,7 @@ def test_mx_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
 
 @pytest.mark.parametrize("comp", [True, False])
 def test_mx_moe_layer(gpu_lib, comp):
-    """The MXFP4 MoE layer stage by stage on the GPU's own intermediates:
+    """The MXFP4 MoE layer stage by stage:
     quantize X, select + requantize per expert, gate/up with SwiGLU and the
     amax of h, quantize h, select per expert, down with the scatter-add."""
     P = gpu_lib
@@ -277,29 +305,34 @@ def test_mx_moe_layer(gpu_lib, comp):
         sel, rc, rs = P.mxfp4_resq_select_and_requant(xc, codes, scales, k, unit_offsets=offs_t,
                                                       rows_total=rows, row_index=slot_tok)
         comp1 = dict(sel_idx=sel, r_codes=rc, r_scales=rs)
-        comp1_ref = (npu8(sel), npu8(rc), npu8(rs))
+    x_np = x.float().numpy()
+    c_r, s_r = ref_mx(x_np, codes, scales)
+    if comp:
+        comp1_ref = ref_mx_resq(x_np, c_r, s_r, offs, k, rt["slot_token"], sel, rc, rs)
     gc, gs = _mx_weights(P, wgu)
+    gc_r, gs_r = ref_mx_weights(wgu, gc, gs)
     amax = torch.empty(1, dtype=torch.float32, device="cuda")
     h = P.moe_mxfp4_grouped_gemm(codes, scales, offs_t, rows, gc, gs, a_row_index=slot_tok,
                                  epilogue=P.EPI_SWIGLU_BF16, out_amax=amax, **comp1)
-    gu_ref = _gate_up_ref(npu8(codes), npu8(scales), rt["slot_token"], offs, npu8(gc), npu8(gs),
-                          *comp1_ref)
+    gu_ref = _gate_up_ref(c_r, s_r, rt["slot_token"], offs, gc_r, gs_r, *comp1_ref)
     g_, u_ = gu_ref[:, :inter], gu_ref[:, inter:]
-    h_r = F.bf16_bits_to_f32(F.f64_to_bf16_bits(g_ / (1 + np.exp(-g_)) * u_))
+    h_bits = F.f64_to_bf16_bits(g_ / (1 + np.exp(-g_)) * u_)
+    h_r = F.bf16_bits_to_f32(h_bits)
     h_np = np32(h)
     tol = np.abs(h_r) * 2.0 ** -7 + GEMM_TOL * np.abs(h_r).max()
     assert np.all(np.abs(h_np - h_r) <= tol)
     assert np32(amax)[0] == np.abs(h_np).max()
+    # down projection: both sides on the oracle's h (the GPU's h matched it
+    # above within the GEMM tolerance)
+    h = torch.from_numpy(h_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    h_np = h_r
     hq_c, hq_s, _ = P.mxfp4_quantize(h)
-    hc_r, hs_r = MX.quantize(h_np)
-    assert np.array_equal(npu8(hq_c), hc_r) and np.array_equal(npu8(hq_s), hs_r)
+    hc_r, hs_r = ref_mx(h_np, hq_c, hq_s)
     comp2, comp2_ref = {}, None
     if comp:
         sel2, rc2, rs2 = P.mxfp4_resq_select_and_requant(h, hq_c, hq_s, k, unit_offsets=offs_t,
                                                          rows_total=rows)
-        s2r = MX.resq_select_and_requant(h_np, hc_r, hs_r, offs, k)
-        assert np.array_equal(npu8(sel2), s2r[0]) and np.array_equal(npu8(rc2), s2r[1])
-        assert np.array_equal(npu8(rs2), s2r[2])
+        s2r = ref_mx_resq(h_np, hc_r, hs_r, offs, k, None, sel2, rc2, rs2)
         comp2, comp2_ref = dict(sel_idx=sel2, r_codes=rc2, r_scales=rs2), s2r
     dc, ds = _mx_weights(P, wd)
     y = torch.zeros(tokens, hidden, dtype=torch.float32, device="cuda")
@@ -307,7 +340,7 @@ def test_mx_moe_layer(gpu_lib, comp):
                              row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
                              scatter_index=slot_tok, out=y, **comp2)
     y_ref = np.zeros((tokens, hidden), np.float64)
-    dc_n, ds_n = npu8(dc), npu8(ds)
+    dc_n, ds_n = ref_mx_weights(wd, dc, ds)
     for e in range(n_exp):
         a, b = int(offs[e]), int(offs[e + 1])
         if a == b:
@@ -382,7 +415,8 @@ def test_w4a8_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
     gu = P.moe_mxfp4_w4a8_grouped_gemm(ac, asc, offs_t, rows, gc, gs, a_row_index=slot_tok)
     h = P.moe_mxfp4_w4a8_grouped_gemm(ac, asc, offs_t, rows, gc, gs, a_row_index=slot_tok,
                                       epilogue=P.EPI_SWIGLU_BF16)
-    ac_n, as_n, gc_n, gs_n = npu8(ac), npu8(asc), npu8(gc), npu8(gs)
+    ac_n, as_n = ref_mx(x.float().numpy(), ac, asc, fp8=True)
+    gc_n, gs_n = ref_mx_weights(wgu, gc, gs)
     ref = np.zeros((rows, 2 * inter))
     for e in range(n_exp):
         a, b = int(offs[e]), int(offs[e + 1])
@@ -411,7 +445,8 @@ def test_w4a8_down_scatter(gpu_lib):
                                   row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
                                   scatter_index=torch.from_numpy(rt["slot_token"]).cuda(), out=y)
     y_ref = np.zeros((tokens, hidden))
-    hc_n, hs_n, dc_n, ds_n = npu8(hc), npu8(hs), npu8(dc), npu8(ds)
+    hc_n, hs_n = ref_mx(hrows.to(torch.bfloat16).float().numpy(), hc, hs, fp8=True)
+    dc_n, ds_n = ref_mx_weights(wd, dc, ds)
     for e in range(n_exp):
         a, b = int(offs[e]), int(offs[e + 1])
         if a < b:
@@ -470,7 +505,8 @@ def test_mx_guided_round(gpu_lib, dtype, rel):
     x_train = synth.guided_noise(x_roll, seed=53, rel=rel).to(dtype)
     rc, rs, _ = P.mxfp4_quantize(x_roll.cuda())
     gc, fq, hist = P.mxfp4_guided_round(x_train.cuda(), rc, rs)
-    gc_r, fq_r, hist_r = MX.guided_round(x_train.float().numpy(), npu8(rc), npu8(rs))
+    rc_r, rs_r = ref_mx(x_roll.float().numpy(), rc, rs)
+    gc_r, fq_r, hist_r = MX.guided_round(x_train.float().numpy(), rc_r, rs_r)
     assert np.array_equal(npu8(gc), gc_r)
     assert np.array_equal(_bits(fq), fq_r)
     assert np.array_equal(hist.cpu().numpy(), hist_r)
@@ -489,7 +525,8 @@ def test_mx_guided_round_tiny_scales(gpu_lib):
     pad[:, :256] = x_train
     xt = pad.cuda()[:, :256]
     gc, fq, hist = P.mxfp4_guided_round(xt, rc, rs)
-    gc_r, fq_r, hist_r = MX.guided_round(x_train.float().numpy(), npu8(rc), npu8(rs))
+    rc_r, rs_r = ref_mx(x_roll.float().numpy(), rc, rs)
+    gc_r, fq_r, hist_r = MX.guided_round(x_train.float().numpy(), rc_r, rs_r)
     assert np.array_equal(npu8(gc), gc_r)
     assert np.array_equal(_bits(fq), fq_r)
     assert np.array_equal(hist.cpu().numpy(), hist_r)

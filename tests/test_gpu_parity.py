@@ -34,6 +34,30 @@ def rel_err(y, ref):
     return float(np.abs(y - ref).max() / (den if den > 0 else 1.0))
 
 
+# The oracle never takes an input from the GPU: each stage's oracle operands
+# are computed from the seeded inputs by the oracle itself, after checking
+# that the GPU's result of that stage is identical.
+def ref_quant(x, codes, scales, g):
+    c_r, s_r, g_r = OQ.quantize(x.float().numpy() if torch.is_tensor(x) else x)
+    assert np.array_equal(npu8(codes), c_r) and np.array_equal(npu8(scales), s_r)
+    assert np32(g)[0] == g_r
+    return c_r, s_r, g_r
+
+
+def ref_resq(x_np, c_r, s_r, g_r, offs, k, row_index, sel, rc, rs, rg):
+    out = OQ.resq_select_and_requant(x_np, c_r, s_r, g_r, offs, k, row_index=row_index)
+    for got, want in zip((npu8(sel), npu8(rc), npu8(rs), np32(rg)), out):
+        assert np.array_equal(got, want)
+    return out
+
+
+def ref_weights(w, wc, ws, wg):
+    _, c_r, s_r, g_r = OQ.qdq_weights(w.float().numpy())
+    assert np.array_equal(npu8(wc), c_r) and np.array_equal(npu8(ws), s_r)
+    assert np.array_equal(np32(wg), g_r)
+    return c_r, s_r, g_r
+
+
 # ---------------------------------------------------------------------------
 # quantize
 # ---------------------------------------------------------------------------
@@ -237,15 +261,17 @@ def test_dense_linear_compensated(gpu_lib):
     y = P.moe_w4a4_grouped_gemm(codes, scales, g, offs, wl.tokens, wc, ws_, wg,
                                 sel_idx=sel, r_codes=rc, r_scales=rs, r_global=rg)
     y0 = P.moe_w4a4_grouped_gemm(codes, scales, g, offs, wl.tokens, wc, ws_, wg)
-    ref = OG.gemm_comp(npu8(codes), npu8(scales), np32(g)[0], npu8(wc)[0], npu8(ws_)[0],
-                       np32(wg)[0], npu8(sel)[0], npu8(rc), npu8(rs), np32(rg)[0])
-    ref0 = OG.gemm_comp(npu8(codes), npu8(scales), np32(g)[0], npu8(wc)[0], npu8(ws_)[0],
-                        np32(wg)[0])
+    c_r, s_r, g_r = ref_quant(x, codes, scales, g)
+    sel_r, rc_r, rs_r, rg_r = ref_resq(x.float().numpy(), c_r, s_r, g_r, [0, wl.tokens], wl.k,
+                                       None, sel, rc, rs, rg)
+    wc_r, ws_r, wg_r = ref_weights(w, wc, ws_, wg)
+    ref = OG.gemm_comp(c_r, s_r, g_r, wc_r[0], ws_r[0], wg_r[0], sel_r[0], rc_r, rs_r, rg_r[0])
+    ref0 = OG.gemm_comp(c_r, s_r, g_r, wc_r[0], ws_r[0], wg_r[0])
     assert rel_err(np32(y), ref) <= GEMM_TOL
     assert rel_err(np32(y0), ref0) <= GEMM_TOL
     # compensation moves the result toward the unquantized product
     exact = x.float().numpy().astype(np.float64) @ OQ.dequantize(
-        npu8(wc)[0], npu8(ws_)[0], np32(wg)[0]).astype(np.float64).T
+        wc_r[0], ws_r[0], wg_r[0]).astype(np.float64).T
     assert np.linalg.norm(np32(y) - exact) < np.linalg.norm(np32(y0) - exact)
 
 
@@ -296,11 +322,16 @@ def _check_moe_layer(P, tokens, hidden, n_exp, inter, k, seed, zipf, top_k, empt
     amax = torch.empty(1, dtype=torch.float32, device="cuda")
     h = P.moe_w4a4_grouped_gemm(codes, scales, g, offs_t, rows, gc, gs, gg, a_row_index=slot_tok,
                                 epilogue=P.EPI_SWIGLU_BF16, out_amax=amax, **comp1)
+    x_np = x.float().numpy()
+    c_r, s_r, g_r = ref_quant(x_np, codes, scales, g)
+    gc_r, gs_r, gg_r = ref_weights(wgu, gc, gs, gg)
     comp_ref = {}
     if comp:
-        comp_ref = dict(sel_idx=npu8(sel), r_codes=npu8(rc), r_scales=npu8(rs), r_g=np32(rg))
-    gu_ref, h_ref = OG.moe_gate_up(npu8(codes), npu8(scales), np32(g)[0], rt["slot_token"], offs,
-                                   npu8(gc), npu8(gs), np32(gg), inter, **comp_ref)
+        sel_r, rc_r, rs_r, rg_r = ref_resq(x_np, c_r, s_r, g_r, offs, k, rt["slot_token"],
+                                           sel, rc, rs, rg)
+        comp_ref = dict(sel_idx=sel_r, r_codes=rc_r, r_scales=rs_r, r_g=rg_r)
+    gu_ref, h_ref = OG.moe_gate_up(c_r, s_r, g_r, rt["slot_token"], offs,
+                                   gc_r, gs_r, gg_r, inter, **comp_ref)
     gu_np = np32(gu)
     for e in range(n_exp):
         a, b = offs[e], offs[e + 1]
@@ -312,26 +343,31 @@ def _check_moe_layer(P, tokens, hidden, n_exp, inter, k, seed, zipf, top_k, empt
     tol = np.abs(h_r) * 2.0 ** -7 + GEMM_TOL * np.abs(h_r).max()
     assert np.all(np.abs(h_np - h_r) <= tol)
     assert np32(amax)[0] == np.abs(h_np).max()
-    # down projection with scatter-add, on the GPU's own h
-    hq_c, hq_s, hq_g, _ = P.nvfp4_quantize(h, amax_in=amax)
-    hc_r, hs_r, hg_r = OQ.quantize(h_np)
-    assert np.array_equal(npu8(hq_c), hc_r) and np.array_equal(npu8(hq_s), hs_r)
+    # down projection with scatter-add, both sides on the oracle's h (the
+    # GPU's h matched it above within the GEMM tolerance; the quantizer's
+    # amax_in path gets the amax of that h)
+    h_in = torch.from_numpy(h_ref.view(np.int16)).view(torch.bfloat16).cuda()
+    h_r32 = F.bf16_bits_to_f32(h_ref)
+    h_amax = torch.tensor([np.abs(h_r32).max()], dtype=torch.float32, device="cuda")
+    hq_c, hq_s, hq_g, _ = P.nvfp4_quantize(h_in, amax_in=h_amax)
+    hc_r, hs_r, hg_r = ref_quant(h_r32, hq_c, hq_s, hq_g)
+    h = h_in
+    h_np = h_r32
     comp2, comp2_ref = {}, {}
     if comp:
         sel2, rc2, rs2, rg2 = P.resq_select_and_requant(h, hq_c, hq_s, hq_g, k, unit_offsets=offs_t,
                                                         rows_total=rows)
-        s2r = OQ.resq_select_and_requant(h_np, hc_r, hs_r, hg_r, offs, k)
-        assert np.array_equal(npu8(sel2), s2r[0]) and np.array_equal(npu8(rc2), s2r[1])
-        assert np.array_equal(npu8(rs2), s2r[2]) and np.array_equal(np32(rg2), s2r[3])
+        s2r = ref_resq(h_np, hc_r, hs_r, hg_r, offs, k, None, sel2, rc2, rs2, rg2)
         comp2 = dict(sel_idx=sel2, r_codes=rc2, r_scales=rs2, r_global=rg2)
         comp2_ref = dict(sel_idx=s2r[0], r_codes=s2r[1], r_scales=s2r[2], r_g=s2r[3])
     dc, ds, dg = _quant_weights(P, wd)
+    dc_r, ds_r, dg_r = ref_weights(wd, dc, ds, dg)
     y = torch.zeros(tokens, hidden, dtype=torch.float32, device="cuda")
     P.moe_w4a4_grouped_gemm(hq_c, hq_s, hq_g, offs_t, rows, dc, ds, dg,
                             epilogue=P.EPI_SCATTER_ADD_F32,
                             row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
                             scatter_index=slot_tok, out=y, **comp2)
-    y_ref = OG.moe_down(hc_r, hs_r, hg_r, offs, npu8(dc), npu8(ds), np32(dg), rt["slot_token"],
+    y_ref = OG.moe_down(hc_r, hs_r, hg_r, offs, dc_r, ds_r, dg_r, rt["slot_token"],
                         rt["slot_weight"], tokens, **comp2_ref)
     assert rel_err(np32(y), y_ref) <= GEMM_TOL
 
@@ -387,7 +423,8 @@ def test_guided_round(gpu_lib, rel):
     x_train = synth.guided_noise(x_roll, seed=11, rel=rel)
     rc, rs, rg, _ = P.nvfp4_quantize(x_roll.cuda())
     gc, fq, hist = P.guided_round(x_train.cuda(), rc, rs, rg)
-    gc_r, fq_r, hist_r = OQ.guided_round(x_train.float().numpy(), npu8(rc), npu8(rs), np32(rg)[0])
+    c_r, s_r, g_r = ref_quant(x_roll, rc, rs, rg)
+    gc_r, fq_r, hist_r = OQ.guided_round(x_train.float().numpy(), c_r, s_r, g_r)
     assert np.array_equal(npu8(gc), gc_r)
     assert np.array_equal(fq.cpu().view(torch.int16).numpy().view(np.uint16), fq_r)
     assert np.array_equal(hist.cpu().numpy(), hist_r)
@@ -405,11 +442,11 @@ def test_guided_round_record(gpu_lib, rel, dtype):
         x_train = x_train + torch.randn(x_train.shape, generator=torch.Generator().manual_seed(2)) * 1e-4
     rc, rs, rg, _ = P.nvfp4_quantize(x_roll.cuda())
     rec = P.guidance_record_pack(rc)
-    rec_r = OQ.guidance_record(npu8(rc))
+    c_r, s_r, g_r = ref_quant(x_roll, rc, rs, rg)
+    rec_r = OQ.guidance_record(c_r)
     assert np.array_equal(npu8(rec), rec_r)
     gc, fq, moved = P.guided_round_record(x_train.cuda(), rec, rs, rg)
-    gc_r, fq_r, moved_r = OQ.guided_round_record(x_train.float().numpy(), rec_r, npu8(rs),
-                                                 np32(rg)[0])
+    gc_r, fq_r, moved_r = OQ.guided_round_record(x_train.float().numpy(), rec_r, s_r, g_r)
     assert np.array_equal(npu8(gc), gc_r)
     assert np.array_equal(fq.cpu().view(torch.int16).numpy().view(np.uint16), fq_r)
     assert np.array_equal(moved.cpu().numpy(), moved_r)
@@ -495,9 +532,13 @@ def test_grouped_gemm_tile_variants(gpu_lib, tokens, n_exp, top_k, zipf):
                                  **comp)
     h = P.moe_w4a4_grouped_gemm(codes, scales, g, offs_t, rows, gc, gs, gg, a_row_index=slot_tok,
                                 epilogue=P.EPI_SWIGLU_BF16, **comp)
-    gu_ref, h_ref = OG.moe_gate_up(npu8(codes), npu8(scales), np32(g)[0], rt["slot_token"], offs,
-                                   npu8(gc), npu8(gs), np32(gg), inter, sel_idx=npu8(sel),
-                                   r_codes=npu8(rc), r_scales=npu8(rs), r_g=np32(rg))
+    x_np = x.float().numpy()
+    c_r, s_r, g_r = ref_quant(x_np, codes, scales, g)
+    sel_r, rc_r, rs_r, rg_r = ref_resq(x_np, c_r, s_r, g_r, offs, k, rt["slot_token"],
+                                       sel, rc, rs, rg)
+    gc_r, gs_r, gg_r = ref_weights(wgu, gc, gs, gg)
+    gu_ref, h_ref = OG.moe_gate_up(c_r, s_r, g_r, rt["slot_token"], offs, gc_r, gs_r, gg_r, inter,
+                                   sel_idx=sel_r, r_codes=rc_r, r_scales=rs_r, r_g=rg_r)
     gu_np = np32(gu)
     for e in range(n_exp):
         a, b = offs[e], offs[e + 1]
@@ -532,7 +573,8 @@ def test_scatter_add_fixed_order_and_ragged_n(gpu_lib):
                                 scatter_index=torch.from_numpy(rt["slot_token"]).cuda(), out=y)
         outs.append(np32(y))
     assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    hc_r, hs_r, hg_r = ref_quant(h, hc, hs, hg)
+    dc_r, ds_r, dg_r = ref_weights(wd, dc, ds, dg)
     y_ref = y0.numpy().astype(np.float64) + OG.moe_down(
-        npu8(hc), npu8(hs), np32(hg)[0], offs, npu8(dc), npu8(ds), np32(dg), rt["slot_token"],
-        rt["slot_weight"], tokens)
+        hc_r, hs_r, hg_r, offs, dc_r, ds_r, dg_r, rt["slot_token"], rt["slot_weight"], tokens)
     assert rel_err(outs[0], y_ref) <= GEMM_TOL
