@@ -401,6 +401,23 @@ int mxfp4_guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int
                        uint8_t* guided_codes, void* x_fq, int64_t* dist_hist, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * mxfp4_guided_round_record -- guided rounding from the mantissa-only record
+ * of MXFP4 rollout codes ([TRACE] core method, second innovation; method
+ * steps two and four).  The record is guidance_record_pack's output for the
+ * MXFP4 codes (the low code bit, the same for both formats); with the E8M0
+ * scales beside it the guidance costs 1 + 8/32 = 1.25 bits per element.  As
+ * guided_round_record with S = 2^X of the element's rollout 32-block.
+ *   x_train       bf16/fp32 [M, ldx];  K multiple of 32
+ *   record        [M, K/8];  roll_scales [M, K/32]
+ *   guided_codes  out [M, K/2];  x_fq NULL or out bf16 [M, K]
+ *   moved         NULL or out int64 [2], as guided_round_record
+ * Errors: EINVAL (shapes, null pointers), EUNSUPPORTED (M*K/16 >= 2^31).
+ * ------------------------------------------------------------------------ */
+int mxfp4_guided_round_record(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                              const uint8_t* record, const uint8_t* roll_scales,
+                              uint8_t* guided_codes, void* x_fq, int64_t* moved, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * moe_mxfp4_grouped_gemm -- the routed grouped expert GEMM over MXFP4
  * activations and weights with the residual compensation term ([QUADS]
  * sec. 1: native W4A4 GEMM on the rollout; sec. 2.2B: the second FP4

@@ -62,6 +62,7 @@ _SIGNATURES = {
                                       _SZ, _P]),
     "mxfp4_qdq_weights": (_INT, [_P, _I64, _I64, _I64, _P, _P, _P, _P]),
     "mxfp4_guided_round": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
+    "mxfp4_guided_round_record": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "mxfp8_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P]),
     "moe_mxfp4_w4a8_grouped_gemm_workspace_size": (_SZ, [_I32, _I64, _I64, _I64, _INT, _I64]),
     "moe_mxfp4_w4a8_grouped_gemm": (_INT, [_P, _P, _P, _I64, _P, _I32, _I64, _I64, _P, _P, _I64,
@@ -321,6 +322,24 @@ def mxfp4_guided_round(x_train, roll_codes, roll_scales, want_fq=True, want_hist
                                   _ptr(roll_codes), _ptr(roll_scales), _ptr(codes), _ptr(fq),
                                   _ptr(hist), _stream()), "mxfp4_guided_round")
     return codes, fq, hist
+
+
+def mxfp4_guided_round_record(x_train, record, roll_scales, want_fq=True, want_moved=True):
+    """Guided rounding from the mantissa-only record [M, K/8] of MXFP4 rollout
+    codes, with their E8M0 scales [M, K/32].  Returns (codes [M, K/2], x_fq
+    bf16 or None, moved int64 [2] or None)."""
+    lib = load()
+    _require_cuda(x_train, record, roll_scales)
+    m, kk = x_train.shape
+    dev = x_train.device
+    codes = torch.empty(m, kk // 2, dtype=torch.uint8, device=dev)
+    fq = torch.empty(m, kk, dtype=torch.bfloat16, device=dev) if want_fq else None
+    moved = torch.empty(2, dtype=torch.int64, device=dev) if want_moved else None
+    _check(lib.mxfp4_guided_round_record(_ptr(x_train), _dtype_code(x_train), m, kk,
+                                         x_train.stride(0), _ptr(record), _ptr(roll_scales),
+                                         _ptr(codes), _ptr(fq), _ptr(moved), _stream()),
+           "mxfp4_guided_round_record")
+    return codes, fq, moved
 
 
 def guidance_record_pack(roll_codes):

@@ -573,6 +573,25 @@ int guided_round(const void* x_train, int dtype, int64_t M, int64_t K, int64_t l
                     fn);
 }
 
+int mxfp4_guided_round_record(const void* x_train, int dtype, int64_t M, int64_t K, int64_t ldx,
+                              const uint8_t* record, const uint8_t* roll_scales,
+                              uint8_t* guided_codes, void* x_fq, int64_t* moved, void* stream) {
+  const char* fn = "mxfp4_guided_round_record";
+  if (int s = check_act(x_train, dtype, M, K, ldx, fn)) return s;
+  if (K % 32 != 0) return fail(NVFP4_EINVAL, "%s: K=%lld is not a multiple of 32", fn, (long long)K);
+  if (M * (K / 16) > 2147483647LL)
+    return fail(NVFP4_EUNSUPPORTED, "%s: more than 2^31-1 blocks", fn);
+  if (M > 0 && (!record || !roll_scales || !guided_codes))
+    return fail(NVFP4_EINVAL, "%s: required pointer is NULL", fn);
+  if ((record && !aligned16(record)) || (guided_codes && !aligned16(guided_codes)) ||
+      (x_fq && !aligned16(x_fq)))
+    return fail(NVFP4_EINVAL, "%s: pointers must be 16-byte aligned", fn);
+  return hip_status(nvfp4::launch_mx_guided_record(x_train, dtype, M, K, ldx, record, roll_scales,
+                                                   guided_codes, static_cast<__bf16*>(x_fq), moved,
+                                                   static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int guidance_record_pack(const uint8_t* roll_codes, int64_t M, int64_t K, uint8_t* record,
                          void* stream) {
   const char* fn = "guidance_record_pack";

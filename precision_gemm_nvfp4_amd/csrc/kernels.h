@@ -96,6 +96,10 @@ hipError_t launch_mx_qdq(const __bf16* w, int64_t rows, int64_t K, __bf16* w_qdq
 hipError_t launch_mx_guided(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                             const uint8_t* roll_codes, const uint8_t* roll_scales, uint8_t* guided,
                             __bf16* x_fq, int64_t* hist, hipStream_t stream);
+hipError_t launch_mx_guided_record(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const uint8_t* record, const uint8_t* roll_scales,
+                                   uint8_t* guided, __bf16* x_fq, int64_t* moved,
+                                   hipStream_t stream);
 hipError_t launch_guided_record(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                                 const uint8_t* record, const uint8_t* roll_scales,
                                 const float* roll_global, uint8_t* guided, __bf16* x_fq,

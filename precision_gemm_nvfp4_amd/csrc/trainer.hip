@@ -394,6 +394,14 @@ hipError_t launch_mx_guided(const void* x, int dtype, int64_t M, int64_t K, int6
                                       guided, x_fq, hist, stream);
 }
 
+hipError_t launch_mx_guided_record(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                                   const uint8_t* record, const uint8_t* roll_scales,
+                                   uint8_t* guided, __bf16* x_fq, int64_t* moved,
+                                   hipStream_t stream) {
+  return launch_guided_t<true, true>(x, dtype, M, K, ldx, record, roll_scales, nullptr, guided,
+                                     x_fq, moved, stream);
+}
+
 hipError_t launch_guided_record(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                                 const uint8_t* record, const uint8_t* roll_scales,
                                 const float* roll_global, uint8_t* guided, __bf16* x_fq,

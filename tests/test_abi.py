@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 25      # 16 operations, 7 workspace queries, version, last error
+    assert len(declared) == 26      # 17 operations, 7 workspace queries, version, last error
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(P.exported_symbols()) == declared
@@ -200,3 +200,5 @@ def test_mxfp4_trainer_validation(lib):
     assert "multiple of 32" in err(lib)
     assert lib.mxfp4_guided_round(FAKE, 0, 4, 64, 64, None, FAKE, FAKE, None, None, None) == -1
     assert "NULL" in err(lib)
+    assert lib.mxfp4_guided_round_record(FAKE, 0, 4, 48, 48, FAKE, FAKE, FAKE, None, None, None) == -1
+    assert "multiple of 32" in err(lib)

@@ -530,3 +530,24 @@ def test_mx_guided_round_tiny_scales(gpu_lib):
     assert np.array_equal(npu8(gc), gc_r)
     assert np.array_equal(_bits(fq), fq_r)
     assert np.array_equal(hist.cpu().numpy(), hist_r)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("rel", [1e-3, 2e-2, 0.2])
+def test_mx_guided_round_record(gpu_lib, dtype, rel):
+    """Mantissa-only record of MXFP4 rollout codes (packed by the format-free
+    record packer), then guided rounding from it: codes, x_fq and the
+    kept/moved counts bit-exact."""
+    P = gpu_lib
+    x_roll = synth.activations(257, 1024, seed=55, heavy_frac=0.01)
+    x_train = synth.guided_noise(x_roll, seed=55, rel=rel).to(dtype)
+    rc, rs, _ = P.mxfp4_quantize(x_roll.cuda())
+    rc_r, rs_r = ref_mx(x_roll.float().numpy(), rc, rs)
+    rec = P.guidance_record_pack(rc)
+    rec_r = OQ.guidance_record(rc_r)
+    assert np.array_equal(npu8(rec), rec_r)
+    gc, fq, moved = P.mxfp4_guided_round_record(x_train.cuda(), rec, rs)
+    gc_r, fq_r, moved_r = MX.guided_round_record(x_train.float().numpy(), rec_r, rs_r)
+    assert np.array_equal(npu8(gc), gc_r)
+    assert np.array_equal(_bits(fq), fq_r)
+    assert np.array_equal(moved.cpu().numpy(), moved_r)
