@@ -446,6 +446,121 @@ def guidance_bench(args, torch, P, synth, wl, dev):
         frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
 
 
+def mask_bench(args, torch, P, synth, wl, dev):
+    """Dense 50% binary-mask compensation of the 8192-token layer's two
+    projections (F32 outputs): per projection the main grouped GEMM, the
+    masked residual of the top half of the channels per expert
+    (resq_mask_select_and_requant, k = K/2) and the second GEMM accumulated
+    into the product (moe_w4a4_masked_comp_gemm).  Gate/up reads X through
+    the routing; down reads seeded activations of the routed rows.
+    value = main-product GEMM TFLOP/s (the compensation counted as cost)."""
+    T, H, E, I = wl.tokens, wl.hidden, wl.experts, wl.inter
+    x = synth.activations(T, H, seed=wl.seed, device=dev.type, heavy_frac=wl.heavy_frac)
+    rt = synth.route(T, E, seed=wl.seed, top_k=wl.top_k, zipf_s=wl.zipf_s)
+    rows = int(rt["offsets"][-1])
+    offs = torch.from_numpy(rt["offsets"]).to(dev)
+    tok = torch.from_numpy(rt["slot_token"]).to(dev)
+    h = synth.activations(rows, I, seed=wl.seed + 1, device=dev.type, heavy_frac=wl.heavy_frac)
+    wgu = synth.weights(E, 2 * I, H, seed=wl.seed, tensor_id=synth.WGU_ID, device=dev.type)
+    wd = synth.weights(E, H, I, seed=wl.seed, tensor_id=synth.WD_ID, device=dev.type)
+    _, gc, gs, gg = P.qdq_weights(wgu)
+    _, dc, ds, dg = P.qdq_weights(wd)
+    del wgu, wd
+    y_gu = torch.empty(rows, 2 * I, dtype=torch.float32, device=dev)
+    y_d = torch.empty(rows, H, dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step(tl):
+        tl.mark("start")
+        xc, xs, xg, _ = P.nvfp4_quantize(x)
+        tl.mark("quantize_x")
+        P.moe_w4a4_grouped_gemm(xc, xs, xg, offs, rows, gc, gs, gg, a_row_index=tok, out=y_gu)
+        tl.mark("gemm_gate_up")
+        _, mc, ms, mg = P.resq_mask_select_and_requant(x, xc, xs, xg, H // 2, unit_offsets=offs,
+                                                       rows_total=rows, row_index=tok)
+        tl.mark("mask_select_x")
+        P.moe_w4a4_masked_comp_gemm(mc, ms, mg, offs, rows, gc, gs, gg, out=y_gu)
+        tl.mark("mask_gemm_gate_up")
+        hc, hs, hg, _ = P.nvfp4_quantize(h)
+        tl.mark("quantize_h")
+        P.moe_w4a4_grouped_gemm(hc, hs, hg, offs, rows, dc, ds, dg, out=y_d)
+        tl.mark("gemm_down")
+        _, mc2, ms2, mg2 = P.resq_mask_select_and_requant(h, hc, hs, hg, I // 2, unit_offsets=offs,
+                                                          rows_total=rows)
+        tl.mark("mask_select_h")
+        P.moe_w4a4_masked_comp_gemm(mc2, ms2, mg2, offs, rows, dc, ds, dg, out=y_d)
+        tl.mark("mask_gemm_down")
+
+    for _ in range(args.warmup):
+        step(Timeline(torch))
+    torch.cuda.synchronize()
+    tls = []
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        tl = Timeline(torch)
+        step(tl)
+        tls.append(tl)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    parts_ms = {}
+    for tl in tls:
+        for name, v in tl.durations().items():
+            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
+    f_gu, f_d = 2.0 * rows * 2 * I * H, 2.0 * rows * H * I
+    parts = {nm: dict(ms=round(v, 4)) for nm, v in parts_ms.items()}
+    for nm, f in (("gemm_gate_up", f_gu), ("mask_gemm_gate_up", f_gu), ("gemm_down", f_d),
+                  ("mask_gemm_down", f_d)):
+        parts[nm]["tflops"] = round(f / (parts_ms[nm] * 1e-3) / 1e12, 2)
+    overhead = {
+        "gate_up": round((parts_ms["mask_select_x"] + parts_ms["mask_gemm_gate_up"])
+                         / parts_ms["gemm_gate_up"], 3),
+        "down": round((parts_ms["mask_select_h"] + parts_ms["mask_gemm_down"])
+                      / parts_ms["gemm_down"], 3)}
+    ach = f_gu / (parts_ms["mask_gemm_gate_up"] * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import gemm as OG
+        from oracle import nvfp4 as OQ
+        xn = x.float().cpu().numpy()
+        g = OQ.global_scale(np.abs(xn).max())
+        w_all = synth.weights(E, 2 * I, H, seed=wl.seed, tensor_id=synth.WGU_ID, device=dev.type)
+        t0, dt, n_rows, n_exp = time.time(), 0.0, 0, 0
+        for e in range(E):                      # whole experts until about 10 s
+            a, b = int(rt["offsets"][e]), int(rt["offsets"][e + 1])
+            sub = xn[rt["slot_token"][a:b]]
+            we = w_all[e:e + 1].float().cpu().numpy()
+            t1 = time.time()
+            c, sc, _ = OQ.quantize(sub, g=g)
+            _, mcn, msn, mgn = OQ.resq_mask_select_and_requant(sub, c, sc, g, [0, b - a], H // 2)
+            _, wc, ws, wgn = OQ.qdq_weights(we)
+            OG.gemm_masked_comp(c, sc, g, wc[0], ws[0], wgn[0], mcn, msn, mgn[0])
+            dt += time.time() - t1
+            n_rows, n_exp = n_rows + (b - a), n_exp + 1
+            if time.time() - t0 > 10.0:
+                break
+        del w_all
+        cpu = dict(value=round(2.0 * n_rows * 2 * I * H / dt / 1e12, 5), unit="TFLOP/s",
+                   cores=torch.get_num_threads(), kind="oracle",
+                   sample=f"{n_exp} expert(s) ({n_rows} routed rows) of the gate/up projection in "
+                          f"expert order: quantize, masked residual (k = {H // 2}), weight "
+                          f"quantization, fp64 main + masked GEMM; {dt:.1f} s")
+    return dict(
+        metric="compensated W4A4 MoE GEMM TFLOPS (% FP4 peak); quantizer GB/s (% HBM)",
+        value=round((f_gu + f_d) / (ms * 1e-3) / 1e12, 2), unit="TFLOP/s",
+        ms_per_step=round(ms, 4),
+        config={"workload": wl.name, "tokens": T, "hidden": H, "experts": E, "inter": I,
+                "top_k": wl.top_k, "mask_fraction": 0.5, "routed_rows": rows,
+                "parallelism": "single GPU"},
+        dtype="nvfp4 (e2m1 + e4m3 scales) operands, fp16 MFMA (exact products), fp32 accumulate",
+        parts=parts, mask_overhead_vs_main_gemm=overhead,
+        roofline=dict(bound="mfma", achieved=round(ach, 2), peak=2500.0, unit="TFLOP/s",
+                      frac=round(ach / 2500.0, 4), traffic=None, mfma_dtype="fp16",
+                      kernel="nvfp4::grouped_gemm_kernel<4, 4, 2, 2, 0> (masked second GEMM)"),
+        cpu_baseline=cpu)
+
+
 def kv_bench(args, torch, P, synth, wl, dev):
     """NVFP4 KV cache with guided KV rounding (bandwidth-bound): per step, for
     the key and the value cache [tokens, heads, head_dim] (blocks along
@@ -547,9 +662,9 @@ def main():
     P.load()
     dev = torch.device("cuda:0")
     wl = synth.WORKLOADS[args.workload]
-    if wl.kind in ("quant_select", "guidance", "kv"):
+    if wl.kind in ("quant_select", "guidance", "kv", "mask"):
         fn = {"quant_select": quant_select_bench, "guidance": guidance_bench,
-              "kv": kv_bench}[wl.kind]
+              "kv": kv_bench, "mask": mask_bench}[wl.kind]
         res = fn(args, torch, P, synth, wl, dev)
         line = {"metric": res.pop("metric"), "value": res.pop("value"), "unit": res.pop("unit"),
                 "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,

@@ -162,6 +162,8 @@ WORKLOADS = {
         Workload("mx_moe_T8192_H4096_E256_I1536_k64_trainer", "moe", seed=4, tokens=8192,
                  hidden=4096, experts=256, inter=1536, k=64, heavy_frac=0.01, fmt="mxfp4",
                  trainer=True),
+        Workload("mask_moe_T8192_H4096_E256_I1536_k50pct", "mask", seed=4, tokens=8192,
+                 hidden=4096, experts=256, inter=1536, k=0, heavy_frac=0.01),
         Workload("guidance_record_T8192_K4096", "guidance", seed=4, tokens=8192, hidden=4096,
                  k=0, heavy_frac=0.01),
         Workload("kv_T65536_H4_D128", "kv", seed=5, tokens=65536, hidden=128, k=0,
