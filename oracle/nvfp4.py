@@ -132,16 +132,6 @@ def dequantize(codes, scales, g):
     return (e2m1_decode(nib) * S).astype(np.float32)
 
 
-def dequantize_exact(codes, scales, g):
-    """Real value represented by an NVFP4 tensor, value * s_b * g, in float64.
-
-    value * s_b has <= 6 significant bits and g <= 24, so the product is
-    exact.  Used as the GEMM operand of the reference result."""
-    nib = unpack_nibbles(codes)
-    s = np.repeat(E4M3_VALUES[np.asarray(scales, dtype=np.int64)], BLOCK, axis=1)
-    return e2m1_decode(nib) * s * np.float64(g)
-
-
 def residual(x, codes, scales, g):
     """R = fp32(x) - DQ(Q(x)) (QUADS section 2.2B: the residual between the
     activation and its FP4 quantization).
