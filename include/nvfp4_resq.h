@@ -112,6 +112,26 @@ int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                    float* tile_partials, void* ws, size_t ws_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * nvfp4_quantize_noalloc -- nvfp4_quantize for callers that cannot allocate
+ * device memory or pass a workspace: code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation.
+ *
+ * Arguments, results and errors are those of nvfp4_quantize without ws and
+ * ws_bytes.  Its scratch (the amax partial maxima, at most 1025 floats) is a
+ * fixed 8 KB array of device memory inside the library, one per GPU, held
+ * until the process ends; the call uses the copy of the current device
+ * (hipGetDevice), whose address it looks up on its first call there.  It
+ * calls no allocating routine.  EUNSUPPORTED if a shape ever needed more
+ * scratch than the array holds (none does: the partial count is capped).
+ * Calls share that array: two calls that overlap on one GPU (different
+ * streams, or threads) race and give unspecified results; calls ordered on
+ * one stream are safe.  Nothing in the array needs clearing between calls.
+ * ------------------------------------------------------------------------ */
+int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                           const float* amax_in, uint8_t* codes, uint8_t* scales, float* g_out,
+                           float* tile_partials, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * resq_select_and_requant -- residual activation compensation: pick the
  * high-residual channels of each selection unit and quantize their residual
  * a second time ([QUADS] sec. 2.2B: binary channel mask over channels of

@@ -36,6 +36,7 @@ _SIGNATURES = {
     "nvfp4_last_error": (ctypes.c_char_p, []),
     "nvfp4_quantize_workspace_size": (_SZ, [_I64, _I64]),
     "nvfp4_quantize": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "nvfp4_quantize_noalloc": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _P]),
     "resq_select_and_requant_workspace_size": (_SZ, [_I64, _I64, _I64, _I32]),
     "resq_select_and_requant": (_INT, [_P, _INT, _I64, _I64, _I64, _P, _P, _P, _P, _P, _I64,
                                        _I64, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
@@ -141,6 +142,21 @@ def nvfp4_quantize(x, amax_in=None, tile_partials=False):
                               _ptr(codes), _ptr(scales), _ptr(g), _ptr(tp), _ptr(ws), ws.numel(),
                               _stream()), "nvfp4_quantize")
     return codes, scales, g, tp
+
+
+def nvfp4_quantize_noalloc(x, codes, scales, g, amax_in=None, tile_partials=None):
+    """nvfp4_quantize into caller-given outputs, with the library's own
+    per-device scratch instead of a workspace: this call allocates nothing.
+
+    codes uint8 [M, K/2], scales uint8 [M, K/16], g fp32 [1] (or None),
+    tile_partials fp32 [ceil(M/128), K] or None; all on the GPU."""
+    lib = load()
+    _require_cuda(x, codes, scales, g, amax_in, tile_partials)
+    m, k = x.shape
+    _check(lib.nvfp4_quantize_noalloc(_ptr(x), _dtype_code(x), m, k, x.stride(0), _ptr(amax_in),
+                                      _ptr(codes), _ptr(scales), _ptr(g), _ptr(tile_partials),
+                                      _stream()), "nvfp4_quantize_noalloc")
+    return codes, scales, g, tile_partials
 
 
 def resq_select_and_requant(x, codes, scales, g, k, unit_offsets=None, rows_total=None,

@@ -6,6 +6,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 
 #include "../../include/nvfp4_resq.h"
 #include "kernels.h"
@@ -66,15 +67,92 @@ size_t nvfp4_quantize_workspace_size(int64_t M, int64_t K) {
   return align256((size_t)(nvfp4::amax_partials_count(M, K) + 1) * sizeof(float));
 }
 
-int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
-                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* g_out,
-                   float* tile_partials, void* ws, size_t ws_bytes, void* stream) {
-  const char* fn = "nvfp4_quantize";
+}  // extern "C"
+
+namespace {
+// Validation shared by nvfp4_quantize and nvfp4_quantize_noalloc (everything
+// but the workspace).  Returns NVFP4_OK, or the status of the first failure.
+int check_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                   const uint8_t* codes, const uint8_t* scales, const float* tile_partials,
+                   const char* fn) {
   if (int s = check_act(x, dtype, M, K, ldx, fn)) return s;
   if (M > 0 && (!codes || !scales)) return fail(NVFP4_EINVAL, "%s: codes/scales are NULL", fn);
   if (codes && !aligned16(codes)) return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
   if (tile_partials && !aligned16(tile_partials))
     return fail(NVFP4_EINVAL, "%s: tile_partials not 16-byte aligned", fn);
+  return NVFP4_OK;
+}
+
+// ---- scratch of nvfp4_quantize_noalloc --------------------------------------
+// The amax partial maxima and their fold: amax_partials_count(M, K) + 1 floats,
+// at most 1025 for any M (the count is capped at 1024), within this bound.
+// Every GPU the library runs on holds its own copy of the array until the
+// process ends.  In host code `scratch` names a host-side stand-in, never a
+// device address: the device address comes from hipGetSymbolAddress, taken
+// once per device with that device current and kept in g_scratch_ptr.
+constexpr size_t kScratchBytes = 8192;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's scratch (nullptr and a status
+// in *status on failure).
+void* scratch_of_current_device(int* status, const char* fn) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) {
+    *status = fail(NVFP4_EHIP, "%s: hipGetDevice: %s", fn, hipGetErrorString(e));
+    return nullptr;
+  }
+  if (dev < 0 || dev >= kMaxDevices) {
+    *status = fail(NVFP4_EUNSUPPORTED, "%s: device %d >= %d", fn, dev, kMaxDevices);
+    return nullptr;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr) {
+      *status = fail(NVFP4_EHIP, "%s: hipGetSymbolAddress(scratch): %s", fn, hipGetErrorString(e));
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = ptr;
+  }
+  *status = NVFP4_OK;
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize_noalloc(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                           const float* amax_in, uint8_t* codes, uint8_t* scales, float* g_out,
+                           float* tile_partials, void* stream) {
+  const char* fn = "nvfp4_quantize_noalloc";
+  if (int s = check_quantize(x, dtype, M, K, ldx, codes, scales, tile_partials, fn)) return s;
+  const size_t need = nvfp4_quantize_workspace_size(M, K);
+  if (need > kScratchBytes)
+    return fail(NVFP4_EUNSUPPORTED, "%s: needs %zu bytes of scratch, more than its %zu", fn, need,
+                kScratchBytes);
+  int status = NVFP4_OK;
+  void* ptr = scratch_of_current_device(&status, fn);
+  if (!ptr) return status;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (M == 0) {
+    if (g_out) return hip_status(nvfp4::launch_fill_f32(g_out, 1, 1.0f, st), fn);
+    return ok();
+  }
+  return hip_status(nvfp4::launch_quantize(x, dtype, M, K, ldx, amax_in, codes, scales, g_out,
+                                           tile_partials, static_cast<float*>(ptr), st),
+                    fn);
+}
+
+int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
+                   const float* amax_in, uint8_t* codes, uint8_t* scales, float* g_out,
+                   float* tile_partials, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "nvfp4_quantize";
+  if (int s = check_quantize(x, dtype, M, K, ldx, codes, scales, tile_partials, fn)) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (M == 0) {
     if (g_out) return hip_status(nvfp4::launch_fill_f32(g_out, 1, 1.0f, st), fn);

@@ -31,7 +31,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     declared = header_functions()
-    assert len(declared) == 26      # 17 operations, 7 workspace queries, version, last error
+    assert len(declared) == 27      # 18 operations, 7 workspace queries, version, last error
     for name in declared:
         assert hasattr(lib, name), name
     assert sorted(P.exported_symbols()) == declared
@@ -47,6 +47,21 @@ def test_workspace_sizes(lib):
 
 def err(lib):
     return lib.nvfp4_last_error().decode()
+
+
+def test_quantize_noalloc_validation(lib):
+    """The no-allocation quantize validates like nvfp4_quantize, before it
+    looks up its device scratch (so these run without a GPU)."""
+    f = lib.nvfp4_quantize_noalloc
+    assert f(None, 0, 4, 32, 32, None, FAKE, FAKE, None, None, None) == -1
+    assert "x is NULL" in err(lib) and "noalloc" in err(lib)
+    assert f(FAKE, 0, 4, 30, 32, None, FAKE, FAKE, None, None, None) == -1
+    assert "multiple of 16" in err(lib)
+    assert f(FAKE, 0, 4, 32, 20, None, FAKE, FAKE, None, None, None) == -1
+    assert f(FAKE, 7, 4, 32, 32, None, FAKE, FAKE, None, None, None) == -2
+    assert f(FAKE, 0, 4, 32, 32, None, None, FAKE, None, None, None) == -1
+    assert f(FAKE, 0, 4, 32, 32, None, ctypes.c_void_p(0x1004), FAKE, None, None, None) == -1
+    assert "aligned" in err(lib)
 
 
 def test_quantize_validation(lib):
