@@ -65,7 +65,8 @@ def gemm_kernel_name(rows, experts, epilogue, fmt="nvfp4"):
           "1, 4, 2, 2" if avg >= 24 else "1, 2, 1, 4"
     if fmt == "mxfp4":     # compensated (the bench always compensates)
         return f"nvfp4::mxg::mx_grouped_gemm_kernel<{cfg}, {epilogue}, true, false>"
-    return f"nvfp4::grouped_gemm_kernel<{cfg}, {epilogue}>"
+    # <MI, NJ, WM, WN, LDS slots, epilogue, compensation substeps> (kc = 64)
+    return f"nvfp4::nvg::grouped_gemm_kernel<{cfg}, 3, {epilogue}, 4>"
 
 
 def gemm_flops(rows, n, k, kc):
@@ -557,7 +558,7 @@ def mask_bench(args, torch, P, synth, wl, dev):
         parts=parts, mask_overhead_vs_main_gemm=overhead,
         roofline=dict(bound="mfma", achieved=round(ach, 2), peak=2500.0, unit="TFLOP/s",
                       frac=round(ach / 2500.0, 4), traffic=None, mfma_dtype="fp16",
-                      kernel="nvfp4::grouped_gemm_kernel<4, 4, 2, 2, 0> (masked second GEMM)"),
+                      kernel="nvfp4::nvg::grouped_gemm_kernel<4, 4, 2, 2, 3, 0, 0> (masked second GEMM)"),
         cpu_baseline=cpu)
 
 

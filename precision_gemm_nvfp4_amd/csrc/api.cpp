@@ -285,6 +285,8 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
   if (rows_total > 0 && (!a_codes || !a_scales)) return fail(NVFP4_EINVAL, "%s: a_codes/a_scales NULL", fn);
   if (rows_total > 0 && a_rows < 1)      // the kernel reads row 0 in place of rows outside a tile
     return fail(NVFP4_EINVAL, "%s: a_rows must be at least 1 when rows_total > 0", fn);
+  if (!nvfp4::grouped_gemm_offsets_fit(a_rows, N, K))
+    return fail(NVFP4_EUNSUPPORTED, "%s: A codes or one expert's W codes span 4 GiB or more", fn);
   if (!aligned16(w_codes) || (a_codes && !aligned16(a_codes)))
     return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
   if (sel_idx) {
@@ -342,6 +344,8 @@ int moe_w4a4_masked_comp_gemm(const uint8_t* m_codes, const uint8_t* m_scales,
   if (!aligned16(w_codes) || (m_codes && !aligned16(m_codes)))
     return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
   if (ldo < N) return fail(NVFP4_EINVAL, "%s: ldo=%lld < N", fn, (long long)ldo);
+  if (!nvfp4::grouped_gemm_offsets_fit(rows_total, N, K))
+    return fail(NVFP4_EUNSUPPORTED, "%s: m_codes or one expert's W codes span 4 GiB or more", fn);
   if (rows_total == 0) return ok();
   nvfp4::GemmArgs a;
   a.a_codes = m_codes; a.a_scales = m_scales; a.a_global = m_global;
@@ -456,6 +460,8 @@ int moe_mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
   if (rows_total > 0 && (!a_codes || !a_scales)) return fail(NVFP4_EINVAL, "%s: a_codes/a_scales NULL", fn);
   if (rows_total > 0 && a_rows < 1)      // the kernel reads row 0 in place of rows outside a tile
     return fail(NVFP4_EINVAL, "%s: a_rows must be at least 1 when rows_total > 0", fn);
+  if (!nvfp4::grouped_gemm_offsets_fit(a_rows, N, K))
+    return fail(NVFP4_EUNSUPPORTED, "%s: A codes or one expert's W codes span 4 GiB or more", fn);
   if (!aligned16(w_codes) || (a_codes && !aligned16(a_codes)))
     return fail(NVFP4_EINVAL, "%s: codes not 16-byte aligned", fn);
   if ((reinterpret_cast<uintptr_t>(w_scales) & 3u) || (reinterpret_cast<uintptr_t>(a_scales) & 3u))

@@ -15,34 +15,52 @@
 // dequantizes its own MFMA fragments in registers right before use: the
 // hardware FP4 -> fp16 convert (two elements per instruction) and one packed
 // fp16 multiply by the block's E4M3 scale (itself converted to fp16 by the
-// hardware FP8 -> fp16 convert), both exact.  The MFMA is
-// v_mfma_f32_32x32x16_f16 with fp32 accumulation (the same rate as bf16);
-// the global scales gA gW (gR gW) are applied in the epilogue.
+// hardware FP8 -> fp16 convert), both exact: one VALU instruction per
+// element.  The MFMA is v_mfma_f32_32x32x16_f16 with fp32 accumulation; the
+// global scales are applied after the K loop.  A wave owns 128 x 128 outputs
+// (MI = NJ = 4 blocks of 32 x 32) in the large tiles, so it dequantizes 8
+// fragments for every 16 MFMAs: about 4 VALU instructions per MFMA, which
+// gfx950 issues while the matrix core works (a SIMD overlaps independent
+// VALU work with an f16 MFMA up to about that rate, measured).
 //
-// K order inside a 32-wide K-step: in both MFMA substeps, lane half h (lanes
-// 32h .. 32h+31) supplies the 16 consecutive k of NVFP4 block h of the step
-// (first 8 in substep 0, last 8 in substep 1), so one 8-byte LDS read and one
-// scale byte give a lane a whole block.  A and B use the same order, so the
-// sum over the step's 32 k is unchanged.
+// Data path (per 256-thread workgroup, one tile of BM rows x 256 weight rows):
+// K moves 128 per pipeline stage through a ring of NSLOT LDS slots, filled by
+// direct global-to-LDS loads (global_load_lds_dwordx4 / _dword: lane l of an
+// instruction writes 16 / 4 bytes at base + 16 l / 4 l, so no registers carry
+// the tiles).  A slot holds, for every A row and W row, the stage's 64 code
+// bytes (16-byte chunks swizzled within a row: chunk c of row r at position
+// c ^ ((r >> 1) & 3), so that the fragment reads of 8 consecutive rows hit
+// distinct banks) and its 8 scale bytes as two words, stored in the order the
+// fragment reads want them.  Every wave issues the same number of load
+// instructions per stage (padding ones go to a dummy area), so one vmcnt wait
+// tells it that its share of a stage has landed.
 //
-// Pipeline: LDS holds two stages of raw codes + scales (9 KB per stage for a
-// 256 x 256 tile); global loads run two K-steps ahead in a double register
-// set.  In step s each wave issues its MFMAs of step s one at a time, and
-// between them (fenced groups, so the order survives scheduling) the LDS
-// reads of its step s+1 fragments, the stage write of step s+2, the global
-// loads of step s+4 and the dequantization of the step s+1 fragments, half a
-// fragment per MFMA.  One barrier per step.  On gfx950 a SIMD does not run
-// VALU instructions while an MFMA executes, so the dequantization adds to the
-// MFMA time (about 4.5 VALU instructions per MFMA for a 128 x 128 wave tile);
-// the schedule keeps the MFMA pipe from also waiting on LDS or memory.  The
-// 32-row tile, bound by memory rather than MFMA, uses 128-K stages with
-// coalesced loads instead (MacroTile below).
+// K order inside a stage: lane half h takes chunks h*2 + t (t = 0, 1), i.e.
+// the 64 K-values of scale word h, and MFMA substep q = 4 t + u (u = 0..3)
+// takes the u-th 8 codes of chunk 2h + t from every lane: 16 K-values per
+// substep, 128 per stage, the same order in A and W, so the sum over the
+// stage is unchanged.  A lane's scale word then holds exactly its four
+// blocks, and the FP8 convert's word select (t) picks the pair it needs
+// without a shift.
 //
-// The compensation term is an extra chunk of kc: while the main loop streams
-// the expert's weight tile through LDS, the elements of the selected columns
-// are dequantized into an fp16 [BN, kc] buffer, so W is read from memory once.
-// After the main loop the accumulators are rescaled by gA/gR, Q(R_S) x W_S is
-// accumulated, and the epilogue multiplies by gR gW.
+// Per stage s a wave holds the stage's raw fragments in registers (read from
+// LDS during stage s - 1) and runs its 8 substeps; during substep q it issues
+// the 16 MFMAs of q and dequantizes the fragments of q + 1.  At substep 3
+// (raw chunk-0 registers consumed) it waits for its loads of stage s + 1,
+// meets the other waves at the stage's one barrier, issues the loads of stage
+// s + NSLOT into the slot stage s used, and reads the chunk-0 fragments and
+// scale words of stage s + 1; at substep 7 the chunk-1 fragments.  A slot is
+// therefore refilled only after every wave passed the barrier that followed
+// its last read, and loads have NSLOT - 1 stages to land.
+//
+// Compensation: while the K loop streams the expert's weight tile through
+// the slots, each thread copies the elements of the selected columns of its
+// weight row into an fp16 W_S [BN, kc] buffer (exact), so W is read once.
+// The Q(R_S) codes of the tile's rows come into LDS by direct loads issued
+// ahead of the stages, their scale bytes into registers.  After the loop each
+// 32 x 32 block's correction is accumulated separately (kc / 16 MFMAs) and
+// combined as acc * gA gW + corr * gR gW, so no ratio of global scales can
+// overflow.
 //
 // Epilogues (gemm_common.h) stage each wave's 32-row blocks through LDS and
 // write whole row segments with 16-byte stores.  Scatter epilogue:
@@ -55,221 +73,410 @@
 // an upper bound ((ceil(rows / BM) + E) x n-tiles, rounded up to a multiple of
 // 8).  Workgroup ids are dealt round-robin to the 8 XCDs, so hardware id h
 // runs logical tile (h % 8) * ceil(T / 8) + h / 8 and the rest exit: each XCD
-// owns a contiguous eighth of the real tiles (dividing the upper bound instead
-// would leave whole XCDs with surplus workgroups only).  Inside an XCD the
-// workgroups go to its shader engines in a fixed rotation and in order, so
-// neighbouring tiles should cost the same: with n-tiles innermost a ragged
-// last m-tile is a run of equally cheap tiles (with m-tiles innermost, full
-// and nearly empty tiles alternate and half the engines get all the full
-// ones).  The m-tiles that share one weight tile still run within one
-// window of the XCD's CUs (the weight tile comes from L2 the second time),
-// and an A tile is reused by consecutive n-tiles.  Four waves per workgroup;
-// each wave owns MI x NJ MFMA blocks of 32 x 32.
+// owns a contiguous eighth of the real tiles.  Inside an XCD the workgroups go
+// to its shader engines in a fixed rotation and in order, so neighbouring
+// tiles should cost the same: with n-tiles innermost a ragged last m-tile is
+// a run of equally cheap tiles.  The m-tiles that share one weight tile run
+// within one window of the XCD's CUs (the weight tile comes from L2 the
+// second time), and an A tile is reused by consecutive n-tiles.
 #include "gemm_common.h"
 
 namespace nvfp4 {
+namespace nvg {
 
-constexpr int BN = 256, BK = 32;
+constexpr int BN = 256;                     // weight rows per tile
+constexpr int KS = 128;                     // K per pipeline stage
+constexpr int MAX_KC = 128;                 // largest compensated channel count
+constexpr int DUMMY_BYTES = 1024;           // target of the padding loads
 
-// 32-channel chunks of a padded compensation width
-__host__ __device__ constexpr int nchunk_of(int kcp) { return kcp / 32; }
+// One LDS slot: A codes [BM][64], W codes [BN][64], A scale words [2 BM],
+// W scale words [2 BN].  Load instructions per stage: NA A-code blocks of 16
+// rows (1 KB), NW W-code blocks, NAS / NWS scale blocks of 64 words; per wave
+// the ceiling of a quarter of each.
+template <int BM>
+struct Layout {
+  static constexpr int A_OFF = 0;
+  static constexpr int B_OFF = BM * 64;
+  static constexpr int AS_OFF = B_OFF + BN * 64;
+  static constexpr int BS_OFF = AS_OFF + BM * 8;
+  static constexpr int STAGE = BS_OFF + BN * 8;
+  static constexpr int NA = BM / 16, NW = BN / 16, NAS = BM / 32, NWS = BN / 32;
+  static constexpr int PA = (NA + 3) / 4, PW = (NW + 3) / 4, PAS = (NAS + 3) / 4, PWS = (NWS + 3) / 4;
+  static constexpr int LPW = PA + PW + PAS + PWS;      // load instructions per wave and stage
+};
 
-// LDS bytes of the epilogue staging (four waves), and the offset of the
-// scatter epilogue's row weights: past the K-loop region (loop_end bytes) and
-// the staging.
-template <int NJ>
-__host__ __device__ constexpr size_t epilogue_lds_bytes() { return (size_t)4 * epilogue_wave_floats<NJ>() * 4; }
-__host__ __device__ constexpr size_t rw_offset(size_t loop_end, size_t epi_end) {
-  return ((loop_end > epi_end ? loop_end : epi_end) + 15) / 16 * 16;
-}
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
 
 template <int V>
 struct IntC {
   static constexpr int value = V;
 };
-constexpr int NSTAGE = 2;                   // LDS stages of raw NVFP4 tiles
-constexpr int MAX_KC = 128;                 // largest compensated channel count handled
 
-struct RowLoad {                            // one row's K-step: 32 codes + 2 scale bytes
-  u32x4 codes;
-  uint32_t scales;
-};
-
-// The E4M3 scale byte b (bits 0..7 of the argument) as fp16 in both halves.
-__device__ __forceinline__ f16x2 e4m3_f16x2(uint32_t b) {
-  const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(b, 1.0f, false);
-  return f16x2{v[0], v[0]};
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+__device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t off, unsigned char* l) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off), (lds_void_t*)l, 16, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(const uint8_t* base, uint32_t off, unsigned char* l) {
+  __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off), (lds_void_t*)l, 4, 0, 0);
+}
+// s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 0-3 and 14-15)
+template <int N>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | 0x70 | ((N >> 4) << 14));
 }
 
-// Two fp16x8 fragments (substeps 0 and 1) from 16 codes (8 bytes) and the
-// block scale s: element i is the code of nibble i (low nibble first).
-__device__ __forceinline__ void dequant16(u32x2 c, f16x2 s, f16x8& f0, f16x8& f1) {
-#define NVFP4_CVT(w, sel) (__builtin_amdgcn_cvt_scalef32_pk_f16_fp4((w), 1.0f, (sel)) * s)
-  const f16x2 v0 = NVFP4_CVT(c[0], 0), v1 = NVFP4_CVT(c[0], 1), v2 = NVFP4_CVT(c[0], 2),
-              v3 = NVFP4_CVT(c[0], 3), v4 = NVFP4_CVT(c[1], 0), v5 = NVFP4_CVT(c[1], 1),
-              v6 = NVFP4_CVT(c[1], 2), v7 = NVFP4_CVT(c[1], 3);
-#undef NVFP4_CVT
-  f0 = f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
-  f1 = f16x8{v4[0], v4[1], v5[0], v5[1], v6[0], v6[1], v7[0], v7[1]};
+// The E4M3 bytes 2 t and 2 t + 1 of word w as fp16 (t = 0: bytes 0, 1).
+template <int T>
+__device__ __forceinline__ f16x2 scale_pair(uint32_t w) {
+  return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, T != 0);
 }
 
-// One fp16x8 fragment half from 8 codes (4 bytes) and the block scale.
-__device__ __forceinline__ f16x8 dequant8(uint32_t w, f16x2 s) {
-#define NVFP4_CVT(sel) (__builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, (sel)) * s)
-  const f16x2 v0 = NVFP4_CVT(0), v1 = NVFP4_CVT(1), v2 = NVFP4_CVT(2), v3 = NVFP4_CVT(3);
-#undef NVFP4_CVT
+// One MFMA operand: the 8 E2M1 codes of w (low nibble first) times scale s.
+__device__ __forceinline__ f16x8 dequant8(uint32_t w, _Float16 s) {
+  const f16x2 ss = f16x2{s, s};
+  const f16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
+  const f16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
+  const f16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
+  const f16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
   return f16x8{v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
 }
 
-// LDS layout of one pipeline stage for a BM-row A tile and the BN-row W tile.
-template <int BM>
-struct StageLayout {
-  static constexpr int AR = BM < 256 ? BM + 1 : BM;
-  static constexpr int A_CODES = 0;
-  static constexpr int A_SC = AR * 16;
-  static constexpr int B_CODES = (A_SC + AR * 2 + 15) / 16 * 16;
-  static constexpr int B_SC = B_CODES + BN * 16;
-  static constexpr int BYTES = (B_SC + BN * 2 + 15) / 16 * 16;
-};
-
-// The 32-row tile (MI = WM = 1) streams W with little reuse (a decode batch
-// gives each expert a few rows), so it is bound by the memory system rather
-// than the matrix cores, and it moves 128 K per pipeline stage instead of 32:
-// four lanes load one row's 64 contiguous code bytes (one 64-byte request
-// where the 32-wide stage needs four 16-byte ones, plus as many for the scale
-// bytes), and there is one barrier per 128 K.  LDS row: 64 code bytes then
-// the 8 scale bytes of its blocks; the 72-byte row stride makes the 8-byte
-// fragment reads of 32 consecutive rows conflict-free.
-template <int MI, int WM>
-struct MacroTile {
-  static constexpr bool on = MI == 1 && WM == 1;
-};
-template <int BM>
-struct MacroLayout {
-  static constexpr int KM = 128;              // K per stage
-  static constexpr int ROW = 72;
-  static constexpr int A_OFF = 0;             // A rows [BM + 1] (row BM: the spare)
-  static constexpr int B_OFF = (BM + 1) * ROW;
-  static constexpr int BYTES = (B_OFF + BN * ROW + 15) / 16 * 16;
-};
-template <int MI, int WM>
-__host__ __device__ constexpr int stage_bytes() {
-  return MacroTile<MI, WM>::on ? MacroLayout<WM * MI * 32>::BYTES : StageLayout<WM * MI * 32>::BYTES;
+// An empty asm that takes the first n registers of v: their values must
+// exist at this point of the program.
+template <int n, int N>
+__device__ __forceinline__ void pin_regs(f16x8 (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < n; ++i) asm volatile("" : "+v"(v[i]));
 }
 
-// EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows), fixed per kernel.
-template <int MI, int NJ, int WM, int WN, int EPI>
+// LDS bytes of the K-loop region: slots, dummy, W_S (fp16 [BN][kq*16 + 8]),
+// sel [MAX_KC], the per-stage gather table [nst + 2] (8 bytes each), and the
+// Q(R_S) codes [BM][kc / 2].
+template <int BM, int NSLOT, int KQ>
+__host__ __device__ constexpr size_t loop_lds_bytes(int64_t K) {
+  return (size_t)NSLOT * Layout<BM>::STAGE + DUMMY_BYTES +
+         (KQ > 0 ? (size_t)BN * (KQ * 16 + 8) * 2 + (size_t)MAX_KC * 4 : 0) +
+         ((((size_t)((K + KS - 1) / KS) + 2) * 8 + 15) / 16 * 16) +
+         (KQ > 0 ? (size_t)BM * KQ * 8 : 0);
+}
+
+// EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows).  KQ: 0 without
+// compensation, else the largest kc / 16 handled.
+template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
   static_assert(WM * WN == 4, "four waves");
-  // LDS: NSTAGE x {A codes [AR][16 B], A scales [AR][2 B], B codes [BN][16 B],
-  // B scales [BN][2 B]}, then the fp16 W_S buffer, the selected channels and
-  // their K-step ranges.  AR = BM + 1 when BM < 256: threads past BM write
-  // their A data into the spare row, so staging has no branch.
-  using L = StageLayout<BM>;
-  constexpr int A_CODES = L::A_CODES, A_SC = L::A_SC, B_CODES = L::B_CODES, B_SC = L::B_SC;
-  constexpr bool kMacro = MacroTile<MI, WM>::on;
-  constexpr int STAGE = stage_bytes<MI, WM>();
+  using L = Layout<BM>;
+  constexpr int STAGE = L::STAGE, LPW = L::LPW;
+  constexpr bool COMP = KQ > 0;
+  constexpr int WSS = KQ * 16 + 8;                        // W_S row stride (halves)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  _Float16* WS = reinterpret_cast<_Float16*>(smem + NSTAGE * STAGE);   // [BN][ws_stride]
+  unsigned char* DUMMY = smem + NSLOT * STAGE;
+  _Float16* WS = reinterpret_cast<_Float16*>(DUMMY + DUMMY_BYTES);
+  int32_t* sel = reinterpret_cast<int32_t*>(WS + (COMP ? BN * WSS : 0));
+  // gather table: per stage the first selected channel j0 and their count
+  // n (j0 | n << 8) and the in-stage offsets of the first four (7 bits each)
+  u32x2* tab = reinterpret_cast<u32x2*>(sel + (COMP ? MAX_KC : 0));
+  // Q(R_S) codes of the tile's rows [BM][kc / 2], 16-byte aligned, after tab
+  unsigned char* RSC = reinterpret_cast<unsigned char*>(
+      (reinterpret_cast<uintptr_t>(tab + ((p.K + KS - 1) / KS) + 2) + 15) & ~static_cast<uintptr_t>(15));
+  float* RW = reinterpret_cast<float*>(smem + p.rw_lds_offset);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // uniform: LDS targets in SGPRs
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
-  // XCD x = blockIdx % 8 takes the logical tiles [x * per_xcd, (x + 1) * per_xcd)
-  // of the T real ones (per_xcd = ceil(T / 8)); the grid, a multiple of 8 and
-  // at least T, leaves surplus workgroups that exit here.
-  const int real = (int)count_mtiles<BM>(p) * ntiles;
-  const int per_xcd = (real + 7) / 8;
-  const int jt = (int)blockIdx.x / 8;
-  const int logical = ((int)blockIdx.x % 8) * per_xcd + jt;
-  if (jt >= per_xcd || logical >= real) return;     // uniform over the workgroup
-  const TileCoord tc = locate_tile<BM>(p, ntiles, logical);
+  TileCoord tc;
+  if (!map_tile<BM>(p, ntiles, tc)) return;       // uniform over the workgroup
   const int e = tc.e, n_tile = tc.n_tile, rows_valid = tc.rows_valid;
   const int64_t row0 = tc.row0;
-
   const int64_t K = p.K;
-  const int nsteps = (int)(K / BK);
-  const bool comp = p.sel_idx != nullptr;
-  const int kc = comp ? p.kc : 0;
-  const int kcp = (kc + BK - 1) / BK * BK;                   // padded to whole K-steps
-  const int ws_stride = kcp + 8;
-  int32_t* sel = reinterpret_cast<int32_t*>(WS + (comp ? BN * ws_stride : 0));   // [MAX_KC]
-  int32_t* jr = sel + MAX_KC;                                                   // [nsteps + 1]
-  // Q(R_S) rows of the tile: chunk c of 32 compact channels at c * BM * 18
-  // bytes, codes [BM][16 B] then scales [BM][2 B]
-  unsigned char* RS = reinterpret_cast<unsigned char*>(
-      (reinterpret_cast<uintptr_t>(jr + nsteps + 1) + 15) & ~static_cast<uintptr_t>(15));
-  // scatter epilogue: row_weight of the tile's rows [BM] (0 past the group),
-  // past both the K-loop region and the epilogue's staging (which it outlives)
-  float* RW = reinterpret_cast<float*>(
-      smem + rw_offset((size_t)(RS - smem) + (comp ? (size_t)nchunk_of(kcp) * BM * 18 : 0),
-                       epilogue_lds_bytes<NJ>()));
+  const int nst = (int)((K + KS - 1) / KS);
+  const int mh = (K % KS) != 0 ? nst - 1 : -1;     // the half-full last stage, if any
+  const uint32_t rbytes = (uint32_t)(K / 2), sbytes = (uint32_t)(K / 16);
+  const int kc = COMP ? p.kc : 0;
 
-
-  // ---- this thread's rows: A row tid (if < BM), W row tid ------------------
-  // Loads are branch-free: a row outside the tile reads row 0 of its operand
-  // (always valid) and is zeroed by a select, so the compiler can count the
-  // loads in flight and keep the prefetch of later K-steps outstanding.
-  bool a_ok = false;
-  int64_t ar = 0;
-  if (tid < rows_valid) {
-    const int64_t ur = row0 + tid;
-    ar = p.a_row_index ? (int64_t)p.a_row_index[ur] : ur;
-    a_ok = ar >= 0 && ar < p.a_rows;
-    if (!a_ok) ar = 0;
+  // ---- prologue ------------------------------------------------------------------
+  // The global reads the set-up needs (row indexes of the tile's A rows, the
+  // selected channels, the row weights) go out together, then the LDS set-up,
+  // then the stage loads: few dependent memory round trips per tile.
+  //
+  // A unit row r of the tile reads activation row a_row(r); rows past the
+  // group read row 0 (their outputs are never stored); a row index outside
+  // [0, a_rows) reads row 0 and its scales are zeroed in registers, so that
+  // row reads as zeros.  Weight rows past N read row 0 (never stored).
+  auto a_index = [&](int r) -> int64_t {
+    if (r >= rows_valid) return 0;
+    const int64_t ur = row0 + r;
+    return p.a_row_index ? (int64_t)p.a_row_index[ur] : ur;
+  };
+  auto a_row = [&](int r) -> int64_t {
+    const int64_t ar = a_index(r);
+    return ar >= 0 && ar < p.a_rows ? ar : 0;
+  };
+  auto w_row = [&](int r) -> int64_t {
+    const int64_t br = weight_row<BN>(p, n_tile, r);
+    return br >= 0 ? br : 0;
+  };
+  // Addresses: a uniform base (argument + expert + stage offsets, in SGPRs)
+  // plus a 32-bit per-lane offset (the host checks that A and one expert's W
+  // span less than 4 GiB), which the load takes as its saddr + voffset form.
+  // (local copies: the loop must not read the argument struct from memory)
+  const uint8_t* const a_codes = p.a_codes;
+  const uint8_t* const a_scales = p.a_scales;
+  const uint8_t* const wc_e = p.w_codes + (int64_t)e * p.N * rbytes;
+  const uint8_t* const ws_e = p.w_scales + (int64_t)e * p.N * sbytes;
+  const int lr = lane >> 2, lp = lane & 3;
+  // code loads: lane l of block b loads tile row 16 b + l / 4, LDS position
+  // l % 4, i.e. logical chunk (l % 4) ^ swz(row)
+  uint32_t a_off[L::PA], b_off[L::PW];
+  int a_chk[L::PA], b_chk[L::PW];
+#pragma unroll
+  for (int i = 0; i < L::PA; ++i) {
+    const int b = wave * L::PA + i;
+    const int r = (b < L::NA ? b : 0) * 16 + lr;
+    a_chk[i] = lp ^ swz(r);
+    a_off[i] = (uint32_t)(a_row(r) * rbytes) + (uint32_t)(a_chk[i] << 4);
   }
-  const uint8_t* a_cp = p.a_codes + ar * (K / 2);
-  const uint8_t* a_sp = p.a_scales + ar * (K / 16);
-  const int64_t b_row = weight_row<BN>(p, n_tile, tid);
-  const bool b_ok = b_row >= 0;
-  const uint8_t* b_cp = p.w_codes + ((int64_t)e * p.N + (b_ok ? b_row : 0)) * (K / 2);
-  const uint8_t* b_sp = p.w_scales + ((int64_t)e * p.N + (b_ok ? b_row : 0)) * (K / 16);
-  // A row outside the tile or with an index outside [0, a_rows) gets zero
-  // scales (so it reads as zeros); a W row past N keeps row 0's data: those
-  // output columns are never stored.
-  const uint32_t a_mask = a_ok ? 0xFFFFu : 0u;
-
-  auto load_step = [&](int s, RowLoad& ta, RowLoad& tb) {
-    ta.codes = *reinterpret_cast<const u32x4*>(a_cp + s * (BK / 2));
-    ta.scales = *reinterpret_cast<const uint16_t*>(a_sp + s * (BK / 16));
-    tb.codes = *reinterpret_cast<const u32x4*>(b_cp + s * (BK / 2));
-    tb.scales = *reinterpret_cast<const uint16_t*>(b_sp + s * (BK / 16));
-  };
-
-  auto stage_write = [&](int st, const RowLoad& ta, const RowLoad& tb) {
-    unsigned char* base = smem + st * STAGE;
-    const int a_slot = tid < BM ? tid : BM;                   // BM: the spare row
-    *reinterpret_cast<u32x4*>(base + A_CODES + a_slot * 16) = ta.codes;
-    *reinterpret_cast<uint16_t*>(base + A_SC + a_slot * 2) = (uint16_t)(ta.scales & a_mask);
-    *reinterpret_cast<u32x4*>(base + B_CODES + tid * 16) = tb.codes;
-    *reinterpret_cast<uint16_t*>(base + B_SC + tid * 2) = (uint16_t)tb.scales;
-  };
-
-  // ---- compensation set-up: selected channels, their K-step ranges, zero W_S
-  if (comp) {
+#pragma unroll
+  for (int i = 0; i < L::PW; ++i) {
+    const int b = wave * L::PW + i;
+    const int r = (b < L::NW ? b : 0) * 16 + lr;
+    b_chk[i] = lp ^ swz(r);
+    b_off[i] = (uint32_t)(w_row(r) * rbytes) + (uint32_t)(b_chk[i] << 4);
+  }
+  // scale loads: word position P = 64 b + l holds, in the read order
+  // ((wm 2 + h) 32 + l32) MI + i, word h of A row wm MI 32 + 32 i + l32
+  // (likewise NJ / wn for W)
+  uint32_t as_off[L::PAS], bs_off[L::PWS];
+  int as_h[L::PAS], bs_h[L::PWS];
+#pragma unroll
+  for (int i = 0; i < L::PAS; ++i) {
+    const int b = wave * L::PAS + i;
+    const int P = (b < L::NAS ? b : 0) * 64 + lane;
+    const int ii = P % MI, ll = (P / MI) % 32, hh = (P / (MI * 32)) % 2, ww = P / (MI * 64);
+    as_h[i] = hh;
+    as_off[i] = (uint32_t)(a_row(ww * MI * 32 + ii * 32 + ll) * sbytes) + (uint32_t)(hh * 4);
+  }
+#pragma unroll
+  for (int i = 0; i < L::PWS; ++i) {
+    const int b = wave * L::PWS + i;
+    const int P = (b < L::NWS ? b : 0) * 64 + lane;
+    const int jj = P % NJ, ll = (P / NJ) % 32, hh = (P / (NJ * 32)) % 2, ww = P / (NJ * 64);
+    bs_h[i] = hh;
+    bs_off[i] = (uint32_t)(w_row(ww * NJ * 32 + jj * 32 + ll) * sbytes) + (uint32_t)(hh * 4);
+  }
+  // A rows whose index lies outside [0, a_rows) read as zeros: their scale
+  // words are masked (per fragment row, fixed for the tile)
+  uint32_t amask[MI];
+#pragma unroll
+  for (int i = 0; i < MI; ++i) {
+    const int r = wm * MI * 32 + i * 32 + l32;
+    const int64_t ar = a_index(r);
+    amask[i] = (r < rows_valid && (ar < 0 || ar >= p.a_rows)) ? 0u : ~0u;
+  }
+  if constexpr (COMP) {
     for (int j = tid; j < kc; j += 256) {
-      int32_t c = p.sel_idx[(int64_t)e * kc + j];
+      const int32_t c = p.sel_idx[(int64_t)e * kc + j];
       sel[j] = c < 0 ? 0 : (c >= K ? (int32_t)(K - 1) : c);
     }
-    for (int i = tid; i < BN * ws_stride / 8; i += 256)
-      reinterpret_cast<u32x4*>(WS)[i] = u32x4{0, 0, 0, 0};
-    __syncthreads();
-    // jr[s]: the first j with sel[j] in pipeline stage s or later
-    constexpr int KSTEP = kMacro ? MacroLayout<BM>::KM : BK;
-    const int nst = kMacro ? (int)((K + KSTEP - 1) / KSTEP) : nsteps;
-    for (int s = tid; s <= nst; s += 256) {
-      int lo = 0, hi = kc;
-      while (lo < hi) {
-        int mid = (lo + hi) >> 1;
-        if (sel[mid] < s * KSTEP) lo = mid + 1; else hi = mid;
-      }
-      jr[s] = lo;
+    // the padding channels kc .. 16 KQ - 1 of W_S are zero (every selected
+    // channel is written by the gather)
+    for (int i = tid; i < BN * (KQ * 16 - kc); i += 256) {
+      const int r = i / (KQ * 16 - kc), c = kc + i % (KQ * 16 - kc);
+      WS[r * WSS + c] = (_Float16)0.0f;
     }
   }
+  if constexpr (EPI == 2) {
+    if (tid < BM) RW[tid] = tid < rows_valid ? p.row_weight[row0 + tid] : 0.0f;
+  }
+  if constexpr (COMP) {
+    __syncthreads();
+    // gather table of stage s (stages nst and nst + 1 are empty)
+    auto lower = [&](int64_t c) {           // first j with sel[j] >= c
+      int lo = 0, hi = kc;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (sel[mid] < c) lo = mid + 1; else hi = mid;
+      }
+      return lo;
+    };
+    for (int s = tid; s <= nst + 1; s += 256) {
+      const int j0 = lower((int64_t)s * KS), n = lower((int64_t)(s + 1) * KS) - j0;
+      uint32_t kk = 0;
+      for (int q = 0; q < 4 && q < n; ++q) kk |= (uint32_t)((sel[j0 + q] - s * KS) & 0x7F) << (8 * q);
+      tab[s] = u32x2{(uint32_t)j0 | ((uint32_t)n << 8), kk};
+    }
+  }
+
+  // The LPW load instructions of stage m into slot `slot`.  In the half-full
+  // last stage (K % 128 == 64) the chunks and the scale word past K are read
+  // from the row's first half instead (their scales are zeroed when read), so
+  // no load leaves its row.
+  auto issue = [&](int m, int slot) {
+    unsigned char* base = smem + slot * STAGE;
+    const uint8_t* ac = a_codes + (int64_t)m * 64;
+    const uint8_t* wc = wc_e + (int64_t)m * 64;
+    const uint8_t* as = a_scales + (int64_t)m * 8;
+    const uint8_t* wsb = ws_e + (int64_t)m * 8;
+    if (m != mh) {
+#pragma unroll
+      for (int i = 0; i < L::PA; ++i) {
+        const int b = wave * L::PA + i;
+        load_lds16(ac, a_off[i], b < L::NA ? base + L::A_OFF + b * 1024 : DUMMY);
+      }
+#pragma unroll
+      for (int i = 0; i < L::PW; ++i) {
+        const int b = wave * L::PW + i;
+        load_lds16(wc, b_off[i], b < L::NW ? base + L::B_OFF + b * 1024 : DUMMY);
+      }
+#pragma unroll
+      for (int i = 0; i < L::PAS; ++i) {
+        const int b = wave * L::PAS + i;
+        load_lds4(as, as_off[i], b < L::NAS ? base + L::AS_OFF + b * 256 : DUMMY);
+      }
+#pragma unroll
+      for (int i = 0; i < L::PWS; ++i) {
+        const int b = wave * L::PWS + i;
+        load_lds4(wsb, bs_off[i], b < L::NWS ? base + L::BS_OFF + b * 256 : DUMMY);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < L::PA; ++i) {
+        const int b = wave * L::PA + i;
+        load_lds16(ac, a_off[i] - (uint32_t)((a_chk[i] & 2) << 4),
+                   b < L::NA ? base + L::A_OFF + b * 1024 : DUMMY);
+      }
+#pragma unroll
+      for (int i = 0; i < L::PW; ++i) {
+        const int b = wave * L::PW + i;
+        load_lds16(wc, b_off[i] - (uint32_t)((b_chk[i] & 2) << 4),
+                   b < L::NW ? base + L::B_OFF + b * 1024 : DUMMY);
+      }
+#pragma unroll
+      for (int i = 0; i < L::PAS; ++i) {
+        const int b = wave * L::PAS + i;
+        load_lds4(as, as_off[i] - (uint32_t)(as_h[i] * 4), b < L::NAS ? base + L::AS_OFF + b * 256 : DUMMY);
+      }
+#pragma unroll
+      for (int i = 0; i < L::PWS; ++i) {
+        const int b = wave * L::PWS + i;
+        load_lds4(wsb, bs_off[i] - (uint32_t)(bs_h[i] * 4), b < L::NWS ? base + L::BS_OFF + b * 256 : DUMMY);
+      }
+    }
+  };
+
+  // Q(R_S) codes of the tile's rows (a contiguous byte range of r_codes) go
+  // into LDS by direct loads ahead of the stages (4 bytes a lane; sources past
+  // the end of r_codes read its first word: those rows are never stored).
+  // Their scale bytes go into registers (used after the K loop): in
+  // compensation substep q (16 compact channels) lane half h takes channels
+  // 16 q + 8 h .. + 7, i.e. code word 2 q + h of the row and scale byte q.
+  constexpr int KQW = COMP ? KQ : 1;
+  uint32_t rqs[MI][(KQW + 3) / 4];
+  if constexpr (COMP) {
+    const uint32_t rrow = (uint32_t)(kc / 2);                   // code bytes per row
+    const int64_t rbase = row0 * rrow, rend = p.rows_total * rrow;
+    const int nword = BM * (kc / 8);                            // words of the tile
+    for (int w0 = wave * 64; w0 < nword; w0 += 256) {           // uniform trip count per wave
+      const int64_t src = rbase + 4 * (int64_t)(w0 + lane);
+      load_lds4(p.r_codes, (uint32_t)(src + 4 <= rend ? src : 0), RSC + 4 * w0);
+    }
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int r = wm * MI * 32 + i * 32 + l32;
+      const bool live = r < rows_valid;
+      const int64_t ur = row0 + (live ? r : 0);
+#pragma unroll
+      for (int w = 0; w < (KQ + 3) / 4; ++w) {
+        uint32_t v = 0;
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+          if (live && 16 * (4 * w + b) < kc) v |= (uint32_t)p.r_scales[ur * (kc / 16) + 4 * w + b] << (8 * b);
+        rqs[i][w] = v;
+      }
+    }
+  }
+
+  // the first NSLOT stages go out (stages past the end repeat the last one
+  // into slots nobody reads, so every wave issues the same count)
+#pragma unroll
+  for (int q = 0; q < NSLOT; ++q) issue(q < nst ? q : nst - 1, q);
+
+  // W_S gather of a stage: thread t copies the selected channels of weight
+  // row t that fall in the stage, as exact fp16 values.  Weight row t's
+  // 16-byte chunk c of a stage sits at t * 64 + ((c ^ swz(t)) << 4) (so the
+  // chunk reads of 8 consecutive rows hit distinct banks, as the fragment
+  // reads do; single-byte reads down a column of rows 64 bytes apart would
+  // conflict 16 ways), its scale word h at position ((wn 2 + h) 32 + l32) NJ
+  // + j for t = wn NJ 32 + 32 j + l32.  The first four channels of a stage
+  // come from the gather table: their chunk and scale-word reads are issued
+  // right after the barrier that makes the stage visible, and the code
+  // nibble and scale byte are picked out (uniform positions) and written to
+  // W_S two substeps later, so nothing waits on LDS latency.  More than four
+  // channels in one stage take a slower loop.
+  const uint32_t g_row = (uint32_t)(L::B_OFF + tid * 64);
+  const int g_sw = swz(tid);
+  const uint32_t g_srow = (uint32_t)(L::BS_OFF + (((tid / (NJ * 32)) * 2 * 32 + tid % 32) * NJ + (tid % (NJ * 32)) / 32) * 4);
+  auto g_chunk = [&](const unsigned char* base, int kk) {
+    return *reinterpret_cast<const u32x4*>(base + g_row + ((((kk >> 5) ^ g_sw)) << 4));
+  };
+  auto g_sword = [&](const unsigned char* base, int kk) {
+    return *reinterpret_cast<const uint32_t*>(base + g_srow + (kk >> 6) * 32 * NJ * 4);
+  };
+  // code nibble of K-offset kk from its chunk, scale byte from its word
+  // (kk uniform: the selects and shifts take scalar operands)
+  auto g_code = [&](const u32x4& ch, int kk) {
+    const int u = (kk & 31) >> 3;
+    const uint32_t w01 = (u & 1) ? ch[1] : ch[0], w23 = (u & 1) ? ch[3] : ch[2];
+    return ((u & 2) ? w23 : w01) >> (4 * (kk & 7)) & 15u;
+  };
+  auto g_sbyte = [&](uint32_t w, int kk) { return (w >> (8 * ((kk >> 4) & 3))) & 0xFFu; };
+  auto ws_value = [&](uint32_t code, uint32_t sbyte) {
+    const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0);
+    const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbyte, 1.0f, false);
+    return (_Float16)(v[0] * sc[0]);                          // exact: see the header
+  };
+  struct Gather {
+    u32x4 chunk[4];
+    uint32_t sword[4];
+    int j0, n, kk[4];
+  };
+  auto gather_read = [&](int slot, u32x2 t, Gather& g) {
+    const unsigned char* base = smem + slot * STAGE;
+    g.j0 = __builtin_amdgcn_readfirstlane((int)(t[0] & 0xFFu));
+    g.n = __builtin_amdgcn_readfirstlane((int)(t[0] >> 8));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      g.kk[q] = __builtin_amdgcn_readfirstlane((int)((t[1] >> (8 * q)) & 0x7Fu));
+      g.chunk[q] = g_chunk(base, g.kk[q]);
+      g.sword[q] = g_sword(base, g.kk[q]);
+    }
+  };
+  // entries past the stage's count go to the row's padding halves (no
+  // branch: this runs beside MFMAs)
+  auto gather_write = [&](const Gather& g) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      WS[tid * WSS + (q < g.n ? g.j0 + q : KQ * 16 + q)] =
+          ws_value(g_code(g.chunk[q], g.kk[q]), g_sbyte(g.sword[q], g.kk[q]));
+  };
+  // channels past the first four of a stage (rare; at the end of the stage)
+  auto gather_rest = [&](int m, int slot, const Gather& g) {
+    if (g.n > 4) {                                            // uniform
+      const unsigned char* base = smem + slot * STAGE;
+      for (int jj = g.j0 + 4; jj < g.j0 + g.n; ++jj) {
+        const int kk = sel[jj] - m * KS;
+        if ((unsigned)kk < (unsigned)KS)                      // false only if sel is not ascending
+          WS[tid * WSS + jj] = ws_value(g_code(g_chunk(base, kk), kk), g_sbyte(g_sword(base, kk), kk));
+      }
+    }
+  };
 
   f32x16 acc[MI][NJ];
 #pragma unroll
@@ -279,394 +486,186 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.0f;
 
-  // A wave's dequantized fragments of one K-step: a0/b0 feed MFMA substep 0,
-  // a1/b1 substep 1.
-  struct Frags {
-    f16x8 a0[MI], a1[MI], b0[NJ], b1[NJ];
-  };
-  auto read_frags = [&](int st, Frags& f) {
-    const unsigned char* base = smem + st * STAGE;
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int r = wm * MI * 32 + i * 32 + l32;
-      const u32x2 c = *reinterpret_cast<const u32x2*>(base + A_CODES + r * 16 + half * 8);
-      dequant16(c, e4m3_f16x2(base[A_SC + r * 2 + half]), f.a0[i], f.a1[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int r = wn * NJ * 32 + j * 32 + l32;
-      const u32x2 c = *reinterpret_cast<const u32x2*>(base + B_CODES + r * 16 + half * 8);
-      dequant16(c, e4m3_f16x2(base[B_SC + r * 2 + half]), f.b0[j], f.b1[j]);
-    }
-  };
-  auto mfma_step = [&](const Frags& f) {
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a0[i], f.b0[j], acc[i][j], 0, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NJ; ++j)
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(f.a1[i], f.b1[j], acc[i][j], 0, 0, 0);
-  };
-
-  // W elements of the selected channels inside K-step s (LDS stage st) into
-  // W_S: thread t handles weight row t of the tile, so the loop count is the
-  // same for every thread.
-  auto gather_ws = [&](int s, int st) {
-    const unsigned char* base = smem + st * STAGE;
-    const int j1 = jr[s + 1];
-    for (int jj = jr[s]; jj < j1; ++jj) {
-      const int kk = sel[jj] - s * BK;                       // 0..31 inside the step
-      const uint32_t byte = base[B_CODES + tid * 16 + (kk >> 1)] >> (4 * (kk & 1));
-      const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(byte, 1.0f, 0);
-      const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(base[B_SC + tid * 2 + (kk >> 4)], 1.0f, false);
-      WS[tid * ws_stride + jj] = v[0] * sc[0];               // exact: see the header
-    }
-  };
-
-  // ---- 128-K pipeline of the 32-row tile (MacroTile) -----------------------
-  // Stage m covers K [128 m, 128 m + 128): code bytes [64 m, 64 m + 64) and
-  // scale bytes [8 m, 8 m + 8) of every row.  Thread t loads the 16 code bytes
-  // 16 (t % 4) .. of W rows t / 4 + 64 i (i = 0..3) and of A row t / 4, and
-  // the 8 scale bytes of W row t and A row t; threads past the tile's A rows
-  // load row 0 and write the spare LDS row.  When K is not a multiple of 128
-  // the last stage is half full: its missing code bytes are read from the
-  // row's start and its missing blocks get scale 0 in A and W, so they add
-  // nothing.  Two LDS stages and two register sets: in stage m a wave reads
-  // its raw fragments of stage m, writes the data of stage m + 1 into the
-  // other LDS stage and issues the loads of stage m + 3 into the register set
-  // just written, so loads have two stages (256 K) to arrive.
-  //
-  // K order of one stage: MFMA substep q (0..7) takes, in lane half h, the 8
-  // codes 8 (q % 4) .. of 16-byte granule 2 (q / 4) + h (granule G holds
-  // blocks 2G and 2G + 1), the same in A and W, so every k of the stage is
-  // summed once.
-  auto macro_loop = [&](auto&& park) {
-    using ML = MacroLayout<BM>;
-    constexpr int KM = ML::KM, ROW = ML::ROW, AO = ML::A_OFF, BO = ML::B_OFF;
-    typedef uint32_t u32x2a __attribute__((ext_vector_type(2), aligned(4)));
-    const int nmac = (int)((K + KM - 1) / KM);
-    const int mlast = nmac - 1;
-    const bool half_last = (K % KM) != 0;
-    const int g4 = tid & 3;
-    const int64_t rbytes = K / 2;
-    int64_t ac = 0;                            // A row of the code loads: tile row tid / 4
-    if ((tid >> 2) < rows_valid) {
-      const int64_t ur = row0 + (tid >> 2);
-      ac = p.a_row_index ? (int64_t)p.a_row_index[ur] : ur;
-      if (ac < 0 || ac >= p.a_rows) ac = 0;    // its scales (row tid / 4's) are zero
-    }
-    const uint8_t* a_cm = p.a_codes + ac * rbytes + g4 * 16;
-    const uint8_t* b_cm[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t br = weight_row<BN>(p, n_tile, i * 64 + (tid >> 2));
-      b_cm[i] = p.w_codes + ((int64_t)e * p.N + (br >= 0 ? br : 0)) * rbytes + g4 * 16;
-    }
-    const uint32_t am32 = a_mask ? 0xFFFFFFFFu : 0u;
-
-    struct MacLoad {
-      u32x4 wc[4], ac;
-      u32x2 ws, as;
-    };
-    auto mload = [&](int m, MacLoad& r) {
-      const int64_t cb = (int64_t)m * 64;
-      const int64_t co = cb + g4 * 16 < rbytes ? cb : -(int64_t)g4 * 16;   // past K: row start
-      const bool part = half_last && m == mlast;
-      const int64_t so = part ? (int64_t)m * 8 - 4 : (int64_t)m * 8;      // 4 valid bytes: the high half
-#pragma unroll
-      for (int i = 0; i < 4; ++i) r.wc[i] = *reinterpret_cast<const u32x4*>(b_cm[i] + co);
-      r.ac = *reinterpret_cast<const u32x4*>(a_cm + co);
-      const u32x2a ws = *reinterpret_cast<const u32x2a*>(b_sp + so);
-      const u32x2a as = *reinterpret_cast<const u32x2a*>(a_sp + so);
-      r.ws = part ? u32x2{ws[1], 0u} : u32x2{ws[0], ws[1]};
-      r.as = part ? u32x2{as[1] & am32, 0u} : u32x2{as[0] & am32, as[1] & am32};
-    };
-    auto mwrite = [&](int st, const MacLoad& r) {
-      unsigned char* base = smem + st * STAGE;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        unsigned char* d = base + BO + (i * 64 + (tid >> 2)) * ROW + g4 * 16;
-        *reinterpret_cast<u32x2*>(d) = u32x2{r.wc[i][0], r.wc[i][1]};
-        *reinterpret_cast<u32x2*>(d + 8) = u32x2{r.wc[i][2], r.wc[i][3]};
-      }
-      *reinterpret_cast<u32x2*>(base + BO + tid * ROW + 64) = r.ws;
-      unsigned char* da = base + AO + ((tid >> 2) < BM ? (tid >> 2) : BM) * ROW + g4 * 16;
-      *reinterpret_cast<u32x2*>(da) = u32x2{r.ac[0], r.ac[1]};
-      *reinterpret_cast<u32x2*>(da + 8) = u32x2{r.ac[2], r.ac[3]};
-      *reinterpret_cast<u32x2*>(base + AO + (tid < BM ? tid : BM) * ROW + 64) = r.as;
-    };
-    // A fragment row's raw data of a stage: granules h and 2 + h, and the
-    // scale pairs of their blocks as fp16 ({2h, 2h+1} and {4+2h, 5+2h})
-    struct RawRow {
-      u32x2 g0a, g0b, g1a, g1b;
-      f16x2 s0, s1;
-    };
-    auto read_raw = [&](const unsigned char* row, RawRow& o) {
-      o.g0a = *reinterpret_cast<const u32x2*>(row + half * 16);
-      o.g0b = *reinterpret_cast<const u32x2*>(row + half * 16 + 8);
-      o.g1a = *reinterpret_cast<const u32x2*>(row + 32 + half * 16);
-      o.g1b = *reinterpret_cast<const u32x2*>(row + 32 + half * 16 + 8);
-      const u32x2 sc = *reinterpret_cast<const u32x2*>(row + 64);
-      o.s0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[0] >> (16 * half), 1.0f, false);
-      o.s1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sc[1] >> (16 * half), 1.0f, false);
-    };
-    auto frag_q = [&](const RawRow& o, int q) {
-      const u32x2 g = q < 4 ? ((q & 2) ? o.g0b : o.g0a) : ((q & 2) ? o.g1b : o.g1a);
-      const f16x2 sp = q < 4 ? o.s0 : o.s1;
-      const _Float16 sv = (q & 2) ? sp[1] : sp[0];
-      return dequant8(g[q & 1], f16x2{sv, sv});
-    };
-    auto gather_ws_m = [&](int m, int st) {
-      const unsigned char* row = smem + st * STAGE + BO + tid * ROW;
-      const int j1 = jr[m + 1];
-      for (int jj = jr[m]; jj < j1; ++jj) {
-        const int kk = sel[jj] - m * KM;                      // 0..127 inside the stage
-        const uint32_t byte = row[kk >> 1] >> (4 * (kk & 1));
-        const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(byte, 1.0f, 0);
-        const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(row[64 + (kk >> 4)], 1.0f, false);
-        WS[tid * ws_stride + jj] = v[0] * sc[0];
-      }
-    };
-    auto mstep = [&](int m, int st, MacLoad& rset) {
-      const unsigned char* base = smem + st * STAGE;
-      RawRow ra_, rb_[NJ];
-      read_raw(base + AO + l32 * ROW, ra_);
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) read_raw(base + BO + (wn * NJ * 32 + j * 32 + l32) * ROW, rb_[j]);
-      if (comp) gather_ws_m(m, st);
-      mwrite(st ^ 1, rset);                     // data of stage m + 1
-      mload(m + 3 < nmac ? m + 3 : mlast, rset);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        const f16x8 fa = frag_q(ra_, q);
-#pragma unroll
-        for (int j = 0; j < NJ; ++j)
-          acc[0][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa, frag_q(rb_[j], q), acc[0][j], 0, 0, 0);
-      }
-    };
-
-    MacLoad R0, R1;
-    mload(0, R0);
-    mload(1 < nmac ? 1 : mlast, R1);
-    park();
-    mwrite(0, R0);
-    mload(2 < nmac ? 2 : mlast, R0);
-    lds_barrier();
-    int m = 0;
-    for (; m + 2 <= nmac; m += 2) {
-      mstep(m, 0, R1);
-      lds_barrier();
-      mstep(m + 1, 1, R0);
-      lds_barrier();
-    }
-    if (m < nmac) {
-      mstep(m, 0, R1);
-      lds_barrier();
-    }
-  };
-
-  // ---- main K loop ----------------------------------------------------------
-  // Step s: MFMAs on the fragments of step s (registers), while the fragments
-  // of step s+1 are read from LDS stage (s+1)%2 and dequantized (and the
-  // selected W columns of step s+1 copied into W_S), the raw data of step s+2
-  // goes from register set s%PD into stage s%2 and the loads of step s+2+PD
-  // are issued into that set: PD K-steps between a load and its use.  Small
-  // tiles (BM <= 64) have short K-steps, so they keep more loads in flight
-  // (PD = 4) to cover the memory latency; large tiles use PD = 2.
-  // One barrier per step: it orders this step's writes of stage s%2 before
-  // the next step's reads of it, and this step's reads of stage (s+1)%2
-  // before the next step's writes.  Every load is issued unconditionally (a step past
-  // the end re-reads the last step; its stage is never read), so the compiler
-  // waits only for the older step's loads.  K is a multiple of 64, so nsteps
-  // is even and at least 2, and the loop, unrolled by PD (plus two steps when
-  // nsteps % PD == 2), sees each stage and register set at a fixed place.
-  constexpr int PD = BM <= 64 ? 4 : 2;
-  RowLoad ra[PD], rb[PD];
-  const int last = nsteps - 1;
-  // The Q(R_S) rows are loaded with the first K-steps (loads complete in
-  // order, so they are in once steps 0 and 1 are) and parked in LDS before
-  // the K loop: the compensation chunk after it waits for no global memory.
-  constexpr int kMaxChunks = MAX_KC / BK;
-  const int nchunk = nchunk_of(kcp);
-  u32x4 rq_codes[kMaxChunks];
-  uint32_t rq_sc[kMaxChunks];
-  if (comp) {
-    const bool ok = tid < rows_valid;
-    const int64_t ur = row0 + (ok ? tid : 0);
-#pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      rq_codes[c] = u32x4{0, 0, 0, 0};
-      rq_sc[c] = 0;
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int j = c * BK + q * 16;
-        if (ok && j < kc) {
-          const u32x2 w = *reinterpret_cast<const u32x2*>(p.r_codes + ur * (kc / 2) + j / 2);
-          rq_codes[c][2 * q] = w[0];
-          rq_codes[c][2 * q + 1] = w[1];
-          rq_sc[c] |= (uint32_t)p.r_scales[ur * (kc / 16) + j / 16] << (8 * q);
-        }
-      }
-    }
-  }
-  float rw = 0.0f;
-  if (EPI == 2 && tid < rows_valid) rw = p.row_weight[row0 + tid];
-  auto park_rows = [&]() {                    // row weights and Q(R_S) rows into LDS
-    if (EPI == 2 && tid < BM) RW[tid] = rw;
-    if (comp && tid < BM) {
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) {
-        if (c < nchunk) {
-          *reinterpret_cast<u32x4*>(RS + c * (BM * 18) + tid * 16) = rq_codes[c];
-          *reinterpret_cast<uint16_t*>(RS + c * (BM * 18) + BM * 16 + tid * 2) = (uint16_t)rq_sc[c];
-        }
-      }
-    }
-  };
-  if constexpr (kMacro) {
-    macro_loop(park_rows);
-  } else {
-  load_step(0, ra[0], rb[0]);
-  load_step(1, ra[1], rb[1]);
-  stage_write(0, ra[0], rb[0]);
-  stage_write(1, ra[1], rb[1]);
-  park_rows();
-  load_step(2 < last ? 2 : last, ra[0], rb[0]);
-#pragma unroll
-  for (int i = 1; i < PD; ++i) {
-    __builtin_amdgcn_sched_barrier(0);        // keep the loop's load order in the prologue
-    load_step(2 + i < last ? 2 + i : last, ra[i], rb[i]);
-  }
-  lds_barrier();
-  if (comp) gather_ws(0, 0);
+  // Per-lane LDS offsets of the fragment reads: row r = (wm MI or wn NJ) 32 +
+  // 32 i + l32, whose swizzle depends on l32 only; chunk 2 half + t.
+  const int sw = swz(l32);
+  const uint32_t fa_off[2] = {(uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 64 + (((2 * half) ^ sw) << 4)),
+                              (uint32_t)(L::A_OFF + (wm * MI * 32 + l32) * 64 + (((2 * half + 1) ^ sw) << 4))};
+  const uint32_t fb_off[2] = {(uint32_t)(L::B_OFF + (wn * NJ * 32 + l32) * 64 + (((2 * half) ^ sw) << 4)),
+                              (uint32_t)(L::B_OFF + (wn * NJ * 32 + l32) * 64 + (((2 * half + 1) ^ sw) << 4))};
+  const uint32_t sa_off = (uint32_t)(L::AS_OFF + ((wm * 2 + half) * 32 + l32) * MI * 4);
+  const uint32_t sb_off = (uint32_t)(L::BS_OFF + ((wn * 2 + half) * 32 + l32) * NJ * 4);
 
   auto main_loop = [&](auto ma_c) {
-  constexpr int MA = decltype(ma_c)::value;
-  // fragment f of the step is read and dequantized only if some MFMA uses it
-  auto frag_live = [&](int f) { return f < MI ? f < MA : MA > 0; };
-  Frags fr[2];
-  {
-    const unsigned char* base = smem;                          // stage 0: fragments of step 0
-#pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      if (i >= MA) continue;
-      const int r = wm * MI * 32 + i * 32 + l32;
-      const u32x2 c = *reinterpret_cast<const u32x2*>(base + A_CODES + r * 16 + half * 8);
-      dequant16(c, e4m3_f16x2(base[A_SC + r * 2 + half]), fr[0].a0[i], fr[0].a1[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      if (MA == 0) continue;
-      const int r = wn * NJ * 32 + j * 32 + l32;
-      const u32x2 c = *reinterpret_cast<const u32x2*>(base + B_CODES + r * 16 + half * 8);
-      dequant16(c, e4m3_f16x2(base[B_SC + r * 2 + half]), fr[0].b0[j], fr[0].b1[j]);
-    }
-  }
-  // Step 0 overwrites stage 0 (with the data of step 2) once every wave has
-  // read its step-0 fragments from it; waves with fewer live fragments get
-  // there sooner.
-  lds_barrier();
+    constexpr int MA = decltype(ma_c)::value;       // live A fragments of this wave (0 .. MI)
+    constexpr int NB = MA > 0 ? NJ : 0;             // live W fragments
+    // raw fragments of the current stage: RA[i][t] = chunk 2 half + t of row i
+    u32x4 RA[MI][2], RB[NJ][2];
+    uint32_t SWA[MI], SWB[NJ];                      // scale words of the next stage
+    f16x2 SCA[MI][2], SCB[NJ][2];                   // scale pairs of the current stage
+    f16x8 DA[2][MI], DB[2][NJ];                     // dequantized operands, by substep parity
 
-  // One K-step in issue order: the MFMAs of this step one at a time, and
-  // between them (each group fenced off from the scheduler) the rest of the
-  // step's work: the LDS reads of the next step's fragments right after MFMA
-  // 0, the stage writes after MFMA 1, the global loads after MFMA 2, and the
-  // dequantization of the next step's fragments, half a fragment (8 VALU
-  // instructions, about one MFMA's duration) per MFMA from MFMA kDeq0 on.
-  constexpr int kFr = MI + NJ;                // fragments per wave and step
-  constexpr int kMf = 2 * MI * NJ;            // MFMAs per wave and step
-  constexpr int kDeq0 = kMf > 8 ? 4 : 3;
-  auto step = [&](int s, int st, const Frags& cur, Frags& nxt, RowLoad& ta, RowLoad& tb) {
-    const unsigned char* nb = smem + (st ^ 1) * STAGE;       // stage of step s+1
-    u32x2 rc[kFr];
-    uint32_t rs[kFr];
-    f16x2 sc[kFr];
+    auto read_raw = [&](int slot, auto t_c) {
+      constexpr int T = decltype(t_c)::value;
+      const unsigned char* base = smem + slot * STAGE;
 #pragma unroll
-    for (int m = 0; m < kMf; ++m) {
+      for (int i = 0; i < MA; ++i) RA[i][T] = *reinterpret_cast<const u32x4*>(base + fa_off[T] + i * 2048);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) RB[j][T] = *reinterpret_cast<const u32x4*>(base + fb_off[T] + j * 2048);
+    };
+    auto read_words = [&](const unsigned char* ptr, uint32_t* w, auto n_c) {
+      constexpr int n = decltype(n_c)::value;
+      if constexpr (n == 4) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(ptr);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+      } else if constexpr (n == 2) {
+        const u32x2 v = *reinterpret_cast<const u32x2*>(ptr);
+        w[0] = v[0]; w[1] = v[1];
+      } else {
+        w[0] = *reinterpret_cast<const uint32_t*>(ptr);
+      }
+    };
+    // scale words of a stage from its slot (used a long while later)
+    auto read_scales = [&](int slot) {
+      if constexpr (MA > 0) {
+        const unsigned char* base = smem + slot * STAGE;
+        read_words(base + sa_off, SWA, IntC<MI>{});
+        read_words(base + sb_off, SWB, IntC<NJ>{});
+      }
+    };
+    // scale pairs of stage m: in the half-full last stage the words of lane
+    // half 1 (blocks past K) are zero, and rows with a bad index have zero
+    // scales
+    auto convert_scales = [&](int m) {
+      const uint32_t hm = (m == mh && half) ? 0u : ~0u;
+#pragma unroll
+      for (int i = 0; i < MA; ++i) {
+        const uint32_t w = SWA[i] & hm & amask[i];
+        SCA[i][0] = scale_pair<0>(w);
+        SCA[i][1] = scale_pair<1>(w);
+      }
+#pragma unroll
+      for (int j = 0; j < NB; ++j) {
+        const uint32_t w = SWB[j] & hm;
+        SCB[j][0] = scale_pair<0>(w);
+        SCB[j][1] = scale_pair<1>(w);
+      }
+    };
+    // operands of substep q = 4 t + u into buffer D[q & 1]
+    auto dequant = [&](auto q_c) {
+      constexpr int Q = decltype(q_c)::value, T = Q / 4, U = Q % 4, B = Q & 1;
+#pragma unroll
+      for (int i = 0; i < MA; ++i) DA[B][i] = dequant8(RA[i][T][U], SCA[i][T][U >> 1]);
+#pragma unroll
+      for (int j = 0; j < NB; ++j) DB[B][j] = dequant8(RB[j][T][U], SCB[j][T][U >> 1]);
+    };
+    auto mfmas = [&](auto q_c) {
+      constexpr int B = decltype(q_c)::value & 1;
+#pragma unroll
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int i = 0; i < MA; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(DA[B][i], DB[B][j], acc[i][j], 0, 0, 0);
+    };
+    // one substep: the MFMAs of q with the dequantization of q + 1 (in the
+    // last substep, of the next stage's first) between them
+    constexpr int NMF = MA * NB;
+    constexpr int NVALU = 8 * (MA + NB);
+    // The dequantized operands are pinned at the end of their substep (an
+    // empty asm that takes them): without it the compiler may sink the
+    // dequantization past a later branch of the stage, next to its MFMAs,
+    // and the substep's MFMAs would run with no VALU work beside them.
+    auto pin = [&](auto q_c) {
+      constexpr int B = decltype(q_c)::value & 1;
+      pin_regs<MA>(DA[B]);
+      pin_regs<NB>(DB[B]);
+    };
+    auto substep = [&](auto q_c, auto next_c, auto&& extra, auto extra_valu) {
+      mfmas(q_c);
+      dequant(next_c);
+      extra();
+      if constexpr (NMF > 0) {
+        constexpr int V = NVALU + decltype(extra_valu)::value;
+#pragma unroll
+        for (int k = 0; k < NMF; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (V + NMF - 1) / NMF, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-      {
-        const int sub = m / (MI * NJ), j = (m % (MI * NJ)) / MI, i = m % MI;
-        if (i < MA)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(sub ? cur.a1[i] : cur.a0[i],
-                                                             sub ? cur.b1[j] : cur.b0[j],
-                                                             acc[i][j], 0, 0, 0);
-      }
-      if (m == 0) {
-#pragma unroll
-        for (int f = 0; f < kFr; ++f) {
-          if (!frag_live(f)) continue;
-          const int r = f < MI ? wm * MI * 32 + f * 32 + l32 : wn * NJ * 32 + (f - MI) * 32 + l32;
-          const int co = f < MI ? A_CODES : B_CODES, so = f < MI ? A_SC : B_SC;
-          rc[f] = *reinterpret_cast<const u32x2*>(nb + co + r * 16 + half * 8);
-          rs[f] = nb[so + r * 2 + half];
-        }
-      }
-      if (m == 1) stage_write(st, ta, tb);                    // data of step s+2
-      if (m == 2) load_step(s + 2 + PD < last ? s + 2 + PD : last, ta, tb);
-      if (m >= kDeq0 || kMf <= kDeq0) {
-#pragma unroll
-        for (int hf = 0; hf < 2 * kFr; ++hf) {
-          const int at = kMf <= kDeq0 ? kMf - 1 : kDeq0 + hf * (kMf - kDeq0) / (2 * kFr);
-          if (at != m) continue;
-          const int f = hf >> 1, h = hf & 1;
-          if (!frag_live(f)) continue;
-          // The empty asm statements fix this work to this slot: inputs pass
-          // through one before it (nothing is hoisted to its loads), outputs
-          // after it (nothing is sunk to its use).
-          uint32_t w = rc[f][h];
-          asm volatile("" : "+v"(w));
-          if (h == 0) {
-            uint32_t b = rs[f];
-            asm volatile("" : "+v"(b));
-            sc[f] = e4m3_f16x2(b);
-            asm volatile("" : "+v"(sc[f]));
-          }
-          f16x8 v = dequant8(w, sc[f]);
-          asm volatile("" : "+v"(v));
-          if (f < MI) {
-            if (h == 0) nxt.a0[f] = v; else nxt.a1[f] = v;
-          } else {
-            if (h == 0) nxt.b0[f - MI] = v; else nxt.b1[f - MI] = v;
-          }
-        }
-      }
+      pin(next_c);
+    };
+    auto nothing = [] {};
+
+    // prologue: stage 0 has landed (stages 1 .. NSLOT - 1 may be in flight)
+    wait_vm_lgkm0<(NSLOT - 1) * LPW>();
+    asm volatile("s_barrier" ::: "memory");
+    read_raw(0, IntC<0>{});
+    read_raw(0, IntC<1>{});
+    read_scales(0);
+    [[maybe_unused]] Gather gth;
+    [[maybe_unused]] u32x2 tnext = u32x2{0, 0};
+    if constexpr (COMP) {
+      gather_read(0, tab[0], gth);
+      gather_write(gth);
+      gather_rest(0, 0, gth);
+      tnext = tab[1];
     }
+    convert_scales(0);
+    dequant(IntC<0>{});
     __builtin_amdgcn_sched_barrier(0);
-    if (comp && s + 1 < nsteps) gather_ws(s + 1, st ^ 1);
-  };
-  int s = 0;
-  for (; s + PD <= nsteps; s += PD) {
-    step(s, 0, fr[0], fr[1], ra[0], rb[0]);
-    lds_barrier();
-    step(s + 1, 1, fr[1], fr[0], ra[1], rb[1]);
-    lds_barrier();
-    if constexpr (PD == 4) {
-      step(s + 2, 0, fr[0], fr[1], ra[2], rb[2]);
-      lds_barrier();
-      step(s + 3, 1, fr[1], fr[0], ra[3], rb[3]);
-      lds_barrier();
+
+    int slot = 0;                               // uniform: slot offsets are scalar adds
+    for (int m = 0; m < nst; ++m) {
+      const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
+      substep(IntC<0>{}, IntC<1>{}, nothing, IntC<0>{});
+      substep(IntC<1>{}, IntC<2>{}, nothing, IntC<0>{});
+      substep(IntC<2>{}, IntC<3>{}, nothing, IntC<0>{});
+      // chunk-0 registers are free: stage m + 1 in, stage m + NSLOT out
+      wait_vm_lgkm0<(NSLOT - 2) * LPW>();
+      asm volatile("s_barrier" ::: "memory");
+      issue(m + NSLOT < nst ? m + NSLOT : nst - 1, slot);
+      read_raw(nslot, IntC<0>{});
+      read_scales(nslot);
+      if constexpr (COMP) gather_read(nslot, tnext, gth);
+      __builtin_amdgcn_sched_barrier(0);
+      substep(IntC<3>{}, IntC<4>{}, nothing, IntC<0>{});
+      substep(IntC<4>{}, IntC<5>{}, nothing, IntC<0>{});
+      // the gather reads issued at substep 3 are in by now
+      if constexpr (COMP) {
+        substep(IntC<5>{}, IntC<6>{}, [&] { gather_write(gth); tnext = tab[m + 2]; }, IntC<40>{});
+      } else {
+        substep(IntC<5>{}, IntC<6>{}, nothing, IntC<0>{});
+      }
+      substep(IntC<6>{}, IntC<7>{}, nothing, IntC<0>{});
+      read_raw(nslot, IntC<1>{});
+      __builtin_amdgcn_sched_barrier(0);
+      // the last substep dequantizes the next stage's first operands: its
+      // scale pairs are converted first (the current ones are used up)
+      mfmas(IntC<7>{});
+      convert_scales(m + 1);
+      dequant(IntC<0>{});
+      if constexpr (NMF > 0) {
+#pragma unroll
+        for (int k = 0; k < NMF; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + 2 * (MA + NB) + NMF - 1) / NMF, 0);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      pin(IntC<0>{});
+      if constexpr (COMP) gather_rest(m + 1, nslot, gth);
+      slot = nslot;
     }
-  }
-  if constexpr (PD == 4) {
-    if (s < nsteps) {                          // nsteps % 4 == 2
-      step(s, 0, fr[0], fr[1], ra[0], rb[0]);
-      lds_barrier();
-      step(s + 1, 1, fr[1], fr[0], ra[1], rb[1]);
-      lds_barrier();
-    }
-  }
+    wait_vm_lgkm0<0>();                         // the repeat loads of the last stages
   };
+
   // The number of this wave's 32-row A fragments that hold rows of the tile
   // (0 .. MI): a ragged last m-tile of an expert skips the MFMAs and the
   // dequantization of its empty fragments (a wave with none skips its W
-  // fragments too), with the loop specialized for each count.
-  // The count is the same for every lane of the wave; readfirstlane makes
-  // that visible to the compiler, so the switch is a scalar branch (a
-  // lane-divergent branch around loops holding barriers would be undefined).
+  // fragments too; it still issues its share of the loads), with the loop
+  // specialized for each count.  readfirstlane makes the count visibly
+  // uniform, so the switch is a scalar branch.
   const int ma_rows = rows_valid - wm * MI * 32;
   const int ma = __builtin_amdgcn_readfirstlane(
       ma_rows <= 0 ? 0 : (ma_rows >= MI * 32 ? MI : (ma_rows + 31) / 32));
@@ -677,62 +676,65 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     case 3: if constexpr (MI >= 3) main_loop(IntC<3>{}); break;
     default: main_loop(IntC<MI>{}); break;
   }
-  }
+  __syncthreads();                             // W_S complete; LDS free afterwards
 
-  // ---- compensation chunk ---------------------------------------------------
+  // ---- global scales and the compensation -------------------------------------
   const float ga = p.a_global[p.a_global_per_group ? e : 0];
-  float scale = ga * p.w_global[e];
-  if (comp) {
-    const float gr = p.r_global[e];
-    const float ratio = ga / gr;
+  const float gw = p.w_global[e];
+  float scale = ga * gw;
+  if constexpr (COMP) {
+    const float sa = ga * gw, sr = p.r_global[e] * gw;
+    // per 32 x 32 block the correction corr = sum_q R_q W_S,q (Q(R_S)
+    // operands dequantized per block: few registers beside the accumulators)
+    // and acc = acc * gA gW + corr * gR gW
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int j = 0; j < NJ; ++j) {
+      const int r = wn * NJ * 32 + j * 32 + l32;
+      f16x8 WF[KQ];
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = acc[i][j][q] * ratio;
-    scale = gr * p.w_global[e];
-    // Q(R_S) x W_S over the compact channels (Q(R_S) parked in RS before
-    // the K loop, W_S gathered during it)
-    for (int c = 0; c < nchunk; ++c) {
-      const unsigned char* base = RS + c * (BM * 18);
-      Frags f;
+      for (int q = 0; q < KQ; ++q)
+        WF[q] = *reinterpret_cast<const f16x8*>(WS + r * WSS + 16 * q + 8 * half);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        const int r = wm * MI * 32 + i * 32 + l32;
-        const u32x2 cc = *reinterpret_cast<const u32x2*>(base + r * 16 + half * 8);
-        dequant16(cc, e4m3_f16x2(base[BM * 16 + r * 2 + half]), f.a0[i], f.a1[i]);
-      }
+        const uint32_t* cw = reinterpret_cast<const uint32_t*>(RSC + (wm * MI * 32 + i * 32 + l32) * (kc / 2));
+        f32x16 corr;
 #pragma unroll
-      for (int j = 0; j < NJ; ++j) {            // W_S in the same K order: block half of the chunk
-        const int r = wn * NJ * 32 + j * 32 + l32;
-        f.b0[j] = *reinterpret_cast<const f16x8*>(WS + r * ws_stride + c * BK + half * 16);
-        f.b1[j] = *reinterpret_cast<const f16x8*>(WS + r * ws_stride + c * BK + half * 16 + 8);
+        for (int v = 0; v < 16; ++v) corr[v] = 0.0f;
+        // substeps past kc add zero: their scale bytes are 0 and the
+        // padding channels of W_S are 0 (the code words read stay inside the
+        // Q(R_S) region)
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+          const uint32_t sbyte = (rqs[i][q >> 2] >> (8 * (q & 3))) & 0xFFu;
+          const f16x8 rf = dequant8(cw[2 * q + half], __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbyte, 1.0f, false)[0]);
+          corr = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf, WF[q], corr, 0, 0, 0);
+        }
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * sa + corr[v] * sr;
+        __builtin_amdgcn_sched_barrier(0);      // one block at a time: few live registers
       }
-      mfma_step(f);
     }
+    scale = 1.0f;
+    __syncthreads();                           // W_S reads done before the epilogue staging
   }
 
-  __syncthreads();                             // LDS free for the epilogue staging
   gemm_epilogue<MI, NJ, BN, EPI>(p, acc, tc, wm * MI * 32, wn * NJ * 32, scale,
-                            reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>(), RW);
+                                 reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>(), RW);
 }
 
-template <int MI, int NJ, int WM, int WN, int EPI>
-static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
+template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ>
+static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   constexpr int BM = WM * MI * 32;
   const int64_t mtiles = (a.rows_total + BM - 1) / BM + a.E;
   const int64_t ntiles = a.epilogue == 1 ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
   const int64_t total = mtiles * ntiles;
-  const int kcp = a.sel_idx ? (a.kc + BK - 1) / BK * BK : 0;
-  const size_t stage = stage_bytes<MI, WM>();
-  const size_t loop_lds = NSTAGE * stage + (a.sel_idx ? (size_t)BN * (kcp + 8) * 2 : 0) +
-                          ((size_t)(MAX_KC + a.K / BK + 1) * 4 + 15) / 16 * 16 +
-                          (a.sel_idx ? (size_t)nchunk_of(kcp) * BM * 18 : 0);
-  const size_t epi_lds = epilogue_lds_bytes<NJ>();
-  const size_t lds = EPI == 2 ? rw_offset(loop_lds, epi_lds) + (size_t)BM * 4
-                              : (loop_lds > epi_lds ? loop_lds : epi_lds);
-  auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, EPI>;
+  const size_t loop = (loop_lds_bytes<BM, NSLOT, KQ>(a.K) + 15) / 16 * 16;
+  const size_t epi = (size_t)4 * epilogue_wave_floats<NJ>() * 4;
+  const size_t body = loop > epi ? loop : epi;
+  a.rw_lds_offset = (int)body;
+  const size_t lds = body + (EPI == 2 ? (size_t)BM * 4 : 0);
+  if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+  auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, NSLOT, EPI, KQ>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -741,14 +743,23 @@ static hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MI, int NJ, int WM, int WN>
+template <int MI, int NJ, int WM, int WN, int NSLOT, int KQ>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
   switch (a.epilogue) {
-    case 0: return launch_cfg<MI, NJ, WM, WN, 0>(a, stream);
-    case 1: return launch_cfg<MI, NJ, WM, WN, 1>(a, stream);
-    default: return launch_cfg<MI, NJ, WM, WN, 2>(a, stream);
+    case 0: return launch_cfg<MI, NJ, WM, WN, NSLOT, 0, KQ>(a, stream);
+    case 1: return launch_cfg<MI, NJ, WM, WN, NSLOT, 1, KQ>(a, stream);
+    default: return launch_cfg<MI, NJ, WM, WN, NSLOT, 2, KQ>(a, stream);
   }
 }
+
+template <int MI, int NJ, int WM, int WN, int NSLOT>
+static hipError_t launch_comp(const GemmArgs& a, hipStream_t stream) {
+  if (!a.sel_idx) return launch_epi<MI, NJ, WM, WN, NSLOT, 0>(a, stream);
+  if (a.kc <= 64) return launch_epi<MI, NJ, WM, WN, NSLOT, 4>(a, stream);
+  return launch_epi<MI, NJ, WM, WN, NSLOT - 1, 8>(a, stream);   // a wider W_S: one slot fewer
+}
+
+}  // namespace nvg
 
 // Rows per m-tile from the average rows per expert.  The last m-tile of an
 // expert is ragged; its empty 32-row fragments cost no MFMAs and no A
@@ -762,6 +773,12 @@ int grouped_gemm_block_m(int64_t rows_total, int32_t E) {
   return 32;
 }
 
+// The kernel reads A codes and one expert's W codes with 32-bit offsets.
+bool grouped_gemm_offsets_fit(int64_t a_rows, int64_t N, int64_t K) {
+  const int64_t lim = (int64_t)1 << 32;
+  return a_rows * (K / 2) < lim && N * (K / 2) < lim;
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.epilogue == 1 && a.out_amax) {
     hipError_t err = launch_fill_f32(a.out_amax, 1, 0.0f, stream);
@@ -769,13 +786,14 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   }
   if (a.rows_total == 0) return hipSuccess;
   hipError_t err;
-  const int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
+  int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
+  // a compensation wider than 64 channels (a larger W_S) needs a shorter tile
+  if (a.sel_idx && a.kc > 64 && bm > 128) bm = 128;
   switch (bm) {
-    case 256: err = launch_epi<4, 4, 2, 2>(a, stream); break;
-    case 128: err = launch_epi<2, 4, 2, 2>(a, stream); break;
-    case 64: err = launch_epi<1, 4, 2, 2>(a, stream); break;
-    // the 32-row tile moves 128 K per stage: K = 64 takes the 64-row tile
-    default: err = a.K >= 128 ? launch_epi<1, 2, 1, 4>(a, stream) : launch_epi<1, 4, 2, 2>(a, stream); break;
+    case 256: err = nvg::launch_comp<4, 4, 2, 2, 3>(a, stream); break;
+    case 128: err = nvg::launch_comp<2, 4, 2, 2, 3>(a, stream); break;
+    case 64: err = nvg::launch_comp<1, 4, 2, 2, 3>(a, stream); break;
+    default: err = nvg::launch_comp<1, 2, 1, 4, 3>(a, stream); break;
   }
   if (err != hipSuccess || a.epilogue != 2) return err;
   return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,

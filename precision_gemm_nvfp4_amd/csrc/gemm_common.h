@@ -55,9 +55,12 @@ __device__ __forceinline__ uint32_t block_scan_256(uint32_t v, uint32_t* sh_wave
   return before + v;
 }
 
-// Number of m-tiles over all experts (the same in every thread).
+// Number of m-tiles over all experts (the same in every thread).  This and
+// locate_tile are inlined: as calls they would take the kernel argument's
+// address, which puts the whole argument block in scratch memory, and every
+// later read of a field from there waits for all earlier memory operations.
 template <int BM>
-__device__ uint32_t count_mtiles(const GemmArgs& p) {
+__device__ __forceinline__ uint32_t count_mtiles(const GemmArgs& p) {
   __shared__ uint32_t sh_waves[4];
   uint32_t carry = 0;
   for (int base = 0; base < p.E; base += 256) {
@@ -75,7 +78,7 @@ __device__ uint32_t count_mtiles(const GemmArgs& p) {
 // comes as a run of ntiles cheap tiles).  Called by all threads of a
 // 256-thread workgroup.
 template <int BM>
-__device__ TileCoord locate_tile(const GemmArgs& p, int ntiles, int logical) {
+__device__ __forceinline__ TileCoord locate_tile(const GemmArgs& p, int ntiles, int logical) {
   __shared__ int32_t sh_e, sh_mt, sh_nt;
   __shared__ uint32_t sh_waves[4];
   const int tid = threadIdx.x;
@@ -103,6 +106,59 @@ __device__ TileCoord locate_tile(const GemmArgs& p, int ntiles, int logical) {
   t.row0 = g0 + (int64_t)sh_mt * BM;
   t.rows_valid = (int)((g1 - t.row0) < BM ? (g1 - t.row0) : BM);
   return t;
+}
+
+// This workgroup's tile, from one pass over the group offsets: the m-tiles
+// of every expert, their prefix sum and total T (T x ntiles real tiles), the
+// XCD mapping of workgroup ids (hardware id h runs logical tile
+// (h % 8) * ceil(T' / 8) + h / 8 of the T' = T x ntiles real ones), and the
+// coordinates of that tile.  Returns false (the same in every thread) for a
+// surplus workgroup.  With E <= 256 the offsets are read once (one memory
+// round trip); more experts take a counting pass first.  Called by all
+// threads of a 256-thread workgroup.
+template <int BM>
+__device__ __forceinline__ bool map_tile(const GemmArgs& p, int ntiles, TileCoord& t) {
+  __shared__ int32_t sh_e, sh_mt, sh_nt;
+  __shared__ int64_t sh_g0, sh_g1;
+  __shared__ uint32_t sh_waves[4];
+  const int tid = threadIdx.x;
+  uint32_t total = 0;
+  int64_t g0 = 0, g1 = 0;
+  uint32_t n = 0, before = 0;
+  if (p.E <= 256) {
+    if (tid < p.E) {
+      g0 = clamp64(p.group_offsets[tid], 0, p.rows_total);
+      g1 = clamp64(p.group_offsets[tid + 1], g0, p.rows_total);
+      n = (uint32_t)((g1 - g0 + BM - 1) / BM);
+    }
+    before = block_scan_256(n, sh_waves, total) - n;
+  } else {
+    total = count_mtiles<BM>(p);
+  }
+  const int real = (int)total * ntiles;
+  const int per_xcd = (real + 7) / 8;
+  const int jt = (int)blockIdx.x / 8;
+  const int logical = ((int)blockIdx.x % 8) * per_xcd + jt;
+  if (jt >= per_xcd || logical >= real) return false;
+  if (p.E > 256) {
+    t = locate_tile<BM>(p, ntiles, logical);
+    return true;
+  }
+  const uint32_t m_key = (uint32_t)(logical / ntiles);
+  if (tid < p.E && m_key >= before && m_key < before + n) {    // exactly one thread
+    const int off = logical - (int)before * ntiles;
+    sh_e = tid;
+    sh_mt = off / ntiles;
+    sh_nt = off % ntiles;
+    sh_g0 = g0;
+    sh_g1 = g1;
+  }
+  __syncthreads();
+  t.e = sh_e;
+  t.n_tile = sh_nt;
+  t.row0 = sh_g0 + (int64_t)sh_mt * BM;
+  t.rows_valid = (int)((sh_g1 - t.row0) < BM ? (sh_g1 - t.row0) : BM);
+  return true;
 }
 
 // Weight row held at row r (0 .. BN-1) of an n-tile, or -1 past the end.

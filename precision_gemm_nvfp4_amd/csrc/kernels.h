@@ -65,6 +65,7 @@ struct GemmArgs {
   int accumulate = 0;          // F32 epilogue: out += Y instead of out = Y
 };
 int grouped_gemm_block_m(int64_t rows_total, int32_t E);
+bool grouped_gemm_offsets_fit(int64_t a_rows, int64_t N, int64_t K);
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream);
 
 // mxfp4.hip
