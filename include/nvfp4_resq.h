@@ -45,7 +45,9 @@
  *     device memory, 256-byte aligned; its contents need no initialization
  *     and are garbage afterwards.  The library allocates nothing.
  *   - Base pointers must be 16-byte aligned; K % 16 == 0 and the compensated
- *     channel count k % 16 == 0, 16 <= k <= K.
+ *     channel count k % 16 == 0, 16 <= k <= K.  The grouped GEMMs need more
+ *     of K (stated in their blocks): K % 64 == 0 for NVFP4, K % 128 == 0 for
+ *     MXFP4.
  *   - Non-finite inputs are outside the contract.
  *   - Calls that share a workspace or outputs on one stream are ordered by
  *     the stream; concurrent use of one workspace from two streams races.
@@ -211,9 +213,15 @@ int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64
  * (the stored NVFP4 weight restricted to the selected channels).  Products
  * of dequantized operands are exact; accumulation is fp32.
  *
+ *   K                  multiple of 64, at most 65536: the kernel moves K through
+ *                      LDS in 128-wide stages of 16-byte code chunks and
+ *                      4-byte scale words, and a half stage (64) is the finest
+ *                      granule it handles; K % 16 != 0 or K % 64 != 0 gives EINVAL
  *   a_codes/a_scales   [a_rows, K/2] / [a_rows, K/16];  a_global fp32 [1];
  *                      a_rows >= 1 whenever rows_total > 0 (row 0 must exist);
- *                      a row index outside [0, a_rows) reads as zeros
+ *                      a row index outside [0, a_rows) reads as zeros;
+ *                      a_rows * K/2 and N * K/2 below 2^32 (the kernel addresses
+ *                      A and one expert's W with 32-bit offsets; EUNSUPPORTED)
  *   group_offsets      int64 [E+1] (device), group_offsets[E] == rows_total
  *   w_codes/w_scales   [E, N, K/2] / [E, N, K/16];  w_global fp32 [E]
  *   sel_idx            NULL (no compensation) or int32 [E, kc] ascending, kc <= 128
@@ -230,7 +238,9 @@ int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64
  *                      initializes out.  Needs the workspace
  *                      (rows_total * N * 4 bytes plus index lists); the
  *                      other epilogues need none.
- * Errors: EINVAL (shapes, pointers, epilogue arguments, kc), EWORKSPACE.
+ * Errors: EINVAL (shapes, K % 64, pointers, epilogue arguments, kc),
+ *         EUNSUPPORTED (K > 65536, rows_total >= 2^31, operands of 4 GiB),
+ *         EWORKSPACE.
  * rows_total == 0 is valid (out_amax set to 0, nothing else written).
  * ------------------------------------------------------------------------ */
 size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K,

@@ -111,6 +111,8 @@ def test_gemm_validation(lib):
         return f(*a.values())
 
     assert call(K=520) == -1 and "multiple of 64" in err(lib)
+    assert call(K=48) == -1 and "multiple of 64" in err(lib)      # K % 16 == 0 is not enough
+    assert call(a_rows=1 << 22, K=4096) == -2 and "4 GiB" in err(lib)
     assert call(sel=FAKE, kc=24, rc=FAKE, rs=FAKE, rg=FAKE) == -1
     assert call(sel=FAKE, kc=64, rg=None, rc=FAKE, rs=FAKE) == -1
     assert call(epi=1, N=255) == -1

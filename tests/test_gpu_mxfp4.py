@@ -221,6 +221,73 @@ def test_mx_dense_linear_compensated(gpu_lib, spread):
         assert np.linalg.norm(np32(y) - exact) < np.linalg.norm(np32(y0) - exact)
 
 
+def _comp_rounding_bound(wc, ws, sel, rc, rs):
+    """Elementwise bound on how far the GPU's compensation term may be from
+    the exact one (the kernel's stated error bound).  The kernel runs the
+    correction on the FP8 form of the scaled MFMA, with E4M3 operands under
+    one power-of-two scale per operand row:
+      W_S[n, j] = e2m1 * 2^(X - Xmax(n)), Xmax(n) the largest block scale of
+        weight row n, is exact in E4M3 when X - Xmax(n) >= -8 and otherwise
+        rounded to E4M3's subnormal grid: error <= 2^(Xmax(n) - 10);
+      Q(R_S)[r, j] likewise against the larger block scale of its 64-wide
+        K-step: error <= 2^(Xr(r, step) - 10) when more than 8 binades apart.
+    So |dY[r, n]| <= sum_j |R[r, j]| dW[n, j] + dR[r, j] (|W[n, S_j]| + dW[n, j])."""
+    w = MX.dequantize(wc, ws).astype(np.float64)
+    xw = ws.astype(np.int64) - 127
+    xmax = xw.max(axis=1)
+    sel = np.asarray(sel, dtype=np.int64)
+    xsel = xw[:, sel // 32]
+    dw = np.where(xsel - xmax[:, None] < -8, 2.0 ** (xmax[:, None] - 10), 0.0)
+    r = MX.dequantize(rc, rs).astype(np.float64)
+    xr = rs.astype(np.int64) - 127
+    kc = r.shape[1]
+    xstep = np.stack([xr[:, 2 * s:2 * s + 2].max(axis=1) for s in range((kc + 63) // 64)], axis=1)
+    xr_el = xr[:, np.arange(kc) // 32]
+    xs_el = xstep[:, np.arange(kc) // 64]
+    dr = np.where(xr_el - xs_el < -8, 2.0 ** (xs_el - 10), 0.0)
+    return np.abs(r) @ dw.T + dr @ (np.abs(w[:, sel]) + dw).T, dw, dr
+
+
+def test_mx_comp_rounding_bound(gpu_lib):
+    """The compensation's stated error bound, exercised on both operands: 32
+    outlier channels at the lowest indices (their residuals fill the first
+    32-block of the compact R_S) and every other channel 2^-12 smaller (the
+    second block, 10+ binades below the first in the same 64-wide K-step),
+    with weight rows whose blocks span 12 binades.  The GPU result stays
+    within the bound plus fp32 accumulation slack, elementwise."""
+    P = gpu_lib
+    rng = np.random.default_rng(81)
+    tokens, k_dim, n_out, kc = 128, 512, 256, 64
+    x = (rng.standard_normal((tokens, k_dim)) * 2.0 ** -12).astype(np.float32)
+    x[:, :32] = (rng.standard_normal((tokens, 32)) * 16.0).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16)
+    w = synth.weights(1, n_out, k_dim, seed=82, tensor_id=synth.WDENSE_ID).clone()
+    w[0, :, 64:192] *= 2.0 ** -12
+    xc = xb.cuda()
+    codes, scales, _ = P.mxfp4_quantize(xc)
+    offs = torch.tensor([0, tokens], dtype=torch.int64, device="cuda")
+    sel, rc, rs = P.mxfp4_resq_select_and_requant(xc, codes, scales, kc, unit_offsets=offs,
+                                                  rows_total=tokens)
+    wc, ws_ = _mx_weights(P, w)
+    y = P.moe_mxfp4_grouped_gemm(codes, scales, offs, tokens, wc, ws_, sel_idx=sel, r_codes=rc,
+                                 r_scales=rs)
+    x_np = xb.float().numpy()
+    c_r, s_r = ref_mx(x_np, codes, scales)
+    sel_r, rc_r, rs_r = ref_mx_resq(x_np, c_r, s_r, [0, tokens], kc, None, sel, rc, rs)
+    assert np.array_equal(sel_r[0][:32], np.arange(32))
+    wc_r, ws_r = ref_mx_weights(w, wc, ws_)
+    ref = _gemm_ref(c_r, s_r, wc_r[0], ws_r[0], sel_r[0], rc_r, rs_r)
+    bound, dw, dr = _comp_rounding_bound(wc_r[0], ws_r[0], sel_r[0], rc_r, rs_r)
+    assert dw.max() > 0 and dr.max() > 0, "both operands take the rounding path"
+    a = np.abs(MX.dequantize(c_r, s_r).astype(np.float64))
+    wa = np.abs(MX.dequantize(wc_r[0], ws_r[0]).astype(np.float64))
+    s_abs = a @ wa.T + np.abs(MX.dequantize(rc_r, rs_r).astype(np.float64)) @ wa[:, sel_r[0]].T
+    slack = (k_dim + kc) * 2.0 ** -24 * s_abs
+    err = np.abs(np32(y) - ref)
+    assert np.all(err <= bound + slack), float((err - bound - slack).max())
+    assert rel_err(np32(y), ref) <= GEMM_TOL
+
+
 def _route_setup(tokens, hidden, n_exp, inter, seed, zipf, top_k, empty_expert=None):
     x = synth.activations(tokens, hidden, seed=seed, heavy_frac=0.01)
     rt = synth.route(tokens, n_exp, seed=seed, top_k=top_k, zipf_s=zipf)
