@@ -80,6 +80,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", default="moe_T8192_H4096_E256_I1536_k64_trainer")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the brief runs of the four smaller workloads after the headline one")
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="calibration: time a plain device copy of this many bytes instead "
@@ -300,11 +302,194 @@ def cpu_baseline(wl, inp, budget_s):
         if time.time() - t0 > budget_s:
             break
     dt = time.time() - t0
+    # the same oracle on one thread, on the first expert only (a bounded sample)
+    one = None
+    try:
+        from threadpoolctl import threadpool_limits
+        e = next(i for i in range(wl.experts) if offs[i + 1] > offs[i])
+        a, b = int(offs[e]), int(offs[e + 1])
+        with threadpool_limits(limits=1):
+            t1 = time.time()
+            wgu = inp["wgu"][e:e + 1].float().cpu().numpy()
+            if mx:
+                sel, rc, rs = OM.resq_select_and_requant(xs, xc, xsc, [0, b - a], wl.k, row_index=tok[a:b])
+                gc, gs = OM.quantize_weights(wgu)
+                OM.gemm_comp(xc[tok[a:b]], xsc[tok[a:b]], gc[0], gs[0], sel[0], rc, rs)
+            else:
+                sel, rc, rs, rg = OQ.resq_select_and_requant(xs, xc, xsc, xg, [0, b - a], wl.k,
+                                                             row_index=tok[a:b])
+                _, gc, gs, gg = OQ.qdq_weights(wgu)
+                OG.gemm_comp(xc[tok[a:b]], xsc[tok[a:b]], xg, gc[0], gs[0], gg[0], sel[0], rc, rs, rg[0])
+            dt1 = time.time() - t1
+        one = dict(value=gemm_flops(b - a, 2 * wl.inter, wl.hidden, wl.k) / dt1 / 1e12, unit="TFLOP/s",
+                   cores=1, seconds=round(dt1, 2),
+                   sample=f"expert {e} of the gate/up projection ({b - a} rows), as above, one thread")
+    except Exception as exc:                       # threadpoolctl missing or no BLAS to limit
+        one = dict(error=str(exc))
+    model, ncpu = host_cpu()
     return dict(value=flops / dt / 1e12, unit="TFLOP/s", cores=int(cores), kind="oracle",
                 sample=f"{wl.fmt.upper()} quantization of X, then {done} expert(s) of the gate/up projection "
                        f"({wl.hidden}->{2 * wl.inter}, k={wl.k}) in expert order, each with residual "
                        f"selection, weight quantization and the fp64 compensated GEMM; {dt:.1f} s",
-                seconds=round(dt, 2))
+                seconds=round(dt, 2), host_cpu=model, host_logical_cpus=ncpu,
+                threads_note="cores = the BLAS thread count numpy used (the GEMM step is the "
+                             "multithreaded part; the quantizer and selection run on one thread)",
+                one_thread=one)
+
+
+def time_call(torch, fn, n=10, warm=2):
+    """Mean ms of fn() over n calls, HIP events on the current stream."""
+    for _ in range(warm):
+        fn()
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(n):
+        fn()
+    e.record()
+    torch.cuda.synchronize()
+    return s.elapsed_time(e) / n
+
+
+def host_cpu():
+    """CPU model and logical core count of the host that runs the bench."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def comp_overhead(torch, P, inp, wl, sel1, sel2, hq, n=5):
+    """Time of each grouped GEMM with and without the compensation term on
+    the step's own operands, and the selection that feeds it: the cost of
+    residual compensation next to the pages' 5-9% (QUADS section 4)."""
+    xq_c, xq_s, xq_g = sel1["xq"]
+    hq_c, hq_s, hq_g = hq
+    h = sel2["h"]
+    gu = dict(a_row_index=inp["slot_token"], out_amax=inp["amax"], epilogue=P.EPI_SWIGLU_BF16)
+    dn = dict(epilogue=P.EPI_SCATTER_ADD_F32, row_weight=inp["slot_weight"],
+              scatter_index=inp["slot_token"], out=inp["y"])
+    s1, s2 = sel1["sel"], sel2["sel"]
+    t = {}
+    t["gate_up_plain"] = time_call(torch, lambda: P.moe_w4a4_grouped_gemm(
+        xq_c, xq_s, xq_g, inp["offs"], inp["rows"], inp["gc"], inp["gs"], inp["gg"], **gu), n)
+    t["gate_up_comp"] = time_call(torch, lambda: P.moe_w4a4_grouped_gemm(
+        xq_c, xq_s, xq_g, inp["offs"], inp["rows"], inp["gc"], inp["gs"], inp["gg"], sel_idx=s1[0],
+        r_codes=s1[1], r_scales=s1[2], r_global=s1[3], **gu), n)
+    t["resq_x"] = time_call(torch, lambda: P.resq_select_and_requant(
+        inp["x"], xq_c, xq_s, xq_g, wl.k, unit_offsets=inp["offs"], rows_total=inp["rows"],
+        row_index=inp["slot_token"]), n)
+    t["down_plain"] = time_call(torch, lambda: P.moe_w4a4_grouped_gemm(
+        hq_c, hq_s, hq_g, inp["offs"], inp["rows"], inp["dc"], inp["ds"], inp["dg"], **dn), n)
+    t["down_comp"] = time_call(torch, lambda: P.moe_w4a4_grouped_gemm(
+        hq_c, hq_s, hq_g, inp["offs"], inp["rows"], inp["dc"], inp["ds"], inp["dg"], sel_idx=s2[0],
+        r_codes=s2[1], r_scales=s2[2], r_global=s2[3], **dn), n)
+    t["resq_h"] = time_call(torch, lambda: P.resq_select_and_requant(
+        h, hq_c, hq_s, hq_g, wl.k, unit_offsets=inp["offs"], rows_total=inp["rows"]), n)
+    plain = t["gate_up_plain"] + t["down_plain"]
+    return dict(
+        ms={k: round(v, 4) for k, v in t.items()},
+        gemm_only=round((t["gate_up_comp"] + t["down_comp"]) / plain - 1, 4),
+        with_selection=round((t["gate_up_comp"] + t["down_comp"] + t["resq_x"] + t["resq_h"]) / plain - 1, 4),
+        flop_fraction=round(wl.k * (2 * wl.inter + wl.hidden) / (wl.hidden * 2 * wl.inter + wl.inter * wl.hidden), 4),
+        pages="5-9% slower than plain NVFP4 W4A4 rollout (QUADS section 4, NVIDIA Blackwell)")
+
+
+def moe_summary(torch, P, synth, wl, dev, steps=5):
+    """One MoE workload timed briefly: step time, per-part times, the gate/up
+    GEMM's rate against the fp16 MFMA peak (prefill) or the weights' HBM
+    stream (decode), and the compensation overhead."""
+    inp, _ = build_inputs(torch, P, synth, wl, dev)
+    for _ in range(2):
+        run_step(P, inp, wl, Timeline(torch), trainer=False)
+    torch.cuda.synchronize()
+    tls = []
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(steps):
+        tl = Timeline(torch)
+        out = run_step(P, inp, wl, tl, trainer=False)
+        tls.append(tl)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / steps
+    parts = {}
+    for tl in tls:
+        for k, v in tl.durations().items():
+            parts[k] = parts.get(k, 0.0) + v / steps
+    work = part_work(wl, inp["rows"])
+    gflop = work["gemm_gate_up"]["flops"] + work["gemm_down"]["flops"]
+    T, H, I, E = wl.tokens, wl.hidden, wl.inter, wl.experts
+    w_bytes = E * (2 * I * H + H * I) * (0.5 + 1 / 16)
+    gu_tf = work["gemm_gate_up"]["flops"] / (parts["gemm_gate_up"] * 1e-3) / 1e12
+    res = dict(workload=wl.name, ms_per_step=round(ms, 4),
+               parts_ms={k: round(v, 4) for k, v in parts.items() if k in work},
+               gemm_tflops=round(gflop / ((parts["gemm_gate_up"] + parts["gemm_down"]) * 1e-3) / 1e12, 2),
+               gate_up=dict(ms=round(parts["gemm_gate_up"], 4), tflops=round(gu_tf, 2),
+                            frac_fp16_peak=round(gu_tf / FP16_PEAK_TFLOPS, 4),
+                            frac_fp4_peak=round(gu_tf / FP4_PEAK_TFLOPS, 4)))
+    if inp["rows"] // E < 24:            # decode: the GEMMs stream the expert weights
+        gbs = w_bytes / ((parts["gemm_gate_up"] + parts["gemm_down"]) * 1e-3) / 1e9
+        res["weights_stream"] = dict(bytes=int(w_bytes), gbs=round(gbs, 1),
+                                     frac_hbm=round(gbs / HBM_PEAK_GBS, 4), bound="hbm")
+    res["comp_overhead"] = comp_overhead(
+        torch, P, inp, wl, dict(xq=out["xq"], sel=out["sel1"]),
+        dict(h=out["h"], sel=out["sel2"]), out["hq"])
+    del inp, out
+    torch.cuda.empty_cache()
+    return res
+
+
+def dense_summary(torch, P, synth, wl, dev, n=20):
+    """The single dense linear (E = 1): the whole path (quantize, select,
+    compensated GEMM) and the GEMM with and without compensation."""
+    x = synth.activations(wl.tokens, wl.hidden, seed=wl.seed, device=dev.type,
+                          outlier_channels=wl.outliers)
+    w = synth.weights(1, wl.n_out, wl.hidden, seed=wl.seed, tensor_id=synth.WDENSE_ID, device=dev.type)
+    _, wc, ws, wg = P.qdq_weights(w)
+    offs = torch.tensor([0, wl.tokens], dtype=torch.int64, device=dev)
+
+    def path():
+        c, sc, g, _ = P.nvfp4_quantize(x)
+        sel = P.resq_select_and_requant(x, c, sc, g, wl.k, unit_offsets=offs, rows_total=wl.tokens)
+        return P.moe_w4a4_grouped_gemm(c, sc, g, offs, wl.tokens, wc, ws, wg, sel_idx=sel[0],
+                                       r_codes=sel[1], r_scales=sel[2], r_global=sel[3])
+    c, sc, g, _ = P.nvfp4_quantize(x)
+    sel = P.resq_select_and_requant(x, c, sc, g, wl.k, unit_offsets=offs, rows_total=wl.tokens)
+    t_path = time_call(torch, path, n)
+    t_comp = time_call(torch, lambda: P.moe_w4a4_grouped_gemm(
+        c, sc, g, offs, wl.tokens, wc, ws, wg, sel_idx=sel[0], r_codes=sel[1], r_scales=sel[2],
+        r_global=sel[3]), n)
+    t_plain = time_call(torch, lambda: P.moe_w4a4_grouped_gemm(c, sc, g, offs, wl.tokens, wc, ws, wg), n)
+    return dict(workload=wl.name, bound="launch latency (142.6 MFLOP)",
+                us_path=round(t_path * 1e3, 1), us_gemm_comp=round(t_comp * 1e3, 1),
+                us_gemm_plain=round(t_plain * 1e3, 1),
+                comp_overhead_gemm=round(t_comp / t_plain - 1, 4))
+
+
+def config_summaries(args, torch, P, synth, dev):
+    """The four smaller workloads, each timed briefly after the headline one
+    (outside its timed region)."""
+    out = {}
+    wl = synth.WORKLOADS["dense_T128_K512_N1024_k32"]
+    out["dense"] = dense_summary(torch, P, synth, wl, dev)
+    wl = synth.WORKLOADS["quant_select_T16384_K4096_k128"]
+    qargs = argparse.Namespace(**vars(args))
+    qargs.steps, qargs.warmup, qargs.no_cpu_baseline = 10, 2, True
+    q = quant_select_bench(qargs, torch, P, synth, wl, dev)
+    out["quant_select"] = dict(workload=wl.name, ms_per_step=q["ms_per_step"], gbs=q["value"],
+                               frac_hbm=round(q["value"] / HBM_PEAK_GBS, 4), parts=q["parts"],
+                               bound="hbm")
+    for key, name in (("decode", "moe_decode_T256_H2048_E128_I768_k64"),
+                      ("prefill", "moe_prefill_T16384_H2048_E128_I768_zipf1.1_k64")):
+        out[key] = moe_summary(torch, P, synth, synth.WORKLOADS[name], dev)
+    return out
 
 
 def quant_select_bench(args, torch, P, synth, wl, dev):
@@ -740,6 +925,16 @@ def main():
                     flops_per_launch=work["gemm_gate_up"]["flops"],
                     frac_fp4_peak=round(ach / FP4_PEAK_TFLOPS, 4))
 
+    comp = None
+    configs = None
+    if not args.no_configs and not mx:
+        print("[bench] compensation overhead and the four smaller workloads", file=sys.stderr, flush=True)
+        out = run_step(P, inp, wl, Timeline(torch), trainer=False)
+        comp = comp_overhead(torch, P, inp, wl, dict(xq=out["xq"], sel=out["sel1"]),
+                             dict(h=out["h"], sel=out["sel2"]), out["hq"])
+        del out
+        configs = config_summaries(args, torch, P, synth, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle sample", file=sys.stderr, flush=True)
@@ -770,6 +965,10 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed": round(wall, 3),
     }
+    if comp is not None:
+        line["comp_overhead"] = comp
+    if configs is not None:
+        line["configs"] = configs
     print(json.dumps(line))
 
 
