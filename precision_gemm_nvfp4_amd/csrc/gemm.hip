@@ -112,13 +112,28 @@ struct IntC {
   static constexpr int value = V;
 };
 
+// Direct global-to-LDS loads through buffer resources: the operand's base
+// and byte size live in four scalar registers, the stage's advance is the
+// scalar offset and each lane's position within the stage a 32-bit vector
+// offset fixed for the whole tile, so a load costs no vector arithmetic.
+// Lane l of an instruction writes its 16 / 4 bytes at LDS l * 16 / l * 4 past
+// the (uniform) destination.  A read at or past the resource's size returns
+// zeros, which is how rows with a bad index and the blocks past K of a
+// half-full last stage get zero scales.
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-__device__ __forceinline__ void load_lds16(const uint8_t* base, uint32_t off, unsigned char* l) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off), (lds_void_t*)l, 16, 0, 0);
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+constexpr uint32_t OOB = 0x80000000u;       // vector offset past every scale array
+__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
+  // raw buffer (stride 0), 32-bit data format: what untyped loads need on gfx9
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
+                                           (int)(uint32_t)(bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll),
+                                           0x00020000);
 }
-__device__ __forceinline__ void load_lds4(const uint8_t* base, uint32_t off, unsigned char* l) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)(base + off), (lds_void_t*)l, 4, 0, 0);
+__device__ __forceinline__ void load_lds16(Rsrc r, uint32_t voff, int soff, unsigned char* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 16, voff, soff, 0, 0);
+}
+__device__ __forceinline__ void load_lds4(Rsrc r, uint32_t voff, int soff, unsigned char* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 4, voff, soff, 0, 0);
 }
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 0-3 and 14-15)
 template <int N>
@@ -223,14 +238,13 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     const int64_t br = weight_row<BN>(p, n_tile, r);
     return br >= 0 ? br : 0;
   };
-  // Addresses: a uniform base (argument + expert + stage offsets, in SGPRs)
-  // plus a 32-bit per-lane offset (the host checks that A and one expert's W
-  // span less than 4 GiB), which the load takes as its saddr + voffset form.
-  // (local copies: the loop must not read the argument struct from memory)
-  const uint8_t* const a_codes = p.a_codes;
-  const uint8_t* const a_scales = p.a_scales;
-  const uint8_t* const wc_e = p.w_codes + (int64_t)e * p.N * rbytes;
-  const uint8_t* const ws_e = p.w_scales + (int64_t)e * p.N * sbytes;
+  // Buffer resources of A's and this expert's W codes and scales (the host
+  // checks that A and one expert's W span less than 4 GiB), built once: the
+  // loop must not read the argument struct from memory.
+  const Rsrc r_ac = make_rsrc(p.a_codes, p.a_rows * rbytes);
+  const Rsrc r_as = make_rsrc(p.a_scales, p.a_rows * sbytes);
+  const Rsrc r_wc = make_rsrc(p.w_codes + (int64_t)e * p.N * rbytes, p.N * rbytes);
+  const Rsrc r_ws = make_rsrc(p.w_scales + (int64_t)e * p.N * sbytes, p.N * sbytes);
   const int lr = lane >> 2, lp = lane & 3;
   // code loads: lane l of block b loads tile row 16 b + l / 4, LDS position
   // l % 4, i.e. logical chunk (l % 4) ^ swz(row)
@@ -252,7 +266,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   }
   // scale loads: word position P = 64 b + l holds, in the read order
   // ((wm 2 + h) 32 + l32) MI + i, word h of A row wm MI 32 + 32 i + l32
-  // (likewise NJ / wn for W)
+  // (likewise NJ / wn for W).  A row of the tile whose index lies outside
+  // [0, a_rows) reads its scales past the end of the array: zeros, so the row
+  // reads as zeros.
   uint32_t as_off[L::PAS], bs_off[L::PWS];
   int as_h[L::PAS], bs_h[L::PWS];
 #pragma unroll
@@ -260,8 +276,12 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     const int b = wave * L::PAS + i;
     const int P = (b < L::NAS ? b : 0) * 64 + lane;
     const int ii = P % MI, ll = (P / MI) % 32, hh = (P / (MI * 32)) % 2, ww = P / (MI * 64);
+    const int r = ww * MI * 32 + ii * 32 + ll;
+    const int64_t ar = a_index(r);
     as_h[i] = hh;
-    as_off[i] = (uint32_t)(a_row(ww * MI * 32 + ii * 32 + ll) * sbytes) + (uint32_t)(hh * 4);
+    as_off[i] = (r < rows_valid && (ar < 0 || ar >= p.a_rows))
+                    ? OOB
+                    : (uint32_t)(a_row(r) * sbytes) + (uint32_t)(hh * 4);
   }
 #pragma unroll
   for (int i = 0; i < L::PWS; ++i) {
@@ -270,15 +290,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     const int jj = P % NJ, ll = (P / NJ) % 32, hh = (P / (NJ * 32)) % 2, ww = P / (NJ * 64);
     bs_h[i] = hh;
     bs_off[i] = (uint32_t)(w_row(ww * NJ * 32 + jj * 32 + ll) * sbytes) + (uint32_t)(hh * 4);
-  }
-  // A rows whose index lies outside [0, a_rows) read as zeros: their scale
-  // words are masked (per fragment row, fixed for the tile)
-  uint32_t amask[MI];
-#pragma unroll
-  for (int i = 0; i < MI; ++i) {
-    const int r = wm * MI * 32 + i * 32 + l32;
-    const int64_t ar = a_index(r);
-    amask[i] = (r < rows_valid && (ar < 0 || ar >= p.a_rows)) ? 0u : ~0u;
   }
   if constexpr (COMP) {
     for (int j = tid; j < kc; j += 256) {
@@ -315,78 +326,73 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   }
 
   // The LPW load instructions of stage m into slot `slot`.  In the half-full
-  // last stage (K % 128 == 64) the chunks and the scale word past K are read
-  // from the row's first half instead (their scales are zeroed when read), so
-  // no load leaves its row.
+  // last stage (K % 128 == 64) the code chunks past K are read from the row's
+  // first half instead, so no load leaves its row, and the scale words past K
+  // are read out of bounds: zeros, so those chunks add nothing.
   auto issue = [&](int m, int slot) {
     unsigned char* base = smem + slot * STAGE;
-    const uint8_t* ac = a_codes + (int64_t)m * 64;
-    const uint8_t* wc = wc_e + (int64_t)m * 64;
-    const uint8_t* as = a_scales + (int64_t)m * 8;
-    const uint8_t* wsb = ws_e + (int64_t)m * 8;
+    const int sc = m * 64, ss = m * 8;                  // the stage's offset in a row
     if (m != mh) {
 #pragma unroll
       for (int i = 0; i < L::PA; ++i) {
         const int b = wave * L::PA + i;
-        load_lds16(ac, a_off[i], b < L::NA ? base + L::A_OFF + b * 1024 : DUMMY);
+        load_lds16(r_ac, a_off[i], sc, b < L::NA ? base + L::A_OFF + b * 1024 : DUMMY);
       }
 #pragma unroll
       for (int i = 0; i < L::PW; ++i) {
         const int b = wave * L::PW + i;
-        load_lds16(wc, b_off[i], b < L::NW ? base + L::B_OFF + b * 1024 : DUMMY);
+        load_lds16(r_wc, b_off[i], sc, b < L::NW ? base + L::B_OFF + b * 1024 : DUMMY);
       }
 #pragma unroll
       for (int i = 0; i < L::PAS; ++i) {
         const int b = wave * L::PAS + i;
-        load_lds4(as, as_off[i], b < L::NAS ? base + L::AS_OFF + b * 256 : DUMMY);
+        load_lds4(r_as, as_off[i], ss, b < L::NAS ? base + L::AS_OFF + b * 256 : DUMMY);
       }
 #pragma unroll
       for (int i = 0; i < L::PWS; ++i) {
         const int b = wave * L::PWS + i;
-        load_lds4(wsb, bs_off[i], b < L::NWS ? base + L::BS_OFF + b * 256 : DUMMY);
+        load_lds4(r_ws, bs_off[i], ss, b < L::NWS ? base + L::BS_OFF + b * 256 : DUMMY);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < L::PA; ++i) {
         const int b = wave * L::PA + i;
-        load_lds16(ac, a_off[i] - (uint32_t)((a_chk[i] & 2) << 4),
+        load_lds16(r_ac, a_off[i] - (uint32_t)((a_chk[i] & 2) << 4), sc,
                    b < L::NA ? base + L::A_OFF + b * 1024 : DUMMY);
       }
 #pragma unroll
       for (int i = 0; i < L::PW; ++i) {
         const int b = wave * L::PW + i;
-        load_lds16(wc, b_off[i] - (uint32_t)((b_chk[i] & 2) << 4),
+        load_lds16(r_wc, b_off[i] - (uint32_t)((b_chk[i] & 2) << 4), sc,
                    b < L::NW ? base + L::B_OFF + b * 1024 : DUMMY);
       }
 #pragma unroll
       for (int i = 0; i < L::PAS; ++i) {
         const int b = wave * L::PAS + i;
-        load_lds4(as, as_off[i] - (uint32_t)(as_h[i] * 4), b < L::NAS ? base + L::AS_OFF + b * 256 : DUMMY);
+        load_lds4(r_as, as_h[i] ? OOB : as_off[i], ss, b < L::NAS ? base + L::AS_OFF + b * 256 : DUMMY);
       }
 #pragma unroll
       for (int i = 0; i < L::PWS; ++i) {
         const int b = wave * L::PWS + i;
-        load_lds4(wsb, bs_off[i] - (uint32_t)(bs_h[i] * 4), b < L::NWS ? base + L::BS_OFF + b * 256 : DUMMY);
+        load_lds4(r_ws, bs_h[i] ? OOB : bs_off[i], ss, b < L::NWS ? base + L::BS_OFF + b * 256 : DUMMY);
       }
     }
   };
 
   // Q(R_S) codes of the tile's rows (a contiguous byte range of r_codes) go
-  // into LDS by direct loads ahead of the stages (4 bytes a lane; sources past
-  // the end of r_codes read its first word: those rows are never stored).
-  // Their scale bytes go into registers (used after the K loop): in
-  // compensation substep q (16 compact channels) lane half h takes channels
-  // 16 q + 8 h .. + 7, i.e. code word 2 q + h of the row and scale byte q.
+  // into LDS by direct loads ahead of the stages (4 bytes a lane; words past
+  // the end of r_codes read as zeros: those rows are never stored).  Their
+  // scale bytes go into registers (used after the K loop): in compensation
+  // substep q (16 compact channels) lane half h takes channels 16 q + 8 h ..
+  // + 7, i.e. code word 2 q + h of the row and scale byte q.
   constexpr int KQW = COMP ? KQ : 1;
   uint32_t rqs[MI][(KQW + 3) / 4];
   if constexpr (COMP) {
-    const uint32_t rrow = (uint32_t)(kc / 2);                   // code bytes per row
-    const int64_t rbase = row0 * rrow, rend = p.rows_total * rrow;
+    const int64_t rrow = kc / 2;                                // code bytes per row
+    const Rsrc r_rc = make_rsrc(p.r_codes + row0 * rrow, (p.rows_total - row0) * rrow);
     const int nword = BM * (kc / 8);                            // words of the tile
-    for (int w0 = wave * 64; w0 < nword; w0 += 256) {           // uniform trip count per wave
-      const int64_t src = rbase + 4 * (int64_t)(w0 + lane);
-      load_lds4(p.r_codes, (uint32_t)(src + 4 <= rend ? src : 0), RSC + 4 * w0);
-    }
+    for (int w0 = wave * 64; w0 < nword; w0 += 256)             // uniform trip count per wave
+      load_lds4(r_rc, 4u * (uint32_t)(w0 + lane), 0, RSC + 4 * w0);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int r = wm * MI * 32 + i * 32 + l32;
@@ -410,52 +416,47 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 
   // W_S gather of a stage: thread t copies the selected channels of weight
   // row t that fall in the stage, as exact fp16 values.  Weight row t's
-  // 16-byte chunk c of a stage sits at t * 64 + ((c ^ swz(t)) << 4) (so the
-  // chunk reads of 8 consecutive rows hit distinct banks, as the fragment
-  // reads do; single-byte reads down a column of rows 64 bytes apart would
-  // conflict 16 ways), its scale word h at position ((wn 2 + h) 32 + l32) NJ
-  // + j for t = wn NJ 32 + 32 j + l32.  The first four channels of a stage
-  // come from the gather table: their chunk and scale-word reads are issued
-  // right after the barrier that makes the stage visible, and the code
-  // nibble and scale byte are picked out (uniform positions) and written to
-  // W_S two substeps later, so nothing waits on LDS latency.  More than four
-  // channels in one stage take a slower loop.
-  const uint32_t g_row = (uint32_t)(L::B_OFF + tid * 64);
-  const int g_sw = swz(tid);
+  // 16-byte chunk c of a stage sits at t * 64 + ((c ^ swz(t)) << 4), i.e. at
+  // g_rowsw ^ (c << 4) with the swizzle bits folded into g_rowsw (the row base
+  // is a multiple of 64, so the XOR only touches bits 4-5); its scale word h
+  // at position ((wn 2 + h) 32 + l32) NJ + j for t = wn NJ 32 + 32 j + l32.
+  // The first four channels of a stage come from the gather table: the code
+  // word and scale word of each are read right after the barrier that makes
+  // the stage visible, and the nibble and the scale byte are picked out
+  // (uniform positions) and written to W_S two substeps later, so nothing
+  // waits on LDS latency.  More than four channels in one stage take a slower
+  // loop.
+  const uint32_t g_rowsw = (uint32_t)(L::B_OFF + tid * 64 + (swz(tid) << 4));
   const uint32_t g_srow = (uint32_t)(L::BS_OFF + (((tid / (NJ * 32)) * 2 * 32 + tid % 32) * NJ + (tid % (NJ * 32)) / 32) * 4);
-  auto g_chunk = [&](const unsigned char* base, int kk) {
-    return *reinterpret_cast<const u32x4*>(base + g_row + ((((kk >> 5) ^ g_sw)) << 4));
+  // the code word and the scale word that hold K-offset kk of a stage in slot
+  // byte offset sb (kk and sb uniform)
+  auto g_cword = [&](uint32_t sb, int kk) {
+    return *reinterpret_cast<const uint32_t*>(smem + sb + ((g_rowsw ^ (uint32_t)((kk >> 5) << 4)) + ((kk & 31) >> 3) * 4));
   };
-  auto g_sword = [&](const unsigned char* base, int kk) {
-    return *reinterpret_cast<const uint32_t*>(base + g_srow + (kk >> 6) * 32 * NJ * 4);
+  auto g_sword = [&](uint32_t sb, int kk) {
+    return *reinterpret_cast<const uint32_t*>(smem + sb + g_srow + (kk >> 6) * 32 * NJ * 4);
   };
-  // code nibble of K-offset kk from its chunk, scale byte from its word
-  // (kk uniform: the selects and shifts take scalar operands)
-  auto g_code = [&](const u32x4& ch, int kk) {
-    const int u = (kk & 31) >> 3;
-    const uint32_t w01 = (u & 1) ? ch[1] : ch[0], w23 = (u & 1) ? ch[3] : ch[2];
-    return ((u & 2) ? w23 : w01) >> (4 * (kk & 7)) & 15u;
-  };
-  auto g_sbyte = [&](uint32_t w, int kk) { return (w >> (8 * ((kk >> 4) & 3))) & 0xFFu; };
-  auto ws_value = [&](uint32_t code, uint32_t sbyte) {
+  // the element as an exact fp16 value from its code word and scale word
+  auto ws_value = [&](uint32_t cw, uint32_t sw, int kk) {
+    const uint32_t code = (cw >> (4 * (kk & 7))) & 15u;
+    const uint32_t sbyte = (sw >> (8 * ((kk >> 4) & 3))) & 0xFFu;
     const f16x2 v = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(code, 1.0f, 0);
     const f16x2 sc = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbyte, 1.0f, false);
     return (_Float16)(v[0] * sc[0]);                          // exact: see the header
   };
   struct Gather {
-    u32x4 chunk[4];
-    uint32_t sword[4];
+    uint32_t cw[4], sw[4];
     int j0, n, kk[4];
   };
   auto gather_read = [&](int slot, u32x2 t, Gather& g) {
-    const unsigned char* base = smem + slot * STAGE;
+    const uint32_t sb = (uint32_t)(slot * STAGE);
     g.j0 = __builtin_amdgcn_readfirstlane((int)(t[0] & 0xFFu));
     g.n = __builtin_amdgcn_readfirstlane((int)(t[0] >> 8));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       g.kk[q] = __builtin_amdgcn_readfirstlane((int)((t[1] >> (8 * q)) & 0x7Fu));
-      g.chunk[q] = g_chunk(base, g.kk[q]);
-      g.sword[q] = g_sword(base, g.kk[q]);
+      g.cw[q] = g_cword(sb, g.kk[q]);
+      g.sw[q] = g_sword(sb, g.kk[q]);
     }
   };
   // entries past the stage's count go to the row's padding halves (no
@@ -463,17 +464,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   auto gather_write = [&](const Gather& g) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-      WS[tid * WSS + (q < g.n ? g.j0 + q : KQ * 16 + q)] =
-          ws_value(g_code(g.chunk[q], g.kk[q]), g_sbyte(g.sword[q], g.kk[q]));
+      WS[tid * WSS + (q < g.n ? g.j0 + q : KQ * 16 + q)] = ws_value(g.cw[q], g.sw[q], g.kk[q]);
   };
   // channels past the first four of a stage (rare; at the end of the stage)
   auto gather_rest = [&](int m, int slot, const Gather& g) {
     if (g.n > 4) {                                            // uniform
-      const unsigned char* base = smem + slot * STAGE;
+      const uint32_t sb = (uint32_t)(slot * STAGE);
       for (int jj = g.j0 + 4; jj < g.j0 + g.n; ++jj) {
         const int kk = sel[jj] - m * KS;
         if ((unsigned)kk < (unsigned)KS)                      // false only if sel is not ascending
-          WS[tid * WSS + jj] = ws_value(g_code(g_chunk(base, kk), kk), g_sbyte(g_sword(base, kk), kk));
+          WS[tid * WSS + jj] = ws_value(g_cword(sb, kk), g_sword(sb, kk), kk);
       }
     }
   };
@@ -533,22 +533,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
         read_words(base + sb_off, SWB, IntC<NJ>{});
       }
     };
-    // scale pairs of stage m: in the half-full last stage the words of lane
-    // half 1 (blocks past K) are zero, and rows with a bad index have zero
-    // scales
-    auto convert_scales = [&](int m) {
-      const uint32_t hm = (m == mh && half) ? 0u : ~0u;
+    // scale pairs of the stage whose words were read last (the loads left
+    // zeros for the blocks past K and for rows with a bad index)
+    auto convert_scales = [&]() {
 #pragma unroll
       for (int i = 0; i < MA; ++i) {
-        const uint32_t w = SWA[i] & hm & amask[i];
-        SCA[i][0] = scale_pair<0>(w);
-        SCA[i][1] = scale_pair<1>(w);
+        SCA[i][0] = scale_pair<0>(SWA[i]);
+        SCA[i][1] = scale_pair<1>(SWA[i]);
       }
 #pragma unroll
       for (int j = 0; j < NB; ++j) {
-        const uint32_t w = SWB[j] & hm;
-        SCB[j][0] = scale_pair<0>(w);
-        SCB[j][1] = scale_pair<1>(w);
+        SCB[j][0] = scale_pair<0>(SWB[j]);
+        SCB[j][1] = scale_pair<1>(SWB[j]);
       }
     };
     // operands of substep q = 4 t + u into buffer D[q & 1]
@@ -611,25 +607,43 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
       gather_rest(0, 0, gth);
       tnext = tab[1];
     }
-    convert_scales(0);
+    convert_scales();
     dequant(IntC<0>{});
     __builtin_amdgcn_sched_barrier(0);
 
     int slot = 0;                               // uniform: slot offsets are scalar adds
+    // LDS reads that go out beside the MFMAs of substep 3 (the chunk-0
+    // fragments and the scale words of the next stage, the gather's words)
+    // and of substep 7 (the chunk-1 fragments)
+    constexpr int NDS3 = MA + NB + (MA > 0 ? 2 : 0) + (COMP ? 8 : 0);
+    constexpr int NDS7 = MA + NB;
     for (int m = 0; m < nst; ++m) {
       const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
       substep(IntC<0>{}, IntC<1>{}, nothing, IntC<0>{});
       substep(IntC<1>{}, IntC<2>{}, nothing, IntC<0>{});
       substep(IntC<2>{}, IntC<3>{}, nothing, IntC<0>{});
-      // chunk-0 registers are free: stage m + 1 in, stage m + NSLOT out
+      // chunk-0 registers are free: stage m + 1 in, stage m + NSLOT out.  The
+      // loads and the LDS reads go out between the MFMAs of substep 3, so the
+      // matrix core keeps working across the barrier's aftermath.
       wait_vm_lgkm0<(NSLOT - 2) * LPW>();
       asm volatile("s_barrier" ::: "memory");
+      mfmas(IntC<3>{});
+      dequant(IntC<4>{});
       issue(m + NSLOT < nst ? m + NSLOT : nst - 1, slot);
       read_raw(nslot, IntC<0>{});
       read_scales(nslot);
       if constexpr (COMP) gather_read(nslot, tnext, gth);
+      if constexpr (NMF > 0) {
+#pragma unroll
+        for (int k = 0; k < NMF; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x020, (LPW + NMF - 1) / NMF, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, (NDS3 + NMF - 1) / NMF, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + NMF - 1) / NMF, 0);
+        }
+      }
       __builtin_amdgcn_sched_barrier(0);
-      substep(IntC<3>{}, IntC<4>{}, nothing, IntC<0>{});
+      pin(IntC<4>{});
       substep(IntC<4>{}, IntC<5>{}, nothing, IntC<0>{});
       // the gather reads issued at substep 3 are in by now
       if constexpr (COMP) {
@@ -638,17 +652,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
         substep(IntC<5>{}, IntC<6>{}, nothing, IntC<0>{});
       }
       substep(IntC<6>{}, IntC<7>{}, nothing, IntC<0>{});
-      read_raw(nslot, IntC<1>{});
-      __builtin_amdgcn_sched_barrier(0);
-      // the last substep dequantizes the next stage's first operands: its
-      // scale pairs are converted first (the current ones are used up)
+      // the last substep dequantizes the next stage's first operands (its
+      // scale pairs are converted first: the current ones are used up) and
+      // reads the next stage's chunk-1 fragments (chunk 1 of this stage was
+      // dequantized in substep 6)
       mfmas(IntC<7>{});
-      convert_scales(m + 1);
+      read_raw(nslot, IntC<1>{});
+      convert_scales();
       dequant(IntC<0>{});
       if constexpr (NMF > 0) {
 #pragma unroll
         for (int k = 0; k < NMF; ++k) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, (NDS7 + NMF - 1) / NMF, 0);
           __builtin_amdgcn_sched_group_barrier(0x002, (NVALU + 2 * (MA + NB) + NMF - 1) / NMF, 0);
         }
       }
