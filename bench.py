@@ -56,17 +56,20 @@ def profiled_traffic(workload, kernel):
     return float(fields["traffic_bytes_per_launch"])
 
 
-def gemm_kernel_name(rows, experts, epilogue, fmt="nvfp4"):
+def gemm_kernel_name(rows, experts, epilogue, fmt="nvfp4", k=4096, kc=64):
     """Name of the grouped-GEMM kernel instance the library picks: rows per
     tile from the average rows per expert (>= 160: 256, >= 64: 128,
-    >= 24: 64, else 32), epilogue 1 = SwiGLU, 2 = scatter."""
+    >= 24: 64, else 32), epilogue 1 = SwiGLU, 2 = scatter, and the gather
+    width (8 when the 128-K stages hold more than 3 selected channels on
+    average, else 4)."""
     avg = rows // max(experts, 1)
     cfg = "4, 4, 2, 2" if avg >= 160 else "2, 4, 2, 2" if avg >= 64 else \
           "1, 4, 2, 2" if avg >= 24 else "1, 2, 1, 4"
     if fmt == "mxfp4":     # compensated (the bench always compensates)
         return f"nvfp4::mxg::mx_grouped_gemm_kernel<{cfg}, {epilogue}, true, false>"
-    # <MI, NJ, WM, WN, LDS slots, epilogue, compensation substeps> (kc = 64)
-    return f"nvfp4::nvg::grouped_gemm_kernel<{cfg}, 3, {epilogue}, 4>"
+    # <MI, NJ, WM, WN, LDS slots, epilogue, compensation substeps, gather width>
+    gw = 8 if kc * 128 > 3 * k else 4
+    return f"nvfp4::nvg::grouped_gemm_kernel<{cfg}, 3, {epilogue}, {4 if kc <= 64 else 8}, {gw}>"
 
 
 def gemm_flops(rows, n, k, kc):
@@ -743,7 +746,7 @@ def mask_bench(args, torch, P, synth, wl, dev):
         parts=parts, mask_overhead_vs_main_gemm=overhead,
         roofline=dict(bound="mfma", achieved=round(ach, 2), peak=2500.0, unit="TFLOP/s",
                       frac=round(ach / 2500.0, 4), traffic=None, mfma_dtype="fp16",
-                      kernel="nvfp4::nvg::grouped_gemm_kernel<4, 4, 2, 2, 3, 0, 0> (masked second GEMM)"),
+                      kernel="nvfp4::nvg::grouped_gemm_kernel<4, 4, 2, 2, 3, 0, 0, 4> (masked second GEMM)"),
         cpu_baseline=cpu)
 
 
@@ -913,7 +916,7 @@ def main():
     # largest single kernel of the step).  Its part also holds the 1-thread
     # fill that zeroes out_amax (about 2 us).
     ach = work["gemm_gate_up"]["flops"] / (parts_ms["gemm_gate_up"] * 1e-3) / 1e12
-    kname = gemm_kernel_name(inp["rows"], wl.experts, 1, wl.fmt)
+    kname = gemm_kernel_name(inp["rows"], wl.experts, 1, wl.fmt, k=wl.hidden, kc=wl.k)
     traffic = profiled_traffic(wl.name, kname)
     mx = wl.fmt == "mxfp4"
     peak = FP4_PEAK_TFLOPS if mx else FP16_PEAK_TFLOPS

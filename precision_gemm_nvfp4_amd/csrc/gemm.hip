@@ -123,12 +123,6 @@ struct IntC {
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __amdgpu_buffer_rsrc_t Rsrc;
 constexpr uint32_t OOB = 0x80000000u;       // vector offset past every scale array
-__device__ __forceinline__ Rsrc make_rsrc(const void* base, int64_t bytes) {
-  // raw buffer (stride 0), 32-bit data format: what untyped loads need on gfx9
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0,
-                                           (int)(uint32_t)(bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll),
-                                           0x00020000);
-}
 __device__ __forceinline__ void load_lds16(Rsrc r, uint32_t voff, int soff, unsigned char* l) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 16, voff, soff, 0, 0);
 }
@@ -167,19 +161,21 @@ __device__ __forceinline__ void pin_regs(f16x8 (&v)[N]) {
 }
 
 // LDS bytes of the K-loop region: slots, dummy, W_S (fp16 [BN][kq*16 + 8]),
-// sel [MAX_KC], the per-stage gather table [nst + 2] (8 bytes each), and the
+// sel [MAX_KC], the per-stage gather table [nst + 2] (16 bytes each), and the
 // Q(R_S) codes [BM][kc / 2].
 template <int BM, int NSLOT, int KQ>
 __host__ __device__ constexpr size_t loop_lds_bytes(int64_t K) {
   return (size_t)NSLOT * Layout<BM>::STAGE + DUMMY_BYTES +
          (KQ > 0 ? (size_t)BN * (KQ * 16 + 8) * 2 + (size_t)MAX_KC * 4 : 0) +
-         ((((size_t)((K + KS - 1) / KS) + 2) * 8 + 15) / 16 * 16) +
+         (((size_t)((K + KS - 1) / KS) + 2) * 16) +
          (KQ > 0 ? (size_t)BM * KQ * 8 : 0);
 }
 
 // EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows).  KQ: 0 without
-// compensation, else the largest kc / 16 handled.
-template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ>
+// compensation, else the largest kc / 16 handled.  GW: selected channels per
+// stage that the gather takes beside the MFMAs (4 or 8; more take a slower
+// loop at the stage's end).
+template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ, int GW>
 __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
@@ -187,17 +183,18 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   using L = Layout<BM>;
   constexpr int STAGE = L::STAGE, LPW = L::LPW;
   constexpr bool COMP = KQ > 0;
+  static_assert(GW == 4 || GW == 8, "gather width");
   constexpr int WSS = KQ * 16 + 8;                        // W_S row stride (halves)
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   unsigned char* DUMMY = smem + NSLOT * STAGE;
   _Float16* WS = reinterpret_cast<_Float16*>(DUMMY + DUMMY_BYTES);
   int32_t* sel = reinterpret_cast<int32_t*>(WS + (COMP ? BN * WSS : 0));
   // gather table: per stage the first selected channel j0 and their count
-  // n (j0 | n << 8) and the in-stage offsets of the first four (7 bits each)
-  u32x2* tab = reinterpret_cast<u32x2*>(sel + (COMP ? MAX_KC : 0));
+  // n (j0 | n << 8), then the in-stage offsets of the first eight (one byte
+  // each, words 1 and 2)
+  u32x4* tab = reinterpret_cast<u32x4*>(sel + (COMP ? MAX_KC : 0));
   // Q(R_S) codes of the tile's rows [BM][kc / 2], 16-byte aligned, after tab
-  unsigned char* RSC = reinterpret_cast<unsigned char*>(
-      (reinterpret_cast<uintptr_t>(tab + ((p.K + KS - 1) / KS) + 2) + 15) & ~static_cast<uintptr_t>(15));
+  unsigned char* RSC = reinterpret_cast<unsigned char*>(tab + ((p.K + KS - 1) / KS) + 2);
   float* RW = reinterpret_cast<float*>(smem + p.rw_lds_offset);
 
   const int tid = threadIdx.x;
@@ -319,9 +316,9 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     };
     for (int s = tid; s <= nst + 1; s += 256) {
       const int j0 = lower((int64_t)s * KS), n = lower((int64_t)(s + 1) * KS) - j0;
-      uint32_t kk = 0;
-      for (int q = 0; q < 4 && q < n; ++q) kk |= (uint32_t)((sel[j0 + q] - s * KS) & 0x7F) << (8 * q);
-      tab[s] = u32x2{(uint32_t)j0 | ((uint32_t)n << 8), kk};
+      uint32_t kk[2] = {0, 0};
+      for (int q = 0; q < 8 && q < n; ++q) kk[q >> 2] |= (uint32_t)((sel[j0 + q] - s * KS) & 0x7F) << (8 * (q & 3));
+      tab[s] = u32x4{(uint32_t)j0 | ((uint32_t)n << 8), kk[0], kk[1], 0u};
     }
   }
 
@@ -379,12 +376,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     }
   };
 
-  // Q(R_S) codes of the tile's rows (a contiguous byte range of r_codes) go
-  // into LDS by direct loads ahead of the stages (4 bytes a lane; words past
-  // the end of r_codes read as zeros: those rows are never stored).  Their
-  // scale bytes go into registers (used after the K loop): in compensation
-  // substep q (16 compact channels) lane half h takes channels 16 q + 8 h ..
-  // + 7, i.e. code word 2 q + h of the row and scale byte q.
+  // The first NSLOT stages go out (stages past the end repeat the last one
+  // into slots nobody reads, so every wave issues the same count).  Between
+  // stage 0 and the others, the Q(R_S) codes of the tile's rows (a contiguous
+  // byte range of r_codes) go into LDS by direct loads (4 bytes a lane; words
+  // past the end of r_codes read as zeros: those rows are never stored) and
+  // their scale bytes into registers, all used after the K loop: the wait for
+  // stage 0 covers them, the loop's waits for later stages are unchanged.  In
+  // compensation substep q (16 compact channels) lane half h takes channels
+  // 16 q + 8 h .. + 7, i.e. code word 2 q + h of the row and scale byte q.
+  issue(0, 0);
   constexpr int KQW = COMP ? KQ : 1;
   uint32_t rqs[MI][(KQW + 3) / 4];
   if constexpr (COMP) {
@@ -393,26 +394,29 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     const int nword = BM * (kc / 8);                            // words of the tile
     for (int w0 = wave * 64; w0 < nword; w0 += 256)             // uniform trip count per wave
       load_lds4(r_rc, 4u * (uint32_t)(w0 + lane), 0, RSC + 4 * w0);
+    const int sb = kc / 16;                                     // scale bytes per row
+    const Rsrc r_rs = make_rsrc(p.r_scales + row0 * sb, (p.rows_total - row0) * sb);
+    const bool words = (sb & 3) == 0 && (reinterpret_cast<uintptr_t>(p.r_scales) & 3) == 0;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int r = wm * MI * 32 + i * 32 + l32;
-      const bool live = r < rows_valid;
-      const int64_t ur = row0 + (live ? r : 0);
+      const uint32_t rb = (uint32_t)((wm * MI * 32 + i * 32 + l32) * sb);
 #pragma unroll
       for (int w = 0; w < (KQ + 3) / 4; ++w) {
         uint32_t v = 0;
+        if (words) {                                            // uniform
+          if (16 * 4 * w < kc) v = __builtin_amdgcn_raw_buffer_load_b32(r_rs, (int)(rb + 4 * w), 0, 0);
+        } else {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-          if (live && 16 * (4 * w + b) < kc) v |= (uint32_t)p.r_scales[ur * (kc / 16) + 4 * w + b] << (8 * b);
+          for (int b = 0; b < 4; ++b)
+            if (16 * (4 * w + b) < kc)
+              v |= (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r_rs, (int)(rb + 4 * w + b), 0, 0) << (8 * b);
+        }
         rqs[i][w] = v;
       }
     }
   }
-
-  // the first NSLOT stages go out (stages past the end repeat the last one
-  // into slots nobody reads, so every wave issues the same count)
 #pragma unroll
-  for (int q = 0; q < NSLOT; ++q) issue(q < nst ? q : nst - 1, q);
+  for (int q = 1; q < NSLOT; ++q) issue(q < nst ? q : nst - 1, q);
 
   // W_S gather of a stage: thread t copies the selected channels of weight
   // row t that fall in the stage, as exact fp16 values.  Weight row t's
@@ -420,11 +424,11 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   // g_rowsw ^ (c << 4) with the swizzle bits folded into g_rowsw (the row base
   // is a multiple of 64, so the XOR only touches bits 4-5); its scale word h
   // at position ((wn 2 + h) 32 + l32) NJ + j for t = wn NJ 32 + 32 j + l32.
-  // The first four channels of a stage come from the gather table: the code
+  // The first GW channels of a stage come from the gather table: the code
   // word and scale word of each are read right after the barrier that makes
   // the stage visible, and the nibble and the scale byte are picked out
   // (uniform positions) and written to W_S two substeps later, so nothing
-  // waits on LDS latency.  More than four channels in one stage take a slower
+  // waits on LDS latency.  More than GW channels in one stage take a slower
   // loop.
   const uint32_t g_rowsw = (uint32_t)(L::B_OFF + tid * 64 + (swz(tid) << 4));
   const uint32_t g_srow = (uint32_t)(L::BS_OFF + (((tid / (NJ * 32)) * 2 * 32 + tid % 32) * NJ + (tid % (NJ * 32)) / 32) * 4);
@@ -445,16 +449,16 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     return (_Float16)(v[0] * sc[0]);                          // exact: see the header
   };
   struct Gather {
-    uint32_t cw[4], sw[4];
-    int j0, n, kk[4];
+    uint32_t cw[GW], sw[GW];
+    int j0, n, kk[GW];
   };
-  auto gather_read = [&](int slot, u32x2 t, Gather& g) {
+  auto gather_read = [&](int slot, u32x4 t, Gather& g) {
     const uint32_t sb = (uint32_t)(slot * STAGE);
     g.j0 = __builtin_amdgcn_readfirstlane((int)(t[0] & 0xFFu));
     g.n = __builtin_amdgcn_readfirstlane((int)(t[0] >> 8));
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      g.kk[q] = __builtin_amdgcn_readfirstlane((int)((t[1] >> (8 * q)) & 0x7Fu));
+    for (int q = 0; q < GW; ++q) {
+      g.kk[q] = __builtin_amdgcn_readfirstlane((int)((t[1 + q / 4] >> (8 * (q % 4))) & 0x7Fu));
       g.cw[q] = g_cword(sb, g.kk[q]);
       g.sw[q] = g_sword(sb, g.kk[q]);
     }
@@ -463,14 +467,14 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   // branch: this runs beside MFMAs)
   auto gather_write = [&](const Gather& g) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < GW; ++q)
       WS[tid * WSS + (q < g.n ? g.j0 + q : KQ * 16 + q)] = ws_value(g.cw[q], g.sw[q], g.kk[q]);
   };
-  // channels past the first four of a stage (rare; at the end of the stage)
+  // channels past the first GW of a stage (rare; at the end of the stage)
   auto gather_rest = [&](int m, int slot, const Gather& g) {
-    if (g.n > 4) {                                            // uniform
+    if (g.n > GW) {                                           // uniform
       const uint32_t sb = (uint32_t)(slot * STAGE);
-      for (int jj = g.j0 + 4; jj < g.j0 + g.n; ++jj) {
+      for (int jj = g.j0 + GW; jj < g.j0 + g.n; ++jj) {
         const int kk = sel[jj] - m * KS;
         if ((unsigned)kk < (unsigned)KS)                      // false only if sel is not ascending
           WS[tid * WSS + jj] = ws_value(g_cword(sb, kk), g_sword(sb, kk), kk);
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     read_raw(0, IntC<1>{});
     read_scales(0);
     [[maybe_unused]] Gather gth;
-    [[maybe_unused]] u32x2 tnext = u32x2{0, 0};
+    [[maybe_unused]] u32x4 tnext = u32x4{0, 0, 0, 0};
     if constexpr (COMP) {
       gather_read(0, tab[0], gth);
       gather_write(gth);
@@ -615,7 +619,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
     // LDS reads that go out beside the MFMAs of substep 3 (the chunk-0
     // fragments and the scale words of the next stage, the gather's words)
     // and of substep 7 (the chunk-1 fragments)
-    constexpr int NDS3 = MA + NB + (MA > 0 ? 2 : 0) + (COMP ? 8 : 0);
+    constexpr int NDS3 = MA + NB + (MA > 0 ? 2 : 0) + (COMP ? 2 * GW : 0);
     constexpr int NDS7 = MA + NB;
     for (int m = 0; m < nst; ++m) {
       const int nslot = slot == NSLOT - 1 ? 0 : slot + 1;
@@ -647,7 +651,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
       substep(IntC<4>{}, IntC<5>{}, nothing, IntC<0>{});
       // the gather reads issued at substep 3 are in by now
       if constexpr (COMP) {
-        substep(IntC<5>{}, IntC<6>{}, [&] { gather_write(gth); tnext = tab[m + 2]; }, IntC<40>{});
+        substep(IntC<5>{}, IntC<6>{}, [&] { gather_write(gth); tnext = tab[m + 2]; }, IntC<10 * GW>{});
       } else {
         substep(IntC<5>{}, IntC<6>{}, nothing, IntC<0>{});
       }
@@ -694,51 +698,64 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   }
   __syncthreads();                             // W_S complete; LDS free afterwards
 
-  // ---- global scales and the compensation -------------------------------------
+  // ---- global scales, the compensation and the epilogue ------------------------
   const float ga = p.a_global[p.a_global_per_group ? e : 0];
   const float gw = p.w_global[e];
-  float scale = ga * gw;
-  if constexpr (COMP) {
-    const float sa = ga * gw, sr = p.r_global[e] * gw;
-    // per 32 x 32 block the correction corr = sum_q R_q W_S,q (Q(R_S)
-    // operands dequantized per block: few registers beside the accumulators)
-    // and acc = acc * gA gW + corr * gR gW
+  const float scale = COMP ? 1.0f : ga * gw;
+  // Row block i's compensation: corr = sum_q R_q W_S,q per 32 x 32 block (the
+  // Q(R_S) operands of the block's rows dequantized once, the W_S operands
+  // read per block), then acc = acc * gA gW + corr * gR gW, so no ratio of
+  // global scales can overflow.  Substeps past kc add zero: their scale bytes
+  // are 0 and the padding channels of W_S are 0 (the code words read stay
+  // inside the Q(R_S) region).
+  auto prep = [&](int i) {
+    if constexpr (COMP) {
+      const float sa = ga * gw, sr = p.r_global[e] * gw;
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(RSC + (wm * MI * 32 + i * 32 + l32) * (kc / 2));
+      f16x8 rf[KQ];
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) {
-      const int r = wn * NJ * 32 + j * 32 + l32;
-      f16x8 WF[KQ];
+      for (int q = 0; q < KQ; ++q) {
+        const uint32_t sbyte = (rqs[i][q >> 2] >> (8 * (q & 3))) & 0xFFu;
+        rf[q] = dequant8(cw[2 * q + half], __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbyte, 1.0f, false)[0]);
+      }
 #pragma unroll
-      for (int q = 0; q < KQ; ++q)
-        WF[q] = *reinterpret_cast<const f16x8*>(WS + r * WSS + 16 * q + 8 * half);
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const uint32_t* cw = reinterpret_cast<const uint32_t*>(RSC + (wm * MI * 32 + i * 32 + l32) * (kc / 2));
+      for (int j = 0; j < NJ; ++j) {
+        const _Float16* wsr = WS + (wn * NJ * 32 + j * 32 + l32) * WSS + 8 * half;
         f32x16 corr;
 #pragma unroll
         for (int v = 0; v < 16; ++v) corr[v] = 0.0f;
-        // substeps past kc add zero: their scale bytes are 0 and the
-        // padding channels of W_S are 0 (the code words read stay inside the
-        // Q(R_S) region)
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-          const uint32_t sbyte = (rqs[i][q >> 2] >> (8 * (q & 3))) & 0xFFu;
-          const f16x8 rf = dequant8(cw[2 * q + half], __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sbyte, 1.0f, false)[0]);
-          corr = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf, WF[q], corr, 0, 0, 0);
-        }
+        for (int q = 0; q < KQ; ++q)
+          corr = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf[q], *reinterpret_cast<const f16x8*>(wsr + 16 * q), corr,
+                                                        0, 0, 0);
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * sa + corr[v] * sr;
-        __builtin_amdgcn_sched_barrier(0);      // one block at a time: few live registers
       }
     }
-    scale = 1.0f;
-    __syncthreads();                           // W_S reads done before the epilogue staging
+  };
+  // Row blocks are compensated right before their output leaves, unless the
+  // epilogue's LDS staging (per wave: 32 rows of bf16 h for SwiGLU, of fp32
+  // otherwise) reaches past the slot ring into W_S and is used (SwiGLU, or
+  // an F32 tile that does not store straight from the accumulators): then
+  // all row blocks first.
+  constexpr size_t WAVE_STAGE = EPI == 1 ? (size_t)32 * (NJ * 16 + 8) * 2 : (size_t)epilogue_wave_floats<NJ>() * 4;
+  constexpr bool STAGING_OVERLAPS = COMP && 4 * WAVE_STAGE > (size_t)NSLOT * STAGE + DUMMY_BYTES;
+  bool early = false;
+  if constexpr (STAGING_OVERLAPS) early = EPI == 1 || !epilogue_direct<MI, BN, EPI>(p, tc);
+  if (early) {                                   // uniform over the workgroup
+#pragma unroll
+    for (int i = 0; i < MI; ++i) prep(i);
+    __syncthreads();                             // W_S reads done before the staging writes
   }
-
-  gemm_epilogue<MI, NJ, BN, EPI>(p, acc, tc, wm * MI * 32, wn * NJ * 32, scale,
-                                 reinterpret_cast<float*>(smem) + wave * epilogue_wave_floats<NJ>(), RW);
+  gemm_epilogue_blocks<MI, NJ, BN, EPI>(
+      p, tc, wm * MI * 32, wn * NJ * 32, reinterpret_cast<float*>(smem + wave * WAVE_STAGE), RW,
+      [&](int i) {
+        if (!early) prep(i);
+      },
+      [&](int i, int j, int q) { return acc[i][j][q] * scale; });
 }
 
-template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ>
+template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ, int GW>
 static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   constexpr int BM = WM * MI * 32;
   const int64_t mtiles = (a.rows_total + BM - 1) / BM + a.E;
@@ -750,7 +767,7 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   a.rw_lds_offset = (int)body;
   const size_t lds = body + (EPI == 2 ? (size_t)BM * 4 : 0);
   if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
-  auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, NSLOT, EPI, KQ>;
+  auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, NSLOT, EPI, KQ, GW>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
@@ -759,20 +776,26 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   return hipGetLastError();
 }
 
-template <int MI, int NJ, int WM, int WN, int NSLOT, int KQ>
+template <int MI, int NJ, int WM, int WN, int NSLOT, int KQ, int GW>
 static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
   switch (a.epilogue) {
-    case 0: return launch_cfg<MI, NJ, WM, WN, NSLOT, 0, KQ>(a, stream);
-    case 1: return launch_cfg<MI, NJ, WM, WN, NSLOT, 1, KQ>(a, stream);
-    default: return launch_cfg<MI, NJ, WM, WN, NSLOT, 2, KQ>(a, stream);
+    case 0: return launch_cfg<MI, NJ, WM, WN, NSLOT, 0, KQ, GW>(a, stream);
+    case 1: return launch_cfg<MI, NJ, WM, WN, NSLOT, 1, KQ, GW>(a, stream);
+    default: return launch_cfg<MI, NJ, WM, WN, NSLOT, 2, KQ, GW>(a, stream);
   }
 }
 
+// The gather takes 8 channels per stage beside the MFMAs where the stages
+// hold more than 3 selected channels on average (e.g. 64 of K = 1536), else 4.
 template <int MI, int NJ, int WM, int WN, int NSLOT>
 static hipError_t launch_comp(const GemmArgs& a, hipStream_t stream) {
-  if (!a.sel_idx) return launch_epi<MI, NJ, WM, WN, NSLOT, 0>(a, stream);
-  if (a.kc <= 64) return launch_epi<MI, NJ, WM, WN, NSLOT, 4>(a, stream);
-  return launch_epi<MI, NJ, WM, WN, NSLOT - 1, 8>(a, stream);   // a wider W_S: one slot fewer
+  if (!a.sel_idx) return launch_epi<MI, NJ, WM, WN, NSLOT, 0, 4>(a, stream);
+  const bool wide = (int64_t)a.kc * KS > 3 * a.K;
+  if (a.kc <= 64)
+    return wide ? launch_epi<MI, NJ, WM, WN, NSLOT, 4, 8>(a, stream) : launch_epi<MI, NJ, WM, WN, NSLOT, 4, 4>(a, stream);
+  // a wider W_S: one slot fewer
+  return wide ? launch_epi<MI, NJ, WM, WN, NSLOT - 1, 8, 8>(a, stream)
+              : launch_epi<MI, NJ, WM, WN, NSLOT - 1, 8, 4>(a, stream);
 }
 
 }  // namespace nvg

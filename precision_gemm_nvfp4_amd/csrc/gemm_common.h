@@ -17,12 +17,42 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
 }
 
+// A raw buffer resource (stride 0, 32-bit data format, what untyped loads
+// and stores need on gfx9) over `bytes` bytes from `base`.  Every field goes
+// through readfirstlane: a resource must sit in scalar registers, and a value
+// the compiler happened to compute on the vector unit would otherwise cost a
+// loop over its distinct values around every instruction that uses it.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane(
+      (uint32_t)(bytes < 0 ? 0 : (bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                           0x00020000);
+}
+
 struct TileCoord {
   int e;            // expert
   int n_tile;
   int64_t row0;     // first unit row of the tile
   int rows_valid;   // rows of the tile inside the expert's group
 };
+
+// The coordinates as visibly uniform values (they come out of LDS, which the
+// compiler cannot prove uniform): scalar registers for everything derived
+// from them, e.g. buffer resources, which would otherwise need a loop per
+// instruction over the distinct values.
+__device__ __forceinline__ TileCoord uniform_tile(TileCoord t) {
+  TileCoord u;
+  u.e = __builtin_amdgcn_readfirstlane(t.e);
+  u.n_tile = __builtin_amdgcn_readfirstlane(t.n_tile);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)(uint64_t)t.row0);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)t.row0 >> 32));
+  u.row0 = (int64_t)(((uint64_t)hi << 32) | lo);
+  u.rows_valid = __builtin_amdgcn_readfirstlane(t.rows_valid);
+  return u;
+}
 
 // m-tiles of BM rows of expert e's group, for the threads of a 256-thread
 // workgroup in chunks of 256 experts.
@@ -141,7 +171,7 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int ntiles, TileCoor
   const int logical = ((int)blockIdx.x % 8) * per_xcd + jt;
   if (jt >= per_xcd || logical >= real) return false;
   if (p.E > 256) {
-    t = locate_tile<BM>(p, ntiles, logical);
+    t = uniform_tile(locate_tile<BM>(p, ntiles, logical));
     return true;
   }
   const uint32_t m_key = (uint32_t)(logical / ntiles);
@@ -158,6 +188,7 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int ntiles, TileCoor
   t.n_tile = sh_nt;
   t.row0 = sh_g0 + (int64_t)sh_mt * BM;
   t.rows_valid = (int)((sh_g1 - t.row0) < BM ? (sh_g1 - t.row0) : BM);
+  t = uniform_tile(t);
   return true;
 }
 
@@ -182,34 +213,84 @@ template <int NJ>
 constexpr int epilogue_wave_floats() { return 32 * (NJ * 32 + 8); }
 
 // Epilogue of a wave's MI x NJ blocks of 32 x 32 (tile rows wr0 + 32 i ..,
-// tile columns wc0 + 32 j ..).  MFMA 32x32 output element q of lane l sits at
-// row (q / 4) * 8 + (l / 32) * 4 + q % 4 and column l % 32 of its block.
-// Each 32-row block goes through the wave's own LDS region (lds, wave-private,
-// epilogue_wave_floats<NJ>() floats) so that it leaves as whole row segments
-// with 16-byte stores (a store per element would write 4 bytes per lane
-// into rows far apart).  The caller has synchronized the workgroup, so the
-// region is free.  rw_lds: the tile's row weights (scatter epilogue).
-template <int MI, int NJ, int BN, int EPI>
-__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&acc)[MI][NJ],
-                                              const TileCoord& t, int wr0, int wc0, float scale,
-                                              float* lds, const float* rw_lds) {
+// tile columns wc0 + 32 j ..), block row by block row: prep(i) runs first
+// (e.g. the compensation of row block i), then val(i, j, q) gives output
+// element q of block (i, j) in fp32.  MFMA 32x32 output element q of lane l
+// sits at row (q / 4) * 8 + (l / 32) * 4 + q % 4 and column l % 32 of its
+// block.  rw_lds: the tile's row weights (scatter epilogue).  The caller has
+// synchronized the workgroup, so `lds` (the wave's own region of
+// epilogue_wave_floats<NJ>() floats) is free.
+//
+// F32 and scatter rows: when the tile's columns lie inside N and nothing is
+// accumulated, every element goes straight out with one 4-byte buffer store
+// per (block, q) (a 32-lane half writes one 128-byte row segment), through a
+// buffer resource that ends at the last valid row, so rows past the group
+// are dropped by the hardware and the stores need no branches.  Otherwise
+// each 32-row block goes through LDS and leaves as whole row segments with
+// 16-byte stores.
+// Whether the F32 / scatter epilogue of this tile stores straight from the
+// accumulators (the tile's columns inside N, nothing accumulated, row offsets
+// within 31 bits); the same for every wave of the tile.
+template <int MI, int BN, int EPI>
+__device__ __forceinline__ bool epilogue_direct(const GemmArgs& p, const TileCoord& t) {
+  if constexpr (EPI == 1) {
+    return false;
+  } else {
+    const int64_t ld = EPI == 2 ? p.N : p.ldo;
+    return (EPI == 2 || !p.accumulate) && (int64_t)(t.n_tile + 1) * BN <= p.N && ld * 4 * MI * 32 < (1ll << 31);
+  }
+}
+
+template <int MI, int NJ, int BN, int EPI, typename Prep, typename Val>
+__device__ __forceinline__ void gemm_epilogue_blocks(const GemmArgs& p, const TileCoord& t, int wr0, int wc0,
+                                                     float* lds, const float* rw_lds, Prep&& prep, Val&& val) {
   constexpr int CS = NJ * 32 + 8;               // LDS row stride (floats)
   const int lane = threadIdx.x & 63, half = lane >> 5, l32 = lane & 31;
   if constexpr (EPI == 0 || EPI == 2) {
     constexpr bool scatter = EPI == 2;
     float* out = scatter ? p.y_rows : static_cast<float*>(p.out);
     const int64_t ld = scatter ? p.N : p.ldo;
-    const bool vec = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
     const int64_t n0 = (int64_t)t.n_tile * BN + wc0;     // first column of the wave
+    if (epilogue_direct<MI, BN, EPI>(p, t)) {
+      // rows wr0 .. rows_valid - 1 of the tile, as bytes from row wr0
+      const int nrows = t.rows_valid - wr0 < 0 ? 0 : (t.rows_valid - wr0 > MI * 32 ? MI * 32 : t.rows_valid - wr0);
+      const __amdgpu_buffer_rsrc_t r_out = make_rsrc(out + (t.row0 + wr0) * ld, (int64_t)nrows * ld * 4);
+      const uint32_t voff = (uint32_t)(((int64_t)half * 4 * ld + n0 + l32) * 4);
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        prep(i);
+        float w[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) w[q] = 1.0f;
+        if constexpr (scatter) {
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 v = *reinterpret_cast<const f32x4*>(rw_lds + wr0 + i * 32 + g * 8 + half * 4);
+            w[4 * g] = v[0]; w[4 * g + 1] = v[1]; w[4 * g + 2] = v[2]; w[4 * g + 3] = v[3];
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const uint32_t ro = (uint32_t)((i * 32 + (q >> 2) * 8 + (q & 3)) * ld * 4);
+#pragma unroll
+          for (int j = 0; j < NJ; ++j)
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val(i, j, q) * w[q]), r_out,
+                                                  (int)(voff + ro + j * 128), 0, 0);
+        }
+      }
+      return;
+    }
+    const bool vec = (ld & 3) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0;
     constexpr int LPR = NJ * 8;                         // lanes per row (4 floats each)
     constexpr int RPI = 64 / LPR;                       // rows per store instruction
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
+      prep(i);
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
         for (int q = 0; q < 16; ++q)
-          lds[((q >> 2) * 8 + half * 4 + (q & 3)) * CS + j * 32 + l32] = acc[i][j][q] * scale;
+          lds[((q >> 2) * 8 + half * 4 + (q & 3)) * CS + j * 32 + l32] = val(i, j, q);
       __builtin_amdgcn_s_waitcnt(0xc07f);               // lgkmcnt(0): the wave's writes landed
 #pragma unroll
       for (int rr = 0; rr < 32; rr += RPI) {
@@ -254,14 +335,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
+      prep(i);
 #pragma unroll
       for (int j = 0; j < NJ; j += 2) {
         const float col_ok = c0 + (j / 2) * 32 + l32 < inter ? 1.0f : 0.0f;
 #pragma unroll
         for (int q = 0; q < 16; q += 2) {
           const int rl = (q >> 2) * 8 + half * 4 + (q & 3);        // rows rl and rl + 1
-          const float v0 = silu_f32(acc[i][j][q] * scale) * (acc[i][j + 1][q] * scale);
-          const float v1 = silu_f32(acc[i][j][q + 1] * scale) * (acc[i][j + 1][q + 1] * scale);
+          const float v0 = silu_f32(val(i, j, q)) * val(i, j + 1, q);
+          const float v1 = silu_f32(val(i, j, q + 1)) * val(i, j + 1, q + 1);
           const uint32_t hb = pack_bf16x2_rne(v0, v1);
           lh[rl * HS + (j / 2) * 32 + l32] = (uint16_t)hb;
           lh[(rl + 1) * HS + (j / 2) * 32 + l32] = (uint16_t)(hb >> 16);
@@ -295,6 +377,15 @@ __device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&
       if (lane == 0) atomic_max_nonneg(p.out_amax, m);
     }
   }
+}
+
+// The plain form: output element = acc * scale.
+template <int MI, int NJ, int BN, int EPI>
+__device__ __forceinline__ void gemm_epilogue(const GemmArgs& p, const f32x16 (&acc)[MI][NJ],
+                                              const TileCoord& t, int wr0, int wc0, float scale,
+                                              float* lds, const float* rw_lds) {
+  gemm_epilogue_blocks<MI, NJ, BN, EPI>(p, t, wr0, wc0, lds, rw_lds, [](int) {},
+                                        [&](int i, int j, int q) { return acc[i][j][q] * scale; });
 }
 
 }  // namespace nvfp4
