@@ -171,12 +171,13 @@ __host__ __device__ constexpr size_t loop_lds_bytes(int64_t K) {
          (KQ > 0 ? (size_t)BM * KQ * 8 : 0);
 }
 
-// EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows).  KQ: 0 without
-// compensation, else the largest kc / 16 handled.  GW: selected channels per
-// stage that the gather takes beside the MFMAs (4 or 8; more take a slower
-// loop at the stage's end).
+// One tile.  EPI: the epilogue (0 F32, 1 SwiGLU bf16, 2 scatter rows).  KQ:
+// 0 without compensation, else the largest kc / 16 handled.  GW: selected
+// channels per stage that the gather takes beside the MFMAs (4 or 8; more
+// take a slower loop at the stage's end).  Inlined into the kernel: as a call
+// it would take the kernel argument's address.
 template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ, int GW>
-__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles) {
+__device__ __forceinline__ void gemm_tile(const GemmArgs& p, const TileCoord& tc) {
   constexpr int BM = WM * MI * 32;
   static_assert(WN * NJ * 32 == BN, "N tile");
   static_assert(WM * WN == 4, "four waves");
@@ -203,8 +204,6 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
-  TileCoord tc;
-  if (!map_tile<BM>(p, ntiles, tc)) return;       // uniform over the workgroup
   const int e = tc.e, n_tile = tc.n_tile, rows_valid = tc.rows_valid;
   const int64_t row0 = tc.row0;
   const int64_t K = p.K;
@@ -704,13 +703,19 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
   const float scale = COMP ? 1.0f : ga * gw;
   // Row block i's compensation: corr = sum_q R_q W_S,q per 32 x 32 block (the
   // Q(R_S) operands of the block's rows dequantized once, the W_S operands
-  // read per block), then acc = acc * gA gW + corr * gR gW, so no ratio of
+  // read per block); the output is acc * gA gW + corr * gR gW, so no ratio of
   // global scales can overflow.  Substeps past kc add zero: their scale bytes
   // are 0 and the padding channels of W_S are 0 (the code words read stay
-  // inside the Q(R_S) region).
+  // inside the Q(R_S) region).  The epilogue's LDS staging reaches past the
+  // slot ring into W_S in the narrow-ring variants (STAGING_OVERLAPS below):
+  // there the sum goes back into acc, else it is formed as the output
+  // element is read.
+  constexpr size_t WAVE_STAGE = EPI == 1 ? (size_t)32 * (NJ * 16 + 8) * 2 : (size_t)epilogue_wave_floats<NJ>() * 4;
+  constexpr bool STAGING_OVERLAPS = COMP && 4 * WAVE_STAGE > (size_t)NSLOT * STAGE + DUMMY_BYTES;
+  const float sa = ga * gw, sr = COMP ? p.r_global[e] * gw : 0.0f;
+  [[maybe_unused]] f32x16 corr[COMP && !STAGING_OVERLAPS ? NJ : 1];
   auto prep = [&](int i) {
     if constexpr (COMP) {
-      const float sa = ga * gw, sr = p.r_global[e] * gw;
       const uint32_t* cw = reinterpret_cast<const uint32_t*>(RSC + (wm * MI * 32 + i * 32 + l32) * (kc / 2));
       f16x8 rf[KQ];
 #pragma unroll
@@ -721,25 +726,30 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 #pragma unroll
       for (int j = 0; j < NJ; ++j) {
         const _Float16* wsr = WS + (wn * NJ * 32 + j * 32 + l32) * WSS + 8 * half;
-        f32x16 corr;
+        f32x16 c;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) corr[v] = 0.0f;
+        for (int v = 0; v < 16; ++v) c[v] = 0.0f;
 #pragma unroll
         for (int q = 0; q < KQ; ++q)
-          corr = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf[q], *reinterpret_cast<const f16x8*>(wsr + 16 * q), corr,
-                                                        0, 0, 0);
+          c = __builtin_amdgcn_mfma_f32_32x32x16_f16(rf[q], *reinterpret_cast<const f16x8*>(wsr + 16 * q), c, 0, 0, 0);
+        if constexpr (STAGING_OVERLAPS) {
 #pragma unroll
-        for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * sa + corr[v] * sr;
+          for (int v = 0; v < 16; ++v) acc[i][j][v] = acc[i][j][v] * sa + c[v] * sr;
+        } else {
+          corr[j] = c;
+        }
       }
     }
+  };
+  auto val = [&](int i, int j, int q) {
+    if constexpr (COMP && !STAGING_OVERLAPS) return acc[i][j][q] * sa + corr[j][q] * sr;
+    else return acc[i][j][q] * scale;
   };
   // Row blocks are compensated right before their output leaves, unless the
   // epilogue's LDS staging (per wave: 32 rows of bf16 h for SwiGLU, of fp32
   // otherwise) reaches past the slot ring into W_S and is used (SwiGLU, or
   // an F32 tile that does not store straight from the accumulators): then
   // all row blocks first.
-  constexpr size_t WAVE_STAGE = EPI == 1 ? (size_t)32 * (NJ * 16 + 8) * 2 : (size_t)epilogue_wave_floats<NJ>() * 4;
-  constexpr bool STAGING_OVERLAPS = COMP && 4 * WAVE_STAGE > (size_t)NSLOT * STAGE + DUMMY_BYTES;
   bool early = false;
   if constexpr (STAGING_OVERLAPS) early = EPI == 1 || !epilogue_direct<MI, BN, EPI>(p, tc);
   if (early) {                                   // uniform over the workgroup
@@ -752,7 +762,27 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
       [&](int i) {
         if (!early) prep(i);
       },
-      [&](int i, int j, int q) { return acc[i][j][q] * scale; });
+      val);
+}
+
+// One tile per workgroup; with 32-row tiles the workgroups may go round the
+// tiles (a capped grid: one round when it has one workgroup per tile), with
+// map_tile's barriers between one tile's last LDS reads and the next tile's
+// first writes.  (A loop around the larger tiles costs them registers.)
+template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ, int GW>
+__global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int ntiles) {
+  constexpr int BM = WM * MI * 32;
+  if constexpr (BM == 32) {
+    for (int round = 0;; ++round) {
+      TileCoord tc;
+      if (!map_tile<BM>(p, ntiles, tc, round)) return;   // uniform over the workgroup
+      gemm_tile<MI, NJ, WM, WN, NSLOT, EPI, KQ, GW>(p, tc);
+    }
+  } else {
+    TileCoord tc;
+    if (!map_tile<BM>(p, ntiles, tc)) return;            // uniform over the workgroup
+    gemm_tile<MI, NJ, WM, WN, NSLOT, EPI, KQ, GW>(p, tc);
+  }
 }
 
 template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ, int GW>
@@ -771,7 +801,8 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (err != hipSuccess) return err;
-  const int64_t grid = (total + 7) / 8 * 8;       // upper bound on the tiles, one share per XCD
+  int64_t grid = (total + 7) / 8 * 8;             // upper bound on the tiles, one share per XCD
+  if (BM == 32 && a.grid_cap > 0 && grid > a.grid_cap) grid = (a.grid_cap + 7) / 8 * 8;
   kern<<<(unsigned)grid, 256, lds, stream>>>(a, (int)ntiles);
   return hipGetLastError();
 }
@@ -828,6 +859,20 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
   // a compensation wider than 64 channels (a larger W_S) needs a shorter tile
   if (a.sel_idx && a.kc > 64 && bm > 128) bm = 128;
+  if (bm == 256 && a.block_m == 0) {
+    // 256-row tiles over each group's rows except a remainder of fewer than
+    // 96 rows, then those remainders in 32-row tiles: 256 workgroups (one
+    // per CU) go round them, as the host does not know how many there are.
+    GemmArgs big = a, rest = a;
+    big.tail_split = 1;
+    rest.tail_split = 2;
+    rest.grid_cap = 256;
+    err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
+    if (err == hipSuccess) err = nvg::launch_comp<1, 2, 1, 4, 3>(rest, stream);
+    if (err != hipSuccess || a.epilogue != 2) return err;
+    return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
+                          static_cast<float*>(a.out), a.ldo, a.y_rows, stream);
+  }
   switch (bm) {
     case 256: err = nvg::launch_comp<4, 4, 2, 2, 3>(a, stream); break;
     case 128: err = nvg::launch_comp<2, 4, 2, 2, 3>(a, stream); break;

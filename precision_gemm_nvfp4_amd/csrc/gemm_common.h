@@ -54,13 +54,36 @@ __device__ __forceinline__ TileCoord uniform_tile(TileCoord t) {
   return u;
 }
 
+// A group's rows in 256-row tiles leave a ragged remainder; one of fewer
+// than TAIL_MIN rows costs a 256-row tile about two thirds of a full one, so
+// the launcher gives those remainders to a second launch of 32-row tiles.
+constexpr int64_t TAIL_BM = 256, TAIL_MIN = 96;
+
+// The rows [g0, g1) of group e that this launch covers (tail_split: 0 all of
+// them; 1 the rows up to the group's last multiple of TAIL_BM, and the
+// remainder too when it has at least TAIL_MIN rows; 2 the remainder
+// otherwise).
+__device__ __forceinline__ void group_rows(const GemmArgs& p, int e, int64_t& g0, int64_t& g1) {
+  const int64_t b = clamp64(p.group_offsets[e], 0, p.rows_total);
+  const int64_t en = clamp64(p.group_offsets[e + 1], b, p.rows_total);
+  if (p.tail_split == 0) {
+    g0 = b;
+    g1 = en;
+    return;
+  }
+  const int64_t cnt = en - b, rem = cnt % TAIL_BM;
+  const int64_t big = rem >= TAIL_MIN ? cnt : cnt - rem;
+  g0 = p.tail_split == 1 ? b : b + big;
+  g1 = p.tail_split == 1 ? b + big : en;
+}
+
 // m-tiles of BM rows of expert e's group, for the threads of a 256-thread
 // workgroup in chunks of 256 experts.
 template <int BM>
 __device__ __forceinline__ uint32_t expert_mtiles(const GemmArgs& p, int e) {
   if (e >= p.E) return 0;
-  const int64_t rb = clamp64(p.group_offsets[e], 0, p.rows_total);
-  const int64_t re = clamp64(p.group_offsets[e + 1], rb, p.rows_total);
+  int64_t rb, re;
+  group_rows(p, e, rb, re);
   return (uint32_t)((re - rb + BM - 1) / BM);
 }
 
@@ -131,23 +154,24 @@ __device__ __forceinline__ TileCoord locate_tile(const GemmArgs& p, int ntiles, 
   TileCoord t;
   t.e = sh_e;
   t.n_tile = sh_nt;
-  const int64_t g0 = clamp64(p.group_offsets[t.e], 0, p.rows_total);
-  const int64_t g1 = clamp64(p.group_offsets[t.e + 1], g0, p.rows_total);
+  int64_t g0, g1;
+  group_rows(p, t.e, g0, g1);
   t.row0 = g0 + (int64_t)sh_mt * BM;
   t.rows_valid = (int)((g1 - t.row0) < BM ? (g1 - t.row0) : BM);
   return t;
 }
 
-// This workgroup's tile, from one pass over the group offsets: the m-tiles
-// of every expert, their prefix sum and total T (T x ntiles real tiles), the
-// XCD mapping of workgroup ids (hardware id h runs logical tile
-// (h % 8) * ceil(T' / 8) + h / 8 of the T' = T x ntiles real ones), and the
-// coordinates of that tile.  Returns false (the same in every thread) for a
-// surplus workgroup.  With E <= 256 the offsets are read once (one memory
-// round trip); more experts take a counting pass first.  Called by all
+// This workgroup's tile in round `round`, from one pass over the group
+// offsets: the m-tiles of every expert, their prefix sum and total T (T x
+// ntiles real tiles), the XCD mapping of workgroup ids (hardware id h runs
+// logical tiles (h % 8) * ceil(T' / 8) + h / 8 + r * G / 8 of the T' = T x
+// ntiles real ones, r = 0, 1, .. for a grid of G workgroups), and the
+// coordinates of that tile.  Returns false (the same in every thread) once
+// the workgroup has none left.  With E <= 256 the offsets are read once (one
+// memory round trip); more experts take a counting pass first.  Called by all
 // threads of a 256-thread workgroup.
 template <int BM>
-__device__ __forceinline__ bool map_tile(const GemmArgs& p, int ntiles, TileCoord& t) {
+__device__ __forceinline__ bool map_tile(const GemmArgs& p, int ntiles, TileCoord& t, int round = 0) {
   __shared__ int32_t sh_e, sh_mt, sh_nt;
   __shared__ int64_t sh_g0, sh_g1;
   __shared__ uint32_t sh_waves[4];
@@ -157,8 +181,7 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int ntiles, TileCoor
   uint32_t n = 0, before = 0;
   if (p.E <= 256) {
     if (tid < p.E) {
-      g0 = clamp64(p.group_offsets[tid], 0, p.rows_total);
-      g1 = clamp64(p.group_offsets[tid + 1], g0, p.rows_total);
+      group_rows(p, tid, g0, g1);
       n = (uint32_t)((g1 - g0 + BM - 1) / BM);
     }
     before = block_scan_256(n, sh_waves, total) - n;
@@ -167,7 +190,7 @@ __device__ __forceinline__ bool map_tile(const GemmArgs& p, int ntiles, TileCoor
   }
   const int real = (int)total * ntiles;
   const int per_xcd = (real + 7) / 8;
-  const int jt = (int)blockIdx.x / 8;
+  const int jt = (int)blockIdx.x / 8 + round * (int)(gridDim.x / 8);
   const int logical = ((int)blockIdx.x % 8) * per_xcd + jt;
   if (jt >= per_xcd || logical >= real) return false;
   if (p.E > 256) {

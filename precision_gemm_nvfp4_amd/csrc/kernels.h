@@ -63,6 +63,12 @@ struct GemmArgs {
   int rw_lds_offset;     // set by the launcher: LDS byte offset of the scatter epilogue's row weights
   int a_global_per_group = 0;  // a_global holds one scale per group (else one for all)
   int accumulate = 0;          // F32 epilogue: out += Y instead of out = Y
+  // set by the launcher: which rows of each group this launch covers (0 all;
+  // 1 the 256-row tiles, plus a remainder of at least 96 rows; 2 the other
+  // remainders) and at most how many workgroups it takes (0: one per tile,
+  // else they go round the tiles)
+  int tail_split = 0;
+  int64_t grid_cap = 0;
 };
 int grouped_gemm_block_m(int64_t rows_total, int32_t E);
 bool grouped_gemm_offsets_fit(int64_t a_rows, int64_t N, int64_t K);

@@ -296,12 +296,8 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   const int wm = wave / WN, wn = wave % WN;
   const int half = lane >> 5, l32 = lane & 31;
 
-  const int real = (int)count_mtiles<BM>(p) * ntiles;
-  const int per_xcd = (real + 7) / 8;
-  const int jt = (int)blockIdx.x / 8;
-  const int logical = ((int)blockIdx.x % 8) * per_xcd + jt;
-  if (jt >= per_xcd || logical >= real) return;     // uniform over the workgroup
-  const TileCoord tc = locate_tile<BM>(p, ntiles, logical);
+  TileCoord tc;
+  if (!map_tile<BM>(p, ntiles, tc)) return;       // uniform over the workgroup
   const int e = tc.e, n_tile = tc.n_tile, rows_valid = tc.rows_valid;
   const int64_t row0 = tc.row0;
   const int64_t K = p.K;
