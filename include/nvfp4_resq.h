@@ -287,6 +287,14 @@ int moe_w4a4_masked_comp_gemm(const uint8_t* m_codes, const uint8_t* m_scales,
  *   w        bf16 [nmat, N, K];  w_qdq out bf16 [nmat, N, K]
  *   codes    NULL or out [nmat, N, K/2];  scales NULL or out [nmat, N, K/16]
  *   g        NULL or out fp32 [nmat]
+ * Matrices of 3.1 M to 12.6 M elements on 256 CUs (one to four 16-blocks per
+ * thread of the grid) take one pass: a cooperative launch keeps each matrix
+ * on chip between its amax and its quantization; others take an amax pass
+ * and a quantize pass.  The workspace (at least 64 KiB) holds the one-pass
+ * kernel's per-workgroup amax slots and, in the 32-bit word at byte offset
+ * 65536, a flag that is nonzero if a gather gave up waiting (it cannot when
+ * the launch succeeded, as every workgroup is then resident); it is
+ * overwritten by every call.
  * Errors: EINVAL (K % 16, null w / w_qdq, in-place w == w_qdq), EWORKSPACE.
  * ------------------------------------------------------------------------ */
 size_t qdq_weights_workspace_size(int64_t nmat, int64_t N, int64_t K);

@@ -106,24 +106,257 @@ __global__ __launch_bounds__(256) void qdq_kernel(const __bf16* __restrict__ w, 
   }
 }
 
-// All matrices in one amax launch, then one quantize launch; both stream at
-// about 5 TB/s.  Single-read alternatives measured on the 256-expert weights
-// (W_gu 3072 x 4096 and W_d 4096 x 1536 per expert; two-pass 4.2 + 2.1 ms):
-//  - groups of matrices small enough for the second read to come from the
-//    MALL: 6.9-13.1 ms (the MALL re-read runs at about 7 TB/s, hardly above
-//    HBM);
-//  - a cooperative kernel holding one matrix in registers across a grid-wide
-//    amax gather: 6.8 ms (load, gather and write in lockstep);
-//  - the same with the next matrix's loads issued before the gather (two or
-//    three matrices in registers, slot-based gathers, LDS-only barriers):
-//    3.8 + 2.6 ms; with two teams of workgroups a CU apart in phase:
-//    5.1 + 2.2 ms.  Each step waits for its gather and its stores drain into
-//    a busy memory system, which costs about what the second read saves.
-size_t qdq_workspace_bytes(int64_t nmat) { return ((size_t)(nmat > 0 ? nmat : 0) * 4 + 255) / 256 * 256; }
+// ---------------------------------------------------------------------------
+// One-pass weight QDQ: every matrix read once
+// ---------------------------------------------------------------------------
+// A cooperative grid (every workgroup resident, one per CU) keeps each
+// workgroup's slice of the matrices on chip from their amax to their
+// quantization.  The matrices go P at a time ("step" s covers matrices
+// s P .. s P + P - 1, each with its own amax), so that a step holds KB P
+// blocks per data thread whatever the matrix size.  A workgroup is QDQ1_DW
+// data waves plus one sync wave.  In step s the data waves
+//   a. wait for their direct loads of step s + 1 into the LDS slice buffer,
+//   b. copy their blocks of it into registers while reducing each matrix's
+//      amax into LDS (one value per wave and matrix),
+//   c. meet the sync wave (barrier A; the slice buffer is free after it),
+//   d. issue the direct loads of step s + 2 into the slice buffer,
+//   e. meet the sync wave again (barrier B: the global amax of step s's
+//      matrices is in LDS),
+//   f. quantize step s's matrices from registers and store them,
+// so one step lands in LDS while the previous one is reduced and the one
+// before it is written.  After barrier B of step s the sync wave publishes
+// this workgroup's amax of each matrix of step s + 1 (one 64-bit store per
+// matrix of sequence number and value into its own slot: nothing is
+// read-modify-written) and polls every workgroup's slots until all carry
+// step s + 1's sequence number, then leaves the maxima in LDS for step s + 1:
+// all while the data waves quantize step s.  Only the sync wave touches the
+// slots, so the data waves never wait for their own loads to publish
+// anything (a wave's memory fence would wait for all of them), and their
+// barriers leave global loads in flight.  A poll that runs past spin_limit
+// gives up, sets a flag in the workspace and lets every wave finish (only
+// possible when the workgroups were not all resident).
+constexpr int QDQ1_DW = 12;                    // data waves per workgroup
+constexpr int QDQ1_DT = 64 * QDQ1_DW;          // data threads
+constexpr int QDQ1_SEG = QDQ1_DT * 32;         // bytes of one block per data thread
+constexpr int QDQ1_MAX_BLK = 4;                // blocks per data thread and step
+constexpr int QDQ1_MAX_WG = 1024;              // workgroups (CUs) the publication slots hold
+constexpr int QDQ1_MAX_P = 4;                  // matrices per step
 
-hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
-                      uint8_t* codes, uint8_t* scales, float* g, void* ws, hipStream_t stream) {
-  float* ws_amax = static_cast<float*>(ws);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t qdq1_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)b);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+  const uint32_t n = __builtin_amdgcn_readfirstlane((uint32_t)(bytes < 0 ? 0 : (bytes < 0xFFFFFFFFll ? bytes : 0xFFFFFFFFll)));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, (int)n,
+                                           0x00020000);
+}
+
+// KB: blocks per data thread and matrix; P: matrices per step; STORES: store
+// instructions per block (bf16 output, plus the codes and the scale byte
+// when asked).  Every store instruction is issued (a block past its matrix,
+// or of a matrix past the last, stores out of bounds and is dropped), so the
+// wait for a step's loads can leave exactly KB P STORES stores outstanding.
+template <int KB, int P, int STORES>
+__global__ __launch_bounds__(64 * (QDQ1_DW + 1), 1) void qdq_onepass_kernel(
+    const __bf16* __restrict__ w, int64_t nmat, int64_t nb, __bf16* __restrict__ w_qdq,
+    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, float* __restrict__ g_out,
+    uint32_t* __restrict__ sync, uint32_t spin_limit) {
+  constexpr int NB = KB * P;                   // blocks per data thread and step
+  static_assert(NB <= QDQ1_MAX_BLK && P <= QDQ1_MAX_P && NB * STORES <= 63, "step size");
+  extern __shared__ __attribute__((aligned(16))) unsigned char slice[];   // NB * QDQ1_SEG bytes
+  __shared__ float red[QDQ1_DW][P];
+  __shared__ float sh_amax[2][P];
+  // publication slots [2][P][nwg] (parity of the step) and the give-up flag
+  uint64_t* slots = reinterpret_cast<uint64_t*>(sync);
+  uint32_t* gave_up = sync + 4 * QDQ1_MAX_P * QDQ1_MAX_WG;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t nwg = gridDim.x;
+  const int64_t wg = blockIdx.x;
+  const int64_t nsteps = (nmat + P - 1) / P;
+  constexpr uint32_t OOB = 0x80000000u;        // past every per-matrix array
+
+  if (wave == QDQ1_DW) {
+    // ---- sync wave: two barriers per step, like the data waves ----
+    for (int64_t s = -1; s < nsteps; ++s) {
+      const bool next = s + 1 < nsteps;
+      lds_barrier();                           // A: red holds step s + 1's wave maxima
+      float m[P];
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        m[p] = 0.0f;
+        if (next) {
+#pragma unroll
+          for (int i = 0; i < QDQ1_DW; ++i) m[p] = fmaxf(m[p], red[i][p]);
+        }
+      }
+      lds_barrier();                           // B: sh_amax[s & 1] is step s's
+      // publish and gather step s + 1 while the data waves quantize step s
+      if (next) {
+        uint64_t* sl = slots + ((s + 1) & 1) * P * nwg;
+        const uint64_t seq = (uint64_t)(s + 2) << 32;
+        if (lane == 0) {
+#pragma unroll
+          for (int p = 0; p < P; ++p)
+            __hip_atomic_store(&sl[p * nwg + wg], seq | __float_as_uint(m[p]), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        // lane l watches slots l, l + 64, .. of every matrix
+        float a[P];
+        uint32_t spins = 0;
+        for (;;) {
+          bool all = true;
+#pragma unroll
+          for (int p = 0; p < P; ++p) {
+            a[p] = 0.0f;
+            for (uint32_t i = (uint32_t)lane; i < nwg; i += 64) {
+              const uint64_t v = __hip_atomic_load(&sl[p * nwg + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              all = all && (v >> 32) == (uint64_t)(s + 2);
+              a[p] = fmaxf(a[p], __uint_as_float((uint32_t)v));
+            }
+          }
+          if (__all(all)) break;
+          __builtin_amdgcn_s_sleep(4);
+          if (++spins >= spin_limit) {
+            if (lane == 0) __hip_atomic_store(gave_up, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+        }
+#pragma unroll
+        for (int p = 0; p < P; ++p) {
+          const float v = wave_max(a[p]);
+          if (lane == 0) sh_amax[(s + 1) & 1][p] = v;
+        }
+      }
+    }
+    return;
+  }
+
+  // ---- data waves ----
+  const int dt = tid;                          // 0 .. QDQ1_DT - 1
+  // Block k of a step (matrix p = k / KB of the step, kk = k % KB) of data
+  // thread dt is block (kk * nwg + wg) * QDQ1_DT + dt of that matrix, so
+  // segment k of the slice is QDQ1_SEG contiguous bytes of the matrix, and
+  // wave `wave` loads (and later reads) its own 2 KB of every segment.
+  uint32_t voff[KB][2];
+#pragma unroll
+  for (int k = 0; k < KB; ++k)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      voff[k][i] = (uint32_t)(((int64_t)k * nwg + wg) * QDQ1_SEG) + (uint32_t)(wave * 2048 + i * 1024 + lane * 16);
+  // matrix mi's bytes, or none past the last matrix (reads give zeros,
+  // stores are dropped)
+  auto mat_bytes = [&](int64_t mi, int64_t per) { return mi < nmat ? per : (int64_t)0; };
+  // The slice of step s into LDS (reads past a matrix return zeros).
+  auto issue = [&](int64_t s) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t mi = s * P + p;
+      const __amdgpu_buffer_rsrc_t r = qdq1_rsrc(w + (mi < nmat ? mi : 0) * nb * kBlock, mat_bytes(mi, nb * kBlock * 2));
+#pragma unroll
+      for (int k = 0; k < KB; ++k)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r, (__attribute__((address_space(3))) void*)(slice + (p * KB + k) * QDQ1_SEG + wave * 2048 + i * 1024),
+              16, (int)voff[k][i], 0, 0, 0);
+    }
+  };
+  auto copy_amax = [&](u32x4 (&b)[NB][2]) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      float m = 0.0f;
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int j = p * KB + k;
+        const u32x4* src = reinterpret_cast<const u32x4*>(slice + j * QDQ1_SEG + dt * 32);
+        b[j][0] = src[0];
+        b[j][1] = src[1];
+        m = absmax8(b[j][1], absmax8(b[j][0], m));
+      }
+      m = wave_max(m);
+      if (lane == 0) red[wave][p] = m;
+    }
+  };
+  // Step s's blocks under their matrices' global amax: bf16(DQ) (two
+  // elements per fp32 multiply and packed convert, as in qdq_block), codes
+  // and scales.
+  auto quant = [&](int64_t s, const u32x4 (&b)[NB][2]) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+      const int64_t mi = s * P + p;
+      const int64_t mb = mi < nmat ? mi : 0;
+      const float g = global_scale_from_amax(sh_amax[s & 1][p]);
+      const BlockScaler bsc = make_block_scaler(g);
+      if (g_out && mi < nmat && wg == 0 && dt == 0) g_out[mi] = g;
+      const __amdgpu_buffer_rsrc_t ro = qdq1_rsrc(w_qdq + mb * nb * kBlock, mat_bytes(mi, nb * kBlock * 2));
+      const __amdgpu_buffer_rsrc_t rc = qdq1_rsrc(codes ? codes + mb * nb * 8 : nullptr, codes ? mat_bytes(mi, nb * 8) : 0);
+      const __amdgpu_buffer_rsrc_t rs = qdq1_rsrc(scales ? scales + mb * nb : nullptr, scales ? mat_bytes(mi, nb) : 0);
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const int j = p * KB + k;
+        const int64_t bi = ((int64_t)k * nwg + wg) * QDQ1_DT + dt;
+        const bool in = bi < nb;
+        float v[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_lo(b[j][0][i]);
+          v[2 * i + 1] = bf16_hi(b[j][0][i]);
+          v[8 + 2 * i] = bf16_lo(b[j][1][i]);
+          v[8 + 2 * i + 1] = bf16_hi(b[j][1][i]);
+        }
+        uint32_t sb, w0, w1;
+        const float S = quantize_block16(v, bsc, &sb, &w0, &w1);
+        float d[16];
+        e2m1_unpack8(w0, d);
+        e2m1_unpack8(w1, d + 8);
+        u32x4 o0, o1;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t word = pack_bf16x2_rne(d[2 * i] * S, d[2 * i + 1] * S);
+          if (i < 4) o0[i] = word; else o1[i - 4] = word;
+        }
+        const uint32_t ob = in ? (uint32_t)(bi * 32) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b128(o0, ro, (int)ob, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b128(o1, ro, (int)(in ? ob + 16 : OOB), 0, 0);
+        if constexpr (STORES >= 3) {
+          if (codes) __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, rc, (int)(in ? (uint32_t)(bi * 8) : OOB), 0, 0);
+          else __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs, (int)(in ? (uint32_t)bi : OOB), 0, 0);
+        }
+        if constexpr (STORES == 4)
+          __builtin_amdgcn_raw_buffer_store_b8((uint8_t)sb, rs, (int)(in ? (uint32_t)bi : OOB), 0, 0);
+      }
+    }
+  };
+  u32x4 R0[NB][2], R1[NB][2];
+  // Step s: R_nxt receives step s + 1 (its loads went out in step s - 1, and
+  // `after` store instructions followed them), R_cur holds step s.
+  auto step = [&](int64_t s, u32x4 (&cur)[NB][2], u32x4 (&nxt)[NB][2], auto after_c) {
+    constexpr int after = decltype(after_c)::value;
+    if (s >= nsteps) return;                   // uniform: no barriers past the last step
+    if (s + 1 < nsteps) {
+      __builtin_amdgcn_s_waitcnt((after & 15) | 0x70 | 0xf00 | ((after >> 4) << 14));   // vmcnt(after)
+      copy_amax(nxt);
+    }
+    lds_barrier();                             // A
+    if (s + 2 < nsteps) issue(s + 2);
+    lds_barrier();                             // B
+    if (s >= 0) quant(s, cur);
+  };
+  issue(0);
+  step(-1, R1, R0, std::integral_constant<int, 0>{});     // step 0 into R0, step 1 out
+  step(0, R0, R1, std::integral_constant<int, 0>{});      // step 0 quantized, 1 into R1, 2 out
+  for (int64_t s = 1; s < nsteps; s += 2) {
+    step(s, R1, R0, std::integral_constant<int, NB * STORES>{});
+    step(s + 1, R0, R1, std::integral_constant<int, NB * STORES>{});
+  }
+}
+
+// Two passes over all matrices (one amax launch, then one quantize launch):
+// for shapes the one-pass kernel does not take.
+static hipError_t launch_qdq_two_pass(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
+                                      uint8_t* codes, uint8_t* scales, float* g, float* ws_amax,
+                                      hipStream_t stream) {
   hipError_t err = launch_fill_f32(ws_amax, nmat, 0.0f, stream);
   if (err != hipSuccess) return err;
   const int64_t per_mat = N * K;
@@ -136,6 +369,73 @@ hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf1
   qdq_kernel<<<dim3((unsigned)gq, (unsigned)nmat), 256, 0, stream>>>(w, N, K, ws_amax, w_qdq, codes,
                                                                      scales, g);
   return hipGetLastError();
+}
+
+// Workspace: the one-pass kernel's publication slots and give-up flag, or
+// the two-pass launch's per-matrix amax.
+size_t qdq_workspace_bytes(int64_t nmat) {
+  const size_t one = (size_t)QDQ1_MAX_P * QDQ1_MAX_WG * 16 + 4, two = (size_t)(nmat > 0 ? nmat : 0) * 4;
+  return ((one > two ? one : two) + 255) / 256 * 256;
+}
+
+template <int KB, int P, int STORES>
+static hipError_t launch_qdq_onepass_kb(const __bf16* w, int64_t nmat, int64_t nb, __bf16* w_qdq, uint8_t* codes,
+                                        uint8_t* scales, float* g, uint32_t* sync, int grid, hipStream_t stream) {
+  auto kern = qdq_onepass_kernel<KB, P, STORES>;
+  const size_t lds = (size_t)KB * P * QDQ1_SEG;
+  hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (err != hipSuccess) return err;
+  int per_cu = 0;
+  err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, 64 * (QDQ1_DW + 1), lds);
+  if (err != hipSuccess) return err;
+  if (per_cu < 1) return hipErrorCooperativeLaunchTooLarge;
+  uint32_t spin_limit = 1u << 21;              // polls of about 256 cycles: well over a second
+  void* args[] = {(void*)&w, (void*)&nmat, (void*)&nb, (void*)&w_qdq, (void*)&codes, (void*)&scales,
+                  (void*)&g, (void*)&sync, (void*)&spin_limit};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(kern), dim3((unsigned)grid),
+                                    dim3(64 * (QDQ1_DW + 1)), args, (unsigned)lds, stream);
+}
+
+template <int STORES>
+static hipError_t launch_qdq_onepass(const __bf16* w, int64_t nmat, int64_t nb, int kb, __bf16* w_qdq,
+                                     uint8_t* codes, uint8_t* scales, float* g, uint32_t* sync, int grid,
+                                     hipStream_t stream) {
+  // P = 4 / KB matrices per step: four blocks per data thread and step
+  switch (kb) {
+    case 1: return launch_qdq_onepass_kb<1, 4, STORES>(w, nmat, nb, w_qdq, codes, scales, g, sync, grid, stream);
+    case 2: return launch_qdq_onepass_kb<2, 2, STORES>(w, nmat, nb, w_qdq, codes, scales, g, sync, grid, stream);
+    case 3: return launch_qdq_onepass_kb<3, 1, STORES>(w, nmat, nb, w_qdq, codes, scales, g, sync, grid, stream);
+    default: return launch_qdq_onepass_kb<4, 1, STORES>(w, nmat, nb, w_qdq, codes, scales, g, sync, grid, stream);
+  }
+}
+
+// The one-pass kernel when the device runs cooperative launches, there are
+// at least two steps of matrices, and each matrix fills one to QDQ1_MAX_BLK
+// blocks per data thread (3.1 M to 12.6 M elements on 256 CUs); else two
+// passes.
+hipError_t launch_qdq(const __bf16* w, int64_t nmat, int64_t N, int64_t K, __bf16* w_qdq,
+                      uint8_t* codes, uint8_t* scales, float* g, void* ws, hipStream_t stream) {
+  uint32_t* sync = static_cast<uint32_t*>(ws);
+  const int64_t nb = N * (K / kBlock);
+  int dev = 0, cus = 0, coop = 0;
+  hipError_t err = hipGetDevice(&dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (err == hipSuccess) err = hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev);
+  if (err != hipSuccess) return err;
+  const int64_t per = (int64_t)cus * QDQ1_DT;                // blocks one pass of the grid takes
+  const int64_t kb = per > 0 ? (nb + per - 1) / per : 0;
+  const int64_t p = kb >= 1 && kb <= QDQ1_MAX_BLK ? QDQ1_MAX_BLK / kb : 1;
+  if (!coop || cus > QDQ1_MAX_WG || nb < per || kb > QDQ1_MAX_BLK || nmat < 2 * p)
+    return launch_qdq_two_pass(w, nmat, N, K, w_qdq, codes, scales, g, reinterpret_cast<float*>(sync), stream);
+  err = launch_fill_f32(reinterpret_cast<float*>(sync), 4 * QDQ1_MAX_P * QDQ1_MAX_WG + 1, 0.0f, stream);
+  if (err != hipSuccess) return err;
+  const int stores = 2 + (codes ? 1 : 0) + (scales ? 1 : 0);
+  switch (stores) {
+    case 2: return launch_qdq_onepass<2>(w, nmat, nb, (int)kb, w_qdq, codes, scales, g, sync, cus, stream);
+    case 3: return launch_qdq_onepass<3>(w, nmat, nb, (int)kb, w_qdq, codes, scales, g, sync, cus, stream);
+    default: return launch_qdq_onepass<4>(w, nmat, nb, (int)kb, w_qdq, codes, scales, g, sync, cus, stream);
+  }
 }
 
 // MXFP4 weight QDQ: blocks of 32 along K with their own E8M0 scale and no

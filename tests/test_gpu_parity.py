@@ -416,6 +416,49 @@ def test_qdq_weights_large_matrix(gpu_lib):
     _check_qdq(P, w)
 
 
+@pytest.mark.parametrize("nmat,n,k", [
+    (9, 2048, 1536),     # 196608 blocks a matrix: four matrices a step, the last step partial
+    (5, 3000, 1536),     # two matrices a step, each past one block per thread, last step partial
+    (3, 3000, 3072),     # one matrix a step, three blocks per thread, the last ragged
+    (2, 3072, 4096),     # one matrix a step, four blocks per thread
+])
+def test_qdq_weights_one_pass(gpu_lib, nmat, n, k):
+    """Weight QDQ of matrices large enough (3.1 M to 12.6 M elements on 256
+    CUs) for the one-pass kernel, which holds each matrix on chip from its
+    amax to its quantization: every global scale against the oracle's from
+    the matrix's amax, the first and last matrices (the last one in a
+    partial step) bit-exact, and the give-up flag of its gathers clear."""
+    P = gpu_lib
+    lib = P.load()
+    w = synth.weights(nmat, n, k, seed=14, tensor_id=synth.WGU_ID)
+    w[1, 7, 9] = 5.0                                  # one outlier sets a matrix's g
+    w[-1] = w[-1] * 1e-20                             # a tiny matrix last
+    wc = w.cuda()
+    wq = torch.empty_like(wc)
+    codes = torch.empty(nmat, n, k // 2, dtype=torch.uint8, device="cuda")
+    scales = torch.empty(nmat, n, k // 16, dtype=torch.uint8, device="cuda")
+    g = torch.empty(nmat, dtype=torch.float32, device="cuda")
+    ws_bytes = lib.qdq_weights_workspace_size(nmat, n, k)
+    ws = torch.full((ws_bytes,), 0x55, dtype=torch.uint8, device="cuda")
+    assert lib.qdq_weights(P._ptr(wc), nmat, n, k, P._ptr(wq), P._ptr(codes), P._ptr(scales), P._ptr(g),
+                           P._ptr(ws), ws_bytes, P._stream()) == 0
+    torch.cuda.synchronize()
+    wf = w.float().numpy()
+    g_ref = np.array([OQ.global_scale(np.abs(wf[m]).max()) for m in range(nmat)], dtype=np.float32)
+    assert np.array_equal(np32(g), g_ref)
+    for m in (0, nmat - 1):
+        wq_r, c_r, s_r, g_r = OQ.qdq_weights(wf[m:m + 1])
+        assert np.array_equal(npu8(codes[m]), c_r[0]) and np.array_equal(npu8(scales[m]), s_r[0])
+        assert np.array_equal(wq[m].cpu().view(torch.int16).numpy().view(np.uint16), wq_r[0])
+    # the one-pass kernel's give-up flag (the word after 4 x 4 x 1024 slot
+    # words), when this device takes the one-pass kernel for the shape
+    per = torch.cuda.get_device_properties(0).multi_processor_count * 768
+    nb = n * k // 16
+    kb = -(-nb // per)
+    if nb >= per and kb <= 4 and nmat >= 2 * (4 // kb):
+        assert int(ws[16384 * 4:16384 * 4 + 4].view(torch.int32).item()) == 0
+
+
 @pytest.mark.parametrize("rel", [1e-3, 8e-3, 0.2])
 def test_guided_round(gpu_lib, rel):
     P = gpu_lib
