@@ -111,30 +111,36 @@ __global__ __launch_bounds__(256) void qdq_kernel(const __bf16* __restrict__ w, 
 // ---------------------------------------------------------------------------
 // A cooperative grid (every workgroup resident, one per CU) keeps each
 // workgroup's slice of the matrices on chip from their amax to their
-// quantization.  The matrices go P at a time ("step" s covers matrices
-// s P .. s P + P - 1, each with its own amax), so that a step holds KB P
+// quantization.  The matrices go P at a time ("step" j covers matrices
+// j P .. j P + P - 1, each with its own amax), so that a step holds KB P
 // blocks per data thread whatever the matrix size.  A workgroup is QDQ1_DW
-// data waves plus one sync wave.  In step s the data waves
-//   a. wait for their direct loads of step s + 1 into the LDS slice buffer,
-//   b. copy their blocks of it into registers while reducing each matrix's
-//      amax into LDS (one value per wave and matrix),
-//   c. meet the sync wave (barrier A; the slice buffer is free after it),
-//   d. issue the direct loads of step s + 2 into the slice buffer,
-//   e. meet the sync wave again (barrier B: the global amax of step s's
-//      matrices is in LDS),
-//   f. quantize step s's matrices from registers and store them,
-// so one step lands in LDS while the previous one is reduced and the one
-// before it is written.  After barrier B of step s the sync wave publishes
-// this workgroup's amax of each matrix of step s + 1 (one 64-bit store per
-// matrix of sequence number and value into its own slot: nothing is
-// read-modify-written) and polls every workgroup's slots until all carry
-// step s + 1's sequence number, then leaves the maxima in LDS for step s + 1:
-// all while the data waves quantize step s.  Only the sync wave touches the
-// slots, so the data waves never wait for their own loads to publish
-// anything (a wave's memory fence would wait for all of them), and their
-// barriers leave global loads in flight.  A poll that runs past spin_limit
-// gives up, sets a flag in the workspace and lets every wave finish (only
-// possible when the workgroups were not all resident).
+// data waves plus one sync wave, which talk only through LDS flags (no
+// workgroup barrier after the start), so a data wave never waits for the
+// grid-wide gather unless it is not done by the time it is needed.
+//
+// Data wave, step s: wait for its own direct loads of step s + 1 into the
+// LDS slice buffer (a wave loads and reads only its own 2 KB of each
+// segment, so the buffer needs no barrier), copy its blocks into registers
+// while reducing each matrix's amax, post the maxima and then its flag;
+// issue the loads of step s + 2 into the slice buffer; wait until the sync
+// wave has posted step s's global maxima and quantize step s from registers
+// (buffer stores).  So one step lands in LDS while the previous one is
+// reduced and the one before it is written.
+//
+// The maxima go through two LDS buffers by step parity: a data wave writes
+// step j + 1's while the sync wave may still read step j's, and writes step
+// j + 2's only after quantizing step j, which waited for the sync wave to
+// finish step j.
+//
+// Sync wave, step j: wait until every data wave has posted step j, reduce
+// the maxima, publish them (one 64-bit store of sequence number and value
+// per matrix into this workgroup's own slot: nothing is read-modify-written)
+// and poll every workgroup's slots until all carry step j's sequence number,
+// then post the global maxima for the data waves.  Only the sync wave
+// touches the slots, so no data wave waits for its own loads to publish
+// anything (a wave's memory fence would wait for all of them).  A wait that
+// runs past spin_limit gives up, sets a flag in the workspace and lets every
+// wave finish (only possible when the workgroups were not all resident).
 constexpr int QDQ1_DW = 12;                    // data waves per workgroup
 constexpr int QDQ1_DT = 64 * QDQ1_DW;          // data threads
 constexpr int QDQ1_SEG = QDQ1_DT * 32;         // bytes of one block per data thread
@@ -151,6 +157,22 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t qdq1_rsrc(const void* base, in
                                            0x00020000);
 }
 
+// LDS flag accesses: volatile, and fenced against the compiler moving other
+// LDS accesses across them.  A wave's LDS operations complete in order, and
+// a writer waits for its data writes before writing the flag.
+__device__ __forceinline__ uint32_t lds_flag_read(const uint32_t* f) {
+  asm volatile("" ::: "memory");
+  const uint32_t v = *reinterpret_cast<const volatile uint32_t*>(f);
+  asm volatile("" ::: "memory");
+  return v;
+}
+__device__ __forceinline__ void lds_flag_write(uint32_t* f, uint32_t v) {
+  __builtin_amdgcn_s_waitcnt(0xc07f);         // lgkmcnt(0): the data went first
+  asm volatile("" ::: "memory");
+  *reinterpret_cast<volatile uint32_t*>(f) = v;
+  asm volatile("" ::: "memory");
+}
+
 // KB: blocks per data thread and matrix; P: matrices per step; STORES: store
 // instructions per block (bf16 output, plus the codes and the scale byte
 // when asked).  Every store instruction is issued (a block past its matrix,
@@ -164,8 +186,10 @@ __global__ __launch_bounds__(64 * (QDQ1_DW + 1), 1) void qdq_onepass_kernel(
   constexpr int NB = KB * P;                   // blocks per data thread and step
   static_assert(NB <= QDQ1_MAX_BLK && P <= QDQ1_MAX_P && NB * STORES <= 63, "step size");
   extern __shared__ __attribute__((aligned(16))) unsigned char slice[];   // NB * QDQ1_SEG bytes
-  __shared__ float red[QDQ1_DW][P];
-  __shared__ float sh_amax[2][P];
+  __shared__ float red[2][QDQ1_DW][P];         // data wave w's maxima of step j in [j & 1]
+  __shared__ uint32_t posted[QDQ1_DW];         // j + 1: data wave w posted step j
+  __shared__ float sh_amax[2][P];              // global maxima of step j in [j & 1]
+  __shared__ uint32_t ready;                   // j + 1: sh_amax holds step j
   // publication slots [2][P][nwg] (parity of the step) and the give-up flag
   uint64_t* slots = reinterpret_cast<uint64_t*>(sync);
   uint32_t* gave_up = sync + 4 * QDQ1_MAX_P * QDQ1_MAX_WG;
@@ -176,59 +200,62 @@ __global__ __launch_bounds__(64 * (QDQ1_DW + 1), 1) void qdq_onepass_kernel(
   const int64_t nsteps = (nmat + P - 1) / P;
   constexpr uint32_t OOB = 0x80000000u;        // past every per-matrix array
 
+  if (tid < QDQ1_DW) posted[tid] = 0u;
+  if (tid == 0) ready = 0u;
+  __syncthreads();
+
   if (wave == QDQ1_DW) {
-    // ---- sync wave: two barriers per step, like the data waves ----
-    for (int64_t s = -1; s < nsteps; ++s) {
-      const bool next = s + 1 < nsteps;
-      lds_barrier();                           // A: red holds step s + 1's wave maxima
+    // ---- sync wave ----
+    bool gave = false;
+    for (int64_t j = 0; j < nsteps; ++j) {
+      const uint32_t tag = (uint32_t)(j + 1);
+      // every data wave's maxima of step j (lane w watches data wave w)
+      uint32_t spins = 0;
+      while (!__all(lane >= QDQ1_DW || lds_flag_read(&posted[lane < QDQ1_DW ? lane : 0]) >= tag)) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++spins >= spin_limit) { gave = true; break; }
+      }
       float m[P];
 #pragma unroll
       for (int p = 0; p < P; ++p) {
         m[p] = 0.0f;
-        if (next) {
 #pragma unroll
-          for (int i = 0; i < QDQ1_DW; ++i) m[p] = fmaxf(m[p], red[i][p]);
-        }
+        for (int i = 0; i < QDQ1_DW; ++i) m[p] = fmaxf(m[p], red[j & 1][i][p]);
       }
-      lds_barrier();                           // B: sh_amax[s & 1] is step s's
-      // publish and gather step s + 1 while the data waves quantize step s
-      if (next) {
-        uint64_t* sl = slots + ((s + 1) & 1) * P * nwg;
-        const uint64_t seq = (uint64_t)(s + 2) << 32;
-        if (lane == 0) {
+      // publish this workgroup's maxima, gather everyone's
+      uint64_t* sl = slots + (j & 1) * P * nwg;
+      const uint64_t seq = (uint64_t)tag << 32;
+      if (lane == 0) {
 #pragma unroll
-          for (int p = 0; p < P; ++p)
-            __hip_atomic_store(&sl[p * nwg + wg], seq | __float_as_uint(m[p]), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        }
-        // lane l watches slots l, l + 64, .. of every matrix
-        float a[P];
-        uint32_t spins = 0;
-        for (;;) {
-          bool all = true;
-#pragma unroll
-          for (int p = 0; p < P; ++p) {
-            a[p] = 0.0f;
-            for (uint32_t i = (uint32_t)lane; i < nwg; i += 64) {
-              const uint64_t v = __hip_atomic_load(&sl[p * nwg + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-              all = all && (v >> 32) == (uint64_t)(s + 2);
-              a[p] = fmaxf(a[p], __uint_as_float((uint32_t)v));
-            }
-          }
-          if (__all(all)) break;
-          __builtin_amdgcn_s_sleep(4);
-          if (++spins >= spin_limit) {
-            if (lane == 0) __hip_atomic_store(gave_up, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
+        for (int p = 0; p < P; ++p)
+          __hip_atomic_store(&sl[p * nwg + wg], seq | __float_as_uint(m[p]), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+      }
+      float a[P];
+      spins = 0;
+      for (;;) {
+        bool all = true;
 #pragma unroll
         for (int p = 0; p < P; ++p) {
-          const float v = wave_max(a[p]);
-          if (lane == 0) sh_amax[(s + 1) & 1][p] = v;
+          a[p] = 0.0f;
+          for (uint32_t i = (uint32_t)lane; i < nwg; i += 64) {
+            const uint64_t v = __hip_atomic_load(&sl[p * nwg + i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            all = all && (v >> 32) == (uint64_t)tag;
+            a[p] = fmaxf(a[p], __uint_as_float((uint32_t)v));
+          }
         }
+        if (__all(all) || gave) break;
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins >= spin_limit) { gave = true; break; }
       }
+#pragma unroll
+      for (int p = 0; p < P; ++p) {
+        const float v = wave_max(a[p]);
+        if (lane == 0) sh_amax[j & 1][p] = v;
+      }
+      if (lane == 0) lds_flag_write(&ready, tag);
     }
+    if (gave && lane == 0) __hip_atomic_store(gave_up, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     return;
   }
 
@@ -262,7 +289,8 @@ __global__ __launch_bounds__(64 * (QDQ1_DW + 1), 1) void qdq_onepass_kernel(
               16, (int)voff[k][i], 0, 0, 0);
     }
   };
-  auto copy_amax = [&](u32x4 (&b)[NB][2]) {
+  // step s's blocks into registers, its maxima and then this wave's flag
+  auto copy_amax = [&](int64_t s, u32x4 (&b)[NB][2]) {
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       float m = 0.0f;
@@ -275,13 +303,22 @@ __global__ __launch_bounds__(64 * (QDQ1_DW + 1), 1) void qdq_onepass_kernel(
         m = absmax8(b[j][1], absmax8(b[j][0], m));
       }
       m = wave_max(m);
-      if (lane == 0) red[wave][p] = m;
+      if (lane == 0) red[s & 1][wave][p] = m;
     }
+    if (lane == 0) lds_flag_write(&posted[wave], (uint32_t)(s + 1));
   };
   // Step s's blocks under their matrices' global amax: bf16(DQ) (two
   // elements per fp32 multiply and packed convert, as in qdq_block), codes
   // and scales.
   auto quant = [&](int64_t s, const u32x4 (&b)[NB][2]) {
+    uint32_t spins = 0;
+    while (lds_flag_read(&ready) < (uint32_t)(s + 1)) {   // uniform: one LDS word
+      __builtin_amdgcn_s_sleep(1);
+      if (++spins >= spin_limit) {
+        if (lane == 0) __hip_atomic_store(gave_up, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+    }
 #pragma unroll
     for (int p = 0; p < P; ++p) {
       const int64_t mi = s * P + p;
@@ -333,14 +370,12 @@ __global__ __launch_bounds__(64 * (QDQ1_DW + 1), 1) void qdq_onepass_kernel(
   // `after` store instructions followed them), R_cur holds step s.
   auto step = [&](int64_t s, u32x4 (&cur)[NB][2], u32x4 (&nxt)[NB][2], auto after_c) {
     constexpr int after = decltype(after_c)::value;
-    if (s >= nsteps) return;                   // uniform: no barriers past the last step
+    if (s >= nsteps) return;                   // uniform
     if (s + 1 < nsteps) {
       __builtin_amdgcn_s_waitcnt((after & 15) | 0x70 | 0xf00 | ((after >> 4) << 14));   // vmcnt(after)
-      copy_amax(nxt);
+      copy_amax(s + 1, nxt);
     }
-    lds_barrier();                             // A
     if (s + 2 < nsteps) issue(s + 2);
-    lds_barrier();                             // B
     if (s >= 0) quant(s, cur);
   };
   issue(0);
