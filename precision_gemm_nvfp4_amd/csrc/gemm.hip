@@ -786,7 +786,7 @@ __global__ __launch_bounds__(256, 1) void grouped_gemm_kernel(GemmArgs p, int nt
 }
 
 template <int MI, int NJ, int WM, int WN, int NSLOT, int EPI, int KQ, int GW>
-static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
+static hipError_t launch_cfg(GemmArgs a, hipStream_t stream, size_t lds_cap) {
   constexpr int BM = WM * MI * 32;
   const int64_t mtiles = (a.rows_total + BM - 1) / BM + a.E;
   const int64_t ntiles = a.epilogue == 1 ? (a.N / 2 + BN / 2 - 1) / (BN / 2) : (a.N + BN - 1) / BN;
@@ -796,7 +796,7 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
   const size_t body = loop > epi ? loop : epi;
   a.rw_lds_offset = (int)body;
   const size_t lds = body + (EPI == 2 ? (size_t)BM * 4 : 0);
-  if (lds > 160 * 1024) return hipErrorInvalidConfiguration;
+  if (lds > lds_cap) return hipErrorInvalidConfiguration;
   auto kern = grouped_gemm_kernel<MI, NJ, WM, WN, NSLOT, EPI, KQ, GW>;
   hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -808,11 +808,11 @@ static hipError_t launch_cfg(GemmArgs a, hipStream_t stream) {
 }
 
 template <int MI, int NJ, int WM, int WN, int NSLOT, int KQ, int GW>
-static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream) {
+static hipError_t launch_epi(const GemmArgs& a, hipStream_t stream, size_t lds_cap = 160 * 1024) {
   switch (a.epilogue) {
-    case 0: return launch_cfg<MI, NJ, WM, WN, NSLOT, 0, KQ, GW>(a, stream);
-    case 1: return launch_cfg<MI, NJ, WM, WN, NSLOT, 1, KQ, GW>(a, stream);
-    default: return launch_cfg<MI, NJ, WM, WN, NSLOT, 2, KQ, GW>(a, stream);
+    case 0: return launch_cfg<MI, NJ, WM, WN, NSLOT, 0, KQ, GW>(a, stream, lds_cap);
+    case 1: return launch_cfg<MI, NJ, WM, WN, NSLOT, 1, KQ, GW>(a, stream, lds_cap);
+    default: return launch_cfg<MI, NJ, WM, WN, NSLOT, 2, KQ, GW>(a, stream, lds_cap);
   }
 }
 
@@ -827,6 +827,20 @@ static hipError_t launch_comp(const GemmArgs& a, hipStream_t stream) {
   // a wider W_S: one slot fewer
   return wide ? launch_epi<MI, NJ, WM, WN, NSLOT - 1, 8, 8>(a, stream)
               : launch_epi<MI, NJ, WM, WN, NSLOT - 1, 8, 4>(a, stream);
+}
+
+// 32-row tiles stream weights with little reuse per byte, so the number of
+// workgroups that a CU holds matters more than the ring depth: with up to 64
+// compensated channels a ring of two slots fits two workgroups per CU.
+static hipError_t launch_32(const GemmArgs& a, hipStream_t stream) {
+  if (a.sel_idx && a.kc <= 64) {
+    constexpr size_t HALF_CU = 80 * 1024 - 256;          // two workgroups' LDS, static arrays included
+    const bool wide = (int64_t)a.kc * KS > 3 * a.K;
+    const hipError_t err = wide ? launch_epi<1, 2, 1, 4, 2, 4, 8>(a, stream, HALF_CU)
+                                : launch_epi<1, 2, 1, 4, 2, 4, 4>(a, stream, HALF_CU);
+    if (err != hipErrorInvalidConfiguration) return err;
+  }
+  return launch_comp<1, 2, 1, 4, 3>(a, stream);
 }
 
 }  // namespace nvg
@@ -868,7 +882,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
     rest.tail_split = 2;
     rest.grid_cap = 256;
     err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
-    if (err == hipSuccess) err = nvg::launch_comp<1, 2, 1, 4, 3>(rest, stream);
+    if (err == hipSuccess) err = nvg::launch_32(rest, stream);
     if (err != hipSuccess || a.epilogue != 2) return err;
     return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
                           static_cast<float*>(a.out), a.ldo, a.y_rows, stream);
@@ -877,7 +891,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
     case 256: err = nvg::launch_comp<4, 4, 2, 2, 3>(a, stream); break;
     case 128: err = nvg::launch_comp<2, 4, 2, 2, 3>(a, stream); break;
     case 64: err = nvg::launch_comp<1, 4, 2, 2, 3>(a, stream); break;
-    default: err = nvg::launch_comp<1, 2, 1, 4, 3>(a, stream); break;
+    default: err = nvg::launch_32(a, stream); break;
   }
   if (err != hipSuccess || a.epilogue != 2) return err;
   return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
