@@ -173,7 +173,8 @@ int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
 size_t resq_select_and_requant_workspace_size(int64_t K, int64_t rows_total, int64_t U, int32_t k) {
   const int64_t slots = nvfp4::resq_max_slots(rows_total, U);
   const int64_t gslots = nvfp4::resq_max_gather_slots(rows_total, U);
-  return 2 * align256((size_t)(U + 1) * 4) + align256((size_t)slots * K * 4) +
+  return 2 * align256((size_t)(U + 1) * 4) + align256((size_t)slots * 16) +
+         align256((size_t)gslots * 32) + align256((size_t)slots * K * 4) +
          align256((size_t)rows_total * k * 4) + align256((size_t)gslots * 4);
 }
 
@@ -218,6 +219,10 @@ int resq_entry(const void* x, int dtype, int64_t x_rows, int64_t K, int64_t ldx,
   w += align256((size_t)(U + 1) * 4);
   rw.slot_start = reinterpret_cast<int32_t*>(w);
   w += align256((size_t)(U + 1) * 4);
+  rw.tile_info = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)slots * 16);
+  rw.slot_info = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)nvfp4::resq_max_gather_slots(rows_total, U) * 32);
   rw.partials = reinterpret_cast<float*>(w);
   w += align256((size_t)slots * K * 4);
   rw.r_s = reinterpret_cast<float*>(w);
@@ -421,6 +426,10 @@ int mxfp4_resq_select_and_requant(const void* x, int dtype, int64_t x_rows, int6
   w += align256((size_t)(U + 1) * 4);
   rw.slot_start = reinterpret_cast<int32_t*>(w);
   w += align256((size_t)(U + 1) * 4);
+  rw.tile_info = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)slots * 16);
+  rw.slot_info = reinterpret_cast<int32_t*>(w);
+  w += align256((size_t)nvfp4::resq_max_gather_slots(rows_total, U) * 32);
   rw.partials = reinterpret_cast<float*>(w);
   w += align256((size_t)slots * K * 4);
   rw.r_s = reinterpret_cast<float*>(w);

@@ -18,6 +18,9 @@ hipError_t launch_fill_f32(float* p, int64_t n, float v, hipStream_t stream);
 struct ResqWorkspace {
   int32_t* tile_start;   // [U+1] first 128-row score tile of each unit
   int32_t* slot_start;   // [U+1] first 32-row gather slot of each unit
+  int32_t* tile_info;    // [max_slots][4] per score tile: unit (-1: none), first row, unit end
+  int32_t* slot_info;    // [max_gather_slots][8] per gather slot: unit (-1: none), first row,
+                         // end row, the unit's first and end slot
   float* partials;       // [max_slots, K] (unused when the caller gives tile partials)
   float* r_s;            // [rows_total, k]
   float* amax_part;      // [max_gather_slots]

@@ -5,7 +5,9 @@
 // R_S a second time with its own global scale.
 //
 // Kernels (one stream, in order):
-//   plan      tile_start[u]: first 128-row tile of unit u (exclusive scan)
+//   plan      tile_start[u]: first 128-row tile of unit u (exclusive scan), and
+//             a record per score tile and per gather slot (its unit and rows),
+//             so that the later kernels find their rows in one read
 //   scores    per (128-row tile, 64 channels): fp32 sum of |R| over the tile's
 //             rows in increasing row order          (skipped when nvfp4_quantize
 //                                                    already produced them)
@@ -48,17 +50,6 @@ struct Units {
   }
 };
 
-// Unit of a tile slot (largest u with tile_start[u] <= slot); -1 if none.
-__device__ __forceinline__ int64_t unit_of_slot(const int32_t* tile_start, int64_t U, int64_t slot) {
-  if (slot >= tile_start[U]) return -1;
-  int64_t lo = 0, hi = U;            // tile_start[lo] <= slot < tile_start[hi]
-  while (hi - lo > 1) {
-    int64_t mid = (lo + hi) >> 1;
-    if (tile_start[mid] <= slot) lo = mid; else hi = mid;
-  }
-  return lo;
-}
-
 // ---------------------------------------------------------------------------
 // block-wide exclusive scan of one uint32 per thread (blockDim multiple of 64)
 // ---------------------------------------------------------------------------
@@ -87,15 +78,21 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // ---------------------------------------------------------------------------
 // plan
 // ---------------------------------------------------------------------------
+// Records: score tile t -> {unit, first row, the unit's end row, 0}; gather
+// slot q -> {unit, first row, end row (at most 32 rows), the unit's first
+// slot} {the unit's end slot, 0, 0, 0}.  Records past the last tile or slot
+// (the grids are sized by upper bounds) get unit -1.
 __global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* tile_start,
-                                                         int32_t* slot_start) {
+                                                         int32_t* slot_start, int4* tile_info,
+                                                         int64_t max_tiles, int4* slot_info,
+                                                         int64_t max_slots) {
   __shared__ uint32_t sh[16];
   uint32_t carry_t = 0, carry_s = 0;
   for (int64_t base = 0; base < units.U; base += blockDim.x) {
     int64_t u = base + threadIdx.x;
     uint32_t nt = 0, ns = 0;
+    int64_t b = 0, e = 0;
     if (u < units.U) {
-      int64_t b, e;
       units.range(u, b, e);
       nt = (uint32_t)((e - b + kScoreTileRows - 1) / kScoreTileRows);
       ns = (uint32_t)((e - b + kGatherRows - 1) / kGatherRows);
@@ -104,8 +101,16 @@ __global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* t
     const uint32_t ex_t = block_exclusive_scan(nt, sh, &tot_t);
     const uint32_t ex_s = block_exclusive_scan(ns, sh, &tot_s);
     if (u < units.U) {
-      tile_start[u] = (int32_t)(carry_t + ex_t);
-      slot_start[u] = (int32_t)(carry_s + ex_s);
+      const int32_t ts = (int32_t)(carry_t + ex_t), ss = (int32_t)(carry_s + ex_s);
+      tile_start[u] = ts;
+      slot_start[u] = ss;
+      for (uint32_t t = 0; t < nt; ++t)
+        tile_info[ts + t] = int4{(int32_t)u, (int32_t)(b + (int64_t)t * kScoreTileRows), (int32_t)e, 0};
+      for (uint32_t q = 0; q < ns; ++q) {
+        const int64_t r0 = b + (int64_t)q * kGatherRows;
+        slot_info[2 * (ss + q)] = int4{(int32_t)u, (int32_t)r0, (int32_t)(r0 + kGatherRows < e ? r0 + kGatherRows : e), ss};
+        slot_info[2 * (ss + q) + 1] = int4{ss + (int32_t)ns, 0, 0, 0};
+      }
     }
     carry_t += tot_t;
     carry_s += tot_s;
@@ -114,6 +119,8 @@ __global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* t
     tile_start[units.U] = (int32_t)carry_t;
     slot_start[units.U] = (int32_t)carry_s;
   }
+  for (int64_t t = carry_t + threadIdx.x; t < max_tiles; t += blockDim.x) tile_info[t] = int4{-1, 0, 0, 0};
+  for (int64_t q = carry_s + threadIdx.x; q < max_slots; q += blockDim.x) slot_info[2 * q] = int4{-1, 0, 0, 0};
 }
 
 // ---------------------------------------------------------------------------
@@ -167,19 +174,17 @@ template <typename T, bool MX>
 __global__ __launch_bounds__(256) void resq_scores_kernel(
     const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
     const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const float* __restrict__ gp, Units units,
-    const int32_t* __restrict__ tile_start, float* __restrict__ partials) {
+    const uint8_t* __restrict__ scales, const float* __restrict__ gp,
+    const int4* __restrict__ tile_info, float* __restrict__ partials) {
   __shared__ float absr[kScoreTileRows * kAbsStride];
   const int64_t slot = blockIdx.y;
-  const int64_t u = unit_of_slot(tile_start, units.U, slot);
-  if (u < 0) return;
+  const int4 ti = tile_info[slot];
+  if (ti.x < 0) return;
   const int tid = threadIdx.x;
   const int64_t nb = K / kBlock;
   const int bl = tid % kScoreBlocks, rsub = tid / kScoreBlocks;
   const int64_t bc = (int64_t)blockIdx.x * kScoreBlocks + bl;
-  int64_t b, e;
-  units.range(u, b, e);
-  const int64_t r0 = b + (slot - tile_start[u]) * kScoreTileRows;
+  const int64_t r0 = ti.y, e = ti.z;
   const float g = MX ? 1.0f : *gp;
   const int64_t nsb = MX ? K / kMxBlock : nb;           // scale bytes per row
   float v[2][16];
@@ -297,54 +302,17 @@ __device__ __forceinline__ uint32_t block_scan_small(uint32_t v, uint32_t* total
   return base + pre;
 }
 
-// Selection with the keys in registers (K <= 256 CH): thread t owns channels
-// [t CH, t CH + CH).  The k-th largest key T is found two bits per pass: the
-// three candidates T | d << lo (d = 1..3) are counted together and the
-// largest with at least k keys >= it is kept (16 passes for the 31 bits of a
-// non-negative float).  The rest is as in the LDS kernel below: keys > T,
-// then keys == T in channel order up to k, written in ascending channel order.
+// Top-k of the scores held in registers: thread t owns channels [c0, c0 +
+// n_my) (c0 = t CH) as non-negative float bits key[].  The k-th largest key T
+// is found two bits per pass: the three candidates T | d << lo (d = 1..3) are
+// counted together and the largest with at least k keys >= it is kept (16
+// passes for the 31 bits of a non-negative float).  Then keys > T, and keys
+// == T in channel order up to k, are written in ascending channel order to
+// out (and to out_lds when given).  All 256 threads call it.
 template <int CH>
-__global__ __launch_bounds__(256) void resq_select_reg_kernel(
-    const float* __restrict__ partials, int64_t K, Units units,
-    const int32_t* __restrict__ tile_start, int32_t k, int32_t* __restrict__ sel_idx,
-    float* __restrict__ r_global) {
-  __shared__ uint32_t sh[2][3][4];
-  const int64_t u = blockIdx.x;
-  const int tid = threadIdx.x;
-  int64_t b, e;
-  units.range(u, b, e);
-  int32_t* out = sel_idx + u * k;
-  if (e == b) {                               // empty unit: channels 0..k-1, g_R = 1
-    for (int j = tid; j < k; j += blockDim.x) out[j] = j;
-    if (tid == 0 && r_global) r_global[u] = 1.0f;   // NULL for MXFP4 (no global scale)
-    return;
-  }
-  const int64_t t0 = tile_start[u], t1 = tile_start[u + 1];
-  const int64_t c0 = (int64_t)tid * CH;
-  const int n_my = (int)(c0 >= K ? 0 : (c0 + CH <= K ? CH : K - c0));
-  float acc[CH];
-#pragma unroll
-  for (int j = 0; j < CH; ++j) acc[j] = 0.0f;
-  if (n_my == CH) {                           // K % 16 == 0: whole 16-byte groups
-    for (int64_t t = t0; t < t1; ++t) {       // tile order
-      const f32x4* src = reinterpret_cast<const f32x4*>(partials + t * K + c0);
-#pragma unroll
-      for (int q = 0; q < CH / 4; ++q) {
-        const f32x4 v = src[q];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[4 * q + i] = acc[4 * q + i] + v[i];
-      }
-    }
-  } else {
-    for (int64_t t = t0; t < t1; ++t)
-#pragma unroll
-      for (int j = 0; j < CH; ++j)
-        if (j < n_my) acc[j] = acc[j] + partials[t * K + c0 + j];
-  }
-  uint32_t key[CH];
-#pragma unroll
-  for (int j = 0; j < CH; ++j) key[j] = __float_as_uint(acc[j]);
-
+__device__ __forceinline__ void topk_reg(const uint32_t (&key)[CH], int n_my, int64_t c0, int32_t k,
+                                         int32_t* __restrict__ out, int32_t* out_lds,
+                                         uint32_t (*sh)[3][4]) {
   // per-thread counts are at most CH (<= 32): 6 bit planes
   constexpr int kBits = 6;
   uint32_t T = 0;
@@ -393,8 +361,57 @@ __global__ __launch_bounds__(256) void resq_select_reg_kernel(
   while (take) {                              // ascending channel order
     const int j = __builtin_ctz(take);
     take &= take - 1;
-    if (pos < (uint32_t)k) out[pos++] = (int32_t)(c0 + j);
+    if (pos < (uint32_t)k) {
+      if (out_lds) out_lds[pos] = (int32_t)(c0 + j);
+      out[pos++] = (int32_t)(c0 + j);
+    }
   }
+}
+
+// Selection with the keys in registers (K <= 256 CH): thread t adds the tile
+// sums of channels [t CH, t CH + CH) in tile order, then topk_reg.
+template <int CH>
+__global__ __launch_bounds__(256) void resq_select_reg_kernel(
+    const float* __restrict__ partials, int64_t K, Units units,
+    const int32_t* __restrict__ tile_start, int32_t k, int32_t* __restrict__ sel_idx,
+    float* __restrict__ r_global) {
+  __shared__ uint32_t sh[2][3][4];
+  const int64_t u = blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t b, e;
+  units.range(u, b, e);
+  int32_t* out = sel_idx + u * k;
+  if (e == b) {                               // empty unit: channels 0..k-1, g_R = 1
+    for (int j = tid; j < k; j += blockDim.x) out[j] = j;
+    if (tid == 0 && r_global) r_global[u] = 1.0f;   // NULL for MXFP4 (no global scale)
+    return;
+  }
+  const int64_t t0 = tile_start[u], t1 = tile_start[u + 1];
+  const int64_t c0 = (int64_t)tid * CH;
+  const int n_my = (int)(c0 >= K ? 0 : (c0 + CH <= K ? CH : K - c0));
+  float acc[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) acc[j] = 0.0f;
+  if (n_my == CH) {                           // K % 16 == 0: whole 16-byte groups
+    for (int64_t t = t0; t < t1; ++t) {       // tile order
+      const f32x4* src = reinterpret_cast<const f32x4*>(partials + t * K + c0);
+#pragma unroll
+      for (int q = 0; q < CH / 4; ++q) {
+        const f32x4 v = src[q];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[4 * q + i] = acc[4 * q + i] + v[i];
+      }
+    }
+  } else {
+    for (int64_t t = t0; t < t1; ++t)
+#pragma unroll
+      for (int j = 0; j < CH; ++j)
+        if (j < n_my) acc[j] = acc[j] + partials[t * K + c0 + j];
+  }
+  uint32_t key[CH];
+#pragma unroll
+  for (int j = 0; j < CH; ++j) key[j] = __float_as_uint(acc[j]);
+  topk_reg<CH>(key, n_my, c0, k, out, nullptr, sh);
 }
 
 // Keys live in LDS chunk by chunk: thread t owns channels [t*chunk, (t+1)*chunk)
@@ -471,46 +488,78 @@ __global__ __launch_bounds__(256) void resq_select_kernel(
 // ---------------------------------------------------------------------------
 // gather R_S and per-slot max |R_S|
 // ---------------------------------------------------------------------------
+// One workgroup per 32-row slot.  The slot's row indexes and the unit's
+// selected channels go to LDS first; then every thread issues the loads of
+// its (row, channel) elements in batches of 8 before any arithmetic, so a
+// thread waits for one memory round trip per batch, not per element.  Rows
+// with a bad index read nothing and give R_S = 0.
 template <typename T, bool MX>
 __global__ __launch_bounds__(256) void resq_gather_kernel(
     const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
     const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
-    const uint8_t* __restrict__ scales, const float* __restrict__ gp, Units units,
-    const int32_t* __restrict__ slot_start, const int32_t* __restrict__ sel_idx, int32_t k,
+    const uint8_t* __restrict__ scales, const float* __restrict__ gp,
+    const int4* __restrict__ slot_info, const int32_t* __restrict__ sel_idx, int32_t k,
     float* __restrict__ r_s, float* __restrict__ amax_part) {
   extern __shared__ int32_t sel[];           // [k]
+  __shared__ int32_t xrow[kGatherRows];
   __shared__ float red[4];
   const int64_t slot = blockIdx.x;
-  const int64_t u = unit_of_slot(slot_start, units.U, slot);
+  const int4 si = slot_info[2 * slot];
+  const int u = si.x;
   if (u < 0) return;
-  int64_t b, e;
-  units.range(u, b, e);
-  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
-  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
+  const int64_t r0 = si.y;
+  const int nrows = si.z - si.y;
+  const float g = MX ? 1.0f : *gp;
   for (int j = threadIdx.x; j < k; j += blockDim.x) {
-    int32_t c = sel_idx[u * k + j];
+    int32_t c = sel_idx[(int64_t)u * k + j];
     sel[j] = c < 0 ? 0 : (c >= K ? (int32_t)(K - 1) : c);
   }
-  __syncthreads();
-  const float g = MX ? 1.0f : *gp;
-  const int64_t nb = K / (MX ? kMxBlock : kBlock);
-  float m = 0.0f;
-  const int64_t n = (r1 - r0) * k;
-  for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
-    const int64_t r = r0 + i / k;
-    const int j = (int)(i % k);
+  if ((int)threadIdx.x < nrows) {
+    const int64_t r = r0 + threadIdx.x;
     const int64_t xr = row_index ? (int64_t)row_index[r] : r;
-    float res = 0.0f;
-    if (xr >= 0 && xr < x_rows) {
-      const int64_t c = sel[j];
-      const float xv = load1<T>(x + xr * ldx + c);
-      const uint32_t code = (codes[xr * (K / 2) + (c >> 1)] >> (4 * (c & 1))) & 15u;
-      const float S = MX ? e8m0_value(scales[xr * nb + (c >> 5)])
-                         : e4m3_value(scales[xr * nb + (c >> 4)]) * g;
-      res = xv - dq(code, S);
+    xrow[threadIdx.x] = xr >= 0 && xr < x_rows ? (int32_t)xr : -1;
+  }
+  __syncthreads();
+  const int64_t nb = K / (MX ? kMxBlock : kBlock);
+  constexpr int B = 8;
+  float m = 0.0f;
+  const int n = nrows * k;
+  for (int i0 = 0; i0 < n; i0 += 256 * B) {
+    float xv[B];
+    uint32_t cb[B], sbyte[B];
+    int rl[B], j[B], c[B], xr[B];
+#pragma unroll
+    for (int q = 0; q < B; ++q) {             // the batch's loads
+      const int i = i0 + (int)threadIdx.x + 256 * q;
+      const int ii = i < n ? i : n - 1;
+      rl[q] = ii / k;
+      j[q] = ii - rl[q] * k;
+      xr[q] = xrow[rl[q]];
+      c[q] = sel[j[q]];
+      xv[q] = 0.0f;
+      cb[q] = 0;
+      sbyte[q] = 0;
+      if (xr[q] >= 0) {
+        const int64_t xe = xr[q];
+        xv[q] = load1<T>(x + xe * ldx + c[q]);
+        cb[q] = codes[xe * (K / 2) + (c[q] >> 1)];
+        sbyte[q] = scales[xe * nb + (c[q] >> (MX ? 5 : 4))];
+      }
     }
-    r_s[r * k + j] = res;
-    m = fmaxf(m, fabsf(res));
+#pragma unroll
+    for (int q = 0; q < B; ++q) {
+      const int i = i0 + (int)threadIdx.x + 256 * q;
+      if (i < n) {
+        float res = 0.0f;
+        if (xr[q] >= 0) {
+          const uint32_t code = (cb[q] >> (4 * (c[q] & 1))) & 15u;
+          const float S = MX ? e8m0_value(sbyte[q]) : e4m3_value(sbyte[q]) * g;
+          res = xv[q] - dq(code, S);
+        }
+        r_s[(r0 + rl[q]) * k + j[q]] = res;
+        m = fmaxf(m, fabsf(res));
+      }
+    }
   }
   m = wave_max(m);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
@@ -526,18 +575,18 @@ __global__ __launch_bounds__(256) void resq_gather_kernel(
 // requantize R_S with the unit's own global scale
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void resq_requant_kernel(
-    const float* __restrict__ r_s, Units units, const int32_t* __restrict__ slot_start,
+    const float* __restrict__ r_s, const int4* __restrict__ slot_info,
     const float* __restrict__ amax_part, int32_t k, uint8_t* __restrict__ r_codes,
     uint8_t* __restrict__ r_scales, float* __restrict__ r_global) {
   __shared__ float sh_g;
   const int64_t slot = blockIdx.x;
-  const int64_t u = unit_of_slot(slot_start, units.U, slot);
+  const int4 si = slot_info[2 * slot];
+  const int u = si.x;
   if (u < 0) return;
-  int64_t b, e;
-  units.range(u, b, e);
+  const int s_end = slot_info[2 * slot + 1].x;
   if (threadIdx.x < 64) {
     float m = 0.0f;
-    for (int64_t t = slot_start[u] + threadIdx.x; t < slot_start[u + 1]; t += 64)
+    for (int t = si.w + (int)threadIdx.x; t < s_end; t += 64)
       m = fmaxf(m, amax_part[t]);
     m = wave_max(m);
     if (threadIdx.x == 0) sh_g = global_scale_from_amax(m);
@@ -545,9 +594,8 @@ __global__ __launch_bounds__(256) void resq_requant_kernel(
   __syncthreads();
   const float g = sh_g;
   const BlockScaler bsc = make_block_scaler(g);
-  if (slot == slot_start[u] && threadIdx.x == 0) r_global[u] = g;
-  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
-  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
+  if (slot == si.w && threadIdx.x == 0) r_global[u] = g;
+  const int64_t r0 = si.y, r1 = si.z;
   const int kb = k / kBlock;
   const int64_t n = (r1 - r0) * kb;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
@@ -569,26 +617,26 @@ __global__ __launch_bounds__(256) void resq_requant_kernel(
 // channel c, or -1 outside the mask (K <= kMaskMaxK).
 constexpr int kMaskMaxK = 16384;
 __global__ __launch_bounds__(256) void resq_mask_requant_kernel(
-    const float* __restrict__ r_s, Units units, const int32_t* __restrict__ slot_start,
+    const float* __restrict__ r_s, const int4* __restrict__ slot_info,
     const float* __restrict__ amax_part, const int32_t* __restrict__ sel_idx, int32_t k, int64_t K,
     uint8_t* __restrict__ m_codes, uint8_t* __restrict__ m_scales, float* __restrict__ m_global) {
   __shared__ int16_t pos[kMaskMaxK];
   __shared__ float sh_g;
   const int64_t slot = blockIdx.x;
-  const int64_t u = unit_of_slot(slot_start, units.U, slot);
+  const int4 si = slot_info[2 * slot];
+  const int u = si.x;
   if (u < 0) return;
-  int64_t b, e;
-  units.range(u, b, e);
+  const int s_end = slot_info[2 * slot + 1].x;
   for (int64_t c = threadIdx.x; c < K; c += blockDim.x) pos[c] = -1;
   __syncthreads();
   for (int j = threadIdx.x; j < k; j += blockDim.x) {
-    int32_t c = sel_idx[u * k + j];
+    int32_t c = sel_idx[(int64_t)u * k + j];
     c = c < 0 ? 0 : (c >= K ? (int32_t)(K - 1) : c);
     pos[c] = (int16_t)j;
   }
   if (threadIdx.x < 64) {
     float m = 0.0f;
-    for (int64_t t = slot_start[u] + threadIdx.x; t < slot_start[u + 1]; t += 64)
+    for (int t = si.w + (int)threadIdx.x; t < s_end; t += 64)
       m = fmaxf(m, amax_part[t]);
     m = wave_max(m);
     if (threadIdx.x == 0) sh_g = global_scale_from_amax(m);
@@ -596,9 +644,8 @@ __global__ __launch_bounds__(256) void resq_mask_requant_kernel(
   __syncthreads();
   const float g = sh_g;
   const BlockScaler bsc = make_block_scaler(g);
-  if (slot == slot_start[u] && threadIdx.x == 0) m_global[u] = g;
-  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
-  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
+  if (slot == si.w && threadIdx.x == 0) m_global[u] = g;
+  const int64_t r0 = si.y, r1 = si.z;
   const int64_t kb = K / kBlock;
   const int64_t n = (r1 - r0) * kb;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
@@ -620,15 +667,12 @@ __global__ __launch_bounds__(256) void resq_mask_requant_kernel(
 // MXFP4 of R_S: 32-blocks along the compact axis, each with its own E8M0
 // scale; no global scale.
 __global__ __launch_bounds__(256) void resq_requant_mx_kernel(
-    const float* __restrict__ r_s, Units units, const int32_t* __restrict__ slot_start, int32_t k,
+    const float* __restrict__ r_s, const int4* __restrict__ slot_info, int32_t k,
     uint8_t* __restrict__ r_codes, uint8_t* __restrict__ r_scales) {
   const int64_t slot = blockIdx.x;
-  const int64_t u = unit_of_slot(slot_start, units.U, slot);
-  if (u < 0) return;
-  int64_t b, e;
-  units.range(u, b, e);
-  const int64_t r0 = b + (slot - slot_start[u]) * kGatherRows;
-  const int64_t r1 = r0 + kGatherRows < e ? r0 + kGatherRows : e;
+  const int4 si = slot_info[2 * slot];
+  if (si.x < 0) return;
+  const int64_t r0 = si.y, r1 = si.z;
   const int kb = k / kMxBlock;
   const int64_t n = (r1 - r0) * kb;
   for (int64_t i = threadIdx.x; i < n; i += blockDim.x) {
@@ -649,6 +693,218 @@ __global__ __launch_bounds__(256) void resq_requant_mx_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// small units: the whole step in one workgroup per unit
+// ---------------------------------------------------------------------------
+// Where the units hold a few rows each (decode batches), one workgroup per
+// unit runs the scores, the selection, the gather and the requantization in
+// one launch, with the unit's rows in L2.  The arithmetic and its order are
+// those of the kernels above: a score is the fp32 sum of |R| over each
+// 128-row tile in row order, the tile sums added in tile order; the selection
+// is topk_reg; R_S = x - DQ at the selected channels; the unit's max |R_S|
+// gives g_R and quantize_block16 the codes.  Thread t owns the score
+// channels [t CH, t CH + CH) (CH = 8 for K <= 2048, 16 for K <= 4096).  R_S
+// stays in LDS when the unit's rows x k fit in kSmallRs floats, else it is
+// computed again (the same values) for the requantization.
+constexpr int kSmallRs = 8192;
+constexpr int kSmallMaxK = 4096;
+
+template <typename T, int CH>
+__device__ __forceinline__ void load_ch(const T* p, float* v) {
+  static_assert(CH == 8 || CH == 16, "channels per thread");
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int h = 0; h < CH / 8; ++h) {
+      const u32x4 a = reinterpret_cast<const u32x4*>(p)[h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[8 * h + 2 * i] = bf16_lo(a[i]);
+        v[8 * h + 2 * i + 1] = bf16_hi(a[i]);
+      }
+    }
+  } else {
+#pragma unroll
+    for (int h = 0; h < CH / 4; ++h) {
+      const f32x4 a = reinterpret_cast<const f32x4*>(p)[h];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * h + i] = a[i];
+    }
+  }
+}
+
+template <typename T, int CH>
+__global__ __launch_bounds__(256) void resq_small_kernel(
+    const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
+    const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ gp, Units units, int32_t k,
+    int32_t* __restrict__ sel_idx, uint8_t* __restrict__ r_codes, uint8_t* __restrict__ r_scales,
+    float* __restrict__ r_global) {
+  __shared__ int32_t xrow[kScoreTileRows];
+  __shared__ int32_t sel[kSmallMaxK];
+  __shared__ float rs[kSmallRs];
+  __shared__ uint32_t sh[2][3][4];
+  __shared__ float red[4];
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x;
+  int64_t b, e;
+  units.range(u, b, e);
+  int32_t* out = sel_idx + (int64_t)u * k;
+  if (e == b) {                               // empty unit: channels 0..k-1, g_R = 1
+    for (int j = tid; j < k; j += blockDim.x) out[j] = j;
+    if (tid == 0) r_global[u] = 1.0f;
+    return;
+  }
+  const float g = *gp;
+  const int64_t nb = K / kBlock;
+  const int64_t c0 = (int64_t)tid * CH;
+  const bool mine = c0 < K;                   // K % 16 == 0: whole groups of CH
+  // x row indexes of the unit rows [t0, t0 + nr) into xrow (-1: bad index)
+  auto load_rows = [&](int64_t t0, int nr) {
+    __syncthreads();                          // earlier readers of xrow are done
+    if (tid < nr) {
+      const int64_t r = t0 + tid;
+      const int64_t xr = row_index ? (int64_t)row_index[r] : r;
+      xrow[tid] = xr >= 0 && xr < x_rows ? (int32_t)xr : -1;
+    }
+    __syncthreads();
+  };
+
+  // ---- scores
+  float total[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) total[i] = 0.0f;
+  for (int64_t t0 = b; t0 < e; t0 += kScoreTileRows) {
+    const int nr = (int)(e - t0 < kScoreTileRows ? e - t0 : kScoreTileRows);
+    load_rows(t0, nr);
+    float ts[CH];
+#pragma unroll
+    for (int i = 0; i < CH; ++i) ts[i] = 0.0f;
+    if (mine) {
+      for (int rb = 0; rb < nr; rb += 8) {    // 8 rows' loads, then their arithmetic
+        float v[8][CH];
+        uint32_t cw[8][CH / 8], sb[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int xr = rb + q < nr ? xrow[rb + q] : -1;
+          if (xr >= 0) {
+            load_ch<T, CH>(x + (int64_t)xr * ldx + c0, v[q]);
+            const uint32_t* cp = reinterpret_cast<const uint32_t*>(codes + (int64_t)xr * (K / 2) + c0 / 2);
+#pragma unroll
+            for (int h = 0; h < CH / 8; ++h) cw[q][h] = cp[h];
+            sb[q] = scales[(int64_t)xr * nb + c0 / kBlock];
+          } else {                            // a bad index scores |0 - 0| = 0
+#pragma unroll
+            for (int i = 0; i < CH; ++i) v[q][i] = 0.0f;
+#pragma unroll
+            for (int h = 0; h < CH / 8; ++h) cw[q][h] = 0;
+            sb[q] = 0;
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (rb + q < nr) {
+            const float S = e4m3_value(sb[q]) * g;
+            float f[CH];
+#pragma unroll
+            for (int h = 0; h < CH / 8; ++h) e2m1_unpack8(cw[q][h], f + 8 * h);
+#pragma unroll
+            for (int i = 0; i < CH; ++i) ts[i] = ts[i] + fabsf(v[q][i] - f[i] * S);   // exact; no contraction
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < CH; ++i) total[i] = total[i] + ts[i];
+  }
+
+  // ---- selection (ascending channel list in out and in sel)
+  uint32_t key[CH];
+#pragma unroll
+  for (int i = 0; i < CH; ++i) key[i] = __float_as_uint(total[i]);
+  topk_reg<CH>(key, mine ? CH : 0, c0, k, out, sel, sh);
+
+  // ---- R_S of (row, 16-channel block) items and the unit's max |R_S|
+  const int kb = k / kBlock;
+  const int64_t n = e - b;
+  const bool keep = n * k <= kSmallRs;
+  auto r_item = [&](int xr, int bl, float* R) {
+    float xv[kBlock];
+    uint32_t cb[kBlock], sbb[kBlock];
+    int c[kBlock];
+#pragma unroll
+    for (int q = 0; q < kBlock; ++q) {
+      c[q] = sel[bl * kBlock + q];
+      xv[q] = 0.0f;
+      cb[q] = 0;
+      sbb[q] = 0;
+      if (xr >= 0) {
+        xv[q] = load1<T>(x + (int64_t)xr * ldx + c[q]);
+        cb[q] = codes[(int64_t)xr * (K / 2) + (c[q] >> 1)];
+        sbb[q] = scales[(int64_t)xr * nb + (c[q] >> 4)];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kBlock; ++q) {
+      float res = 0.0f;
+      if (xr >= 0) {
+        const uint32_t code = (cb[q] >> (4 * (c[q] & 1))) & 15u;
+        res = xv[q] - dq(code, e4m3_value(sbb[q]) * g);
+      }
+      R[q] = res;
+    }
+  };
+  float m = 0.0f;
+  for (int64_t t0 = b; t0 < e; t0 += kScoreTileRows) {
+    const int nr = (int)(e - t0 < kScoreTileRows ? e - t0 : kScoreTileRows);
+    load_rows(t0, nr);                        // its first barrier also orders the sel writes
+    for (int i = tid; i < nr * kb; i += blockDim.x) {
+      const int rl = i / kb, bl = i - rl * kb;
+      float R[kBlock];
+      r_item(xrow[rl], bl, R);
+#pragma unroll
+      for (int q = 0; q < kBlock; ++q) {
+        m = fmaxf(m, fabsf(R[q]));
+        if (keep) rs[(t0 - b + rl) * k + bl * kBlock + q] = R[q];
+      }
+    }
+  }
+  m = wave_max(m);
+  if ((tid & 63) == 0) red[tid >> 6] = m;
+  __syncthreads();
+  const float gr = global_scale_from_amax(fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])));
+  const BlockScaler bsc = make_block_scaler(gr);
+  if (tid == 0) r_global[u] = gr;
+
+  // ---- requantization of R_S with the unit's own global scale
+  auto requant = [&](int64_t r, int bl, const float* R) {
+    uint32_t sb, w0, w1;
+    quantize_block16(R, bsc, &sb, &w0, &w1);
+    *reinterpret_cast<u32x2*>(r_codes + r * (k / 2) + bl * 8) = u32x2{w0, w1};
+    r_scales[r * kb + bl] = (uint8_t)sb;
+  };
+  if (keep) {
+    for (int64_t i = tid; i < n * kb; i += blockDim.x) {
+      const int64_t rl = i / kb;
+      const int bl = (int)(i - rl * kb);
+      float R[kBlock];
+#pragma unroll
+      for (int q = 0; q < kBlock; ++q) R[q] = rs[rl * k + bl * kBlock + q];
+      requant(b + rl, bl, R);
+    }
+  } else {
+    for (int64_t t0 = b; t0 < e; t0 += kScoreTileRows) {
+      const int nr = (int)(e - t0 < kScoreTileRows ? e - t0 : kScoreTileRows);
+      load_rows(t0, nr);
+      for (int i = tid; i < nr * kb; i += blockDim.x) {
+        const int rl = i / kb, bl = i - rl * kb;
+        float R[kBlock];
+        r_item(xrow[rl], bl, R);
+        requant(t0 + rl, bl, R);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
 template <typename T, bool MX>
@@ -660,14 +916,30 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
                                 uint8_t* r_codes, uint8_t* r_scales, float* r_global,
                                 const ResqWorkspace& ws, hipStream_t stream, bool masked) {
   Units units{tile_partials ? nullptr : unit_offsets, U, rows_total};
+  // Few rows per unit (at most 32 on average, at most 8192 in all): the whole
+  // step per unit in one launch.
+  if constexpr (!MX) {
+    if (!masked && !tile_partials && K <= kSmallMaxK && rows_total <= 32 * U && rows_total <= 8192) {
+      if (K <= 256 * 8)
+        resq_small_kernel<T, 8><<<(unsigned)U, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
+                                                                 units, k, sel_idx, r_codes, r_scales, r_global);
+      else
+        resq_small_kernel<T, 16><<<(unsigned)U, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
+                                                                  units, k, sel_idx, r_codes, r_scales, r_global);
+      return hipGetLastError();
+    }
+  }
   const int64_t slots = tile_partials ? U : resq_max_slots(rows_total, U);
   const int64_t gslots = resq_max_gather_slots(rows_total, U);
-  resq_plan_kernel<<<1, 1024, 0, stream>>>(units, ws.tile_start, ws.slot_start);
+  int4* tile_info = reinterpret_cast<int4*>(ws.tile_info);
+  int4* slot_info = reinterpret_cast<int4*>(ws.slot_info);
+  resq_plan_kernel<<<1, 1024, 0, stream>>>(units, ws.tile_start, ws.slot_start, tile_info, slots,
+                                           slot_info, gslots);
   const float* partials = tile_partials;
   if (!tile_partials) {
     dim3 grid((unsigned)((K + kScoreCols - 1) / kScoreCols), (unsigned)slots);
     resq_scores_kernel<T, MX><<<grid, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
-                                                    units, ws.tile_start, ws.partials);
+                                                    tile_info, ws.partials);
     partials = ws.partials;
   }
   if (K <= 256 * 4) {
@@ -694,18 +966,17 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
   }
   if (gslots > 0) {
     resq_gather_kernel<T, MX><<<(unsigned)gslots, 256, (size_t)k * 4, stream>>>(
-        x, x_rows, K, ldx, row_index, codes, scales, g, units, ws.slot_start, sel_idx, k, ws.r_s,
+        x, x_rows, K, ldx, row_index, codes, scales, g, slot_info, sel_idx, k, ws.r_s,
         ws.amax_part);
     if constexpr (MX)
-      resq_requant_mx_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start, k,
-                                                                   r_codes, r_scales);
+      resq_requant_mx_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, slot_info, k, r_codes,
+                                                                   r_scales);
     else if (masked)
       resq_mask_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(
-          ws.r_s, units, ws.slot_start, ws.amax_part, sel_idx, k, K, r_codes, r_scales, r_global);
+          ws.r_s, slot_info, ws.amax_part, sel_idx, k, K, r_codes, r_scales, r_global);
     else
-      resq_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, units, ws.slot_start,
-                                                                ws.amax_part, k, r_codes, r_scales,
-                                                                r_global);
+      resq_requant_kernel<<<(unsigned)gslots, 256, 0, stream>>>(ws.r_s, slot_info, ws.amax_part, k,
+                                                                r_codes, r_scales, r_global);
   }
   return hipGetLastError();
 }

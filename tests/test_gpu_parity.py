@@ -236,6 +236,34 @@ def test_resq_gathered_expert_units(gpu_lib, k):
     assert np.array_equal(npu8(rc), rc_r)
 
 
+@pytest.mark.parametrize("hidden,k", [(768, 64), (2048, 16), (2048, 64), (3072, 64)])
+def test_resq_small_units(gpu_lib, hidden, k):
+    """Decode-sized units (at most 32 routed rows per unit on average), which
+    the library handles in one launch with one workgroup per unit: 64 experts,
+    many of them empty, and a hot expert of 381 rows (scores over three
+    128-row tiles; with k = 64 its R_S is computed a second time for the
+    requantization instead of being kept on chip)."""
+    P = gpu_lib
+    tokens, n_exp = 512, 64
+    x = synth.activations(tokens, hidden, seed=21, heavy_frac=0.02)
+    rt = synth.route(tokens, n_exp, seed=21, top_k=2, zipf_s=1.1)
+    offs = rt["offsets"]
+    assert offs[-1] <= 32 * n_exp and np.diff(offs).max() > 2 * 128 and (np.diff(offs) == 0).any()
+    xc = x.cuda()
+    codes, scales, g, _ = P.nvfp4_quantize(xc)
+    sel, rc, rs, rg = P.resq_select_and_requant(
+        xc, codes, scales, g, k, unit_offsets=torch.from_numpy(offs).cuda(),
+        rows_total=int(offs[-1]), row_index=torch.from_numpy(rt["slot_token"]).cuda())
+    x_np = x.float().numpy()
+    c_ref, s_ref, g_ref = OQ.quantize(x_np)
+    sel_r, rc_r, rs_r, rg_r = OQ.resq_select_and_requant(x_np, c_ref, s_ref, g_ref, offs, k,
+                                                         row_index=rt["slot_token"])
+    assert np.array_equal(npu8(sel), sel_r)
+    assert np.array_equal(np32(rg), rg_r)
+    assert np.array_equal(npu8(rs), rs_r)
+    assert np.array_equal(npu8(rc), rc_r)
+
+
 # ---------------------------------------------------------------------------
 # GEMM
 # ---------------------------------------------------------------------------
