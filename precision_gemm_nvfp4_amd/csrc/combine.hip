@@ -9,12 +9,15 @@
 //   place    each row appended to its output row's list (atomic cursor), then
 //   combine  one workgroup per output row: the list is sorted ascending in LDS
 //            and the rows are added in that order, 4 columns per thread.
+// With few output rows (decode batches) count, scan and place run in one
+// workgroup with the counters in LDS: two launches in all instead of six.
 #include "device_common.h"
 #include "kernels.h"
 
 namespace nvfp4 {
 
 constexpr int kMaxListLds = 1024;           // rows per output row sorted in LDS
+constexpr int kPlanSmallOut = 4096;         // output rows of the one-workgroup plan
 
 __global__ void combine_zero_kernel(int32_t* p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
@@ -70,6 +73,54 @@ __global__ void combine_place_kernel(const int32_t* __restrict__ scatter_index, 
   }
 }
 
+// count, scan and place in one workgroup (out_rows <= kPlanSmallOut): the
+// counts and the cursors live in LDS, start[] goes to memory.
+__global__ __launch_bounds__(1024) void combine_plan_small_kernel(const int32_t* __restrict__ scatter_index,
+                                                                 int64_t rows, int64_t out_rows,
+                                                                 int32_t* __restrict__ start,
+                                                                 int32_t* __restrict__ list) {
+  __shared__ int32_t cnt[kPlanSmallOut + 1];
+  __shared__ int32_t sh[16];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int64_t t = tid; t <= out_rows; t += blockDim.x) cnt[t] = 0;
+  __syncthreads();
+  for (int64_t r = tid; r < rows; r += blockDim.x) {
+    const int64_t t = scatter_index[r];
+    if (t >= 0 && t < out_rows) atomicAdd(cnt + t, 1);
+  }
+  __syncthreads();
+  // exclusive prefix of cnt in chunks of blockDim; cnt[t] becomes start[t]
+  int32_t carry = 0;
+  for (int64_t base = 0; base < out_rows; base += blockDim.x) {
+    const int64_t t = base + tid;
+    const int32_t v = t < out_rows ? cnt[t] : 0;
+    int32_t inc = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int32_t u = __shfl_up(inc, o, 64);
+      if (lane >= o) inc += u;
+    }
+    if (lane == 63) sh[wid] = inc;
+    __syncthreads();
+    int32_t before = carry, tot = 0;
+    for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+      if (w < wid) before += sh[w];
+      tot += sh[w];
+    }
+    if (t < out_rows) {
+      cnt[t] = before + inc - v;
+      start[t] = before + inc - v;
+    }
+    carry += tot;
+    __syncthreads();
+  }
+  if (tid == 0) start[out_rows] = carry;
+  for (int64_t r = tid; r < rows; r += blockDim.x) {
+    const int64_t t = scatter_index[r];
+    if (t >= 0 && t < out_rows) list[atomicAdd(cnt + t, 1)] = (int32_t)r;
+  }
+}
+
 __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restrict__ y_rows,
                                                            int64_t N, const int32_t* __restrict__ start,
                                                            int32_t* __restrict__ list,
@@ -98,13 +149,24 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
   for (int64_t c = (int64_t)threadIdx.x * 4; c < N; c += (int64_t)blockDim.x * 4) {
     if (vec4 && c + 4 <= N) {
       f32x4 acc = *reinterpret_cast<const f32x4*>(o + c);
-      for (int32_t i = 0; i < n; ++i) {
-        const int32_t r = i < kMaxListLds ? srt[i] : lst[i];
-        const f32x4 v = *reinterpret_cast<const f32x4*>(y_rows + (int64_t)r * N + c);
-        acc[0] = acc[0] + v[0];
-        acc[1] = acc[1] + v[1];
-        acc[2] = acc[2] + v[2];
-        acc[3] = acc[3] + v[3];
+      // rows in groups of 8: the group's loads go out before its additions
+      for (int32_t i0 = 0; i0 < n; i0 += 8) {
+        f32x4 v[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          const int32_t i = i0 + q < n ? i0 + q : n - 1;
+          const int32_t r = i < kMaxListLds ? srt[i] : lst[i];
+          v[q] = *reinterpret_cast<const f32x4*>(y_rows + (int64_t)r * N + c);
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          if (i0 + q < n) {
+            acc[0] = acc[0] + v[q][0];
+            acc[1] = acc[1] + v[q][1];
+            acc[2] = acc[2] + v[q][2];
+            acc[3] = acc[3] + v[q][3];
+          }
+        }
       }
       *reinterpret_cast<f32x4*>(o + c) = acc;
     } else {
@@ -137,6 +199,14 @@ hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
   int32_t* cursor = reinterpret_cast<int32_t*>(w);
   w += a256((size_t)(out_rows + 1) * 4);
   int32_t* list = reinterpret_cast<int32_t*>(w);
+  if (out_rows <= kPlanSmallOut) {
+    combine_plan_small_kernel<<<1, 1024, 0, stream>>>(scatter_index, rows, out_rows, start, list);
+    if (out_rows > 0)
+      combine_rows_kernel<<<(unsigned)out_rows, 256, 0, stream>>>(
+          y_rows, N, start, list, out, ldo,
+          N % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0);
+    return hipGetLastError();
+  }
   const int64_t zb = (out_rows + 255) / 256;
   combine_zero_kernel<<<(unsigned)(zb > 1024 ? 1024 : (zb < 1 ? 1 : zb)), 256, 0, stream>>>(count, out_rows + 1);
   combine_zero_kernel<<<(unsigned)(zb > 1024 ? 1024 : (zb < 1 ? 1 : zb)), 256, 0, stream>>>(cursor, out_rows + 1);

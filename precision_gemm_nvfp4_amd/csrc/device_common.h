@@ -321,6 +321,20 @@ __device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// The same sum by DPP row operations (no LDS traffic), returned as a uniform
+// value: sums within quads, half rows and rows of 16 lanes, then row 0 into
+// row 1 and row 2 into row 3 (row_bcast:15), then rows 0-1 into rows 2-3
+// (row_bcast:31), leaving the total in lane 63.  Lanes outside a row mask
+// take the old operand, 0.
+__device__ __forceinline__ uint32_t wave_sum_dpp(uint32_t v) {
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);    // quad_perm [1,0,3,2]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);    // quad_perm [2,3,0,1]
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);   // row_half_mirror
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);   // row_mirror
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xA, 0xF, false);   // row_bcast:15
+  v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xC, 0xF, false);   // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
 
 // Atomic max of a non-negative float stored as fp32 bits (non-negative
 // floats order like their bit patterns).

@@ -258,27 +258,31 @@ __device__ __forceinline__ uint32_t wave_scan_small(uint32_t v, uint32_t* total)
   return pre;
 }
 
-// Workgroup (4 waves) sums of three small counts with one barrier: the wave
-// sums go to sh[parity], and callers alternate the parity, so a slot is
+// Workgroup (4 waves) sums of three counts (each below 2^16 over a wave)
+// with one barrier: two DPP wave sums (a and b packed in one word), the wave
+// totals to sh[parity], and callers alternate the parity, so a slot is
 // rewritten only after the next call's barrier, which every reader of it has
 // passed.
-template <int BITS>
-__device__ __forceinline__ void block_sum3_small(uint32_t& a, uint32_t& b, uint32_t& c,
-                                                 uint32_t (*sh)[3][4], int parity) {
-  uint32_t ta, tb, tc;
-  wave_scan_small<BITS>(a, &ta);
-  wave_scan_small<BITS>(b, &tb);
-  wave_scan_small<BITS>(c, &tc);
+__device__ __forceinline__ void block_sum3(uint32_t& a, uint32_t& b, uint32_t& c,
+                                           uint32_t (*sh)[3][4], int parity) {
+  const uint32_t ab = wave_sum_dpp(a | (b << 16)), cc = wave_sum_dpp(c);
   const int w = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
-    sh[parity][0][w] = ta;
-    sh[parity][1][w] = tb;
-    sh[parity][2][w] = tc;
+    sh[parity][0][w] = ab;
+    sh[parity][1][w] = cc;
   }
   __syncthreads();
-  a = sh[parity][0][0] + sh[parity][0][1] + sh[parity][0][2] + sh[parity][0][3];
-  b = sh[parity][1][0] + sh[parity][1][1] + sh[parity][1][2] + sh[parity][1][3];
-  c = sh[parity][2][0] + sh[parity][2][1] + sh[parity][2][2] + sh[parity][2][3];
+  uint32_t ta = 0, tb = 0, tc = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t t = sh[parity][0][i];
+    ta += t & 0xFFFFu;
+    tb += t >> 16;
+    tc += sh[parity][1][i];
+  }
+  a = ta;
+  b = tb;
+  c = tc;
 }
 
 // Workgroup (4 waves) exclusive prefix and total of a small count, with the
@@ -327,7 +331,7 @@ __device__ __forceinline__ void topk_reg(const uint32_t (&key)[CH], int n_my, in
       n2 += (uint32_t)(key[j] >= c2);
       n3 += (uint32_t)(key[j] >= c3);
     }
-    block_sum3_small<kBits>(n1, n2, n3, sh, parity);
+    block_sum3(n1, n2, n3, sh, parity);
     parity ^= 1;
     if (hi > 0 && n3 >= (uint32_t)k) T = c3;
     else if (hi > 0 && n2 >= (uint32_t)k) T = c2;
