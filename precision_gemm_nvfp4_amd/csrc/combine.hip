@@ -126,13 +126,24 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
                                                            int32_t* __restrict__ list,
                                                            float* __restrict__ out, int64_t ldo,
                                                            bool vec4) {
-  __shared__ int32_t srt[kMaxListLds];
+  __shared__ int32_t srt[kMaxListLds], raw[kMaxListLds];
   const int64_t t = blockIdx.x;
   const int32_t b = start[t], n = start[t + 1] - b;
   if (n == 0) return;
-  // ascending row order: insertion sort by one thread (lists hold top-k rows)
+  // ascending row order.  Lists that fit in LDS: each entry's rank is the
+  // number of smaller entries (the rows are distinct), computed by all
+  // threads at once.  Longer lists: insertion sort in place by one thread.
   int32_t* lst = list + b;
-  if (threadIdx.x == 0) {
+  if (n <= kMaxListLds) {
+    for (int32_t i = threadIdx.x; i < n; i += blockDim.x) raw[i] = lst[i];
+    __syncthreads();
+    for (int32_t i = threadIdx.x; i < n; i += blockDim.x) {
+      const int32_t v = raw[i];
+      int32_t rank = 0;
+      for (int32_t j = 0; j < n; ++j) rank += raw[j] < v;
+      srt[rank] = v;
+    }
+  } else if (threadIdx.x == 0) {
     for (int32_t i = 1; i < n; ++i) {
       const int32_t v = lst[i];
       int32_t j = i - 1;
@@ -142,7 +153,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
       }
       lst[j + 1] = v;
     }
-    for (int32_t i = 0; i < n && i < kMaxListLds; ++i) srt[i] = lst[i];
+    for (int32_t i = 0; i < kMaxListLds; ++i) srt[i] = lst[i];
   }
   __syncthreads();
   float* o = out + t * ldo;
