@@ -153,9 +153,8 @@ hipError_t launch_mx_quantize(const void* x, int dtype, int64_t M, int64_t K, in
 // XCD-aware tile order and the epilogues are the NVFP4 GEMM's
 // (gemm_common.h).  K moves 128 per pipeline stage through a ring of LDS
 // slots (four for tiles of 128 rows or more, else three), filled by direct
-// global-to-LDS loads (global_load_lds_dwordx4:
-// lane l of the instruction writes 16 bytes at base + 16 l, so no registers
-// carry the tiles).  A slot holds the stage's 64 code bytes of every A and W
+// global-to-LDS buffer loads (lane l of an instruction writes 16 bytes at
+// base + 16 l, so no registers carry the tiles).  A slot holds the stage's 64 code bytes of every A and W
 // row, 16-byte chunks swizzled within a row (chunk c of row r at position
 // c ^ ((r >> 1) & 3), so that the fragment reads of 8 consecutive rows hit
 // distinct banks), then the 4 scale bytes of every row.  Each wave issues the
@@ -229,13 +228,18 @@ struct KC {                                 // a compile-time count
 };
 
 
+// Direct global-to-LDS loads through buffer resources: base and size in
+// scalar registers, the stage's advance as the scalar offset, each lane's
+// position a vector offset fixed for the tile, so a load costs no vector
+// arithmetic.  Lane l writes its 16 / 4 bytes at LDS l * 16 / l * 4 past the
+// (uniform) destination.
 typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) void glb_void_t;
-__device__ __forceinline__ void load_lds16(const void* g, unsigned char* l) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 16, 0, 0);
+typedef __amdgpu_buffer_rsrc_t Rsrc;
+__device__ __forceinline__ void load_lds16(Rsrc r, uint32_t voff, int soff, unsigned char* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 16, voff, soff, 0, 0);
 }
-__device__ __forceinline__ void load_lds4(const void* g, unsigned char* l) {
-  __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)l, 4, 0, 0);
+__device__ __forceinline__ void load_lds4(Rsrc r, uint32_t voff, int soff, unsigned char* l) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void_t*)l, 4, voff, soff, 0, 0);
 }
 // s_waitcnt vmcnt(N) lgkmcnt(0) (gfx9 encoding: vmcnt in bits 0-3 and 14-15)
 template <int N>
@@ -324,14 +328,17 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
     const int64_t br = weight_row<BN>(p, n_tile, r);
     return br >= 0 ? br : 0;
   };
-  // Global addresses are a uniform base (kernel argument plus the expert's
-  // and the stage's offsets, kept in SGPRs) plus a 32-bit per-lane offset
-  // (the host checks that each operand spans less than 4 GiB).
+  // Buffer resources of A's and this expert's W codes and scales (the host
+  // checks that each operand spans less than 4 GiB), built once.
   const uint8_t* wc_e = p.w_codes + (int64_t)e * p.N * rbytes;
   const uint8_t* ws_e = p.w_scales + (int64_t)e * p.N * sbytes;
   const int lr = lane >> 2, lp = lane & 3;
   // MXFP8 rows: 8 chunks of 16 bytes a stage, chunk c at position c ^ (r & 7)
   const int64_t arbytes = A8 ? K : rbytes;
+  const Rsrc r_ac = make_rsrc(p.a_codes, p.a_rows * arbytes);
+  const Rsrc r_as = make_rsrc(p.a_scales, p.a_rows * sbytes);
+  const Rsrc r_wc = make_rsrc(wc_e, p.N * rbytes);
+  const Rsrc r_ws = make_rsrc(ws_e, p.N * sbytes);
   uint32_t a_off[NAI];
 #pragma unroll
   for (int i = 0; i < NAI; ++i) {
@@ -364,17 +371,15 @@ __global__ __launch_bounds__(256, 1) void mx_grouped_gemm_kernel(GemmArgs p, int
   // the LPW load instructions of stage m into slot `slot`
   auto issue = [&](int m, int slot) {
     unsigned char* base = smem + slot * STAGE;
-    const uint8_t* ac = p.a_codes + (int64_t)m * L::AROW;
-    const uint8_t* wcm = wc_e + (int64_t)m * 64;
 #pragma unroll
     for (int i = 0; i < NAI; ++i) {
       const int b = wave * NAI + i;
-      load_lds16(ac + a_off[i], b < L::ABLK ? base + L::A_OFF + b * 1024 : DUMMY);
+      load_lds16(r_ac, a_off[i], m * L::AROW, b < L::ABLK ? base + L::A_OFF + b * 1024 : DUMMY);
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) load_lds16(wcm + b_off[i], base + L::B_OFF + (wave * 4 + i) * 1024);
-    load_lds4(p.a_scales + (int64_t)m * 4 + as_off, 64 * wave < BM ? base + L::AS_OFF + wave * 256 : DUMMY);
-    load_lds4(ws_e + (int64_t)m * 4 + bs_off, base + L::BS_OFF + wave * 256);
+    for (int i = 0; i < 4; ++i) load_lds16(r_wc, b_off[i], m * 64, base + L::B_OFF + (wave * 4 + i) * 1024);
+    load_lds4(r_as, as_off, m * 4, 64 * wave < BM ? base + L::AS_OFF + wave * 256 : DUMMY);
+    load_lds4(r_ws, bs_off, m * 4, base + L::BS_OFF + wave * 256);
   };
 
   // xmax: the largest scale byte of weight row tid (read in the prologue).
