@@ -59,17 +59,19 @@ def profiled_traffic(workload, kernel):
 def gemm_kernel_name(rows, experts, epilogue, fmt="nvfp4", k=4096, kc=64):
     """Name of the grouped-GEMM kernel instance the library picks: rows per
     tile from the average rows per expert (>= 160: 256, >= 64: 128,
-    >= 24: 64, else 32), epilogue 1 = SwiGLU, 2 = scatter, and the gather
-    width (8 when the 128-K stages hold more than 3 selected channels on
-    average, else 4)."""
+    >= 24: 64, else 32), the LDS slots, epilogue 1 = SwiGLU, 2 = scatter, and
+    the gather width (8 when the 128-K stages hold more than 3 selected
+    channels on average, else 4)."""
     avg = rows // max(experts, 1)
     cfg = "4, 4, 2, 2" if avg >= 160 else "2, 4, 2, 2" if avg >= 64 else \
           "1, 4, 2, 2" if avg >= 24 else "1, 2, 1, 4"
     if fmt == "mxfp4":     # compensated (the bench always compensates)
         return f"nvfp4::mxg::mx_grouped_gemm_kernel<{cfg}, {epilogue}, true, false>"
-    # <MI, NJ, WM, WN, LDS slots, epilogue, compensation substeps, gather width>
+    # <MI, NJ, WM, WN, LDS slots, epilogue, compensation substeps, gather width>;
+    # the 32-row tile keeps two slots when two workgroups then fit a CU (k <= 64, K <= 4096)
     gw = 8 if kc * 128 > 3 * k else 4
-    return f"nvfp4::nvg::grouped_gemm_kernel<{cfg}, 3, {epilogue}, {4 if kc <= 64 else 8}, {gw}>"
+    slots = 2 if cfg == "1, 2, 1, 4" and kc <= 64 and k <= 4096 else 3
+    return f"nvfp4::nvg::grouped_gemm_kernel<{cfg}, {slots}, {epilogue}, {4 if kc <= 64 else 8}, {gw}>"
 
 
 def gemm_flops(rows, n, k, kc):
