@@ -77,6 +77,7 @@ extern "C" {
 #define NVFP4_EPI_F32              0  /* out fp32 [rows, N] = Y */
 #define NVFP4_EPI_SWIGLU_BF16      1  /* out bf16 [rows, N/2] = silu(Y[:, :N/2]) * Y[:, N/2:] */
 #define NVFP4_EPI_SCATTER_ADD_F32  2  /* out fp32 [out_rows, N]: out[scatter_index[r]] += row_weight[r] * Y[r] */
+#define NVFP4_EPI_SCATTER_F32      3  /* out fp32 [out_rows, N]: out[t] = sum of row_weight[r] * Y[r] over the rows with scatter_index[r] == t */
 
 /* Library version (major*10000 + minor*100 + patch). */
 int nvfp4_version(void);
@@ -235,7 +236,10 @@ int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64
  *                      scatter_index[r] (< out_rows) of fp32 [out_rows, ldo],
  *                      the rows of each output row in increasing r (a fixed
  *                      order: the result is reproducible); the caller
- *                      initializes out.  Needs the workspace
+ *                      initializes out.  SCATTER_F32 writes the same sums
+ *                      started from zero instead (every out row is written,
+ *                      rows that no r names with zeros; out need not be
+ *                      initialized).  Both need the workspace
  *                      (rows_total * N * 4 bytes plus index lists); the
  *                      other epilogues need none.
  * Errors: EINVAL (shapes, K % 64, pointers, epilogue arguments, kc),

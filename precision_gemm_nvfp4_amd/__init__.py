@@ -22,6 +22,7 @@ NVFP4_DTYPE_F32 = 1
 EPI_F32 = 0
 EPI_SWIGLU_BF16 = 1
 EPI_SCATTER_ADD_F32 = 2
+EPI_SCATTER_F32 = 3
 
 _lib = None
 
@@ -247,7 +248,8 @@ def moe_w4a4_grouped_gemm(a_codes, a_scales, a_global, group_offsets, rows_total
 
     w_codes [E, N, K/2].  Returns out: fp32 [rows_total, N] (EPI_F32), bf16
     [rows_total, N/2] (EPI_SWIGLU_BF16), or the given fp32 out
-    [out_rows, N] after the scatter-add (EPI_SCATTER_ADD_F32)."""
+    [out_rows, N] after the scatter-add (EPI_SCATTER_ADD_F32: out += the
+    routed rows; EPI_SCATTER_F32: out = them, allocated when out is None)."""
     lib = load()
     _require_cuda(a_codes, a_scales, a_global, group_offsets, w_codes, w_scales, w_global,
                   a_row_index, sel_idx, r_codes, r_scales, r_global, row_weight, scatter_index,
@@ -260,8 +262,11 @@ def moe_w4a4_grouped_gemm(a_codes, a_scales, a_global, group_offsets, rows_total
             out = torch.empty(rows_total, n, dtype=torch.float32, device=dev)
         elif epilogue == EPI_SWIGLU_BF16:
             out = torch.empty(rows_total, n // 2, dtype=torch.bfloat16, device=dev)
+        elif epilogue == EPI_SCATTER_F32 and out_rows is not None:
+            out = torch.empty(out_rows, n, dtype=torch.float32, device=dev)
         else:
-            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor")
+            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor "
+                             "(EPI_SCATTER_F32 an out tensor or out_rows)")
     if out_rows is None:
         out_rows = out.shape[0]
     kc = 0 if sel_idx is None else sel_idx.shape[1]
@@ -449,8 +454,11 @@ def moe_mxfp4_grouped_gemm(a_codes, a_scales, group_offsets, rows_total, w_codes
             out = torch.empty(rows_total, n, dtype=torch.float32, device=dev)
         elif epilogue == EPI_SWIGLU_BF16:
             out = torch.empty(rows_total, n // 2, dtype=torch.bfloat16, device=dev)
+        elif epilogue == EPI_SCATTER_F32 and out_rows is not None:
+            out = torch.empty(out_rows, n, dtype=torch.float32, device=dev)
         else:
-            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor")
+            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor "
+                             "(EPI_SCATTER_F32 an out tensor or out_rows)")
     if out_rows is None:
         out_rows = out.shape[0]
     kc = 0 if sel_idx is None else sel_idx.shape[1]
@@ -494,8 +502,11 @@ def moe_mxfp4_w4a8_grouped_gemm(a_codes, a_scales, group_offsets, rows_total, w_
             out = torch.empty(rows_total, n, dtype=torch.float32, device=dev)
         elif epilogue == EPI_SWIGLU_BF16:
             out = torch.empty(rows_total, n // 2, dtype=torch.bfloat16, device=dev)
+        elif epilogue == EPI_SCATTER_F32 and out_rows is not None:
+            out = torch.empty(out_rows, n, dtype=torch.float32, device=dev)
         else:
-            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor")
+            raise ValueError("EPI_SCATTER_ADD_F32 needs an initialised out tensor "
+                             "(EPI_SCATTER_F32 an out tensor or out_rows)")
     if out_rows is None:
         out_rows = out.shape[0]
     ws = _workspace(lib.moe_mxfp4_w4a8_grouped_gemm_workspace_size(n_exp, rows_total, n, kk,

@@ -262,9 +262,18 @@ int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64
 }
 
 // ---------------------------------------------------------------------------
+// NVFP4_EPI_SCATTER_F32 is the scatter-add epilogue into zeros: the same GEMM
+// kernels, with the combine writing its sums instead of adding them to out.
+static bool scatter_overwrite(int& epilogue) {
+  if (epilogue != NVFP4_EPI_SCATTER_F32) return false;
+  epilogue = NVFP4_EPI_SCATTER_ADD_F32;
+  return true;
+}
+
 size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K,
                                             int epilogue, int64_t out_rows) {
   (void)E; (void)K;
+  scatter_overwrite(epilogue);
   if (epilogue != NVFP4_EPI_SCATTER_ADD_F32 || rows_total < 0 || N < 0 || out_rows < 0) return 0;
   return nvfp4::combine_workspace_bytes(rows_total, N, out_rows);
 }
@@ -279,6 +288,7 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
                           int64_t out_rows, void* out, int64_t ldo, float* out_amax,
                           void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "moe_w4a4_grouped_gemm";
+  const bool overwrite = scatter_overwrite(epilogue);
   if (E <= 0 || K <= 0 || N <= 0 || rows_total < 0 || a_rows < 0)
     return fail(NVFP4_EINVAL, "%s: E=%d K=%lld N=%lld rows_total=%lld", fn, E, (long long)K,
                 (long long)N, (long long)rows_total);
@@ -328,6 +338,7 @@ int moe_w4a4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const
   a.out_amax = epilogue == NVFP4_EPI_SWIGLU_BF16 ? out_amax : nullptr;
   a.block_m = 0;
   a.y_rows = epilogue == NVFP4_EPI_SCATTER_ADD_F32 ? static_cast<float*>(ws) : nullptr;
+  a.combine_overwrite = overwrite;
   return hip_status(nvfp4::launch_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -456,6 +467,7 @@ int moe_mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                            const int32_t* scatter_index, int64_t out_rows, void* out, int64_t ldo,
                            float* out_amax, void* ws, size_t ws_bytes, void* stream) {
   const char* fn = "moe_mxfp4_grouped_gemm";
+  const bool overwrite = scatter_overwrite(epilogue);
   if (E <= 0 || K <= 0 || N <= 0 || rows_total < 0 || a_rows < 0)
     return fail(NVFP4_EINVAL, "%s: E=%d K=%lld N=%lld rows_total=%lld", fn, E, (long long)K,
                 (long long)N, (long long)rows_total);
@@ -509,6 +521,7 @@ int moe_mxfp4_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
   a.out_amax = epilogue == NVFP4_EPI_SWIGLU_BF16 ? out_amax : nullptr;
   a.block_m = 0;
   a.y_rows = epilogue == NVFP4_EPI_SCATTER_ADD_F32 ? static_cast<float*>(ws) : nullptr;
+  a.combine_overwrite = overwrite;
   return hip_status(nvfp4::launch_mx_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }
 
@@ -541,6 +554,7 @@ int moe_mxfp4_w4a8_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
                                 int64_t ldo, float* out_amax, void* ws, size_t ws_bytes,
                                 void* stream) {
   const char* fn = "moe_mxfp4_w4a8_grouped_gemm";
+  const bool overwrite = scatter_overwrite(epilogue);
   if (E <= 0 || K <= 0 || N <= 0 || rows_total < 0 || a_rows < 0)
     return fail(NVFP4_EINVAL, "%s: E=%d K=%lld N=%lld rows_total=%lld", fn, E, (long long)K,
                 (long long)N, (long long)rows_total);
@@ -584,6 +598,7 @@ int moe_mxfp4_w4a8_grouped_gemm(const uint8_t* a_codes, const uint8_t* a_scales,
   a.out_amax = epilogue == NVFP4_EPI_SWIGLU_BF16 ? out_amax : nullptr;
   a.block_m = 0;
   a.y_rows = epilogue == NVFP4_EPI_SCATTER_ADD_F32 ? static_cast<float*>(ws) : nullptr;
+  a.combine_overwrite = overwrite;
   return hip_status(nvfp4::launch_mx_w4a8_grouped_gemm(a, static_cast<hipStream_t>(stream)), fn);
 }
 

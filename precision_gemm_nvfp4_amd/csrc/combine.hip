@@ -1,5 +1,6 @@
 // Scatter-add combine of the routed expert outputs:
 //   out[t, :] += sum over rows r with scatter_index[r] == t of y_rows[r, :]
+// (or, overwriting, out[t, :] = that sum, every output row written)
 // where y_rows already holds row_weight[r] * Y[r] (written by the grouped GEMM
 // into the workspace).  The rows of each output row are added in increasing
 // row order, so the result does not depend on scheduling (fp32 atomics would).
@@ -19,10 +20,13 @@ namespace nvfp4 {
 constexpr int kMaxListLds = 1024;           // rows per output row sorted in LDS
 constexpr int kPlanSmallOut = 4096;         // output rows of the one-workgroup plan
 
-__global__ void combine_zero_kernel(int32_t* p, int64_t n) {
+// zeroes p[0..n) and q[0..n)
+__global__ void combine_zero_kernel(int32_t* p, int32_t* q, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-       i += (int64_t)gridDim.x * blockDim.x)
+       i += (int64_t)gridDim.x * blockDim.x) {
     p[i] = 0;
+    q[i] = 0;
+  }
 }
 
 __global__ void combine_count_kernel(const int32_t* __restrict__ scatter_index, int64_t rows,
@@ -125,11 +129,15 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
                                                            int64_t N, const int32_t* __restrict__ start,
                                                            int32_t* __restrict__ list,
                                                            float* __restrict__ out, int64_t ldo,
-                                                           bool vec4) {
+                                                           bool vec4, bool overwrite) {
   __shared__ int32_t srt[kMaxListLds], raw[kMaxListLds];
   const int64_t t = blockIdx.x;
   const int32_t b = start[t], n = start[t + 1] - b;
-  if (n == 0) return;
+  if (n == 0) {
+    if (overwrite)
+      for (int64_t c = threadIdx.x; c < N; c += blockDim.x) out[t * ldo + c] = 0.0f;
+    return;
+  }
   // ascending row order.  Lists that fit in LDS: each entry's rank is the
   // number of smaller entries (the rows are distinct), computed by all
   // threads at once.  Longer lists: insertion sort in place by one thread.
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
   float* o = out + t * ldo;
   for (int64_t c = (int64_t)threadIdx.x * 4; c < N; c += (int64_t)blockDim.x * 4) {
     if (vec4 && c + 4 <= N) {
-      f32x4 acc = *reinterpret_cast<const f32x4*>(o + c);
+      f32x4 acc = overwrite ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const f32x4*>(o + c);
       // rows in groups of 8: the group's loads go out before its additions
       for (int32_t i0 = 0; i0 < n; i0 += 8) {
         f32x4 v[8];
@@ -182,7 +190,7 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
       *reinterpret_cast<f32x4*>(o + c) = acc;
     } else {
       for (int64_t cc = c; cc < c + 4 && cc < N; ++cc) {
-        float acc = o[cc];
+        float acc = overwrite ? 0.0f : o[cc];
         for (int32_t i = 0; i < n; ++i) {
           const int32_t r = i < kMaxListLds ? srt[i] : lst[i];
           acc = acc + y_rows[(int64_t)r * N + cc];
@@ -200,7 +208,7 @@ size_t combine_workspace_bytes(int64_t rows, int64_t N, int64_t out_rows) {
 
 hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
                           const int32_t* scatter_index, int64_t out_rows, float* out, int64_t ldo,
-                          void* ws, hipStream_t stream) {
+                          bool overwrite, void* ws, hipStream_t stream) {
   auto a256 = [](size_t n) { return (n + 255) & ~size_t(255); };
   char* w = static_cast<char*>(ws) + a256((size_t)rows * N * 4);
   int32_t* count = reinterpret_cast<int32_t*>(w);
@@ -215,12 +223,12 @@ hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
     if (out_rows > 0)
       combine_rows_kernel<<<(unsigned)out_rows, 256, 0, stream>>>(
           y_rows, N, start, list, out, ldo,
-          N % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0);
+          N % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0, overwrite);
     return hipGetLastError();
   }
   const int64_t zb = (out_rows + 255) / 256;
-  combine_zero_kernel<<<(unsigned)(zb > 1024 ? 1024 : (zb < 1 ? 1 : zb)), 256, 0, stream>>>(count, out_rows + 1);
-  combine_zero_kernel<<<(unsigned)(zb > 1024 ? 1024 : (zb < 1 ? 1 : zb)), 256, 0, stream>>>(cursor, out_rows + 1);
+  combine_zero_kernel<<<(unsigned)(zb > 1024 ? 1024 : (zb < 1 ? 1 : zb)), 256, 0, stream>>>(count, cursor,
+                                                                                          out_rows + 1);
   const int64_t rb = (rows + 255) / 256;
   const unsigned rg = (unsigned)(rb > 2048 ? 2048 : (rb < 1 ? 1 : rb));
   combine_count_kernel<<<rg, 256, 0, stream>>>(scatter_index, rows, out_rows, count);
@@ -229,7 +237,7 @@ hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
   if (out_rows > 0)
     combine_rows_kernel<<<(unsigned)out_rows, 256, 0, stream>>>(
         y_rows, N, start, list, out, ldo,
-        N % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0);
+        N % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0, overwrite);
   return hipGetLastError();
 }
 

@@ -868,7 +868,11 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
     hipError_t err = launch_fill_f32(a.out_amax, 1, 0.0f, stream);
     if (err != hipSuccess) return err;
   }
-  if (a.rows_total == 0) return hipSuccess;
+  if (a.rows_total == 0)     // nothing to add; an overwriting scatter still writes zeros
+    return a.epilogue == 2 && a.combine_overwrite
+               ? launch_combine(a.y_rows, 0, a.N, a.scatter_index, a.out_rows, static_cast<float*>(a.out),
+                                a.ldo, true, a.y_rows, stream)
+               : hipSuccess;
   hipError_t err;
   int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
   // a compensation wider than 64 channels (a larger W_S) needs a shorter tile
@@ -885,7 +889,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
     if (err == hipSuccess) err = nvg::launch_32(rest, stream);
     if (err != hipSuccess || a.epilogue != 2) return err;
     return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
-                          static_cast<float*>(a.out), a.ldo, a.y_rows, stream);
+                          static_cast<float*>(a.out), a.ldo, a.combine_overwrite, a.y_rows, stream);
   }
   switch (bm) {
     case 256: err = nvg::launch_comp<4, 4, 2, 2, 3>(a, stream); break;
@@ -895,7 +899,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   }
   if (err != hipSuccess || a.epilogue != 2) return err;
   return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
-                        static_cast<float*>(a.out), a.ldo, a.y_rows, stream);
+                        static_cast<float*>(a.out), a.ldo, a.combine_overwrite, a.y_rows, stream);
 }
 
 }  // namespace nvfp4

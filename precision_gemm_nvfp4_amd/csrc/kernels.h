@@ -62,6 +62,7 @@ struct GemmArgs {
   int64_t ldo;
   float* out_amax;
   float* y_rows;         // scatter epilogue: row_weight * Y rows [rows_total, N] (workspace)
+  bool combine_overwrite = false;   // scatter epilogue: out = the sums (else out += the sums)
   int block_m;           // rows per tile: 256, 128, 64, 32, or 0 to pick from the average group size
   int rw_lds_offset;     // set by the launcher: LDS byte offset of the scatter epilogue's row weights
   int a_global_per_group = 0;  // a_global holds one scale per group (else one for all)
@@ -91,7 +92,7 @@ hipError_t launch_mx8_quantize(const void* x, int dtype, int64_t M, int64_t K, i
 size_t combine_workspace_bytes(int64_t rows, int64_t N, int64_t out_rows);
 hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
                           const int32_t* scatter_index, int64_t out_rows, float* out, int64_t ldo,
-                          void* ws, hipStream_t stream);
+                          bool overwrite, void* ws, hipStream_t stream);
 
 // trainer.hip
 size_t qdq_workspace_bytes(int64_t nmat);

@@ -766,7 +766,11 @@ static hipError_t launch_any(const GemmArgs& a, hipStream_t stream) {
     hipError_t err = launch_fill_f32(a.out_amax, 1, 0.0f, stream);
     if (err != hipSuccess) return err;
   }
-  if (a.rows_total == 0) return hipSuccess;
+  if (a.rows_total == 0)     // nothing to add; an overwriting scatter still writes zeros
+    return a.epilogue == 2 && a.combine_overwrite
+               ? launch_combine(a.y_rows, 0, a.N, a.scatter_index, a.out_rows, static_cast<float*>(a.out),
+                                a.ldo, true, a.y_rows, stream)
+               : hipSuccess;
   hipError_t err;
   int bm = a.block_m > 0 ? a.block_m : grouped_gemm_block_m(a.rows_total, a.E);
   // a long K (a long gather table) can push the tallest tile past the LDS
@@ -780,7 +784,7 @@ static hipError_t launch_any(const GemmArgs& a, hipStream_t stream) {
   }
   if (err != hipSuccess || a.epilogue != 2) return err;
   return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
-                        static_cast<float*>(a.out), a.ldo, a.y_rows, stream);
+                        static_cast<float*>(a.out), a.ldo, a.combine_overwrite, a.y_rows, stream);
 }
 
 }  // namespace mxg

@@ -159,11 +159,12 @@ __device__ __forceinline__ float load1(const T* p) {
   }
 }
 
-// One workgroup per (128-row tile of a unit, 64 channels).  Thread t computes
-// |R| of block column t % 4 for rows t / 4 and t / 4 + 64 (loads first, then
-// arithmetic) into LDS; then threads 0..63 add one channel each over the
-// tile's rows in increasing row order (missing rows add +0, which changes no
-// fp32 sum).
+// Contiguous rows (no row index): one workgroup per (128-row tile of a unit,
+// 64 channels).  Thread t computes |R| of block column t % 4 for rows t / 4
+// and t / 4 + 64 (loads first, then arithmetic) into LDS; then threads 0..63
+// add one channel each over the tile's rows in increasing row order (missing
+// rows add +0, which changes no fp32 sum).  The whole tile's loads go out at
+// once, which suits rows streamed from HBM once.
 constexpr int kScoreCols = 64;
 constexpr int kScoreBlocks = kScoreCols / kBlock;
 constexpr int kAbsStride = kScoreCols + 4;
@@ -171,7 +172,7 @@ constexpr int kAbsStride = kScoreCols + 4;
 // MX: the operand is MXFP4 (E8M0 scale per 32-block, no global scale; gp
 // unused), else NVFP4 (E4M3 per 16-block times *gp).
 template <typename T, bool MX>
-__global__ __launch_bounds__(256) void resq_scores_kernel(
+__global__ __launch_bounds__(256) void resq_scores_tile_kernel(
     const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
     const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
     const uint8_t* __restrict__ scales, const float* __restrict__ gp,
@@ -228,6 +229,85 @@ __global__ __launch_bounds__(256) void resq_scores_kernel(
     for (int rl = 0; rl < kScoreTileRows; ++rl) sum = sum + absr[rl * kAbsStride + tid];
     partials[slot * K + c] = sum;
   }
+}
+
+// Gathered rows (a row index, each row read by every unit that it is routed
+// to, mostly from cache): one wave per (128-row tile of a unit, 512
+// channels), four tiles per workgroup.  Lane l owns channels c0 + 8l .. c0 + 8l + 7 and adds |R| of
+// the tile's rows into its eight sums in increasing row order (rows past the
+// unit's end, or whose index lies outside x, add nothing, which changes no
+// fp32 sum); the rows go eight at a time, their loads (16 or 32 bytes of x,
+// one code word and one scale byte per lane) issued before their additions.
+// No LDS and no barrier: every lane of every wave works through the sum.  On
+// the 8192-token layer's X (65536 gathered rows of 4096 channels) this took
+// 0.09 ms where the tile kernel above took 0.16; on contiguous rows the tile
+// kernel is the faster one.
+constexpr int kScoreLaneCols = 8;
+constexpr int kScoreWaveCols = 64 * kScoreLaneCols;
+constexpr int kScoreBatch = 8;
+// MX: as in the tile kernel above.
+template <typename T, bool MX>
+__global__ __launch_bounds__(256) void resq_scores_rows_kernel(
+    const T* __restrict__ x, int64_t x_rows, int64_t K, int64_t ldx,
+    const int32_t* __restrict__ row_index, const uint8_t* __restrict__ codes,
+    const uint8_t* __restrict__ scales, const float* __restrict__ gp,
+    const int4* __restrict__ tile_info, int64_t slots, float* __restrict__ partials) {
+  constexpr int XW = sizeof(T) / 2;                      // 16-byte words of x per lane and row
+  const int lane = threadIdx.x & 63;
+  const int64_t slot = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  if (slot >= slots) return;
+  const int4 ti = tile_info[slot];
+  if (ti.x < 0) return;
+  const int64_t c = (int64_t)blockIdx.x * kScoreWaveCols + lane * kScoreLaneCols;
+  if (c >= K) return;                                    // K % 16 == 0: all eight channels exist
+  const float g = MX ? 1.0f : *gp;
+  const int64_t nsb = MX ? K / kMxBlock : K / kBlock;    // scale bytes per row
+  const int64_t sc = MX ? c / kMxBlock : c / kBlock;
+  const int64_t r0 = ti.y;
+  const int nr = (int)(ti.z - r0 < kScoreTileRows ? ti.z - r0 : kScoreTileRows);
+  float acc[kScoreLaneCols];
+#pragma unroll
+  for (int i = 0; i < kScoreLaneCols; ++i) acc[i] = 0.0f;
+  for (int i0 = 0; i0 < nr; i0 += kScoreBatch) {
+    u32x4 xv[kScoreBatch][XW];
+    uint32_t cw[kScoreBatch], sb[kScoreBatch];
+    bool live[kScoreBatch];
+#pragma unroll
+    for (int q = 0; q < kScoreBatch; ++q) {              // all loads first
+      const int64_t r = r0 + i0 + q;
+      const int64_t xr = i0 + q < nr ? (row_index ? (int64_t)row_index[r] : r) : -1;
+      live[q] = xr >= 0 && xr < x_rows;
+      if (live[q]) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(x + xr * ldx + c);
+#pragma unroll
+        for (int w = 0; w < XW; ++w) xv[q][w] = src[w];
+        cw[q] = *reinterpret_cast<const uint32_t*>(codes + xr * (K / 2) + c / 2);
+        sb[q] = scales[xr * nsb + sc];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < kScoreBatch; ++q) {              // then the sums, in row order
+      if (!live[q]) continue;
+      const float S = MX ? e8m0_value(sb[q]) : e4m3_value(sb[q]) * g;
+      float f[8], v[8];
+      e2m1_unpack8(cw[q], f);
+      if constexpr (XW == 1) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          v[2 * i] = bf16_lo(xv[q][0][i]);
+          v[2 * i + 1] = bf16_hi(xv[q][0][i]);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(xv[q][i >> 2][i & 3]);
+      }
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[i] = acc[i] + fabsf(v[i] - f[i] * S);   // exact; no contraction
+    }
+  }
+  f32x4* dst = reinterpret_cast<f32x4*>(partials + slot * K + c);
+  dst[0] = f32x4{acc[0], acc[1], acc[2], acc[3]};
+  dst[1] = f32x4{acc[4], acc[5], acc[6], acc[7]};
 }
 
 // ---------------------------------------------------------------------------
@@ -941,9 +1021,15 @@ static hipError_t launch_resq_t(const T* x, int64_t x_rows, int64_t K, int64_t l
                                            slot_info, gslots);
   const float* partials = tile_partials;
   if (!tile_partials) {
-    dim3 grid((unsigned)((K + kScoreCols - 1) / kScoreCols), (unsigned)slots);
-    resq_scores_kernel<T, MX><<<grid, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales, g,
-                                                    tile_info, ws.partials);
+    if (row_index) {
+      dim3 grid((unsigned)((K + kScoreWaveCols - 1) / kScoreWaveCols), (unsigned)((slots + 3) / 4));
+      resq_scores_rows_kernel<T, MX><<<grid, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales,
+                                                               g, tile_info, slots, ws.partials);
+    } else {
+      dim3 grid((unsigned)((K + kScoreCols - 1) / kScoreCols), (unsigned)slots);
+      resq_scores_tile_kernel<T, MX><<<grid, 256, 0, stream>>>(x, x_rows, K, ldx, row_index, codes, scales,
+                                                               g, tile_info, ws.partials);
+    }
     partials = ws.partials;
   }
   if (K <= 256 * 4) {

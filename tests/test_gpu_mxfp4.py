@@ -522,6 +522,32 @@ def test_w4a8_down_scatter(gpu_lib):
     assert rel_err(np32(y), y_ref) <= GEMM_TOL
 
 
+
+def test_w4a8_down_scatter_overwrite(gpu_lib):
+    """EPI_SCATTER_F32 on the MXFP4 path: the add-into-zeros sums bit for bit
+    over an out full of NaN, and zeros from a launch with no rows."""
+    P = gpu_lib
+    tokens, hidden, n_exp, inter = 160, 256, 8, 256
+    _, rt, offs, _, wd = _route_setup(tokens, hidden, n_exp, inter, 24, 1.0, 4)
+    rows = int(offs[-1])
+    hrows = torch.from_numpy(np.random.default_rng(5).standard_normal((rows, inter)).astype(np.float32))
+    hc, hs = P.mxfp8_quantize(hrows.to(torch.bfloat16).cuda())
+    dc, ds = _mx_weights(P, wd)
+    kw = dict(row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
+              scatter_index=torch.from_numpy(rt["slot_token"]).cuda())
+    offs_t = torch.from_numpy(offs).cuda()
+    y_add = torch.zeros(tokens, hidden, dtype=torch.float32, device="cuda")
+    P.moe_mxfp4_w4a8_grouped_gemm(hc, hs, offs_t, rows, dc, ds, epilogue=P.EPI_SCATTER_ADD_F32,
+                                  out=y_add, **kw)
+    y_ow = torch.full((tokens, hidden), float("nan"), dtype=torch.float32, device="cuda")
+    P.moe_mxfp4_w4a8_grouped_gemm(hc, hs, offs_t, rows, dc, ds, epilogue=P.EPI_SCATTER_F32,
+                                  out=y_ow, **kw)
+    assert np.array_equal(np32(y_add).view(np.uint32), np32(y_ow).view(np.uint32))
+    y_none = torch.full((tokens, hidden), float("nan"), dtype=torch.float32, device="cuda")
+    P.moe_mxfp4_w4a8_grouped_gemm(hc, hs, torch.zeros(n_exp + 1, dtype=torch.int64, device="cuda"), 0,
+                                  dc, ds, epilogue=P.EPI_SCATTER_F32, out=y_none, **kw)
+    assert np.all(np32(y_none) == 0.0)
+
 # ---------------------------------------------------------------------------
 # trainer side: MXFP4 weight QDQ and guided rounding
 # ---------------------------------------------------------------------------

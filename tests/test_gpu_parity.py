@@ -654,3 +654,40 @@ def test_scatter_add_fixed_order_and_ragged_n(gpu_lib):
     # magnitude here) do not loosen the tolerance on it; subtracting y0 in
     # float64 from the fp32 output adds at most half an fp32 ulp of |y|
     assert rel_err(outs[0].astype(np.float64) - y0.numpy().astype(np.float64), y_gemm) <= GEMM_TOL
+
+
+@pytest.mark.gpu
+def test_scatter_overwrite_equals_add_into_zeros(gpu_lib):
+    """EPI_SCATTER_F32 writes the same sums as EPI_SCATTER_ADD_F32 into a
+    zeroed out, bit for bit; output rows that no slot names (here the five
+    past the tokens) and an out full of NaN before the call end as zeros; a
+    launch with no rows writes zeros everywhere."""
+    P = gpu_lib
+    tokens, hidden, n_exp, inter = 96, 100, 5, 64
+    rng = np.random.default_rng(4)
+    h = torch.from_numpy(rng.standard_normal((tokens * 3, inter)).astype(np.float32)).to(torch.bfloat16)
+    rt = synth.route(tokens, n_exp, seed=14, top_k=3)
+    offs = torch.from_numpy(rt["offsets"]).cuda()
+    rows = int(rt["offsets"][-1])
+    wd = synth.weights(n_exp, hidden, inter, seed=14, tensor_id=synth.WD_ID)
+    hc, hs, hg, _ = P.nvfp4_quantize(h.cuda())
+    dc, ds, dg = _quant_weights(P, wd)
+    kw = dict(row_weight=torch.from_numpy(rt["slot_weight"]).cuda(),
+              scatter_index=torch.from_numpy(rt["slot_token"]).cuda())
+    out_rows = tokens + 5
+    y_add = torch.zeros(out_rows, hidden, dtype=torch.float32, device="cuda")
+    P.moe_w4a4_grouped_gemm(hc, hs, hg, offs, rows, dc, ds, dg, epilogue=P.EPI_SCATTER_ADD_F32,
+                            out=y_add, **kw)
+    y_ow = torch.full((out_rows, hidden), float("nan"), dtype=torch.float32, device="cuda")
+    P.moe_w4a4_grouped_gemm(hc, hs, hg, offs, rows, dc, ds, dg, epilogue=P.EPI_SCATTER_F32,
+                            out=y_ow, **kw)
+    a, b = np32(y_add), np32(y_ow)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    assert np.all(b[tokens:] == 0.0) and np.all(np.abs(b[:tokens]).sum(axis=1) > 0)
+    y_alloc = P.moe_w4a4_grouped_gemm(hc, hs, hg, offs, rows, dc, ds, dg, epilogue=P.EPI_SCATTER_F32,
+                                      out_rows=out_rows, **kw)
+    assert np.array_equal(np32(y_alloc).view(np.uint32), a.view(np.uint32))
+    y_none = torch.full((out_rows, hidden), float("nan"), dtype=torch.float32, device="cuda")
+    P.moe_w4a4_grouped_gemm(hc, hs, hg, torch.zeros(n_exp + 1, dtype=torch.int64, device="cuda"), 0,
+                            dc, ds, dg, epilogue=P.EPI_SCATTER_F32, out=y_none, **kw)
+    assert np.all(np32(y_none) == 0.0)
