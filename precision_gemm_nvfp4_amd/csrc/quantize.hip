@@ -54,25 +54,43 @@ struct Row16<float> {
 // ---------------------------------------------------------------------------
 // pass 1: per-workgroup amax
 // ---------------------------------------------------------------------------
+// Workgroup b takes rows b, b + G, b + 2G, ... four at a time: the four rows'
+// chunks at a thread's position are loaded before their maxima are taken, so
+// each thread keeps four loads in flight.
+template <typename T>
+__device__ __forceinline__ float absmax_chunk(const u32x4& w, float m) {
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(__uint_as_float(w[i])));
+  }
+  return m;
+}
 template <typename T>
 __global__ __launch_bounds__(256) void amax_partials_kernel(const T* __restrict__ x, int64_t M,
                                                             int64_t K, int64_t ldx,
                                                             float* __restrict__ partials) {
   constexpr int kPer = 16 / sizeof(T);                       // elements per 16-byte chunk
   const int64_t chunks = K / kPer;
+  const int64_t G = gridDim.x;
   float m = 0.0f;
-  for (int64_t r = blockIdx.x; r < M; r += gridDim.x) {
+  int64_t r = blockIdx.x;
+  for (; r + 3 * G < M; r += 4 * G) {
     const T* row = x + r * ldx;
     for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
-      u32x4 w = *reinterpret_cast<const u32x4*>(row + c * kPer);
-      if constexpr (sizeof(T) == 2) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fmaxf(fabsf(bf16_lo(w[i])), fabsf(bf16_hi(w[i]))));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m = fmaxf(m, fabsf(__uint_as_float(w[i])));
-      }
+      const u32x4 w0 = *reinterpret_cast<const u32x4*>(row + c * kPer);
+      const u32x4 w1 = *reinterpret_cast<const u32x4*>(row + G * ldx + c * kPer);
+      const u32x4 w2 = *reinterpret_cast<const u32x4*>(row + 2 * G * ldx + c * kPer);
+      const u32x4 w3 = *reinterpret_cast<const u32x4*>(row + 3 * G * ldx + c * kPer);
+      m = absmax_chunk<T>(w3, absmax_chunk<T>(w2, absmax_chunk<T>(w1, absmax_chunk<T>(w0, m))));
     }
+  }
+  for (; r < M; r += G) {
+    const T* row = x + r * ldx;
+    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x)
+      m = absmax_chunk<T>(*reinterpret_cast<const u32x4*>(row + c * kPer), m);
   }
   m = wave_max(m);
   __shared__ float red[4];
