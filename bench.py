@@ -346,6 +346,32 @@ def cpu_baseline(wl, inp, budget_s):
                 one_thread=one)
 
 
+def timed_steps(torch, step, steps):
+    """(ms per step, {part: ms}): `steps` steps timed with no events between
+    their parts, then as many again (at least 3, at most 10) with an event at
+    each part boundary for the per-part times."""
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record()
+    for _ in range(steps):
+        step(NoMarks())
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / steps
+    n = max(3, min(steps, 10))
+    tls = []
+    for _ in range(n):
+        tl = Timeline(torch)
+        step(tl)
+        tls.append(tl)
+    torch.cuda.synchronize()
+    parts = {}
+    for tl in tls:
+        for k, v in tl.durations().items():
+            parts[k] = parts.get(k, 0.0) + v / n
+    return ms, parts
+
+
 def time_call(torch, fn, n=10, warm=2):
     """Mean ms of fn() over n calls, HIP events on the current stream."""
     for _ in range(warm):
@@ -418,20 +444,13 @@ def moe_summary(torch, P, synth, wl, dev, steps=5):
     for _ in range(2):
         run_step(P, inp, wl, Timeline(torch), trainer=False)
     torch.cuda.synchronize()
-    tls = []
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s.record()
-    for _ in range(steps):
-        tl = Timeline(torch)
-        out = run_step(P, inp, wl, tl, trainer=False)
-        tls.append(tl)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / steps
-    parts = {}
-    for tl in tls:
-        for k, v in tl.durations().items():
-            parts[k] = parts.get(k, 0.0) + v / steps
+    res_out = {}
+
+    def step(tl):
+        res_out["out"] = run_step(P, inp, wl, tl, trainer=False)
+
+    ms, parts = timed_steps(torch, step, steps)
+    out = res_out["out"]
     work = part_work(wl, inp["rows"])
     gflop = work["gemm_gate_up"]["flops"] + work["gemm_down"]["flops"]
     T, H, I, E = wl.tokens, wl.hidden, wl.inter, wl.experts
@@ -520,25 +539,12 @@ def quant_select_bench(args, torch, P, synth, wl, dev):
     for _ in range(args.warmup):
         step(Timeline(torch))
     torch.cuda.synchronize()
-    tls = []
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        tl = Timeline(torch)
-        step(tl)
-        tls.append(tl)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, parts_ms = timed_steps(torch, step, args.steps)
     T, K, k = wl.tokens, wl.hidden, wl.k
     tiles = (T + 127) // 128
     nv = lambda n: n * (0.5 + 1 / 16)
     b_quant = T * K * 2 + nv(T * K)
     b_resq = tiles * k * 4 + nv(T * k) + tiles * 4
-    parts_ms = {}
-    for tl in tls:
-        for name, v in tl.durations().items():
-            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
     parts = {n: dict(ms=round(v, 4)) for n, v in parts_ms.items()}
     parts["quantize"]["gbs"] = round(b_quant / (parts_ms["quantize"] * 1e-3) / 1e9, 1)
     total_bytes = b_quant + b_resq
@@ -591,23 +597,10 @@ def guidance_bench(args, torch, P, synth, wl, dev):
     for _ in range(args.warmup):
         step(Timeline(torch))
     torch.cuda.synchronize()
-    tls = []
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        tl = Timeline(torch)
-        step(tl)
-        tls.append(tl)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, parts_ms = timed_steps(torch, step, args.steps)
     n = wl.tokens * wl.hidden
     b_pack = n * (0.5 + 0.125)                              # codes in, record out
     b_guided = n * (2 + 0.125 + 1 / 16 + 0.5 + 2)           # x, record, scales in; codes, x_fq out
-    parts_ms = {}
-    for tl in tls:
-        for name, v in tl.durations().items():
-            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
     parts = {nm: dict(ms=round(v, 4)) for nm, v in parts_ms.items()}
     for nm, b in (("pack", b_pack), ("guided_record", b_guided)):
         gbs = b / (parts_ms[nm] * 1e-3) / 1e9
@@ -689,20 +682,7 @@ def mask_bench(args, torch, P, synth, wl, dev):
     for _ in range(args.warmup):
         step(Timeline(torch))
     torch.cuda.synchronize()
-    tls = []
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        tl = Timeline(torch)
-        step(tl)
-        tls.append(tl)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
-    parts_ms = {}
-    for tl in tls:
-        for name, v in tl.durations().items():
-            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
+    ms, parts_ms = timed_steps(torch, step, args.steps)
     f_gu, f_d = 2.0 * rows * 2 * I * H, 2.0 * rows * H * I
     parts = {nm: dict(ms=round(v, 4)) for nm, v in parts_ms.items()}
     for nm, f in (("gemm_gate_up", f_gu), ("mask_gemm_gate_up", f_gu), ("gemm_down", f_d),
@@ -787,23 +767,10 @@ def kv_bench(args, torch, P, synth, wl, dev):
     for _ in range(args.warmup):
         step(Timeline(torch))
     torch.cuda.synchronize()
-    tls = []
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        tl = Timeline(torch)
-        step(tl)
-        tls.append(tl)
-    end.record()
-    torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    ms, parts_ms = timed_steps(torch, step, args.steps)
     n = 2 * T * H * D                                      # key and value elements
     b = {"quantize_kv": n * (2 + 0.5625), "record_pack": n * (0.5 + 0.125),
          "guided_kv": n * (2 + 0.125 + 1 / 16 + 0.5 + 2)}
-    parts_ms = {}
-    for tl in tls:
-        for name, v in tl.durations().items():
-            parts_ms[name] = parts_ms.get(name, 0.0) + v / args.steps
     parts = {nm: dict(ms=round(v, 4)) for nm, v in parts_ms.items()}
     for nm, nb in b.items():
         gbs = nb / (parts_ms[nm] * 1e-3) / 1e9
