@@ -33,13 +33,15 @@ FP16_PEAK_TFLOPS = 2500.0        # dense fp16 / bf16 MFMA, MI355X
 FP4_PEAK_TFLOPS = 10100.0
 
 
-def profiled_traffic(workload, kernel):
+def profiled_traffic(workload, kernel, summary=None):
     """HBM bytes per launch of `kernel` on `workload` from the committed
-    rocprofv3 summary (profiles/), or None when there is none or the kernel's
-    sources have changed since the counters were taken (hash of its files)."""
+    rocprofv3 summary (profiles/<summary>.md, by default the grouped-GEMM one
+    of the workload), or None when there is none or the kernel's sources have
+    changed since the counters were taken (hash of its files)."""
     import hashlib
     import re
-    path = os.path.join(ROOT, "profiles", f"grouped_gemm_{workload.replace('_trainer', '')}.md")
+    name = summary or f"grouped_gemm_{workload.replace('_trainer', '')}"
+    path = os.path.join(ROOT, "profiles", f"{name}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -54,6 +56,10 @@ def profiled_traffic(workload, kernel):
     if h.hexdigest()[:16] != fields["source_sha256_16"].strip():
         return None
     return float(fields["traffic_bytes_per_launch"])
+
+
+def traffic_int(t):
+    return None if t is None else int(t)
 
 
 def gemm_kernel_name(rows, experts, epilogue, fmt="nvfp4", k=4096, kc=64):
@@ -629,7 +635,8 @@ def guidance_bench(args, torch, P, synth, wl, dev):
                 "record_bits_per_value": 1.5, "parallelism": "single GPU"},
         algorithmic_bytes=int(b_pack + b_guided), parts=parts,
         roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic_int(profiled_traffic(
+                          wl.name, "guided_kernel", "guidance_record_T8192_K4096")),
                       kernel="guided_kernel<bf16, record>"),
         frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
 
@@ -800,7 +807,8 @@ def kv_bench(args, torch, P, synth, wl, dev):
                 "caches": "key and value", "parallelism": "single GPU"},
         algorithmic_bytes=int(total), parts=parts,
         roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=traffic_int(profiled_traffic(
+                          wl.name, "guided_kernel", "kv_T65536_H4_D128")),
                       kernel="guided_kernel<bf16, record>"),
         frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
 
