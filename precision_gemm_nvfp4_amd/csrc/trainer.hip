@@ -542,6 +542,21 @@ __device__ __forceinline__ int signed_index(uint32_t c) {
 // MX = true: MXFP4 rollout scales, one E8M0 byte per 32 elements (16-element
 // chunk b of a row takes byte b / 2, K being a multiple of 32), S = 2^X and no
 // global scale (roll_global unused).
+// Nibble-parallel helpers: eight 4-bit fields of a word at once.
+// Bit 3 of each nibble set where the nibble's low three bits are zero (bit 3
+// of the nibble must be clear: t + 7 <= 14 carries into bit 3 only).
+__device__ __forceinline__ uint32_t nibble_zero3(uint32_t t) { return ~(t + 0x77777777u) & 0x88888888u; }
+// Bit 3 of each nibble set where the whole nibble is zero.
+__device__ __forceinline__ uint32_t nibble_zero4(uint32_t t) {
+  return ~(t | ((t & 0x77777777u) + 0x77777777u)) & 0x88888888u;
+}
+// Bit j of b (j < 8) to bit 0 of nibble j.
+__device__ __forceinline__ uint32_t nibble_spread8(uint32_t b) {
+  b = (b | (b << 12)) & 0x000F000Fu;
+  b = (b | (b << 6)) & 0x03030303u;
+  return (b | (b << 3)) & 0x11111111u;
+}
+
 template <typename T, bool RECORD, bool MX = false>
 __global__ __launch_bounds__(256) void guided_kernel(
     const T* __restrict__ x, uint32_t M, uint32_t K, int64_t ldx, const uint8_t* __restrict__ roll,
@@ -608,53 +623,60 @@ __global__ __launch_bounds__(256) void guided_kernel(
     // takes x's sign).  The full-code rule picks the candidate on the rollout
     // level's side in signed index order, which for two adjacent levels is
     // the one closer to it; the record rule picks the one whose index has the
-    // recorded low bit.
-    float Lm[16];
-    e2m1_unpack8(w0 & 0x77777777u, Lm);
-    e2m1_unpack8(w1 & 0x77777777u, Lm + 8);
+    // recorded low bit.  Only the sign of each element's difference is taken
+    // per element (bit 3 of its nibble in LT or GT); the choice itself runs
+    // on the eight nibbles of a code word at once (nibble_*: no carry or
+    // borrow crosses a nibble, as each comment shows).
     const bool live = S != 0.0f;                  // S == 0: every code stays at magnitude 0
-    uint32_t g0 = 0, g1 = 0;
-    uint32_t e0 = 0, e1 = 0;                      // full-code rule: index distance 0, 1 masks
-    uint32_t fq[8];
+    uint32_t g[2];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t c = ((j < 8 ? w0 : w1) >> (4 * (j & 7))) & 15u;
-      const uint32_t i = c & 7u, sgn = c & 8u;
-      const float d = __builtin_fmaf(Lm[j], S, -fabsf(v[j]));     // exact sign
-      const uint32_t other = d < 0.0f ? (i < 7u ? i + 1u : 7u) : (d > 0.0f ? i - 1u : i);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t w = h ? w1 : w0;
+      float Lm[8];
+      e2m1_unpack8(w & 0x77777777u, Lm);
+      uint32_t LT = 0, GT = 0;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float d = __builtin_fmaf(Lm[j], S, -fabsf(v[8 * h + j]));   // exact sign
+        LT |= d < 0.0f ? 8u << (4 * j) : 0u;
+        GT |= d > 0.0f ? 8u << (4 * j) : 0u;
+      }
+      const uint32_t I = w & 0x77777777u, SGN = w & 0x88888888u;
+      // i < 7: bit 3 of i + 1 clear (i + 1 <= 8)
+      const uint32_t INC = (LT & ~(I + 0x11111111u) & 0x88888888u) >> 3;   // neighbour i + 1
+      const uint32_t DEC = GT >> 3;               // neighbour i - 1 (d > 0 needs i >= 1)
       uint32_t pick;
       if constexpr (RECORD) {
-        pick = (live && ((i ^ (rbits >> j)) & 1u)) ? other : i;
+        const uint32_t flip = live ? (I ^ nibble_spread8((rbits >> (8 * h)) & 0xFFu)) & 0x11111111u : 0u;
+        pick = I + (flip & INC) - (flip & DEC);
+        const uint32_t moved = __builtin_popcount(flip & (INC | DEC));
+        h0 += 8u - moved;
+        h1 += moved;
       } else {
-        // In magnitude space: r = the rollout index, negated when its sign
-        // differs from x's (a rollout zero is on either side).  The candidate
-        // on the rollout level's side is the larger magnitude when r reaches
-        // it.  (Checked against the signed-index rule for every index,
-        // neighbour, sign and rollout code.)
-        const uint32_t cr = (rw[j >> 3] >> (4 * (j & 7))) & 15u;
-        const int ir = (int)(cr & 7u);
-        const bool same = (cr & 8u) == sgn || ir == 0;
-        const int r = same ? ir : -ir;
-        const int mx = (int)(other > i ? other : i), mn = (int)(other > i ? i : other);
-        pick = (live && r >= mx) ? (uint32_t)mx : (live ? (uint32_t)mn : i);
-        const int dist = same ? (ir > (int)i ? ir - (int)i : (int)i - ir) : ir + (int)i;
-        e0 |= (uint32_t)(dist == 0) << j;
-        e1 |= (uint32_t)(dist == 1) << j;
+        // r = the rollout index, on x's side when its sign is x's or it is
+        // zero ("same"); the larger candidate HI is picked when same and
+        // r >= HI, else the smaller one.  (Checked against the signed-index
+        // rule for every index, neighbour, sign and rollout code.)
+        const uint32_t R = rw[h] & 0x77777777u, RS = rw[h] & 0x88888888u;
+        const uint32_t same = (~(RS ^ SGN) | ~(R + 0x77777777u)) & 0x88888888u;   // r + 7 <= 14
+        const uint32_t HI = I + INC;
+        const uint32_t ge = ((R | 0x88888888u) - HI) & 0x88888888u;           // 8 + r - HI in 1..15
+        const uint32_t sel = live ? (same & ge) >> 3 : 0u;
+        pick = I - DEC + (sel & (INC | DEC));
+        // index distance 0 and 1 (same side: |r - i|, else r + i)
+        const uint32_t AD = (R | 0x88888888u) - I;                         // 8 + r - i in 1..15
+        const uint32_t e0 = same & nibble_zero3(R ^ I);
+        const uint32_t e1 = (same & (nibble_zero4(AD ^ 0x99999999u) | nibble_zero4(AD ^ 0x77777777u))) |
+                            (~same & nibble_zero4((R + I) ^ 0x11111111u));  // r + i <= 14
+        const uint32_t n0 = __builtin_popcount(e0), n1 = __builtin_popcount(e1);
+        h0 += n0;
+        h1 += n1;
+        h2 += 8u - n0 - n1;
       }
-      const uint32_t code = sgn | pick;
-      if (j < 8) g0 |= code << (4 * j); else g1 |= code << (4 * (j - 8));
+      g[h] = SGN | pick;
     }
-    if constexpr (RECORD) {                       // moved = nibbles that left round-to-nearest
-      auto nz = [](uint32_t x) { return (x | (x >> 1) | (x >> 2) | (x >> 3)) & 0x11111111u; };
-      const uint32_t moved = __builtin_popcount(nz(g0 ^ w0)) + __builtin_popcount(nz(g1 ^ w1));
-      h0 += 16u - moved;
-      h1 += moved;
-    } else {
-      const uint32_t n0 = __builtin_popcount(e0), n1 = __builtin_popcount(e1);
-      h0 += n0;
-      h1 += n1;
-      h2 += 16u - n0 - n1;
-    }
+    const uint32_t g0 = g[0], g1 = g[1];
+    uint32_t fq[8];
     *reinterpret_cast<u32x2*>(guided + (int64_t)b * 8) = u32x2{g0, g1};
     if (x_fq) {
       // bf16(RNE32(value * S)) two elements at a time, as in the weight QDQ
