@@ -527,21 +527,6 @@ hipError_t launch_mx_qdq(const __bf16* w, int64_t rows, int64_t K, __bf16* w_qdq
 // ---------------------------------------------------------------------------
 // guided rounding
 // ---------------------------------------------------------------------------
-// signed level index -7..7 of a 4-bit code (+0 and -0 are both 0)
-__device__ __forceinline__ int signed_index(uint32_t c) {
-  const int i = (int)(c & 7u);
-  return (c & 8u) ? -i : i;
-}
-
-// RECORD = false: roll holds the rollout codes [M, K/2], and hist counts the
-// elements whose round-to-nearest index is 0, 1 and >= 2 from the rollout's.
-// RECORD = true: roll holds the mantissa-only record [M, K/8] (the low code
-// bit of each element, element 8i + j in bit j of byte i); the output is the
-// neighbour whose magnitude index has that low bit (neighbouring levels differ
-// in it), and hist counts the elements kept at round-to-nearest and moved.
-// MX = true: MXFP4 rollout scales, one E8M0 byte per 32 elements (16-element
-// chunk b of a row takes byte b / 2, K being a multiple of 32), S = 2^X and no
-// global scale (roll_global unused).
 // Nibble-parallel helpers: eight 4-bit fields of a word at once.
 // Bit 3 of each nibble set where the nibble's low three bits are zero (bit 3
 // of the nibble must be clear: t + 7 <= 14 carries into bit 3 only).
@@ -557,6 +542,15 @@ __device__ __forceinline__ uint32_t nibble_spread8(uint32_t b) {
   return (b | (b << 3)) & 0x11111111u;
 }
 
+// RECORD = false: roll holds the rollout codes [M, K/2], and hist counts the
+// elements whose round-to-nearest index is 0, 1 and >= 2 from the rollout's.
+// RECORD = true: roll holds the mantissa-only record [M, K/8] (the low code
+// bit of each element, element 8i + j in bit j of byte i); the output is the
+// neighbour whose magnitude index has that low bit (neighbouring levels differ
+// in it), and hist counts the elements kept at round-to-nearest and moved.
+// MX = true: MXFP4 rollout scales, one E8M0 byte per 32 elements (16-element
+// chunk b of a row takes byte b / 2, K being a multiple of 32), S = 2^X and no
+// global scale (roll_global unused).
 template <typename T, bool RECORD, bool MX = false>
 __global__ __launch_bounds__(256) void guided_kernel(
     const T* __restrict__ x, uint32_t M, uint32_t K, int64_t ldx, const uint8_t* __restrict__ roll,
