@@ -245,7 +245,12 @@ int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64
  * Errors: EINVAL (shapes, K % 64, pointers, epilogue arguments, kc),
  *         EUNSUPPORTED (K > 65536, rows_total >= 2^31, operands of 4 GiB),
  *         EWORKSPACE.
- * rows_total == 0 is valid (out_amax set to 0, nothing else written).
+ * rows_total == 0 is valid (out_amax set to 0, nothing else written; with
+ * SCATTER_F32, out is zeroed).
+ * Streams: with 256-row tiles the groups' ragged remainders run on a stream
+ * that the library keeps per device, forked from `stream` and joined back
+ * into it with events, so the call is ordered on `stream` as one operation
+ * (also under graph capture).
  * ------------------------------------------------------------------------ */
 size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K,
                                             int epilogue, int64_t out_rows);

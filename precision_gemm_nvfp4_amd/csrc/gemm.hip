@@ -81,6 +81,8 @@
 // second time), and an A tile is reused by consecutive n-tiles.
 #include "gemm_common.h"
 
+#include <mutex>
+
 namespace nvfp4 {
 namespace nvg {
 
@@ -863,6 +865,37 @@ bool grouped_gemm_offsets_fit(int64_t a_rows, int64_t N, int64_t K) {
   return a_rows * (K / 2) < lim && N * (K / 2) < lim;
 }
 
+// A second stream per device for the launch of ragged remainders, forked
+// from and joined back into the caller's stream with two events: its 32-row
+// tiles then run on the CUs that the 256-row launch's last round leaves idle
+// (0.02-0.06 ms per projection on the 8192-token layer, 0.04-0.07 on the
+// 16384-token prefill).  Created on first use and kept for the process; the
+// mutex keeps the event record/wait pairs of concurrent host threads apart.
+// Where the stream or its events cannot be had, the launch stays on the
+// caller's stream.
+struct SideStream {
+  std::mutex mu;
+  bool tried = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+static SideStream* side_stream() {
+  static std::mutex mu;
+  static SideStream per_dev[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  std::lock_guard<std::mutex> lk(mu);
+  SideStream& ss = per_dev[dev];
+  if (!ss.tried) {
+    ss.tried = true;
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      ss.s = nullptr;
+  }
+  return ss.s ? &ss : nullptr;
+}
+
 hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.epilogue == 1 && a.out_amax) {
     hipError_t err = launch_fill_f32(a.out_amax, 1, 0.0f, stream);
@@ -879,14 +912,25 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
   if (a.sel_idx && a.kc > 64 && bm > 128) bm = 128;
   if (bm == 256 && a.block_m == 0) {
     // 256-row tiles over each group's rows except a remainder of fewer than
-    // 96 rows, then those remainders in 32-row tiles: 256 workgroups (one
+    // 96 rows, and those remainders in 32-row tiles: 256 workgroups (one
     // per CU) go round them, as the host does not know how many there are.
+    // The two launches write disjoint rows (and max into one amax).
     GemmArgs big = a, rest = a;
     big.tail_split = 1;
     rest.tail_split = 2;
     rest.grid_cap = 256;
-    err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
-    if (err == hipSuccess) err = nvg::launch_32(rest, stream);
+    if (SideStream* ss = side_stream()) {
+      std::lock_guard<std::mutex> lk(ss->mu);
+      err = hipEventRecord(ss->fork, stream);
+      if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
+      if (err == hipSuccess) err = nvg::launch_32(rest, ss->s);
+      if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
+      if (err == hipSuccess) err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
+      if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
+    } else {
+      err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
+      if (err == hipSuccess) err = nvg::launch_32(rest, stream);
+    }
     if (err != hipSuccess || a.epilogue != 2) return err;
     return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
                           static_cast<float*>(a.out), a.ldo, a.combine_overwrite, a.y_rows, stream);
