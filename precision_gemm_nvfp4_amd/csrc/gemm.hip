@@ -879,11 +879,16 @@ struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
-static SideStream* side_stream() {
+static SideStream* side_stream(hipStream_t caller) {
   static std::mutex mu;
   static SideStream per_dev[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  // Not while the caller's stream is being captured into a graph: the fork
+  // would pull the shared stream into that capture, and with it the work of
+  // other threads.  Captured calls keep to the caller's stream.
+  hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(caller, &st) != hipSuccess || st != hipStreamCaptureStatusNone) return nullptr;
   std::lock_guard<std::mutex> lk(mu);
   SideStream& ss = per_dev[dev];
   if (!ss.tried) {
@@ -919,7 +924,7 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
     big.tail_split = 1;
     rest.tail_split = 2;
     rest.grid_cap = 256;
-    if (SideStream* ss = side_stream()) {
+    if (SideStream* ss = side_stream(stream)) {
       std::lock_guard<std::mutex> lk(ss->mu);
       err = hipEventRecord(ss->fork, stream);
       if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);

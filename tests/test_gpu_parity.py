@@ -696,9 +696,10 @@ def test_scatter_overwrite_equals_add_into_zeros(gpu_lib):
 @pytest.mark.gpu
 def test_grouped_gemm_tail_split_graph_replays(gpu_lib):
     """Groups of 256 rows and more take 256-row tiles plus a launch of 32-row
-    tiles for their ragged remainders on the library's second stream; the
-    call captured in a HIP graph and replayed (eager work in between) gives
-    the eager result bit for bit every time."""
+    tiles for their ragged remainders (on the library's second stream when
+    eager, on the capturing stream under capture); the call captured in a HIP
+    graph and replayed (eager work in between) gives the eager result bit for
+    bit every time."""
     P = gpu_lib
     rng = np.random.default_rng(21)
     counts = np.array([300, 280, 512, 261], dtype=np.int64)          # remainders 44, 24, 0, 5
