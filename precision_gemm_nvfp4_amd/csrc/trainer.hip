@@ -548,68 +548,71 @@ __device__ __forceinline__ uint32_t nibble_spread8(uint32_t b) {
 // bit of each element, element 8i + j in bit j of byte i); the output is the
 // neighbour whose magnitude index has that low bit (neighbouring levels differ
 // in it), and hist counts the elements kept at round-to-nearest and moved.
-// MX = true: MXFP4 rollout scales, one E8M0 byte per 32 elements (16-element
-// chunk b of a row takes byte b / 2, K being a multiple of 32), S = 2^X and no
-// global scale (roll_global unused).
+// MX = true: MXFP4 rollout scales, one E8M0 byte per 32 elements, S = 2^X
+// and no global scale (roll_global unused).
+//
+// Every element is rounded on its own once its block's rollout scale is
+// known, so a lane takes 8 consecutive elements (item e: elements 8e .. 8e+7
+// of the row-major [M, K] tensor, half a scale block): its 16-byte load of x,
+// its code word or record byte, and its 16-byte store of x_fq sit next to the
+// neighbouring lanes' and every access of a wave is one contiguous run.
+constexpr int kGuidedThreads = 1024;
+
 template <typename T, bool RECORD, bool MX = false>
-__global__ __launch_bounds__(256) void guided_kernel(
+__global__ __launch_bounds__(kGuidedThreads) void guided_kernel(
     const T* __restrict__ x, uint32_t M, uint32_t K, int64_t ldx, const uint8_t* __restrict__ roll,
     const uint8_t* __restrict__ roll_scales, const float* __restrict__ roll_global,
     uint8_t* __restrict__ guided, __bf16* __restrict__ x_fq, unsigned long long* __restrict__ hist) {
-  const uint32_t nb = K / kBlock;
-  const uint32_t total = M * nb;                  // >= 1: the launcher skips empty inputs
+  const uint32_t per_row = K / 8;
+  const uint64_t total = (uint64_t)M * per_row;   // >= 1: the launcher skips empty inputs
   const float g_roll = MX ? 1.0f : *roll_global;
+  const bool dense = ldx == (int64_t)K;
   uint32_t h0 = 0, h1 = 0, h2 = 0;
-  // The inputs of a thread's next block are loaded before the current one is
-  // rounded (from a clamped index, unconditionally), so each trip of the
-  // grid-stride loop has its loads in flight during the previous trip.
+  // A lane's next item is loaded before the current one is rounded (from a
+  // clamped index, unconditionally), so each trip of the grid-stride loop has
+  // its loads in flight during the previous trip's arithmetic.
   struct In {
-    u32x4 q[sizeof(T)];                           // 16 elements
+    u32x4 q[sizeof(T) / 2];                       // 8 elements
     uint32_t sc;                                  // rollout scale byte
-    u32x2 roll;                                   // codes (8 bytes) or record bits (low 16)
+    uint32_t rw;                                  // code word or record byte
   };
-  auto fetch = [&](uint32_t bb, In& in) {
-    const uint32_t r = bb / nb, bc = bb - r * nb;
-    const u32x4* src = reinterpret_cast<const u32x4*>(x + (int64_t)r * ldx + bc * kBlock);
+  auto fetch = [&](uint64_t i, In& in) {
+    int64_t xo = (int64_t)i * 8;
+    if (!dense) xo += (int64_t)((uint32_t)i / per_row) * (ldx - (int64_t)K);
 #pragma unroll
-    for (int i = 0; i < (int)sizeof(T); ++i) in.q[i] = src[i];
-    in.sc = roll_scales[MX ? bb >> 1 : bb];
-    if constexpr (RECORD) in.roll = u32x2{*reinterpret_cast<const uint16_t*>(roll + (int64_t)bb * 2), 0u};
-    else in.roll = *reinterpret_cast<const u32x2*>(roll + (int64_t)bb * 8);
+    for (int j = 0; j < (int)(sizeof(T) / 2); ++j) in.q[j] = reinterpret_cast<const u32x4*>(x + xo)[j];
+    in.sc = roll_scales[MX ? i >> 2 : i >> 1];
+    in.rw = RECORD ? (uint32_t)roll[i] : reinterpret_cast<const uint32_t*>(roll)[i];
   };
-  const uint32_t stride = gridDim.x * blockDim.x;
-  uint32_t b = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint64_t stride = (uint64_t)gridDim.x * blockDim.x;
+  uint64_t e = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x;
   In cur, nxt;
-  fetch(b < total ? b : total - 1, cur);
-  for (; b < total; b += stride) {
-    fetch(b + stride < total ? b + stride : b, nxt);
-    float v[16];
+  fetch(e < total ? e : total - 1, cur);
+  for (; e < total; e += stride) {
+    fetch(e + stride < total ? e + stride : e, nxt);
+    const u32x4* q = cur.q;
+    const uint32_t sc = cur.sc, rw = cur.rw;
+    float v[8];
     if constexpr (sizeof(T) == 2) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_lo(cur.q[0][i]);
-        v[2 * i + 1] = bf16_hi(cur.q[0][i]);
-        v[8 + 2 * i] = bf16_lo(cur.q[1][i]);
-        v[8 + 2 * i + 1] = bf16_hi(cur.q[1][i]);
+        v[2 * i] = bf16_lo(q[0][i]);
+        v[2 * i + 1] = bf16_hi(q[0][i]);
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) v[i] = __uint_as_float(cur.q[i >> 2][i & 3]);
+      for (int i = 0; i < 8; ++i) v[i] = __uint_as_float(q[i >> 2][i & 3]);
     }
-    const float S = MX ? e8m0_value(cur.sc) : e4m3_value(cur.sc) * g_roll;
+    const float S = MX ? e8m0_value(sc) : e4m3_value(sc) * g_roll;
     // round-to-nearest codes under S (fast path, exact fallback)
-    uint32_t w0, w1;
+    uint32_t w;
     if (S >= 0x1p-100f) {
       float iu, id;
       e2m1_brackets(S, iu, id);
-      w0 = e2m1_pack8_fast(v, iu, id, S);
-      w1 = e2m1_pack8_fast(v + 8, iu, id, S);
+      w = e2m1_pack8_fast(v, iu, id, S);
     } else {
-      w0 = e2m1_pack8_exact(v, S);
-      w1 = e2m1_pack8_exact(v + 8, S);
+      w = e2m1_pack8_exact(v, S);
     }
-    const u32x2 rw = cur.roll;
-    const uint32_t rbits = cur.roll[0];
     // Candidates in magnitude space: the round-to-nearest index i and, by the
     // exact sign of i's level * S - |x|, its neighbour on x's side (i + 1 up
     // to 7, i - 1, or none when x sits on the level).  Both carry x's sign
@@ -619,74 +622,65 @@ __global__ __launch_bounds__(256) void guided_kernel(
     // the one closer to it; the record rule picks the one whose index has the
     // recorded low bit.  Only the sign of each element's difference is taken
     // per element (bit 3 of its nibble in LT or GT); the choice itself runs
-    // on the eight nibbles of a code word at once (nibble_*: no carry or
+    // on the eight nibbles of the code word at once (nibble_*: no carry or
     // borrow crosses a nibble, as each comment shows).
     const bool live = S != 0.0f;                  // S == 0: every code stays at magnitude 0
-    uint32_t g[2];
+    float Lm[8];
+    e2m1_unpack8(w & 0x77777777u, Lm);
+    uint32_t LT = 0, GT = 0;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t w = h ? w1 : w0;
-      float Lm[8];
-      e2m1_unpack8(w & 0x77777777u, Lm);
-      uint32_t LT = 0, GT = 0;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float d = __builtin_fmaf(Lm[j], S, -fabsf(v[8 * h + j]));   // exact sign
-        LT |= d < 0.0f ? 8u << (4 * j) : 0u;
-        GT |= d > 0.0f ? 8u << (4 * j) : 0u;
-      }
-      const uint32_t I = w & 0x77777777u, SGN = w & 0x88888888u;
-      // i < 7: bit 3 of i + 1 clear (i + 1 <= 8)
-      const uint32_t INC = (LT & ~(I + 0x11111111u) & 0x88888888u) >> 3;   // neighbour i + 1
-      const uint32_t DEC = GT >> 3;               // neighbour i - 1 (d > 0 needs i >= 1)
-      uint32_t pick;
-      if constexpr (RECORD) {
-        const uint32_t flip = live ? (I ^ nibble_spread8((rbits >> (8 * h)) & 0xFFu)) & 0x11111111u : 0u;
-        pick = I + (flip & INC) - (flip & DEC);
-        const uint32_t moved = __builtin_popcount(flip & (INC | DEC));
-        h0 += 8u - moved;
-        h1 += moved;
-      } else {
-        // r = the rollout index, on x's side when its sign is x's or it is
-        // zero ("same"); the larger candidate HI is picked when same and
-        // r >= HI, else the smaller one.  (Checked against the signed-index
-        // rule for every index, neighbour, sign and rollout code.)
-        const uint32_t R = rw[h] & 0x77777777u, RS = rw[h] & 0x88888888u;
-        const uint32_t same = (~(RS ^ SGN) | ~(R + 0x77777777u)) & 0x88888888u;   // r + 7 <= 14
-        const uint32_t HI = I + INC;
-        const uint32_t ge = ((R | 0x88888888u) - HI) & 0x88888888u;           // 8 + r - HI in 1..15
-        const uint32_t sel = live ? (same & ge) >> 3 : 0u;
-        pick = I - DEC + (sel & (INC | DEC));
-        // index distance 0 and 1 (same side: |r - i|, else r + i)
-        const uint32_t AD = (R | 0x88888888u) - I;                         // 8 + r - i in 1..15
-        const uint32_t e0 = same & nibble_zero3(R ^ I);
-        const uint32_t e1 = (same & (nibble_zero4(AD ^ 0x99999999u) | nibble_zero4(AD ^ 0x77777777u))) |
-                            (~same & nibble_zero4((R + I) ^ 0x11111111u));  // r + i <= 14
-        const uint32_t n0 = __builtin_popcount(e0), n1 = __builtin_popcount(e1);
-        h0 += n0;
-        h1 += n1;
-        h2 += 8u - n0 - n1;
-      }
-      g[h] = SGN | pick;
+    for (int j = 0; j < 8; ++j) {
+      const float d = __builtin_fmaf(Lm[j], S, -fabsf(v[j]));   // exact sign
+      LT |= d < 0.0f ? 8u << (4 * j) : 0u;
+      GT |= d > 0.0f ? 8u << (4 * j) : 0u;
     }
-    const uint32_t g0 = g[0], g1 = g[1];
-    uint32_t fq[8];
-    *reinterpret_cast<u32x2*>(guided + (int64_t)b * 8) = u32x2{g0, g1};
+    const uint32_t I = w & 0x77777777u, SGN = w & 0x88888888u;
+    // i < 7: bit 3 of i + 1 clear (i + 1 <= 8)
+    const uint32_t INC = (LT & ~(I + 0x11111111u) & 0x88888888u) >> 3;   // neighbour i + 1
+    const uint32_t DEC = GT >> 3;                 // neighbour i - 1 (d > 0 needs i >= 1)
+    uint32_t pick;
+    if constexpr (RECORD) {
+      const uint32_t flip = live ? (I ^ nibble_spread8(rw)) & 0x11111111u : 0u;
+      pick = I + (flip & INC) - (flip & DEC);
+      const uint32_t moved = __builtin_popcount(flip & (INC | DEC));
+      h0 += 8u - moved;
+      h1 += moved;
+    } else {
+      // r = the rollout index, on x's side when its sign is x's or it is
+      // zero ("same"); the larger candidate HI is picked when same and
+      // r >= HI, else the smaller one.  (Checked against the signed-index
+      // rule for every index, neighbour, sign and rollout code.)
+      const uint32_t R = rw & 0x77777777u, RS = rw & 0x88888888u;
+      const uint32_t same = (~(RS ^ SGN) | ~(R + 0x77777777u)) & 0x88888888u;   // r + 7 <= 14
+      const uint32_t HI = I + INC;
+      const uint32_t ge = ((R | 0x88888888u) - HI) & 0x88888888u;           // 8 + r - HI in 1..15
+      const uint32_t sel = live ? (same & ge) >> 3 : 0u;
+      pick = I - DEC + (sel & (INC | DEC));
+      // index distance 0 and 1 (same side: |r - i|, else r + i)
+      const uint32_t AD = (R | 0x88888888u) - I;                         // 8 + r - i in 1..15
+      const uint32_t e0 = same & nibble_zero3(R ^ I);
+      const uint32_t e1 = (same & (nibble_zero4(AD ^ 0x99999999u) | nibble_zero4(AD ^ 0x77777777u))) |
+                          (~same & nibble_zero4((R + I) ^ 0x11111111u));  // r + i <= 14
+      const uint32_t n0 = __builtin_popcount(e0), n1 = __builtin_popcount(e1);
+      h0 += n0;
+      h1 += n1;
+      h2 += 8u - n0 - n1;
+    }
+    const uint32_t gw = SGN | pick;
+    reinterpret_cast<uint32_t*>(guided)[e] = gw;
     if (x_fq) {
       // bf16(RNE32(value * S)) two elements at a time, as in the weight QDQ
-      float d[16];
-      e2m1_unpack8(g0, d);
-      e2m1_unpack8(g1, d + 8);
+      float d[8];
+      e2m1_unpack8(gw, d);
+      u32x4 fq;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) fq[i] = pack_bf16x2_rne(d[2 * i] * S, d[2 * i + 1] * S);
-      u32x4* dst = reinterpret_cast<u32x4*>(x_fq + (int64_t)b * kBlock);
-      dst[0] = u32x4{fq[0], fq[1], fq[2], fq[3]};
-      dst[1] = u32x4{fq[4], fq[5], fq[6], fq[7]};
+      for (int i = 0; i < 4; ++i) fq[i] = pack_bf16x2_rne(d[2 * i] * S, d[2 * i + 1] * S);
+      reinterpret_cast<u32x4*>(x_fq)[e] = fq;
     }
     cur = nxt;
   }
   if (hist) {                                // one atomic per bin per workgroup
-    __shared__ uint32_t sh[3][4];
+    __shared__ uint32_t sh[3][kGuidedThreads / 64];
     h0 = wave_sum_u32(h0);
     h1 = wave_sum_u32(h1);
     h2 = wave_sum_u32(h2);
@@ -708,6 +702,8 @@ __global__ void zero_i64_kernel(unsigned long long* p, int n) {
   if ((int)threadIdx.x < n) p[threadIdx.x] = 0ull;
 }
 
+constexpr int64_t kGuidedGrid = 512;   // also bounds the histogram's atomics (3 per workgroup)
+
 template <bool RECORD, bool MX = false>
 static hipError_t launch_guided_t(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
                                   const uint8_t* roll, const uint8_t* roll_scales,
@@ -715,16 +711,16 @@ static hipError_t launch_guided_t(const void* x, int dtype, int64_t M, int64_t K
                                   int64_t* hist, hipStream_t stream) {
   unsigned long long* h = reinterpret_cast<unsigned long long*>(hist);
   if (h) zero_i64_kernel<<<1, 64, 0, stream>>>(h, RECORD ? 2 : 3);
-  const int64_t nb = M * (K / kBlock);
-  if (nb == 0) return hipGetLastError();
-  int64_t grid = (nb + 255) / 256;
-  if (grid > 2048) grid = 2048;
+  const int64_t items = M * (K / 8);             // 8-element items, one per lane and trip
+  if (items == 0) return hipGetLastError();
+  int64_t grid = (items + kGuidedThreads - 1) / kGuidedThreads;
+  if (grid > kGuidedGrid) grid = kGuidedGrid;
   if (dtype == 0)
-    guided_kernel<__bf16, RECORD, MX><<<(unsigned)grid, 256, 0, stream>>>(
+    guided_kernel<__bf16, RECORD, MX><<<(unsigned)grid, kGuidedThreads, 0, stream>>>(
         static_cast<const __bf16*>(x), (uint32_t)M, (uint32_t)K, ldx, roll, roll_scales,
         roll_global, guided, x_fq, h);
   else
-    guided_kernel<float, RECORD, MX><<<(unsigned)grid, 256, 0, stream>>>(
+    guided_kernel<float, RECORD, MX><<<(unsigned)grid, kGuidedThreads, 0, stream>>>(
         static_cast<const float*>(x), (uint32_t)M, (uint32_t)K, ldx, roll, roll_scales,
         roll_global, guided, x_fq, h);
   return hipGetLastError();
