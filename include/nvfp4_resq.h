@@ -120,7 +120,7 @@ int nvfp4_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
  * serving loops, harnesses that forbid allocation.
  *
  * Arguments, results and errors are those of nvfp4_quantize without ws and
- * ws_bytes.  Its scratch (the amax partial maxima, at most 1025 floats) is a
+ * ws_bytes.  Its scratch (the amax partial maxima, at most 256 floats) is a
  * fixed 8 KB array of device memory inside the library, one per GPU, held
  * until the process ends; the call uses the copy of the current device
  * (hipGetDevice), whose address it looks up on its first call there.  It

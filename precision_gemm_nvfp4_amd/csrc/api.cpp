@@ -84,8 +84,8 @@ int check_quantize(const void* x, int dtype, int64_t M, int64_t K, int64_t ldx,
 }
 
 // ---- scratch of nvfp4_quantize_noalloc --------------------------------------
-// The amax partial maxima and their fold: amax_partials_count(M, K) + 1 floats,
-// at most 1025 for any M (the count is capped at 1024), within this bound.
+// The amax partial maxima: amax_partials_count(M, K) floats, at most 256 for
+// any shape (the count is capped), within this bound.
 // Every GPU the library runs on holds its own copy of the array until the
 // process ends.  In host code `scratch` names a host-side stand-in, never a
 // device address: the device address comes from hipGetSymbolAddress, taken

@@ -6,9 +6,9 @@
 // Two passes over x, both coalesced HBM streams:
 //   amax_partials_kernel  per-workgroup max |x|  -> workspace (no atomics, no
 //                         initialisation, order-independent hence deterministic)
-//   amax_fold_kernel      one workgroup folds the partial maxima into one float
-//   quantize_tile_kernel  every workgroup derives g from that amax, then
-//                         quantizes a 128 x 64 tile;
+//   quantize_tile_kernel  every workgroup folds the partial maxima into the
+//                         tensor's amax, derives g from it, then quantizes a
+//                         128 x 64 tile;
 //                         optionally it also sums |x - DQ| of each channel over
 //                         the tile's 128 rows in fp32, in row order (the residual
 //                         channel-score partials of the residual activation
@@ -54,9 +54,10 @@ struct Row16<float> {
 // ---------------------------------------------------------------------------
 // pass 1: per-workgroup amax
 // ---------------------------------------------------------------------------
-// Workgroup b takes rows b, b + G, b + 2G, ... four at a time: the four rows'
-// chunks at a thread's position are loaded before their maxima are taken, so
-// each thread keeps four loads in flight.
+// The tensor is a flat sequence of 16-byte chunks (row r's chunks after row
+// r - 1's, the row stride skipped); thread t of the grid takes chunks t,
+// t + G, t + 2G, ... (G = grid threads), eight at a time, all eight loaded
+// before their maxima are taken.
 template <typename T>
 __device__ __forceinline__ float absmax_chunk(const u32x4& w, float m) {
   if constexpr (sizeof(T) == 2) {
@@ -68,32 +69,34 @@ __device__ __forceinline__ float absmax_chunk(const u32x4& w, float m) {
   }
   return m;
 }
+constexpr int kAmaxBatch = 8;
+constexpr int kAmaxThreads = 1024;
 template <typename T>
-__global__ __launch_bounds__(256) void amax_partials_kernel(const T* __restrict__ x, int64_t M,
+__global__ __launch_bounds__(kAmaxThreads) void amax_partials_kernel(const T* __restrict__ x, int64_t M,
                                                             int64_t K, int64_t ldx,
                                                             float* __restrict__ partials) {
   constexpr int kPer = 16 / sizeof(T);                       // elements per 16-byte chunk
-  const int64_t chunks = K / kPer;
-  const int64_t G = gridDim.x;
+  const int64_t cpr = K / kPer;                              // chunks per row
+  const int64_t total = M * cpr;
+  const int64_t G = (int64_t)gridDim.x * blockDim.x;
+  const bool dense = ldx == K;
+  auto chunk = [&](int64_t c) -> u32x4 {
+    if (dense) return reinterpret_cast<const u32x4*>(x)[c];
+    const int64_t r = c / cpr;
+    return reinterpret_cast<const u32x4*>(x + r * ldx)[c - r * cpr];
+  };
   float m = 0.0f;
-  int64_t r = blockIdx.x;
-  for (; r + 3 * G < M; r += 4 * G) {
-    const T* row = x + r * ldx;
-    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x) {
-      const u32x4 w0 = *reinterpret_cast<const u32x4*>(row + c * kPer);
-      const u32x4 w1 = *reinterpret_cast<const u32x4*>(row + G * ldx + c * kPer);
-      const u32x4 w2 = *reinterpret_cast<const u32x4*>(row + 2 * G * ldx + c * kPer);
-      const u32x4 w3 = *reinterpret_cast<const u32x4*>(row + 3 * G * ldx + c * kPer);
-      m = absmax_chunk<T>(w3, absmax_chunk<T>(w2, absmax_chunk<T>(w1, absmax_chunk<T>(w0, m))));
-    }
+  int64_t c = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  for (; c + (kAmaxBatch - 1) * G < total; c += kAmaxBatch * G) {
+    u32x4 w[kAmaxBatch];
+#pragma unroll
+    for (int q = 0; q < kAmaxBatch; ++q) w[q] = chunk(c + q * G);
+#pragma unroll
+    for (int q = 0; q < kAmaxBatch; ++q) m = absmax_chunk<T>(w[q], m);
   }
-  for (; r < M; r += G) {
-    const T* row = x + r * ldx;
-    for (int64_t c = threadIdx.x; c < chunks; c += blockDim.x)
-      m = absmax_chunk<T>(*reinterpret_cast<const u32x4*>(row + c * kPer), m);
-  }
+  for (; c < total; c += G) m = absmax_chunk<T>(chunk(c), m);
   m = wave_max(m);
-  __shared__ float red[4];
+  __shared__ float red[kAmaxThreads / 64];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -101,18 +104,6 @@ __global__ __launch_bounds__(256) void amax_partials_kernel(const T* __restrict_
     for (int i = 1; i < (int)(blockDim.x >> 6); ++i) b = fmaxf(b, red[i]);
     partials[blockIdx.x] = b;
   }
-}
-
-// Folds the n partial maxima into partials[n] (one workgroup), so that every
-// quantize workgroup reads a single float.
-__global__ __launch_bounds__(256) void amax_fold_kernel(float* __restrict__ partials, int n) {
-  float m = 0.0f;
-  for (int i = threadIdx.x; i < n; i += blockDim.x) m = fmaxf(m, partials[i]);
-  m = wave_max(m);
-  __shared__ float red[4];
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
-  __syncthreads();
-  if (threadIdx.x == 0) partials[n] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
 }
 
 // ---------------------------------------------------------------------------
@@ -140,13 +131,10 @@ constexpr int kAbsStride = kTileCols + 4;          // floats per LDS row
 template <typename T, bool SCORES>
 __global__ __launch_bounds__(256) void quantize_tile_kernel(
     const T* __restrict__ x, int64_t M, int64_t K, int64_t ldx,
-    const float* __restrict__ amax, uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
-    float* __restrict__ g_out, float* __restrict__ tile_partials) {
+    const float* __restrict__ amax, int n_amax, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales, float* __restrict__ g_out, float* __restrict__ tile_partials) {
   __shared__ float absr[SCORES ? kScoreTileRows * kAbsStride : 1];
   const int tid = threadIdx.x;
-  const float g = global_scale_from_amax(*amax);
-  const BlockScaler bsc = make_block_scaler(g);
-  if (g_out && blockIdx.x == 0 && tid == 0) *g_out = g;
 
   const int64_t nb = K / kBlock;
   const int64_t tiles_x = (nb + kTileBlocks - 1) / kTileBlocks;
@@ -158,6 +146,18 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
   const int bl = tid % kTileBlocks, rsub = tid / kTileBlocks;
   const int64_t bc = tx * kTileBlocks + bl;
   const int64_t r0 = ty * kScoreTileRows;
+  // The tensor's amax: one value, or the n_amax (<= 256) partial maxima of
+  // the amax pass, which every wave folds by itself, four per lane (max is
+  // exact in any order).  Loaded ahead of x, so that waiting for them does
+  // not wait for x.
+  float pm[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (n_amax == 1) {
+    pm[0] = *amax;                                   // as given (a caller's amax_in)
+  } else {
+    const int l4 = (tid & 63) * 4;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pm[i] = l4 + i < n_amax ? amax[l4 + i] : 0.0f;
+  }
   float v[kRowsPerThread][16];
   bool live[kRowsPerThread];
 #pragma unroll
@@ -166,6 +166,10 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
     live[j] = r < M && bc < nb;
     if (live[j]) Row16<T>::load(x + r * ldx + bc * kBlock, v[j]);
   }
+  const float am = n_amax == 1 ? pm[0] : wave_max(fmaxf(fmaxf(pm[0], pm[1]), fmaxf(pm[2], pm[3])));
+  const float g = global_scale_from_amax(am);
+  const BlockScaler bsc = make_block_scaler(g);
+  if (g_out && tile == 0 && tid == 0) *g_out = g;
 #pragma unroll
   for (int j = 0; j < kRowsPerThread; ++j) {
     const int rl = rsub + (256 / kTileBlocks) * j;
@@ -208,10 +212,14 @@ __global__ __launch_bounds__(256) void quantize_tile_kernel(
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+// One partial maximum per workgroup of the amax pass: enough workgroups of
+// 1024 threads for one batch of eight 16-byte loads per thread on a bf16
+// tensor (8192 elements per thread), at most 256, one per CU (each quantize
+// wave folds them with one load per lane).
 int amax_partials_count(int64_t M, int64_t K) {
-  (void)K;
-  int64_t n = M < 1024 ? M : 1024;
-  return n < 1 ? 1 : (int)n;
+  const int64_t per = (int64_t)kAmaxThreads * kAmaxBatch * 8;
+  const int64_t n = (M * K + per - 1) / per;
+  return n < 1 ? 1 : (n > 256 ? 256 : (int)n);
 }
 
 template <typename T>
@@ -219,22 +227,22 @@ static hipError_t launch_quantize_t(const T* x, int64_t M, int64_t K, int64_t ld
                                     const float* amax_in, uint8_t* codes, uint8_t* scales,
                                     float* g_out, float* tile_partials, float* ws_partials,
                                     hipStream_t stream) {
-  const int np = amax_partials_count(M, K);
   const float* amax = amax_in;
+  int n_amax = 1;
   if (!amax_in) {
-    amax_partials_kernel<T><<<np, 256, 0, stream>>>(x, M, K, ldx, ws_partials);
-    amax_fold_kernel<<<1, 256, 0, stream>>>(ws_partials, np);
-    amax = ws_partials + np;
+    n_amax = amax_partials_count(M, K);
+    amax_partials_kernel<T><<<n_amax, kAmaxThreads, 0, stream>>>(x, M, K, ldx, ws_partials);
+    amax = ws_partials;
   }
   const int64_t ntiles = ((K / kBlock + kTileBlocks - 1) / kTileBlocks) *
                          ((M + kScoreTileRows - 1) / kScoreTileRows);
   const unsigned grid = (unsigned)(ntiles > 0 ? (ntiles + 7) / 8 * 8 : 8);   // whole eighths, one per XCD
   if (tile_partials)
-    quantize_tile_kernel<T, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, amax, codes, scales,
-                                                            g_out, tile_partials);
+    quantize_tile_kernel<T, true><<<grid, 256, 0, stream>>>(x, M, K, ldx, amax, n_amax, codes,
+                                                            scales, g_out, tile_partials);
   else
-    quantize_tile_kernel<T, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, amax, codes, scales,
-                                                             g_out, nullptr);
+    quantize_tile_kernel<T, false><<<grid, 256, 0, stream>>>(x, M, K, ldx, amax, n_amax, codes,
+                                                             scales, g_out, nullptr);
   return hipGetLastError();
 }
 

@@ -39,7 +39,7 @@ def test_exports_every_declared_symbol(lib):
 
 
 def test_workspace_sizes(lib):
-    assert lib.nvfp4_quantize_workspace_size(16384, 4096) >= 1024 * 4
+    assert lib.nvfp4_quantize_workspace_size(16384, 4096) >= 256 * 4   # one partial per amax workgroup, at most 256
     n = lib.resq_select_and_requant_workspace_size(2048, 131072, 128, 64)
     assert n >= (131072 // 128 + 128) * 2048 * 4 + 131072 * 64 * 4
     assert lib.qdq_weights_workspace_size(512, 3072, 4096) >= 512 * 4
