@@ -206,39 +206,58 @@ size_t combine_workspace_bytes(int64_t rows, int64_t N, int64_t out_rows) {
   return a256((size_t)rows * N * 4) + 3 * a256((size_t)(out_rows + 1) * 4) + a256((size_t)rows * 4);
 }
 
-hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
-                          const int32_t* scatter_index, int64_t out_rows, float* out, int64_t ldo,
-                          bool overwrite, void* ws, hipStream_t stream) {
-  auto a256 = [](size_t n) { return (n + 255) & ~size_t(255); };
-  char* w = static_cast<char*>(ws) + a256((size_t)rows * N * 4);
-  int32_t* count = reinterpret_cast<int32_t*>(w);
-  w += a256((size_t)(out_rows + 1) * 4);
-  int32_t* start = reinterpret_cast<int32_t*>(w);
-  w += a256((size_t)(out_rows + 1) * 4);
-  int32_t* cursor = reinterpret_cast<int32_t*>(w);
-  w += a256((size_t)(out_rows + 1) * 4);
-  int32_t* list = reinterpret_cast<int32_t*>(w);
+// The workspace: the rows, then count, start and cursor ([out_rows + 1]
+// each) and the row lists ([rows]).
+struct CombineWs {
+  int32_t *count, *start, *cursor, *list;
+  CombineWs(void* ws, int64_t rows, int64_t N, int64_t out_rows) {
+    auto a256 = [](size_t n) { return (n + 255) & ~size_t(255); };
+    char* w = static_cast<char*>(ws) + a256((size_t)rows * N * 4);
+    count = reinterpret_cast<int32_t*>(w);
+    w += a256((size_t)(out_rows + 1) * 4);
+    start = reinterpret_cast<int32_t*>(w);
+    w += a256((size_t)(out_rows + 1) * 4);
+    cursor = reinterpret_cast<int32_t*>(w);
+    w += a256((size_t)(out_rows + 1) * 4);
+    list = reinterpret_cast<int32_t*>(w);
+  }
+};
+
+hipError_t launch_combine_plan(int64_t rows, int64_t N, const int32_t* scatter_index,
+                               int64_t out_rows, void* ws, hipStream_t stream) {
+  const CombineWs w(ws, rows, N, out_rows);
   if (out_rows <= kPlanSmallOut) {
-    combine_plan_small_kernel<<<1, 1024, 0, stream>>>(scatter_index, rows, out_rows, start, list);
-    if (out_rows > 0)
-      combine_rows_kernel<<<(unsigned)out_rows, 256, 0, stream>>>(
-          y_rows, N, start, list, out, ldo,
-          N % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0, overwrite);
+    combine_plan_small_kernel<<<1, 1024, 0, stream>>>(scatter_index, rows, out_rows, w.start, w.list);
     return hipGetLastError();
   }
   const int64_t zb = (out_rows + 255) / 256;
-  combine_zero_kernel<<<(unsigned)(zb > 1024 ? 1024 : (zb < 1 ? 1 : zb)), 256, 0, stream>>>(count, cursor,
+  combine_zero_kernel<<<(unsigned)(zb > 1024 ? 1024 : (zb < 1 ? 1 : zb)), 256, 0, stream>>>(w.count, w.cursor,
                                                                                           out_rows + 1);
   const int64_t rb = (rows + 255) / 256;
   const unsigned rg = (unsigned)(rb > 2048 ? 2048 : (rb < 1 ? 1 : rb));
-  combine_count_kernel<<<rg, 256, 0, stream>>>(scatter_index, rows, out_rows, count);
-  combine_scan_kernel<<<1, 1024, 0, stream>>>(count, out_rows, start);
-  combine_place_kernel<<<rg, 256, 0, stream>>>(scatter_index, rows, out_rows, start, cursor, list);
+  combine_count_kernel<<<rg, 256, 0, stream>>>(scatter_index, rows, out_rows, w.count);
+  combine_scan_kernel<<<1, 1024, 0, stream>>>(w.count, out_rows, w.start);
+  combine_place_kernel<<<rg, 256, 0, stream>>>(scatter_index, rows, out_rows, w.start, w.cursor, w.list);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_rows(const float* y_rows, int64_t rows, int64_t N, int64_t out_rows,
+                               float* out, int64_t ldo, bool overwrite, void* ws,
+                               hipStream_t stream) {
+  const CombineWs w(ws, rows, N, out_rows);
   if (out_rows > 0)
     combine_rows_kernel<<<(unsigned)out_rows, 256, 0, stream>>>(
-        y_rows, N, start, list, out, ldo,
+        y_rows, N, w.start, w.list, out, ldo,
         N % 4 == 0 && ldo % 4 == 0 && (reinterpret_cast<uintptr_t>(out) & 15u) == 0, overwrite);
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
+                          const int32_t* scatter_index, int64_t out_rows, float* out, int64_t ldo,
+                          bool overwrite, void* ws, hipStream_t stream) {
+  const hipError_t err = launch_combine_plan(rows, N, scatter_index, out_rows, ws, stream);
+  if (err != hipSuccess) return err;
+  return launch_combine_rows(y_rows, rows, N, out_rows, out, ldo, overwrite, ws, stream);
 }
 
 }  // namespace nvfp4

@@ -865,11 +865,11 @@ bool grouped_gemm_offsets_fit(int64_t a_rows, int64_t N, int64_t K) {
   return a_rows * (K / 2) < lim && N * (K / 2) < lim;
 }
 
-// A second stream per device for the launch of ragged remainders, forked
-// from and joined back into the caller's stream with two events: its 32-row
-// tiles then run on the CUs that the 256-row launch's last round leaves idle
-// (0.02-0.06 ms per projection on the 8192-token layer, 0.04-0.07 on the
-// 16384-token prefill).  Created on first use and kept for the process; the
+// A second stream per device for the launch of ragged remainders (and, ahead
+// of it, the scatter's plan), forked from and joined back into the caller's
+// stream with two events: its 32-row tiles then run on the CUs that the
+// 256-row launch's last round leaves idle (0.02-0.06 ms per projection on the
+// 8192-token layer, 0.04-0.07 on the 16384-token prefill).  Created on first use and kept for the process; the
 // mutex keeps the event record/wait pairs of concurrent host threads apart.
 // Where the stream or its events cannot be had, the launch stays on the
 // caller's stream.
@@ -924,18 +924,26 @@ hipError_t launch_grouped_gemm(const GemmArgs& a, hipStream_t stream) {
     big.tail_split = 1;
     rest.tail_split = 2;
     rest.grid_cap = 256;
+    // The scatter's plan (the row lists of each output row) needs only the
+    // scatter index, so it goes on the side stream ahead of the remainder
+    // launch and is hidden behind the 256-row launch; the ordered sum of the
+    // rows follows the join.
     if (SideStream* ss = side_stream(stream)) {
       std::lock_guard<std::mutex> lk(ss->mu);
       err = hipEventRecord(ss->fork, stream);
       if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
+      if (err == hipSuccess && a.epilogue == 2)
+        err = launch_combine_plan(a.rows_total, a.N, a.scatter_index, a.out_rows, a.y_rows, ss->s);
       if (err == hipSuccess) err = nvg::launch_32(rest, ss->s);
       if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
       if (err == hipSuccess) err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
       if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
-    } else {
-      err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
-      if (err == hipSuccess) err = nvg::launch_32(rest, stream);
+      if (err != hipSuccess || a.epilogue != 2) return err;
+      return launch_combine_rows(a.y_rows, a.rows_total, a.N, a.out_rows, static_cast<float*>(a.out),
+                                 a.ldo, a.combine_overwrite, a.y_rows, stream);
     }
+    err = nvg::launch_comp<4, 4, 2, 2, 3>(big, stream);
+    if (err == hipSuccess) err = nvg::launch_32(rest, stream);
     if (err != hipSuccess || a.epilogue != 2) return err;
     return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
                           static_cast<float*>(a.out), a.ldo, a.combine_overwrite, a.y_rows, stream);

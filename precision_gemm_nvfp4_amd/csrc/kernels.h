@@ -93,6 +93,13 @@ size_t combine_workspace_bytes(int64_t rows, int64_t N, int64_t out_rows);
 hipError_t launch_combine(const float* y_rows, int64_t rows, int64_t N,
                           const int32_t* scatter_index, int64_t out_rows, float* out, int64_t ldo,
                           bool overwrite, void* ws, hipStream_t stream);
+// The two halves of launch_combine: the plan (row lists per output row, from
+// scatter_index alone) and the ordered sum of the rows.
+hipError_t launch_combine_plan(int64_t rows, int64_t N, const int32_t* scatter_index,
+                               int64_t out_rows, void* ws, hipStream_t stream);
+hipError_t launch_combine_rows(const float* y_rows, int64_t rows, int64_t N, int64_t out_rows,
+                               float* out, int64_t ldo, bool overwrite, void* ws,
+                               hipStream_t stream);
 
 // trainer.hip
 size_t qdq_workspace_bytes(int64_t nmat);
