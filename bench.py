@@ -575,8 +575,11 @@ def quant_select_bench(args, torch, P, synth, wl, dev):
                 "units": "128-token tiles", "parallelism": "single GPU"},
         algorithmic_bytes=int(total_bytes), parts=parts,
         roofline=dict(bound="hbm", achieved=round(ach, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                      frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
-                      kernel="amax_partials_kernel + quantize_kernel<SCORES>"),
+                      frac=round(ach / HBM_PEAK_GBS, 4),
+                      traffic=traffic_int(profiled_traffic(
+                          wl.name, "amax_partials_kernel + quantize_tile_kernel",
+                          "quantizer_quant_select_T16384_K4096_k128")),
+                      kernel="amax_partials_kernel + quantize_tile_kernel<SCORES>"),
         frac_hbm=round(value / HBM_PEAK_GBS, 4), cpu_baseline=cpu)
 
 

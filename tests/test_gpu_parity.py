@@ -525,6 +525,33 @@ def test_guided_round_record(gpu_lib, rel, dtype):
         assert moved_r[1] > 0
 
 
+def test_guided_round_grid_stride_and_stride(gpu_lib):
+    """2100 x 2048 with a padded row stride: 537600 eight-element items, more
+    than one grid's worth (512 workgroups of 1024 lanes), so lanes take a
+    second, ragged trip with their prefetched item; codes, fake-quant values,
+    histogram and record form bit-exact against the oracle."""
+    P = gpu_lib
+    m, k, ld = 2100, 2048, 2056
+    x_roll = synth.activations(m, k, seed=41, heavy_frac=0.01)
+    x_train = synth.guided_noise(x_roll, seed=41, rel=8e-3)
+    buf = torch.zeros(m, ld, dtype=x_train.dtype)
+    buf[:, :k] = x_train
+    xt = buf.cuda()[:, :k]
+    assert xt.stride(0) == ld and m * k // 8 > 512 * 1024
+    rc, rs, rg, _ = P.nvfp4_quantize(x_roll.cuda())
+    c_r, s_r, g_r = ref_quant(x_roll, rc, rs, rg)
+    xt_np = x_train.float().numpy()
+    gc, fq, hist = P.guided_round(xt, rc, rs, rg)
+    gc_r, fq_r, hist_r = OQ.guided_round(xt_np, c_r, s_r, g_r)
+    assert np.array_equal(npu8(gc), gc_r) and np.array_equal(hist.cpu().numpy(), hist_r)
+    assert np.array_equal(fq.cpu().view(torch.int16).numpy().view(np.uint16), fq_r)
+    rec = P.guidance_record_pack(rc)
+    gc2, fq2, moved = P.guided_round_record(xt, rec, rs, rg)
+    gc2_r, fq2_r, moved_r = OQ.guided_round_record(xt_np, OQ.guidance_record(c_r), s_r, g_r)
+    assert np.array_equal(npu8(gc2), gc2_r) and np.array_equal(moved.cpu().numpy(), moved_r)
+    assert np.array_equal(fq2.cpu().view(torch.int16).numpy().view(np.uint16), fq2_r)
+
+
 @pytest.mark.parametrize("padded", [False, True])
 def test_kv_cache_quantize_and_guided(gpu_lib, padded):
     """KV-cache shapes: a key cache [300 tokens, 4 heads, 128] viewed as 1200
