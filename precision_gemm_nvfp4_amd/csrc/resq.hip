@@ -82,11 +82,23 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 // slot q -> {unit, first row, end row (at most 32 rows), the unit's first
 // slot} {the unit's end slot, 0, 0, 0}.  Records past the last tile or slot
 // (the grids are sized by upper bounds) get unit -1.
+// A unit's thread writes its records itself, except for units of more than
+// kPlanBigSlots gather slots (a hot expert's thousands of rows): the first
+// kPlanBig of those go to a list in LDS, and after the scan whole waves write
+// their records, one record per lane.
+constexpr int kPlanBigSlots = 32, kPlanBig = 64;
+struct PlanBigUnit {
+  int64_t b, e;
+  int32_t u, ts, nt, ss, ns;
+};
 __global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* tile_start,
                                                          int32_t* slot_start, int4* tile_info,
                                                          int64_t max_tiles, int4* slot_info,
                                                          int64_t max_slots) {
   __shared__ uint32_t sh[16];
+  __shared__ PlanBigUnit big[kPlanBig];
+  __shared__ int nbig;
+  if (threadIdx.x == 0) nbig = 0;             // the scans' barriers order this before any use
   uint32_t carry_t = 0, carry_s = 0;
   for (int64_t base = 0; base < units.U; base += blockDim.x) {
     int64_t u = base + threadIdx.x;
@@ -100,10 +112,22 @@ __global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* t
     uint32_t tot_t, tot_s;
     const uint32_t ex_t = block_exclusive_scan(nt, sh, &tot_t);
     const uint32_t ex_s = block_exclusive_scan(ns, sh, &tot_s);
+    bool deferred = false;
+    if (u < units.U && ns > (uint32_t)kPlanBigSlots) {
+      const int j = atomicAdd(&nbig, 1);
+      if (j < kPlanBig) {
+        big[j] = PlanBigUnit{b, e, (int32_t)u, (int32_t)(carry_t + ex_t), (int32_t)nt,
+                             (int32_t)(carry_s + ex_s), (int32_t)ns};
+        deferred = true;
+      }
+    }
     if (u < units.U) {
       const int32_t ts = (int32_t)(carry_t + ex_t), ss = (int32_t)(carry_s + ex_s);
       tile_start[u] = ts;
       slot_start[u] = ss;
+    }
+    if (u < units.U && !deferred) {
+      const int32_t ts = (int32_t)(carry_t + ex_t), ss = (int32_t)(carry_s + ex_s);
       for (uint32_t t = 0; t < nt; ++t)
         tile_info[ts + t] = int4{(int32_t)u, (int32_t)(b + (int64_t)t * kScoreTileRows), (int32_t)e, 0};
       for (uint32_t q = 0; q < ns; ++q) {
@@ -118,6 +142,18 @@ __global__ __launch_bounds__(1024) void resq_plan_kernel(Units units, int32_t* t
   if (threadIdx.x == 0) {
     tile_start[units.U] = (int32_t)carry_t;
     slot_start[units.U] = (int32_t)carry_s;
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63, nb = nbig < kPlanBig ? nbig : kPlanBig;
+  for (int j = threadIdx.x >> 6; j < nb; j += blockDim.x >> 6) {
+    const PlanBigUnit g = big[j];
+    for (int32_t t = lane; t < g.nt; t += 64)
+      tile_info[g.ts + t] = int4{g.u, (int32_t)(g.b + (int64_t)t * kScoreTileRows), (int32_t)g.e, 0};
+    for (int32_t q = lane; q < g.ns; q += 64) {
+      const int64_t r0 = g.b + (int64_t)q * kGatherRows;
+      slot_info[2 * (g.ss + q)] = int4{g.u, (int32_t)r0, (int32_t)(r0 + kGatherRows < g.e ? r0 + kGatherRows : g.e), g.ss};
+      slot_info[2 * (g.ss + q) + 1] = int4{g.ss + g.ns, 0, 0, 0};
+    }
   }
   for (int64_t t = carry_t + threadIdx.x; t < max_tiles; t += blockDim.x) tile_info[t] = int4{-1, 0, 0, 0};
   for (int64_t q = carry_s + threadIdx.x; q < max_slots; q += blockDim.x) slot_info[2 * q] = int4{-1, 0, 0, 0};
