@@ -513,7 +513,26 @@ __global__ __launch_bounds__(256) void resq_select_reg_kernel(
 #pragma unroll
   for (int j = 0; j < CH; ++j) acc[j] = 0.0f;
   if (n_my == CH) {                           // K % 16 == 0: whole 16-byte groups
-    for (int64_t t = t0; t < t1; ++t) {       // tile order
+    // NB tiles' loads go out before their additions (a unit of many tiles,
+    // e.g. a hot expert's 124, would otherwise wait out one round trip per
+    // tile); the additions keep the tile order.
+    constexpr int NB = 128 / CH;
+    int64_t t = t0;
+    for (; t + NB <= t1; t += NB) {
+      f32x4 v[NB][CH / 4];
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt)
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q)
+          v[bt][q] = reinterpret_cast<const f32x4*>(partials + (t + bt) * K + c0)[q];
+#pragma unroll
+      for (int bt = 0; bt < NB; ++bt)
+#pragma unroll
+        for (int q = 0; q < CH / 4; ++q)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[4 * q + i] = acc[4 * q + i] + v[bt][q][i];
+    }
+    for (; t < t1; ++t) {                     // the rest, in tile order
       const f32x4* src = reinterpret_cast<const f32x4*>(partials + t * K + c0);
 #pragma unroll
       for (int q = 0; q < CH / 4; ++q) {
