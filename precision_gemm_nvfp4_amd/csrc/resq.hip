@@ -290,7 +290,10 @@ __global__ __launch_bounds__(256) void resq_scores_rows_kernel(
     const int4* __restrict__ tile_info, int64_t slots, float* __restrict__ partials) {
   constexpr int XW = sizeof(T) / 2;                      // 16-byte words of x per lane and row
   const int lane = threadIdx.x & 63;
-  const int64_t slot = (int64_t)blockIdx.y * 4 + (threadIdx.x >> 6);
+  // The wave's tile, hence its rows and their row indexes, are the same for
+  // all its lanes: kept uniform, they come through scalar loads and the row
+  // addresses are scalar arithmetic.
+  const int64_t slot = (int64_t)blockIdx.y * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   if (slot >= slots) return;
   const int4 ti = tile_info[slot];
   if (ti.x < 0) return;
