@@ -354,8 +354,8 @@ def cpu_baseline(wl, inp, budget_s):
 
 def timed_steps(torch, step, steps):
     """(ms per step, {part: ms}): `steps` steps timed with no events between
-    their parts, then as many again (at least 3, at most 10) with an event at
-    each part boundary for the per-part times."""
+    their parts, then one untimed step, then as many again (at least 3, at
+    most 10) with an event at each part boundary for the per-part times."""
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record()
@@ -365,6 +365,10 @@ def timed_steps(torch, step, steps):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / steps
     n = max(3, min(steps, 10))
+    # One unmarked step first, with no synchronisation after it: the host
+    # enqueues the marked steps while the GPU runs it, so a part's events
+    # time the GPU's work rather than the host's launches of the first parts.
+    step(NoMarks())
     tls = []
     for _ in range(n):
         tl = Timeline(torch)
