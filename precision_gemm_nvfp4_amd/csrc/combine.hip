@@ -169,13 +169,14 @@ __global__ __launch_bounds__(256) void combine_rows_kernel(const float* __restri
     if (vec4 && c + 4 <= N) {
       f32x4 acc = overwrite ? f32x4{0.0f, 0.0f, 0.0f, 0.0f} : *reinterpret_cast<const f32x4*>(o + c);
       // rows in groups of 8: the group's loads go out before its additions
+      // (non-temporal: each routed row is read once)
       for (int32_t i0 = 0; i0 < n; i0 += 8) {
         f32x4 v[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
           const int32_t i = i0 + q < n ? i0 + q : n - 1;
           const int32_t r = i < kMaxListLds ? srt[i] : lst[i];
-          v[q] = *reinterpret_cast<const f32x4*>(y_rows + (int64_t)r * N + c);
+          v[q] = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y_rows + (int64_t)r * N + c));
         }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {

@@ -580,7 +580,8 @@ __global__ __launch_bounds__(kGuidedThreads) void guided_kernel(
     int64_t xo = (int64_t)i * 8;
     if (!dense) xo += (int64_t)((uint32_t)i / per_row) * (ldx - (int64_t)K);
 #pragma unroll
-    for (int j = 0; j < (int)(sizeof(T) / 2); ++j) in.q[j] = reinterpret_cast<const u32x4*>(x + xo)[j];
+    for (int j = 0; j < (int)(sizeof(T) / 2); ++j)   // x_train is read once: non-temporal
+      in.q[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(x + xo) + j);
     in.sc = roll_scales[MX ? i >> 2 : i >> 1];
     in.rw = RECORD ? (uint32_t)roll[i] : reinterpret_cast<const uint32_t*>(roll)[i];
   };
