@@ -292,13 +292,15 @@ __device__ __forceinline__ void gemm_epilogue_blocks(const GemmArgs& p, const Ti
             w[4 * g] = v[0]; w[4 * g + 1] = v[1]; w[4 * g + 2] = v[2]; w[4 * g + 3] = v[3];
           }
         }
+        // The scatter's rows are read once, by the combine: non-temporal
+        // stores (cache policy bit 1, nt on gfx950).
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const uint32_t ro = (uint32_t)((i * 32 + (q >> 2) * 8 + (q & 3)) * ld * 4);
 #pragma unroll
           for (int j = 0; j < NJ; ++j)
             __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, val(i, j, q) * w[q]), r_out,
-                                                  (int)(voff + ro + j * 128), 0, 0);
+                                                  (int)(voff + ro + j * 128), 0, scatter ? 2 : 0);
         }
       }
       return;
