@@ -247,9 +247,10 @@ int resq_mask_select_and_requant(const void* x, int dtype, int64_t x_rows, int64
  *         EWORKSPACE.
  * rows_total == 0 is valid (out_amax set to 0, nothing else written; with
  * SCATTER_F32, out is zeroed).
- * Streams: with 256-row tiles the groups' ragged remainders run on a stream
- * that the library keeps per device, forked from `stream` and joined back
- * into it with events, so the call is ordered on `stream` as one operation.
+ * Streams: with 256-row tiles the groups' ragged remainders (and, for the
+ * scatter epilogues, the plan of the row lists) run on a stream that the
+ * library keeps per device, forked from `stream` and joined back into it
+ * with events, so the call is ordered on `stream` as one operation.
  * While `stream` is being captured into a graph, everything stays on it.
  * ------------------------------------------------------------------------ */
 size_t moe_w4a4_grouped_gemm_workspace_size(int32_t E, int64_t rows_total, int64_t N, int64_t K,
