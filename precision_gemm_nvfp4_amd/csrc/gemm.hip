@@ -873,13 +873,7 @@ bool grouped_gemm_offsets_fit(int64_t a_rows, int64_t N, int64_t K) {
 // mutex keeps the event record/wait pairs of concurrent host threads apart.
 // Where the stream or its events cannot be had, the launch stays on the
 // caller's stream.
-struct SideStream {
-  std::mutex mu;
-  bool tried = false;
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-};
-static SideStream* side_stream(hipStream_t caller) {
+SideStream* side_stream(hipStream_t caller) {
   static std::mutex mu;
   static SideStream per_dev[64];
   int dev = 0;

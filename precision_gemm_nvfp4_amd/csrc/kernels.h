@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
+
 namespace nvfp4 {
 
 // quantize.hip
@@ -124,5 +126,18 @@ hipError_t launch_guided_record(const void* x, int dtype, int64_t M, int64_t K, 
                                 int64_t* moved, hipStream_t stream);
 hipError_t launch_guidance_pack(const uint8_t* codes, int64_t M, int64_t K, uint8_t* record,
                                 hipStream_t stream);
+
+// The library's second stream on the current device, with the two events
+// that fork it from and join it into a caller's stream; the mutex keeps the
+// record/wait pairs of concurrent host threads apart.  nullptr while the
+// caller's stream is being captured into a graph, or where the stream or its
+// events cannot be had: the work then stays on the caller's stream.
+struct SideStream {
+  std::mutex mu;
+  bool tried = false;
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream* side_stream(hipStream_t caller);
 
 }  // namespace nvfp4

@@ -776,12 +776,35 @@ static hipError_t launch_any(const GemmArgs& a, hipStream_t stream) {
   // a long K (a long gather table) can push the tallest tile past the LDS
   if (bm == 256 && cfg_lds<4, 4, 2, 2, A8>(a) == 0) bm = 128;
   if (bm == 128 && cfg_lds<2, 4, 2, 2, A8>(a) == 0) bm = 64;
-  switch (bm) {
-    case 256: err = launch_epi<4, 4, 2, 2, A8>(a, stream); break;
-    case 128: err = launch_epi<2, 4, 2, 2, A8>(a, stream); break;
-    case 64: err = launch_epi<1, 4, 2, 2, A8>(a, stream); break;
-    default: err = launch_epi<1, 2, 1, 4, A8>(a, stream); break;
+  auto gemm = [&]() -> hipError_t {
+    switch (bm) {
+      case 256: return launch_epi<4, 4, 2, 2, A8>(a, stream);
+      case 128: return launch_epi<2, 4, 2, 2, A8>(a, stream);
+      case 64: return launch_epi<1, 4, 2, 2, A8>(a, stream);
+      default: return launch_epi<1, 2, 1, 4, A8>(a, stream);
+    }
+  };
+  // The scatter's plan (the row lists of each output row) needs only the
+  // scatter index: with 256-row tiles (a long launch) it runs beside the GEMM
+  // on the side stream, and the ordered sum of the rows follows the join.
+  // Beside a short launch of small tiles its one workgroup waits for a CU
+  // and the fork and join cost more than they hide.
+  if (a.epilogue == 2 && bm == 256) {
+    if (SideStream* ss = side_stream(stream)) {
+      std::lock_guard<std::mutex> lk(ss->mu);
+      err = hipEventRecord(ss->fork, stream);
+      if (err == hipSuccess) err = hipStreamWaitEvent(ss->s, ss->fork, 0);
+      if (err == hipSuccess)
+        err = launch_combine_plan(a.rows_total, a.N, a.scatter_index, a.out_rows, a.y_rows, ss->s);
+      if (err == hipSuccess) err = hipEventRecord(ss->join, ss->s);
+      if (err == hipSuccess) err = gemm();
+      if (err == hipSuccess) err = hipStreamWaitEvent(stream, ss->join, 0);
+      if (err != hipSuccess) return err;
+      return launch_combine_rows(a.y_rows, a.rows_total, a.N, a.out_rows, static_cast<float*>(a.out),
+                                 a.ldo, a.combine_overwrite, a.y_rows, stream);
+    }
   }
+  err = gemm();
   if (err != hipSuccess || a.epilogue != 2) return err;
   return launch_combine(a.y_rows, a.rows_total, a.N, a.scatter_index, a.out_rows,
                         static_cast<float*>(a.out), a.ldo, a.combine_overwrite, a.y_rows, stream);
