@@ -548,6 +548,47 @@ def test_w4a8_down_scatter_overwrite(gpu_lib):
                                   dc, ds, epilogue=P.EPI_SCATTER_F32, out=y_none, **kw)
     assert np.all(np32(y_none) == 0.0)
 
+def test_mx_scatter_256_row_tiles_graph_replays(gpu_lib):
+    """Groups of 256 rows and more take 256-row tiles, and with the scatter
+    epilogue the plan of the row lists runs on the library's second stream
+    when eager (on the capturing stream under capture): the call captured in
+    a HIP graph and replayed, with eager work in between, gives the eager
+    result bit for bit; the eager result matches the oracle."""
+    P = gpu_lib
+    rng = np.random.default_rng(23)
+    counts = np.array([300, 280, 512, 261], dtype=np.int64)
+    offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    rows, n_exp, K, N, tokens = int(offs[-1]), len(counts), 256, 256, 700
+    x = torch.from_numpy(rng.standard_normal((rows, K)).astype(np.float32)).to(torch.bfloat16)
+    w = synth.weights(n_exp, N, K, seed=23, tensor_id=synth.WD_ID)
+    slot_token = rng.integers(0, tokens, size=rows).astype(np.int32)
+    slot_weight = rng.uniform(0.05, 1.0, size=rows).astype(np.float32)
+    xc, xs, _ = P.mxfp4_quantize(x.cuda())
+    wc, ws = _mx_weights(P, w)
+    kw = dict(epilogue=P.EPI_SCATTER_F32, row_weight=torch.from_numpy(slot_weight).cuda(),
+              scatter_index=torch.from_numpy(slot_token).cuda(), out_rows=tokens)
+    offs_t = torch.from_numpy(offs).cuda()
+    y0 = P.moe_mxfp4_grouped_gemm(xc, xs, offs_t, rows, wc, ws, **kw)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        y = P.moe_mxfp4_grouped_gemm(xc, xs, offs_t, rows, wc, ws, **kw)
+    for _ in range(3):
+        y.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int32), y0.view(torch.int32))
+    xc_r, xs_r = ref_mx(x.float().numpy(), xc, xs)
+    wc_r, ws_r = ref_mx_weights(w, wc, ws)
+    y_ref = np.zeros((tokens, N))
+    for e in range(n_exp):
+        a, b = int(offs[e]), int(offs[e + 1])
+        out = _gemm_ref(xc_r[a:b], xs_r[a:b], wc_r[e], ws_r[e])
+        np.add.at(y_ref, slot_token[a:b], out * slot_weight[a:b, None].astype(np.float64))
+    assert rel_err(np32(y0), y_ref) <= GEMM_TOL
+
+
 # ---------------------------------------------------------------------------
 # trainer side: MXFP4 weight QDQ and guided rounding
 # ---------------------------------------------------------------------------
